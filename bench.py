@@ -1,0 +1,186 @@
+"""Benchmark of the gfx950 tile-rANS decode path on one MI355X.
+
+Default workload (a "step"): the 4096 x 4096 BF16 Student-t(5) matrix with log-normal row scales,
+compressed at 3.0, 4.0 and 4.5 bits per weight, each decoded to BF16 and to FP16, plus the
+lossless BF16 tile-rANS decode of the same matrix: seven full-matrix decodes per step. Inputs are
+resident in HBM before timing starts; several copies of the step's buffers are used in rotation
+(> 2 GB between reuses) so that neither the compressed input nor the output of a step is still
+in the 256 MB Infinity Cache.
+
+Prints one JSON line (rank 0, N = 1): decoded-weight GB/s (container bytes written per second),
+the roofline of the dominant kernel (lossy decode to BF16) from HIP events on the launch stream,
+and the oracle's CPU decode of one step on the host cores as a reported baseline.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def c2_items():
+    """(name, stream bytes, container, rows, cols) of one step of the 4096^2 workload."""
+    import decode_tile_interleaved_rans_amd as ep
+    from decode_tile_interleaved_rans_amd import workloads as W
+    w = W.student_t_rowscaled(4096, 4096, 2)
+    items = []
+    for t in (3.0, 4.0, 4.5):
+        t0 = time.time()
+        s, bpp = ep.compress(w, t, dtype=ep.BF16)
+        log(f"encoded 4096x4096 at target {t}: actual {bpp:.4f} bpp in {time.time() - t0:.2f} s")
+        items.append((f"lossy{t}_bf16", s, "bf16", bpp))
+        items.append((f"lossy{t}_f16", s, "f16", bpp))
+    t0 = time.time()
+    s, bpp = ep.lossless_compress(w, dtype=ep.BF16)
+    log(f"lossless bf16: {bpp:.4f} bpp in {time.time() - t0:.2f} s")
+    items.append(("lossless_bf16", s, "bf16", bpp))
+    return items, w.shape
+
+
+def cpu_baseline(items, budget_s: float = 10.0):
+    import oracle
+    cores = min(16, os.cpu_count() or 1)
+    odt = {"bf16": oracle.BF16, "f16": oracle.F16}
+    t0 = time.time()
+    steps = 0
+    out_bytes = 0
+    while True:
+        for name, s, ct, _ in items:
+            out, _ = oracle.decompress(s, odt[ct], n_threads=cores)
+            out_bytes += out.nbytes
+        steps += 1
+        if time.time() - t0 >= budget_s or steps >= 3:
+            break
+    dt = time.time() - t0
+    return {"value": out_bytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{steps} full step(s) of the same workload (7 full-matrix decodes each) decoded by the "
+                      f"oracle with {cores} threads in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the decode path has no cross-GPU step (tiles, rows and "
+              "matrices shard without exchange), so run it with --gpus 1.", file=sys.stderr)
+        sys.exit(1)
+
+    import torch
+    import decode_tile_interleaved_rans_amd as ep
+
+    torch.cuda.set_device(0)
+    items, (R, C) = c2_items()
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}
+    step_out_bytes = sum(R * C * 2 for _ in items)
+    step_in_bytes = sum(len(s) for _, s, _, _ in items)
+    set_bytes = step_out_bytes + step_in_bytes
+    n_sets = max(2, math.ceil(2.5e9 / set_bytes))
+    log(f"step: {len(items)} decodes, {step_in_bytes / 1e6:.1f} MB in, {step_out_bytes / 1e6:.1f} MB out; "
+        f"{n_sets} rotating buffer sets")
+    sets = []
+    for k in range(n_sets):
+        hs = [ep.upload(s) for _, s, _, _ in items]
+        outs = [torch.empty((R, C), dtype=tdt[ct], device="cuda") for _, _, ct, _ in items]
+        sets.append((hs, outs))
+    torch.cuda.synchronize()
+
+    dominant = [i for i, (name, _, ct, _) in enumerate(items) if name.startswith("lossy") and ct == "bf16"]
+    ev = []
+
+    def step(k: int, record: bool):
+        hs, outs = sets[k % n_sets]
+        for i, (h, o) in enumerate(zip(hs, outs)):
+            if record and i in dominant:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                h.decompress_into(o)
+                b.record()
+                ev.append((i, a, b))
+            else:
+                h.decompress_into(o)
+
+    for k in range(args.warmup):
+        step(k, False)
+    torch.cuda.synchronize()
+    for hs, _ in sets:
+        for h in hs:
+            h.check()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record()
+    for k in range(args.steps):
+        step(args.warmup + k, True)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = t_start.elapsed_time(t_end)
+    for hs, _ in sets:
+        for h in hs:
+            h.check()
+    sec = ms / 1e3
+    value = step_out_bytes * args.steps / sec / 1e9
+    weights_per_s = len(items) * R * C * args.steps / sec
+
+    # dominant kernel: lossy decode to BF16; algorithmic bytes = stream bytes read + 2 B/weight written
+    dur = {}
+    for i, a, b in ev:
+        dur.setdefault(i, []).append(a.elapsed_time(b) / 1e3)
+    tot_bytes = sum(len(items[i][1]) + 2 * R * C for i in dur for _ in dur[i])
+    tot_time = sum(sum(v) for v in dur.values())
+    n_launch = sum(len(v) for v in dur.values())
+    achieved = tot_bytes / tot_time / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "decode_lossy_kernel<BF16>", "avg_launch_us": round(tot_time / n_launch * 1e6, 2),
+                "bytes_per_launch": round(tot_bytes / n_launch)}
+    per_item = {}
+    for i in dur:
+        name = items[i][0]
+        t = float(np.mean(dur[i]))
+        per_item[name] = {"us": round(t * 1e6, 2), "actual_bpp": round(items[i][3], 4),
+                          "alg_GBs": round((len(items[i][1]) + 2 * R * C) / t / 1e9, 1)}
+    cpu = None
+    if not args.no_cpu:
+        log("timing the oracle on the host cores")
+        cpu = cpu_baseline(items)
+    line = {
+        "metric": "decoded weight GB/s + % HBM roofline; fused decode+GEMM overhead vs BF16",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u32 rANS state -> fp32 -> bf16/f16", "data": "synthetic",
+        "config": {"workload": "4096x4096 bf16 Student-t(5)x0.015 rows scaled by lognormal(0.5); lossy at "
+                               "3.0/4.0/4.5 bpp decoded to BF16 and FP16 + lossless BF16 decode (7 decodes/step)",
+                   "rows": R, "cols": C, "tile": "16x256, 32 rANS lanes", "prob_bits": 12},
+        "weights_per_s": round(weights_per_s / 1e9, 3), "weights_per_s_unit": "Gweights/s",
+        "hbm_frac_step": round((step_out_bytes + step_in_bytes) * args.steps / sec / 1e9 / HBM_PEAK_GBS, 4),
+        "wall_s": round(wall, 4),
+        "roofline": roofline,
+        "per_decode": per_item,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,289 @@
+"""MI355X (gfx950) tile-rANS weight codec: Python binding of ``libentropack.so``.
+
+The functions mirror the C ABI in ``include/entropack.h`` and only marshal arguments: the host
+encoder, the stream validator and every GPU step run in the compiled library. PyTorch provides
+device memory and the current HIP stream. There is no fallback path: if the library is missing,
+every call raises.
+
+    stream, bpp = compress(weight, target_bpp=4.0)       # host encoder
+    w_hat = decompress(stream, torch.bfloat16)           # GPU decode into a container
+    layer = CompressedLinear.from_linear(linear, 4.0)    # fused decode + BF16 MFMA GEMM
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libentropack.so")
+
+F32, BF16, F16, F8E4M3, I8, U8 = 0, 1, 2, 3, 4, 5
+LOSSY, LOSSLESS = 0, 1
+STATUS = {0: "EP_OK", -1: "EP_EINVAL", -2: "EP_ECORRUPT", -3: "EP_EUNSUPPORTED", -4: "EP_ERANGE",
+          -5: "EP_EHIP", -6: "EP_ENOMEM", -7: "EP_EDEVICE"}
+EXPORTS = ["ep_compress", "ep_free", "ep_stream_info", "ep_upload", "ep_handle_info", "ep_decompress",
+           "ep_decompress_many", "ep_decode_symbols", "ep_linear_forward", "ep_gemm_bf16", "ep_handle_check",
+           "ep_release", "ep_last_error", "ep_version"]
+
+
+class EPError(RuntimeError):
+    def __init__(self, status: int, call: str, msg: str):
+        super().__init__(f"{call}: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class EncodeOpts(C.Structure):
+    _fields_ = [("mode", C.c_int), ("target_bpp", C.c_double), ("prob_bits", C.c_int), ("tile_rows", C.c_int),
+                ("n_threads", C.c_int)]
+
+
+class Info(C.Structure):
+    _fields_ = [("rows", C.c_int64), ("cols", C.c_int64), ("mode", C.c_int32), ("src_dtype", C.c_int32),
+                ("tile_rows", C.c_int32), ("prob_bits", C.c_int32), ("n_tiles", C.c_uint32),
+                ("n_escapes", C.c_uint32), ("step", C.c_float), ("target_bpp", C.c_float),
+                ("actual_bpp", C.c_double), ("total_bytes", C.c_uint64), ("payload_bytes", C.c_uint64),
+                ("state_bytes", C.c_uint64), ("meta_bytes", C.c_uint64)]
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load the compiled library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m decode_tile_interleaved_rans_amd.build")
+        L = C.CDLL(LIB_PATH)
+        vp, i64, sz = C.c_void_p, C.c_int64, C.c_size_t
+        L.ep_compress.argtypes = [vp, C.c_int, i64, i64, C.POINTER(EncodeOpts), C.POINTER(C.POINTER(C.c_uint8)),
+                                  C.POINTER(sz), C.POINTER(C.c_double)]
+        L.ep_free.argtypes = [vp]
+        L.ep_free.restype = None
+        L.ep_stream_info.argtypes = [C.c_char_p, sz, C.POINTER(Info)]
+        L.ep_upload.argtypes = [C.c_char_p, sz, vp, C.POINTER(vp)]
+        L.ep_handle_info.argtypes = [vp, C.POINTER(Info)]
+        L.ep_decompress.argtypes = [vp, C.c_int, vp, vp, vp]
+        L.ep_decompress_many.argtypes = [vp, vp, vp, vp, C.c_int, vp]
+        L.ep_decode_symbols.argtypes = [vp, vp, vp]
+        L.ep_linear_forward.argtypes = [vp, vp, i64, vp, vp, vp]
+        L.ep_gemm_bf16.argtypes = [vp, vp, i64, i64, i64, vp, vp]
+        L.ep_handle_check.argtypes = [vp, vp]
+        L.ep_release.argtypes = [vp]
+        L.ep_release.restype = None
+        L.ep_last_error.restype = C.c_char_p
+        L.ep_version.restype = C.c_char_p
+        for name in EXPORTS:
+            if name not in ("ep_free", "ep_release", "ep_last_error", "ep_version"):
+                getattr(L, name).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, call: str):
+    if rc != 0:
+        raise EPError(rc, call, lib().ep_last_error().decode(errors="replace"))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+_DT_OF_TORCH = None
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    table = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16, torch.float8_e4m3fn: F8E4M3,
+             torch.int8: I8, torch.uint8: U8}
+    if t not in table:
+        raise ValueError(f"unsupported dtype {t}")
+    return table[t]
+
+
+def _torch_dtype(code: int):
+    torch = _torch()
+    return {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16, F8E4M3: torch.float8_e4m3fn,
+            I8: torch.int8, U8: torch.uint8}[code]
+
+
+def _stream_ptr(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+# ------------------------------------------------------------------------------------ host side
+def compress(w, target_bpp: float = 4.0, *, mode: int = LOSSY, prob_bits: int = 12, tile_rows: int = 16,
+             n_threads: int = 0, dtype: int | None = None) -> tuple[bytes, float]:
+    """Compress a 2-D weight (torch tensor on any device, or numpy array) on the host.
+    Returns (stream bytes, actual bits per weight including every byte of metadata)."""
+    if hasattr(w, "detach"):
+        torch = _torch()
+        code = _dtype_code(w.dtype)
+        t = w.detach().contiguous().cpu()
+        view = t.view(torch.int16) if t.element_size() == 2 else (t.view(torch.uint8) if t.element_size() == 1 else t)
+        arr = view.numpy()
+    else:
+        arr = np.ascontiguousarray(w)
+        code = dtype if dtype is not None else {np.dtype(np.float32): F32, np.dtype(np.uint8): U8}.get(arr.dtype)
+        if code is None:
+            raise ValueError("numpy inputs other than float32/uint8 need dtype= (16-bit data as uint16 bits)")
+    if arr.ndim != 2:
+        raise ValueError("compress takes a 2-D [out_features, in_features] matrix")
+    R, Cc = arr.shape
+    opts = EncodeOpts(mode, float(target_bpp), prob_bits, tile_rows, n_threads)
+    out = C.POINTER(C.c_uint8)()
+    n = C.c_size_t()
+    bpp = C.c_double()
+    _check(lib().ep_compress(arr.ctypes.data_as(C.c_void_p), code, R, Cc, C.byref(opts), C.byref(out), C.byref(n),
+                             C.byref(bpp)), "ep_compress")
+    data = C.string_at(out, n.value)
+    lib().ep_free(out)
+    return data, bpp.value
+
+
+def lossless_compress(w, **kw) -> tuple[bytes, float]:
+    return compress(w, 0.0, mode=LOSSLESS, **kw)
+
+
+def stream_info(stream: bytes) -> dict:
+    info = Info()
+    _check(lib().ep_stream_info(stream, len(stream), C.byref(info)), "ep_stream_info")
+    return info.as_dict()
+
+
+# ------------------------------------------------------------------------------------ device side
+class Handle:
+    """A validated stream resident on the current GPU."""
+
+    def __init__(self, stream: bytes, hip_stream=None):
+        self._h = C.c_void_p()
+        _check(lib().ep_upload(stream, len(stream), _stream_ptr(hip_stream), C.byref(self._h)), "ep_upload")
+        info = Info()
+        _check(lib().ep_handle_info(self._h, C.byref(info)), "ep_handle_info")
+        self.info = info.as_dict()
+        self.shape = (self.info["rows"], self.info["cols"])
+
+    @property
+    def ptr(self):
+        return self._h
+
+    def decompress_into(self, out, row_scale=None, stream=None):
+        torch = _torch()
+        code = _dtype_code(out.dtype) if out.dtype != torch.int16 else None
+        if code is None:
+            raise ValueError("use decode_symbols_into for int16 outputs")
+        if tuple(out.shape) != self.shape or not out.is_contiguous() or not out.is_cuda:
+            raise ValueError(f"output must be a contiguous CUDA tensor of shape {self.shape}")
+        sp = C.c_void_p(row_scale.data_ptr()) if row_scale is not None else None
+        _check(lib().ep_decompress(self._h, code, C.c_void_p(out.data_ptr()), sp, _stream_ptr(stream)),
+               "ep_decompress")
+        return out
+
+    def decompress(self, dtype=None, stream=None):
+        """Decode into a new tensor. FP8 / INT8 return (values, per-row fp32 scale)."""
+        torch = _torch()
+        if dtype is None:
+            dtype = _torch_dtype(self.info["src_dtype"]) if self.info["mode"] == LOSSLESS else torch.bfloat16
+        out = torch.empty(self.shape, dtype=dtype, device="cuda")
+        scale = None
+        if self.info["mode"] == LOSSY and dtype in (torch.float8_e4m3fn, torch.int8):
+            scale = torch.empty(self.shape[0], dtype=torch.float32, device="cuda")
+        self.decompress_into(out, scale, stream)
+        return (out, scale) if scale is not None else out
+
+    def decode_symbols(self, stream=None):
+        torch = _torch()
+        q = torch.empty(self.shape, dtype=torch.int16, device="cuda")
+        _check(lib().ep_decode_symbols(self._h, C.c_void_p(q.data_ptr()), _stream_ptr(stream)), "ep_decode_symbols")
+        return q
+
+    def check(self, stream=None):
+        _check(lib().ep_handle_check(self._h, _stream_ptr(stream)), "ep_handle_check")
+
+    def release(self):
+        if self._h:
+            lib().ep_release(self._h)
+            self._h = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.release()
+        except Exception:
+            pass
+
+
+def upload(stream: bytes, hip_stream=None) -> Handle:
+    return Handle(stream, hip_stream)
+
+
+def decompress(stream: bytes, dtype=None, device: str = "cuda"):
+    """Decode a stream on the GPU ("decompress(stream) returns a tensor")."""
+    h = Handle(stream)
+    try:
+        return h.decompress(dtype)
+    finally:
+        _torch().cuda.current_stream().synchronize()
+        h.release()
+
+
+def decompress_many(handles, outs, scales=None, stream=None):
+    """One grouped call over several uploaded matrices."""
+    n = len(handles)
+    hs = (C.c_void_p * n)(*[h.ptr.value for h in handles])
+    cts = (C.c_int * n)(*[_dtype_code(o.dtype) for o in outs])
+    os_ = (C.c_void_p * n)(*[o.data_ptr() for o in outs])
+    sc = (C.c_void_p * n)(*[(s.data_ptr() if s is not None else None) for s in (scales or [None] * n)])
+    _check(lib().ep_decompress_many(hs, cts, os_, sc, n, _stream_ptr(stream)), "ep_decompress_many")
+
+
+def gemm_bf16(x, w, stream=None):
+    """Y = X W^T in BF16 with fp32 accumulation (the library's own MFMA GEMM)."""
+    torch = _torch()
+    M, K = x.shape
+    N = w.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(lib().ep_gemm_bf16(C.c_void_p(x.data_ptr()), C.c_void_p(w.data_ptr()), M, N, K, C.c_void_p(y.data_ptr()),
+                              _stream_ptr(stream)), "ep_gemm_bf16")
+    return y
+
+
+class CompressedLinear:
+    """Linear layer that keeps only the compressed weight; forward decodes it inside the GEMM."""
+
+    def __init__(self, stream: bytes, bias=None):
+        self.stream = stream
+        self.handle = Handle(stream)
+        self.out_features, self.in_features = self.handle.shape
+        self.bias = bias
+
+    @classmethod
+    def from_linear(cls, linear, target_bpp: float = 4.0, **kw):
+        s, _ = compress(linear.weight, target_bpp, **kw)
+        bias = None
+        if linear.bias is not None:
+            bias = linear.bias.detach().to(device="cuda", dtype=_torch().bfloat16).contiguous()
+        return cls(s, bias)
+
+    @property
+    def actual_bpp(self) -> float:
+        return self.handle.info["actual_bpp"]
+
+    def forward(self, x, stream=None):
+        torch = _torch()
+        shp = x.shape
+        x2 = x.reshape(-1, shp[-1]).to(torch.bfloat16).contiguous()
+        y = torch.empty((x2.shape[0], self.out_features), dtype=torch.bfloat16, device=x.device)
+        bp = C.c_void_p(self.bias.data_ptr()) if self.bias is not None else None
+        _check(lib().ep_linear_forward(self.handle.ptr, C.c_void_p(x2.data_ptr()), x2.shape[0], bp,
+                                       C.c_void_p(y.data_ptr()), _stream_ptr(stream)), "ep_linear_forward")
+        return y.reshape(*shp[:-1], self.out_features)
+
+    __call__ = forward

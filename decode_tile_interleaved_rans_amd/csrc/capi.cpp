@@ -1,0 +1,279 @@
+// C ABI of the tile-rANS weight codec: argument checks, stream upload, and kernel dispatch.
+// The calls and their contracts are documented in include/entropack.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "entropack.h"
+#include "ep_internal.h"
+#include "kernels.h"
+
+struct ep_handle {
+    ep::StreamView view;        // header fields and tables (the view's byte pointers are not kept)
+    ep_info info;
+    uint8_t* dev = nullptr;     // one allocation: stream copy | table blob | error flag
+    size_t stream_off = 0, tables_off = 0, err_off = 0, bytes = 0;
+    int device = 0;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+ep_status fail(ep_status st, const std::string& msg) {
+    g_err = msg;
+    return st;
+}
+
+ep_status hip_fail(hipError_t e, const char* what) {
+    return fail(e == hipErrorOutOfMemory ? EP_ENOMEM : EP_EHIP,
+                std::string(what) + ": " + hipGetErrorString(e));
+}
+
+size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Device decode tables: lut [t][slot] = symbol, then sym [t][s] = f | c << 13 | value << 32.
+std::vector<uint8_t> build_tables(const ep::StreamView& v) {
+    const int n = v.prob_bits;
+    const size_t M = (size_t)1 << n;
+    std::vector<uint8_t> blob(ep::table_blob_bytes(v.n_tables, n), 0);
+    uint8_t* lut = blob.data();
+    uint64_t* sym = reinterpret_cast<uint64_t*>(blob.data() + ((size_t)v.n_tables << n));
+    for (int t = 0; t < v.n_tables; ++t) {
+        const ep::Table& T = v.tables[t];
+        uint32_t c = 0;
+        for (int s = 0; s < 256; ++s) {
+            const uint32_t f = T.freq[s];
+            int32_t value;
+            if (v.mode == EP_MODE_LOSSLESS) value = s;
+            else if (t == 0) value = T.lo + s;
+            else value = s == ep::kEscape ? 0 : 2 * (T.lo + s) + ((t - 1) & 1);
+            sym[(size_t)t * 256 + s] = (uint64_t)(f | c << 13) | (uint64_t)(uint32_t)value << 32;
+            for (uint32_t k = 0; k < f; ++k) lut[(size_t)t * M + c + k] = (uint8_t)s;
+            c += f;
+        }
+    }
+    return blob;
+}
+
+ep::DecodeParams params_for(const ep_handle* h) {
+    const ep::StreamView& v = h->view;
+    const uint8_t* s = h->dev + h->stream_off;
+    ep::DecodeParams p{};
+    p.payload = reinterpret_cast<const uint32_t*>(s + v.off_payload);
+    p.index = reinterpret_cast<const uint32_t*>(s + v.off_index);
+    p.row_scale = reinterpret_cast<const float*>(s + v.off_scale);
+    p.row_qmax = reinterpret_cast<const uint16_t*>(s + v.off_qmax);
+    p.tables = h->dev + h->tables_off;
+    p.mode = v.mode;
+    p.n_tables = v.n_tables;
+    p.prob_bits = v.prob_bits;
+    p.tile_rows = v.tile_rows;
+    p.rows = v.rows;
+    p.cols = v.cols;
+    p.tiles_c = v.tiles_c;
+    p.pairs_c = (v.tiles_c + 1) / 2;
+    p.n_pairs = v.tiles_r * p.pairs_c;
+    p.step = v.step;
+    p.err = reinterpret_cast<int*>(h->dev + h->err_off);
+    return p;
+}
+
+bool container_ok(const ep_handle* h, int ct) {
+    if (h->view.mode == EP_MODE_LOSSLESS) return ct == h->view.dtype;
+    return ct == EP_BF16 || ct == EP_F16 || ct == EP_F8E4M3 || ct == EP_I8;
+}
+
+ep_status check_decode_args(const ep_handle* h, ep_dtype ct, void* out, float* scale) {
+    if (!h) return fail(EP_EINVAL, "null handle");
+    if (!container_ok(h, ct))
+        return fail(EP_EUNSUPPORTED, h->view.mode == EP_MODE_LOSSLESS
+                                         ? "a lossless stream decodes only to its own dtype"
+                                         : "lossy streams decode to BF16, F16, F8E4M3 or I8");
+    if (!out && h->view.rows * h->view.cols > 0) return fail(EP_EINVAL, "null output pointer");
+    const bool wants_scale = h->view.mode == EP_MODE_LOSSY_E8 && (ct == EP_F8E4M3 || ct == EP_I8);
+    if (wants_scale && !scale && h->view.rows > 0) return fail(EP_EINVAL, "F8E4M3 and I8 need a row-scale output");
+    if (!wants_scale && scale) return fail(EP_EINVAL, "row-scale output given for a container without one");
+    return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ep_last_error(void) { return g_err.c_str(); }
+
+const char* ep_version(void) { return "entropack-mi355x 0.1 (EPK1, gfx950)"; }
+
+void ep_free(void* p) { std::free(p); }
+
+ep_status ep_compress(const void* host_w, ep_dtype src, int64_t rows, int64_t cols, const ep_encode_opts* opts,
+                      uint8_t** out_stream, size_t* out_len, double* actual_bpp) {
+    if (!out_stream || !out_len) return fail(EP_EINVAL, "null output pointer");
+    if (rows < 0 || cols < 0) return fail(EP_EINVAL, "negative shape");
+    if (rows * cols > 0 && !host_w) return fail(EP_EINVAL, "null input");
+    if (rows > 0xFFFFFFFFll || cols >= (1ll << 28)) return fail(EP_ERANGE, "shape too large (cols must be < 2^28)");
+    ep_encode_opts o = opts ? *opts : ep_encode_opts{EP_MODE_LOSSY_E8, 4.0, 12, 16, 0};
+    if (o.prob_bits < 10 || o.prob_bits > 12) return fail(EP_EINVAL, "prob_bits must be 10..12");
+    if (o.tile_rows != 16 && o.tile_rows != 32) return fail(EP_EINVAL, "tile_rows must be 16 or 32");
+    if (o.mode == EP_MODE_LOSSY_E8) {
+        if (src != EP_F32 && src != EP_BF16 && src != EP_F16)
+            return fail(EP_EUNSUPPORTED, "lossy mode takes F32, BF16 or F16 input");
+        if (!(o.target_bpp > 0.0 && o.target_bpp <= 32.0)) return fail(EP_EINVAL, "target_bpp must be in (0, 32]");
+    } else if (o.mode == EP_MODE_LOSSLESS) {
+        if (ep::element_bytes(src) == 0) return fail(EP_EUNSUPPORTED, "unknown dtype");
+    } else {
+        return fail(EP_EINVAL, "unknown mode");
+    }
+    std::vector<uint8_t> buf;
+    std::string why;
+    ep_status st;
+    try {
+        st = ep::encode(host_w, src, rows, cols, o, &buf, &why);
+    } catch (const std::bad_alloc&) {
+        return fail(EP_ENOMEM, "host allocation failed while encoding");
+    }
+    if (st != EP_OK) return fail(st, why);
+    uint8_t* p = static_cast<uint8_t*>(std::malloc(buf.size() ? buf.size() : 1));
+    if (!p) return fail(EP_ENOMEM, "host allocation failed");
+    std::memcpy(p, buf.data(), buf.size());
+    *out_stream = p;
+    *out_len = buf.size();
+    if (actual_bpp) *actual_bpp = rows * cols > 0 ? 8.0 * (double)buf.size() / ((double)rows * (double)cols) : 0.0;
+    return EP_OK;
+}
+
+ep_status ep_stream_info(const uint8_t* host_stream, size_t len, ep_info* out) {
+    if (!host_stream || !out) return fail(EP_EINVAL, "null pointer");
+    ep::StreamView v;
+    std::string why;
+    ep_status st = ep::parse_stream(host_stream, len, &v, &why);
+    if (st != EP_OK) return fail(st, why);
+    ep::fill_info(v, out);
+    return EP_OK;
+}
+
+ep_status ep_upload(const uint8_t* host_stream, size_t len, void* hip_stream, ep_handle** out) {
+    if (!host_stream || !out) return fail(EP_EINVAL, "null pointer");
+    *out = nullptr;
+    ep_handle* h = new (std::nothrow) ep_handle();
+    if (!h) return fail(EP_ENOMEM, "host allocation failed");
+    std::string why;
+    ep_status st = ep::parse_stream(host_stream, len, &h->view, &why);
+    if (st != EP_OK) {
+        delete h;
+        return fail(st, why);
+    }
+    ep::fill_info(h->view, &h->info);
+    std::vector<uint8_t> blob = build_tables(h->view);
+    h->stream_off = 0;
+    h->tables_off = up(len, 256);
+    h->err_off = up(h->tables_off + blob.size(), 256);
+    h->bytes = h->err_off + 256;
+    hipGetDevice(&h->device);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&h->dev), h->bytes);
+    if (e != hipSuccess) {
+        delete h;
+        return hip_fail(e, "hipMalloc for the stream");
+    }
+    e = hipMemcpyAsync(h->dev + h->stream_off, host_stream, len, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(h->dev + h->tables_off, blob.data(), blob.size(), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipMemsetAsync(h->dev + h->err_off, 0, 256, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        hipFree(h->dev);
+        delete h;
+        return hip_fail(e, "copying the stream to the device");
+    }
+    // the view's pointers referred to the caller's bytes: drop them
+    h->view.base = nullptr;
+    *out = h;
+    return EP_OK;
+}
+
+ep_status ep_handle_info(const ep_handle* h, ep_info* out) {
+    if (!h || !out) return fail(EP_EINVAL, "null pointer");
+    *out = h->info;
+    return EP_OK;
+}
+
+void ep_release(ep_handle* h) {
+    if (!h) return;
+    if (h->dev) (void)hipFree(h->dev);
+    delete h;
+}
+
+ep_status ep_decompress(const ep_handle* h, ep_dtype container, void* dev_out, float* dev_row_scale, void* hip_stream) {
+    ep_status st = check_decode_args(h, container, dev_out, dev_row_scale);
+    if (st != EP_OK) return st;
+    ep::DecodeParams p = params_for(h);
+    p.out = dev_out;
+    p.scale_out = dev_row_scale;
+    hipError_t e = ep::launch_decode(p, (int)container, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return EP_OK;
+}
+
+ep_status ep_decompress_many(const ep_handle* const* hs, const ep_dtype* containers, void* const* dev_outs,
+                             float* const* dev_row_scales, int count, void* hip_stream) {
+    if (count < 0 || (count > 0 && (!hs || !containers || !dev_outs))) return fail(EP_EINVAL, "null array");
+    for (int i = 0; i < count; ++i) {
+        ep_status st = check_decode_args(hs[i], containers[i], dev_outs[i], dev_row_scales ? dev_row_scales[i] : nullptr);
+        if (st != EP_OK) return fail(st, "matrix " + std::to_string(i) + ": " + g_err);
+    }
+    for (int i = 0; i < count; ++i) {
+        ep::DecodeParams p = params_for(hs[i]);
+        p.out = dev_outs[i];
+        p.scale_out = dev_row_scales ? dev_row_scales[i] : nullptr;
+        hipError_t e = ep::launch_decode(p, (int)containers[i], static_cast<hipStream_t>(hip_stream));
+        if (e != hipSuccess) return hip_fail(e, "decode launch");
+    }
+    return EP_OK;
+}
+
+ep_status ep_decode_symbols(const ep_handle* h, int16_t* dev_q, void* hip_stream) {
+    if (!h) return fail(EP_EINVAL, "null handle");
+    if (h->view.mode != EP_MODE_LOSSY_E8) return fail(EP_EUNSUPPORTED, "symbols exist only for lossy streams");
+    if (!dev_q && h->view.rows * h->view.cols > 0) return fail(EP_EINVAL, "null output pointer");
+    ep::DecodeParams p = params_for(h);
+    p.out = dev_q;
+    hipError_t e = ep::launch_decode(p, ep::CT_Q16, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return EP_OK;
+}
+
+ep_status ep_handle_check(ep_handle* h, void* hip_stream) {
+    if (!h) return fail(EP_EINVAL, "null handle");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    int flag = 0;
+    hipError_t e = hipMemcpyAsync(&flag, h->dev + h->err_off, sizeof flag, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "reading the device error flag");
+    if (flag) {
+        e = hipMemsetAsync(h->dev + h->err_off, 0, sizeof(int), s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        return fail(EP_EDEVICE, std::string("decode kernel flagged the stream:") + (flag & 1 ? " word count" : "") +
+                                    (flag & 2 ? " final state" : ""));
+    }
+    return EP_OK;
+}
+
+ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias, void* dev_y,
+                            void* hip_stream) {
+    (void)w; (void)dev_x; (void)M; (void)dev_bias; (void)dev_y; (void)hip_stream;
+    return fail(EP_EUNSUPPORTED, "fused linear forward not built yet");
+}
+
+ep_status ep_gemm_bf16(const void* dev_x, const void* dev_w, int64_t M, int64_t N, int64_t K, void* dev_y,
+                       void* hip_stream) {
+    (void)dev_x; (void)dev_w; (void)M; (void)N; (void)K; (void)dev_y; (void)hip_stream;
+    return fail(EP_EUNSUPPORTED, "bf16 GEMM not built yet");
+}
+
+}  // extern "C"

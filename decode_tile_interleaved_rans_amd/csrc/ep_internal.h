@@ -1,0 +1,67 @@
+// Internal declarations shared by the host encoder, the stream validator, the C ABI and the
+// kernel launchers of the MI355X tile-rANS codec.
+//
+// Stream layout (EPK1, little-endian). A 128-byte header, then sections that each start on a
+// 16-byte boundary: row scales f32[R] and row max |q| u16[R] (lossy only), the symbol tables
+// (per table: i16 window start, u16 window width S, u16 escape frequency, u16 freq[S]), the tile
+// index u32[n_tiles + 1] (offsets in 4-byte units from the payload start) and the payload.
+// A tile is 32 u32 rANS states followed by its u16 words (plus one zero pad word when their
+// count is odd). The pages fix none of this; it is this codec's own container for "entropy-coded
+// in independently decodable tiles" (EntroPack paper, Abstract).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "entropack.h"
+
+namespace ep {
+
+constexpr int kLanes = 32;             // interleaved rANS states per tile
+constexpr int kTileCols = 256;         // columns per tile: 32 lanes x one 8-wide E8 block
+constexpr int kHeaderBytes = 128;
+constexpr int kLossyTables = 17;       // coset bit + 8 coordinate positions x 2 cosets
+constexpr int kEscape = 255;           // escape symbol of the lossy coordinate tables
+constexpr uint32_t kRansLow = 1u << 16;
+
+// header field offsets
+enum HeaderField : int {
+    kMagic = 0, kVersion = 4, kMode = 6, kDtype = 7, kRows = 8, kCols = 12, kTileRows = 16,
+    kTileColsField = 18, kLanesField = 20, kProbBits = 22, kNumTables = 23, kStep = 24,
+    kTarget = 28, kNumTiles = 32, kNumEscapes = 36, kOffScale = 40, kOffQmax = 48,
+    kOffTables = 56, kOffIndex = 64, kOffPayload = 72, kTotalLen = 80, kPayloadCrc = 88
+};
+
+struct Table {
+    int32_t lo = 0;        // first coordinate value of the window (lossless: 0)
+    int32_t width = 1;     // window width S
+    uint32_t freq[256];    // normalized frequency per symbol (escape at 255 for lossy tables)
+};
+
+// A validated stream (views into the caller's bytes).
+struct StreamView {
+    const uint8_t* base = nullptr;
+    size_t len = 0;
+    int mode = 0, dtype = 0, tile_rows = 16, prob_bits = 12, n_tables = 0;
+    int64_t rows = 0, cols = 0, tiles_r = 0, tiles_c = 0;
+    uint32_t n_tiles = 0, n_escapes = 0;
+    float step = 0.0f, target = 0.0f;
+    uint64_t off_scale = 0, off_qmax = 0, off_tables = 0, off_index = 0, off_payload = 0;
+    uint64_t payload_len = 0;
+    std::vector<Table> tables;
+};
+
+int element_bytes(int dtype);
+uint32_t crc32(const uint8_t* p, size_t n);
+
+// Validation (host). Returns EP_OK or EP_ECORRUPT with a message in *why.
+ep_status parse_stream(const uint8_t* s, size_t len, StreamView* out, std::string* why);
+void fill_info(const StreamView& v, ep_info* info);
+
+// Host encoder.
+ep_status encode(const void* w, int dtype, int64_t rows, int64_t cols, const ep_encode_opts& o,
+                 std::vector<uint8_t>* out, std::string* why);
+
+}  // namespace ep

@@ -1,0 +1,160 @@
+/*
+ * entropack.h — C ABI of the MI355X (gfx950) tile-rANS weight codec.
+ *
+ * What the library computes. Weights are compressed by row normalization, nearest-point
+ * quantization on the E8 lattice, a probability model of the lattice coordinates, a sampled
+ * estimate that picks the quantization step for a target bitrate, and entropy coding in tiles
+ * that decode independently; on the GPU the symbols are decoded and the weights reconstructed
+ * into BF16, FP16, FP8 or INT8 containers in one fused pass ("EntroPack: Fast and Accurate
+ * Entropy-Coded Weight Compression at Arbitrary Bitrates", Abstract). The calls follow the
+ * pages' statement of the interface: compress(tensor, target) returning a stream and its actual
+ * bitrate, which includes metadata ("EntroPack PyTorch Guide: Lossless Weights, Bitrates and
+ * Memory Checks", sections "Choose a compression contract" and "Start with a tensor round
+ * trip"); decompress(stream) returning a tensor; a compressed linear layer whose forward pass
+ * consumes the compressed weight (same guide, "Replace one linear layer before a whole model").
+ *
+ * Conventions for every call:
+ *   - Status: every call returns ep_status (0 = EP_OK, negative = error). No C++ exception
+ *     crosses the ABI. After an error, ep_last_error() returns a message for the calling thread.
+ *   - Matrices are row-major [rows][cols]; for a linear layer rows = out_features.
+ *   - "host" pointers are CPU memory; "dev" pointers are device memory of the current HIP
+ *     device; hip_stream is a hipStream_t (NULL = the default stream). Device work is queued
+ *     on hip_stream and returns without synchronizing unless stated otherwise.
+ *   - Ownership: buffers returned by ep_compress belong to the caller and are freed with
+ *     ep_free; ep_handle objects belong to the caller and are freed with ep_release; device
+ *     outputs are always allocated by the caller.
+ *   - Thread safety: distinct handles may be used from distinct threads; a handle is immutable
+ *     after ep_upload except for its device error flag.
+ */
+#ifndef ENTROPACK_H
+#define ENTROPACK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EP_OK = 0,
+    EP_EINVAL = -1,        /* bad argument (null pointer, bad size, bad option) */
+    EP_ECORRUPT = -2,      /* stream fails validation, or a decode found it inconsistent */
+    EP_EUNSUPPORTED = -3,  /* container / dtype / mode the stream cannot supply (no silent casts) */
+    EP_ERANGE = -4,        /* value out of the representable range (non-finite input, too wide) */
+    EP_EHIP = -5,          /* a HIP runtime call failed; the message names it */
+    EP_ENOMEM = -6,        /* host or device allocation failed */
+    EP_EDEVICE = -7        /* a kernel flagged a stream inconsistency (see ep_handle_check) */
+} ep_status;
+
+typedef enum { EP_F32 = 0, EP_BF16 = 1, EP_F16 = 2, EP_F8E4M3 = 3, EP_I8 = 4, EP_U8 = 5 } ep_dtype;
+
+typedef enum {
+    EP_MODE_LOSSY_E8 = 0,  /* target bitrate, E8 lattice coordinates */
+    EP_MODE_LOSSLESS = 1   /* bit-exact byte-plane coding of any supported dtype */
+} ep_mode;
+
+/* Encoder options. A NULL pointer means: lossy, target 4.0, prob_bits 12, tile_rows 16, all
+ * host threads. */
+typedef struct {
+    ep_mode mode;
+    double target_bpp;     /* lossy only: target payload bits per weight (0 < t <= 32) */
+    int prob_bits;         /* probability precision n (10..12); frequencies sum to 2^n */
+    int tile_rows;         /* 16 or 32 rows per tile; tiles are tile_rows x 256 */
+    int n_threads;         /* host encoder threads, 0 = all hardware threads */
+} ep_encode_opts;
+
+/* Stream summary. actual_bpp = 8 * total_bytes / (rows * cols) (0 for an empty matrix). */
+typedef struct {
+    int64_t rows, cols;
+    int32_t mode, src_dtype, tile_rows, prob_bits;
+    uint32_t n_tiles, n_escapes;
+    float step, target_bpp;
+    double actual_bpp;
+    uint64_t total_bytes, payload_bytes, state_bytes, meta_bytes;
+} ep_info;
+
+typedef struct ep_handle ep_handle;   /* device-resident, validated stream */
+
+/* Compress a host matrix.
+ *   host_w: [rows][cols] elements of dtype src (lossy: EP_F32, EP_BF16, EP_F16; lossless: any).
+ *   *out_stream receives a library-allocated byte buffer (free with ep_free), *out_len its size,
+ *   *actual_bpp (optional) the stored bits per weight including all metadata.
+ * Errors: EP_EINVAL (null pointers, bad options), EP_EUNSUPPORTED (dtype not allowed for the
+ * mode), EP_ERANGE (non-finite lossy input, cols >= 2^28), EP_ENOMEM. */
+ep_status ep_compress(const void* host_w, ep_dtype src, int64_t rows, int64_t cols,
+                      const ep_encode_opts* opts, uint8_t** out_stream, size_t* out_len,
+                      double* actual_bpp);
+
+/* Free a buffer returned by ep_compress. NULL is allowed. */
+void ep_free(void* p);
+
+/* Validate a host stream (magic, version, section bounds, every table summing to 2^n, tile
+ * offsets, payload CRC-32) and summarize it. Host only; no device work. EP_ECORRUPT on any
+ * inconsistency. */
+ep_status ep_stream_info(const uint8_t* host_stream, size_t len, ep_info* out);
+
+/* Validate a host stream and copy it to the current device together with its decode tables.
+ * Synchronizes hip_stream before returning (the host buffer may be freed afterwards).
+ * *out receives the handle. Errors: EP_ECORRUPT, EP_ENOMEM, EP_EHIP. */
+ep_status ep_upload(const uint8_t* host_stream, size_t len, void* hip_stream, ep_handle** out);
+
+/* Summary of an uploaded stream (same fields as ep_stream_info). */
+ep_status ep_handle_info(const ep_handle* h, ep_info* out);
+
+/* Decode a whole matrix into a device container (the "decompress" call).
+ *   dev_out: [rows][cols] elements of `container`, row-major, 16-byte aligned when cols % 8 == 0
+ *            for the vector-store path (any alignment of the element size is accepted).
+ *   dev_row_scale: [rows] fp32 dequantization scales, written for EP_F8E4M3 and EP_I8 (the
+ *            weight is value * scale[row]); must be NULL for other containers.
+ * Lossy streams accept EP_BF16, EP_F16, EP_F8E4M3, EP_I8; lossless streams accept only their
+ * own dtype (EP_EUNSUPPORTED otherwise). Asynchronous on hip_stream. */
+ep_status ep_decompress(const ep_handle* h, ep_dtype container, void* dev_out,
+                        float* dev_row_scale, void* hip_stream);
+
+/* Decode `count` matrices in one grouped launch. Arrays are host arrays of length count with
+ * the same meaning as ep_decompress's arguments; NULL entries in dev_row_scales are allowed
+ * where the container needs none. Asynchronous on hip_stream. */
+ep_status ep_decompress_many(const ep_handle* const* hs, const ep_dtype* containers,
+                             void* const* dev_outs, float* const* dev_row_scales, int count,
+                             void* hip_stream);
+
+/* Decode a lossy stream's lattice symbols: dev_q [rows][cols] int16 doubled coordinates
+ * q = 2p of the E8 point p (the reconstructed weight is q * step / 2 * row_scale).
+ * EP_EUNSUPPORTED for lossless streams. Asynchronous on hip_stream. */
+ep_status ep_decode_symbols(const ep_handle* h, int16_t* dev_q, void* hip_stream);
+
+/* Compressed linear layer forward: Y[M][N] = X[M][K] * W^T (+ bias), W = the decoded BF16
+ * weight [N][K] of handle w, fp32 accumulation, BF16 output. Decoding is fused into the GEMM:
+ * decoded tiles go to LDS as the MFMA B operand, and no decoded copy of W is written.
+ *   dev_x: [M][K] bf16; dev_bias: [N] bf16 or NULL; dev_y: [M][N] bf16.
+ * Requires a lossy stream. Asynchronous on hip_stream. */
+ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias,
+                            void* dev_y, void* hip_stream);
+
+/* Plain BF16 GEMM with the same tiling as ep_linear_forward, for overhead comparisons:
+ * Y[M][N] = X[M][K] * W^T, X [M][K] bf16, W [N][K] bf16, Y [M][N] bf16, fp32 accumulation.
+ * Asynchronous on hip_stream. */
+ep_status ep_gemm_bf16(const void* dev_x, const void* dev_w, int64_t M, int64_t N, int64_t K,
+                       void* dev_y, void* hip_stream);
+
+/* Synchronize hip_stream and read the handle's device error flag, which kernels set when a
+ * tile's words run out or overrun, or a lane's final rANS state differs from its initial
+ * value. EP_EDEVICE if set (the flag is then cleared), else EP_OK. */
+ep_status ep_handle_check(ep_handle* h, void* hip_stream);
+
+/* Free a handle and its device memory. NULL is allowed. The caller must ensure no queued
+ * work still uses it. */
+void ep_release(ep_handle* h);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char* ep_last_error(void);
+
+/* Library build string (version, target architecture). */
+const char* ep_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENTROPACK_H */

@@ -1,0 +1,212 @@
+"""GPU parity of the gfx950 decode kernels against the oracle (bit-exact: symbols, container
+bytes and row scales), through the C ABI.
+
+Inputs are the seeded synthetic workloads: a 1024x1024 fp32 Gaussian matrix with 0.1% outliers
+at 4.0 bpp; 4096x4096 bf16 Student-t(5) rows with log-normal row scales at 3.0 / 4.0 / 4.5 bpp
+plus the lossless bf16 round trip; ragged shapes, escapes, degenerate matrices; sampled tiles of
+8192x8192 at 4.5 bpp and of one full-size DiT-like block."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import decode_tile_interleaved_rans_amd as ep
+from decode_tile_interleaved_rans_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+CONTAINERS = {"bf16": (torch.bfloat16, oracle.BF16), "f16": (torch.float16, oracle.F16),
+              "f8": (torch.float8_e4m3fn, oracle.F8E4M3), "i8": (torch.int8, oracle.I8)}
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    t = t.cpu()
+    if t.element_size() == 2:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.element_size() == 1:
+        return t.view(torch.uint8).numpy()
+    return t.view(torch.int32).numpy().view(np.uint32)
+
+
+def gpu_decode(stream: bytes, dtype):
+    h = ep.upload(stream)
+    out = h.decompress(dtype)
+    torch.cuda.synchronize()
+    h.check()
+    return out
+
+
+def assert_parity(stream: bytes, names=("bf16", "f16", "f8", "i8"), threads=16):
+    h = ep.upload(stream)
+    q = h.decode_symbols()
+    qo, _ = oracle.decode_symbols(stream, n_threads=threads)
+    torch.cuda.synchronize()
+    h.check()
+    assert np.array_equal(q.cpu().numpy(), qo), "decoded symbols"
+    for name in names:
+        tdt, odt = CONTAINERS[name]
+        res = h.decompress(tdt)
+        torch.cuda.synchronize()
+        h.check()
+        want, wscale = oracle.decompress(stream, odt, n_threads=threads)
+        if isinstance(res, tuple):
+            out, scale = res
+            assert np.array_equal(scale.cpu().numpy(), wscale), f"{name} row scales"
+        else:
+            out = res
+        assert np.array_equal(bits(out), want), f"{name} container bytes"
+    h.release()
+
+
+def test_c1_gaussian_outliers_all_containers():
+    w = W.gaussian_with_outliers()
+    s, bpp = ep.compress(w, 4.0)
+    assert bpp >= 4.0
+    assert_parity(s)
+
+
+@pytest.mark.parametrize("target", [3.0, 4.0, 4.5])
+def test_c2_student_t_4096(target):
+    w = W.student_t_rowscaled(4096, 4096, 2)
+    s, _ = ep.compress(w, target, dtype=ep.BF16)
+    assert_parity(s, names=("bf16", "f16"))
+
+
+def test_c2_lossless_bf16_roundtrip():
+    w = W.student_t_rowscaled(4096, 4096, 2)
+    s, bpp = ep.lossless_compress(w, dtype=ep.BF16)
+    out = gpu_decode(s, torch.bfloat16)
+    assert np.array_equal(bits(out), w)
+    assert bpp < 16.0
+
+
+@pytest.mark.parametrize("shape,prob_bits,tile_rows", [((17, 300), 12, 16), ((1, 1), 12, 16), ((33, 513), 11, 32),
+                                                       ((5, 7), 10, 16), ((16, 768), 12, 16), ((48, 2304), 10, 32),
+                                                       ((130, 1000), 11, 16)])
+def test_ragged_shapes_and_options(shape, prob_bits, tile_rows):
+    rng = np.random.default_rng(sum(shape))
+    w = (0.02 * rng.standard_t(5, shape)).astype(np.float32)
+    s, _ = ep.compress(w, 4.0, prob_bits=prob_bits, tile_rows=tile_rows)
+    assert_parity(s)
+
+
+def test_escapes_and_small_rows():
+    rng = np.random.default_rng(5)
+    w = rng.normal(0, 0.01, (64, 512)).astype(np.float32)
+    w[rng.random(w.shape) < 0.002] = 3.0
+    w[10] *= 1e-30                       # tiny row scale: FP16 subnormal outputs
+    w[11] = 0.0
+    s, _ = ep.compress(w, 7.0)
+    assert ep.stream_info(s)["n_escapes"] > 0
+    assert_parity(s)
+
+
+def test_degenerate_matrices():
+    for w in [np.zeros((40, 300), np.float32), np.full((16, 256), 0.5, np.float32)]:
+        s, _ = ep.compress(w, 4.0)
+        assert_parity(s)
+    s, _ = ep.compress(np.zeros((0, 16), np.float32), 4.0)
+    h = ep.upload(s)
+    out = torch.empty((0, 16), dtype=torch.bfloat16, device="cuda")
+    h.decompress_into(out)
+    torch.cuda.synchronize()
+    h.check()
+
+
+@pytest.mark.parametrize("dt", ["f16", "f32", "u8", "zeros"])
+def test_lossless_other_dtypes(dt):
+    rng = np.random.default_rng(6)
+    shape = (37, 600)
+    if dt == "f16":
+        x, code, tdt = rng.normal(0, 1, shape).astype(np.float16).view(np.uint16), ep.F16, torch.float16
+    elif dt == "f32":
+        x, code, tdt = rng.normal(0, 1, shape).astype(np.float32).view(np.uint32), ep.F32, torch.float32
+    elif dt == "u8":
+        x, code, tdt = rng.integers(0, 9, shape).astype(np.uint8), ep.U8, torch.uint8
+    else:
+        x, code, tdt = np.zeros(shape, np.uint16), ep.BF16, torch.bfloat16
+    s, _ = ep.lossless_compress(x, dtype=code)
+    out = gpu_decode(s, tdt)
+    assert np.array_equal(bits(out), x)
+
+
+def test_grouped_decode_matches_single():
+    rng = np.random.default_rng(7)
+    streams, conts = [], []
+    for i, (R, Cc, t) in enumerate([(256, 512, 3.0), (128, 1024, 6.0), (300, 700, 2.5), (64, 256, 4.5)]):
+        w = (0.02 * rng.standard_t(5, (R, Cc))).astype(np.float32)
+        streams.append(ep.compress(w, t)[0])
+        conts.append([torch.bfloat16, torch.float8_e4m3fn, torch.int8, torch.float16][i])
+    hs = [ep.upload(s) for s in streams]
+    outs = [torch.empty(h.shape, dtype=c, device="cuda") for h, c in zip(hs, conts)]
+    scales = [torch.empty(h.shape[0], dtype=torch.float32, device="cuda") if c in (torch.float8_e4m3fn, torch.int8)
+              else None for h, c in zip(hs, conts)]
+    ep.decompress_many(hs, outs, scales)
+    torch.cuda.synchronize()
+    for h, s, o, sc, c in zip(hs, streams, outs, scales, conts):
+        h.check()
+        odt = {torch.bfloat16: oracle.BF16, torch.float16: oracle.F16, torch.float8_e4m3fn: oracle.F8E4M3,
+               torch.int8: oracle.I8}[c]
+        want, wsc = oracle.decompress(s, odt, n_threads=8)
+        assert np.array_equal(bits(o), want)
+        if sc is not None:
+            assert np.array_equal(sc.cpu().numpy(), wsc)
+
+
+def test_device_flag_on_inconsistent_stream():
+    """A stream that passes host validation (CRC recomputed) but whose lane state was altered:
+    the kernel's bounded reads keep it in range and the final-state check raises the flag."""
+    import zlib
+    w = W.gaussian_with_outliers(64, 512, seed=8)
+    s, _ = ep.compress(w, 4.0)
+    off_pay = int.from_bytes(s[72:80], "little")
+    bad = bytearray(s)
+    bad[off_pay + 4 * 3 + 1] ^= 0x10                       # tile 0, lane 3 state
+    bad[88:92] = zlib.crc32(bytes(bad[off_pay:])).to_bytes(4, "little")
+    h = ep.upload(bytes(bad))
+    h.decompress(torch.bfloat16)
+    with pytest.raises(ep.EPError) as e:
+        h.check()
+    assert e.value.status == -7
+    h.check()                                              # the flag was cleared
+
+
+def test_unsupported_container_is_an_error():
+    x = np.zeros((16, 256), np.uint16)
+    s, _ = ep.lossless_compress(x, dtype=ep.BF16)
+    h = ep.upload(s)
+    with pytest.raises(ep.EPError) as e:
+        h.decompress(torch.float16)
+    assert e.value.status == -3
+
+
+def sampled_tile_parity(stream: bytes, n_sample: int, seed: int, dtype=torch.bfloat16, odt=oracle.BF16):
+    """Decode the full matrix on the GPU, then compare randomly chosen tiles with the oracle's
+    decode of just those tiles."""
+    info = ep.stream_info(stream)
+    h = ep.upload(stream)
+    out = h.decompress(dtype)
+    torch.cuda.synchronize()
+    h.check()
+    rng = np.random.default_rng(seed)
+    tiles = np.sort(rng.choice(info["n_tiles"], size=min(n_sample, info["n_tiles"]), replace=False))
+    want = oracle.decompress_tiles(stream, tiles, odt)
+    tr_rows, tiles_c = info["tile_rows"], -(-info["cols"] // 256)
+    got = bits(out)
+    for k, t in enumerate(tiles):
+        r0, c0 = (t // tiles_c) * tr_rows, (t % tiles_c) * 256
+        blk = got[r0:r0 + tr_rows, c0:c0 + 256]
+        assert np.array_equal(blk, want[k][: blk.shape[0], : blk.shape[1]]), f"tile {t}"
+
+
+def test_c4_8192_sampled_tiles():
+    w = W.student_t(8192, 8192, 4, 0.02)
+    s, bpp = ep.compress(w, 4.5, dtype=ep.BF16)
+    sampled_tile_parity(s, 400, 1)
+
+
+def test_c3_one_dit_block_sampled_tiles():
+    for m in range(5):
+        w = W.dit_matrix(0, m)
+        s, _ = ep.compress(w, 4.0, dtype=ep.BF16)
+        sampled_tile_parity(s, 100, m)

@@ -1,0 +1,162 @@
+"""Host-side tests of the product library (no GPU): the C ABI exports, the threaded host encoder
+against the oracle encoder (byte-identical streams), and stream validation errors.
+
+Encoder parity: both encoders implement the same stream definition independently (the oracle in
+plain C, the product in threaded C++), so equal bytes on varied inputs pin the product's
+quantizer, model, rate search and tile coder to the oracle, whose own pins live in the
+test_oracle_* files."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import decode_tile_interleaved_rans_amd as ep
+from decode_tile_interleaved_rans_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            names |= set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(ep_\w+)\s*\(", src, re.M))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"ep_compress", "ep_upload", "ep_decompress", "ep_linear_forward"} <= names
+    L = ep.lib()
+    for n in sorted(names):
+        assert hasattr(L, n), n
+    assert set(ep.EXPORTS) == names
+    assert b"gfx950" in L.ep_version()
+
+
+def oracle_and_product(w, target, dtype=None, mode=0, prob_bits=12, tile_rows=16, threads=4):
+    so, bo = oracle.compress(w, target, dtype=dtype, mode=mode, prob_bits=prob_bits, tile_rows=tile_rows)
+    sp, bp = ep.compress(w, target, dtype=dtype, mode=mode, prob_bits=prob_bits, tile_rows=tile_rows,
+                         n_threads=threads)
+    return so, sp, bo, bp
+
+
+@pytest.mark.parametrize("target", [2.5, 4.0, 6.0])
+def test_encoder_matches_oracle_gaussian_outliers(target):
+    w = W.gaussian_with_outliers(1024, 1024, seed=1)
+    so, sp, bo, bp = oracle_and_product(w, target)
+    assert so == sp and bo == bp
+
+
+@pytest.mark.parametrize("shape,prob_bits,tile_rows", [((100, 300), 10, 16), ((33, 513), 11, 32), ((16, 256), 12, 16),
+                                                       ((1, 9), 12, 16), ((257, 1000), 12, 32)])
+def test_encoder_matches_oracle_shapes(shape, prob_bits, tile_rows):
+    rng = np.random.default_rng(sum(shape) + prob_bits)
+    w = (0.02 * rng.standard_t(5, shape)).astype(np.float32)
+    w[rng.random(shape) < 0.003] *= 40
+    so, sp, *_ = oracle_and_product(w, 4.5, prob_bits=prob_bits, tile_rows=tile_rows, threads=3)
+    assert so == sp
+
+
+def test_encoder_matches_oracle_bf16_rowscaled():
+    w = W.student_t_rowscaled(512, 768, 2)
+    so, sp, *_ = oracle_and_product(w, 3.0, dtype=ep.BF16, threads=8)
+    assert so == sp
+
+
+def test_encoder_matches_oracle_fp16_and_escapes():
+    rng = np.random.default_rng(3)
+    x = rng.normal(0, 0.01, (64, 512)).astype(np.float32)
+    x[rng.random(x.shape) < 0.002] = 3.0
+    h = x.astype(np.float16).view(np.uint16)
+    so, sp, *_ = oracle_and_product(h, 7.0, dtype=ep.F16)
+    assert so == sp
+    assert oracle.info(so)["n_escapes"] > 0
+
+
+def test_encoder_matches_oracle_degenerate():
+    for w in [np.zeros((40, 300), np.float32), np.zeros((0, 7), np.float32), np.full((16, 256), 0.5, np.float32)]:
+        so, sp, *_ = oracle_and_product(w, 4.0)
+        assert so == sp
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32", "u8"])
+def test_lossless_encoder_matches_oracle(dt):
+    rng = np.random.default_rng(4)
+    shape = (37, 600)
+    if dt == "bf16":
+        x, code = W.student_t_rowscaled(*shape, seed=9), ep.BF16
+    elif dt == "f16":
+        x, code = rng.normal(0, 1, shape).astype(np.float16).view(np.uint16), ep.F16
+    elif dt == "f32":
+        x, code = rng.normal(0, 1, shape).astype(np.float32).view(np.uint32), ep.F32
+    else:
+        x, code = rng.integers(0, 7, shape).astype(np.uint8), ep.U8
+    so, sp, *_ = oracle_and_product(x, 0.0, dtype=code, mode=ep.LOSSLESS)
+    assert so == sp
+
+
+@pytest.mark.slow
+def test_encoder_matches_oracle_4096_student_t():
+    w = W.student_t_rowscaled(4096, 4096, 2)
+    for t in (3.0, 4.0, 4.5):
+        so, sp, *_ = oracle_and_product(w, t, dtype=ep.BF16, threads=8)
+        assert so == sp
+    so, sp, *_ = oracle_and_product(w, 0.0, dtype=ep.BF16, mode=ep.LOSSLESS, threads=8)
+    assert so == sp
+
+
+def test_stream_info_matches_oracle():
+    w = W.gaussian_with_outliers(256, 512, seed=2)
+    s, bpp = ep.compress(w, 4.0)
+    a, b = ep.stream_info(s), oracle.info(s)
+    assert a["rows"] == b["rows"] and a["payload_bytes"] == b["payload_bytes"] and a["n_tiles"] == b["n_tiles"]
+    assert a["actual_bpp"] == bpp == 8 * len(s) / w.size
+    assert a["meta_bytes"] + a["payload_bytes"] == len(s)
+
+
+def test_validation_errors():
+    w = W.gaussian_with_outliers(64, 512, seed=3)
+    s, _ = ep.compress(w, 4.0)
+    cases = {
+        "magic": b"EPK2" + s[4:],
+        "truncated": s[:-4],
+        "header": s[:100],
+        "crc": s[:-10] + bytes([s[-10] ^ 1]) + s[-9:],
+        "table_sum": s[:0x200] + s[0x200:],  # placeholder replaced below
+    }
+    info = oracle.info(s)
+    off_tables = int.from_bytes(s[56:64], "little")
+    bad = bytearray(s)
+    bad[off_tables + 6] ^= 1                       # first frequency of table 0
+    cases["table_sum"] = bytes(bad)
+    bad = bytearray(s)
+    off_index = int.from_bytes(s[64:72], "little")
+    bad[off_index + 4:off_index + 8] = (10).to_bytes(4, "little")   # tile 0 shorter than its states
+    cases["index"] = bytes(bad)
+    for name, blob in cases.items():
+        with pytest.raises(ep.EPError) as e:
+            ep.stream_info(blob)
+        assert e.value.status == -2, name
+    assert info["n_tiles"] == 8
+
+
+def test_bad_arguments():
+    w = np.zeros((4, 4), np.float32)
+    with pytest.raises(ep.EPError) as e:
+        ep.compress(w, 0.0)
+    assert e.value.status == -1
+    with pytest.raises(ep.EPError) as e:
+        ep.compress(w, 4.0, prob_bits=9)
+    assert e.value.status == -1
+    with pytest.raises(ep.EPError) as e:
+        ep.compress(np.zeros((4, 4), np.uint8), 4.0, dtype=ep.U8)
+    assert e.value.status == -3
+    bad = np.ones((4, 4), np.float32)
+    bad[1, 1] = np.inf
+    with pytest.raises(ep.EPError) as e:
+        ep.compress(bad, 4.0)
+    assert e.value.status == -4
