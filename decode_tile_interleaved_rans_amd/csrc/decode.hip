@@ -40,8 +40,15 @@ __device__ inline uint32_t bf16_rne(float v) {
     uint32_t u = __float_as_uint(v);
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;      // finite inputs only
 }
+// The fp32 product is rounded first and then converted: without the register barrier the
+// backend folds "multiply then narrow" into one mixed-precision FMA that rounds only once,
+// which differs from the two-step rounding in rare ties.
+__device__ inline float materialize(float v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
 __device__ inline uint32_t f16_rne(float v) {
-    _Float16 h = (_Float16)v;                            // v_cvt_f16_f32: round to nearest even
+    _Float16 h = (_Float16)materialize(v);               // v_cvt_f16_f32: round to nearest even
     return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 // OCP E4M3FN, round to nearest even, saturating at +-448.

@@ -36,13 +36,24 @@ def gpu_decode(stream: bytes, dtype):
     return out
 
 
+def mismatch_report(name, got, want, q=None):
+    bad = np.argwhere(got != want)
+    msg = f"{name}: {len(bad)} of {got.size} elements differ"
+    for r, c in bad[:6]:
+        msg += f"\n  [{r},{c}] gpu={int(got[r, c]):#x} oracle={int(want[r, c]):#x}"
+        if q is not None:
+            msg += f" q={int(q[r, c])}"
+    return msg
+
+
 def assert_parity(stream: bytes, names=("bf16", "f16", "f8", "i8"), threads=16):
     h = ep.upload(stream)
     q = h.decode_symbols()
     qo, _ = oracle.decode_symbols(stream, n_threads=threads)
     torch.cuda.synchronize()
     h.check()
-    assert np.array_equal(q.cpu().numpy(), qo), "decoded symbols"
+    assert np.array_equal(q.cpu().numpy(), qo), mismatch_report("symbols", q.cpu().numpy(), qo)
+    errors = []
     for name in names:
         tdt, odt = CONTAINERS[name]
         res = h.decompress(tdt)
@@ -51,11 +62,15 @@ def assert_parity(stream: bytes, names=("bf16", "f16", "f8", "i8"), threads=16):
         want, wscale = oracle.decompress(stream, odt, n_threads=threads)
         if isinstance(res, tuple):
             out, scale = res
-            assert np.array_equal(scale.cpu().numpy(), wscale), f"{name} row scales"
+            if not np.array_equal(scale.cpu().numpy(), wscale):
+                errors.append(mismatch_report(f"{name} row scales", scale.cpu().numpy()[:, None], wscale[:, None]))
         else:
             out = res
-        assert np.array_equal(bits(out), want), f"{name} container bytes"
+        got = bits(out)
+        if not np.array_equal(got, want):
+            errors.append(mismatch_report(f"{name} container", got, want, qo))
     h.release()
+    assert not errors, "\n".join(errors)
 
 
 def test_c1_gaussian_outliers_all_containers():
