@@ -2,6 +2,7 @@
 // The calls and their contracts are documented in include/entropack.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -37,13 +38,15 @@ ep_status hip_fail(hipError_t e, const char* what) {
 
 size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Device decode tables: lut [t][slot] = symbol, then sym [t][s] = f | c << 13 | value << 32.
+// Device decode tables: lut [t][slot] = symbol, fc [t][s] = f | c << 13, val [t][s] = the value
+// a lossy symbol stands for (doubled coordinate 2 (lo + s) + b, or the coset for table 0).
 std::vector<uint8_t> build_tables(const ep::StreamView& v) {
     const int n = v.prob_bits;
     const size_t M = (size_t)1 << n;
     std::vector<uint8_t> blob(ep::table_blob_bytes(v.n_tables, n), 0);
     uint8_t* lut = blob.data();
-    uint64_t* sym = reinterpret_cast<uint64_t*>(blob.data() + ((size_t)v.n_tables << n));
+    uint32_t* fc = reinterpret_cast<uint32_t*>(blob.data() + ((size_t)v.n_tables << n));
+    int16_t* val = reinterpret_cast<int16_t*>(blob.data() + ((size_t)v.n_tables << n) + (size_t)v.n_tables * 1024);
     for (int t = 0; t < v.n_tables; ++t) {
         const ep::Table& T = v.tables[t];
         uint32_t c = 0;
@@ -52,8 +55,9 @@ std::vector<uint8_t> build_tables(const ep::StreamView& v) {
             int32_t value;
             if (v.mode == EP_MODE_LOSSLESS) value = s;
             else if (t == 0) value = T.lo + s;
-            else value = s == ep::kEscape ? 0 : 2 * (T.lo + s) + ((t - 1) & 1);
-            sym[(size_t)t * 256 + s] = (uint64_t)(f | c << 13) | (uint64_t)(uint32_t)value << 32;
+            else value = (s == ep::kEscape || s >= T.width) ? 0 : 2 * (T.lo + s) + ((t - 1) & 1);
+            fc[(size_t)t * 256 + s] = f | c << 13;
+            val[(size_t)t * 256 + s] = (int16_t)value;
             for (uint32_t k = 0; k < f; ++k) lut[(size_t)t * M + c + k] = (uint8_t)s;
             c += f;
         }
@@ -61,27 +65,38 @@ std::vector<uint8_t> build_tables(const ep::StreamView& v) {
     return blob;
 }
 
-ep::DecodeParams params_for(const ep_handle* h) {
+ep::MatDesc desc_for(const ep_handle* h, int container, void* out, float* scale) {
     const ep::StreamView& v = h->view;
     const uint8_t* s = h->dev + h->stream_off;
-    ep::DecodeParams p{};
-    p.payload = reinterpret_cast<const uint32_t*>(s + v.off_payload);
-    p.index = reinterpret_cast<const uint32_t*>(s + v.off_index);
-    p.row_scale = reinterpret_cast<const float*>(s + v.off_scale);
-    p.row_qmax = reinterpret_cast<const uint16_t*>(s + v.off_qmax);
-    p.tables = h->dev + h->tables_off;
-    p.mode = v.mode;
-    p.n_tables = v.n_tables;
-    p.prob_bits = v.prob_bits;
-    p.tile_rows = v.tile_rows;
-    p.rows = v.rows;
-    p.cols = v.cols;
-    p.tiles_c = v.tiles_c;
-    p.pairs_c = (v.tiles_c + 1) / 2;
-    p.n_pairs = v.tiles_r * p.pairs_c;
-    p.step = v.step;
-    p.err = reinterpret_cast<int*>(h->dev + h->err_off);
-    return p;
+    ep::MatDesc d{};
+    d.payload = reinterpret_cast<const uint32_t*>(s + v.off_payload);
+    d.index = reinterpret_cast<const uint32_t*>(s + v.off_index);
+    d.row_scale = reinterpret_cast<const float*>(s + v.off_scale);
+    d.row_qmax = reinterpret_cast<const uint16_t*>(s + v.off_qmax);
+    d.tables = h->dev + h->tables_off;
+    d.out = out;
+    d.scale_out = scale;
+    d.err = reinterpret_cast<int*>(h->dev + h->err_off);
+    d.rows = (uint32_t)v.rows;
+    d.cols = (uint32_t)v.cols;
+    d.tiles_c = (uint32_t)v.tiles_c;
+    d.pairs_c = (uint32_t)((v.tiles_c + 1) / 2);
+    d.step = v.step;
+    d.prob_bits = (uint8_t)v.prob_bits;
+    d.tile_rows = (uint8_t)v.tile_rows;
+    d.container = (uint8_t)container;
+    d.n_tables = (uint8_t)v.n_tables;
+    return d;
+}
+
+// Launch the matrices of one mode in groups of at most kMaxGroup.
+hipError_t launch_all(const std::vector<ep::MatDesc>& ds, int mode, hipStream_t stream) {
+    for (size_t i = 0; i < ds.size(); i += ep::kMaxGroup) {
+        const int n = (int)std::min<size_t>(ep::kMaxGroup, ds.size() - i);
+        hipError_t e = ep::launch_group(ds.data() + i, n, mode, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 bool container_ok(const ep_handle* h, int ct) {
@@ -212,10 +227,8 @@ void ep_release(ep_handle* h) {
 ep_status ep_decompress(const ep_handle* h, ep_dtype container, void* dev_out, float* dev_row_scale, void* hip_stream) {
     ep_status st = check_decode_args(h, container, dev_out, dev_row_scale);
     if (st != EP_OK) return st;
-    ep::DecodeParams p = params_for(h);
-    p.out = dev_out;
-    p.scale_out = dev_row_scale;
-    hipError_t e = ep::launch_decode(p, (int)container, static_cast<hipStream_t>(hip_stream));
+    std::vector<ep::MatDesc> one{desc_for(h, (int)container, dev_out, dev_row_scale)};
+    hipError_t e = launch_all(one, h->view.mode, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return EP_OK;
 }
@@ -223,16 +236,16 @@ ep_status ep_decompress(const ep_handle* h, ep_dtype container, void* dev_out, f
 ep_status ep_decompress_many(const ep_handle* const* hs, const ep_dtype* containers, void* const* dev_outs,
                              float* const* dev_row_scales, int count, void* hip_stream) {
     if (count < 0 || (count > 0 && (!hs || !containers || !dev_outs))) return fail(EP_EINVAL, "null array");
+    std::vector<ep::MatDesc> by_mode[2];
     for (int i = 0; i < count; ++i) {
-        ep_status st = check_decode_args(hs[i], containers[i], dev_outs[i], dev_row_scales ? dev_row_scales[i] : nullptr);
+        float* sc = dev_row_scales ? dev_row_scales[i] : nullptr;
+        ep_status st = check_decode_args(hs[i], containers[i], dev_outs[i], sc);
         if (st != EP_OK) return fail(st, "matrix " + std::to_string(i) + ": " + g_err);
+        by_mode[hs[i]->view.mode].push_back(desc_for(hs[i], (int)containers[i], dev_outs[i], sc));
     }
-    for (int i = 0; i < count; ++i) {
-        ep::DecodeParams p = params_for(hs[i]);
-        p.out = dev_outs[i];
-        p.scale_out = dev_row_scales ? dev_row_scales[i] : nullptr;
-        hipError_t e = ep::launch_decode(p, (int)containers[i], static_cast<hipStream_t>(hip_stream));
-        if (e != hipSuccess) return hip_fail(e, "decode launch");
+    for (int mode = 0; mode < 2; ++mode) {
+        hipError_t e = launch_all(by_mode[mode], mode, static_cast<hipStream_t>(hip_stream));
+        if (e != hipSuccess) return hip_fail(e, "grouped decode launch");
     }
     return EP_OK;
 }
@@ -241,9 +254,8 @@ ep_status ep_decode_symbols(const ep_handle* h, int16_t* dev_q, void* hip_stream
     if (!h) return fail(EP_EINVAL, "null handle");
     if (h->view.mode != EP_MODE_LOSSY_E8) return fail(EP_EUNSUPPORTED, "symbols exist only for lossy streams");
     if (!dev_q && h->view.rows * h->view.cols > 0) return fail(EP_EINVAL, "null output pointer");
-    ep::DecodeParams p = params_for(h);
-    p.out = dev_q;
-    hipError_t e = ep::launch_decode(p, ep::CT_Q16, static_cast<hipStream_t>(hip_stream));
+    std::vector<ep::MatDesc> one{desc_for(h, ep::CT_Q16, dev_q, nullptr)};
+    hipError_t e = launch_all(one, 0, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return EP_OK;
 }

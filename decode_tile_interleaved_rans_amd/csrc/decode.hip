@@ -1,29 +1,36 @@
 // gfx950 decode kernels of the tile-rANS weight codec.
 //
-// "The final coordinates are entropy-coded in independently decodable tiles, enabling fast,
-// fused symbol decoding and numerical weight reconstruction on the GPU", with BF16, FP16, FP8 and
-// INT8 containers ("EntroPack: Fast and Accurate Entropy-Coded Weight Compression at Arbitrary
-// Bitrates", Abstract). Lossless byte-plane tiles follow the lossless tile-ANS contract named in
-// "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", "Choose a compression
-// contract".
+// The method codes lattice coordinates in tiles that decode independently, so that symbol
+// decoding and weight reconstruction run fused on the GPU, into BF16, FP16, FP8 or INT8
+// containers ("EntroPack: Fast and Accurate Entropy-Coded Weight Compression at Arbitrary
+// Bitrates", Abstract). Lossless byte-plane tiles implement the lossless tile-ANS option listed in
+// "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section "Choose a
+// compression contract".
 //
 // Work mapping. A tile is tile_rows x 256 weights coded by 32 interleaved rANS states; lane l of
 // a tile owns the 8-column block l of every tile row. One wave64 decodes two horizontally
-// adjacent tiles of the same tile row: lanes 0-31 the even tile, lanes 32-63 the odd one, so
-// every decoded block row becomes one contiguous store of 1 KiB (BF16) per wave, and both halves
-// share the row's scale. Blocks of 16 waves stage the symbol tables of the matrix in LDS once
-// and walk tile pairs persistently.
+// adjacent tiles of one tile row: lanes 0-31 the even tile, lanes 32-63 the odd one, so each
+// decoded block row is one contiguous 1 KiB store (BF16) per wave and both halves share the
+// row's scale. A launch covers up to 32 matrices; each block of 16 waves serves one matrix,
+// stages that matrix's decode tables in LDS, and walks its range of tile pairs.
+//
+// Word staging. Every half-wave keeps a 1024-word LDS ring of its tile's word stream, filled by
+// coalesced 512-byte chunk loads that are issued one chunk ahead, so the serial rANS chain only
+// ever waits on LDS. Before each block row the ring is topped up until it holds more than the
+// most a row can consume (9 steps x 64 words), so the steps need no bounds checks; a damaged
+// stream can only read stale ring words, and is caught by the end-of-tile checks.
 //
 // Per decoding step every lane looks up its slot in the LDS table, updates its state, and lanes
-// whose state fell below 2^16 take the next word of their tile; a wave ballot plus a popcount of
-// the lower lanes gives each refilling lane its word index, so each half reads one compact run
-// of words. Lanes that decoded the escape symbol then read their raw value the same way.
+// whose state fell below 2^16 take the next word of their tile; a wave ballot, shifted to the
+// lane's half and popcounted below the lane, gives each refilling lane its word index. Lanes
+// that decoded the escape symbol then read their raw value the same way.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstdint>
 #include <mutex>
 #include <set>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -31,9 +38,12 @@ namespace ep {
 namespace {
 
 constexpr uint32_t kLow = 1u << 16;
-constexpr int kWavesPerBlock = 16;
-constexpr int kErrWords = 1;    // a tile ran out of words / did not end on its last word
-constexpr int kErrState = 2;    // a final state differs from 2^16
+constexpr int kWaves = 16;                 // waves per block
+constexpr int kRingWords = 1024;           // per tile
+constexpr int kRingBytes = 2 * kRingWords;
+constexpr int kChunkDw = 128;              // one chunk: 32 lanes x 4 dwords = 256 words
+constexpr int kErrWords = 1;               // words ran out or were left over
+constexpr int kErrState = 2;               // a final state differs from 2^16
 
 // ----------------------------------------------------------------------------- containers
 __device__ inline uint32_t bf16_rne(float v) {
@@ -60,8 +70,7 @@ __device__ inline uint32_t e4m3_rne_sat(float v) {
     if (u >= 0x43E00000u) {                              // >= 448 (448..464 rounds to 448 too)
         r = 0x7Eu;
     } else if (u < 0x3C800000u) {                        // below 2^-6: subnormal grid of 2^-9
-        float m = __builtin_rintf(__uint_as_float(u) * 512.0f);
-        r = (uint32_t)m;                                 // 8 -> 0x08, the smallest normal
+        r = (uint32_t)__builtin_rintf(__uint_as_float(u) * 512.0f);   // 8 -> 0x08, smallest normal
     } else {
         u += 0x7FFFFu + ((u >> 20) & 1u);                // round the mantissa to 3 bits
         uint32_t e = (u >> 23) - 127u + 7u;
@@ -71,277 +80,344 @@ __device__ inline uint32_t e4m3_rne_sat(float v) {
     return r | sign;
 }
 
-// ----------------------------------------------------------------------------- LDS tables
-// lut[t][slot] = symbol; sym[t][s] = (f | c << 13) | (int64)value << 32, where value is the
-// doubled coordinate 2 (lo + s) + b for lossy coordinate tables, the coset b for table 0 and the
-// byte s for lossless planes.
-struct Lds {
+// ----------------------------------------------------------------------------- matrix setup
+struct Tables {
     const uint8_t* lut;
-    const uint64_t* sym;
+    const uint32_t* fc;
+    const int16_t* val;
 };
 
-__device__ inline void stage_tables(const DecodeParams& p, uint8_t* smem, Lds* L) {
-    const size_t lut_bytes = (size_t)p.n_tables << p.prob_bits;
-    const size_t total = lut_bytes + (size_t)p.n_tables * 256 * 8;
-    const uint4* src = reinterpret_cast<const uint4*>(p.tables);
-    uint4* dst = reinterpret_cast<uint4*>(smem);
-    for (size_t i = threadIdx.x; i < total / 16; i += blockDim.x) dst[i] = src[i];
-    __syncthreads();
-    L->lut = smem;
-    L->sym = reinterpret_cast<const uint64_t*>(smem + lut_bytes);
+__device__ inline const MatDesc& my_matrix(const GroupArgs& g, int* block_in_matrix) {
+    int mi = 0;
+    while (mi + 1 < g.count && (int)blockIdx.x >= g.block_start[mi + 1]) ++mi;
+    *block_in_matrix = (int)blockIdx.x - g.block_start[mi];
+    return g.m[mi];
 }
 
-struct Lane {
-    uint32_t x;          // rANS state
-    uint32_t pos;        // next word of this half's tile
-    uint32_t nwords;     // words in this half's tile
-    const uint16_t* words;
-    bool valid;          // this half has a tile
-    int half, l;         // half of the wave, lane within the half
+__device__ inline Tables stage_tables(const MatDesc& M, uint8_t* smem) {
+    const int n = M.prob_bits;
+    const size_t bytes = table_blob_bytes(M.n_tables, n);
+    const uint4* src = reinterpret_cast<const uint4*>(M.tables);
+    uint4* dst = reinterpret_cast<uint4*>(smem);
+    for (size_t i = threadIdx.x; i < bytes / 16; i += blockDim.x) dst[i] = src[i];
+    __syncthreads();
+    Tables T;
+    T.lut = smem;
+    T.fc = reinterpret_cast<const uint32_t*>(smem + ((size_t)M.n_tables << n));
+    T.val = reinterpret_cast<const int16_t*>(smem + ((size_t)M.n_tables << n) + (size_t)M.n_tables * 1024);
+    return T;
+}
+
+// ----------------------------------------------------------------------------- one half-wave tile
+struct Tile {
+    uint32_t x;            // rANS state of this lane
+    uint32_t pos;          // words consumed
+    uint32_t fill;         // words placed in the ring (multiple of 256)
+    uint32_t nwords;       // words of the tile (pad word included)
+    uint32_t ndw;          // the same in dwords
+    const uint32_t* gdw;   // the tile's words in global memory, as dwords
+    uint16_t* ring;        // this half's LDS ring
+    uint32_t pf[4];        // next chunk, loaded ahead
+    uint32_t below;        // lanes below this one within the half
+    uint32_t sh;           // 0 for the low half, 32 for the high half
+    int l;                 // lane within the half
+    bool valid;
     int err;
 };
 
-__device__ inline uint32_t half_mask(uint64_t m, int half) {
-    return half ? (uint32_t)(m >> 32) : (uint32_t)m;
+__device__ inline void load_chunk(Tile& t, uint32_t chunk, uint32_t* dst) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t d = chunk * kChunkDw + t.l + 32 * i;
+        dst[i] = (t.valid && d < t.ndw) ? t.gdw[d] : 0u;
+    }
+}
+__device__ inline void store_chunk(Tile& t, uint32_t chunk, const uint32_t* src) {
+    uint32_t* ring = reinterpret_cast<uint32_t*>(t.ring);
+    const uint32_t base = (chunk * kChunkDw) & (kRingWords / 2 - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ring[base + t.l + 32 * i] = src[i];
 }
 
-// Decode one symbol of table t; returns the table entry of the decoded symbol (with bit 63 of
-// nothing special: the escape symbol is reported through *sym_out).
-__device__ inline uint64_t rans_step(Lane& s, const Lds& L, int t, int n, uint32_t* sym_out) {
-    const uint32_t slot = s.x & ((1u << n) - 1u);
-    const uint32_t sy = L.lut[((uint32_t)t << n) + slot];
-    const uint64_t e = L.sym[t * 256 + sy];
-    const uint32_t fc = (uint32_t)e;
-    s.x = (fc & 0x1FFFu) * (s.x >> n) + slot - (fc >> 13);
-    *sym_out = sy;
-    return e;
+__device__ inline void begin_tile(const MatDesc& M, uint64_t tile, Tile& t) {
+    if (t.valid) {
+        const uint32_t a = M.index[tile], b = M.index[tile + 1];
+        const uint32_t* p = M.payload + a;
+        t.x = p[t.l];
+        t.gdw = p + 32;
+        t.ndw = b - a - 32;
+    } else {
+        t.x = kLow;
+        t.gdw = M.payload;
+        t.ndw = 0;
+    }
+    t.nwords = 2 * t.ndw;
+    t.pos = 0;
+    uint32_t first[16];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) load_chunk(t, k, first + 4 * k);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) store_chunk(t, k, first + 4 * k);
+    t.fill = kRingWords;
+    load_chunk(t, 4, t.pf);
+    __builtin_amdgcn_wave_barrier();
 }
 
-// Take the next word for every lane in `need`, compacted in ascending lane order per half.
-__device__ inline uint32_t take_words(Lane& s, bool need) {
-    const uint32_t m = half_mask(__ballot(need), s.half);
-    const uint32_t below = m & ((1u << s.l) - 1u);
+// Keep more than one row's worst-case consumption (9 x 64 words) in the ring.
+__device__ inline void top_up(Tile& t) {
+    while (t.fill < t.nwords && t.fill - t.pos <= kRingWords - 256) {
+        store_chunk(t, t.fill / 256, t.pf);
+        t.fill += 256;
+        if (t.fill < t.nwords) load_chunk(t, t.fill / 256, t.pf);
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Word for each lane in `need`, compacted in ascending lane order per half.
+__device__ inline uint32_t take_words(Tile& t, bool need) {
+    const uint64_t m = __ballot(need);
+    const uint32_t mine = (uint32_t)(m >> t.sh);
     uint32_t w = 0;
     if (need) {
-        const uint32_t idx = s.pos + __popc(below);
-        if (idx < s.nwords) w = s.words[idx];
-        else s.err |= kErrWords;
+        const uint32_t idx = t.pos + __popc(mine & t.below);
+        w = t.ring[idx & (kRingWords - 1)];
     }
-    s.pos += __popc(m);
+    t.pos += __popc(mine);
     return w;
 }
 
-__device__ inline void refill(Lane& s) {
-    const bool need = s.valid && s.x < kLow;
-    const uint32_t w = take_words(s, need);
-    if (need) s.x = (s.x << 16) | w;
+__device__ inline void refill(Tile& t) {
+    const bool need = t.x < kLow;
+    const uint32_t w = take_words(t, need);
+    if (need) t.x = (t.x << 16) | w;
 }
 
-__device__ inline void begin_tile(const DecodeParams& p, int64_t tile, Lane& s) {
-    if (s.valid) {
-        const uint32_t a = p.index[tile], b = p.index[tile + 1];
-        const uint32_t* t = p.payload + a;
-        s.x = t[s.l];
-        s.words = reinterpret_cast<const uint16_t*>(t + 32);
-        s.nwords = 2 * (b - a - 32);
-    } else {
-        s.x = kLow;
-        s.words = nullptr;
-        s.nwords = 0;
-    }
-    s.pos = 0;
+// One rANS decode step with table `tab`; returns the symbol.
+__device__ inline uint32_t rans_step(Tile& t, const Tables& T, uint32_t tab, int n) {
+    const uint32_t mask = (1u << n) - 1u;
+    const uint32_t slot = t.x & mask;
+    const uint32_t s = T.lut[(tab << n) | slot];
+    const uint32_t fc = T.fc[tab * 256 + s];
+    t.x = (fc & 0x1FFFu) * (t.x >> n) + slot - (fc >> 13);
+    return s;
 }
 
-__device__ inline void end_tile(Lane& s) {
-    if (!s.valid) return;
-    if (s.x != kLow) s.err |= kErrState;
-    // all words consumed, except possibly the one zero pad word
-    if (!(s.pos == s.nwords || (s.pos + 1 == s.nwords && s.words[s.pos] == 0))) s.err |= kErrWords;
+__device__ inline void end_tile(Tile& t) {
+    if (!t.valid) return;
+    if (t.x != kLow) t.err |= kErrState;
+    const bool exact = t.pos == t.nwords;
+    const bool pad = t.pos + 1 == t.nwords && (t.gdw[t.ndw - 1] >> 16) == 0;
+    if (!exact && !pad) t.err |= kErrWords;
+}
+
+__device__ inline void init_lane(Tile& t, uint8_t* ring_base) {
+    const int lane = threadIdx.x & 63;
+    t.l = lane & 31;
+    t.sh = (uint32_t)(lane & 32);
+    t.below = (1u << t.l) - 1u;
+    t.ring = reinterpret_cast<uint16_t*>(ring_base + ((threadIdx.x >> 6) * 2 + (lane >> 5)) * kRingBytes);
+    t.err = 0;
 }
 
 // ----------------------------------------------------------------------------- stores
 template <int CT>
-struct Store;
-
+struct Conv;
 template <>
-struct Store<CT_BF16> {
+struct Conv<CT_BF16> {
     using T = uint16_t;
-    __device__ static uint32_t conv(int32_t q, float alpha, float, uint32_t) { return bf16_rne((float)q * alpha); }
+    __device__ static uint32_t f(int32_t q, float alpha, float, uint32_t, uint32_t) { return bf16_rne((float)q * alpha); }
 };
 template <>
-struct Store<CT_F16> {
+struct Conv<CT_F16> {
     using T = uint16_t;
-    __device__ static uint32_t conv(int32_t q, float alpha, float, uint32_t) { return f16_rne((float)q * alpha); }
+    __device__ static uint32_t f(int32_t q, float alpha, float, uint32_t, uint32_t) { return f16_rne((float)q * alpha); }
 };
 template <>
-struct Store<CT_F8E4M3> {
+struct Conv<CT_F8E4M3> {
     using T = uint8_t;
-    __device__ static uint32_t conv(int32_t q, float, float h, uint32_t) { return e4m3_rne_sat((float)q * h); }
+    __device__ static uint32_t f(int32_t q, float, float h, uint32_t, uint32_t) { return e4m3_rne_sat((float)q * h); }
 };
 template <>
-struct Store<CT_I8> {
+struct Conv<CT_I8> {
     using T = uint8_t;
-    // round-half-away(q / k): floor((2|q| + k) / 2k) by a multiply with ceil(2^32 / 2k), exact
+    // round-half-away(q / k) = floor((2|q| + k) / 2k), by a multiply with ceil(2^32 / 2k); exact
     // because (2|q| + k) * 2k < 2^32.
-    __device__ static uint32_t conv(int32_t q, float, float, uint32_t kk) {
-        const uint32_t k = kk & 0xFFFFu, a = (uint32_t)(q < 0 ? -q : q);
-        const uint32_t D = 2u * k;
-        const uint32_t m = 0xFFFFFFFFu / D + 1u;
-        const uint32_t v = __umulhi(2u * a + k, m);
-        return (uint32_t)(uint8_t)(int8_t)(q < 0 ? -(int32_t)v : (int32_t)v);
+    __device__ static uint32_t f(int32_t q, float, float, uint32_t k, uint32_t magic) {
+        const uint32_t a = (uint32_t)(q < 0 ? -q : q);
+        const int32_t v = (int32_t)__umulhi(2u * a + k, magic);
+        return (uint32_t)(uint8_t)(int8_t)(q < 0 ? -v : v);
     }
 };
 template <>
-struct Store<CT_Q16> {
+struct Conv<CT_Q16> {
     using T = uint16_t;
-    __device__ static uint32_t conv(int32_t q, float, float, uint32_t) { return (uint32_t)(uint16_t)(int16_t)q; }
+    __device__ static uint32_t f(int32_t q, float, float, uint32_t, uint32_t) { return (uint32_t)(uint16_t)(int16_t)q; }
 };
 
 template <int CT>
-__device__ inline void store_block(const DecodeParams& p, int64_t row, int64_t col0, const int32_t* q, float alpha,
-                                   float h, uint32_t k) {
-    using T = typename Store<CT>::T;
-    T* out = static_cast<T*>(p.out) + row * p.cols;
+__device__ inline void store_block(const MatDesc& M, uint32_t row, uint32_t col0, const int32_t* q, float alpha,
+                                   float h, uint32_t k, uint32_t magic) {
+    using T = typename Conv<CT>::T;
+    T* out = static_cast<T*>(M.out) + (size_t)row * M.cols;
     uint32_t v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = Store<CT>::conv(q[j], alpha, h, k);
-    if (col0 + 8 <= p.cols && (p.cols & 7) == 0) {
+    for (int j = 0; j < 8; ++j) v[j] = Conv<CT>::f(q[j], alpha, h, k, magic);
+    if (col0 + 8 <= M.cols && (M.cols & 7) == 0) {
         if constexpr (sizeof(T) == 2) {
-            uint4 pk = make_uint4(v[0] | v[1] << 16, v[2] | v[3] << 16, v[4] | v[5] << 16, v[6] | v[7] << 16);
-            *reinterpret_cast<uint4*>(out + col0) = pk;
+            *reinterpret_cast<uint4*>(out + col0) =
+                make_uint4(v[0] | v[1] << 16, v[2] | v[3] << 16, v[4] | v[5] << 16, v[6] | v[7] << 16);
         } else {
-            uint2 pk = make_uint2(v[0] | v[1] << 8 | v[2] << 16 | v[3] << 24, v[4] | v[5] << 8 | v[6] << 16 | v[7] << 24);
-            *reinterpret_cast<uint2*>(out + col0) = pk;
+            *reinterpret_cast<uint2*>(out + col0) =
+                make_uint2(v[0] | v[1] << 8 | v[2] << 16 | v[3] << 24, v[4] | v[5] << 8 | v[6] << 16 | v[7] << 24);
         }
     } else {
         for (int j = 0; j < 8; ++j)
-            if (col0 + j < p.cols) out[col0 + j] = (T)v[j];
+            if (col0 + j < M.cols) out[col0 + j] = (T)v[j];
     }
 }
 
 // ----------------------------------------------------------------------------- lossy kernel
 template <int CT>
-__global__ __launch_bounds__(64 * kWavesPerBlock) void decode_lossy_kernel(DecodeParams p) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    Lds L;
-    stage_tables(p, smem, &L);
-    const int n = p.prob_bits;
-    const float h = p.step * 0.5f;
-    Lane s;
-    s.half = (threadIdx.x >> 5) & 1;
-    s.l = threadIdx.x & 31;
-    s.err = 0;
-    const int64_t wave0 = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    const int64_t wstride = (int64_t)gridDim.x * kWavesPerBlock;
-    for (int64_t pair = wave0; pair < p.n_pairs; pair += wstride) {
-        const int64_t tr = pair / p.pairs_c;
-        const int64_t tc = 2 * (pair % p.pairs_c) + s.half;
-        s.valid = tc < p.tiles_c;
-        begin_tile(p, tr * p.tiles_c + tc, s);
-        for (int rr = 0; rr < p.tile_rows; ++rr) {
-            uint32_t sy;
-            const uint64_t e0 = rans_step(s, L, 0, n, &sy);
-            refill(s);
-            const int b = (int)(e0 >> 32);
+__device__ void lossy_pairs(const MatDesc& M, const Tables& T, Tile& t, uint64_t pair0, uint64_t pair1) {
+    const int n = M.prob_bits;
+    const float h = M.step * 0.5f;
+    const uint32_t wave = threadIdx.x >> 6;
+    for (uint64_t pair = pair0 + wave; pair < pair1; pair += kWaves) {
+        const uint32_t tr = (uint32_t)(pair / M.pairs_c);
+        const uint32_t tc = 2 * (uint32_t)(pair % M.pairs_c) + (t.sh ? 1u : 0u);
+        t.valid = tc < M.tiles_c;
+        begin_tile(M, (uint64_t)tr * M.tiles_c + tc, t);
+        const uint32_t row0 = tr * M.tile_rows;
+        // row scale (and row max |q| for INT8) of the tile's rows, one per lane, read back per row
+        const uint32_t my_row = row0 + t.l;
+        const float sc_l = (t.l < M.tile_rows && my_row < M.rows) ? M.row_scale[my_row] : 0.0f;
+        uint32_t qm_l = 0;
+        if constexpr (CT == CT_I8) qm_l = (t.l < M.tile_rows && my_row < M.rows) ? M.row_qmax[my_row] : 0u;
+        for (int rr = 0; rr < M.tile_rows; ++rr) {
+            top_up(t);
+            const uint32_t s0 = rans_step(t, T, 0, n);
+            refill(t);
+            const int b = T.val[s0];
             int32_t q[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const uint64_t e = rans_step(s, L, 1 + 2 * j + b, n, &sy);
-                q[j] = (int32_t)(e >> 32);
-                refill(s);
-                const bool esc = s.valid && sy == 255u;
+                const uint32_t tab = 1 + 2 * j + b;
+                const uint32_t s = rans_step(t, T, tab, n);
+                refill(t);
+                q[j] = T.val[tab * 256 + s];
+                const bool esc = s == 255u;
                 if (__ballot(esc)) {
-                    const uint32_t w = take_words(s, esc);
+                    const uint32_t w = take_words(t, esc);
                     if (esc) q[j] = 2 * (int32_t)(int16_t)w + b;
                 }
             }
-            const int64_t row = tr * p.tile_rows + rr;
-            if (row < p.rows && s.valid) {
-                const float sc = p.row_scale[row];
+            const uint32_t row = row0 + rr;
+            const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_l), rr));
+            if (row < M.rows && t.valid) {
                 const float alpha = h * sc;
-                uint32_t k = 1;
+                uint32_t k = 1, magic = 0;
                 if constexpr (CT == CT_I8) {
-                    const uint32_t qm = p.row_qmax[row];
+                    const uint32_t qm = (uint32_t)__builtin_amdgcn_readlane((int)qm_l, rr);
                     k = qm > 127u ? (qm + 126u) / 127u : 1u;
+                    magic = 0xFFFFFFFFu / (2u * k) + 1u;
                 }
-                const int64_t col0 = tc * 256 + 8 * s.l;
-                if (col0 < p.cols) store_block<CT>(p, row, col0, q, alpha, h, k);
+                const uint32_t col0 = tc * 256 + 8 * t.l;
+                if (col0 < M.cols) store_block<CT>(M, row, col0, q, alpha, h, k, magic);
                 if constexpr (CT == CT_F8E4M3 || CT == CT_I8) {
-                    if (tc == 0 && s.l == 0) p.scale_out[row] = CT == CT_F8E4M3 ? sc : alpha * (float)k;
+                    if (tc == 0 && t.l == 0) M.scale_out[row] = CT == CT_F8E4M3 ? sc : alpha * (float)k;
                 }
             }
         }
-        end_tile(s);
+        end_tile(t);
     }
-    if (s.err) atomicOr(p.err, s.err);
+}
+
+__global__ __launch_bounds__(64 * kWaves) void decode_lossy_group(GroupArgs g) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    int bim;
+    const MatDesc& M = my_matrix(g, &bim);
+    const Tables T = stage_tables(M, smem);
+    Tile t;
+    init_lane(t, smem + table_blob_bytes(M.n_tables, M.prob_bits));
+    const uint64_t n_pairs = (uint64_t)((M.rows + M.tile_rows - 1) / M.tile_rows) * M.pairs_c;
+    const uint64_t pair0 = (uint64_t)bim * g.pairs_per_block;
+    const uint64_t pair1 = std::min<uint64_t>(pair0 + g.pairs_per_block, n_pairs);
+    switch (M.container) {
+        case CT_BF16: lossy_pairs<CT_BF16>(M, T, t, pair0, pair1); break;
+        case CT_F16: lossy_pairs<CT_F16>(M, T, t, pair0, pair1); break;
+        case CT_F8E4M3: lossy_pairs<CT_F8E4M3>(M, T, t, pair0, pair1); break;
+        case CT_I8: lossy_pairs<CT_I8>(M, T, t, pair0, pair1); break;
+        default: lossy_pairs<CT_Q16>(M, T, t, pair0, pair1); break;
+    }
+    if (t.err) atomicOr(M.err, t.err);
 }
 
 // ----------------------------------------------------------------------------- lossless kernel
 template <int P>
-__global__ __launch_bounds__(64 * kWavesPerBlock) void decode_lossless_kernel(DecodeParams p) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    Lds L;
-    stage_tables(p, smem, &L);
-    const int n = p.prob_bits;
-    Lane s;
-    s.half = (threadIdx.x >> 5) & 1;
-    s.l = threadIdx.x & 31;
-    s.err = 0;
-    const int64_t wave0 = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    const int64_t wstride = (int64_t)gridDim.x * kWavesPerBlock;
-    for (int64_t pair = wave0; pair < p.n_pairs; pair += wstride) {
-        const int64_t tr = pair / p.pairs_c;
-        const int64_t tc = 2 * (pair % p.pairs_c) + s.half;
-        s.valid = tc < p.tiles_c;
-        begin_tile(p, tr * p.tiles_c + tc, s);
-        for (int rr = 0; rr < p.tile_rows; ++rr) {
+__device__ void lossless_pairs(const MatDesc& M, const Tables& T, Tile& t, uint64_t pair0, uint64_t pair1) {
+    const int n = M.prob_bits;
+    const uint32_t wave = threadIdx.x >> 6;
+    using E = typename std::conditional<P == 1, uint8_t, typename std::conditional<P == 2, uint16_t, uint32_t>::type>::type;
+    for (uint64_t pair = pair0 + wave; pair < pair1; pair += kWaves) {
+        const uint32_t tr = (uint32_t)(pair / M.pairs_c);
+        const uint32_t tc = 2 * (uint32_t)(pair % M.pairs_c) + (t.sh ? 1u : 0u);
+        t.valid = tc < M.tiles_c;
+        begin_tile(M, (uint64_t)tr * M.tiles_c + tc, t);
+        for (int rr = 0; rr < M.tile_rows; ++rr) {
             uint32_t v[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
+                top_up(t);                  // an element is at most 4 steps x 32 words
                 uint32_t acc = 0;
 #pragma unroll
                 for (int pl = 0; pl < P; ++pl) {
-                    uint32_t sy;
-                    rans_step(s, L, pl, n, &sy);
-                    refill(s);
-                    acc = acc << 8 | sy;
+                    const uint32_t s = rans_step(t, T, pl, n);
+                    refill(t);
+                    acc = acc << 8 | s;
                 }
                 v[e] = acc;
             }
-            const int64_t row = tr * p.tile_rows + rr;
-            const int64_t col0 = tc * 256 + 8 * s.l;
-            if (row < p.rows && s.valid && col0 < p.cols) {
-                if constexpr (P == 2) {
-                    uint16_t* out = static_cast<uint16_t*>(p.out) + row * p.cols;
-                    if (col0 + 8 <= p.cols && (p.cols & 7) == 0)
+            const uint32_t row = tr * M.tile_rows + rr;
+            const uint32_t col0 = tc * 256 + 8 * t.l;
+            if (row < M.rows && t.valid && col0 < M.cols) {
+                E* out = static_cast<E*>(M.out) + (size_t)row * M.cols;
+                if (col0 + 8 <= M.cols && (M.cols & 7) == 0) {
+                    if constexpr (P == 2) {
                         *reinterpret_cast<uint4*>(out + col0) =
                             make_uint4(v[0] | v[1] << 16, v[2] | v[3] << 16, v[4] | v[5] << 16, v[6] | v[7] << 16);
-                    else
-                        for (int j = 0; j < 8; ++j)
-                            if (col0 + j < p.cols) out[col0 + j] = (uint16_t)v[j];
-                } else if constexpr (P == 1) {
-                    uint8_t* out = static_cast<uint8_t*>(p.out) + row * p.cols;
-                    if (col0 + 8 <= p.cols && (p.cols & 7) == 0)
-                        *reinterpret_cast<uint2*>(out + col0) =
-                            make_uint2(v[0] | v[1] << 8 | v[2] << 16 | v[3] << 24, v[4] | v[5] << 8 | v[6] << 16 | v[7] << 24);
-                    else
-                        for (int j = 0; j < 8; ++j)
-                            if (col0 + j < p.cols) out[col0 + j] = (uint8_t)v[j];
-                } else {
-                    uint32_t* out = static_cast<uint32_t*>(p.out) + row * p.cols;
-                    if (col0 + 8 <= p.cols && (p.cols & 7) == 0) {
+                    } else if constexpr (P == 1) {
+                        *reinterpret_cast<uint2*>(out + col0) = make_uint2(v[0] | v[1] << 8 | v[2] << 16 | v[3] << 24,
+                                                                           v[4] | v[5] << 8 | v[6] << 16 | v[7] << 24);
+                    } else {
                         *reinterpret_cast<uint4*>(out + col0) = make_uint4(v[0], v[1], v[2], v[3]);
                         *reinterpret_cast<uint4*>(out + col0 + 4) = make_uint4(v[4], v[5], v[6], v[7]);
-                    } else {
-                        for (int j = 0; j < 8; ++j)
-                            if (col0 + j < p.cols) out[col0 + j] = v[j];
                     }
+                } else {
+                    for (int j = 0; j < 8; ++j)
+                        if (col0 + j < M.cols) out[col0 + j] = (E)v[j];
                 }
             }
         }
-        end_tile(s);
+        end_tile(t);
     }
-    if (s.err) atomicOr(p.err, s.err);
+}
+
+__global__ __launch_bounds__(64 * kWaves) void decode_lossless_group(GroupArgs g) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    int bim;
+    const MatDesc& M = my_matrix(g, &bim);
+    const Tables T = stage_tables(M, smem);
+    Tile t;
+    init_lane(t, smem + table_blob_bytes(M.n_tables, M.prob_bits));
+    const uint64_t n_pairs = (uint64_t)((M.rows + M.tile_rows - 1) / M.tile_rows) * M.pairs_c;
+    const uint64_t pair0 = (uint64_t)bim * g.pairs_per_block;
+    const uint64_t pair1 = std::min<uint64_t>(pair0 + g.pairs_per_block, n_pairs);
+    switch (M.n_tables) {
+        case 1: lossless_pairs<1>(M, T, t, pair0, pair1); break;
+        case 2: lossless_pairs<2>(M, T, t, pair0, pair1); break;
+        default: lossless_pairs<4>(M, T, t, pair0, pair1); break;
+    }
+    if (t.err) atomicOr(M.err, t.err);
 }
 
 int device_cus() {
@@ -350,7 +426,7 @@ int device_cus() {
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
     if (!cache[dev]) {
         int v = 0;
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) v = 0;
         cache[dev] = v > 0 ? v : 256;
     }
     return cache[dev];
@@ -367,39 +443,43 @@ hipError_t allow_lds(const void* kernel) {
     return e;
 }
 
-template <class K>
-hipError_t launch(K kernel, const DecodeParams& p, hipStream_t stream) {
-    const size_t lds = table_blob_bytes(p.n_tables, p.prob_bits);
-    hipError_t e = allow_lds(reinterpret_cast<const void*>(kernel));
-    if (e != hipSuccess) return e;
-    const int per_cu = std::max<int>(1, std::min<int>(2, (int)((160 * 1024) / lds)));
-    int64_t blocks = (p.n_pairs + kWavesPerBlock - 1) / kWavesPerBlock;
-    blocks = std::min<int64_t>(blocks, (int64_t)device_cus() * per_cu);
-    if (blocks < 1) return hipSuccess;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(64 * kWavesPerBlock), lds, stream, p);
-    return hipGetLastError();
-}
-
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int container, hipStream_t stream) {
-    if (p.n_pairs == 0) return hipSuccess;
-    if (p.mode == 0) {
-        switch (container) {
-            case CT_BF16: return launch(decode_lossy_kernel<CT_BF16>, p, stream);
-            case CT_F16: return launch(decode_lossy_kernel<CT_F16>, p, stream);
-            case CT_F8E4M3: return launch(decode_lossy_kernel<CT_F8E4M3>, p, stream);
-            case CT_I8: return launch(decode_lossy_kernel<CT_I8>, p, stream);
-            case CT_Q16: return launch(decode_lossy_kernel<CT_Q16>, p, stream);
-            default: return hipErrorInvalidValue;
-        }
+hipError_t launch_group(const MatDesc* mats, int count, int mode, hipStream_t stream) {
+    if (count <= 0) return hipSuccess;
+    if (count > kMaxGroup) return hipErrorInvalidValue;
+    GroupArgs g{};
+    g.count = count;
+    uint64_t total_pairs = 0;
+    size_t lds = 0;
+    for (int i = 0; i < count; ++i) {
+        g.m[i] = mats[i];
+        total_pairs += (uint64_t)((mats[i].rows + mats[i].tile_rows - 1) / mats[i].tile_rows) * mats[i].pairs_c;
+        lds = std::max(lds, table_blob_bytes(mats[i].n_tables, mats[i].prob_bits) + (size_t)kWaves * 2 * kRingBytes);
     }
-    switch (p.n_tables) {
-        case 1: return launch(decode_lossless_kernel<1>, p, stream);
-        case 2: return launch(decode_lossless_kernel<2>, p, stream);
-        case 4: return launch(decode_lossless_kernel<4>, p, stream);
-        default: return hipErrorInvalidValue;
+    if (total_pairs == 0) return hipSuccess;
+    // about four blocks per CU over the launch, at least one pair per wave
+    const uint64_t target_blocks = 4ull * device_cus();
+    uint64_t ppb = (total_pairs + target_blocks - 1) / target_blocks;
+    ppb = std::max<uint64_t>(kWaves, (ppb + kWaves - 1) / kWaves * kWaves);
+    g.pairs_per_block = (int32_t)std::min<uint64_t>(ppb, 1u << 20);
+    int32_t blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        g.block_start[i] = blocks;
+        const uint64_t pairs = (uint64_t)((mats[i].rows + mats[i].tile_rows - 1) / mats[i].tile_rows) * mats[i].pairs_c;
+        blocks += (int32_t)((pairs + g.pairs_per_block - 1) / g.pairs_per_block);
     }
+    g.block_start[count] = blocks;
+    if (blocks == 0) return hipSuccess;
+    const void* k = mode == 0 ? reinterpret_cast<const void*>(decode_lossy_group)
+                              : reinterpret_cast<const void*>(decode_lossless_group);
+    hipError_t e = allow_lds(k);
+    if (e != hipSuccess) return e;
+    if (mode == 0)
+        hipLaunchKernelGGL(decode_lossy_group, dim3(blocks), dim3(64 * kWaves), lds, stream, g);
+    else
+        hipLaunchKernelGGL(decode_lossless_group, dim3(blocks), dim3(64 * kWaves), lds, stream, g);
+    return hipGetLastError();
 }
 
 }  // namespace ep

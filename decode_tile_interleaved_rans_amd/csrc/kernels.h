@@ -10,26 +10,39 @@ namespace ep {
 // container codes (the first four equal the ep_dtype values)
 enum Container : int { CT_BF16 = 1, CT_F16 = 2, CT_F8E4M3 = 3, CT_I8 = 4, CT_Q16 = 100 };
 
-// Everything a decode kernel needs about one uploaded matrix and one output.
-struct DecodeParams {
+constexpr int kMaxGroup = 32;        // matrices per grouped launch (kernel-argument space)
+
+// One matrix of a grouped decode launch: the uploaded stream and its output.
+struct MatDesc {
     const uint32_t* payload;    // tile payload, 4-byte units
     const uint32_t* index;      // [n_tiles + 1] tile offsets into payload
     const float* row_scale;     // [rows] (lossy)
     const uint16_t* row_qmax;   // [rows] (lossy)
-    const uint8_t* tables;      // lut [n_tables][2^n] u8, then sym [n_tables][256] u64
-    int mode, n_tables, prob_bits, tile_rows;
-    int64_t rows, cols, tiles_c, pairs_c, n_pairs;
-    float step;
+    const uint8_t* tables;      // decode tables (see table_blob_bytes)
     void* out;                  // [rows][cols] container elements
-    float* scale_out;           // [rows] for FP8 / INT8
-    int* err;                   // device error flag (bit 0: words, bit 1: final state)
+    float* scale_out;           // [rows] for FP8 / INT8, else unused
+    int* err;                   // device error flag (bit 0: word count, bit 1: final state)
+    uint32_t rows, cols, tiles_c, pairs_c;
+    float step;
+    uint8_t prob_bits, tile_rows, container, n_tables;
 };
 
-// Size in bytes of the device table blob for a stream (lut + sym), a multiple of 16.
-inline size_t table_blob_bytes(int n_tables, int prob_bits) {
-    return ((size_t)n_tables << prob_bits) + (size_t)n_tables * 256 * 8;
+struct GroupArgs {
+    int32_t count;              // matrices in this launch (<= kMaxGroup)
+    int32_t pairs_per_block;    // tile pairs handled by one block
+    int32_t block_start[kMaxGroup + 1];
+    MatDesc m[kMaxGroup];
+};
+
+// Decode tables of one stream, in device memory and in LDS:
+//   lut [n_tables][2^n] u8   slot -> symbol
+//   fc  [n_tables][256] u32  f | c << 13 (frequency, cumulative frequency)
+//   val [n_tables][256] i16  doubled lattice coordinate 2 (lo + s) + b (lossy), coset (table 0)
+__host__ __device__ inline size_t table_blob_bytes(int n_tables, int prob_bits) {
+    return ((size_t)n_tables << prob_bits) + (size_t)n_tables * 256 * 4 + (size_t)n_tables * 256 * 2;
 }
 
-hipError_t launch_decode(const DecodeParams& p, int container, hipStream_t stream);
+// Launch one grouped decode (all matrices of the same mode: 0 lossy, 1 lossless).
+hipError_t launch_group(const MatDesc* mats, int count, int mode, hipStream_t stream);
 
 }  // namespace ep
