@@ -46,23 +46,27 @@ constexpr int kErrWords = 1;               // words ran out or were left over
 constexpr int kErrState = 2;               // a final state differs from 2^16
 
 // ----------------------------------------------------------------------------- containers
-__device__ inline uint32_t bf16_rne(float v) {
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t bf16_rne(float v) {
     uint32_t u = __float_as_uint(v);
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;      // finite inputs only
 }
 // The fp32 product is rounded first and then converted: without the register barrier the
 // backend folds "multiply then narrow" into one mixed-precision FMA that rounds only once,
 // which differs from the two-step rounding in rare ties.
-__device__ inline float materialize(float v) {
+__device__ __forceinline__ float materialize(float v) {
     asm volatile("" : "+v"(v));
     return v;
 }
-__device__ inline uint32_t f16_rne(float v) {
+__device__ __forceinline__ uint32_t f16_rne(float v) {
     _Float16 h = (_Float16)materialize(v);               // v_cvt_f16_f32: round to nearest even
     return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 // OCP E4M3FN, round to nearest even, saturating at +-448.
-__device__ inline uint32_t e4m3_rne_sat(float v) {
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
     uint32_t u = __float_as_uint(v);
     uint32_t sign = (u >> 24) & 0x80u;
     u &= 0x7FFFFFFFu;
@@ -87,14 +91,14 @@ struct Tables {
     const int16_t* val;
 };
 
-__device__ inline const MatDesc& my_matrix(const GroupArgs& g, int* block_in_matrix) {
+__device__ __forceinline__ MatDesc my_matrix(const GroupArgs& g, int* block_in_matrix) {
     int mi = 0;
     while (mi + 1 < g.count && (int)blockIdx.x >= g.block_start[mi + 1]) ++mi;
     *block_in_matrix = (int)blockIdx.x - g.block_start[mi];
     return g.m[mi];
 }
 
-__device__ inline Tables stage_tables(const MatDesc& M, uint8_t* smem) {
+__device__ __forceinline__ Tables stage_tables(const MatDesc& M, uint8_t* smem) {
     const int n = M.prob_bits;
     const size_t bytes = table_blob_bytes(M.n_tables, n);
     const uint4* src = reinterpret_cast<const uint4*>(M.tables);
@@ -125,21 +129,21 @@ struct Tile {
     int err;
 };
 
-__device__ inline void load_chunk(Tile& t, uint32_t chunk, uint32_t* dst) {
+__device__ __forceinline__ void load_chunk(Tile& t, uint32_t chunk, uint32_t* dst) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t d = chunk * kChunkDw + t.l + 32 * i;
         dst[i] = (t.valid && d < t.ndw) ? t.gdw[d] : 0u;
     }
 }
-__device__ inline void store_chunk(Tile& t, uint32_t chunk, const uint32_t* src) {
+__device__ __forceinline__ void store_chunk(Tile& t, uint32_t chunk, const uint32_t* src) {
     uint32_t* ring = reinterpret_cast<uint32_t*>(t.ring);
     const uint32_t base = (chunk * kChunkDw) & (kRingWords / 2 - 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i) ring[base + t.l + 32 * i] = src[i];
 }
 
-__device__ inline void begin_tile(const MatDesc& M, uint64_t tile, Tile& t) {
+__device__ __forceinline__ void begin_tile(const MatDesc& M, uint64_t tile, Tile& t) {
     if (t.valid) {
         const uint32_t a = M.index[tile], b = M.index[tile + 1];
         const uint32_t* p = M.payload + a;
@@ -164,7 +168,7 @@ __device__ inline void begin_tile(const MatDesc& M, uint64_t tile, Tile& t) {
 }
 
 // Keep more than one row's worst-case consumption (9 x 64 words) in the ring.
-__device__ inline void top_up(Tile& t) {
+__device__ __forceinline__ void top_up(Tile& t) {
     while (t.fill < t.nwords && t.fill - t.pos <= kRingWords - 256) {
         store_chunk(t, t.fill / 256, t.pf);
         t.fill += 256;
@@ -173,36 +177,46 @@ __device__ inline void top_up(Tile& t) {
     __builtin_amdgcn_wave_barrier();
 }
 
-// Word for each lane in `need`, compacted in ascending lane order per half.
-__device__ inline uint32_t take_words(Tile& t, bool need) {
+// Word for each lane in `need`, compacted in ascending lane order per half. Branch-free: every
+// lane reads the ring (always in range) and the caller keeps the word only where it was needed.
+__device__ __forceinline__ uint32_t take_words(Tile& t, bool need) {
     const uint64_t m = __ballot(need);
     const uint32_t mine = (uint32_t)(m >> t.sh);
-    uint32_t w = 0;
-    if (need) {
-        const uint32_t idx = t.pos + __popc(mine & t.below);
-        w = t.ring[idx & (kRingWords - 1)];
-    }
+    const uint32_t idx = t.pos + __popc(mine & t.below);
+    const uint32_t w = t.ring[idx & (kRingWords - 1)];
     t.pos += __popc(mine);
     return w;
 }
 
-__device__ inline void refill(Tile& t) {
+__device__ __forceinline__ void refill(Tile& t) {
     const bool need = t.x < kLow;
     const uint32_t w = take_words(t, need);
-    if (need) t.x = (t.x << 16) | w;
+    t.x = need ? (t.x << 16) | w : t.x;
 }
 
-// One rANS decode step with table `tab`; returns the symbol.
-__device__ inline uint32_t rans_step(Tile& t, const Tables& T, uint32_t tab, int n) {
-    const uint32_t mask = (1u << n) - 1u;
-    const uint32_t slot = t.x & mask;
-    const uint32_t s = T.lut[(tab << n) | slot];
-    const uint32_t fc = T.fc[tab * 256 + s];
-    t.x = (fc & 0x1FFFu) * (t.x >> n) + slot - (fc >> 13);
+// One rANS decode step: lut/fc are the LUT and frequency table of the step's table; returns the
+// symbol. f <= 2^12 and x >> N < 2^22 fit the 24-bit multiplier.
+template <int N>
+__device__ __forceinline__ uint32_t rans_step(Tile& t, const uint8_t* lut, const uint32_t* fc) {
+    const uint32_t slot = t.x & ((1u << N) - 1u);
+    const uint32_t s = lut[slot];
+    const uint32_t e = fc[s];
+    t.x = __umul24(e & 0x1FFFu, t.x >> N) + slot - (e >> 13);
     return s;
 }
 
-__device__ inline void end_tile(Tile& t) {
+// The coset table has at most two symbols (0 and 1, cumulative 0 and f0), decoded arithmetically.
+template <int N>
+__device__ __forceinline__ uint32_t coset_step(Tile& t, uint32_t f0, uint32_t f1) {
+    const uint32_t slot = t.x & ((1u << N) - 1u);
+    const bool one = slot >= f0;
+    const uint32_t f = one ? f1 : f0;
+    const uint32_t c = one ? f0 : 0u;
+    t.x = __umul24(f, t.x >> N) + slot - c;
+    return one ? 1u : 0u;
+}
+
+__device__ __forceinline__ void end_tile(Tile& t) {
     if (!t.valid) return;
     if (t.x != kLow) t.err |= kErrState;
     const bool exact = t.pos == t.nwords;
@@ -210,7 +224,7 @@ __device__ inline void end_tile(Tile& t) {
     if (!exact && !pad) t.err |= kErrWords;
 }
 
-__device__ inline void init_lane(Tile& t, uint8_t* ring_base) {
+__device__ __forceinline__ void init_lane(Tile& t, uint8_t* ring_base) {
     const int lane = threadIdx.x & 63;
     t.l = lane & 31;
     t.sh = (uint32_t)(lane & 32);
@@ -255,13 +269,26 @@ struct Conv<CT_Q16> {
 };
 
 template <int CT>
-__device__ inline void store_block(const MatDesc& M, uint32_t row, uint32_t col0, const int32_t* q, float alpha,
+__device__ __forceinline__ void store_block(const MatDesc& M, uint32_t row, uint32_t col0, const int32_t* q, float alpha,
                                    float h, uint32_t k, uint32_t magic) {
     using T = typename Conv<CT>::T;
     T* out = static_cast<T*>(M.out) + (size_t)row * M.cols;
     uint32_t v[8];
+    if constexpr (CT == CT_BF16 || CT == CT_F16) {
+        // two values per v_cvt_pk_{bf16,f16}_f32 (round to nearest even) of the rounded fp32 products
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = Conv<CT>::f(q[j], alpha, h, k, magic);
+        for (int j = 0; j < 8; j += 2) {
+            f32x2 p = {materialize((float)q[j] * alpha), materialize((float)q[j + 1] * alpha)};
+            uint32_t pk;
+            if constexpr (CT == CT_BF16) pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+            else pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, f16x2));
+            v[j] = pk & 0xFFFFu;
+            v[j + 1] = pk >> 16;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = Conv<CT>::f(q[j], alpha, h, k, magic);
+    }
     if (col0 + 8 <= M.cols && (M.cols & 7) == 0) {
         if constexpr (sizeof(T) == 2) {
             *reinterpret_cast<uint4*>(out + col0) =
@@ -277,11 +304,12 @@ __device__ inline void store_block(const MatDesc& M, uint32_t row, uint32_t col0
 }
 
 // ----------------------------------------------------------------------------- lossy kernel
-template <int CT>
-__device__ void lossy_pairs(const MatDesc& M, const Tables& T, Tile& t, uint64_t pair0, uint64_t pair1) {
-    const int n = M.prob_bits;
+template <int CT, int N>
+__device__ __forceinline__ void lossy_pairs(const MatDesc& M, const Tables& T, Tile& t, uint64_t pair0, uint64_t pair1) {
     const float h = M.step * 0.5f;
     const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t f0 = T.fc[0] & 0x1FFFu, f1 = T.fc[1] & 0x1FFFu;    // coset table
+    const int lo0 = T.val[0];
     for (uint64_t pair = pair0 + wave; pair < pair1; pair += kWaves) {
         const uint32_t tr = (uint32_t)(pair / M.pairs_c);
         const uint32_t tc = 2 * (uint32_t)(pair % M.pairs_c) + (t.sh ? 1u : 0u);
@@ -295,16 +323,18 @@ __device__ void lossy_pairs(const MatDesc& M, const Tables& T, Tile& t, uint64_t
         if constexpr (CT == CT_I8) qm_l = (t.l < M.tile_rows && my_row < M.rows) ? M.row_qmax[my_row] : 0u;
         for (int rr = 0; rr < M.tile_rows; ++rr) {
             top_up(t);
-            const uint32_t s0 = rans_step(t, T, 0, n);
+            const int b = lo0 + (int)coset_step<N>(t, f0, f1);
             refill(t);
-            const int b = T.val[s0];
+            // tables 1 + 2j + b for this lane's coset; j selects a compile-time offset
+            const uint8_t* lut_b = T.lut + ((1 + b) << N);
+            const uint32_t* fc_b = T.fc + (1 + b) * 256;
+            const int16_t* val_b = T.val + (1 + b) * 256;
             int32_t q[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const uint32_t tab = 1 + 2 * j + b;
-                const uint32_t s = rans_step(t, T, tab, n);
+                const uint32_t s = rans_step<N>(t, lut_b + ((2 * j) << N), fc_b + 2 * j * 256);
                 refill(t);
-                q[j] = T.val[tab * 256 + s];
+                q[j] = val_b[2 * j * 256 + s];
                 const bool esc = s == 255u;
                 if (__ballot(esc)) {
                     const uint32_t w = take_words(t, esc);
@@ -332,30 +362,38 @@ __device__ void lossy_pairs(const MatDesc& M, const Tables& T, Tile& t, uint64_t
     }
 }
 
+template <int N>
+__device__ __forceinline__ void lossy_dispatch(const MatDesc& M, const Tables& T, Tile& t, uint64_t pair0, uint64_t pair1) {
+    switch (M.container) {
+        case CT_BF16: lossy_pairs<CT_BF16, N>(M, T, t, pair0, pair1); break;
+        case CT_F16: lossy_pairs<CT_F16, N>(M, T, t, pair0, pair1); break;
+        case CT_F8E4M3: lossy_pairs<CT_F8E4M3, N>(M, T, t, pair0, pair1); break;
+        case CT_I8: lossy_pairs<CT_I8, N>(M, T, t, pair0, pair1); break;
+        default: lossy_pairs<CT_Q16, N>(M, T, t, pair0, pair1); break;
+    }
+}
+
 __global__ __launch_bounds__(64 * kWaves) void decode_lossy_group(GroupArgs g) {
     extern __shared__ __align__(16) uint8_t smem[];
     int bim;
-    const MatDesc& M = my_matrix(g, &bim);
+    const MatDesc M = my_matrix(g, &bim);
     const Tables T = stage_tables(M, smem);
     Tile t;
     init_lane(t, smem + table_blob_bytes(M.n_tables, M.prob_bits));
     const uint64_t n_pairs = (uint64_t)((M.rows + M.tile_rows - 1) / M.tile_rows) * M.pairs_c;
     const uint64_t pair0 = (uint64_t)bim * g.pairs_per_block;
     const uint64_t pair1 = std::min<uint64_t>(pair0 + g.pairs_per_block, n_pairs);
-    switch (M.container) {
-        case CT_BF16: lossy_pairs<CT_BF16>(M, T, t, pair0, pair1); break;
-        case CT_F16: lossy_pairs<CT_F16>(M, T, t, pair0, pair1); break;
-        case CT_F8E4M3: lossy_pairs<CT_F8E4M3>(M, T, t, pair0, pair1); break;
-        case CT_I8: lossy_pairs<CT_I8>(M, T, t, pair0, pair1); break;
-        default: lossy_pairs<CT_Q16>(M, T, t, pair0, pair1); break;
+    switch (M.prob_bits) {
+        case 10: lossy_dispatch<10>(M, T, t, pair0, pair1); break;
+        case 11: lossy_dispatch<11>(M, T, t, pair0, pair1); break;
+        default: lossy_dispatch<12>(M, T, t, pair0, pair1); break;
     }
     if (t.err) atomicOr(M.err, t.err);
 }
 
 // ----------------------------------------------------------------------------- lossless kernel
-template <int P>
-__device__ void lossless_pairs(const MatDesc& M, const Tables& T, Tile& t, uint64_t pair0, uint64_t pair1) {
-    const int n = M.prob_bits;
+template <int P, int N>
+__device__ __forceinline__ void lossless_pairs(const MatDesc& M, const Tables& T, Tile& t, uint64_t pair0, uint64_t pair1) {
     const uint32_t wave = threadIdx.x >> 6;
     using E = typename std::conditional<P == 1, uint8_t, typename std::conditional<P == 2, uint16_t, uint32_t>::type>::type;
     for (uint64_t pair = pair0 + wave; pair < pair1; pair += kWaves) {
@@ -371,7 +409,7 @@ __device__ void lossless_pairs(const MatDesc& M, const Tables& T, Tile& t, uint6
                 uint32_t acc = 0;
 #pragma unroll
                 for (int pl = 0; pl < P; ++pl) {
-                    const uint32_t s = rans_step(t, T, pl, n);
+                    const uint32_t s = rans_step<N>(t, T.lut + (pl << N), T.fc + pl * 256);
                     refill(t);
                     acc = acc << 8 | s;
                 }
@@ -405,17 +443,23 @@ __device__ void lossless_pairs(const MatDesc& M, const Tables& T, Tile& t, uint6
 __global__ __launch_bounds__(64 * kWaves) void decode_lossless_group(GroupArgs g) {
     extern __shared__ __align__(16) uint8_t smem[];
     int bim;
-    const MatDesc& M = my_matrix(g, &bim);
+    const MatDesc M = my_matrix(g, &bim);
     const Tables T = stage_tables(M, smem);
     Tile t;
     init_lane(t, smem + table_blob_bytes(M.n_tables, M.prob_bits));
     const uint64_t n_pairs = (uint64_t)((M.rows + M.tile_rows - 1) / M.tile_rows) * M.pairs_c;
     const uint64_t pair0 = (uint64_t)bim * g.pairs_per_block;
     const uint64_t pair1 = std::min<uint64_t>(pair0 + g.pairs_per_block, n_pairs);
-    switch (M.n_tables) {
-        case 1: lossless_pairs<1>(M, T, t, pair0, pair1); break;
-        case 2: lossless_pairs<2>(M, T, t, pair0, pair1); break;
-        default: lossless_pairs<4>(M, T, t, pair0, pair1); break;
+    switch (M.n_tables * 16 + M.prob_bits) {
+        case 16 + 10: lossless_pairs<1, 10>(M, T, t, pair0, pair1); break;
+        case 16 + 11: lossless_pairs<1, 11>(M, T, t, pair0, pair1); break;
+        case 16 + 12: lossless_pairs<1, 12>(M, T, t, pair0, pair1); break;
+        case 32 + 10: lossless_pairs<2, 10>(M, T, t, pair0, pair1); break;
+        case 32 + 11: lossless_pairs<2, 11>(M, T, t, pair0, pair1); break;
+        case 32 + 12: lossless_pairs<2, 12>(M, T, t, pair0, pair1); break;
+        case 64 + 10: lossless_pairs<4, 10>(M, T, t, pair0, pair1); break;
+        case 64 + 11: lossless_pairs<4, 11>(M, T, t, pair0, pair1); break;
+        default: lossless_pairs<4, 12>(M, T, t, pair0, pair1); break;
     }
     if (t.err) atomicOr(M.err, t.err);
 }
