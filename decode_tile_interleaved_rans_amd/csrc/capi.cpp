@@ -38,7 +38,7 @@ ep_status hip_fail(hipError_t e, const char* what) {
 
 size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Device decode tables: lut [t][slot] = symbol, fc [t][s] = f | c << 13, val [t][s] = the value
+// Device decode tables: lut [t][slot] = symbol, fc [t][s] = f | c << 16, val [t][s] = the value
 // a lossy symbol stands for (doubled coordinate 2 (lo + s) + b, or the coset for table 0).
 std::vector<uint8_t> build_tables(const ep::StreamView& v) {
     const int n = v.prob_bits;
@@ -56,7 +56,7 @@ std::vector<uint8_t> build_tables(const ep::StreamView& v) {
             if (v.mode == EP_MODE_LOSSLESS) value = s;
             else if (t == 0) value = T.lo + s;
             else value = (s == ep::kEscape || s >= T.width) ? 0 : 2 * (T.lo + s) + ((t - 1) & 1);
-            fc[(size_t)t * 256 + s] = f | c << 13;
+            fc[(size_t)t * 256 + s] = f | c << 16;
             val[(size_t)t * 256 + s] = (int16_t)value;
             for (uint32_t k = 0; k < f; ++k) lut[(size_t)t * M + c + k] = (uint8_t)s;
             c += f;
@@ -81,6 +81,7 @@ ep::MatDesc desc_for(const ep_handle* h, int container, void* out, float* scale)
     d.cols = (uint32_t)v.cols;
     d.tiles_c = (uint32_t)v.tiles_c;
     d.pairs_c = (uint32_t)((v.tiles_c + 1) / 2);
+    d.payload_bytes = (uint32_t)v.payload_len;
     d.step = v.step;
     d.prob_bits = (uint8_t)v.prob_bits;
     d.tile_rows = (uint8_t)v.tile_rows;

@@ -39,9 +39,11 @@ namespace {
 
 constexpr uint32_t kLow = 1u << 16;
 constexpr int kWaves = 16;                 // waves per block
-constexpr int kRingWords = 1024;           // per tile
+constexpr int kRingWords = 512;            // per tile
 constexpr int kRingBytes = 2 * kRingWords;
+constexpr int kChains = 2;                 // independent tile pairs decoded together by a wave
 constexpr int kChunkDw = 128;              // one chunk: 32 lanes x 4 dwords = 256 words
+constexpr int kChunkWords = 2 * kChunkDw;
 constexpr int kErrWords = 1;               // words ran out or were left over
 constexpr int kErrState = 2;               // a final state differs from 2^16
 
@@ -91,13 +93,6 @@ struct Tables {
     const int16_t* val;
 };
 
-__device__ __forceinline__ MatDesc my_matrix(const GroupArgs& g, int* block_in_matrix) {
-    int mi = 0;
-    while (mi + 1 < g.count && (int)blockIdx.x >= g.block_start[mi + 1]) ++mi;
-    *block_in_matrix = (int)blockIdx.x - g.block_start[mi];
-    return g.m[mi];
-}
-
 __device__ __forceinline__ Tables stage_tables(const MatDesc& M, uint8_t* smem) {
     const int n = M.prob_bits;
     const size_t bytes = table_blob_bytes(M.n_tables, n);
@@ -119,7 +114,7 @@ struct Tile {
     uint32_t fill;         // words placed in the ring (multiple of 256)
     uint32_t nwords;       // words of the tile (pad word included)
     uint32_t ndw;          // the same in dwords
-    const uint32_t* gdw;   // the tile's words in global memory, as dwords
+    uint32_t gdw;          // byte offset of the tile's words in the payload (buffer loads)
     uint16_t* ring;        // this half's LDS ring
     uint32_t pf[4];        // next chunk, loaded ahead
     uint32_t below;        // lanes below this one within the half
@@ -129,50 +124,56 @@ struct Tile {
     int err;
 };
 
-__device__ __forceinline__ void load_chunk(Tile& t, uint32_t chunk, uint32_t* dst) {
+// Chunk loads go through a buffer resource over the matrix payload: reads past the tile fetch
+// the next tile's words (never consumed by a valid stream) and reads past the payload return 0,
+// so no per-lane bounds test is needed. Lanes without a tile use an out-of-range offset.
+__device__ __forceinline__ void load_chunk(const Tile& t, __amdgpu_buffer_rsrc_t rs, uint32_t chunk, uint32_t* dst) {
+    const uint32_t off = t.valid ? t.gdw + 4u * (chunk * kChunkDw + t.l) : 0x80000000u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t d = chunk * kChunkDw + t.l + 32 * i;
-        dst[i] = (t.valid && d < t.ndw) ? t.gdw[d] : 0u;
-    }
+    for (int i = 0; i < 4; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 128u * i, 0, 0);
 }
 __device__ __forceinline__ void store_chunk(Tile& t, uint32_t chunk, const uint32_t* src) {
     uint32_t* ring = reinterpret_cast<uint32_t*>(t.ring);
-    const uint32_t base = (chunk * kChunkDw) & (kRingWords / 2 - 1);
+    const uint32_t base = (chunk * kChunkDw) & (kRingWords / 2 - 1);   // kRingWords / 2 dwords
 #pragma unroll
     for (int i = 0; i < 4; ++i) ring[base + t.l + 32 * i] = src[i];
 }
 
-__device__ __forceinline__ void begin_tile(const MatDesc& M, uint64_t tile, Tile& t) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t payload_rsrc(const MatDesc& M) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(M.payload), 0, (int)M.payload_bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void begin_tile(const MatDesc& M, __amdgpu_buffer_rsrc_t rs, uint64_t tile, Tile& t) {
     if (t.valid) {
         const uint32_t a = M.index[tile], b = M.index[tile + 1];
-        const uint32_t* p = M.payload + a;
-        t.x = p[t.l];
-        t.gdw = p + 32;
+        t.x = M.payload[a + t.l];
+        t.gdw = 4u * (a + 32);
         t.ndw = b - a - 32;
     } else {
         t.x = kLow;
-        t.gdw = M.payload;
+        t.gdw = 0;
         t.ndw = 0;
     }
     t.nwords = 2 * t.ndw;
     t.pos = 0;
-    uint32_t first[16];
+    constexpr int kFirst = kRingWords / kChunkWords;
+    uint32_t first[4 * kFirst];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) load_chunk(t, k, first + 4 * k);
+    for (int k = 0; k < kFirst; ++k) load_chunk(t, rs, k, first + 4 * k);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) store_chunk(t, k, first + 4 * k);
+    for (int k = 0; k < kFirst; ++k) store_chunk(t, k, first + 4 * k);
     t.fill = kRingWords;
-    load_chunk(t, 4, t.pf);
+    load_chunk(t, rs, kFirst, t.pf);
     __builtin_amdgcn_wave_barrier();
 }
 
-// Keep more than one row's worst-case consumption (9 x 64 words) in the ring.
-__device__ __forceinline__ void top_up(Tile& t) {
-    while (t.fill < t.nwords && t.fill - t.pos <= kRingWords - 256) {
-        store_chunk(t, t.fill / 256, t.pf);
-        t.fill += 256;
-        if (t.fill < t.nwords) load_chunk(t, t.fill / 256, t.pf);
+// Keep more than three steps' worst-case consumption (3 x 64 words) in the ring: after this, the
+// ring holds more than kRingWords - kChunkWords = 256 unread words, or the rest of the tile.
+__device__ __forceinline__ void top_up(Tile& t, __amdgpu_buffer_rsrc_t rs) {
+    while (t.fill < t.nwords && t.fill - t.pos <= kRingWords - kChunkWords) {
+        store_chunk(t, t.fill / kChunkWords, t.pf);
+        t.fill += kChunkWords;
+        load_chunk(t, rs, t.fill / kChunkWords, t.pf);
     }
     __builtin_amdgcn_wave_barrier();
 }
@@ -201,7 +202,7 @@ __device__ __forceinline__ uint32_t rans_step(Tile& t, const uint8_t* lut, const
     const uint32_t slot = t.x & ((1u << N) - 1u);
     const uint32_t s = lut[slot];
     const uint32_t e = fc[s];
-    t.x = __umul24(e & 0x1FFFu, t.x >> N) + slot - (e >> 13);
+    t.x = __umul24(e & 0xFFFFu, t.x >> N) + slot - (e >> 16);     // SDWA word selects
     return s;
 }
 
@@ -220,17 +221,21 @@ __device__ __forceinline__ void end_tile(Tile& t) {
     if (!t.valid) return;
     if (t.x != kLow) t.err |= kErrState;
     const bool exact = t.pos == t.nwords;
-    const bool pad = t.pos + 1 == t.nwords && (t.gdw[t.ndw - 1] >> 16) == 0;
-    if (!exact && !pad) t.err |= kErrWords;
+    const bool loaded = t.fill >= t.nwords;
+    const bool pad = t.pos + 1 == t.nwords && t.ring[t.pos & (kRingWords - 1)] == 0;
+    if (!loaded || (!exact && !pad)) t.err |= kErrWords;
 }
 
-__device__ __forceinline__ void init_lane(Tile& t, uint8_t* ring_base) {
+// Lane constants; each (wave, chain, half) owns one ring.
+__device__ __forceinline__ void init_lane(Tile& t, uint8_t* ring_base, int chain) {
     const int lane = threadIdx.x & 63;
     t.l = lane & 31;
     t.sh = (uint32_t)(lane & 32);
     t.below = (1u << t.l) - 1u;
-    t.ring = reinterpret_cast<uint16_t*>(ring_base + ((threadIdx.x >> 6) * 2 + (lane >> 5)) * kRingBytes);
+    const int ring = ((threadIdx.x >> 6) * kChains + chain) * 2 + (lane >> 5);
+    t.ring = reinterpret_cast<uint16_t*>(ring_base + ring * kRingBytes);
     t.err = 0;
+    t.valid = false;
 }
 
 // ----------------------------------------------------------------------------- stores
@@ -304,108 +309,148 @@ __device__ __forceinline__ void store_block(const MatDesc& M, uint32_t row, uint
 }
 
 // ----------------------------------------------------------------------------- lossy kernel
-template <int CT, int N>
-__device__ __forceinline__ void lossy_pairs(const MatDesc& M, const Tables& T, Tile& t, uint64_t pair0, uint64_t pair1) {
+// Rows of one tile pair: tile coordinates and the per-row scales, one row per lane, read back
+// per row with readlane.
+struct PairRows {
+    uint32_t tc, row0;
+    float sc_l;
+    uint32_t qm_l;
+};
+
+template <int CT>
+__device__ __forceinline__ void begin_pair(const MatDesc& M, __amdgpu_buffer_rsrc_t rs, uint64_t pair, Tile& t,
+                                           PairRows& P) {
+    const uint32_t tr = (uint32_t)(pair / M.pairs_c);
+    P.tc = 2 * (uint32_t)(pair % M.pairs_c) + (t.sh ? 1u : 0u);
+    t.valid = P.tc < M.tiles_c;
+    begin_tile(M, rs, (uint64_t)tr * M.tiles_c + P.tc, t);
+    P.row0 = tr * M.tile_rows;
+    const uint32_t my_row = P.row0 + t.l;
+    const bool mine = t.l < M.tile_rows && my_row < M.rows;
+    P.sc_l = mine ? M.row_scale[my_row] : 0.0f;
+    P.qm_l = 0;
+    if constexpr (CT == CT_I8) P.qm_l = mine ? M.row_qmax[my_row] : 0u;
+}
+
+template <int CT>
+__device__ __forceinline__ void store_row(const MatDesc& M, const Tile& t, const PairRows& P, int rr, const int32_t* q,
+                                          float h) {
+    const uint32_t row = P.row0 + rr;
+    const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, P.sc_l), rr));
+    if (row >= M.rows || !t.valid) return;
+    const float alpha = h * sc;
+    uint32_t k = 1, magic = 0;
+    if constexpr (CT == CT_I8) {
+        const uint32_t qm = (uint32_t)__builtin_amdgcn_readlane((int)P.qm_l, rr);
+        k = qm > 127u ? (qm + 126u) / 127u : 1u;
+        magic = 0xFFFFFFFFu / (2u * k) + 1u;
+    }
+    const uint32_t col0 = P.tc * 256 + 8 * t.l;
+    if (col0 < M.cols) store_block<CT>(M, row, col0, q, alpha, h, k, magic);
+    if constexpr (CT == CT_F8E4M3 || CT == CT_I8) {
+        if (P.tc == 0 && t.l == 0) M.scale_out[row] = CT == CT_F8E4M3 ? sc : alpha * (float)k;
+    }
+}
+
+// Decode C tile pairs side by side (C independent rANS chains per lane, interleaved by the
+// compiler to hide LDS latency).
+template <int CT, int N, int C>
+__device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Tile* t, const uint64_t* pair) {
     const float h = M.step * 0.5f;
-    const uint32_t wave = threadIdx.x >> 6;
-    const uint32_t f0 = T.fc[0] & 0x1FFFu, f1 = T.fc[1] & 0x1FFFu;    // coset table
+    const uint32_t f0 = T.fc[0] & 0xFFFFu, f1 = T.fc[1] & 0xFFFFu;    // coset table
     const int lo0 = T.val[0];
-    for (uint64_t pair = pair0 + wave; pair < pair1; pair += kWaves) {
-        const uint32_t tr = (uint32_t)(pair / M.pairs_c);
-        const uint32_t tc = 2 * (uint32_t)(pair % M.pairs_c) + (t.sh ? 1u : 0u);
-        t.valid = tc < M.tiles_c;
-        begin_tile(M, (uint64_t)tr * M.tiles_c + tc, t);
-        const uint32_t row0 = tr * M.tile_rows;
-        // row scale (and row max |q| for INT8) of the tile's rows, one per lane, read back per row
-        const uint32_t my_row = row0 + t.l;
-        const float sc_l = (t.l < M.tile_rows && my_row < M.rows) ? M.row_scale[my_row] : 0.0f;
-        uint32_t qm_l = 0;
-        if constexpr (CT == CT_I8) qm_l = (t.l < M.tile_rows && my_row < M.rows) ? M.row_qmax[my_row] : 0u;
-        for (int rr = 0; rr < M.tile_rows; ++rr) {
-            top_up(t);
-            const int b = lo0 + (int)coset_step<N>(t, f0, f1);
-            refill(t);
-            // tables 1 + 2j + b for this lane's coset; j selects a compile-time offset
-            const uint8_t* lut_b = T.lut + ((1 + b) << N);
-            const uint32_t* fc_b = T.fc + (1 + b) * 256;
-            const int16_t* val_b = T.val + (1 + b) * 256;
-            int32_t q[8];
+    const __amdgpu_buffer_rsrc_t rs = payload_rsrc(M);
+    PairRows P[C];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t s = rans_step<N>(t, lut_b + ((2 * j) << N), fc_b + 2 * j * 256);
-                refill(t);
-                q[j] = val_b[2 * j * 256 + s];
-                const bool esc = s == 255u;
-                if (__ballot(esc)) {
-                    const uint32_t w = take_words(t, esc);
-                    if (esc) q[j] = 2 * (int32_t)(int16_t)w + b;
-                }
+    for (int c = 0; c < C; ++c) begin_pair<CT>(M, rs, pair[c], t[c], P[c]);
+    for (int rr = 0; rr < M.tile_rows; ++rr) {
+        int b[C];
+        const uint8_t* lut_b[C];
+        const uint32_t* fc_b[C];
+        const int16_t* val_b[C];
+        int32_t q[C][8];
+#pragma unroll
+        for (int c = 0; c < C; ++c) top_up(t[c], rs);
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            b[c] = lo0 + (int)coset_step<N>(t[c], f0, f1);
+            refill(t[c]);
+            // tables 1 + 2j + b for this lane's coset; j selects a compile-time offset
+            lut_b[c] = T.lut + ((1 + b[c]) << N);
+            fc_b[c] = T.fc + (1 + b[c]) * 256;
+            val_b[c] = T.val + (1 + b[c]) * 256;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j == 2 || j == 5) {                       // before steps 3 and 6 of the row
+#pragma unroll
+                for (int c = 0; c < C; ++c) top_up(t[c], rs);
             }
-            const uint32_t row = row0 + rr;
-            const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_l), rr));
-            if (row < M.rows && t.valid) {
-                const float alpha = h * sc;
-                uint32_t k = 1, magic = 0;
-                if constexpr (CT == CT_I8) {
-                    const uint32_t qm = (uint32_t)__builtin_amdgcn_readlane((int)qm_l, rr);
-                    k = qm > 127u ? (qm + 126u) / 127u : 1u;
-                    magic = 0xFFFFFFFFu / (2u * k) + 1u;
-                }
-                const uint32_t col0 = tc * 256 + 8 * t.l;
-                if (col0 < M.cols) store_block<CT>(M, row, col0, q, alpha, h, k, magic);
-                if constexpr (CT == CT_F8E4M3 || CT == CT_I8) {
-                    if (tc == 0 && t.l == 0) M.scale_out[row] = CT == CT_F8E4M3 ? sc : alpha * (float)k;
+            // all chains' step j in one basic block, so the scheduler can interleave the chains;
+            // the rare escapes branch once for all chains
+            uint32_t sy[C];
+            bool esc[C], any = false;
+#pragma unroll
+            for (int c = 0; c < C; ++c) sy[c] = rans_step<N>(t[c], lut_b[c] + ((2 * j) << N), fc_b[c] + 2 * j * 256);
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                refill(t[c]);
+                q[c][j] = val_b[c][2 * j * 256 + sy[c]];
+                esc[c] = sy[c] == 255u;
+                any = any || esc[c];
+            }
+            if (__ballot(any)) {
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    const uint32_t w = take_words(t[c], esc[c]);
+                    if (esc[c]) q[c][j] = 2 * (int32_t)(int16_t)w + b[c];
                 }
             }
         }
-        end_tile(t);
+#pragma unroll
+        for (int c = 0; c < C; ++c) store_row<CT>(M, t[c], P[c], rr, q[c], h);
     }
+#pragma unroll
+    for (int c = 0; c < C; ++c) end_tile(t[c]);
+}
+
+// Pairs [p0, p1) of one matrix: wave w takes p0 + w, p0 + w + 16, ..., two at a time.
+template <int CT, int N>
+__device__ __forceinline__ void lossy_pairs(const MatDesc& M, const Tables& T, Tile* t, uint64_t p0, uint64_t p1) {
+    uint64_t p = p0 + (threadIdx.x >> 6);
+    for (; p + kWaves < p1; p += 2 * kWaves) {
+        const uint64_t two[2] = {p, p + kWaves};
+        lossy_run<CT, N, 2>(M, T, t, two);
+    }
+    if (p < p1) lossy_run<CT, N, 1>(M, T, t, &p);
 }
 
 template <int N>
-__device__ __forceinline__ void lossy_dispatch(const MatDesc& M, const Tables& T, Tile& t, uint64_t pair0, uint64_t pair1) {
+__device__ __forceinline__ void lossy_dispatch(const MatDesc& M, const Tables& T, Tile* t, uint64_t p0, uint64_t p1) {
     switch (M.container) {
-        case CT_BF16: lossy_pairs<CT_BF16, N>(M, T, t, pair0, pair1); break;
-        case CT_F16: lossy_pairs<CT_F16, N>(M, T, t, pair0, pair1); break;
-        case CT_F8E4M3: lossy_pairs<CT_F8E4M3, N>(M, T, t, pair0, pair1); break;
-        case CT_I8: lossy_pairs<CT_I8, N>(M, T, t, pair0, pair1); break;
-        default: lossy_pairs<CT_Q16, N>(M, T, t, pair0, pair1); break;
+        case CT_BF16: lossy_pairs<CT_BF16, N>(M, T, t, p0, p1); break;
+        case CT_F16: lossy_pairs<CT_F16, N>(M, T, t, p0, p1); break;
+        case CT_F8E4M3: lossy_pairs<CT_F8E4M3, N>(M, T, t, p0, p1); break;
+        case CT_I8: lossy_pairs<CT_I8, N>(M, T, t, p0, p1); break;
+        default: lossy_pairs<CT_Q16, N>(M, T, t, p0, p1); break;
     }
-}
-
-__global__ __launch_bounds__(64 * kWaves) void decode_lossy_group(GroupArgs g) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    int bim;
-    const MatDesc M = my_matrix(g, &bim);
-    const Tables T = stage_tables(M, smem);
-    Tile t;
-    init_lane(t, smem + table_blob_bytes(M.n_tables, M.prob_bits));
-    const uint64_t n_pairs = (uint64_t)((M.rows + M.tile_rows - 1) / M.tile_rows) * M.pairs_c;
-    const uint64_t pair0 = (uint64_t)bim * g.pairs_per_block;
-    const uint64_t pair1 = std::min<uint64_t>(pair0 + g.pairs_per_block, n_pairs);
-    switch (M.prob_bits) {
-        case 10: lossy_dispatch<10>(M, T, t, pair0, pair1); break;
-        case 11: lossy_dispatch<11>(M, T, t, pair0, pair1); break;
-        default: lossy_dispatch<12>(M, T, t, pair0, pair1); break;
-    }
-    if (t.err) atomicOr(M.err, t.err);
 }
 
 // ----------------------------------------------------------------------------- lossless kernel
 template <int P, int N>
-__device__ __forceinline__ void lossless_pairs(const MatDesc& M, const Tables& T, Tile& t, uint64_t pair0, uint64_t pair1) {
-    const uint32_t wave = threadIdx.x >> 6;
+__device__ __forceinline__ void lossless_pairs(const MatDesc& M, const Tables& T, Tile& t, uint64_t p0, uint64_t p1) {
     using E = typename std::conditional<P == 1, uint8_t, typename std::conditional<P == 2, uint16_t, uint32_t>::type>::type;
-    for (uint64_t pair = pair0 + wave; pair < pair1; pair += kWaves) {
+    const __amdgpu_buffer_rsrc_t rs = payload_rsrc(M);
+    for (uint64_t pair = p0 + (threadIdx.x >> 6); pair < p1; pair += kWaves) {
         const uint32_t tr = (uint32_t)(pair / M.pairs_c);
         const uint32_t tc = 2 * (uint32_t)(pair % M.pairs_c) + (t.sh ? 1u : 0u);
         t.valid = tc < M.tiles_c;
-        begin_tile(M, (uint64_t)tr * M.tiles_c + tc, t);
+        begin_tile(M, rs, (uint64_t)tr * M.tiles_c + tc, t);
         for (int rr = 0; rr < M.tile_rows; ++rr) {
             uint32_t v[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                top_up(t);                  // an element is at most 4 steps x 32 words
+                top_up(t, rs);              // an element is at most 4 steps x 32 words
                 uint32_t acc = 0;
 #pragma unroll
                 for (int pl = 0; pl < P; ++pl) {
@@ -440,28 +485,56 @@ __device__ __forceinline__ void lossless_pairs(const MatDesc& M, const Tables& T
     }
 }
 
-__global__ __launch_bounds__(64 * kWaves) void decode_lossless_group(GroupArgs g) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    int bim;
-    const MatDesc M = my_matrix(g, &bim);
-    const Tables T = stage_tables(M, smem);
-    Tile t;
-    init_lane(t, smem + table_blob_bytes(M.n_tables, M.prob_bits));
-    const uint64_t n_pairs = (uint64_t)((M.rows + M.tile_rows - 1) / M.tile_rows) * M.pairs_c;
-    const uint64_t pair0 = (uint64_t)bim * g.pairs_per_block;
-    const uint64_t pair1 = std::min<uint64_t>(pair0 + g.pairs_per_block, n_pairs);
+__device__ __forceinline__ void lossless_dispatch(const MatDesc& M, const Tables& T, Tile* t, uint64_t p0, uint64_t p1) {
     switch (M.n_tables * 16 + M.prob_bits) {
-        case 16 + 10: lossless_pairs<1, 10>(M, T, t, pair0, pair1); break;
-        case 16 + 11: lossless_pairs<1, 11>(M, T, t, pair0, pair1); break;
-        case 16 + 12: lossless_pairs<1, 12>(M, T, t, pair0, pair1); break;
-        case 32 + 10: lossless_pairs<2, 10>(M, T, t, pair0, pair1); break;
-        case 32 + 11: lossless_pairs<2, 11>(M, T, t, pair0, pair1); break;
-        case 32 + 12: lossless_pairs<2, 12>(M, T, t, pair0, pair1); break;
-        case 64 + 10: lossless_pairs<4, 10>(M, T, t, pair0, pair1); break;
-        case 64 + 11: lossless_pairs<4, 11>(M, T, t, pair0, pair1); break;
-        default: lossless_pairs<4, 12>(M, T, t, pair0, pair1); break;
+        case 16 + 10: lossless_pairs<1, 10>(M, T, t[0], p0, p1); break;
+        case 16 + 11: lossless_pairs<1, 11>(M, T, t[0], p0, p1); break;
+        case 16 + 12: lossless_pairs<1, 12>(M, T, t[0], p0, p1); break;
+        case 32 + 10: lossless_pairs<2, 10>(M, T, t[0], p0, p1); break;
+        case 32 + 11: lossless_pairs<2, 11>(M, T, t[0], p0, p1); break;
+        case 32 + 12: lossless_pairs<2, 12>(M, T, t[0], p0, p1); break;
+        case 64 + 10: lossless_pairs<4, 10>(M, T, t[0], p0, p1); break;
+        case 64 + 11: lossless_pairs<4, 11>(M, T, t[0], p0, p1); break;
+        default: lossless_pairs<4, 12>(M, T, t[0], p0, p1); break;
     }
-    if (t.err) atomicOr(M.err, t.err);
+}
+
+// ----------------------------------------------------------------------------- grouped kernel
+// Persistent blocks: block k owns pairs [k P, (k + 1) P) of the launch's matrix-major pair
+// space, so every CU gets the same amount of work. A block walks its range one matrix segment at
+// a time and restages the decode tables when it crosses into the next matrix.
+template <bool LOSSY>
+__global__ __launch_bounds__(64 * kWaves) void decode_group(GroupArgs g) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const uint64_t a = (uint64_t)blockIdx.x * (uint64_t)g.block_pairs;
+    const uint64_t b = std::min<uint64_t>(a + (uint64_t)g.block_pairs, (uint64_t)g.pair_start[g.count]);
+    int mi = 0;
+    int err[kChains] = {};
+    for (uint64_t pos = a; pos < b;) {
+        while ((uint64_t)g.pair_start[mi + 1] <= pos) ++mi;
+        const uint64_t base = (uint64_t)g.pair_start[mi];
+        const uint64_t end = std::min<uint64_t>(b, (uint64_t)g.pair_start[mi + 1]);
+        const MatDesc M = g.m[mi];
+        __syncthreads();                            // every wave is done with the previous tables
+        const Tables T = stage_tables(M, smem);
+        Tile t[kChains];
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) init_lane(t[c], smem + table_blob_bytes(M.n_tables, M.prob_bits), c);
+        if constexpr (LOSSY) {
+            switch (M.prob_bits) {
+                case 10: lossy_dispatch<10>(M, T, t, pos - base, end - base); break;
+                case 11: lossy_dispatch<11>(M, T, t, pos - base, end - base); break;
+                default: lossy_dispatch<12>(M, T, t, pos - base, end - base); break;
+            }
+        } else {
+            lossless_dispatch(M, T, t, pos - base, end - base);
+        }
+#pragma unroll
+        for (int c = 0; c < kChains; ++c)
+            if (t[c].err) atomicOr(M.err, t[c].err);
+        pos = end;
+    }
+    (void)err;
 }
 
 int device_cus() {
@@ -494,35 +567,29 @@ hipError_t launch_group(const MatDesc* mats, int count, int mode, hipStream_t st
     if (count > kMaxGroup) return hipErrorInvalidValue;
     GroupArgs g{};
     g.count = count;
-    uint64_t total_pairs = 0;
+    uint64_t total = 0;
     size_t lds = 0;
     for (int i = 0; i < count; ++i) {
         g.m[i] = mats[i];
-        total_pairs += (uint64_t)((mats[i].rows + mats[i].tile_rows - 1) / mats[i].tile_rows) * mats[i].pairs_c;
-        lds = std::max(lds, table_blob_bytes(mats[i].n_tables, mats[i].prob_bits) + (size_t)kWaves * 2 * kRingBytes);
+        g.pair_start[i] = (uint32_t)total;
+        total += (uint64_t)((mats[i].rows + mats[i].tile_rows - 1) / mats[i].tile_rows) * mats[i].pairs_c;
+        lds = std::max(lds, table_blob_bytes(mats[i].n_tables, mats[i].prob_bits) +
+                                (size_t)kWaves * kChains * 2 * kRingBytes);
     }
-    if (total_pairs == 0) return hipSuccess;
-    // about four blocks per CU over the launch, at least one pair per wave
-    const uint64_t target_blocks = 4ull * device_cus();
-    uint64_t ppb = (total_pairs + target_blocks - 1) / target_blocks;
-    ppb = std::max<uint64_t>(kWaves, (ppb + kWaves - 1) / kWaves * kWaves);
-    g.pairs_per_block = (int32_t)std::min<uint64_t>(ppb, 1u << 20);
-    int32_t blocks = 0;
-    for (int i = 0; i < count; ++i) {
-        g.block_start[i] = blocks;
-        const uint64_t pairs = (uint64_t)((mats[i].rows + mats[i].tile_rows - 1) / mats[i].tile_rows) * mats[i].pairs_c;
-        blocks += (int32_t)((pairs + g.pairs_per_block - 1) / g.pairs_per_block);
-    }
-    g.block_start[count] = blocks;
-    if (blocks == 0) return hipSuccess;
-    const void* k = mode == 0 ? reinterpret_cast<const void*>(decode_lossy_group)
-                              : reinterpret_cast<const void*>(decode_lossless_group);
+    g.pair_start[count] = (uint32_t)total;
+    if (total == 0) return hipSuccess;
+    if (total >= (1ull << 32)) return hipErrorInvalidValue;
+    const uint64_t blocks = std::min<uint64_t>((uint64_t)device_cus(), total);
+    g.block_pairs = (uint32_t)((total + blocks - 1) / blocks);
+    const uint64_t used = (total + g.block_pairs - 1) / g.block_pairs;
+    const void* k = mode == 0 ? reinterpret_cast<const void*>(decode_group<true>)
+                              : reinterpret_cast<const void*>(decode_group<false>);
     hipError_t e = allow_lds(k);
     if (e != hipSuccess) return e;
     if (mode == 0)
-        hipLaunchKernelGGL(decode_lossy_group, dim3(blocks), dim3(64 * kWaves), lds, stream, g);
+        hipLaunchKernelGGL(decode_group<true>, dim3((unsigned)used), dim3(64 * kWaves), lds, stream, g);
     else
-        hipLaunchKernelGGL(decode_lossless_group, dim3(blocks), dim3(64 * kWaves), lds, stream, g);
+        hipLaunchKernelGGL(decode_group<false>, dim3((unsigned)used), dim3(64 * kWaves), lds, stream, g);
     return hipGetLastError();
 }
 

@@ -23,20 +23,21 @@ struct MatDesc {
     float* scale_out;           // [rows] for FP8 / INT8, else unused
     int* err;                   // device error flag (bit 0: word count, bit 1: final state)
     uint32_t rows, cols, tiles_c, pairs_c;
+    uint32_t payload_bytes;     // size of the tile payload (buffer-load bounds)
     float step;
     uint8_t prob_bits, tile_rows, container, n_tables;
 };
 
 struct GroupArgs {
     int32_t count;              // matrices in this launch (<= kMaxGroup)
-    int32_t pairs_per_block;    // tile pairs handled by one block
-    int32_t block_start[kMaxGroup + 1];
+    uint32_t block_pairs;       // tile pairs per block (the last block may get fewer)
+    uint32_t pair_start[kMaxGroup + 1];   // matrix-major prefix sums of the matrices' tile pairs
     MatDesc m[kMaxGroup];
 };
 
 // Decode tables of one stream, in device memory and in LDS:
 //   lut [n_tables][2^n] u8   slot -> symbol
-//   fc  [n_tables][256] u32  f | c << 13 (frequency, cumulative frequency)
+//   fc  [n_tables][256] u32  f | c << 16 (frequency, cumulative frequency)
 //   val [n_tables][256] i16  doubled lattice coordinate 2 (lo + s) + b (lossy), coset (table 0)
 __host__ __device__ inline size_t table_blob_bytes(int n_tables, int prob_bits) {
     return ((size_t)n_tables << prob_bits) + (size_t)n_tables * 256 * 4 + (size_t)n_tables * 256 * 2;
