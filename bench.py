@@ -79,6 +79,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain 256 MiB device copy first (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the decode path has no cross-GPU step (tiles, rows and "
@@ -89,6 +91,12 @@ def main():
     import decode_tile_interleaved_rans_amd as ep
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     items, (R, C) = c2_items()
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16}
     step_out_bytes = sum(R * C * 2 for _ in items)

@@ -18,7 +18,8 @@
 // coalesced 512-byte chunk loads that are issued one chunk ahead, so the serial rANS chain only
 // ever waits on LDS. Before each block row the ring is topped up until it holds more than the
 // most a row can consume (9 steps x 64 words), so the steps need no bounds checks; a damaged
-// stream can only read stale ring words, and is caught by the end-of-tile checks.
+// stream can only read stale ring words, and is caught by the end-of-tile checks. Lossless tiles
+// top up before every element (at most 4 steps x 32 words).
 //
 // Per decoding step every lane looks up its slot in the LDS table, updates its state, and lanes
 // whose state fell below 2^16 take the next word of their tile; a wave ballot, shifted to the
@@ -39,9 +40,9 @@ namespace {
 
 constexpr uint32_t kLow = 1u << 16;
 constexpr int kWaves = 16;                 // waves per block
-constexpr int kRingWords = 512;            // per tile
+constexpr int kRingWords = 1024;           // per tile
 constexpr int kRingBytes = 2 * kRingWords;
-constexpr int kChains = 2;                 // independent tile pairs decoded together by a wave
+constexpr int kChains = 1;                 // tile pairs decoded together by a wave (see lossy_pairs)
 constexpr int kChunkDw = 128;              // one chunk: 32 lanes x 4 dwords = 256 words
 constexpr int kChunkWords = 2 * kChunkDw;
 constexpr int kErrWords = 1;               // words ran out or were left over
@@ -124,13 +125,18 @@ struct Tile {
     int err;
 };
 
-// Chunk loads go through a buffer resource over the matrix payload: reads past the tile fetch
-// the next tile's words (never consumed by a valid stream) and reads past the payload return 0,
-// so no per-lane bounds test is needed. Lanes without a tile use an out-of-range offset.
+// Chunk loads go through a buffer resource over the matrix payload; lanes whose dword lies past
+// the tile (or that have no tile) use an out-of-range offset, which the buffer unit answers with
+// 0 without touching memory.
 __device__ __forceinline__ void load_chunk(const Tile& t, __amdgpu_buffer_rsrc_t rs, uint32_t chunk, uint32_t* dst) {
-    const uint32_t off = t.valid ? t.gdw + 4u * (chunk * kChunkDw + t.l) : 0x80000000u;
+    const uint32_t d = chunk * kChunkDw + t.l;
+    const uint32_t off = t.gdw + 4u * d;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 128u * i, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+        // only the tile's own words are fetched: other lanes take an out-of-range offset (reads 0)
+        const uint32_t o = (t.valid && d + 32u * i < t.ndw) ? off + 128u * i : 0x80000000u;
+        dst[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, o, 0, 0);
+    }
 }
 __device__ __forceinline__ void store_chunk(Tile& t, uint32_t chunk, const uint32_t* src) {
     uint32_t* ring = reinterpret_cast<uint32_t*>(t.ring);
@@ -167,13 +173,14 @@ __device__ __forceinline__ void begin_tile(const MatDesc& M, __amdgpu_buffer_rsr
     __builtin_amdgcn_wave_barrier();
 }
 
-// Keep more than three steps' worst-case consumption (3 x 64 words) in the ring: after this, the
-// ring holds more than kRingWords - kChunkWords = 256 unread words, or the rest of the tile.
+// Keep more than one block row's worst-case consumption (9 steps x 64 words) in the ring: after
+// this, the ring holds more than kRingWords - kChunkWords = 768 unread words, or the rest of the
+// tile.
 __device__ __forceinline__ void top_up(Tile& t, __amdgpu_buffer_rsrc_t rs) {
     while (t.fill < t.nwords && t.fill - t.pos <= kRingWords - kChunkWords) {
         store_chunk(t, t.fill / kChunkWords, t.pf);
         t.fill += kChunkWords;
-        load_chunk(t, rs, t.fill / kChunkWords, t.pf);
+        if (t.fill < t.nwords) load_chunk(t, rs, t.fill / kChunkWords, t.pf);
     }
     __builtin_amdgcn_wave_barrier();
 }
@@ -382,10 +389,7 @@ __device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Til
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            if (j == 2 || j == 5) {                       // before steps 3 and 6 of the row
-#pragma unroll
-                for (int c = 0; c < C; ++c) top_up(t[c], rs);
-            }
+
             // all chains' step j in one basic block, so the scheduler can interleave the chains;
             // the rare escapes branch once for all chains
             uint32_t sy[C];
@@ -414,15 +418,12 @@ __device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Til
     for (int c = 0; c < C; ++c) end_tile(t[c]);
 }
 
-// Pairs [p0, p1) of one matrix: wave w takes p0 + w, p0 + w + 16, ..., two at a time.
+// Pairs [p0, p1) of one matrix: wave w takes p0 + w, p0 + w + 16, ... One chain per wave: two
+// interleaved chains (twice the rings, a top-up every three steps) measured slower on gfx950,
+// where the LDS lookups rather than their latency bound the loop.
 template <int CT, int N>
 __device__ __forceinline__ void lossy_pairs(const MatDesc& M, const Tables& T, Tile* t, uint64_t p0, uint64_t p1) {
-    uint64_t p = p0 + (threadIdx.x >> 6);
-    for (; p + kWaves < p1; p += 2 * kWaves) {
-        const uint64_t two[2] = {p, p + kWaves};
-        lossy_run<CT, N, 2>(M, T, t, two);
-    }
-    if (p < p1) lossy_run<CT, N, 1>(M, T, t, &p);
+    for (uint64_t p = p0 + (threadIdx.x >> 6); p < p1; p += kWaves) lossy_run<CT, N, 1>(M, T, t, &p);
 }
 
 template <int N>
