@@ -30,6 +30,23 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
 
 
+PROFILE = os.path.join(ROOT, "profiles", "decode_group_lossy_4096sq_step.txt")
+
+
+def profiled_traffic():
+    """HBM bytes per grouped lossy launch from the committed rocprofv3 counter summary, or None
+    when the decode kernel source changed since the counters were taken."""
+    import hashlib
+    try:
+        kv = dict(l.split(": ", 1) for l in open(PROFILE).read().splitlines() if l and not l.startswith("#"))
+        src = os.path.join(ROOT, "decode_tile_interleaved_rans_amd", "csrc")
+        sha = hashlib.sha256(open(os.path.join(src, "decode.hip"), "rb").read() +
+                             open(os.path.join(src, "kernels.h"), "rb").read()).hexdigest()
+        return int(kv["traffic_bytes_per_launch"]) if kv.get("kernel_source_sha256") == sha else None
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -158,7 +175,7 @@ def main():
     t_launch = float(np.mean(durs))
     achieved = launch_bytes / t_launch / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(),
                 "kernel": "decode_lossy_group (6 matrices: 3.0/4.0/4.5 bpp x BF16/FP16)",
                 "avg_launch_us": round(t_launch * 1e6, 2), "bytes_per_launch": launch_bytes,
                 "launch_us_min": round(min(durs) * 1e6, 2)}

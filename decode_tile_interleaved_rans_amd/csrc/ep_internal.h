@@ -6,8 +6,8 @@
 // (per table: i16 window start, u16 window width S, u16 escape frequency, u16 freq[S]), the tile
 // index u32[n_tiles + 1] (offsets in 4-byte units from the payload start) and the payload.
 // A tile is 32 u32 rANS states followed by its u16 words (plus one zero pad word when their
-// count is odd). The pages fix none of this; it is this codec's own container for "entropy-coded
-// in independently decodable tiles" (EntroPack paper, Abstract).
+// count is odd). The pages fix none of this; it is this codec's own container for tile-wise
+// entropy coding where every tile decodes on its own (EntroPack paper, Abstract).
 #pragma once
 
 #include <cstddef>

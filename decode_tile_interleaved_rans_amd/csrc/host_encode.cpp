@@ -2,9 +2,10 @@
 // model, sampled rate search and tile rANS coding, threaded over rows, samples and tiles.
 //
 // Method steps follow "EntroPack: Fast and Accurate Entropy-Coded Weight Compression at Arbitrary
-// Bitrates", Abstract: row-normalized E8 lattice quantization, a conditional probability model
-// of lattice coordinates, sampled storage estimates choosing the quantization resolution
-// without repeated full-stream encoding, and entropy coding in independently decodable tiles.
+// Bitrates", Abstract: each row is scaled to unit size and quantized to the E8 lattice, the lattice
+// coordinates get a conditional symbol model, the quantization step is chosen from a size estimate
+// on a sample (one full encode only), and the symbols are entropy-coded in tiles that decode on
+// their own.
 // The rules the page leaves open are fixed as follows (the decoder relies on all of them):
 //   row scale      s_r = fp32(sqrt(sum_j w_rj^2 / C)), fp64 sum in column order; s_r = 0 rows
 //                  quantize to 0

@@ -10,9 +10,9 @@
  *        (paper listing 2609.34185v1), Abstract.
  *   [G]  "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", by section.
  *   [P]  "EntroPack 開源：模型壓縮不必只選 4 位元，如何配合顯示記憶體預算？", by section.
- * [A] names the steps: row-normalized E8 lattice quantization, a conditional probability model of
- * lattice coordinates, sampled storage estimates choosing the quantization resolution, entropy
- * coding in independently decodable tiles, and reconstruction into BF16/FP16/FP8/INT8 containers.
+ * [A] names the steps: rows scaled to unit size and quantized to the E8 lattice, a conditional
+ * model of the lattice coordinates, a step size picked from a size estimate on a sample, entropy
+ * coding in tiles that decode on their own, and reconstruction into BF16/FP16/FP8/INT8 containers.
  * Every finer rule (norm, tie-breaking, alphabet, rANS parameters, tile geometry, byte layout,
  * rounding) is a reading where the pages are silent; each is marked "reading:" where it is used.
  *
@@ -183,7 +183,7 @@ static double src_value(const void* w, int dt, int64_t i) {
 }
 
 /* ------------------------------------------------------------------------------------------ */
-/* E8 nearest point. [A, Abstract]: "row-normalized E8 lattice quantization".                  */
+/* E8 nearest point. [A, Abstract]: normalized rows are quantized on the E8 lattice.           */
 /* Reading: E8 = D8 u (D8 + 1/2), unimodular scaling, lattice spacing set by the step.          */
 /* ------------------------------------------------------------------------------------------ */
 
@@ -235,7 +235,7 @@ void or_e8_nearest_batch(const double* y, int64_t n, int32_t* q, int32_t* coset)
 }
 
 /* ------------------------------------------------------------------------------------------ */
-/* Row scale. [A, Abstract] "row-normalized". Reading: unit-RMS rows; the sum of squares over    */
+/* Row scale. [A, Abstract]: rows are normalized. Reading: unit-RMS rows; the sum of squares over */
 /* the real columns is accumulated in fp64 in column order, divided by C, square-rooted in fp64  */
 /* and rounded once to fp32.                                                                    */
 /* ------------------------------------------------------------------------------------------ */
@@ -250,7 +250,7 @@ static float row_scale(const void* w, int dt, int64_t r, int64_t C) {
 }
 
 /* ------------------------------------------------------------------------------------------ */
-/* Symbol model. [A, Abstract]: "conditional probability model of lattice coordinates".         */
+/* Symbol model. [A, Abstract]: the lattice coordinates are coded with a conditional model.     */
 /* Reading: 17 static tables per tensor: table 0 codes the coset bit; table 1 + 2j + b codes    */
 /* coordinate j of a block in coset b. Each table keeps a window of at most 255 consecutive     */
 /* values; values outside it are coded as symbol 255 (escape) followed by a raw 16-bit word.     */
@@ -358,7 +358,7 @@ static void cumulate(const uint32_t* f, uint32_t* c) {
 }
 
 /* ------------------------------------------------------------------------------------------ */
-/* rANS tile coder. [A, Abstract]: "entropy-coded in independently decodable tiles".            */
+/* rANS tile coder. [A, Abstract]: entropy coding in tiles that decode on their own.            */
 /* Reading: every tile has 32 interleaved states (Giesen). Each step codes one symbol per lane. */
 /* Decoding step t: every lane decodes its symbol; lanes whose state fell below L then take one */
 /* refill word each, in ascending lane order; then lanes that decoded the escape symbol take    */
@@ -548,8 +548,8 @@ static void block_y(const void* w, int dt, int64_t R, int64_t C, const float* sc
 }
 
 /* ------------------------------------------------------------------------------------------ */
-/* Sampled rate estimate and step search. [A, Abstract]: "Sampled storage estimates select the  */
-/* quantization resolution without repeated full-stream encoding."                              */
+/* Sampled rate estimate and step search. [A, Abstract]: the step size comes from a storage     */
+/* estimate on a sample, so the full stream is encoded once.                                    */
 /* Reading: S_b = min(NB, 65536) blocks at indices floor(i NB / S_b) of the row-major real      */
 /* blocks; est = (sum over tables and symbols of -c log2(c / T) + 16 per escape) / (8 S_b) bits */
 /* per weight; the step is bisected in log2 between max(2^-12, 2 (U + 1) / 32767) and 64 for 48 */
@@ -1092,7 +1092,7 @@ int or_compress(const void* w, int src_dtype, int64_t rows, int64_t cols, int mo
 void or_free(void* p) { free(p); }
 
 /* ------------------------------------------------------------------------------------------ */
-/* Decoder and reconstruction. [A, Abstract]: fused symbol decoding and numerical weight        */
+/* Decoder and reconstruction. [A, Abstract]: decoding and weight reconstruction are fused;     */
 /* reconstruction; containers BF16, FP16, FP8, INT8 with the bitrate independent of precision.  */
 /* Reading: alpha_r = fp32(h s_r) with h = step / 2; BF16 and FP16 are RNE casts of             */
 /* fp32(q alpha_r); FP8 E4M3 stores fp32(q h) with s_r as the per-row dequantization scale; INT8 */

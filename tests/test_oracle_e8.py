@@ -1,5 +1,5 @@
 """Pins of the oracle's nearest-E8 quantizer against brute force, lattice invariants and the
-lattice's known second moment ("row-normalized E8 lattice quantization", EntroPack paper,
+lattice's known second moment (normalized rows quantized on the E8 lattice, EntroPack paper,
 Abstract). The oracle is reached through its C library; nothing here shares its code."""
 import itertools
 

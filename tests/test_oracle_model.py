@@ -1,7 +1,6 @@
-"""Pins of the oracle's symbol model (the "conditional probability model of lattice
-coordinates", EntroPack paper, Abstract) and of its sampled rate search ("sampled storage
-estimates select the quantization resolution without repeated full-stream encoding", same
-passage). Pins: normalization invariants, closed forms for a Gaussian source, monotonicity of
+"""Pins of the oracle's symbol model (a conditional model of the E8 lattice coordinates, EntroPack
+paper, Abstract) and of its sampled rate search (the step size picked from a storage estimate on
+a sample, same passage). Pins: normalization invariants, closed forms for a Gaussian source, monotonicity of
 the estimate, and the target being met by the coded payload."""
 import numpy as np
 import pytest

@@ -1,4 +1,4 @@
-"""Pins of the oracle's tile rANS coder (entropy coding "in independently decodable tiles",
+"""Pins of the oracle's tile rANS coder (entropy coding in tiles that decode on their own,
 EntroPack paper, Abstract; rANS after Duda arXiv:1311.2540, interleaved states after Giesen
 arXiv:1402.3392).
 
