@@ -12,6 +12,7 @@
 
 #include "entropack.h"
 #include "ep_internal.h"
+#include "gemm.h"
 #include "kernels.h"
 
 struct ep_handle {
@@ -20,6 +21,8 @@ struct ep_handle {
     uint8_t* dev = nullptr;     // one allocation: stream copy | table blob | error flag
     size_t stream_off = 0, tables_off = 0, err_off = 0, bytes = 0;
     int device = 0;
+    uint16_t* scratch = nullptr;  // decoded weight slice for the linear forward (lazily allocated)
+    size_t scratch_bytes = 0;
 };
 
 namespace {
@@ -221,6 +224,7 @@ ep_status ep_handle_info(const ep_handle* h, ep_info* out) {
 
 void ep_release(ep_handle* h) {
     if (!h) return;
+    if (h->scratch) (void)hipFree(h->scratch);
     if (h->dev) (void)hipFree(h->dev);
     delete h;
 }
@@ -277,16 +281,67 @@ ep_status ep_handle_check(ep_handle* h, void* hip_stream) {
     return EP_OK;
 }
 
-ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias, void* dev_y,
-                            void* hip_stream) {
-    (void)w; (void)dev_x; (void)M; (void)dev_bias; (void)dev_y; (void)hip_stream;
-    return fail(EP_EUNSUPPORTED, "fused linear forward not built yet");
-}
-
 ep_status ep_gemm_bf16(const void* dev_x, const void* dev_w, int64_t M, int64_t N, int64_t K, void* dev_y,
                        void* hip_stream) {
-    (void)dev_x; (void)dev_w; (void)M; (void)N; (void)K; (void)dev_y; (void)hip_stream;
-    return fail(EP_EUNSUPPORTED, "bf16 GEMM not built yet");
+    if (M < 0 || N < 0 || K < 0) return fail(EP_EINVAL, "negative size");
+    if (M == 0 || N == 0) return EP_OK;
+    if (!dev_x || !dev_w || !dev_y) return fail(EP_EINVAL, "null pointer");
+    if (K % 8 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(EP_EINVAL, "K must be a multiple of 8");
+    if ((reinterpret_cast<uintptr_t>(dev_x) | reinterpret_cast<uintptr_t>(dev_w)) & 15)
+        return fail(EP_EINVAL, "X and W must be 16-byte aligned");
+    ep::GemmArgs g{static_cast<const uint16_t*>(dev_x), static_cast<const uint16_t*>(dev_w), nullptr,
+                   static_cast<uint16_t*>(dev_y), (int)M, (int)N, (int)K, (int)K, (int)K, (int)N};
+    hipError_t e = ep::launch_gemm(g, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "gemm launch");
+    return EP_OK;
+}
+
+// Compressed linear forward. The weight is decoded once per call, one slice of output rows at a
+// time, into a scratch buffer of at most kSliceBytes (so it stays in the Infinity Cache between
+// the decode and the GEMM that reads it), and each slice's GEMM writes its columns of Y.
+ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias, void* dev_y,
+                            void* hip_stream) {
+    constexpr size_t kSliceBytes = 32u << 20;
+    if (!w) return fail(EP_EINVAL, "null handle");
+    if (w->view.mode != EP_MODE_LOSSY_E8) return fail(EP_EUNSUPPORTED, "the linear forward takes a lossy stream");
+    const int64_t N = w->view.rows, K = w->view.cols;
+    if (M < 0) return fail(EP_EINVAL, "negative M");
+    if (M == 0 || N == 0) return EP_OK;
+    if (!dev_x || !dev_y) return fail(EP_EINVAL, "null pointer");
+    if (K % 8 || M > INT32_MAX) return fail(EP_EINVAL, "in_features must be a multiple of 8");
+    if (reinterpret_cast<uintptr_t>(dev_x) & 15) return fail(EP_EINVAL, "X must be 16-byte aligned");
+    ep_handle* h = const_cast<ep_handle*>(w);
+    const int tr = w->view.tile_rows;
+    int64_t slice = (int64_t)(kSliceBytes / (2 * (size_t)K)) / tr * tr;
+    if (slice < tr) slice = tr;
+    if (slice > N) slice = (N + tr - 1) / tr * tr;
+    const size_t need = (size_t)slice * (size_t)K * 2;
+    if (h->scratch_bytes < need) {
+        if (h->scratch) (void)hipFree(h->scratch);
+        h->scratch = nullptr;
+        h->scratch_bytes = 0;
+        hipError_t e = hipMalloc(reinterpret_cast<void**>(&h->scratch), need);
+        if (e != hipSuccess) return hip_fail(e, "hipMalloc for the decoded weight slice");
+        h->scratch_bytes = need;
+    }
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const ep::MatDesc full = desc_for(w, ep::CT_BF16, h->scratch, nullptr);
+    for (int64_t r0 = 0; r0 < N; r0 += slice) {
+        const int64_t rows = std::min<int64_t>(slice, N - r0);
+        ep::MatDesc d = full;                  // rows r0 .. r0 + rows of the weight
+        d.index += (size_t)(r0 / tr) * w->view.tiles_c;
+        d.row_scale += r0;
+        d.row_qmax += r0;
+        d.rows = (uint32_t)rows;
+        hipError_t e = ep::launch_group(&d, 1, 0, s);
+        if (e != hipSuccess) return hip_fail(e, "slice decode launch");
+        ep::GemmArgs g{static_cast<const uint16_t*>(dev_x), h->scratch,
+                       dev_bias ? static_cast<const uint16_t*>(dev_bias) + r0 : nullptr,
+                       static_cast<uint16_t*>(dev_y) + r0, (int)M, (int)rows, (int)K, (int)K, (int)K, (int)N};
+        e = ep::launch_gemm(g, s);
+        if (e != hipSuccess) return hip_fail(e, "slice gemm launch");
+    }
+    return EP_OK;
 }
 
 }  // extern "C"

@@ -1,0 +1,108 @@
+"""GPU tests of the BF16 MFMA GEMM and of the compressed linear forward (decoding fused into the
+layer's forward, "EntroPack PyTorch Guide", section "Replace one linear layer before a whole
+model"), through the C ABI.
+
+Reference: fp32 GEMM on the CPU of the BF16 inputs (exact in fp32) and, for the linear forward,
+of the oracle-decoded BF16 weight; the bar is relative L2 error <= 2e-2 (BF16 output rounding
+alone is about 2e-3)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import decode_tile_interleaved_rans_amd as ep
+from decode_tile_interleaved_rans_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def rel_l2(got, want):
+    got = got.astype(np.float64)
+    want = want.astype(np.float64)
+    return float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30))
+
+
+def bf16_tensor(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 256, 512), (256, 384, 1024), (130, 200, 264), (1, 8, 8), (300, 1000, 776)])
+def test_gemm_bf16_matches_fp32(M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    x = W.to_bf16_bits(rng.normal(0, 1, (M, K)))
+    w = W.to_bf16_bits(rng.normal(0, 0.05, (N, K)))
+    X, Wt = bf16_tensor(x).cuda(), bf16_tensor(w).cuda()
+    y = ep.gemm_bf16(X, Wt)
+    torch.cuda.synchronize()
+    ref = W.bf16_bits_to_f32(x) @ W.bf16_bits_to_f32(w).T
+    assert rel_l2(y.float().cpu().numpy(), ref) < 5e-3
+
+
+def test_gemm_bf16_prefill_shape_sampled_rows():
+    M, N, K = 4096, 8192, 8192
+    rng = np.random.default_rng(9)
+    X = torch.randn(M, K, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+    Wt = (0.02 * torch.randn(N, K, generator=torch.Generator().manual_seed(2))).to(torch.bfloat16)
+    y = ep.gemm_bf16(X.cuda(), Wt.cuda())
+    torch.cuda.synchronize()
+    rows = rng.choice(M, 48, replace=False)
+    ref = X[rows].float() @ Wt.float().T
+    assert rel_l2(y[rows].float().cpu().numpy(), ref.numpy()) < 5e-3
+
+
+def linear_case(M, N, K, target, seed, bias=False):
+    rng = np.random.default_rng(seed)
+    w = (0.02 * rng.standard_t(5, (N, K))).astype(np.float32)
+    x = W.to_bf16_bits(rng.normal(0, 1, (M, K)))
+    s, _ = ep.compress(w, target)
+    layer = ep.CompressedLinear(s, bias=None)
+    b = None
+    if bias:
+        b = bf16_tensor(W.to_bf16_bits(rng.normal(0, 0.1, N))).cuda()
+        layer.bias = b
+    y = layer(bf16_tensor(x).cuda())
+    torch.cuda.synchronize()
+    layer.handle.check()
+    w_hat = W.bf16_bits_to_f32(oracle.decompress(s, oracle.BF16, n_threads=16)[0])
+    return y.float().cpu().numpy(), W.bf16_bits_to_f32(x), w_hat, (b.float().cpu().numpy() if bias else None)
+
+
+@pytest.mark.parametrize("M,N,K,target", [(16, 512, 1024, 4.0), (256, 768, 2048, 4.5), (33, 300, 264, 3.0),
+                                          (4, 4096, 512, 6.0)])
+def test_linear_forward_matches_decoded_fp32_gemm(M, N, K, target):
+    y, x, w_hat, _ = linear_case(M, N, K, target, seed=M + N)
+    assert rel_l2(y, x @ w_hat.T) < 2e-2
+
+
+def test_linear_forward_with_bias_and_multi_slice():
+    # 5000 x 4096 weight: 32 MiB slices of 4096 rows -> two slices, the last one ragged
+    M, N, K = 64, 5000, 4096
+    y, x, w_hat, b = linear_case(M, N, K, 4.0, seed=3, bias=True)
+    assert rel_l2(y, x @ w_hat.T + b[None, :]) < 2e-2
+
+
+def test_linear_forward_prefill_sampled_rows():
+    M, N, K = 4096, 8192, 8192
+    w, xb = W.prefill_case()
+    s, bpp = ep.compress(w, 4.5, dtype=ep.BF16)
+    layer = ep.CompressedLinear(s)
+    X = bf16_tensor(xb).cuda()
+    y = layer(X)
+    torch.cuda.synchronize()
+    layer.handle.check()
+    w_hat = W.bf16_bits_to_f32(oracle.decompress(s, oracle.BF16, n_threads=16)[0])
+    rows = np.random.default_rng(4).choice(M, 32, replace=False)
+    ref = W.bf16_bits_to_f32(xb[rows]) @ w_hat.T
+    assert rel_l2(y[rows].float().cpu().numpy(), ref) < 2e-2
+
+
+def test_from_linear_roundtrip():
+    lin = torch.nn.Linear(1024, 512, bias=True)
+    layer = ep.CompressedLinear.from_linear(lin, 5.0)
+    x = torch.randn(8, 1024)
+    y = layer(x.cuda().to(torch.bfloat16))
+    torch.cuda.synchronize()
+    ref = lin(x).detach()
+    # lossy 5 bpp weights: the layer output stays close to the original layer
+    assert rel_l2(y.float().cpu().numpy(), ref.numpy()) < 0.05
+    assert layer.actual_bpp > 5.0
