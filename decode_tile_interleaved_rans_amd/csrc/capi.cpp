@@ -297,11 +297,13 @@ ep_status ep_gemm_bf16(const void* dev_x, const void* dev_w, int64_t M, int64_t 
 }
 
 // Compressed linear forward. The weight is decoded once per call, one slice of output rows at a
-// time, into a scratch buffer of at most kSliceBytes (so it stays in the Infinity Cache between
-// the decode and the GEMM that reads it), and each slice's GEMM writes its columns of Y.
+// time, into a scratch buffer of at most kSliceBytes, and each slice's GEMM writes its columns of
+// Y. A slice is large enough to keep every CU's decode block busy (>= 16 tile pairs per CU at
+// K = 8192) and small enough to stay in the 256 MB Infinity Cache between the decode that writes
+// it and the GEMM that reads it.
 ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias, void* dev_y,
                             void* hip_stream) {
-    constexpr size_t kSliceBytes = 32u << 20;
+    constexpr size_t kSliceBytes = 64u << 20;
     if (!w) return fail(EP_EINVAL, "null handle");
     if (w->view.mode != EP_MODE_LOSSY_E8) return fail(EP_EUNSUPPORTED, "the linear forward takes a lossy stream");
     const int64_t N = w->view.rows, K = w->view.cols;
