@@ -9,9 +9,11 @@ in the 256 MB Infinity Cache.
 
 Prints one JSON line (rank 0, N = 1): decoded-weight GB/s (container bytes written per second),
 the roofline of the dominant kernel (lossy decode to BF16) from HIP events on the launch stream,
-and the oracle's CPU decode of one step on the host cores as a reported baseline.
+the fused decode + GEMM forward of an 8192 x 8192 weight at 4.5 bpp against the plain BF16 GEMM
+(M = 4096, 256, 16), and the oracle's CPU decode of one step on the host cores as a reported
+baseline.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-gemm]
 """
 from __future__ import annotations
 
@@ -90,12 +92,76 @@ def cpu_baseline(items, budget_s: float = 10.0):
                       f"oracle with {cores} threads in {dt:.1f} s"}
 
 
+def fused_gemm_section(torch, ep, reps: int = 10):
+    """Fused decode + BF16 MFMA GEMM against the plain BF16 GEMM on the uncompressed weight.
+
+    Workload: W = 0.02 t5 bf16 [8192, 8192] coded at 4.5 bpp, X ~ N(0, 1) bf16 [M, 8192],
+    Y = X W^T in BF16 with fp32 accumulation, M = 4096 (prefill), 256 and 16. Each rep is timed
+    with HIP events on the launch stream and a 1 GiB buffer is rewritten between reps, so neither
+    the weight nor the activations are served from the Infinity Cache."""
+    from decode_tile_interleaved_rans_amd import workloads as W
+    w, xb = W.prefill_case()
+    t0 = time.time()
+    s, bpp = ep.compress(w, 4.5, dtype=ep.BF16)
+    log(f"encoded 8192x8192 at target 4.5: actual {bpp:.4f} bpp in {time.time() - t0:.2f} s")
+    layer = ep.CompressedLinear(s)
+    Wt = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda()
+    Xf = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
+    N, K = Wt.shape
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        ds = []
+        for _ in range(reps):
+            flush.fill_(1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            fn()
+            b.record(st)
+            ds.append((a, b))
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in ds)
+        return us[len(us) // 2], us[0]
+
+    wdec = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    t_dec, _ = timed(lambda: layer.handle.decompress_into(wdec))
+    layer.handle.check()
+    out = {"workload": "W 0.02 t5 bf16 [8192, 8192] at 4.5 bpp, X N(0,1) bf16 [M, 8192], Y = X W^T bf16, "
+                       "fp32 accumulate",
+           "actual_bpp": round(bpp, 4), "stream_bytes": len(s), "decode_full_us": round(t_dec, 2),
+           "reps": reps, "timing": "median of per-rep HIP events, 1 GiB cache flush between reps"}
+    for M in (4096, 256, 16):
+        X = Xf[:M].contiguous()
+        t_f, t_f_min = timed(lambda: layer(X))
+        t_o, _ = timed(lambda: ep.gemm_bf16(X, Wt))
+        t_t, _ = timed(lambda: torch.matmul(X, Wt.t()))
+        layer.handle.check()
+        fl = 2.0 * M * N * K
+        out[f"M{M}"] = {
+            "fused_us": round(t_f, 2), "fused_min_us": round(t_f_min, 2), "own_gemm_us": round(t_o, 2),
+            "torch_matmul_us": round(t_t, 2),
+            "overhead_vs_own_gemm": round(t_f / t_o - 1, 4), "overhead_vs_torch": round(t_f / t_t - 1, 4),
+            "fused_tflops": round(fl / t_f / 1e6, 1), "own_gemm_tflops": round(fl / t_o / 1e6, 1),
+            "torch_tflops": round(fl / t_t / 1e6, 1),
+            # HBM-bound view for small M: X + compressed W + Y
+            "fused_hbm_frac": round((2 * M * K + len(s) + 2 * M * N) / t_f / 1e3 / HBM_PEAK_GBS, 4),
+        }
+        log(f"fused GEMM M={M}: fused {t_f:.1f} us, own GEMM {t_o:.1f} us, torch {t_t:.1f} us")
+    del flush, wdec, Wt, Xf, layer
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-gemm", action="store_true", help="skip the fused decode + GEMM measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 256 MiB device copy first (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -181,6 +247,11 @@ def main():
                 "launch_us_min": round(min(durs) * 1e6, 2)}
     per_item = {items[i][0]: {"actual_bpp": round(items[i][3], 4), "stream_bytes": len(items[i][1])}
                 for i in range(len(items))}
+    fused = None
+    if not args.no_gemm:
+        sets.clear()
+        torch.cuda.empty_cache()
+        fused = fused_gemm_section(torch, ep)
     cpu = None
     if not args.no_cpu:
         log("timing the oracle on the host cores")
@@ -198,6 +269,7 @@ def main():
         "wall_s": round(wall, 4),
         "roofline": roofline,
         "per_decode": per_item,
+        "fused_gemm": fused,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
