@@ -48,10 +48,11 @@ std::vector<uint8_t> build_tables(const ep::StreamView& v) {
     const size_t M = (size_t)1 << n;
     std::vector<uint8_t> blob(ep::table_blob_bytes(v.n_tables, n), 0);
     uint8_t* lut = blob.data();
-    uint32_t* fc = reinterpret_cast<uint32_t*>(blob.data() + ((size_t)v.n_tables << n));
-    int16_t* val = reinterpret_cast<int16_t*>(blob.data() + ((size_t)v.n_tables << n) + (size_t)v.n_tables * 1024);
+    uint32_t* ent = reinterpret_cast<uint32_t*>(blob.data() + ((size_t)v.n_tables << n));
     for (int t = 0; t < v.n_tables; ++t) {
         const ep::Table& T = v.tables[t];
+        const bool coord = v.mode != EP_MODE_LOSSLESS && t > 0;
+        const uint32_t base = coord ? (uint32_t)((t - 1) & 1) << n : 0u;
         uint32_t c = 0;
         for (int s = 0; s < 256; ++s) {
             const uint32_t f = T.freq[s];
@@ -59,8 +60,8 @@ std::vector<uint8_t> build_tables(const ep::StreamView& v) {
             if (v.mode == EP_MODE_LOSSLESS) value = s;
             else if (t == 0) value = T.lo + s;
             else value = (s == ep::kEscape || s >= T.width) ? 0 : 2 * (T.lo + s) + ((t - 1) & 1);
-            fc[(size_t)t * 256 + s] = f | c << 16;
-            val[(size_t)t * 256 + s] = (int16_t)value;
+            ent[2 * ((size_t)t * 256 + s)] = f | (coord && s == ep::kEscape ? 0x80000000u : 0u);
+            ent[2 * ((size_t)t * 256 + s) + 1] = ((c + base) & 0xFFFFu) | (uint32_t)(uint16_t)(int16_t)value << 16;
             for (uint32_t k = 0; k < f; ++k) lut[(size_t)t * M + c + k] = (uint8_t)s;
             c += f;
         }
@@ -276,7 +277,7 @@ ep_status ep_handle_check(ep_handle* h, void* hip_stream) {
         e = hipMemsetAsync(h->dev + h->err_off, 0, sizeof(int), s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         return fail(EP_EDEVICE, std::string("decode kernel flagged the stream:") + (flag & 1 ? " word count" : "") +
-                                    (flag & 2 ? " final state" : ""));
+                                    (flag & 2 ? " final state" : "") + (flag & 4 ? " kernel LDS layout" : ""));
     }
     return EP_OK;
 }

@@ -14,16 +14,17 @@
 // row's scale. A launch covers up to 32 matrices; each block of 16 waves serves one matrix,
 // stages that matrix's decode tables in LDS, and walks its range of tile pairs.
 //
-// Word staging. Every half-wave keeps a 1024-word LDS ring of its tile's word stream, filled by
+// Word staging. Every half-wave keeps a 512-word LDS ring of its tile's word stream, filled by
 // coalesced 512-byte chunk loads that are issued one chunk ahead, so the serial rANS chain only
-// ever waits on LDS. Before each block row the ring is topped up until it holds more than the
-// most a row can consume (9 steps x 64 words), so the steps need no bounds checks; a damaged
-// stream can only read stale ring words, and is caught by the end-of-tile checks. Lossless tiles
-// top up before every element (at most 4 steps x 32 words).
+// ever waits on LDS. Every three steps the ring is topped up until it holds more than three
+// steps can consume (3 x 64 words), so the steps need no bounds checks; a damaged stream can
+// only read stale ring words, and is caught by the end-of-tile checks. Lossless tiles top up
+// before every element (at most 4 steps x 32 words).
 //
-// Per decoding step every lane looks up its slot in the LDS table, updates its state, and lanes
-// whose state fell below 2^16 take the next word of their tile; a wave ballot, shifted to the
-// lane's half and popcounted below the lane, gives each refilling lane its word index. Lanes
+// Per decoding step every lane looks up its slot in the LDS LUT (one byte read), then reads the
+// symbol's 8-byte entry (frequency, cumulative frequency, decoded value) and updates its state;
+// lanes whose state fell below 2^16 take the next word of their tile: a wave ballot, shifted to
+// the lane's half and popcounted below the lane, gives each refilling lane its word index. Lanes
 // that decoded the escape symbol then read their raw value the same way.
 #include <hip/hip_runtime.h>
 
@@ -41,12 +42,14 @@ namespace {
 constexpr uint32_t kLow = 1u << 16;
 constexpr int kWaves = 16;                 // waves per block
 constexpr int kRingWords = 1024;           // per tile
+constexpr int kTopUps = kRingWords >= 1024 ? 1 : 3;   // ring top-ups per block row (see top_up)
 constexpr int kRingBytes = 2 * kRingWords;
 constexpr int kChains = 1;                 // tile pairs decoded together by a wave (see lossy_pairs)
 constexpr int kChunkDw = 128;              // one chunk: 32 lanes x 4 dwords = 256 words
 constexpr int kChunkWords = 2 * kChunkDw;
 constexpr int kErrWords = 1;               // words ran out or were left over
 constexpr int kErrState = 2;               // a final state differs from 2^16
+constexpr int kErrLayout = 4;              // the kernel's LDS does not start at address 0
 
 // ----------------------------------------------------------------------------- containers
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -88,23 +91,29 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
 }
 
 // ----------------------------------------------------------------------------- matrix setup
+typedef const __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
 struct Tables {
     const uint8_t* lut;
-    const uint32_t* fc;
-    const int16_t* val;
+    const uint2* ent;
 };
 
-__device__ __forceinline__ Tables stage_tables(const MatDesc& M, uint8_t* smem) {
+__device__ __forceinline__ Tables stage_tables(const MatDesc& M, uint8_t* smem, bool lossy) {
     const int n = M.prob_bits;
-    const size_t bytes = table_blob_bytes(M.n_tables, n);
-    const uint4* src = reinterpret_cast<const uint4*>(M.tables);
+    const int skip = lossy ? 1 : 0;                 // the coset table stays out of LDS
+    const int nt = M.n_tables - skip;
+    const size_t lut_bytes = (size_t)nt << n, ent_bytes = (size_t)nt * 2048;
+    const uint4* lut_src = reinterpret_cast<const uint4*>(M.tables + ((size_t)skip << n));
+    const uint4* ent_src = reinterpret_cast<const uint4*>(M.tables + ((size_t)M.n_tables << n) + (size_t)skip * 2048);
     uint4* dst = reinterpret_cast<uint4*>(smem);
-    for (size_t i = threadIdx.x; i < bytes / 16; i += blockDim.x) dst[i] = src[i];
+    for (size_t i = threadIdx.x; i < lut_bytes / 16; i += blockDim.x) dst[i] = lut_src[i];
+    for (size_t i = threadIdx.x; i < ent_bytes / 16; i += blockDim.x) dst[lut_bytes / 16 + i] = ent_src[i];
     __syncthreads();
     Tables T;
     T.lut = smem;
-    T.fc = reinterpret_cast<const uint32_t*>(smem + ((size_t)M.n_tables << n));
-    T.val = reinterpret_cast<const int16_t*>(smem + ((size_t)M.n_tables << n) + (size_t)M.n_tables * 1024);
+    T.ent = reinterpret_cast<const uint2*>(smem + lut_bytes);
     return T;
 }
 
@@ -116,7 +125,7 @@ struct Tile {
     uint32_t nwords;       // words of the tile (pad word included)
     uint32_t ndw;          // the same in dwords
     uint32_t gdw;          // byte offset of the tile's words in the payload (buffer loads)
-    uint16_t* ring;        // this half's LDS ring
+    lds_u16* ring;         // this half's LDS ring
     uint32_t pf[4];        // next chunk, loaded ahead
     uint32_t below;        // lanes below this one within the half
     uint32_t sh;           // 0 for the low half, 32 for the high half
@@ -139,7 +148,7 @@ __device__ __forceinline__ void load_chunk(const Tile& t, __amdgpu_buffer_rsrc_t
     }
 }
 __device__ __forceinline__ void store_chunk(Tile& t, uint32_t chunk, const uint32_t* src) {
-    uint32_t* ring = reinterpret_cast<uint32_t*>(t.ring);
+    lds_u32* ring = (lds_u32*)t.ring;
     const uint32_t base = (chunk * kChunkDw) & (kRingWords / 2 - 1);   // kRingWords / 2 dwords
 #pragma unroll
     for (int i = 0; i < 4; ++i) ring[base + t.l + 32 * i] = src[i];
@@ -173,9 +182,8 @@ __device__ __forceinline__ void begin_tile(const MatDesc& M, __amdgpu_buffer_rsr
     __builtin_amdgcn_wave_barrier();
 }
 
-// Keep more than one block row's worst-case consumption (9 steps x 64 words) in the ring: after
-// this, the ring holds more than kRingWords - kChunkWords = 768 unread words, or the rest of the
-// tile.
+// Keep more than three steps' worst-case consumption (3 x 64 words) in the ring: after this, the
+// ring holds more than kRingWords - kChunkWords = 256 unread words, or the rest of the tile.
 __device__ __forceinline__ void top_up(Tile& t, __amdgpu_buffer_rsrc_t rs) {
     while (t.fill < t.nwords && t.fill - t.pos <= kRingWords - kChunkWords) {
         store_chunk(t, t.fill / kChunkWords, t.pf);
@@ -202,15 +210,59 @@ __device__ __forceinline__ void refill(Tile& t) {
     t.x = need ? (t.x << 16) | w : t.x;
 }
 
-// One rANS decode step: lut/fc are the LUT and frequency table of the step's table; returns the
-// symbol. f <= 2^12 and x >> N < 2^22 fit the 24-bit multiplier.
+// refill() for C chains, written phase by phase so that the chains' LDS reads are in flight
+// together.
+template <int C>
+__device__ __forceinline__ void refill_all(Tile* t) {
+    bool need[C];
+    uint32_t idx[C], w[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) need[c] = t[c].x < kLow;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const uint32_t mine = (uint32_t)(__ballot(need[c]) >> t[c].sh);
+        idx[c] = t[c].pos + __popc(mine & t[c].below);
+        t[c].pos += __popc(mine);
+    }
+    // volatile: read by every lane (always in range), so the compiler keeps the selects below
+    // instead of branching around the reads
+#pragma unroll
+    for (int c = 0; c < C; ++c) w[c] = *(volatile lds_u16*)(t[c].ring + (idx[c] & (kRingWords - 1)));
+#pragma unroll
+    for (int c = 0; c < C; ++c) t[c].x = need[c] ? (t[c].x << 16) | w[c] : t[c].x;
+}
+
+// One rANS decode step. The lookup address is the slot or'ed into `base` (the LDS offset of the
+// lane's LUT group, a multiple of 2^N), `lut` adds the step's table (an absolute LDS byte address:
+// the LUTs start at LDS address 0, which the kernel checks, so this is an immediate offset), and
+// `ent` points at the entries of the same table; the entry's cumulative frequency carries `base`,
+// so slot - c is the address minus that field. Returns the symbol; `v` receives the entry's
+// second word (value in the high half). f <= 2^12 and x >> N < 2^22 fit the 24-bit multiplier.
 template <int N>
-__device__ __forceinline__ uint32_t rans_step(Tile& t, const uint8_t* lut, const uint32_t* fc) {
-    const uint32_t slot = t.x & ((1u << N) - 1u);
-    const uint32_t s = lut[slot];
-    const uint32_t e = fc[s];
-    t.x = __umul24(e & 0xFFFFu, t.x >> N) + slot - (e >> 16);     // SDWA word selects
+__device__ __forceinline__ uint32_t rans_step(Tile& t, uint32_t lut, uint32_t base, const uint2* ent, uint32_t& v) {
+    uint32_t a;                                         // (x & (2^N - 1)) | base in one instruction
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(a) : "v"(t.x), "s"((1u << N) - 1u), "v"(base));
+    const uint32_t s = ((lds_u8*)(size_t)lut)[a];      // LDS byte address lut + a
+    const uint2 e = ent[s];
+    t.x = __umul24(e.x, t.x >> N) + (a - (e.y & 0xFFFFu));
+    v = e.y;
     return s;
+}
+
+// rans_step() for C chains at the same step, phase by phase (see refill_all).
+// Returns each chain's entry: .x = frequency (bit 31: escape symbol), .y = value << 16 | c + base.
+template <int N, int C>
+__device__ __forceinline__ void rans_steps(Tile* t, uint32_t lut, const uint32_t* base, const uint2* const* ent,
+                                           uint2* e) {
+    uint32_t a[C], s[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(a[c]) : "v"(t[c].x), "s"((1u << N) - 1u), "v"(base[c]));
+#pragma unroll
+    for (int c = 0; c < C; ++c) s[c] = ((lds_u8*)(size_t)lut)[a[c]];
+#pragma unroll
+    for (int c = 0; c < C; ++c) e[c] = ent[c][s[c]];
+#pragma unroll
+    for (int c = 0; c < C; ++c) t[c].x = __umul24(e[c].x, t[c].x >> N) + (a[c] - (e[c].y & 0xFFFFu));
 }
 
 // The coset table has at most two symbols (0 and 1, cumulative 0 and f0), decoded arithmetically.
@@ -240,35 +292,37 @@ __device__ __forceinline__ void init_lane(Tile& t, uint8_t* ring_base, int chain
     t.sh = (uint32_t)(lane & 32);
     t.below = (1u << t.l) - 1u;
     const int ring = ((threadIdx.x >> 6) * kChains + chain) * 2 + (lane >> 5);
-    t.ring = reinterpret_cast<uint16_t*>(ring_base + ring * kRingBytes);
+    t.ring = (lds_u16*)(ring_base + ring * kRingBytes);
     t.err = 0;
     t.valid = false;
 }
 
 // ----------------------------------------------------------------------------- stores
+// Decoded coordinates are carried as fp32 values (exact: |q| < 2^17).
 template <int CT>
 struct Conv;
 template <>
 struct Conv<CT_BF16> {
     using T = uint16_t;
-    __device__ static uint32_t f(int32_t q, float alpha, float, uint32_t, uint32_t) { return bf16_rne((float)q * alpha); }
+    __device__ static uint32_t f(float q, float alpha, float, uint32_t, uint32_t) { return bf16_rne(q * alpha); }
 };
 template <>
 struct Conv<CT_F16> {
     using T = uint16_t;
-    __device__ static uint32_t f(int32_t q, float alpha, float, uint32_t, uint32_t) { return f16_rne((float)q * alpha); }
+    __device__ static uint32_t f(float q, float alpha, float, uint32_t, uint32_t) { return f16_rne(q * alpha); }
 };
 template <>
 struct Conv<CT_F8E4M3> {
     using T = uint8_t;
-    __device__ static uint32_t f(int32_t q, float, float h, uint32_t, uint32_t) { return e4m3_rne_sat((float)q * h); }
+    __device__ static uint32_t f(float q, float, float h, uint32_t, uint32_t) { return e4m3_rne_sat(q * h); }
 };
 template <>
 struct Conv<CT_I8> {
     using T = uint8_t;
     // round-half-away(q / k) = floor((2|q| + k) / 2k), by a multiply with ceil(2^32 / 2k); exact
     // because (2|q| + k) * 2k < 2^32.
-    __device__ static uint32_t f(int32_t q, float, float, uint32_t k, uint32_t magic) {
+    __device__ static uint32_t f(float qf, float, float, uint32_t k, uint32_t magic) {
+        const int32_t q = (int32_t)qf;
         const uint32_t a = (uint32_t)(q < 0 ? -q : q);
         const int32_t v = (int32_t)__umulhi(2u * a + k, magic);
         return (uint32_t)(uint8_t)(int8_t)(q < 0 ? -v : v);
@@ -277,11 +331,11 @@ struct Conv<CT_I8> {
 template <>
 struct Conv<CT_Q16> {
     using T = uint16_t;
-    __device__ static uint32_t f(int32_t q, float, float, uint32_t, uint32_t) { return (uint32_t)(uint16_t)(int16_t)q; }
+    __device__ static uint32_t f(float q, float, float, uint32_t, uint32_t) { return (uint32_t)(uint16_t)(int16_t)(int32_t)q; }
 };
 
 template <int CT>
-__device__ __forceinline__ void store_block(const MatDesc& M, uint32_t row, uint32_t col0, const int32_t* q, float alpha,
+__device__ __forceinline__ void store_block(const MatDesc& M, uint32_t row, uint32_t col0, const float* q, float alpha,
                                    float h, uint32_t k, uint32_t magic) {
     using T = typename Conv<CT>::T;
     T* out = static_cast<T*>(M.out) + (size_t)row * M.cols;
@@ -290,7 +344,7 @@ __device__ __forceinline__ void store_block(const MatDesc& M, uint32_t row, uint
         // two values per v_cvt_pk_{bf16,f16}_f32 (round to nearest even) of the rounded fp32 products
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
-            f32x2 p = {materialize((float)q[j] * alpha), materialize((float)q[j + 1] * alpha)};
+            f32x2 p = {materialize(q[j] * alpha), materialize(q[j + 1] * alpha)};
             uint32_t pk;
             if constexpr (CT == CT_BF16) pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
             else pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, f16x2));
@@ -325,11 +379,11 @@ struct PairRows {
 };
 
 template <int CT>
-__device__ __forceinline__ void begin_pair(const MatDesc& M, __amdgpu_buffer_rsrc_t rs, uint64_t pair, Tile& t,
-                                           PairRows& P) {
+__device__ __forceinline__ void begin_pair(const MatDesc& M, __amdgpu_buffer_rsrc_t rs, uint64_t pair, bool live,
+                                           Tile& t, PairRows& P) {
     const uint32_t tr = (uint32_t)(pair / M.pairs_c);
     P.tc = 2 * (uint32_t)(pair % M.pairs_c) + (t.sh ? 1u : 0u);
-    t.valid = P.tc < M.tiles_c;
+    t.valid = live && P.tc < M.tiles_c;
     begin_tile(M, rs, (uint64_t)tr * M.tiles_c + P.tc, t);
     P.row0 = tr * M.tile_rows;
     const uint32_t my_row = P.row0 + t.l;
@@ -340,7 +394,7 @@ __device__ __forceinline__ void begin_pair(const MatDesc& M, __amdgpu_buffer_rsr
 }
 
 template <int CT>
-__device__ __forceinline__ void store_row(const MatDesc& M, const Tile& t, const PairRows& P, int rr, const int32_t* q,
+__device__ __forceinline__ void store_row(const MatDesc& M, const Tile& t, const PairRows& P, int rr, const float* q,
                                           float h) {
     const uint32_t row = P.row0 + rr;
     const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, P.sc_l), rr));
@@ -362,52 +416,59 @@ __device__ __forceinline__ void store_row(const MatDesc& M, const Tile& t, const
 // Decode C tile pairs side by side (C independent rANS chains per lane, interleaved by the
 // compiler to hide LDS latency).
 template <int CT, int N, int C>
-__device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Tile* t, const uint64_t* pair) {
+__device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Tile* t, const uint64_t* pair,
+                                          uint64_t pend) {
     const float h = M.step * 0.5f;
-    const uint32_t f0 = T.fc[0] & 0xFFFFu, f1 = T.fc[1] & 0xFFFFu;    // coset table
-    const int lo0 = T.val[0];
+    const uint2* coset = reinterpret_cast<const uint2*>(M.tables + ((size_t)M.n_tables << N));   // table 0
+    const uint32_t f0 = coset[0].x, f1 = coset[1].x;
+    const int lo0 = (int32_t)coset[0].y >> 16;
     const __amdgpu_buffer_rsrc_t rs = payload_rsrc(M);
     PairRows P[C];
 #pragma unroll
-    for (int c = 0; c < C; ++c) begin_pair<CT>(M, rs, pair[c], t[c], P[c]);
+    for (int c = 0; c < C; ++c) begin_pair<CT>(M, rs, pair[c], pair[c] < pend, t[c], P[c]);
     for (int rr = 0; rr < M.tile_rows; ++rr) {
         int b[C];
-        const uint8_t* lut_b[C];
-        const uint32_t* fc_b[C];
-        const int16_t* val_b[C];
-        int32_t q[C][8];
+        uint32_t base[C];
+        const uint2* ent_b[C];
+        float q[C][8];
 #pragma unroll
         for (int c = 0; c < C; ++c) top_up(t[c], rs);
 #pragma unroll
+        for (int c = 0; c < C; ++c) b[c] = lo0 + (int)coset_step<N>(t[c], f0, f1);
+        refill_all<C>(t);
+#pragma unroll
         for (int c = 0; c < C; ++c) {
-            b[c] = lo0 + (int)coset_step<N>(t[c], f0, f1);
-            refill(t[c]);
             // tables 1 + 2j + b for this lane's coset; j selects a compile-time offset
-            lut_b[c] = T.lut + ((1 + b[c]) << N);
-            fc_b[c] = T.fc + (1 + b[c]) * 256;
-            val_b[c] = T.val + (1 + b[c]) * 256;
+            base[c] = (uint32_t)b[c] << N;
+            ent_b[c] = T.ent + b[c] * 256;
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-
+            if (kTopUps == 3 && (j == 2 || j == 5)) {
+#pragma unroll
+                for (int c = 0; c < C; ++c) top_up(t[c], rs);
+            }
             // all chains' step j in one basic block, so the scheduler can interleave the chains;
             // the rare escapes branch once for all chains
-            uint32_t sy[C];
-            bool esc[C], any = false;
+            uint2 e[C];
+            const uint2* ent_j[C];
+            bool esc[C];
+            uint64_t any = 0;
 #pragma unroll
-            for (int c = 0; c < C; ++c) sy[c] = rans_step<N>(t[c], lut_b[c] + ((2 * j) << N), fc_b[c] + 2 * j * 256);
+            for (int c = 0; c < C; ++c) ent_j[c] = ent_b[c] + 2 * j * 256;
+            rans_steps<N, C>(t, (2 * j) << N, base, ent_j, e);
+            refill_all<C>(t);
 #pragma unroll
             for (int c = 0; c < C; ++c) {
-                refill(t[c]);
-                q[c][j] = val_b[c][2 * j * 256 + sy[c]];
-                esc[c] = sy[c] == 255u;
-                any = any || esc[c];
+                q[c][j] = (float)((int32_t)e[c].y >> 16);
+                esc[c] = (int32_t)e[c].x < 0;
+                any |= __ballot(esc[c]);
             }
-            if (__ballot(any)) {
+            if (any) {
 #pragma unroll
                 for (int c = 0; c < C; ++c) {
                     const uint32_t w = take_words(t[c], esc[c]);
-                    if (esc[c]) q[c][j] = 2 * (int32_t)(int16_t)w + b[c];
+                    if (esc[c]) q[c][j] = (float)(2 * (int32_t)(int16_t)w + b[c]);
                 }
             }
         }
@@ -418,12 +479,17 @@ __device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Til
     for (int c = 0; c < C; ++c) end_tile(t[c]);
 }
 
-// Pairs [p0, p1) of one matrix: wave w takes p0 + w, p0 + w + 16, ... One chain per wave: two
-// interleaved chains (twice the rings, a top-up every three steps) measured slower on gfx950,
-// where the LDS lookups rather than their latency bound the loop.
+// Pairs [p0, p1) of one matrix: wave w decodes pairs p0 + w and p0 + w + 16 together, then
+// p0 + w + 32 and p0 + w + 48, ...: two independent chains per lane keep the SIMDs busy while
+// the other chain waits on LDS.
 template <int CT, int N>
 __device__ __forceinline__ void lossy_pairs(const MatDesc& M, const Tables& T, Tile* t, uint64_t p0, uint64_t p1) {
-    for (uint64_t p = p0 + (threadIdx.x >> 6); p < p1; p += kWaves) lossy_run<CT, N, 1>(M, T, t, &p);
+    for (uint64_t p = p0 + (threadIdx.x >> 6); p < p1; p += kChains * kWaves) {
+        uint64_t pr[kChains];
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) pr[c] = p + (uint64_t)c * kWaves;
+        lossy_run<CT, N, kChains>(M, T, t, pr, p1);
+    }
 }
 
 template <int N>
@@ -455,7 +521,8 @@ __device__ __forceinline__ void lossless_pairs(const MatDesc& M, const Tables& T
                 uint32_t acc = 0;
 #pragma unroll
                 for (int pl = 0; pl < P; ++pl) {
-                    const uint32_t s = rans_step<N>(t, T.lut + (pl << N), T.fc + pl * 256);
+                    uint32_t v;
+                    const uint32_t s = rans_step<N>(t, pl << N, 0u, T.ent + pl * 256, v);
                     refill(t);
                     acc = acc << 8 | s;
                 }
@@ -507,6 +574,12 @@ __device__ __forceinline__ void lossless_dispatch(const MatDesc& M, const Tables
 template <bool LOSSY>
 __global__ __launch_bounds__(64 * kWaves) void decode_group(GroupArgs g) {
     extern __shared__ __align__(16) uint8_t smem[];
+    // the lookups address the LUTs absolutely: the dynamic LDS must start at address 0
+    if ((uint32_t)(size_t)(lds_u8*)smem != 0u) {
+        if (threadIdx.x == 0)
+            for (int i = 0; i < g.count; ++i) atomicOr(g.m[i].err, kErrLayout);
+        return;
+    }
     const uint64_t a = (uint64_t)blockIdx.x * (uint64_t)g.block_pairs;
     const uint64_t b = std::min<uint64_t>(a + (uint64_t)g.block_pairs, (uint64_t)g.pair_start[g.count]);
     int mi = 0;
@@ -517,10 +590,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_group(GroupArgs g) {
         const uint64_t end = std::min<uint64_t>(b, (uint64_t)g.pair_start[mi + 1]);
         const MatDesc M = g.m[mi];
         __syncthreads();                            // every wave is done with the previous tables
-        const Tables T = stage_tables(M, smem);
+        const Tables T = stage_tables(M, smem, LOSSY);
         Tile t[kChains];
 #pragma unroll
-        for (int c = 0; c < kChains; ++c) init_lane(t[c], smem + table_blob_bytes(M.n_tables, M.prob_bits), c);
+        for (int c = 0; c < kChains; ++c) init_lane(t[c], smem + lds_table_bytes(M.n_tables, M.prob_bits, LOSSY), c);
         if constexpr (LOSSY) {
             switch (M.prob_bits) {
                 case 10: lossy_dispatch<10>(M, T, t, pos - base, end - base); break;
@@ -574,7 +647,7 @@ hipError_t launch_group(const MatDesc* mats, int count, int mode, hipStream_t st
         g.m[i] = mats[i];
         g.pair_start[i] = (uint32_t)total;
         total += (uint64_t)((mats[i].rows + mats[i].tile_rows - 1) / mats[i].tile_rows) * mats[i].pairs_c;
-        lds = std::max(lds, table_blob_bytes(mats[i].n_tables, mats[i].prob_bits) +
+        lds = std::max(lds, lds_table_bytes(mats[i].n_tables, mats[i].prob_bits, mode == 0) +
                                 (size_t)kWaves * kChains * 2 * kRingBytes);
     }
     g.pair_start[count] = (uint32_t)total;

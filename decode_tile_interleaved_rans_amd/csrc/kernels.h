@@ -35,12 +35,22 @@ struct GroupArgs {
     MatDesc m[kMaxGroup];
 };
 
-// Decode tables of one stream, in device memory and in LDS:
-//   lut [n_tables][2^n] u8   slot -> symbol
-//   fc  [n_tables][256] u32  f | c << 16 (frequency, cumulative frequency)
-//   val [n_tables][256] i16  doubled lattice coordinate 2 (lo + s) + b (lossy), coset (table 0)
+// Decode tables of one stream, in device memory:
+//   lut [n_tables][2^n] u8      slot -> symbol
+//   ent [n_tables][256] 2 x u32 {f | esc << 31, (c + base) | v << 16}: frequency f (bit 31 set
+//                               for the escape symbol of a lossy coordinate table), cumulative
+//                               frequency c, and the decoded value v (int16): the doubled lattice
+//                               coordinate 2 (lo + s) + b of a lossy coordinate table, lo + s of
+//                               the coset table, the byte s of a lossless plane.
+// In LDS a lossy stream keeps only its coordinate tables 1..16 (the two-symbol coset table is
+// decoded arithmetically from its frequencies), LUTs first, so coordinate table 1 + 2j + b has
+// its LUT at LDS address (2j + b) << n. base is b << n for that table and 0 for the others, so
+// that slot - c = address - (c + base) for a lookup address (slot | b << n) + (2j << n).
 __host__ __device__ inline size_t table_blob_bytes(int n_tables, int prob_bits) {
-    return ((size_t)n_tables << prob_bits) + (size_t)n_tables * 256 * 4 + (size_t)n_tables * 256 * 2;
+    return ((size_t)n_tables << prob_bits) + (size_t)n_tables * 256 * 8;
+}
+__host__ __device__ inline size_t lds_table_bytes(int n_tables, int prob_bits, bool lossy) {
+    return table_blob_bytes(lossy ? n_tables - 1 : n_tables, prob_bits);
 }
 
 // Launch one grouped decode (all matrices of the same mode: 0 lossy, 1 lossless).

@@ -140,7 +140,8 @@ ep_status ep_gemm_bf16(const void* dev_x, const void* dev_w, int64_t M, int64_t 
 
 /* Synchronize hip_stream and read the handle's device error flag, which kernels set when a
  * tile's words run out or overrun, or a lane's final rANS state differs from its initial
- * value. EP_EDEVICE if set (the flag is then cleared), else EP_OK. */
+ * value (or, as an internal consistency check, when a decode kernel finds its LDS tables
+ * misplaced). EP_EDEVICE if set (the flag is then cleared), else EP_OK. */
 ep_status ep_handle_check(ep_handle* h, void* hip_stream);
 
 /* Free a handle and its device memory. NULL is allowed. The caller must ensure no queued
