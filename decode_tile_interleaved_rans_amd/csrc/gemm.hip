@@ -1,14 +1,20 @@
 // gfx950 BF16 GEMM for the compressed linear layer: Y[M][N] = X[M][K] W[N][K]^T (+ bias), fp32
 // accumulation on the matrix cores (v_mfma_f32_32x32x16_bf16), BF16 output.
 //
-// Tiling. A block of 4 waves owns a 128 x 128 tile of Y and walks K in steps of 64: both operand
-// tiles (128 rows x 64 K of X and of W, K contiguous, as the MFMA wants 8 consecutive K per lane)
-// are staged in LDS with a 16-byte row pad against bank conflicts, double-buffered, the next K
-// step being fetched into registers while the current one feeds the MFMAs. Each wave computes
-// 64 x 64 as 2 x 2 MFMA tiles of 32 x 32, reusing every A and B fragment twice. Operand lane
-// layout of the 32x32x16 BF16 MFMA (checked on the device): lane l supplies A[l % 32][8 (l / 32)
-// + i] and B[8 (l / 32) + i][l % 32], i < 8, and receives C[8 (i / 4) + 4 (l / 32) + i % 4][l % 32]
-// for i < 16.
+// Tiled kernels (gemm_nt). A block of WGM x WGN waves owns a BM x BN tile of Y and walks K in
+// steps of 64: both operand tiles (rows x 64 K of X and of W, K contiguous, as the MFMA wants 8
+// consecutive K per lane) are staged in LDS with a 16-byte row pad against bank conflicts,
+// double-buffered; global loads go through buffer resources (rows past the matrix and K past the
+// end read as zero) into two register stages, so the loads of step k + 2 are in flight while
+// step k feeds the MFMAs. Each wave computes its (BM / WGM) x (BN / WGN) part as 32 x 32 MFMA
+// tiles. Tile choice (launch_gemm): 256 x 256 with 16 waves when that still gives every CU a
+// block, 128 x 128 with 4 waves, or 64 x 64 with 4 waves for few output tiles; the skinny kernel
+// streams W straight into registers for M <= 64. Block order: consecutive block ids land on
+// different XCDs, so each XCD gets a contiguous range of tiles, walked in groups of 4 M tiles so
+// that the blocks running together share X and W slices in that XCD's L2. Operand lane layout of
+// the 32x32x16 BF16 MFMA (checked on the device): lane l supplies A[l % 32][8 (l / 32) + i] and
+// B[8 (l / 32) + i][l % 32], i < 8, and receives C[8 (i / 4) + 4 (l / 32) + i % 4][l % 32] for
+// i < 16.
 //
 // The compressed linear forward (capi.cpp) decodes the weight slice by slice into a scratch
 // buffer small enough to stay in the Infinity Cache and runs this GEMM on each slice: every
@@ -33,32 +39,48 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int BK = 64;
 constexpr int kPad = 8;                      // bf16 elements of padding per LDS row
 constexpr int kLd = BK + kPad;               // LDS row stride in elements (144 bytes)
-constexpr int kThreads = 256;
+constexpr int kPrefetch = 2;                 // register stages of the tiled kernels (see gemm_nt)
+constexpr int kGroupM = 4;                   // M tiles per group in the block order (see gemm_nt)
 
-template <int ROWS>
+template <int ROWS, int NT>
 struct Frag {
-    uint4 v[ROWS / 32];                      // ROWS x 64 bf16 = ROWS * 8 chunks of 16 bytes over 256 threads
+    uint4 v[ROWS * 8 / NT];                  // ROWS x 64 bf16 = ROWS * 8 chunks of 16 bytes over NT threads
 };
 
-// Fetch a ROWS x 64 operand tile (rows r0.., K k0..) into registers: thread t takes 16-byte
-// chunks t, t + 256, ... (row = chunk / 8, K chunk = chunk % 8); rows past `rows` and chunks
-// past K read as zero.
+// Operand rows [r0, r0 + ROWS) of a row-major bf16 matrix as a buffer resource: rows past `rows`
+// lie past the resource's end and read as zero.
 template <int ROWS>
-__device__ __forceinline__ void fetch(const uint16_t* src, int ld, int r0, int rows, int k0, int K, Frag<ROWS>& f) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const uint16_t* src, int ld, int r0, int rows) {
+    const int n = rows - r0 < ROWS ? rows - r0 : ROWS;
+    // readfirstlane: the size is block-uniform; without it the backend may build it in VGPRs and
+    // wrap every load in a loop over distinct resources
+    const int bytes = __builtin_amdgcn_readfirstlane((int)((size_t)(n > 0 ? n : 0) * ld * 2));
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src + (size_t)r0 * ld), 0, bytes, 0x00020000);
+}
+
+constexpr uint32_t kOob = 0x80000000u;      // an offset past every resource: the load returns 0
+
+// Fetch a ROWS x 64 operand tile (K k0..) into registers: thread t of NT takes 16-byte chunks t,
+// t + NT, ... (row = chunk / 8, K chunk = chunk % 8); rows past the resource and chunks past K
+// read as zero (K % 8 == 0, so a chunk is either wholly inside K or wholly past it).
+template <int ROWS, int NT>
+__device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rs, int ld, int k0, int K, Frag<ROWS, NT>& f) {
 #pragma unroll
-    for (int j = 0; j < ROWS / 32; ++j) {
-        const int c = threadIdx.x + kThreads * j;
-        const int r = r0 + (c >> 3), k = k0 + 8 * (c & 7);
-        // K % 8 == 0, so a chunk is either wholly inside K or wholly past it
-        f.v[j] = (r < rows && k < K) ? *reinterpret_cast<const uint4*>(src + (size_t)r * ld + k) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < ROWS * 8 / NT; ++j) {
+        const int c = threadIdx.x + NT * j;
+        const int r = c >> 3, k = k0 + 8 * (c & 7);
+        // k >= K moves the offset past the resource; arithmetic rather than a select, which the
+        // backend would turn into a branch around the load
+        const uint32_t off = (uint32_t)(r * ld + k) * 2u | ((uint32_t)((K - 1 - k) >> 31) & kOob);
+        f.v[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
     }
 }
 
-template <int ROWS>
-__device__ __forceinline__ void stash(const Frag<ROWS>& f, uint16_t* lds) {
+template <int ROWS, int NT>
+__device__ __forceinline__ void stash(const Frag<ROWS, NT>& f, uint16_t* lds) {
 #pragma unroll
-    for (int j = 0; j < ROWS / 32; ++j) {
-        const int c = threadIdx.x + kThreads * j;
+    for (int j = 0; j < ROWS * 8 / NT; ++j) {
+        const int c = threadIdx.x + NT * j;
         *reinterpret_cast<uint4*>(lds + (c >> 3) * kLd + 8 * (c & 7)) = f.v[j];
     }
 }
@@ -68,11 +90,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// BM x BN output tile per block of 4 waves (2 x 2), each wave (BM / 2) x (BN / 2) as
-// (BM / 64) x (BN / 64) MFMA tiles of 32 x 32.
-template <int BM, int BN, bool BIAS>
-__global__ __launch_bounds__(kThreads) void gemm_nt(GemmArgs g) {
-    constexpr int TI = BM / 64, TJ = BN / 64;
+// BM x BN output tile per block of WGM x WGN waves, each wave (BM / WGM) x (BN / WGN) as
+// TI x TJ MFMA tiles of 32 x 32.
+template <int BM, int BN, int WGM, int WGN, int PF, bool BIAS>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt(GemmArgs g) {
+    constexpr int NT = 64 * WGM * WGN;
+    constexpr int TI = BM / WGM / 32, TJ = BN / WGN / 32;
     __shared__ __align__(16) uint16_t As[2][BM * kLd];
     __shared__ __align__(16) uint16_t Bs[2][BN * kLd];
     // XCD-aware order: consecutive block ids go to different XCDs, so give each XCD a compact
@@ -81,10 +104,15 @@ __global__ __launch_bounds__(kThreads) void gemm_nt(GemmArgs g) {
     const int nblk = tiles_m * tiles_n;
     int b = blockIdx.x;
     if (nblk % 8 == 0) b = (b % 8) * (nblk / 8) + b / 8;
-    const int tm = b % tiles_m, tn = b / tiles_m;
-    const int m0 = tm * BM, n0 = tn * BN;
+    // then groups of kGroupM M tiles: the blocks that run together share both X and W slices
+    constexpr int G = kGroupM;
+    const int per_group = G * tiles_n, first_m = (b / per_group) * G;
+    const int gsize = tiles_m - first_m < G ? tiles_m - first_m : G;
+    const int tm = first_m + (b % per_group) % gsize, tn = (b % per_group) / gsize;
+    // block-uniform (kept in SGPRs, so the operand resources below are scalar)
+    const int m0 = __builtin_amdgcn_readfirstlane(tm * BM), n0 = __builtin_amdgcn_readfirstlane(tn * BN);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = (wave >> 1) * (BM / 2), wn = (wave & 1) * (BN / 2);
+    const int wm = (wave / WGN) * (BM / WGM), wn = (wave % WGN) * (BN / WGN);
 
     f32x16 acc[TI][TJ];
 #pragma unroll
@@ -92,41 +120,52 @@ __global__ __launch_bounds__(kThreads) void gemm_nt(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
 
-    Frag<BM> fa;
-    Frag<BN> fb;
-    fetch<BM>(g.X, g.ldx, m0, g.M, 0, g.K, fa);
-    fetch<BN>(g.W, g.ldw, n0, g.N, 0, g.K, fb);
-    stash<BM>(fa, As[0]);
-    stash<BN>(fb, Bs[0]);
+    const __amdgpu_buffer_rsrc_t rx = operand_rsrc<BM>(g.X, g.ldx, m0, g.M);
+    const __amdgpu_buffer_rsrc_t rw = operand_rsrc<BN>(g.W, g.ldw, n0, g.N);
+    // PF register stages: step kt + PF is fetched while step kt is multiplied out of LDS, and
+    // step kt + 1 (fetched PF - 1 steps ago) is stored into the other LDS buffer behind it.
+    // Fetches past K read zeros, so the loop needs no tail guards on them.
+    Frag<BM, NT> fa[PF];
+    Frag<BN, NT> fb[PF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        fetch<BM, NT>(rx, g.ldx, p * BK, g.K, fa[p]);
+        fetch<BN, NT>(rw, g.ldw, p * BK, g.K, fb[p]);
+    }
+    stash<BM, NT>(fa[0], As[0]);
+    stash<BN, NT>(fb[0], Bs[0]);
     __syncthreads();
     const int nk = (g.K + BK - 1) / BK;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            fetch<BM>(g.X, g.ldx, m0, g.M, (kt + 1) * BK, g.K, fa);
-            fetch<BN>(g.W, g.ldw, n0, g.N, (kt + 1) * BK, g.K, fb);
-        }
+    for (int kt0 = 0; kt0 < nk; kt0 += PF) {
 #pragma unroll
-        for (int ks = 0; ks < BK; ks += 16) {
-            bf16x8 a[TI], bb[TJ];
-            const int kk = ks + 8 * (lane >> 5);
+        for (int u = 0; u < PF; ++u) {
+            const int kt = kt0 + u;
+            if (kt >= nk) break;
+            const int cur = kt & 1;
+            fetch<BM, NT>(rx, g.ldx, (kt + PF) * BK, g.K, fa[u]);
+            fetch<BN, NT>(rw, g.ldw, (kt + PF) * BK, g.K, fb[u]);
 #pragma unroll
-            for (int i = 0; i < TI; ++i)
-                a[i] = *reinterpret_cast<const bf16x8*>(&As[cur][(wm + 32 * i + (lane & 31)) * kLd + kk]);
+            for (int ks = 0; ks < BK; ks += 16) {
+                bf16x8 a[TI], bb[TJ];
+                const int kk = ks + 8 * (lane >> 5);
 #pragma unroll
-            for (int j = 0; j < TJ; ++j)
-                bb[j] = *reinterpret_cast<const bf16x8*>(&Bs[cur][(wn + 32 * j + (lane & 31)) * kLd + kk]);
-#pragma unroll
-            for (int i = 0; i < TI; ++i)
+                for (int i = 0; i < TI; ++i)
+                    a[i] = *reinterpret_cast<const bf16x8*>(&As[cur][(wm + 32 * i + (lane & 31)) * kLd + kk]);
 #pragma unroll
                 for (int j = 0; j < TJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+                    bb[j] = *reinterpret_cast<const bf16x8*>(&Bs[cur][(wn + 32 * j + (lane & 31)) * kLd + kk]);
+#pragma unroll
+                for (int i = 0; i < TI; ++i)
+#pragma unroll
+                    for (int j = 0; j < TJ; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+            }
+            if (kt + 1 < nk) {
+                stash<BM, NT>(fa[(u + 1) % PF], As[cur ^ 1]);
+                stash<BN, NT>(fb[(u + 1) % PF], Bs[cur ^ 1]);
+            }
+            __syncthreads();
         }
-        if (kt + 1 < nk) {
-            stash<BM>(fa, As[cur ^ 1]);
-            stash<BN>(fb, Bs[cur ^ 1]);
-        }
-        __syncthreads();
     }
 
     // epilogue: C[8 (r / 4) + 4 (lane / 32) + r % 4][lane % 32] of each 32 x 32 tile
@@ -157,7 +196,6 @@ __global__ __launch_bounds__(kThreads) void gemm_nt(GemmArgs g) {
 // resources bounded to the block's rows, so rows past N or M and K past the end read as zero.
 constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnyUnroll = 4;
-constexpr uint32_t kOob = 0x80000000u;      // an offset past every resource: the load returns 0
 
 template <int MT, bool BIAS>
 __global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny(GemmArgs g) {
@@ -230,13 +268,13 @@ int gemm_device_cus() {
     return cache[dev];
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WGM, int WGN, int PF>
 hipError_t launch_tiled(const GemmArgs& g, hipStream_t stream) {
     const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
     if (g.bias)
-        hipLaunchKernelGGL((gemm_nt<BM, BN, true>), dim3(tiles), dim3(kThreads), 0, stream, g);
+        hipLaunchKernelGGL((gemm_nt<BM, BN, WGM, WGN, PF, true>), dim3(tiles), dim3(64 * WGM * WGN), 0, stream, g);
     else
-        hipLaunchKernelGGL((gemm_nt<BM, BN, false>), dim3(tiles), dim3(kThreads), 0, stream, g);
+        hipLaunchKernelGGL((gemm_nt<BM, BN, WGM, WGN, PF, false>), dim3(tiles), dim3(64 * WGM * WGN), 0, stream, g);
     return hipGetLastError();
 }
 
@@ -254,14 +292,16 @@ hipError_t launch_skinny(const GemmArgs& g, hipStream_t stream) {
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
-    // tile choice: the skinny kernel for a few rows of X; 128 x 128 tiles when they give every CU
-    // at least two blocks, else 64 x 64 tiles
+    // tile choice: the skinny kernel for a few rows of X; 256 x 256 tiles when every CU gets one,
+    // 128 x 128 tiles when every CU gets two, else 64 x 64 tiles
     if (g.M <= 16) return launch_skinny<1>(g, stream);
     if (g.M <= 32) return launch_skinny<2>(g, stream);
     if (g.M <= 64) return launch_skinny<4>(g, stream);
+    const long tiles256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
+    if (tiles256 >= gemm_device_cus()) return launch_tiled<256, 256, 4, 4, kPrefetch>(g, stream);
     const long tiles128 = (long)((g.M + 127) / 128) * ((g.N + 127) / 128);
-    if (tiles128 >= 2L * gemm_device_cus()) return launch_tiled<128, 128>(g, stream);
-    return launch_tiled<64, 64>(g, stream);
+    if (tiles128 >= 2L * gemm_device_cus()) return launch_tiled<128, 128, 2, 2, kPrefetch>(g, stream);
+    return launch_tiled<64, 64, 2, 2, kPrefetch>(g, stream);
 }
 
 }  // namespace ep

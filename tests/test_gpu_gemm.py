@@ -27,10 +27,11 @@ def bf16_tensor(bits: np.ndarray) -> torch.Tensor:
 
 
 # shapes cover every tile choice: the skinny kernel (M <= 16, 32, 64: one, two or four 16-row
-# tiles), 64 x 64 tiles (few output tiles) and 128 x 128 tiles (the prefill test below), with
-# ragged M, N and K tails
+# tiles), 64 x 64 tiles (few output tiles), 128 x 128 tiles (2 x 256 of them or more) and
+# 256 x 256 tiles (the prefill test below and the 4100 x 4000 case), with ragged M, N and K tails
 @pytest.mark.parametrize("M,N,K", [(16, 256, 512), (256, 384, 1024), (130, 200, 264), (1, 8, 8), (300, 1000, 776),
-                                   (33, 1000, 520), (64, 4100, 1032), (20, 17, 4104), (5, 4096, 8192)])
+                                   (33, 1000, 520), (64, 4100, 1032), (20, 17, 4104), (5, 4096, 8192),
+                                   (2000, 4000, 136), (4100, 4000, 136)])
 def test_gemm_bf16_matches_fp32(M, N, K):
     rng = np.random.default_rng(M + N + K)
     x = W.to_bf16_bits(rng.normal(0, 1, (M, K)))
