@@ -56,7 +56,7 @@ def lib():
         L.or_free.argtypes = [vp]
         L.or_decompress.argtypes = [vp, sz, C.c_int, vp, vp, C.c_int]
         L.or_decode_symbols.argtypes = [vp, sz, vp, vp, C.c_int]
-        L.or_decompress_tiles.argtypes = [vp, sz, C.c_int, vp, C.c_int, vp, vp]
+        L.or_decompress_tiles.argtypes = [vp, sz, C.c_int, vp, C.c_int, vp, vp, vp]
         L.or_stream_info.argtypes = [vp, sz, vp, vp]
         L.or_stream_tables.argtypes = [vp, sz, vp, vp, vp]
         L.or_e8_nearest_batch.argtypes = [vp, i64, vp, vp]
@@ -161,17 +161,21 @@ def decode_symbols(stream: bytes, n_threads: int = 1):
     return q, b
 
 
-def decompress_tiles(stream: bytes, tiles, container: int = BF16, want_q: bool = False):
-    """Decode only the listed tiles: returns [n, tile_rows, 256] container bits (and q if asked)."""
+def decompress_tiles(stream: bytes, tiles, container: int = BF16, want_q: bool = False, want_scale: bool = False):
+    """Decode only the listed tiles: returns [n, tile_rows, 256] container bits, plus q
+    [n, tile_rows, 256] if want_q and the rows' output scales [n, tile_rows] (FP8 / INT8) if
+    want_scale, in that order."""
     d = info(stream)
     tiles = np.ascontiguousarray(np.asarray(tiles, np.uint32))
     n = len(tiles)
     out = np.zeros((n, d["tile_rows"], 256), _NP[container])
     q = np.zeros((n, d["tile_rows"], 256), np.int16) if want_q else None
-    rc = lib().or_decompress_tiles(stream, len(stream), container, _ptr(tiles), n, _ptr(out), _ptr(q))
+    sc = np.zeros((n, d["tile_rows"]), np.float32) if want_scale else None
+    rc = lib().or_decompress_tiles(stream, len(stream), container, _ptr(tiles), n, _ptr(out), _ptr(q), _ptr(sc))
     if rc != 0:
         raise OracleError(rc, "decompress_tiles")
-    return (out, q) if want_q else out
+    res = (out,) + ((q,) if want_q else ()) + ((sc,) if want_scale else ())
+    return res if len(res) > 1 else out
 
 
 def e8_nearest(y: np.ndarray):

@@ -1325,9 +1325,11 @@ int or_decode_symbols(const uint8_t* s, size_t len, int16_t* q, uint8_t* coset, 
 }
 
 /* Decode only the listed tiles. out receives, per listed tile, tile_rows x 256 container
- * elements (padding positions included, as decoded); qout (optional) the doubled coordinates. */
+ * elements (padding positions included, as decoded); qout (optional) the doubled coordinates;
+ * scale_out (optional, FP8 and INT8 containers of a lossy stream) the output scale of each of
+ * the tile's rows, as or_decompress gives it (0 for padding rows). */
 int or_decompress_tiles(const uint8_t* s, size_t len, int container, const uint32_t* tiles, int n,
-                        void* out, int16_t* qout) {
+                        void* out, int16_t* qout, float* scale_out) {
     parsed P;
     int rc = parse_stream(s, len, &P);
     if (rc != OR_OK) return rc;
@@ -1352,6 +1354,8 @@ int or_decompress_tiles(const uint8_t* s, size_t len, int container, const uint3
         if (rc != OR_OK) break;
         for (int rr = 0; rr < P.tile_rows; ++rr) {
             int64_t r = tr * P.tile_rows + rr;
+            if (scale_out && P.mode == MODE_LOSSY && (container == DT_F8E4M3 || container == DT_I8))
+                scale_out[(size_t)i * P.tile_rows + rr] = r < P.R ? row_out_scale(&P, container, r) : 0.0f;
             for (int c = 0; c < TILE_COLS; ++c) {
                 size_t o = (size_t)i * per_tile + (size_t)rr * TILE_COLS + c;
                 if (P.mode == MODE_LOSSY) {

@@ -4,7 +4,9 @@ bytes and row scales), through the C ABI.
 Inputs are the seeded synthetic workloads: a 1024x1024 fp32 Gaussian matrix with 0.1% outliers
 at 4.0 bpp; 4096x4096 bf16 Student-t(5) rows with log-normal row scales at 3.0 / 4.0 / 4.5 bpp
 plus the lossless bf16 round trip; ragged shapes, escapes, degenerate matrices; sampled tiles of
-8192x8192 at 4.5 bpp and of one full-size DiT-like block."""
+8192x8192 at 4.5 bpp; the DiT-like model (one block in a grouped launch, two matrices in full,
+sampled tiles of the rest and of other blocks); the 64-matrix mixed-rate set in FP8, INT8 and
+BF16."""
 import numpy as np
 import pytest
 import torch
@@ -220,8 +222,73 @@ def test_c4_8192_sampled_tiles():
     sampled_tile_parity(s, 400, 1)
 
 
-def test_c3_one_dit_block_sampled_tiles():
-    for m in range(5):
-        w = W.dit_matrix(0, m)
-        s, _ = ep.compress(w, 4.0, dtype=ep.BF16)
-        sampled_tile_parity(s, 100, m)
+def test_c3_dit_block_grouped_full_and_sampled():
+    """DiT-like model at 4.0 bpp: block 0's five matrices decoded to BF16 in one grouped launch;
+    the attention output projection and the FFN down projection compared in full, 1% of the
+    tiles of the other three; then 1% of the tiles of one matrix from each of five other
+    blocks (all 150 matrices would take minutes of host-side generation)."""
+    streams = [ep.compress(W.dit_matrix(0, m), 4.0, dtype=ep.BF16)[0] for m in range(5)]
+    hs = [ep.upload(s) for s in streams]
+    outs = [torch.empty(h.shape, dtype=torch.bfloat16, device="cuda") for h in hs]
+    ep.decompress_many(hs, outs)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(30)
+    for m, (h, s, o) in enumerate(zip(hs, streams, outs)):
+        h.check()
+        got = bits(o)
+        if m in (1, 4):
+            want, _ = oracle.decompress(s, oracle.BF16, n_threads=16)
+            assert np.array_equal(got, want), mismatch_report(f"block 0 matrix {m}", got, want)
+        else:
+            info = ep.stream_info(s)
+            tiles = np.sort(rng.choice(info["n_tiles"], size=info["n_tiles"] // 100, replace=False))
+            want = oracle.decompress_tiles(s, tiles, oracle.BF16)
+            tiles_c = -(-info["cols"] // 256)
+            for k, t in enumerate(tiles):
+                r0, c0 = (t // tiles_c) * 16, (t % tiles_c) * 256
+                assert np.array_equal(got[r0:r0 + 16, c0:c0 + 256], want[k]), f"block 0 matrix {m} tile {t}"
+        h.release()
+    for b in (6, 12, 18, 24, 29):
+        s, _ = ep.compress(W.dit_matrix(b, b % 5), 4.0, dtype=ep.BF16)
+        sampled_tile_parity(s, ep.stream_info(s)["n_tiles"] // 100, b)
+
+
+def test_c5_mixed_rate_set_all_containers():
+    """The 64-matrix mixed-rate set (rows, cols in {2048, 4096, 8192}, targets U[2.5, 6.0]), each
+    decoded to FP8 E4M3 (+ row scale), INT8 (+ row scale) and BF16 by grouped launches over all
+    64 matrices; every matrix is checked on 8 tiles (first, last and 6 random ones) against the
+    oracle's decode of those tiles, container bytes and row scales."""
+    items = W.mixed_rate_set()
+    streams = []
+    for R, Cc, t, wseed, _ in items:
+        s, bpp = ep.compress(W.student_t(R, Cc, wseed, 0.02), t, dtype=ep.BF16)
+        assert bpp > t                                  # metadata included: the target is a floor
+        streams.append(s)
+    hs = [ep.upload(s) for s in streams]
+    rng = np.random.default_rng(64)
+    for name in ("f8", "i8", "bf16"):
+        tdt, odt = CONTAINERS[name]
+        outs = [torch.empty(h.shape, dtype=tdt, device="cuda") for h in hs]
+        scales = [torch.empty(h.shape[0], dtype=torch.float32, device="cuda") for h in hs] if name != "bf16" else None
+        ep.decompress_many(hs, outs, scales)
+        torch.cuda.synchronize()
+        for i, (h, s) in enumerate(zip(hs, streams)):
+            h.check()
+            info = ep.stream_info(s)
+            n = info["n_tiles"]
+            tiles = np.unique(np.r_[0, n - 1, rng.choice(n, 6, replace=False)])
+            got = bits(outs[i])
+            tiles_c = -(-info["cols"] // 256)
+            if scales is None:
+                want = oracle.decompress_tiles(s, tiles, odt)
+            else:
+                want, wsc = oracle.decompress_tiles(s, tiles, odt, want_scale=True)
+                gsc = scales[i].cpu().numpy()
+            for k, t in enumerate(tiles):
+                r0, c0 = (t // tiles_c) * 16, (t % tiles_c) * 256
+                assert np.array_equal(got[r0:r0 + 16, c0:c0 + 256], want[k]), f"matrix {i} {name} tile {t}"
+                if scales is not None:
+                    assert np.array_equal(gsc[r0:r0 + 16], wsc[k]), f"matrix {i} {name} row scales, tile {t}"
+        del outs, scales
+    for h in hs:
+        h.release()

@@ -101,6 +101,30 @@ def test_linear_forward_prefill_sampled_rows():
     assert rel_l2(y[rows].float().cpu().numpy(), ref) < 2e-2
 
 
+def test_c5_linear_forward_token_counts():
+    """Fused forward on three matrices of the mixed-rate set (different shapes and rates) at 16
+    and 256 tokens: all rows (M = 16) or 32 sampled rows (M = 256) against the oracle-decoded
+    weight in fp32."""
+    items = W.mixed_rate_set()
+    picked, shapes = [], set()
+    for R, Cc, t, wseed, aseed in items:
+        if (R, Cc) not in shapes and len(picked) < 3:
+            shapes.add((R, Cc))
+            picked.append((R, Cc, t, wseed, aseed))
+    for R, Cc, t, wseed, aseed in picked:
+        s, _ = ep.compress(W.student_t(R, Cc, wseed, 0.02), t, dtype=ep.BF16)
+        layer = ep.CompressedLinear(s)
+        w_hat = W.bf16_bits_to_f32(oracle.decompress(s, oracle.BF16, n_threads=16)[0])
+        for M in (16, 256):
+            xb = W.activations(M, Cc, aseed)
+            y = layer(bf16_tensor(xb).cuda())
+            torch.cuda.synchronize()
+            layer.handle.check()
+            rows = np.arange(M) if M <= 16 else np.random.default_rng(M).choice(M, 32, replace=False)
+            ref = W.bf16_bits_to_f32(xb[rows]) @ w_hat.T
+            assert rel_l2(y[rows].float().cpu().numpy(), ref) < 2e-2, (R, Cc, t, M)
+
+
 def test_from_linear_roundtrip():
     lin = torch.nn.Linear(1024, 512, bias=True)
     layer = ep.CompressedLinear.from_linear(lin, 5.0)

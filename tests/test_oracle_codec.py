@@ -194,6 +194,24 @@ def test_ragged_shapes_roundtrip(shape):
     assert np.array_equal(full[: shape[0], : shape[1]], bf)
 
 
+@pytest.mark.parametrize("container", [oracle.F8E4M3, oracle.I8])
+def test_tile_decode_row_scales_match_full_decode(container):
+    """The per-tile decode's row scales (used to check sampled tiles of large matrices) are the
+    full decode's, row for row; padding rows of the last tile row give 0."""
+    w = W.gaussian_with_outliers(40, 600, seed=12)
+    s, _ = oracle.compress(w, 5.0)
+    d = oracle.info(s)
+    full, scale = oracle.decompress(s, container)
+    tiles = np.arange(d["n_tiles"])
+    out, sc = oracle.decompress_tiles(s, tiles, container, want_scale=True)
+    tc = -(-600 // 256)
+    for t in tiles:
+        r0 = (t // tc) * 16
+        rows = np.arange(r0, r0 + 16)
+        want = np.where(rows < 40, scale[np.minimum(rows, 39)], 0.0).astype(np.float32)
+        assert np.array_equal(sc[t], want)
+
+
 def test_zero_rows_decode_to_positive_zero():
     rng = np.random.default_rng(6)
     w = rng.normal(0, 0.02, (32, 256)).astype(np.float32)
