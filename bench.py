@@ -2,13 +2,14 @@
 
 Default workload (a "step"): the 4096 x 4096 BF16 Student-t(5) matrix with log-normal row scales,
 compressed at 3.0, 4.0 and 4.5 bits per weight, each decoded to BF16 and to FP16, plus the
-lossless BF16 tile-rANS decode of the same matrix: seven full-matrix decodes per step. Inputs are
+lossless BF16 tile-rANS decode of the same matrix: seven full-matrix decodes per step, issued as
+one grouped launch (the kernel balances lossy and lossless tiles by their cost). Inputs are
 resident in HBM before timing starts; several copies of the step's buffers are used in rotation
 (> 2 GB between reuses) so that neither the compressed input nor the output of a step is still
 in the 256 MB Infinity Cache.
 
 Prints one JSON line (rank 0, N = 1): decoded-weight GB/s (container bytes written per second),
-the roofline of the dominant kernel (lossy decode to BF16) from HIP events on the launch stream,
+the roofline of the step's one grouped decode launch from HIP events on the launch stream,
 the fused decode + GEMM forward of an 8192 x 8192 weight at 4.5 bpp against the plain BF16 GEMM
 (M = 4096, 256, 16), and the oracle's CPU decode of one step on the host cores as a reported
 baseline.
@@ -32,11 +33,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
 
 
-PROFILE = os.path.join(ROOT, "profiles", "decode_group_lossy_4096sq_step.txt")
+PROFILE = os.path.join(ROOT, "profiles", "decode_group_4096sq_step.txt")
 
 
 def profiled_traffic():
-    """HBM bytes per grouped lossy launch from the committed rocprofv3 counter summary, or None
+    """HBM bytes per grouped decode launch from the committed rocprofv3 counter summary, or None
     when the decode kernel source changed since the counters were taken."""
     import hashlib
     try:
@@ -195,8 +196,6 @@ def main():
         sets.append((hs, outs))
     torch.cuda.synchronize()
 
-    lossy = [i for i, (name, _, _, _) in enumerate(items) if name.startswith("lossy")]
-    lossless = [i for i in range(len(items)) if i not in lossy]
     ev = []
 
     def step(k: int, record: bool):
@@ -205,11 +204,10 @@ def main():
         if record:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-        ep.decompress_many([hs[i] for i in lossy], [outs[i] for i in lossy])     # one grouped launch
+        ep.decompress_many(hs, outs)                # the whole step: one grouped launch
         if record:
             b.record()
             ev.append((a, b))
-        ep.decompress_many([hs[i] for i in lossless], [outs[i] for i in lossless])
 
     for k in range(args.warmup):
         step(k, False)
@@ -234,15 +232,15 @@ def main():
     value = step_out_bytes * args.steps / sec / 1e9
     weights_per_s = len(items) * R * C * args.steps / sec
 
-    # dominant kernel: the grouped lossy decode (six matrices per launch); algorithmic bytes =
+    # the step's kernel: one grouped decode of the seven matrices; algorithmic bytes =
     # stream bytes read + container bytes written
     durs = [a.elapsed_time(b) / 1e3 for a, b in ev]
-    launch_bytes = sum(len(items[i][1]) + 2 * R * C for i in lossy)
+    launch_bytes = sum(len(items[i][1]) + 2 * R * C for i in range(len(items)))
     t_launch = float(np.mean(durs))
     achieved = launch_bytes / t_launch / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(),
-                "kernel": "decode_lossy_group (6 matrices: 3.0/4.0/4.5 bpp x BF16/FP16)",
+                "kernel": "decode_group (7 matrices: 3.0/4.0/4.5 bpp x BF16/FP16 + lossless BF16)",
                 "avg_launch_us": round(t_launch * 1e6, 2), "bytes_per_launch": launch_bytes,
                 "launch_us_min": round(min(durs) * 1e6, 2)}
     per_item = {items[i][0]: {"actual_bpp": round(items[i][3], 4), "stream_bytes": len(items[i][1])}

@@ -91,14 +91,16 @@ ep::MatDesc desc_for(const ep_handle* h, int container, void* out, float* scale)
     d.tile_rows = (uint8_t)v.tile_rows;
     d.container = (uint8_t)container;
     d.n_tables = (uint8_t)v.n_tables;
+    d.mode = (uint8_t)v.mode;
+    d.pair_cost = ep::pair_cost_of(v.mode, v.tile_rows, v.n_tables);
     return d;
 }
 
-// Launch the matrices of one mode in groups of at most kMaxGroup.
-hipError_t launch_all(const std::vector<ep::MatDesc>& ds, int mode, hipStream_t stream) {
+// Launch the matrices in groups of at most kMaxGroup.
+hipError_t launch_all(const std::vector<ep::MatDesc>& ds, hipStream_t stream) {
     for (size_t i = 0; i < ds.size(); i += ep::kMaxGroup) {
         const int n = (int)std::min<size_t>(ep::kMaxGroup, ds.size() - i);
-        hipError_t e = ep::launch_group(ds.data() + i, n, mode, stream);
+        hipError_t e = ep::launch_group(ds.data() + i, n, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -234,7 +236,7 @@ ep_status ep_decompress(const ep_handle* h, ep_dtype container, void* dev_out, f
     ep_status st = check_decode_args(h, container, dev_out, dev_row_scale);
     if (st != EP_OK) return st;
     std::vector<ep::MatDesc> one{desc_for(h, (int)container, dev_out, dev_row_scale)};
-    hipError_t e = launch_all(one, h->view.mode, static_cast<hipStream_t>(hip_stream));
+    hipError_t e = launch_all(one, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return EP_OK;
 }
@@ -242,17 +244,15 @@ ep_status ep_decompress(const ep_handle* h, ep_dtype container, void* dev_out, f
 ep_status ep_decompress_many(const ep_handle* const* hs, const ep_dtype* containers, void* const* dev_outs,
                              float* const* dev_row_scales, int count, void* hip_stream) {
     if (count < 0 || (count > 0 && (!hs || !containers || !dev_outs))) return fail(EP_EINVAL, "null array");
-    std::vector<ep::MatDesc> by_mode[2];
+    std::vector<ep::MatDesc> ds;
     for (int i = 0; i < count; ++i) {
         float* sc = dev_row_scales ? dev_row_scales[i] : nullptr;
         ep_status st = check_decode_args(hs[i], containers[i], dev_outs[i], sc);
         if (st != EP_OK) return fail(st, "matrix " + std::to_string(i) + ": " + g_err);
-        by_mode[hs[i]->view.mode].push_back(desc_for(hs[i], (int)containers[i], dev_outs[i], sc));
+        ds.push_back(desc_for(hs[i], (int)containers[i], dev_outs[i], sc));
     }
-    for (int mode = 0; mode < 2; ++mode) {
-        hipError_t e = launch_all(by_mode[mode], mode, static_cast<hipStream_t>(hip_stream));
-        if (e != hipSuccess) return hip_fail(e, "grouped decode launch");
-    }
+    hipError_t e = launch_all(ds, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "grouped decode launch");
     return EP_OK;
 }
 
@@ -261,7 +261,7 @@ ep_status ep_decode_symbols(const ep_handle* h, int16_t* dev_q, void* hip_stream
     if (h->view.mode != EP_MODE_LOSSY_E8) return fail(EP_EUNSUPPORTED, "symbols exist only for lossy streams");
     if (!dev_q && h->view.rows * h->view.cols > 0) return fail(EP_EINVAL, "null output pointer");
     std::vector<ep::MatDesc> one{desc_for(h, ep::CT_Q16, dev_q, nullptr)};
-    hipError_t e = launch_all(one, 0, static_cast<hipStream_t>(hip_stream));
+    hipError_t e = launch_all(one, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return EP_OK;
 }
@@ -336,7 +336,7 @@ ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, co
         d.row_scale += r0;
         d.row_qmax += r0;
         d.rows = (uint32_t)rows;
-        hipError_t e = ep::launch_group(&d, 1, 0, s);
+        hipError_t e = ep::launch_group(&d, 1, s);
         if (e != hipSuccess) return hip_fail(e, "slice decode launch");
         ep::GemmArgs g{static_cast<const uint16_t*>(dev_x), h->scratch,
                        dev_bias ? static_cast<const uint16_t*>(dev_bias) + r0 : nullptr,

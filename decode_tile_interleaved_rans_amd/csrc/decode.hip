@@ -19,7 +19,7 @@
 // ever waits on LDS. Every three steps the ring is topped up until it holds more than three
 // steps can consume (3 x 64 words), so the steps need no bounds checks; a damaged stream can
 // only read stale ring words, and is caught by the end-of-tile checks. Lossless tiles top up
-// before every element (at most 4 steps x 32 words).
+// once per row (once per four elements for 4-byte elements).
 //
 // Per decoding step every lane looks up its slot in the LDS LUT (one byte read), then reads the
 // symbol's 8-byte entry (frequency, cumulative frequency, decoded value) and updates its state;
@@ -515,9 +515,12 @@ __device__ __forceinline__ void lossless_pairs(const MatDesc& M, const Tables& T
         begin_tile(M, rs, (uint64_t)tr * M.tiles_c + tc, t);
         for (int rr = 0; rr < M.tile_rows; ++rr) {
             uint32_t v[8];
+            // an element is at most P steps x 32 words, and a top-up leaves more than
+            // kRingWords - kChunkWords unread: enough for the whole row when P <= 2
+            constexpr int kElemsPerTopUp = (kRingWords - kChunkWords) / (32 * P) >= 8 ? 8 : 4;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                top_up(t, rs);              // an element is at most 4 steps x 32 words
+                if (e % kElemsPerTopUp == 0) top_up(t, rs);
                 uint32_t acc = 0;
 #pragma unroll
                 for (int pl = 0; pl < P; ++pl) {
@@ -568,10 +571,11 @@ __device__ __forceinline__ void lossless_dispatch(const MatDesc& M, const Tables
 }
 
 // ----------------------------------------------------------------------------- grouped kernel
-// Persistent blocks: block k owns pairs [k P, (k + 1) P) of the launch's matrix-major pair
-// space, so every CU gets the same amount of work. A block walks its range one matrix segment at
-// a time and restages the decode tables when it crosses into the next matrix.
-template <bool LOSSY>
+// Persistent blocks over a launch's matrix-major tile pairs, lossy and lossless matrices alike.
+// Work is balanced by cost, not by pair count: a pair costs its relative decode time
+// (pair_cost), matrix i spans cost units [cost_start[i], cost_start[i + 1]), and block k owns
+// the pairs whose first unit falls in [k C, (k + 1) C). A block walks its range one matrix
+// segment at a time and restages the decode tables when it crosses into the next matrix.
 __global__ __launch_bounds__(64 * kWaves) void decode_group(GroupArgs g) {
     extern __shared__ __align__(16) uint8_t smem[];
     // the lookups address the LUTs absolutely: the dynamic LDS must start at address 0
@@ -580,35 +584,35 @@ __global__ __launch_bounds__(64 * kWaves) void decode_group(GroupArgs g) {
             for (int i = 0; i < g.count; ++i) atomicOr(g.m[i].err, kErrLayout);
         return;
     }
-    const uint64_t a = (uint64_t)blockIdx.x * (uint64_t)g.block_pairs;
-    const uint64_t b = std::min<uint64_t>(a + (uint64_t)g.block_pairs, (uint64_t)g.pair_start[g.count]);
-    int mi = 0;
-    int err[kChains] = {};
-    for (uint64_t pos = a; pos < b;) {
-        while ((uint64_t)g.pair_start[mi + 1] <= pos) ++mi;
-        const uint64_t base = (uint64_t)g.pair_start[mi];
-        const uint64_t end = std::min<uint64_t>(b, (uint64_t)g.pair_start[mi + 1]);
+    const uint64_t a = (uint64_t)blockIdx.x * g.block_cost;
+    const uint64_t b = std::min<uint64_t>(a + g.block_cost, g.cost_start[g.count]);
+    for (int mi = 0; mi < g.count; ++mi) {
+        const uint64_t cs = g.cost_start[mi], ce = g.cost_start[mi + 1];
+        if (ce <= a || cs >= b) continue;
         const MatDesc M = g.m[mi];
+        const uint64_t w = M.pair_cost;
+        const uint64_t p0 = (std::max(a, cs) - cs + w - 1) / w;
+        const uint64_t p1 = (std::min(b, ce) - cs + w - 1) / w;
+        if (p0 >= p1) continue;
+        const bool lossy = M.mode == 0;
         __syncthreads();                            // every wave is done with the previous tables
-        const Tables T = stage_tables(M, smem, LOSSY);
+        const Tables T = stage_tables(M, smem, lossy);
         Tile t[kChains];
 #pragma unroll
-        for (int c = 0; c < kChains; ++c) init_lane(t[c], smem + lds_table_bytes(M.n_tables, M.prob_bits, LOSSY), c);
-        if constexpr (LOSSY) {
+        for (int c = 0; c < kChains; ++c) init_lane(t[c], smem + lds_table_bytes(M.n_tables, M.prob_bits, lossy), c);
+        if (lossy) {
             switch (M.prob_bits) {
-                case 10: lossy_dispatch<10>(M, T, t, pos - base, end - base); break;
-                case 11: lossy_dispatch<11>(M, T, t, pos - base, end - base); break;
-                default: lossy_dispatch<12>(M, T, t, pos - base, end - base); break;
+                case 10: lossy_dispatch<10>(M, T, t, p0, p1); break;
+                case 11: lossy_dispatch<11>(M, T, t, p0, p1); break;
+                default: lossy_dispatch<12>(M, T, t, p0, p1); break;
             }
         } else {
-            lossless_dispatch(M, T, t, pos - base, end - base);
+            lossless_dispatch(M, T, t, p0, p1);
         }
 #pragma unroll
         for (int c = 0; c < kChains; ++c)
             if (t[c].err) atomicOr(M.err, t[c].err);
-        pos = end;
     }
-    (void)err;
 }
 
 int device_cus() {
@@ -636,7 +640,7 @@ hipError_t allow_lds(const void* kernel) {
 
 }  // namespace
 
-hipError_t launch_group(const MatDesc* mats, int count, int mode, hipStream_t stream) {
+hipError_t launch_group(const MatDesc* mats, int count, hipStream_t stream) {
     if (count <= 0) return hipSuccess;
     if (count > kMaxGroup) return hipErrorInvalidValue;
     GroupArgs g{};
@@ -645,25 +649,22 @@ hipError_t launch_group(const MatDesc* mats, int count, int mode, hipStream_t st
     size_t lds = 0;
     for (int i = 0; i < count; ++i) {
         g.m[i] = mats[i];
-        g.pair_start[i] = (uint32_t)total;
-        total += (uint64_t)((mats[i].rows + mats[i].tile_rows - 1) / mats[i].tile_rows) * mats[i].pairs_c;
-        lds = std::max(lds, lds_table_bytes(mats[i].n_tables, mats[i].prob_bits, mode == 0) +
-                                (size_t)kWaves * kChains * 2 * kRingBytes);
+        g.cost_start[i] = total;
+        const uint64_t pairs = (uint64_t)((mats[i].rows + mats[i].tile_rows - 1) / mats[i].tile_rows) * mats[i].pairs_c;
+        total += pairs * mats[i].pair_cost;
+        if (pairs)
+            lds = std::max(lds, lds_table_bytes(mats[i].n_tables, mats[i].prob_bits, mats[i].mode == 0) +
+                                    (size_t)kWaves * kChains * 2 * kRingBytes);
     }
-    g.pair_start[count] = (uint32_t)total;
+    g.cost_start[count] = total;
     if (total == 0) return hipSuccess;
-    if (total >= (1ull << 32)) return hipErrorInvalidValue;
-    const uint64_t blocks = std::min<uint64_t>((uint64_t)device_cus(), total);
-    g.block_pairs = (uint32_t)((total + blocks - 1) / blocks);
-    const uint64_t used = (total + g.block_pairs - 1) / g.block_pairs;
-    const void* k = mode == 0 ? reinterpret_cast<const void*>(decode_group<true>)
-                              : reinterpret_cast<const void*>(decode_group<false>);
+    const uint64_t blocks = (uint64_t)device_cus();
+    g.block_cost = (total + blocks - 1) / blocks;
+    const uint64_t used = (total + g.block_cost - 1) / g.block_cost;
+    const void* k = reinterpret_cast<const void*>(decode_group);
     hipError_t e = allow_lds(k);
     if (e != hipSuccess) return e;
-    if (mode == 0)
-        hipLaunchKernelGGL(decode_group<true>, dim3((unsigned)used), dim3(64 * kWaves), lds, stream, g);
-    else
-        hipLaunchKernelGGL(decode_group<false>, dim3((unsigned)used), dim3(64 * kWaves), lds, stream, g);
+    hipLaunchKernelGGL(decode_group, dim3((unsigned)used), dim3(64 * kWaves), lds, stream, g);
     return hipGetLastError();
 }
 

@@ -26,12 +26,22 @@ struct MatDesc {
     uint32_t payload_bytes;     // size of the tile payload (buffer-load bounds)
     float step;
     uint8_t prob_bits, tile_rows, container, n_tables;
+    uint8_t mode;               // 0 lossy E8 coordinates, 1 lossless byte planes
+    uint32_t pair_cost;         // relative decode time of one tile pair (load balancing)
 };
+
+// Relative decode time of one tile pair, per tile row: a lossy row is 9 steps (coset + 8
+// coordinates) at 9 units each; a lossless row is one step per byte plane per element (8
+// elements) at 7.25 units, as measured on gfx950 (a lossless BF16 pair takes 1.43 times a lossy
+// pair).
+inline uint32_t pair_cost_of(int mode, int tile_rows, int n_tables) {
+    return (uint32_t)tile_rows * (mode == 0 ? 81u : 58u * (uint32_t)n_tables);
+}
 
 struct GroupArgs {
     int32_t count;              // matrices in this launch (<= kMaxGroup)
-    uint32_t block_pairs;       // tile pairs per block (the last block may get fewer)
-    uint32_t pair_start[kMaxGroup + 1];   // matrix-major prefix sums of the matrices' tile pairs
+    uint64_t block_cost;        // cost units per block (the last block may get fewer)
+    uint64_t cost_start[kMaxGroup + 1];   // matrix-major prefix sums of pairs x pair_cost
     MatDesc m[kMaxGroup];
 };
 
@@ -53,7 +63,7 @@ __host__ __device__ inline size_t lds_table_bytes(int n_tables, int prob_bits, b
     return table_blob_bytes(lossy ? n_tables - 1 : n_tables, prob_bits);
 }
 
-// Launch one grouped decode (all matrices of the same mode: 0 lossy, 1 lossless).
-hipError_t launch_group(const MatDesc* mats, int count, int mode, hipStream_t stream);
+// Launch one grouped decode of up to kMaxGroup matrices (lossy and lossless may be mixed).
+hipError_t launch_group(const MatDesc* mats, int count, hipStream_t stream);
 
 }  // namespace ep

@@ -148,20 +148,31 @@ def test_lossless_other_dtypes(dt):
 
 
 def test_grouped_decode_matches_single():
+    """One grouped call over lossy matrices in four containers and lossless BF16 / U8 / FP32
+    matrices: the kernel balances the two kinds of tiles by cost within one launch."""
     rng = np.random.default_rng(7)
     streams, conts = [], []
     for i, (R, Cc, t) in enumerate([(256, 512, 3.0), (128, 1024, 6.0), (300, 700, 2.5), (64, 256, 4.5)]):
         w = (0.02 * rng.standard_t(5, (R, Cc))).astype(np.float32)
         streams.append(ep.compress(w, t)[0])
         conts.append([torch.bfloat16, torch.float8_e4m3fn, torch.int8, torch.float16][i])
+    lossless = [W.student_t(200, 600, 71), rng.integers(0, 255, (40, 300)).astype(np.uint8),
+                rng.normal(0, 1, (33, 257)).astype(np.float32)]
+    for x, code, tdt in zip(lossless, (ep.BF16, ep.U8, ep.F32), (torch.bfloat16, torch.uint8, torch.float32)):
+        streams.append(ep.lossless_compress(x, dtype=code)[0])
+        conts.append(tdt)
     hs = [ep.upload(s) for s in streams]
     outs = [torch.empty(h.shape, dtype=c, device="cuda") for h, c in zip(hs, conts)]
     scales = [torch.empty(h.shape[0], dtype=torch.float32, device="cuda") if c in (torch.float8_e4m3fn, torch.int8)
               else None for h, c in zip(hs, conts)]
     ep.decompress_many(hs, outs, scales)
     torch.cuda.synchronize()
-    for h, s, o, sc, c in zip(hs, streams, outs, scales, conts):
+    for i, (h, s, o, sc, c) in enumerate(zip(hs, streams, outs, scales, conts)):
         h.check()
+        if i >= 4:
+            x = lossless[i - 4]
+            assert np.array_equal(bits(o), x.view(np.uint32) if x.dtype == np.float32 else x)
+            continue
         odt = {torch.bfloat16: oracle.BF16, torch.float16: oracle.F16, torch.float8_e4m3fn: oracle.F8E4M3,
                torch.int8: oracle.I8}[c]
         want, wsc = oracle.decompress(s, odt, n_threads=8)
