@@ -93,7 +93,7 @@ def cpu_baseline(items, budget_s: float = 10.0):
                       f"oracle with {cores} threads in {dt:.1f} s"}
 
 
-def fused_gemm_section(torch, ep, reps: int = 10):
+def fused_gemm_section(torch, ep, reps: int = 15):
     """Fused decode + BF16 MFMA GEMM against the plain BF16 GEMM on the uncompressed weight.
 
     Workload: W = 0.02 t5 bf16 [8192, 8192] coded at 4.5 bpp, X ~ N(0, 1) bf16 [M, 8192],
@@ -112,33 +112,40 @@ def fused_gemm_section(torch, ep, reps: int = 10):
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     st = torch.cuda.current_stream()
 
-    def timed(fn):
-        for _ in range(2):
-            fn()
-        ds = []
+    def timed(fns):
+        """Median and min per-rep time (us) of each function; the functions take turns within
+        every rep, so clock and thermal drift affect them alike."""
+        for fn in fns:
+            for _ in range(2):
+                fn()
+        ds = [[] for _ in fns]
         for _ in range(reps):
-            flush.fill_(1.0)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(st)
-            fn()
-            b.record(st)
-            ds.append((a, b))
+            for i, fn in enumerate(fns):
+                flush.fill_(1.0)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(st)
+                fn()
+                b.record(st)
+                ds[i].append((a, b))
         torch.cuda.synchronize()
-        us = sorted(a.elapsed_time(b) * 1e3 for a, b in ds)
-        return us[len(us) // 2], us[0]
+        out = []
+        for d in ds:
+            us = sorted(a.elapsed_time(b) * 1e3 for a, b in d)
+            out.append((us[len(us) // 2], us[0]))
+        return out
 
     wdec = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
-    t_dec, _ = timed(lambda: layer.handle.decompress_into(wdec))
+    (t_dec, _), = timed([lambda: layer.handle.decompress_into(wdec)])
     layer.handle.check()
     out = {"workload": "W 0.02 t5 bf16 [8192, 8192] at 4.5 bpp, X N(0,1) bf16 [M, 8192], Y = X W^T bf16, "
                        "fp32 accumulate",
            "actual_bpp": round(bpp, 4), "stream_bytes": len(s), "decode_full_us": round(t_dec, 2),
-           "reps": reps, "timing": "median of per-rep HIP events, 1 GiB cache flush between reps"}
+           "reps": reps, "timing": "median of per-rep HIP events, the three variants interleaved within each "
+                                   "rep, 1 GiB cache flush before every timed call"}
     for M in (4096, 256, 16):
         X = Xf[:M].contiguous()
-        t_f, t_f_min = timed(lambda: layer(X))
-        t_o, _ = timed(lambda: ep.gemm_bf16(X, Wt))
-        t_t, _ = timed(lambda: torch.matmul(X, Wt.t()))
+        (t_f, t_f_min), (t_o, _), (t_t, _) = timed([lambda: layer(X), lambda: ep.gemm_bf16(X, Wt),
+                                                     lambda: torch.matmul(X, Wt.t())])
         layer.handle.check()
         fl = 2.0 * M * N * K
         out[f"M{M}"] = {

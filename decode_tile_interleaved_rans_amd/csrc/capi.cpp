@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <mutex>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -21,8 +22,6 @@ struct ep_handle {
     uint8_t* dev = nullptr;     // one allocation: stream copy | table blob | error flag
     size_t stream_off = 0, tables_off = 0, err_off = 0, bytes = 0;
     int device = 0;
-    uint16_t* scratch = nullptr;  // decoded weight slice for the linear forward (lazily allocated)
-    size_t scratch_bytes = 0;
 };
 
 namespace {
@@ -41,8 +40,9 @@ ep_status hip_fail(hipError_t e, const char* what) {
 
 size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Device decode tables: lut [t][slot] = symbol, fc [t][s] = f | c << 16, val [t][s] = the value
-// a lossy symbol stands for (doubled coordinate 2 (lo + s) + b, or the coset for table 0).
+// Device decode tables (layout in kernels.h): per table, the slot -> symbol LUT and one 8-byte
+// entry per symbol holding its frequency (bit 31: escape), its cumulative frequency plus the LDS
+// offset of the lookup's LUT group, and the value the symbol stands for.
 std::vector<uint8_t> build_tables(const ep::StreamView& v) {
     const int n = v.prob_bits;
     const size_t M = (size_t)1 << n;
@@ -103,6 +103,42 @@ hipError_t launch_all(const std::vector<ep::MatDesc>& ds, hipStream_t stream) {
         hipError_t e = ep::launch_group(ds.data() + i, n, stream);
         if (e != hipSuccess) return e;
     }
+    return hipSuccess;
+}
+
+// Library-owned device workspaces, one per (device, stream), grown on demand and kept until the
+// process ends (work queued on the stream may still use a workspace after a call returns).
+hipError_t workspace(int device, hipStream_t stream, size_t need, uint16_t** out) {
+    struct Entry {
+        int device;
+        hipStream_t stream;
+        uint16_t* ptr;
+        size_t bytes;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> pool;
+    std::lock_guard<std::mutex> lock(mu);
+    for (Entry& e : pool) {
+        if (e.device != device || e.stream != stream) continue;
+        if (e.bytes < need) {
+            // earlier calls on this stream may still read the old buffer: wait for them
+            hipError_t r = hipStreamSynchronize(stream);
+            if (r == hipSuccess) r = hipFree(e.ptr);
+            if (r != hipSuccess) return r;
+            e.ptr = nullptr;
+            e.bytes = 0;
+            r = hipMalloc(reinterpret_cast<void**>(&e.ptr), need);
+            if (r != hipSuccess) return r;
+            e.bytes = need;
+        }
+        *out = e.ptr;
+        return hipSuccess;
+    }
+    Entry e{device, stream, nullptr, need};
+    hipError_t r = hipMalloc(reinterpret_cast<void**>(&e.ptr), need);
+    if (r != hipSuccess) return r;
+    pool.push_back(e);
+    *out = e.ptr;
     return hipSuccess;
 }
 
@@ -227,7 +263,6 @@ ep_status ep_handle_info(const ep_handle* h, ep_info* out) {
 
 void ep_release(ep_handle* h) {
     if (!h) return;
-    if (h->scratch) (void)hipFree(h->scratch);
     if (h->dev) (void)hipFree(h->dev);
     delete h;
 }
@@ -298,13 +333,13 @@ ep_status ep_gemm_bf16(const void* dev_x, const void* dev_w, int64_t M, int64_t 
 }
 
 // Compressed linear forward. The weight is decoded once per call, one slice of output rows at a
-// time, into a scratch buffer of at most kSliceBytes, and each slice's GEMM writes its columns of
-// Y. A slice is large enough to keep every CU's decode block busy (>= 16 tile pairs per CU at
-// K = 8192) and small enough to stay in the 256 MB Infinity Cache between the decode that writes
-// it and the GEMM that reads it.
+// time, into the (device, stream) workspace of at most kSliceBytes, and each slice's GEMM writes
+// its columns of Y. A slice is large enough to keep every CU's decode block busy and, with the
+// activations, small enough to stay in the 256 MB Infinity Cache between the decode that writes
+// it and the GEMM that reads it (128 MiB measured best against 64 and 256 for M = 256 ... 4096).
 ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias, void* dev_y,
                             void* hip_stream) {
-    constexpr size_t kSliceBytes = 64u << 20;
+    constexpr size_t kSliceBytes = 128u << 20;
     if (!w) return fail(EP_EINVAL, "null handle");
     if (w->view.mode != EP_MODE_LOSSY_E8) return fail(EP_EUNSUPPORTED, "the linear forward takes a lossy stream");
     const int64_t N = w->view.rows, K = w->view.cols;
@@ -313,22 +348,18 @@ ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, co
     if (!dev_x || !dev_y) return fail(EP_EINVAL, "null pointer");
     if (K % 8 || M > INT32_MAX) return fail(EP_EINVAL, "in_features must be a multiple of 8");
     if (reinterpret_cast<uintptr_t>(dev_x) & 15) return fail(EP_EINVAL, "X must be 16-byte aligned");
-    ep_handle* h = const_cast<ep_handle*>(w);
     const int tr = w->view.tile_rows;
     int64_t slice = (int64_t)(kSliceBytes / (2 * (size_t)K)) / tr * tr;
     if (slice < tr) slice = tr;
     if (slice > N) slice = (N + tr - 1) / tr * tr;
     const size_t need = (size_t)slice * (size_t)K * 2;
-    if (h->scratch_bytes < need) {
-        if (h->scratch) (void)hipFree(h->scratch);
-        h->scratch = nullptr;
-        h->scratch_bytes = 0;
-        hipError_t e = hipMalloc(reinterpret_cast<void**>(&h->scratch), need);
-        if (e != hipSuccess) return hip_fail(e, "hipMalloc for the decoded weight slice");
-        h->scratch_bytes = need;
-    }
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    const ep::MatDesc full = desc_for(w, ep::CT_BF16, h->scratch, nullptr);
+    uint16_t* scratch = nullptr;
+    int dev = 0;
+    hipError_t we = hipGetDevice(&dev);
+    if (we == hipSuccess) we = workspace(dev, s, need, &scratch);
+    if (we != hipSuccess) return hip_fail(we, "hipMalloc for the linear forward workspace");
+    const ep::MatDesc full = desc_for(w, ep::CT_BF16, scratch, nullptr);
     for (int64_t r0 = 0; r0 < N; r0 += slice) {
         const int64_t rows = std::min<int64_t>(slice, N - r0);
         ep::MatDesc d = full;                  // rows r0 .. r0 + rows of the weight
@@ -338,7 +369,7 @@ ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, co
         d.rows = (uint32_t)rows;
         hipError_t e = ep::launch_group(&d, 1, s);
         if (e != hipSuccess) return hip_fail(e, "slice decode launch");
-        ep::GemmArgs g{static_cast<const uint16_t*>(dev_x), h->scratch,
+        ep::GemmArgs g{static_cast<const uint16_t*>(dev_x), scratch,
                        dev_bias ? static_cast<const uint16_t*>(dev_bias) + r0 : nullptr,
                        static_cast<uint16_t*>(dev_y) + r0, (int)M, (int)rows, (int)K, (int)K, (int)K, (int)N};
         e = ep::launch_gemm(g, s);

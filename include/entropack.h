@@ -125,16 +125,21 @@ ep_status ep_decompress_many(const ep_handle* const* hs, const ep_dtype* contain
 ep_status ep_decode_symbols(const ep_handle* h, int16_t* dev_q, void* hip_stream);
 
 /* Compressed linear layer forward: Y[M][N] = X[M][K] * W^T (+ bias), W = the decoded BF16
- * weight [N][K] of handle w, fp32 accumulation, BF16 output. Decoding is fused into the GEMM:
- * decoded tiles go to LDS as the MFMA B operand, and no decoded copy of W is written.
- *   dev_x: [M][K] bf16; dev_bias: [N] bf16 or NULL; dev_y: [M][N] bf16.
- * Requires a lossy stream. Asynchronous on hip_stream. */
+ * weight [N][K] of handle w, fp32 accumulation, BF16 output ("EntroPack PyTorch Guide", section
+ * "Replace one linear layer before a whole model"). The weight is decoded once per call, up to
+ * 128 MiB of BF16 rows at a time, into a library-owned workspace that stays in the Infinity
+ * Cache, and each slice is multiplied by the BF16 MFMA GEMM; no decoded copy of W outlives the
+ * call. The workspace belongs to the (device, hip_stream) pair: calls on one stream reuse it in
+ * order, calls on different streams get different workspaces; it is allocated on first use
+ * (hipMalloc, which may synchronize the device) and kept until the process ends.
+ *   dev_x: [M][K] bf16, 16-byte aligned; dev_bias: [N] bf16 or NULL; dev_y: [M][N] bf16.
+ * Requires a lossy stream and K % 8 == 0. Asynchronous on hip_stream. */
 ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias,
                             void* dev_y, void* hip_stream);
 
-/* Plain BF16 GEMM with the same tiling as ep_linear_forward, for overhead comparisons:
- * Y[M][N] = X[M][K] * W^T, X [M][K] bf16, W [N][K] bf16, Y [M][N] bf16, fp32 accumulation.
- * Asynchronous on hip_stream. */
+/* Plain BF16 GEMM, the one ep_linear_forward runs on each decoded slice, for overhead
+ * comparisons: Y[M][N] = X[M][K] * W^T, X [M][K] bf16, W [N][K] bf16, Y [M][N] bf16, fp32
+ * accumulation. Requires K % 8 == 0 and 16-byte aligned X and W. Asynchronous on hip_stream. */
 ep_status ep_gemm_bf16(const void* dev_x, const void* dev_w, int64_t M, int64_t N, int64_t K,
                        void* dev_y, void* hip_stream);
 

@@ -80,8 +80,8 @@ def test_linear_forward_matches_decoded_fp32_gemm(M, N, K, target):
 
 
 def test_linear_forward_with_bias_and_multi_slice():
-    # 5000 x 8192 weight: 64 MiB slices of 4096 rows -> two slices, the last one ragged
-    M, N, K = 64, 5000, 8192
+    # 5000 x 16384 weight: 128 MiB slices of 4096 rows -> two slices, the last one ragged
+    M, N, K = 64, 5000, 16384
     y, x, w_hat, b = linear_case(M, N, K, 4.0, seed=3, bias=True)
     assert rel_l2(y, x @ w_hat.T + b[None, :]) < 2e-2
 
