@@ -140,11 +140,13 @@ struct Tile {
 __device__ __forceinline__ void load_chunk(const Tile& t, __amdgpu_buffer_rsrc_t rs, uint32_t chunk, uint32_t* dst) {
     const uint32_t d = chunk * kChunkDw + t.l;
     const uint32_t off = t.gdw + 4u * d;
+    // only the tile's own words are fetched: other lanes take an out-of-range offset (reads 0);
+    // arithmetic rather than a select, which the backend would turn into branches around loads
+    const uint32_t lim = t.valid ? t.ndw : 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        // only the tile's own words are fetched: other lanes take an out-of-range offset (reads 0)
-        const uint32_t o = (t.valid && d + 32u * i < t.ndw) ? off + 128u * i : 0x80000000u;
-        dst[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, o, 0, 0);
+        const uint32_t oob = (uint32_t)((int32_t)(d + 32u * i - lim) >> 31) ^ 0xFFFFFFFFu;   // d + 32 i >= lim
+        dst[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, (off + 128u * i) | (oob & 0x80000000u), 0, 0);
     }
 }
 __device__ __forceinline__ void store_chunk(Tile& t, uint32_t chunk, const uint32_t* src) {
@@ -391,6 +393,10 @@ __device__ __forceinline__ void begin_pair(const MatDesc& M, __amdgpu_buffer_rsr
     P.sc_l = mine ? M.row_scale[my_row] : 0.0f;
     P.qm_l = 0;
     if constexpr (CT == CT_I8) P.qm_l = mine ? M.row_qmax[my_row] : 0u;
+    // Wait for these loads here, once per pair: first used inside the row loop, their wait would
+    // land inside it, on every row, and (the vector-memory counter being in order) would also
+    // wait for the ring chunk just prefetched.
+    asm volatile("" ::"v"(P.sc_l), "v"(P.qm_l), "v"(t.x));
 }
 
 template <int CT>
@@ -426,6 +432,10 @@ __device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Til
     PairRows P[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) begin_pair<CT>(M, rs, pair[c], pair[c] < pend, t[c], P[c]);
+    // A row's values are stored after the next row's ring top-up: the top-up waits for its chunk
+    // loads with the vector-memory counter, which also counts stores, so a store issued just
+    // before it would be waited for too; issued after it, the store has a whole row to drain.
+    float qp[C][8];
     for (int rr = 0; rr < M.tile_rows; ++rr) {
         int b[C];
         uint32_t base[C];
@@ -433,6 +443,10 @@ __device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Til
         float q[C][8];
 #pragma unroll
         for (int c = 0; c < C; ++c) top_up(t[c], rs);
+        if (rr > 0) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) store_row<CT>(M, t[c], P[c], rr - 1, qp[c], h);
+        }
 #pragma unroll
         for (int c = 0; c < C; ++c) b[c] = lo0 + (int)coset_step<N>(t[c], f0, f1);
         refill_all<C>(t);
@@ -473,8 +487,12 @@ __device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Til
             }
         }
 #pragma unroll
-        for (int c = 0; c < C; ++c) store_row<CT>(M, t[c], P[c], rr, q[c], h);
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) qp[c][j] = q[c][j];
     }
+#pragma unroll
+    for (int c = 0; c < C; ++c) store_row<CT>(M, t[c], P[c], M.tile_rows - 1, qp[c], h);
 #pragma unroll
     for (int c = 0; c < C; ++c) end_tile(t[c]);
 }
@@ -484,7 +502,10 @@ __device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Til
 // the other chain waits on LDS.
 template <int CT, int N>
 __device__ __forceinline__ void lossy_pairs(const MatDesc& M, const Tables& T, Tile* t, uint64_t p0, uint64_t p1) {
-    for (uint64_t p = p0 + (threadIdx.x >> 6); p < p1; p += kChains * kWaves) {
+    // the wave's index is uniform across its lanes: keep it (and so the pair, tile row and row
+    // addresses) in SGPRs
+    const uint64_t w0 = (uint64_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    for (uint64_t p = p0 + w0; p < p1; p += kChains * kWaves) {
         uint64_t pr[kChains];
 #pragma unroll
         for (int c = 0; c < kChains; ++c) pr[c] = p + (uint64_t)c * kWaves;
@@ -508,7 +529,8 @@ template <int P, int N>
 __device__ __forceinline__ void lossless_pairs(const MatDesc& M, const Tables& T, Tile& t, uint64_t p0, uint64_t p1) {
     using E = typename std::conditional<P == 1, uint8_t, typename std::conditional<P == 2, uint16_t, uint32_t>::type>::type;
     const __amdgpu_buffer_rsrc_t rs = payload_rsrc(M);
-    for (uint64_t pair = p0 + (threadIdx.x >> 6); pair < p1; pair += kWaves) {
+    const uint64_t w0 = (uint64_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    for (uint64_t pair = p0 + w0; pair < p1; pair += kWaves) {
         const uint32_t tr = (uint32_t)(pair / M.pairs_c);
         const uint32_t tc = 2 * (uint32_t)(pair % M.pairs_c) + (t.sh ? 1u : 0u);
         t.valid = tc < M.tiles_c;
