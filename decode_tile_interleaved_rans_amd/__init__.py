@@ -159,6 +159,35 @@ def stream_info(stream: bytes) -> dict:
     return info.as_dict()
 
 
+def save(path, stream: bytes, bias=None) -> None:
+    """Write a stream (and an optional bias vector) to a file. The stream is the whole artifact:
+    it is self-describing and versioned, and holds everything the decoder needs ("EntroPack
+    PyTorch Guide", sections "Test saved artifacts" and "Diagnose the common failure cases").
+    The file is a numpy .npz archive without pickled objects."""
+    import numpy as np
+    arrays = {"stream": np.frombuffer(stream, np.uint8)}
+    if bias is not None:
+        if isinstance(bias, np.ndarray):                 # BF16 bit patterns
+            arrays["bias_bf16"] = np.asarray(bias, np.uint16)
+        else:                                            # a torch tensor of any float dtype
+            torch = _torch()
+            b = bias.detach().to("cpu", torch.bfloat16).contiguous()
+            arrays["bias_bf16"] = b.view(torch.int16).numpy().view(np.uint16)
+    with open(path, "wb") as f:
+        np.savez(f, **arrays)
+
+
+def load(path):
+    """Read a file written by save(): returns (stream bytes, bias bf16 bits as uint16 or None).
+    The stream is validated before it is returned."""
+    import numpy as np
+    with np.load(path, allow_pickle=False) as z:
+        stream = z["stream"].tobytes()
+        bias = z["bias_bf16"].copy() if "bias_bf16" in z.files else None
+    stream_info(stream)
+    return stream, bias
+
+
 # ------------------------------------------------------------------------------------ device side
 class Handle:
     """A validated stream resident on the current GPU."""
@@ -275,6 +304,20 @@ class CompressedLinear:
     @property
     def actual_bpp(self) -> float:
         return self.handle.info["actual_bpp"]
+
+    def save(self, path) -> None:
+        """Write the compressed weight and the bias to a file (see save())."""
+        save(path, self.stream, self.bias)
+
+    @classmethod
+    def load(cls, path):
+        """Rebuild a layer from a file written by save(); the bias goes to the current GPU."""
+        stream, bias = load(path)
+        b = None
+        if bias is not None:
+            torch = _torch()
+            b = torch.from_numpy(bias.view("int16")).view(torch.bfloat16).cuda()
+        return cls(stream, b)
 
     def forward(self, x, stream=None):
         torch = _torch()

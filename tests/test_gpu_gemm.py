@@ -135,3 +135,28 @@ def test_from_linear_roundtrip():
     # lossy 5 bpp weights: the layer output stays close to the original layer
     assert rel_l2(y.float().cpu().numpy(), ref.numpy()) < 0.05
     assert layer.actual_bpp > 5.0
+
+
+def test_compressed_linear_save_and_reload_in_a_fresh_process(tmp_path):
+    """A compressed layer saved to disk and rebuilt by a new process gives the same forward
+    output, bit for bit."""
+    import os
+    import subprocess
+    import sys
+    lin = torch.nn.Linear(768, 320, bias=True)
+    layer = ep.CompressedLinear.from_linear(lin, 4.0)
+    x = bf16_tensor(W.activations(24, 768, 77))
+    y = layer(x.cuda())
+    torch.cuda.synchronize()
+    path = tmp_path / "layer.npz"
+    layer.save(path)
+    np.save(tmp_path / "x.npy", W.activations(24, 768, 77))
+    out = tmp_path / "y.npy"
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys, numpy as np, torch; sys.path.insert(0, %r); import decode_tile_interleaved_rans_amd as ep; "
+            "layer = ep.CompressedLinear.load(%r); "
+            "x = torch.from_numpy(np.load(%r).view(np.int16)).view(torch.bfloat16).cuda(); "
+            "y = layer(x); torch.cuda.synchronize(); np.save(%r, y.cpu().view(torch.int16).numpy())"
+            ) % (root, str(path), str(tmp_path / "x.npy"), str(out))
+    subprocess.run([sys.executable, "-c", code], check=True, timeout=300)
+    assert np.array_equal(np.load(out), y.cpu().view(torch.int16).numpy())

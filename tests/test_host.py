@@ -160,3 +160,37 @@ def test_bad_arguments():
     with pytest.raises(ep.EPError) as e:
         ep.compress(bad, 4.0)
     assert e.value.status == -4
+
+
+def test_saved_stream_reloads_in_a_fresh_process(tmp_path):
+    """Save / reload ("EntroPack PyTorch Guide", section "Test saved artifacts"): a stream and its
+    bias written to disk are read back by a new Python process, which decodes the stream with
+    the oracle; the result equals the oracle's decode of the original stream bit for bit."""
+    import subprocess
+    import sys
+    w = W.gaussian_with_outliers(96, 700, seed=21)
+    s, _ = ep.compress(w, 4.5)
+    bias = W.to_bf16_bits(np.linspace(-1, 1, 96))
+    path = tmp_path / "layer.npz"
+    ep.save(path, s, bias)
+    out = tmp_path / "decoded.npy"
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys, numpy as np; sys.path.insert(0, %r); import oracle, decode_tile_interleaved_rans_amd as ep; "
+            "s, b = ep.load(%r); q, _ = oracle.decompress(s, oracle.BF16); "
+            "np.save(%r, np.concatenate([q.ravel(), b]))") % (root, str(path), str(out))
+    subprocess.run([sys.executable, "-c", code], check=True, timeout=120)
+    got = np.load(out)
+    want, _ = oracle.decompress(s, oracle.BF16)
+    assert np.array_equal(got, np.concatenate([want.ravel(), bias]))
+
+
+def test_load_rejects_a_damaged_file(tmp_path):
+    w = W.gaussian_with_outliers(32, 256, seed=22)
+    s, _ = ep.compress(w, 4.0)
+    bad = bytearray(s)
+    bad[-3] ^= 0x5A                                        # payload byte: the CRC no longer matches
+    path = tmp_path / "bad.npz"
+    ep.save(path, bytes(bad))
+    with pytest.raises(ep.EPError) as e:
+        ep.load(path)
+    assert e.value.status == -2
