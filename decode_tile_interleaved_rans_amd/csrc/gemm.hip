@@ -1,15 +1,15 @@
 // gfx950 BF16 GEMM for the compressed linear layer: Y[M][N] = X[M][K] W[N][K]^T (+ bias), fp32
 // accumulation on the matrix cores (v_mfma_f32_32x32x16_bf16), BF16 output.
 //
-// Tiled kernels (gemm_nt). A block of WGM x WGN waves owns a BM x BN tile of Y and walks K in
-// steps of 64: both operand tiles (rows x 64 K of X and of W, K contiguous, as the MFMA wants 8
-// consecutive K per lane) are staged in LDS with a 16-byte row pad against bank conflicts,
-// double-buffered; global loads go through buffer resources (rows past the matrix and K past the
-// end read as zero) into two register stages, so the loads of step k + 2 are in flight while
-// step k feeds the MFMAs. Each wave computes its (BM / WGM) x (BN / WGN) part as 32 x 32 MFMA
-// tiles. Tile choice (launch_gemm): 256 x 256 with 16 waves when that still gives every CU a
-// block, 128 x 128 with 4 waves, or 64 x 64 with 4 waves for few output tiles; the skinny kernel
-// streams W straight into registers for M <= 64. Block order: consecutive block ids land on
+// Tiled kernels. A block of WGM x WGN waves owns a BM x BN tile of Y and walks K in steps of 64:
+// both operand tiles (rows x 64 K of X and of W, K contiguous, as the MFMA wants 8 consecutive K
+// per lane) are staged in LDS, double-buffered; global loads go through buffer resources (rows
+// past the matrix and K past the end read as zero). Each wave computes its (BM / WGM) x
+// (BN / WGN) part as 32 x 32 MFMA tiles. 256 x 256 tiles with 16 waves (gemm_dma) load straight
+// from global memory into LDS; 128 x 128 and 64 x 64 tiles with 4 waves (gemm_nt) go through two
+// register stages and a padded LDS layout. Tile choice (launch_gemm): 256 x 256 when every CU
+// gets a block, 128 x 128 when every CU gets two, else 64 x 64; the skinny kernel streams W
+// straight into registers for M <= 64. Block order: consecutive block ids land on
 // different XCDs, so each XCD gets a contiguous range of tiles, walked in groups of 4 M tiles so
 // that the blocks running together share X and W slices in that XCD's L2. Operand lane layout of
 // the 32x32x16 BF16 MFMA (checked on the device): lane l supplies A[l % 32][8 (l / 32) + i] and
@@ -187,6 +187,116 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt(GemmArgs g) {
         }
 }
 
+// Tiled kernel with direct global -> LDS loads (buffer_load ... lds): a wave's load instruction
+// writes its 64 lanes' 16 bytes to 1 KiB of LDS in lane order, 8 operand rows of 128 bytes, so no
+// registers stage the tiles. Rows are unpadded and their eight 16-byte K chunks swizzled (chunk c
+// of row r at slot c ^ (r % 8)), which keeps the MFMA fragment reads free of bank conflicts. Two
+// LDS stages: the loads of step k + 1 run while step k multiplies.
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int ROWS, int NW>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, int ld, int k0, int K, uint8_t* lds) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rr = lane >> 3, kc = (lane & 7) ^ rr;          // row within the 8-row group; its chunk
+    const int k = k0 + 8 * kc;
+#pragma unroll
+    for (int j = 0; j < ROWS / 8 / NW; ++j) {
+        const int g = wave + NW * j;                          // 8-row group of this instruction
+        const uint32_t off = (uint32_t)((8 * g + rr) * ld + k) * 2u | ((uint32_t)((K - 1 - k) >> 31) & kOob);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + 1024 * g), 16, off, 0, 0, 0);
+    }
+}
+
+template <int BM, int BN, int WGM, int WGN, bool BIAS>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_dma(GemmArgs g) {
+    constexpr int NW = WGM * WGN;
+    constexpr int TI = BM / WGM / 32, TJ = BN / WGN / 32;
+    constexpr int kStage = (BM + BN) * 128;                   // bytes of one LDS stage
+    __shared__ __align__(1024) uint8_t lds[2 * kStage];
+    const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+    const int nblk = tiles_m * tiles_n;
+    int b = blockIdx.x;
+    if (nblk % 8 == 0) b = (b % 8) * (nblk / 8) + b / 8;
+    constexpr int G = kGroupM;
+    const int per_group = G * tiles_n, first_m = (b / per_group) * G;
+    const int gsize = tiles_m - first_m < G ? tiles_m - first_m : G;
+    const int tm = first_m + (b % per_group) % gsize, tn = (b % per_group) / gsize;
+    const int m0 = __builtin_amdgcn_readfirstlane(tm * BM), n0 = __builtin_amdgcn_readfirstlane(tn * BN);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = (wave / WGN) * (BM / WGM), wn = (wave % WGN) * (BN / WGN);
+    const __amdgpu_buffer_rsrc_t rx = operand_rsrc<BM>(g.X, g.ldx, m0, g.M);
+    const __amdgpu_buffer_rsrc_t rw = operand_rsrc<BN>(g.W, g.ldw, n0, g.N);
+
+    f32x16 acc[TI][TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
+
+    dma_tile<BM, NW>(rx, g.ldx, 0, g.K, lds);
+    dma_tile<BN, NW>(rw, g.ldw, 0, g.K, lds + BM * 128);
+    __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0): this wave's tile loads landed
+    __syncthreads();
+    const int nk = (g.K + BK - 1) / BK;
+    for (int kt = 0; kt < nk; ++kt) {
+        uint8_t* cur = lds + (kt & 1) * kStage;
+        if (kt + 1 < nk) {
+            uint8_t* nxt = lds + ((kt + 1) & 1) * kStage;
+            dma_tile<BM, NW>(rx, g.ldx, (kt + 1) * BK, g.K, nxt);
+            dma_tile<BN, NW>(rw, g.ldw, (kt + 1) * BK, g.K, nxt + BM * 128);
+        }
+#pragma unroll
+        for (int ks = 0; ks < BK; ks += 16) {
+            bf16x8 a[TI], bb[TJ];
+            const int kc = ks / 8 + (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < TI; ++i) {
+                const int r = wm + 32 * i + (lane & 31);
+                a[i] = *reinterpret_cast<const bf16x8*>(cur + r * 128 + ((kc ^ (r & 7)) << 4));
+            }
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+                const int r = wn + 32 * j + (lane & 31);
+                bb[j] = *reinterpret_cast<const bf16x8*>(cur + BM * 128 + r * 128 + ((kc ^ (r & 7)) << 4));
+            }
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0): the next stage's loads landed
+        __syncthreads();                                     // ... for every wave; this stage is free
+    }
+
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+            const int col = n0 + wn + 32 * j + (lane & 31);
+            if (col >= g.N) continue;
+            float bv = 0.0f;
+            if constexpr (BIAS) bv = __uint_as_float((uint32_t)g.bias[col] << 16);
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const int row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const uint32_t pk = pack_bf16x2(acc[i][j][r] + bv, acc[i][j][r + 1] + bv);
+                if (row < g.M) g.Y[(size_t)row * g.ldy + col] = (uint16_t)(pk & 0xFFFFu);
+                if (row + 1 < g.M) g.Y[(size_t)(row + 1) * g.ldy + col] = (uint16_t)(pk >> 16);
+            }
+        }
+}
+
+template <int BM, int BN, int WGM, int WGN>
+hipError_t launch_dma(const GemmArgs& g, hipStream_t stream) {
+    const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+    if (g.bias)
+        hipLaunchKernelGGL((gemm_dma<BM, BN, WGM, WGN, true>), dim3(tiles), dim3(64 * WGM * WGN), 0, stream, g);
+    else
+        hipLaunchKernelGGL((gemm_dma<BM, BN, WGM, WGN, false>), dim3(tiles), dim3(64 * WGM * WGN), 0, stream, g);
+    return hipGetLastError();
+}
+
 // Skinny GEMM for M <= 64 (a few tokens): W is streamed once from HBM straight into MFMA
 // registers, no LDS staging. A block owns 16 output columns; its 8 waves split K (wave w takes
 // the 64-wide K chunks w, w + 8, ..., four chunks per iteration with all loads issued first),
@@ -298,7 +408,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
     if (g.M <= 32) return launch_skinny<2>(g, stream);
     if (g.M <= 64) return launch_skinny<4>(g, stream);
     const long tiles256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
-    if (tiles256 >= gemm_device_cus()) return launch_tiled<256, 256, 4, 4, kPrefetch>(g, stream);
+    if (tiles256 >= gemm_device_cus()) return launch_dma<256, 256, 4, 4>(g, stream);
     const long tiles128 = (long)((g.M + 127) / 128) * ((g.N + 127) / 128);
     if (tiles128 >= 2L * gemm_device_cus()) return launch_tiled<128, 128, 2, 2, kPrefetch>(g, stream);
     return launch_tiled<64, 64, 2, 2, kPrefetch>(g, stream);
