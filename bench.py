@@ -172,6 +172,9 @@ def main():
     ap.add_argument("--no-gemm", action="store_true", help="skip the fused decode + GEMM measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 256 MiB device copy first (reference for HBM byte counters)")
+    ap.add_argument("--gemm-only", action="store_true",
+                    help="profiling aid: run only the fused decode + GEMM measurement and print its JSON")
+    ap.add_argument("--gemm-reps", type=int, default=15, help="timed reps per variant in the GEMM measurement")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the decode path has no cross-GPU step (tiles, rows and "
@@ -188,6 +191,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.gemm_only:
+        print(json.dumps(fused_gemm_section(torch, ep, reps=args.gemm_reps)), flush=True)
+        return
     items, (R, C) = c2_items()
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16}
     step_out_bytes = sum(R * C * 2 for _ in items)
@@ -256,7 +262,7 @@ def main():
     if not args.no_gemm:
         sets.clear()
         torch.cuda.empty_cache()
-        fused = fused_gemm_section(torch, ep)
+        fused = fused_gemm_section(torch, ep, reps=args.gemm_reps)
     cpu = None
     if not args.no_cpu:
         log("timing the oracle on the host cores")
