@@ -11,15 +11,16 @@
 // a tile owns the 8-column block l of every tile row. One wave64 decodes two horizontally
 // adjacent tiles of one tile row: lanes 0-31 the even tile, lanes 32-63 the odd one, so each
 // decoded block row is one contiguous 1 KiB store (BF16) per wave and both halves share the
-// row's scale. A launch covers up to 32 matrices; each block of 16 waves serves one matrix,
-// stages that matrix's decode tables in LDS, and walks its range of tile pairs.
+// row's scale. A launch covers up to 32 matrices (lossy and lossless alike); a persistent block
+// of 16 waves per CU takes an equal share of the launch's decode cost, stages the decode tables
+// of each matrix its share touches in LDS, and walks that matrix's tile pairs.
 //
-// Word staging. Every half-wave keeps a 512-word LDS ring of its tile's word stream, filled by
+// Word staging. Every half-wave keeps a 1024-word LDS ring of its tile's word stream, filled by
 // coalesced 512-byte chunk loads that are issued one chunk ahead, so the serial rANS chain only
-// ever waits on LDS. Every three steps the ring is topped up until it holds more than three
-// steps can consume (3 x 64 words), so the steps need no bounds checks; a damaged stream can
-// only read stale ring words, and is caught by the end-of-tile checks. Lossless tiles top up
-// once per row (once per four elements for 4-byte elements).
+// ever waits on LDS. Before each block row the ring is topped up until it holds more than a row
+// can consume (9 steps x 64 words), so the steps need no bounds checks; a damaged stream can
+// only read stale ring words, and is caught by the end-of-tile checks. Lossless tiles top up once
+// per row (once per four elements for 4-byte elements).
 //
 // Per decoding step every lane looks up its slot in the LDS LUT (one byte read), then reads the
 // symbol's 8-byte entry (frequency, cumulative frequency, decoded value) and updates its state;
@@ -184,8 +185,9 @@ __device__ __forceinline__ void begin_tile(const MatDesc& M, __amdgpu_buffer_rsr
     __builtin_amdgcn_wave_barrier();
 }
 
-// Keep more than three steps' worst-case consumption (3 x 64 words) in the ring: after this, the
-// ring holds more than kRingWords - kChunkWords = 256 unread words, or the rest of the tile.
+// After a top-up the ring holds more than kRingWords - kChunkWords unread words (768 with the
+// 1024-word ring: more than a block row's worst case of 9 steps x 64 words; 256 with a 512-word
+// ring, which then needs kTopUps = 3 top-ups per row), or the rest of the tile.
 __device__ __forceinline__ void top_up(Tile& t, __amdgpu_buffer_rsrc_t rs) {
     while (t.fill < t.nwords && t.fill - t.pos <= kRingWords - kChunkWords) {
         store_chunk(t, t.fill / kChunkWords, t.pf);
