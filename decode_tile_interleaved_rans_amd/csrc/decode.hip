@@ -359,7 +359,20 @@ __device__ __forceinline__ void store_block(const MatDesc& M, uint32_t row, uint
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = Conv<CT>::f(q[j], alpha, h, k, magic);
     }
-    if (col0 + 8 <= M.cols && (M.cols & 7) == 0) {
+    if ((M.cols * (uint32_t)sizeof(T)) % 4 == 0) {
+        // one unconditional buffer store per row: the resource spans this row, so dwords past its
+        // end are dropped by the bounds check (whole dwords, as the row length is a multiple of 4)
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+            out, 0, (int)__builtin_amdgcn_readfirstlane((int)(M.cols * sizeof(T))), 0x00020000);
+        const uint32_t off = col0 < M.cols ? col0 * (uint32_t)sizeof(T) : 0x80000000u;
+        if constexpr (sizeof(T) == 2) {
+            const uint4 d = make_uint4(v[0] | v[1] << 16, v[2] | v[3] << 16, v[4] | v[5] << 16, v[6] | v[7] << 16);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, d), ro, off, 0, 0);
+        } else {
+            const uint2 d = make_uint2(v[0] | v[1] << 8 | v[2] << 16 | v[3] << 24, v[4] | v[5] << 8 | v[6] << 16 | v[7] << 24);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, d), ro, off, 0, 0);
+        }
+    } else if (col0 + 8 <= M.cols && (M.cols & 7) == 0) {
         if constexpr (sizeof(T) == 2) {
             *reinterpret_cast<uint4*>(out + col0) =
                 make_uint4(v[0] | v[1] << 16, v[2] | v[3] << 16, v[4] | v[5] << 16, v[6] | v[7] << 16);
@@ -367,7 +380,7 @@ __device__ __forceinline__ void store_block(const MatDesc& M, uint32_t row, uint
             *reinterpret_cast<uint2*>(out + col0) =
                 make_uint2(v[0] | v[1] << 8 | v[2] << 16 | v[3] << 24, v[4] | v[5] << 8 | v[6] << 16 | v[7] << 24);
         }
-    } else {
+    } else if (col0 < M.cols) {
         for (int j = 0; j < 8; ++j)
             if (col0 + j < M.cols) out[col0 + j] = (T)v[j];
     }
@@ -406,7 +419,7 @@ __device__ __forceinline__ void store_row(const MatDesc& M, const Tile& t, const
                                           float h) {
     const uint32_t row = P.row0 + rr;
     const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, P.sc_l), rr));
-    if (row >= M.rows || !t.valid) return;
+    if (row >= M.rows) return;
     const float alpha = h * sc;
     uint32_t k = 1, magic = 0;
     if constexpr (CT == CT_I8) {
@@ -414,8 +427,8 @@ __device__ __forceinline__ void store_row(const MatDesc& M, const Tile& t, const
         k = qm > 127u ? (qm + 126u) / 127u : 1u;
         magic = 0xFFFFFFFFu / (2u * k) + 1u;
     }
-    const uint32_t col0 = P.tc * 256 + 8 * t.l;
-    if (col0 < M.cols) store_block<CT>(M, row, col0, q, alpha, h, k, magic);
+    const uint32_t col0 = t.valid ? P.tc * 256 + 8 * t.l : 0xFFFFFFF0u;     // no tile: out of range
+    store_block<CT>(M, row, col0, q, alpha, h, k, magic);
     if constexpr (CT == CT_F8E4M3 || CT == CT_I8) {
         if (P.tc == 0 && t.l == 0) M.scale_out[row] = CT == CT_F8E4M3 ? sc : alpha * (float)k;
     }
