@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libep_oracle.so")
 
 # element type codes shared by the stream header
 F32, BF16, F16, F8E4M3, I8, U8 = 0, 1, 2, 3, 4, 5
-LOSSY, LOSSLESS = 0, 1
+LOSSY, LOSSLESS, LOSSLESS_EXP = 0, 1, 2
 STATUS = {0: "ok", -1: "invalid argument", -2: "corrupt stream", -3: "unsupported", -4: "out of range",
           -6: "out of memory"}
 

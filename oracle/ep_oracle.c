@@ -31,6 +31,8 @@
  *   rate search            pinned: monotone estimate, Gaussian closed form, |payload - target|
  *   containers             pinned: library casts (torch CPU) for BF16/FP16/FP8, integer closed form
  *   lossless byte planes   pinned: bit-exact round trips on special values
+ *   exponent-coded BF16    pinned: bit-exact round trips on special values, raw plane closed
+ *                          form, exponent table from the exponent histogram
  *   accounting             pinned: identity actual_bpp = 8 * bytes / (R * C)
  */
 #include <math.h>
@@ -47,7 +49,7 @@
 #define OR_ENOMEM (-6)
 
 enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_F8E4M3 = 3, DT_I8 = 4, DT_U8 = 5 };
-enum { MODE_LOSSY = 0, MODE_LOSSLESS = 1 };
+enum { MODE_LOSSY = 0, MODE_LOSSLESS = 1, MODE_LOSSLESS_EXP = 2 };
 
 #define LANES 32
 #define TILE_COLS 256
@@ -675,14 +677,16 @@ float or_select_step(const void* w, int dt, int64_t R, int64_t C, double target)
 /* Stream layout (reading). Little-endian. A 128-byte header, then sections, each starting at a */
 /* 16-byte boundary: row_scale f32[R], row_qmax u16[R] (both empty in lossless mode), tables    */
 /* (per table: i16 lo, u16 S, u16 escape frequency, u16 freq[S]), tile_index u32[n_tiles + 1]   */
-/* (offsets in 4-byte units from the payload start), payload. [G, "Start with a tensor round    */
-/* trip"]: the reported bitrate includes the metadata, so actual_bpp = 8 * total bytes / (R C). */
+/* (offsets in 4-byte units from the payload start), in the exponent-coded mode the raw plane   */
+/* u8[Rp][Cp] (offset and CRC-32 in header bytes 96 and 104), payload. [G, "Start with a tensor */
+/* round trip"]: the reported bitrate includes the metadata, so actual_bpp = 8 total / (R C).   */
 /* ------------------------------------------------------------------------------------------ */
 enum {
     H_MAGIC = 0, H_VERSION = 4, H_MODE = 6, H_DTYPE = 7, H_ROWS = 8, H_COLS = 12,
     H_TILE_ROWS = 16, H_TILE_COLS = 18, H_LANES = 20, H_PROB_BITS = 22, H_NTABLES = 23,
     H_STEP = 24, H_TARGET = 28, H_NTILES = 32, H_NESC = 36, H_OFF_SCALE = 40, H_OFF_QMAX = 48,
-    H_OFF_TABLES = 56, H_OFF_INDEX = 64, H_OFF_PAYLOAD = 72, H_TOTAL = 80, H_CRC = 88
+    H_OFF_TABLES = 56, H_OFF_INDEX = 64, H_OFF_PAYLOAD = 72, H_TOTAL = 80, H_CRC = 88,
+    H_OFF_RAW = 96, H_RAW_CRC = 104    /* exponent-coded mode only; zero in the other modes */
 };
 
 static size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
@@ -697,6 +701,8 @@ typedef struct {
     const uint8_t* index_bytes;
     const uint8_t* payload;
     uint64_t payload_len;
+    const uint8_t* raw;             /* exponent-coded mode: sign/mantissa bytes [Rp][Cp] */
+    uint64_t raw_len;
     int32_t lo[N_LOSSY_TABLES];
     int32_t S[N_LOSSY_TABLES];
     uint32_t freq[N_LOSSY_TABLES][256];
@@ -719,14 +725,15 @@ static int parse_stream(const uint8_t* s, size_t len, parsed* P) {
     P->target = f32_from_bits(get32(s + H_TARGET));
     P->n_tiles = get32(s + H_NTILES);
     P->n_esc = get32(s + H_NESC);
-    if (P->mode != MODE_LOSSY && P->mode != MODE_LOSSLESS) return OR_ECORRUPT;
+    if (P->mode != MODE_LOSSY && P->mode != MODE_LOSSLESS && P->mode != MODE_LOSSLESS_EXP) return OR_ECORRUPT;
+    if (P->mode == MODE_LOSSLESS_EXP && P->dtype != DT_BF16) return OR_ECORRUPT;
     if (P->mode == MODE_LOSSY && P->dtype != DT_F32 && P->dtype != DT_BF16 && P->dtype != DT_F16)
         return OR_ECORRUPT;
     if (P->mode == MODE_LOSSLESS && elem_bytes(P->dtype) == 0) return OR_ECORRUPT;
     if (P->tile_rows != 16 && P->tile_rows != 32) return OR_ECORRUPT;
     if (get16(s + H_TILE_COLS) != TILE_COLS || get16(s + H_LANES) != LANES) return OR_ECORRUPT;
     if (P->prob_bits < 10 || P->prob_bits > 12) return OR_ECORRUPT;
-    int want_tables = P->mode == MODE_LOSSY ? N_LOSSY_TABLES : dtype_planes(P->dtype);
+    int want_tables = P->mode == MODE_LOSSY ? N_LOSSY_TABLES : P->mode == MODE_LOSSLESS_EXP ? 1 : dtype_planes(P->dtype);
     if (P->n_tables != want_tables) return OR_ECORRUPT;
     if (P->mode == MODE_LOSSY && !(isfinite(P->step) && P->step > 0.0f)) return OR_ECORRUPT;
     P->Rp = ceil_div(P->R, P->tile_rows) * P->tile_rows;
@@ -748,6 +755,15 @@ static int parse_stream(const uint8_t* s, size_t len, parsed* P) {
     P->payload = s + o_pl;
     P->payload_len = total - o_pl;
     if (P->payload_len % 4) return OR_ECORRUPT;
+    uint64_t o_raw = get64(s + H_OFF_RAW);
+    if (P->mode == MODE_LOSSLESS_EXP) {
+        P->raw_len = (uint64_t)P->Rp * (uint64_t)P->Cp;
+        if (o_raw % 16 || o_raw < o_ix + 4 * ((uint64_t)P->n_tiles + 1) || o_raw + P->raw_len > o_pl) return OR_ECORRUPT;
+        P->raw = s + o_raw;
+        if (crc32_ieee(P->raw, (size_t)P->raw_len) != get32(s + H_RAW_CRC)) return OR_ECORRUPT;
+    } else if (o_raw != 0 || get32(s + H_RAW_CRC) != 0) {
+        return OR_ECORRUPT;
+    }
     /* tables */
     uint32_t M = 1u << P->prob_bits;
     uint64_t pos = o_tb;
@@ -759,7 +775,7 @@ static int parse_stream(const uint8_t* s, size_t len, parsed* P) {
         pos += 6;
         int maxS = P->mode == MODE_LOSSY ? 255 : 256;
         if (S < 1 || S > maxS || pos + 2 * (uint64_t)S > o_ix) return OR_ECORRUPT;
-        if (P->mode == MODE_LOSSLESS && (lo != 0 || S != 256 || esc != 0)) return OR_ECORRUPT;
+        if (P->mode != MODE_LOSSY && (lo != 0 || S != 256 || esc != 0)) return OR_ECORRUPT;
         if (P->mode == MODE_LOSSY && lo + S - 1 > 32767) return OR_ECORRUPT;
         if (P->mode == MODE_LOSSY && t == 0 && (lo < 0 || lo + S - 1 > 1 || esc != 0)) return OR_ECORRUPT;
         uint64_t sum = esc;
@@ -824,7 +840,8 @@ static int serialize(bytes_out* o, int mode, int dt, int64_t R, int64_t C, int t
                      int n_tables, const int32_t* lo, const int32_t* S, uint32_t (*f)[256],
                      float step, float target, const float* scale, const uint16_t* qmax,
                      const uint32_t* tile_off /* [n_tiles + 1], 4-byte units */, uint32_t n_tiles,
-                     const uint8_t* payload, uint64_t payload_len, uint32_t n_esc) {
+                     const uint8_t* payload, uint64_t payload_len, uint32_t n_esc,
+                     const uint8_t* raw /* exponent-coded mode, else NULL */, uint64_t raw_len) {
     uint64_t rows_meta = mode == MODE_LOSSY ? (uint64_t)R : 0;
     uint64_t tables_len = 0;
     for (int t = 0; t < n_tables; ++t) tables_len += 6 + 2 * (uint64_t)S[t];
@@ -832,7 +849,8 @@ static int serialize(bytes_out* o, int mode, int dt, int64_t R, int64_t C, int t
     uint64_t o_qm = align16(o_sc + 4 * rows_meta);
     uint64_t o_tb = align16(o_qm + 2 * rows_meta);
     uint64_t o_ix = align16(o_tb + tables_len);
-    uint64_t o_pl = align16(o_ix + 4 * ((uint64_t)n_tiles + 1));
+    uint64_t o_raw = raw ? align16(o_ix + 4 * ((uint64_t)n_tiles + 1)) : 0;
+    uint64_t o_pl = raw ? align16(o_raw + raw_len) : align16(o_ix + 4 * ((uint64_t)n_tiles + 1));
     uint64_t total = o_pl + payload_len;
     if (out_reserve(o, (size_t)total) != OR_OK) return OR_ENOMEM;
     uint8_t* s = o->buf;
@@ -859,6 +877,11 @@ static int serialize(bytes_out* o, int mode, int dt, int64_t R, int64_t C, int t
     put64(s + H_OFF_PAYLOAD, o_pl);
     put64(s + H_TOTAL, total);
     put32(s + H_CRC, crc32_ieee(payload, (size_t)payload_len));
+    if (raw) {
+        put64(s + H_OFF_RAW, o_raw);
+        put32(s + H_RAW_CRC, crc32_ieee(raw, (size_t)raw_len));
+        memcpy(s + o_raw, raw, (size_t)raw_len);
+    }
     for (uint64_t r = 0; r < rows_meta; ++r) {
         put32(s + o_sc + 4 * r, bits_from_f32(scale[r]));
         put16(s + o_qm + 2 * r, qmax[r]);
@@ -981,7 +1004,7 @@ static int encode_lossy(const void* w, int dt, int64_t R, int64_t C, double targ
             tile_off[tr * tc_n + tc + 1] = (uint32_t)(pl.len / 4);
         }
     rc = serialize(o, MODE_LOSSY, dt, R, C, tile_rows, prob_bits, N_LOSSY_TABLES, lo, S, f, step,
-                   (float)target, scale, qmax, tile_off, n_tiles, pl.buf, pl.len, n_esc);
+                   (float)target, scale, qmax, tile_off, n_tiles, pl.buf, pl.len, n_esc, NULL, 0);
     free(pl.buf);
 done:
     for (int t = 0; t < N_LOSSY_TABLES; ++t) { free(h[t].hist); rans_table_free(&RT[t]); }
@@ -1056,10 +1079,78 @@ static int encode_lossless(const void* w, int dt, int64_t R, int64_t C, int prob
             tile_off[tr * tc_n + tc + 1] = (uint32_t)(pl.len / 4);
         }
     rc = serialize(o, MODE_LOSSLESS, dt, R, C, tile_rows, prob_bits, P, lo, S, f, 0.0f, 0.0f, NULL, NULL,
-                   tile_off, n_tiles, pl.buf, pl.len, 0);
+                   tile_off, n_tiles, pl.buf, pl.len, 0, NULL, 0);
 done:
     for (int p = 0; p < 4; ++p) rans_table_free(&RT[p]);
     free(pl.buf); free(tab); free(sym); free(esc); free(stack); free(tile_off);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Exponent-coded lossless BF16. [G, "Choose a compression contract"] names a DFloat11 config   */
+/* for lossless BF16 without describing it. Reading (after the published DFloat11 idea): the    */
+/* 8-bit exponent of every element is entropy coded, here with the same tile rANS as the other  */
+/* modes (one order-0 table over 256 symbols, one step per element, steps row -> element,      */
+/* lane l owning columns 8l..8l+7 of the tile), and sign and mantissa are stored uncoded as one */
+/* byte per element, (sign << 7) | mantissa, in a plane [Rp][Cp] laid out like the padded       */
+/* matrix (padding elements are +0.0: exponent 0 and raw byte 0).                              */
+/* ------------------------------------------------------------------------------------------ */
+static uint32_t bf16_exponent(uint32_t v) { return (v >> 7) & 0xFFu; }
+static uint32_t bf16_raw_byte(uint32_t v) { return ((v >> 8) & 0x80u) | (v & 0x7Fu); }
+static uint32_t bf16_join(uint32_t e, uint32_t r) { return ((r & 0x80u) << 8) | (e << 7) | (r & 0x7Fu); }
+
+static int encode_lossless_exp(const void* w, int64_t R, int64_t C, int prob_bits, int tile_rows, bytes_out* o) {
+    int rc = OR_OK;
+    int64_t Rp = ceil_div(R, tile_rows) * tile_rows, Cp = ceil_div(C, TILE_COLS) * TILE_COLS;
+    uint64_t cnt[256];
+    uint32_t f[N_LOSSY_TABLES][256];
+    int32_t lo[1] = { 0 }, S[1] = { 256 };
+    rans_table RT[1];
+    memset(cnt, 0, sizeof cnt);
+    memset(RT, 0, sizeof RT);
+    uint8_t *tab = NULL, *sym = NULL, *raw = NULL;
+    uint16_t *esc = NULL, *stack = NULL;
+    uint32_t* tile_off = NULL;
+    bytes_out pl = { NULL, 0, 0 };
+    raw = (uint8_t*)calloc((size_t)(Rp * Cp > 0 ? Rp * Cp : 1), 1);
+    if (!raw) { rc = OR_ENOMEM; goto done; }
+    for (int64_t r = 0; r < Rp; ++r)
+        for (int64_t c = 0; c < Cp; ++c) {
+            uint32_t v = (r < R && c < C) ? elem_bits(w, 2, r * C + c) : 0;
+            cnt[bf16_exponent(v)]++;
+            raw[r * Cp + c] = (uint8_t)bf16_raw_byte(v);
+        }
+    if ((rc = or_normalize(cnt, prob_bits, f[0])) != OR_OK) goto done;
+    if ((rc = rans_table_init(&RT[0], f[0], prob_bits)) != OR_OK) goto done;
+    int64_t tr_n = Rp / tile_rows, tc_n = Cp / TILE_COLS;
+    uint32_t n_tiles = (uint32_t)(tr_n * tc_n);
+    int n_steps = tile_rows * 8;
+    size_t tile_cap = 4 * LANES + 4 * (size_t)LANES * n_steps + 4;
+    tab = (uint8_t*)calloc((size_t)n_steps * LANES, 1);
+    sym = (uint8_t*)malloc((size_t)n_steps * LANES);
+    esc = (uint16_t*)calloc((size_t)n_steps * LANES, sizeof(uint16_t));
+    stack = (uint16_t*)malloc(sizeof(uint16_t) * 64 * (size_t)n_steps + 2);
+    tile_off = (uint32_t*)malloc(sizeof(uint32_t) * ((size_t)n_tiles + 1));
+    if (!tab || !sym || !esc || !stack || !tile_off) { rc = OR_ENOMEM; goto done; }
+    tile_off[0] = 0;
+    for (int64_t tr = 0; tr < tr_n; ++tr)
+        for (int64_t tc = 0; tc < tc_n; ++tc) {
+            for (int rr = 0; rr < tile_rows; ++rr)
+                for (int e = 0; e < 8; ++e)
+                    for (int l = 0; l < LANES; ++l) {
+                        int64_t r = tr * tile_rows + rr, c = tc * TILE_COLS + 8 * l + e;
+                        uint32_t v = (r < R && c < C) ? elem_bits(w, 2, r * C + c) : 0;
+                        sym[(rr * 8 + e) * LANES + l] = (uint8_t)bf16_exponent(v);
+                    }
+            if ((rc = out_reserve(&pl, tile_cap)) != OR_OK) goto done;
+            pl.len += rans_encode_tile(RT, prob_bits, n_steps, tab, sym, esc, -1, stack, pl.buf + pl.len);
+            tile_off[tr * tc_n + tc + 1] = (uint32_t)(pl.len / 4);
+        }
+    rc = serialize(o, MODE_LOSSLESS_EXP, DT_BF16, R, C, tile_rows, prob_bits, 1, lo, S, f, 0.0f, 0.0f, NULL, NULL,
+                   tile_off, n_tiles, pl.buf, pl.len, 0, raw, (uint64_t)(Rp * Cp));
+done:
+    rans_table_free(&RT[0]);
+    free(pl.buf); free(tab); free(sym); free(esc); free(stack); free(tile_off); free(raw);
     return rc;
 }
 
@@ -1079,6 +1170,9 @@ int or_compress(const void* w, int src_dtype, int64_t rows, int64_t cols, int mo
     } else if (mode == MODE_LOSSLESS) {
         if (elem_bytes(src_dtype) == 0) return OR_EUNSUPPORTED;
         rc = encode_lossless(w, src_dtype, rows, cols, prob_bits, tile_rows, &o);
+    } else if (mode == MODE_LOSSLESS_EXP) {
+        if (src_dtype != DT_BF16) return OR_EUNSUPPORTED;
+        rc = encode_lossless_exp(w, rows, cols, prob_bits, tile_rows, &o);
     } else {
         return OR_EINVAL;
     }
@@ -1184,6 +1278,33 @@ static int decode_lossless_tile(const parsed* P, const decoder_tables* D, uint32
     return OR_OK;
 }
 
+/* Decode tile `tile` of an exponent-coded stream into BF16 bit patterns vt[tile_rows][256]. */
+static int decode_exp_tile(const parsed* P, const decoder_tables* D, uint32_t tile, uint32_t* vt,
+                           uint8_t* sym, uint16_t* esc) {
+    uint64_t a = get32(P->index_bytes + 4 * (uint64_t)tile), b = get32(P->index_bytes + 4 * ((uint64_t)tile + 1));
+    lossless_ctx ctx = { 1 };
+    int n_steps = P->tile_rows * 8;
+    int rc = rans_decode_tile(D->T, P->prob_bits, n_steps, P->payload + 4 * a, (size_t)(4 * (b - a)),
+                              lossless_tables, &ctx, -1, sym, esc, NULL);
+    if (rc != OR_OK) return rc;
+    int64_t tr = tile / P->tiles_c, tc = tile % P->tiles_c;
+    for (int rr = 0; rr < P->tile_rows; ++rr)
+        for (int e = 0; e < 8; ++e)
+            for (int l = 0; l < LANES; ++l) {
+                int64_t r = tr * P->tile_rows + rr, c = tc * TILE_COLS + 8 * l + e;
+                uint32_t rb = P->raw[r * P->Cp + c];
+                vt[rr * TILE_COLS + 8 * l + e] = bf16_join(sym[(rr * 8 + e) * LANES + l], rb);
+            }
+    return OR_OK;
+}
+
+/* Decode tile `tile` of either lossless mode. */
+static int decode_bits_tile(const parsed* P, const decoder_tables* D, uint32_t tile, uint32_t* vt,
+                            uint8_t* sym, uint16_t* esc) {
+    return P->mode == MODE_LOSSLESS_EXP ? decode_exp_tile(P, D, tile, vt, sym, esc)
+                                        : decode_lossless_tile(P, D, tile, vt, sym, esc);
+}
+
 static int container_bytes(int ct) { return elem_bytes(ct); }
 
 /* One reconstructed element of a lossy stream, written as container `ct` at dst. */
@@ -1242,7 +1363,7 @@ static void* decode_worker(void* arg) {
     for (int64_t t = J->t_begin; t < J->t_end; ++t) {
         int64_t tr = t / P->tiles_c, tc = t % P->tiles_c;
         int rc = P->mode == MODE_LOSSY ? decode_lossy_tile(P, J->D, (uint32_t)t, qt, bt, sym, esc)
-                                       : decode_lossless_tile(P, J->D, (uint32_t)t, vt, sym, esc);
+                                       : decode_bits_tile(P, J->D, (uint32_t)t, vt, sym, esc);
         if (rc != OR_OK) { J->rc = rc; goto done; }
         for (int rr = 0; rr < P->tile_rows; ++rr) {
             int64_t r = tr * P->tile_rows + rr;
@@ -1296,7 +1417,7 @@ static int run_decode(const parsed* P, int container, uint8_t* out, int16_t* qou
 }
 
 static int container_ok(const parsed* P, int container) {
-    if (P->mode == MODE_LOSSLESS) return container == P->dtype;
+    if (P->mode != MODE_LOSSY) return container == P->dtype;
     return container == DT_BF16 || container == DT_F16 || container == DT_F8E4M3 || container == DT_I8;
 }
 
@@ -1350,7 +1471,7 @@ int or_decompress_tiles(const uint8_t* s, size_t len, int container, const uint3
         if (tiles[i] >= P.n_tiles) { rc = OR_EINVAL; break; }
         int64_t tr = tiles[i] / P.tiles_c;
         rc = P.mode == MODE_LOSSY ? decode_lossy_tile(&P, &D, tiles[i], qt, bt, sym, esc)
-                                  : decode_lossless_tile(&P, &D, tiles[i], vt, sym, esc);
+                                  : decode_bits_tile(&P, &D, tiles[i], vt, sym, esc);
         if (rc != OR_OK) break;
         for (int rr = 0; rr < P.tile_rows; ++rr) {
             int64_t r = tr * P.tile_rows + rr;
@@ -1376,16 +1497,18 @@ int or_decompress_tiles(const uint8_t* s, size_t len, int container, const uint3
 }
 
 /* Header fields and section sizes of a validated stream, for the accounting tests.
- * info[0..11] = R, C, mode, dtype, tile_rows, prob_bits, n_tiles, n_escapes, payload bytes,
- * metadata bytes (total - payload), state bytes (4 * 32 * n_tiles), total bytes;
+ * info[0..11] = R, C, mode, dtype, tile_rows, prob_bits, n_tiles, n_escapes, payload bytes (the
+ * tile payload, plus the raw plane in the exponent-coded mode), metadata bytes (total - payload),
+ * state bytes (4 * 32 * n_tiles), total bytes;
  * fstep receives the step and target. */
 int or_stream_info(const uint8_t* s, size_t len, int64_t* info, float* fstep) {
     parsed P;
     int rc = parse_stream(s, len, &P);
     if (rc != OR_OK) return rc;
     info[0] = P.R; info[1] = P.C; info[2] = P.mode; info[3] = P.dtype; info[4] = P.tile_rows;
-    info[5] = P.prob_bits; info[6] = P.n_tiles; info[7] = P.n_esc; info[8] = (int64_t)P.payload_len;
-    info[9] = (int64_t)(len - P.payload_len); info[10] = 4ll * LANES * P.n_tiles; info[11] = (int64_t)len;
+    info[5] = P.prob_bits; info[6] = P.n_tiles; info[7] = P.n_esc;
+    info[8] = (int64_t)(P.payload_len + P.raw_len);       /* coded words plus uncoded raw bytes */
+    info[9] = (int64_t)(len - P.payload_len - P.raw_len); info[10] = 4ll * LANES * P.n_tiles; info[11] = (int64_t)len;
     fstep[0] = P.step;
     fstep[1] = P.target;
     return OR_OK;

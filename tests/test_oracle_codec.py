@@ -298,3 +298,102 @@ def test_corrupt_and_unsupported_streams(c1_stream):
     with pytest.raises(oracle.OracleError) as e:
         oracle.decompress(sl, oracle.F16)             # no silent cast of a lossless stream
     assert e.value.rc == -3
+
+
+# ---------------------------------------------------------------- exponent-coded lossless BF16
+# Reading of the DFloat11 config the guide names for lossless BF16 ("Choose a compression
+# contract"): the 8-bit exponent is entropy coded with the tile rANS, sign and mantissa are kept
+# uncoded as one byte per element in a raw plane (offset in header bytes 96..103, its CRC-32 in
+# 104..107).
+def header_field(s: bytes, off: int, size: int) -> int:
+    return int.from_bytes(s[off:off + size], "little")
+
+
+def exp_cases():
+    cases = {k: v for k, v in lossless_cases().items() if v[1] == oracle.BF16}
+    rng = np.random.default_rng(11)
+    cases["ragged_5x9"] = (W.to_bf16_bits(rng.normal(0, 3, (5, 9))), oracle.BF16)
+    cases["all_bits"] = (np.arange(1 << 16, dtype=np.uint16).reshape(64, 1024), oracle.BF16)
+    return cases
+
+
+@pytest.mark.parametrize("name", list(exp_cases()))
+def test_lossless_exp_bit_exact(name):
+    x, dt = exp_cases()[name]
+    s, bpp = oracle.compress(x, dtype=dt, mode=oracle.LOSSLESS_EXP)
+    out, _ = oracle.decompress(s, dt)
+    assert out.dtype == x.dtype and np.array_equal(out, x)
+    tiles = np.arange(oracle.info(s)["n_tiles"])
+    t_out = oracle.decompress_tiles(s, tiles, dt)
+    R, Cc = x.shape
+    padded = np.zeros((len(tiles) and t_out.shape[1] * ((R + t_out.shape[1] - 1) // t_out.shape[1]),
+                       (Cc + 255) // 256 * 256), np.uint16)
+    tc = padded.shape[1] // 256
+    for i in tiles:
+        padded[i // tc * t_out.shape[1]:(i // tc + 1) * t_out.shape[1], i % tc * 256:(i % tc + 1) * 256] = t_out[i]
+    assert np.array_equal(padded[:R, :Cc], x)
+    assert not padded[R:].any() and not padded[:, Cc:].any(), "padding decodes to +0.0"
+
+
+def test_lossless_exp_sections_closed_form():
+    """The raw plane holds (sign << 7) | mantissa of the zero-padded matrix, byte for byte; the
+    single table has f > 0 exactly for the exponents present (padding counts as exponent 0)."""
+    rng = np.random.default_rng(5)
+    x = W.to_bf16_bits(rng.standard_t(3, (40, 300)) * 0.05)
+    x[3, :7] = [0x7F80, 0xFF80, 0x7FC1, 0x0001, 0x8000, 0x807F, 0x3F80]
+    s, _ = oracle.compress(x, dtype=oracle.BF16, mode=oracle.LOSSLESS_EXP, tile_rows=16)
+    Rp, Cp = 48, 512
+    pad = np.zeros((Rp, Cp), np.uint16)
+    pad[:40, :300] = x
+    o_raw = header_field(s, 96, 8)
+    assert s[6] == 2 and s[23] == 1 and o_raw % 16 == 0
+    raw = np.frombuffer(s[o_raw:o_raw + Rp * Cp], np.uint8).reshape(Rp, Cp)
+    want = (((pad >> 8) & 0x80) | (pad & 0x7F)).astype(np.uint8)
+    assert np.array_equal(raw, want)
+    assert zlib.crc32(raw.tobytes()) == header_field(s, 104, 4)
+    o_pl = header_field(s, 72, 8)
+    assert o_pl >= o_raw + Rp * Cp and zlib.crc32(s[o_pl:]) == header_field(s, 88, 4)
+    lo, S, f = oracle.tables(s)
+    assert len(S) == 1 and S[0] == 256 and lo[0] == 0 and f[0].sum() == 1 << 12
+    present = np.bincount(((pad >> 7) & 0xFF).ravel(), minlength=256) > 0
+    assert np.array_equal(f[0] > 0, present)
+    d = oracle.info(s)
+    assert d["payload_bytes"] == len(s) - o_pl + Rp * Cp
+
+
+def test_lossless_exp_rate_close_to_exponent_entropy():
+    """Coded size: at least N (H(exponent) + 8) bits (the order-0 entropy bound), at most that
+    plus the 32 states per tile and 2%, and no larger than the two-plane lossless stream of the
+    same tensor by more than 1%."""
+    w = W.student_t_rowscaled(1024, 1024, 2)
+    s, bpp = oracle.compress(w, dtype=oracle.BF16, mode=oracle.LOSSLESS_EXP)
+    s2, bpp2 = oracle.compress(w, dtype=oracle.BF16, mode=oracle.LOSSLESS)
+    e = ((w >> 7) & 0xFF).astype(np.int64)
+    p = np.bincount(e.ravel(), minlength=256) / e.size
+    h = -(p[p > 0] * np.log2(p[p > 0])).sum()
+    assert h + 8 <= bpp <= (h + 8 + 32 * 32 / 4096) * 1.02, (bpp, h)
+    assert bpp <= bpp2 * 1.01, (bpp, bpp2)
+    out, _ = oracle.decompress(s, oracle.BF16, n_threads=4)
+    assert np.array_equal(out, w)
+
+
+def test_lossless_exp_validation():
+    x = W.to_bf16_bits(np.random.default_rng(1).normal(0, 1, (16, 256)))
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.compress(x, dtype=oracle.F16, mode=oracle.LOSSLESS_EXP)      # BF16 only
+    assert e.value.rc == -3
+    s, _ = oracle.compress(x, dtype=oracle.BF16, mode=oracle.LOSSLESS_EXP)
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.decompress(s, oracle.F16)                                     # no silent cast
+    assert e.value.rc == -3
+    bad = bytearray(s)
+    bad[header_field(s, 96, 8) + 5] ^= 0x40                                 # raw byte: its CRC catches it
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.decompress(bytes(bad))
+    assert e.value.rc == -2
+    s1, _ = oracle.compress(x, dtype=oracle.BF16, mode=oracle.LOSSLESS)
+    bad = bytearray(s1)
+    bad[96] = 16                                                             # raw offset in a two-plane stream
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.decompress(bytes(bad))
+    assert e.value.rc == -2

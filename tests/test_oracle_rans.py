@@ -165,3 +165,39 @@ def test_corrupt_tiles_are_rejected():
     bad[5] ^= 0x40                                              # damaged state of lane 1
     rc, *_ = oracle.rans_decode(f, n, tab, bytes(bad))
     assert rc == -2
+
+
+def test_exponent_coded_tiles_read_back_by_the_python_reader():
+    """The exponent-coded lossless BF16 stream (the guide's DFloat11 config, "Choose a
+    compression contract", read as exponent by tile rANS + raw sign/mantissa plane): every tile
+    of the oracle's stream, read by py_decode with the stream's single table (one step per
+    element, row -> element order, lane l on columns 8l..8l+7), joined with the raw plane, gives
+    the input bits."""
+    rng = np.random.default_rng(3)
+    R, C = 33, 520
+    x = (rng.standard_t(4, (R, C)) * 0.02).astype(np.float32)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)      # truncation is fine: any bit pattern
+    s, _ = oracle.compress(bits, dtype=oracle.BF16, mode=oracle.LOSSLESS_EXP, prob_bits=11)
+    info = oracle.info(s)
+    _, _, f = oracle.tables(s)
+    Rp, Cp, tr = 48, 768, 16
+    o_ix = int.from_bytes(s[64:72], "little")
+    o_pl = int.from_bytes(s[72:80], "little")
+    o_raw = int.from_bytes(s[96:104], "little")
+    raw = np.frombuffer(s[o_raw:o_raw + Rp * Cp], np.uint8).reshape(Rp, Cp).astype(np.uint16)
+    index = np.frombuffer(s[o_ix:o_ix + 4 * (info["n_tiles"] + 1)], np.uint32)
+    out = np.zeros((Rp, Cp), np.uint16)
+    tab = np.zeros((tr * 8, LANES), np.uint8)
+    for t in range(info["n_tiles"]):
+        tile = s[o_pl + 4 * int(index[t]):o_pl + 4 * int(index[t + 1])]
+        syms, _, fin, used, nwords = py_decode(tile, f, 11, tab)
+        assert all(v == L for v in fin) and nwords - used in (0, 1)
+        r0, c0 = t // 3 * tr, t % 3 * 256
+        for rr in range(tr):
+            for e in range(8):
+                for lane in range(LANES):
+                    r, c = r0 + rr, c0 + 8 * lane + e
+                    rb = raw[r, c]
+                    out[r, c] = ((rb & 0x80) << 8) | (int(syms[rr * 8 + e, lane]) << 7) | (rb & 0x7F)
+    assert np.array_equal(out[:R, :C], bits)
+    assert not out[R:].any() and not out[:, C:].any()
