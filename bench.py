@@ -10,7 +10,8 @@ in the 256 MB Infinity Cache.
 
 Prints one JSON line (rank 0, N = 1): decoded-weight GB/s (container bytes written per second),
 the roofline of the step's one grouped decode launch from HIP events on the launch stream,
-the fused decode + GEMM forward of an 8192 x 8192 weight at 4.5 bpp against the plain BF16 GEMM
+the two lossless BF16 codings side by side (byte planes, and the exponent-coded variant), the
+fused decode + GEMM forward of an 8192 x 8192 weight at 4.5 bpp against the plain BF16 GEMM
 (M = 4096, 256, 16), and the oracle's CPU decode of one step on the host cores as a reported
 baseline.
 
@@ -163,6 +164,45 @@ def fused_gemm_section(torch, ep, reps: int = 15):
     return out
 
 
+def lossless_section(torch, ep, reps: int = 10):
+    """The two lossless BF16 codings of the 4096 x 4096 matrix side by side, outside the step:
+    byte-plane tile rANS (the step's lossless decode) and the exponent-coded variant (exponent
+    byte by tile rANS, sign and mantissa uncoded). Each launch decodes 8 copies of one stream
+    (grouped), rotating over 4 buffer sets so that no launch finds its data in the Infinity
+    Cache; median of per-launch HIP events."""
+    from decode_tile_interleaved_rans_amd import workloads as W
+    w = W.student_t_rowscaled(4096, 4096, 2)
+    src = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda()
+    out = {}
+    for name, kw in (("byte_planes", {}), ("exponent_coded", {"exponent_coded": True})):
+        s, bpp = ep.lossless_compress(w, dtype=ep.BF16, **kw)
+        sets = [([ep.upload(s) for _ in range(8)],
+                 [torch.empty((4096, 4096), dtype=torch.bfloat16, device="cuda") for _ in range(8)]) for _ in range(4)]
+        for k in range(2):
+            ep.decompress_many(*sets[k % 4])
+        ev = []
+        for k in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            ep.decompress_many(*sets[k % 4])
+            b.record()
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        for hs, outs in sets:
+            for h in hs:
+                h.check()
+        if not all(torch.equal(o, src) for o in sets[0][1]):
+            raise RuntimeError(f"lossless {name} decode differs from the input")
+        us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+        nbytes = 8 * (len(s) + 2 * w.size)
+        out[name] = {"actual_bpp": round(bpp, 4), "us_per_matrix": round(us / 8, 2),
+                     "algorithmic_gbs": round(nbytes / us / 1e3, 1), "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+        log(f"lossless {name}: {bpp:.4f} bpp, {us / 8:.1f} us per 4096^2 matrix")
+        del sets
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,10 +298,11 @@ def main():
                 "launch_us_min": round(min(durs) * 1e6, 2)}
     per_item = {items[i][0]: {"actual_bpp": round(items[i][3], 4), "stream_bytes": len(items[i][1])}
                 for i in range(len(items))}
+    sets.clear()
+    torch.cuda.empty_cache()
+    lossless = lossless_section(torch, ep)
     fused = None
     if not args.no_gemm:
-        sets.clear()
-        torch.cuda.empty_cache()
         fused = fused_gemm_section(torch, ep, reps=args.gemm_reps)
     cpu = None
     if not args.no_cpu:
@@ -280,6 +321,7 @@ def main():
         "wall_s": round(wall, 4),
         "roofline": roofline,
         "per_decode": per_item,
+        "lossless_bf16_codings": lossless,
         "fused_gemm": fused,
         "cpu_baseline": cpu,
     }

@@ -20,7 +20,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libentropack.so")
 
 F32, BF16, F16, F8E4M3, I8, U8 = 0, 1, 2, 3, 4, 5
-LOSSY, LOSSLESS = 0, 1
+LOSSY, LOSSLESS, LOSSLESS_EXP = 0, 1, 2
 STATUS = {0: "EP_OK", -1: "EP_EINVAL", -2: "EP_ECORRUPT", -3: "EP_EUNSUPPORTED", -4: "EP_ERANGE",
           -5: "EP_EHIP", -6: "EP_ENOMEM", -7: "EP_EDEVICE"}
 EXPORTS = ["ep_compress", "ep_free", "ep_stream_info", "ep_upload", "ep_handle_info", "ep_decompress",
@@ -149,8 +149,10 @@ def compress(w, target_bpp: float = 4.0, *, mode: int = LOSSY, prob_bits: int = 
     return data, bpp.value
 
 
-def lossless_compress(w, **kw) -> tuple[bytes, float]:
-    return compress(w, 0.0, mode=LOSSLESS, **kw)
+def lossless_compress(w, *, exponent_coded: bool = False, **kw) -> tuple[bytes, float]:
+    """Bit-exact compression. exponent_coded=True (BF16 only) codes the exponent byte with the
+    tile rANS and keeps sign and mantissa as uncoded bytes; otherwise every byte plane is coded."""
+    return compress(w, 0.0, mode=LOSSLESS_EXP if exponent_coded else LOSSLESS, **kw)
 
 
 def stream_info(stream: bytes) -> dict:
@@ -220,7 +222,7 @@ class Handle:
         """Decode into a new tensor. FP8 / INT8 return (values, per-row fp32 scale)."""
         torch = _torch()
         if dtype is None:
-            dtype = _torch_dtype(self.info["src_dtype"]) if self.info["mode"] == LOSSLESS else torch.bfloat16
+            dtype = _torch_dtype(self.info["src_dtype"]) if self.info["mode"] != LOSSY else torch.bfloat16
         out = torch.empty(self.shape, dtype=dtype, device="cuda")
         scale = None
         if self.info["mode"] == LOSSY and dtype in (torch.float8_e4m3fn, torch.int8):

@@ -51,13 +51,13 @@ std::vector<uint8_t> build_tables(const ep::StreamView& v) {
     uint32_t* ent = reinterpret_cast<uint32_t*>(blob.data() + ((size_t)v.n_tables << n));
     for (int t = 0; t < v.n_tables; ++t) {
         const ep::Table& T = v.tables[t];
-        const bool coord = v.mode != EP_MODE_LOSSLESS && t > 0;
+        const bool coord = v.mode == EP_MODE_LOSSY_E8 && t > 0;
         const uint32_t base = coord ? (uint32_t)((t - 1) & 1) << n : 0u;
         uint32_t c = 0;
         for (int s = 0; s < 256; ++s) {
             const uint32_t f = T.freq[s];
             int32_t value;
-            if (v.mode == EP_MODE_LOSSLESS) value = s;
+            if (v.mode != EP_MODE_LOSSY_E8) value = s;
             else if (t == 0) value = T.lo + s;
             else value = (s == ep::kEscape || s >= T.width) ? 0 : 2 * (T.lo + s) + ((t - 1) & 1);
             ent[2 * ((size_t)t * 256 + s)] = f | (coord && s == ep::kEscape ? 0x80000000u : 0u);
@@ -77,6 +77,7 @@ ep::MatDesc desc_for(const ep_handle* h, int container, void* out, float* scale)
     d.index = reinterpret_cast<const uint32_t*>(s + v.off_index);
     d.row_scale = reinterpret_cast<const float*>(s + v.off_scale);
     d.row_qmax = reinterpret_cast<const uint16_t*>(s + v.off_qmax);
+    d.raw = v.mode == EP_MODE_LOSSLESS_EXP ? s + v.off_raw : nullptr;
     d.tables = h->dev + h->tables_off;
     d.out = out;
     d.scale_out = scale;
@@ -143,14 +144,14 @@ hipError_t workspace(int device, hipStream_t stream, size_t need, uint16_t** out
 }
 
 bool container_ok(const ep_handle* h, int ct) {
-    if (h->view.mode == EP_MODE_LOSSLESS) return ct == h->view.dtype;
+    if (h->view.mode != EP_MODE_LOSSY_E8) return ct == h->view.dtype;
     return ct == EP_BF16 || ct == EP_F16 || ct == EP_F8E4M3 || ct == EP_I8;
 }
 
 ep_status check_decode_args(const ep_handle* h, ep_dtype ct, void* out, float* scale) {
     if (!h) return fail(EP_EINVAL, "null handle");
     if (!container_ok(h, ct))
-        return fail(EP_EUNSUPPORTED, h->view.mode == EP_MODE_LOSSLESS
+        return fail(EP_EUNSUPPORTED, h->view.mode != EP_MODE_LOSSY_E8
                                          ? "a lossless stream decodes only to its own dtype"
                                          : "lossy streams decode to BF16, F16, F8E4M3 or I8");
     if (!out && h->view.rows * h->view.cols > 0) return fail(EP_EINVAL, "null output pointer");
@@ -185,6 +186,8 @@ ep_status ep_compress(const void* host_w, ep_dtype src, int64_t rows, int64_t co
         if (!(o.target_bpp > 0.0 && o.target_bpp <= 32.0)) return fail(EP_EINVAL, "target_bpp must be in (0, 32]");
     } else if (o.mode == EP_MODE_LOSSLESS) {
         if (ep::element_bytes(src) == 0) return fail(EP_EUNSUPPORTED, "unknown dtype");
+    } else if (o.mode == EP_MODE_LOSSLESS_EXP) {
+        if (src != EP_BF16) return fail(EP_EUNSUPPORTED, "exponent-coded lossless mode takes BF16 input");
     } else {
         return fail(EP_EINVAL, "unknown mode");
     }

@@ -5,7 +5,9 @@
 // containers ("EntroPack: Fast and Accurate Entropy-Coded Weight Compression at Arbitrary
 // Bitrates", Abstract). Lossless byte-plane tiles implement the lossless tile-ANS option listed in
 // "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section "Choose a
-// compression contract".
+// compression contract"; exponent-coded BF16 tiles (the same section's DFloat11 config for
+// lossless BF16, read after the published DFloat11 split) code only the exponent and join it with
+// uncoded sign and mantissa bytes.
 //
 // Work mapping. A tile is tile_rows x 256 weights coded by 32 interleaved rANS states; lane l of
 // a tile owns the 8-column block l of every tile row. One wave64 decodes two horizontally
@@ -607,6 +609,58 @@ __device__ __forceinline__ void lossless_dispatch(const MatDesc& M, const Tables
     }
 }
 
+// ----------------------------------------------------------------------------- exponent-coded BF16
+// One rANS step per element decodes its exponent byte; the sign and mantissa bytes of the lane's
+// 8 elements of a row come from the raw plane [Rp][Cp] with one 8-byte load, issued a row ahead.
+// bf16 = (r & 0x80) << 8 | e << 7 | (r & 0x7F) for raw byte r and exponent e.
+__device__ __forceinline__ uint32_t join_pair(uint32_t raw_word, uint32_t sel, uint32_t e0, uint32_t e1) {
+    const uint32_t r = __builtin_amdgcn_perm(0u, raw_word, sel);   // two raw bytes at bits 0 and 16
+    return (r & 0x007F007Fu) | ((r << 8) & 0x80008000u) | (e0 << 7) | (e1 << 23);
+}
+
+template <int N>
+__device__ __forceinline__ void split_pairs(const MatDesc& M, const Tables& T, Tile& t, uint64_t p0, uint64_t p1) {
+    const __amdgpu_buffer_rsrc_t rs = payload_rsrc(M);
+    const uint64_t w0 = (uint64_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const uint64_t stride = (uint64_t)M.tiles_c * 256u;     // raw plane row length Cp
+    for (uint64_t pair = p0 + w0; pair < p1; pair += kWaves) {
+        const uint32_t tr = (uint32_t)(pair / M.pairs_c);
+        const uint32_t tc = 2 * (uint32_t)(pair % M.pairs_c) + (t.sh ? 1u : 0u);
+        t.valid = tc < M.tiles_c;
+        begin_tile(M, rs, (uint64_t)tr * M.tiles_c + tc, t);
+        // a half without a tile reads the bytes of the tile row's first tile (in range, unused)
+        const uint8_t* raw = M.raw + (uint64_t)tr * M.tile_rows * stride + (t.valid ? tc * 256u : 0u) + 8u * t.l;
+        uint2 next = *reinterpret_cast<const uint2*>(raw);
+        for (int rr = 0; rr < M.tile_rows; ++rr) {
+            top_up(t, rs);
+            const uint2 cur = next;
+            if (rr + 1 < M.tile_rows) next = *reinterpret_cast<const uint2*>(raw + (uint64_t)(rr + 1) * stride);
+            uint32_t e[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                uint32_t v;
+                e[k] = rans_step<N>(t, 0u, 0u, T.ent, v);
+                refill(t);
+            }
+            const uint4 o = make_uint4(join_pair(cur.x, 0x0C010C00u, e[0], e[1]), join_pair(cur.x, 0x0C030C02u, e[2], e[3]),
+                                       join_pair(cur.y, 0x0C010C00u, e[4], e[5]), join_pair(cur.y, 0x0C030C02u, e[6], e[7]));
+            const uint32_t row = tr * M.tile_rows + rr;
+            const uint32_t col0 = tc * 256 + 8 * t.l;
+            if (row < M.rows && t.valid && col0 < M.cols) {
+                uint16_t* out = static_cast<uint16_t*>(M.out) + (size_t)row * M.cols;
+                if (col0 + 8 <= M.cols && (M.cols & 7) == 0) {
+                    *reinterpret_cast<uint4*>(out + col0) = o;
+                } else {
+                    const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+                    for (int j = 0; j < 8; ++j)
+                        if (col0 + j < M.cols) out[col0 + j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+                }
+            }
+        }
+        end_tile(t);
+    }
+}
+
 // ----------------------------------------------------------------------------- grouped kernel
 // Persistent blocks over a launch's matrix-major tile pairs, lossy and lossless matrices alike.
 // Work is balanced by cost, not by pair count: a pair costs its relative decode time
@@ -642,6 +696,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_group(GroupArgs g) {
                 case 10: lossy_dispatch<10>(M, T, t, p0, p1); break;
                 case 11: lossy_dispatch<11>(M, T, t, p0, p1); break;
                 default: lossy_dispatch<12>(M, T, t, p0, p1); break;
+            }
+        } else if (M.mode == 2) {
+            switch (M.prob_bits) {
+                case 10: split_pairs<10>(M, T, t[0], p0, p1); break;
+                case 11: split_pairs<11>(M, T, t[0], p0, p1); break;
+                default: split_pairs<12>(M, T, t[0], p0, p1); break;
             }
         } else {
             lossless_dispatch(M, T, t, p0, p1);

@@ -6,8 +6,11 @@
 // (per table: i16 window start, u16 window width S, u16 escape frequency, u16 freq[S]), the tile
 // index u32[n_tiles + 1] (offsets in 4-byte units from the payload start) and the payload.
 // A tile is 32 u32 rANS states followed by its u16 words (plus one zero pad word when their
-// count is odd). The pages fix none of this; it is this codec's own container for tile-wise
-// entropy coding where every tile decodes on its own (EntroPack paper, Abstract).
+// count is odd). An exponent-coded lossless BF16 stream also holds a raw plane u8[Rp][Cp] of
+// (sign << 7) | mantissa bytes between the index and the payload (offset and CRC-32 in header
+// bytes 96 and 104, zero in the other modes). The pages fix none of this; it is this codec's own
+// container for tile-wise entropy coding where every tile decodes on its own (EntroPack paper,
+// Abstract).
 #pragma once
 
 #include <cstddef>
@@ -31,7 +34,8 @@ enum HeaderField : int {
     kMagic = 0, kVersion = 4, kMode = 6, kDtype = 7, kRows = 8, kCols = 12, kTileRows = 16,
     kTileColsField = 18, kLanesField = 20, kProbBits = 22, kNumTables = 23, kStep = 24,
     kTarget = 28, kNumTiles = 32, kNumEscapes = 36, kOffScale = 40, kOffQmax = 48,
-    kOffTables = 56, kOffIndex = 64, kOffPayload = 72, kTotalLen = 80, kPayloadCrc = 88
+    kOffTables = 56, kOffIndex = 64, kOffPayload = 72, kTotalLen = 80, kPayloadCrc = 88,
+    kOffRaw = 96, kRawCrc = 104
 };
 
 struct Table {
@@ -50,6 +54,7 @@ struct StreamView {
     float step = 0.0f, target = 0.0f;
     uint64_t off_scale = 0, off_qmax = 0, off_tables = 0, off_index = 0, off_payload = 0;
     uint64_t payload_len = 0;
+    uint64_t off_raw = 0, raw_len = 0;   // exponent-coded mode: raw plane [Rp][Cp]
     std::vector<Table> tables;
 };
 

@@ -290,7 +290,8 @@ struct TileSet {
 
 void serialize(int mode, int dt, int64_t R, int64_t C, int tile_rows, int n, const std::vector<Table>& tables,
                float step, float target, const std::vector<float>& scale, const std::vector<uint16_t>& qmax,
-               const TileSet& ts, uint32_t n_esc, std::vector<uint8_t>* out) {
+               const TileSet& ts, uint32_t n_esc, std::vector<uint8_t>* out,
+               const std::vector<uint8_t>* raw = nullptr) {
     const uint64_t meta_rows = mode == EP_MODE_LOSSY_E8 ? (uint64_t)R : 0;
     uint64_t tables_len = 0;
     for (const Table& t : tables) tables_len += 6 + 2 * (uint64_t)t.width;
@@ -299,7 +300,8 @@ void serialize(int mode, int dt, int64_t R, int64_t C, int tile_rows, int n, con
     const uint64_t o_qmax = up16(o_scale + 4 * meta_rows);
     const uint64_t o_tab = up16(o_qmax + 2 * meta_rows);
     const uint64_t o_idx = up16(o_tab + tables_len);
-    const uint64_t o_pay = up16(o_idx + 4 * ((uint64_t)n_tiles + 1));
+    const uint64_t o_raw = raw ? up16(o_idx + 4 * ((uint64_t)n_tiles + 1)) : 0;
+    const uint64_t o_pay = raw ? up16(o_raw + raw->size()) : up16(o_idx + 4 * ((uint64_t)n_tiles + 1));
     const uint64_t total = o_pay + ts.payload.size();
     out->assign(total, 0);
     uint8_t* s = out->data();
@@ -325,6 +327,11 @@ void serialize(int mode, int dt, int64_t R, int64_t C, int tile_rows, int n, con
     w64(s + kOffPayload, o_pay);
     w64(s + kTotalLen, total);
     w32(s + kPayloadCrc, crc32(ts.payload.data(), ts.payload.size()));
+    if (raw) {
+        w64(s + kOffRaw, o_raw);
+        w32(s + kRawCrc, crc32(raw->data(), raw->size()));
+        if (!raw->empty()) std::memcpy(s + o_raw, raw->data(), raw->size());
+    }
     for (uint64_t r = 0; r < meta_rows; ++r) {
         w32(s + o_scale + 4 * r, f32bits(scale[r]));
         w16(s + o_qmax + 2 * r, qmax[r]);
@@ -623,6 +630,57 @@ ep_status encode_lossless(const void* w, int dt, int64_t R, int64_t C, const ep_
     return EP_OK;
 }
 
+// ------------------------------------------------------------------------------ exponent-coded BF16
+// Lossless BF16 as the guide's DFloat11 config ("Choose a compression contract"), read after the
+// published DFloat11 split: the exponent byte of every element is coded by the tile rANS (one
+// table, one step per element, steps row -> element, lane l on columns 8l..8l+7), and sign and
+// mantissa are stored uncoded as (sign << 7) | mantissa in a raw plane [Rp][Cp] shaped like the
+// zero-padded matrix, so that the decoder reads each lane's 8 bytes of a row with one load.
+ep_status encode_lossless_exp(const void* w, int64_t R, int64_t C, const ep_encode_opts& o, int threads,
+                              std::vector<uint8_t>* out, std::string* why) {
+    const int tr = o.tile_rows, n = o.prob_bits;
+    const int64_t Rp = (R + tr - 1) / tr * tr, Cp = (C + kTileCols - 1) / kTileCols * kTileCols;
+    const uint16_t* src = static_cast<const uint16_t*>(w);
+    auto element = [&](int64_t r, int64_t c) -> uint32_t { return r < R && c < C ? src[r * C + c] : 0u; };
+    std::vector<uint8_t> raw((size_t)(Rp * Cp));
+    const int workers = (int)std::max<int64_t>(1, std::min<int64_t>(threads, std::max<int64_t>(Rp, 1)));
+    std::vector<std::vector<uint64_t>> wh(workers, std::vector<uint64_t>(256, 0));
+    parallel_for(Rp, workers, [&](int64_t r, int k) {
+        uint64_t* h = wh[k].data();
+        for (int64_t c = 0; c < Cp; ++c) {
+            const uint32_t v = element(r, c);
+            h[v >> 7 & 0xFF] += 1;
+            raw[(size_t)(r * Cp + c)] = (uint8_t)((v >> 8 & 0x80u) | (v & 0x7Fu));
+        }
+    });
+    std::vector<Table> tables(1);
+    std::vector<EncTable> enc(1);
+    uint64_t cnt[256] = {};
+    for (int k = 0; k < workers; ++k)
+        for (int s = 0; s < 256; ++s) cnt[s] += wh[k][s];
+    tables[0].lo = 0;
+    tables[0].width = 256;
+    if (!normalize_freq(cnt, n, tables[0].freq)) {
+        *why = "frequency normalization failed";
+        return EP_ERANGE;
+    }
+    make_enc_table(tables[0].freq, &enc[0]);
+    const int64_t tiles_c = Cp / kTileCols, n_tiles = (Rp / tr) * tiles_c;
+    TileSet ts = encode_tiles(n_tiles, tr * 8, n, enc, false, threads,
+                              [&](int64_t tile, uint8_t* tab, uint8_t* sym, uint16_t*) {
+        const int64_t r0 = tile / tiles_c * tr, c0 = tile % tiles_c * kTileCols;
+        for (int rr = 0; rr < tr; ++rr)
+            for (int e = 0; e < 8; ++e)
+                for (int l = 0; l < kLanes; ++l) {
+                    const int idx = (rr * 8 + e) * kLanes + l;
+                    tab[idx] = 0;
+                    sym[idx] = (uint8_t)(element(r0 + rr, c0 + 8 * l + e) >> 7);
+                }
+    });
+    serialize(EP_MODE_LOSSLESS_EXP, EP_BF16, R, C, tr, n, tables, 0.0f, 0.0f, {}, {}, ts, 0, out, &raw);
+    return EP_OK;
+}
+
 }  // namespace
 
 ep_status encode(const void* w, int dt, int64_t R, int64_t C, const ep_encode_opts& o, std::vector<uint8_t>* out,
@@ -630,6 +688,7 @@ ep_status encode(const void* w, int dt, int64_t R, int64_t C, const ep_encode_op
     int threads = o.n_threads > 0 ? o.n_threads : (int)std::max(1u, std::thread::hardware_concurrency());
     threads = std::min(threads, 64);
     if (o.mode == EP_MODE_LOSSY_E8) return encode_lossy(w, dt, R, C, o, threads, out, why);
+    if (o.mode == EP_MODE_LOSSLESS_EXP) return encode_lossless_exp(w, R, C, o, threads, out, why);
     return encode_lossless(w, dt, R, C, o, threads, out, why);
 }
 

@@ -77,7 +77,9 @@ ep_status parse_stream(const uint8_t* s, size_t len, StreamView* v, std::string*
     v->n_tiles = r32(s + kNumTiles);
     v->n_escapes = r32(s + kNumEscapes);
     const bool lossy = v->mode == EP_MODE_LOSSY_E8;
-    if (!lossy && v->mode != EP_MODE_LOSSLESS) return bad(why, "unknown mode");
+    const bool split = v->mode == EP_MODE_LOSSLESS_EXP;
+    if (!lossy && !split && v->mode != EP_MODE_LOSSLESS) return bad(why, "unknown mode");
+    if (split && v->dtype != EP_BF16) return bad(why, "exponent-coded lossless stream with a dtype other than bf16");
     if (lossy && v->dtype != EP_F32 && v->dtype != EP_BF16 && v->dtype != EP_F16)
         return bad(why, "lossy stream with a source dtype other than f32/bf16/f16");
     if (!lossy && element_bytes(v->dtype) == 0) return bad(why, "unknown source dtype");
@@ -85,7 +87,7 @@ ep_status parse_stream(const uint8_t* s, size_t len, StreamView* v, std::string*
     if (r16(s + kTileColsField) != (uint32_t)kTileCols || r16(s + kLanesField) != (uint32_t)kLanes)
         return bad(why, "tile width must be 256 columns and 32 lanes");
     if (v->prob_bits < 10 || v->prob_bits > 12) return bad(why, "prob_bits outside 10..12");
-    const int want_tables = lossy ? kLossyTables : element_bytes(v->dtype);
+    const int want_tables = lossy ? kLossyTables : split ? 1 : element_bytes(v->dtype);
     if (v->n_tables != want_tables) return bad(why, "wrong number of tables for the mode");
     if (lossy && !(std::isfinite(v->step) && v->step > 0.0f)) return bad(why, "step must be finite and > 0");
     v->tiles_r = (v->rows + v->tile_rows - 1) / v->tile_rows;
@@ -109,6 +111,16 @@ ep_status parse_stream(const uint8_t* s, size_t len, StreamView* v, std::string*
     if (v->off_payload - v->off_index < 4 * ((uint64_t)v->n_tiles + 1)) return bad(why, "tile index section too short");
     v->payload_len = total - v->off_payload;
     if (v->payload_len % 4) return bad(why, "payload length not a multiple of 4");
+    v->off_raw = r64(s + kOffRaw);
+    if (split) {
+        v->raw_len = (uint64_t)(v->tiles_r * v->tile_rows) * (uint64_t)(v->tiles_c * kTileCols);
+        if ((v->off_raw & 15) || v->off_raw < v->off_index + 4 * ((uint64_t)v->n_tiles + 1) ||
+            v->off_raw + v->raw_len > v->off_payload)
+            return bad(why, "raw sign/mantissa plane out of place or too short");
+        if (crc32(s + v->off_raw, v->raw_len) != r32(s + kRawCrc)) return bad(why, "raw plane CRC-32 mismatch");
+    } else if (v->off_raw != 0 || r32(s + kRawCrc) != 0) {
+        return bad(why, "raw plane fields set in a stream without a raw plane");
+    }
     // tables
     const uint32_t M = 1u << v->prob_bits;
     uint64_t pos = v->off_tables;
@@ -167,9 +179,9 @@ void fill_info(const StreamView& v, ep_info* info) {
     info->step = v.step;
     info->target_bpp = v.target;
     info->total_bytes = v.len;
-    info->payload_bytes = v.payload_len;
+    info->payload_bytes = v.payload_len + v.raw_len;
     info->state_bytes = 4ull * kLanes * v.n_tiles;
-    info->meta_bytes = v.len - v.payload_len;
+    info->meta_bytes = v.len - info->payload_bytes;
     info->actual_bpp = v.rows * v.cols > 0 ? 8.0 * (double)v.len / ((double)v.rows * (double)v.cols) : 0.0;
 }
 

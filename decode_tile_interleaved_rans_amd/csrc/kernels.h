@@ -18,6 +18,7 @@ struct MatDesc {
     const uint32_t* index;      // [n_tiles + 1] tile offsets into payload
     const float* row_scale;     // [rows] (lossy)
     const uint16_t* row_qmax;   // [rows] (lossy)
+    const uint8_t* raw;         // [Rp][Cp] sign/mantissa bytes (exponent-coded lossless BF16)
     const uint8_t* tables;      // decode tables (see table_blob_bytes)
     void* out;                  // [rows][cols] container elements
     float* scale_out;           // [rows] for FP8 / INT8, else unused
@@ -26,16 +27,17 @@ struct MatDesc {
     uint32_t payload_bytes;     // size of the tile payload (buffer-load bounds)
     float step;
     uint8_t prob_bits, tile_rows, container, n_tables;
-    uint8_t mode;               // 0 lossy E8 coordinates, 1 lossless byte planes
+    uint8_t mode;               // 0 lossy E8 coordinates, 1 lossless byte planes, 2 exponent-coded BF16
     uint32_t pair_cost;         // relative decode time of one tile pair (load balancing)
 };
 
 // Relative decode time of one tile pair, per tile row: a lossy row is 9 steps (coset + 8
 // coordinates) at 9 units each; a lossless row is one step per byte plane per element (8
 // elements) at 7.5 units, as measured on gfx950 (a lossless BF16 pair takes 1.47 times a lossy
-// pair).
+// pair); an exponent-coded BF16 row (8 steps plus joining the raw bytes) takes 0.92 of a lossy
+// row.
 inline uint32_t pair_cost_of(int mode, int tile_rows, int n_tables) {
-    return (uint32_t)tile_rows * (mode == 0 ? 81u : 60u * (uint32_t)n_tables);
+    return (uint32_t)tile_rows * (mode == 0 ? 81u : mode == 2 ? 74u : 60u * (uint32_t)n_tables);
 }
 
 struct GroupArgs {

@@ -50,8 +50,12 @@ typedef enum {
 typedef enum { EP_F32 = 0, EP_BF16 = 1, EP_F16 = 2, EP_F8E4M3 = 3, EP_I8 = 4, EP_U8 = 5 } ep_dtype;
 
 typedef enum {
-    EP_MODE_LOSSY_E8 = 0,  /* target bitrate, E8 lattice coordinates */
-    EP_MODE_LOSSLESS = 1   /* bit-exact byte-plane coding of any supported dtype */
+    EP_MODE_LOSSY_E8 = 0,     /* target bitrate, E8 lattice coordinates */
+    EP_MODE_LOSSLESS = 1,     /* bit-exact byte-plane coding of any supported dtype */
+    EP_MODE_LOSSLESS_EXP = 2  /* bit-exact BF16: the 8-bit exponent coded by tile rANS, sign and
+                                 mantissa stored as one uncoded byte per element (the guide's
+                                 DFloat11 config for lossless BF16, section "Choose a compression
+                                 contract", read after the published DFloat11 split) */
 } ep_mode;
 
 /* Encoder options. A NULL pointer means: lossy, target 4.0, prob_bits 12, tile_rows 16, all
@@ -64,7 +68,9 @@ typedef struct {
     int n_threads;         /* host encoder threads, 0 = all hardware threads */
 } ep_encode_opts;
 
-/* Stream summary. actual_bpp = 8 * total_bytes / (rows * cols) (0 for an empty matrix). */
+/* Stream summary. actual_bpp = 8 * total_bytes / (rows * cols) (0 for an empty matrix).
+ * payload_bytes counts the tile payload, plus the raw sign/mantissa plane of an exponent-coded
+ * stream; meta_bytes = total_bytes - payload_bytes. */
 typedef struct {
     int64_t rows, cols;
     int32_t mode, src_dtype, tile_rows, prob_bits;
@@ -77,7 +83,8 @@ typedef struct {
 typedef struct ep_handle ep_handle;   /* device-resident, validated stream */
 
 /* Compress a host matrix.
- *   host_w: [rows][cols] elements of dtype src (lossy: EP_F32, EP_BF16, EP_F16; lossless: any).
+ *   host_w: [rows][cols] elements of dtype src (lossy: EP_F32, EP_BF16, EP_F16; lossless: any;
+ *           exponent-coded lossless: EP_BF16).
  *   *out_stream receives a library-allocated byte buffer (free with ep_free), *out_len its size,
  *   *actual_bpp (optional) the stored bits per weight including all metadata.
  * Errors: EP_EINVAL (null pointers, bad options), EP_EUNSUPPORTED (dtype not allowed for the

@@ -97,6 +97,39 @@ def test_c2_lossless_bf16_roundtrip():
     assert bpp < 16.0
 
 
+def test_c2_lossless_exponent_coded_roundtrip():
+    """The guide's DFloat11 config for lossless BF16 ("Choose a compression contract"), read as
+    exponent by tile rANS + uncoded sign/mantissa bytes: bit-exact on the 4096 x 4096 matrix."""
+    w = W.student_t_rowscaled(4096, 4096, 2)
+    s, bpp = ep.lossless_compress(w, exponent_coded=True, dtype=ep.BF16)
+    out = gpu_decode(s, torch.bfloat16)
+    assert np.array_equal(bits(out), w)
+    want, _ = oracle.decompress(s, oracle.BF16, n_threads=16)
+    assert np.array_equal(want, w)
+    assert bpp < 12.0
+
+
+@pytest.mark.parametrize("case", ["ragged_17x300", "one", "ragged_33x513_t32_n11", "ragged_5x7_n10",
+                                  "all_bit_patterns", "zeros", "ragged_130x1000_n11"])
+def test_lossless_exponent_coded_shapes(case):
+    rng = np.random.default_rng(len(case))
+    opts = {"prob_bits": 12, "tile_rows": 16}
+    if case == "all_bit_patterns":
+        x = np.arange(1 << 16, dtype=np.uint16).reshape(64, 1024)
+    elif case == "zeros":
+        x = np.zeros((40, 300), np.uint16)
+    elif case == "one":
+        x = np.array([[0xBF80]], np.uint16)
+    else:
+        R, Cc = (int(v) for v in case.split("_")[1].split("x"))
+        x = W.to_bf16_bits(rng.standard_t(4, (R, Cc)) * 0.03)
+        opts["tile_rows"] = 32 if "_t32" in case else 16
+        opts["prob_bits"] = 11 if "_n11" in case else 10 if "_n10" in case else 12
+    s, _ = ep.lossless_compress(x, exponent_coded=True, dtype=ep.BF16, **opts)
+    out = gpu_decode(s, torch.bfloat16)
+    assert np.array_equal(bits(out), x)
+
+
 @pytest.mark.parametrize("shape,prob_bits,tile_rows", [((17, 300), 12, 16), ((1, 1), 12, 16), ((33, 513), 11, 32),
                                                        ((5, 7), 10, 16), ((16, 768), 12, 16), ((48, 2304), 10, 32),
                                                        ((130, 1000), 11, 16)])
@@ -148,8 +181,9 @@ def test_lossless_other_dtypes(dt):
 
 
 def test_grouped_decode_matches_single():
-    """One grouped call over lossy matrices in four containers and lossless BF16 / U8 / FP32
-    matrices: the kernel balances the two kinds of tiles by cost within one launch."""
+    """One grouped call over lossy matrices in four containers, lossless BF16 / U8 / FP32
+    matrices and an exponent-coded BF16 matrix: the kernel balances the kinds of tiles by cost
+    within one launch."""
     rng = np.random.default_rng(7)
     streams, conts = [], []
     for i, (R, Cc, t) in enumerate([(256, 512, 3.0), (128, 1024, 6.0), (300, 700, 2.5), (64, 256, 4.5)]):
@@ -157,9 +191,10 @@ def test_grouped_decode_matches_single():
         streams.append(ep.compress(w, t)[0])
         conts.append([torch.bfloat16, torch.float8_e4m3fn, torch.int8, torch.float16][i])
     lossless = [W.student_t(200, 600, 71), rng.integers(0, 255, (40, 300)).astype(np.uint8),
-                rng.normal(0, 1, (33, 257)).astype(np.float32)]
-    for x, code, tdt in zip(lossless, (ep.BF16, ep.U8, ep.F32), (torch.bfloat16, torch.uint8, torch.float32)):
-        streams.append(ep.lossless_compress(x, dtype=code)[0])
+                rng.normal(0, 1, (33, 257)).astype(np.float32), W.student_t(300, 1000, 72)]
+    for x, code, tdt in zip(lossless, (ep.BF16, ep.U8, ep.F32, ep.BF16),
+                            (torch.bfloat16, torch.uint8, torch.float32, torch.bfloat16)):
+        streams.append(ep.lossless_compress(x, dtype=code, exponent_coded=len(streams) == 7)[0])
         conts.append(tdt)
     hs = [ep.upload(s) for s in streams]
     outs = [torch.empty(h.shape, dtype=c, device="cuda") for h, c in zip(hs, conts)]
@@ -199,9 +234,10 @@ def test_device_flag_on_inconsistent_stream():
     h.check()                                              # the flag was cleared
 
 
-def test_unsupported_container_is_an_error():
+@pytest.mark.parametrize("exponent_coded", [False, True])
+def test_unsupported_container_is_an_error(exponent_coded):
     x = np.zeros((16, 256), np.uint16)
-    s, _ = ep.lossless_compress(x, dtype=ep.BF16)
+    s, _ = ep.lossless_compress(x, dtype=ep.BF16, exponent_coded=exponent_coded)
     h = ep.upload(s)
     with pytest.raises(ep.EPError) as e:
         h.decompress(torch.float16)

@@ -99,6 +99,51 @@ def test_lossless_encoder_matches_oracle(dt):
     assert so == sp
 
 
+@pytest.mark.parametrize("shape,prob_bits,tile_rows", [((37, 600), 12, 16), ((5, 9), 10, 16), ((64, 1024), 11, 32),
+                                                      ((0, 256), 12, 16)])
+def test_exponent_coded_encoder_matches_oracle(shape, prob_bits, tile_rows):
+    rng = np.random.default_rng(sum(shape))
+    x = W.student_t_rowscaled(*shape, seed=9) if shape[0] else np.zeros(shape, np.uint16)
+    if x.size:
+        x.ravel()[rng.choice(x.size, min(7, x.size), replace=False)] = [0x7F80, 0xFF80, 0x7FC1, 0x0001, 0x8000,
+                                                                      0x807F, 0xFFFF][:min(7, x.size)]
+    so, sp, *_ = oracle_and_product(x, 0.0, dtype=ep.BF16, mode=ep.LOSSLESS_EXP, prob_bits=prob_bits,
+                                    tile_rows=tile_rows)
+    assert so == sp
+    a, b = ep.stream_info(sp), oracle.info(so)
+    assert a["payload_bytes"] == b["payload_bytes"] and a["meta_bytes"] == b["meta_bytes"] and a["mode"] == 2
+
+
+def test_exponent_coded_validation():
+    x = W.student_t_rowscaled(32, 512, seed=1)
+    s, _ = ep.lossless_compress(x, exponent_coded=True, dtype=ep.BF16)
+    o_raw = int.from_bytes(s[96:104], "little")
+    bad = bytearray(s)
+    bad[o_raw + 100] ^= 4                           # raw plane byte: its CRC-32 catches it
+    with pytest.raises(ep.EPError) as e:
+        ep.stream_info(bytes(bad))
+    assert e.value.status == -2
+    bad = bytearray(s)
+    bad[96:104] = (o_raw + 16).to_bytes(8, "little")   # raw plane overlapping the payload
+    with pytest.raises(ep.EPError) as e:
+        ep.stream_info(bytes(bad))
+    assert e.value.status == -2
+    bad = bytearray(s)
+    bad[7] = ep.F16                                  # exponent coding is defined for BF16 only
+    with pytest.raises(ep.EPError) as e:
+        ep.stream_info(bytes(bad))
+    assert e.value.status == -2
+    with pytest.raises(ep.EPError) as e:
+        ep.compress(x.view(np.uint16), 0.0, mode=ep.LOSSLESS_EXP, dtype=ep.F16)
+    assert e.value.status == -3
+    s1, _ = ep.lossless_compress(x, dtype=ep.BF16)
+    bad = bytearray(s1)
+    bad[104] = 1                                     # raw plane CRC in a two-plane stream
+    with pytest.raises(ep.EPError) as e:
+        ep.stream_info(bytes(bad))
+    assert e.value.status == -2
+
+
 @pytest.mark.slow
 def test_encoder_matches_oracle_4096_student_t():
     w = W.student_t_rowscaled(4096, 4096, 2)
@@ -106,6 +151,8 @@ def test_encoder_matches_oracle_4096_student_t():
         so, sp, *_ = oracle_and_product(w, t, dtype=ep.BF16, threads=8)
         assert so == sp
     so, sp, *_ = oracle_and_product(w, 0.0, dtype=ep.BF16, mode=ep.LOSSLESS, threads=8)
+    assert so == sp
+    so, sp, *_ = oracle_and_product(w, 0.0, dtype=ep.BF16, mode=ep.LOSSLESS_EXP, threads=8)
     assert so == sp
 
 
