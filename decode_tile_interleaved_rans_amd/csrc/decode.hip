@@ -542,9 +542,35 @@ __device__ __forceinline__ void lossy_dispatch(const MatDesc& M, const Tables& T
 }
 
 // ----------------------------------------------------------------------------- lossless kernel
+template <int P>
+__device__ __forceinline__ void store_lossless_row(const MatDesc& M, const Tile& t, uint32_t row, uint32_t col0,
+                                                   const uint32_t* v) {
+    using E = typename std::conditional<P == 1, uint8_t, typename std::conditional<P == 2, uint16_t, uint32_t>::type>::type;
+    if (row < M.rows && t.valid && col0 < M.cols) {
+        E* out = static_cast<E*>(M.out) + (size_t)row * M.cols;
+        if (col0 + 8 <= M.cols && (M.cols & 7) == 0) {
+            if constexpr (P == 2) {
+                *reinterpret_cast<uint4*>(out + col0) =
+                    make_uint4(v[0] | v[1] << 16, v[2] | v[3] << 16, v[4] | v[5] << 16, v[6] | v[7] << 16);
+            } else if constexpr (P == 1) {
+                *reinterpret_cast<uint2*>(out + col0) = make_uint2(v[0] | v[1] << 8 | v[2] << 16 | v[3] << 24,
+                                                                   v[4] | v[5] << 8 | v[6] << 16 | v[7] << 24);
+            } else {
+                *reinterpret_cast<uint4*>(out + col0) = make_uint4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<uint4*>(out + col0 + 4) = make_uint4(v[4], v[5], v[6], v[7]);
+            }
+        } else {
+            for (int j = 0; j < 8; ++j)
+                if (col0 + j < M.cols) out[col0 + j] = (E)v[j];
+        }
+    }
+}
+
+// A row's elements are stored after the next row's first ring top-up (as in the lossy kernel):
+// the top-up waits for its chunk with the in-order vector-memory counter, which would also wait
+// for a store issued just before it.
 template <int P, int N>
 __device__ __forceinline__ void lossless_pairs(const MatDesc& M, const Tables& T, Tile& t, uint64_t p0, uint64_t p1) {
-    using E = typename std::conditional<P == 1, uint8_t, typename std::conditional<P == 2, uint16_t, uint32_t>::type>::type;
     const __amdgpu_buffer_rsrc_t rs = payload_rsrc(M);
     const uint64_t w0 = (uint64_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     for (uint64_t pair = p0 + w0; pair < p1; pair += kWaves) {
@@ -552,6 +578,8 @@ __device__ __forceinline__ void lossless_pairs(const MatDesc& M, const Tables& T
         const uint32_t tc = 2 * (uint32_t)(pair % M.pairs_c) + (t.sh ? 1u : 0u);
         t.valid = tc < M.tiles_c;
         begin_tile(M, rs, (uint64_t)tr * M.tiles_c + tc, t);
+        const uint32_t row0 = tr * M.tile_rows, col0 = tc * 256 + 8 * t.l;
+        uint32_t prev[8];
         for (int rr = 0; rr < M.tile_rows; ++rr) {
             uint32_t v[8];
             // an element is at most P steps x 32 words, and a top-up leaves more than
@@ -560,6 +588,7 @@ __device__ __forceinline__ void lossless_pairs(const MatDesc& M, const Tables& T
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 if (e % kElemsPerTopUp == 0) top_up(t, rs);
+                if (e == 0 && rr > 0) store_lossless_row<P>(M, t, row0 + rr - 1, col0, prev);
                 uint32_t acc = 0;
 #pragma unroll
                 for (int pl = 0; pl < P; ++pl) {
@@ -570,27 +599,10 @@ __device__ __forceinline__ void lossless_pairs(const MatDesc& M, const Tables& T
                 }
                 v[e] = acc;
             }
-            const uint32_t row = tr * M.tile_rows + rr;
-            const uint32_t col0 = tc * 256 + 8 * t.l;
-            if (row < M.rows && t.valid && col0 < M.cols) {
-                E* out = static_cast<E*>(M.out) + (size_t)row * M.cols;
-                if (col0 + 8 <= M.cols && (M.cols & 7) == 0) {
-                    if constexpr (P == 2) {
-                        *reinterpret_cast<uint4*>(out + col0) =
-                            make_uint4(v[0] | v[1] << 16, v[2] | v[3] << 16, v[4] | v[5] << 16, v[6] | v[7] << 16);
-                    } else if constexpr (P == 1) {
-                        *reinterpret_cast<uint2*>(out + col0) = make_uint2(v[0] | v[1] << 8 | v[2] << 16 | v[3] << 24,
-                                                                           v[4] | v[5] << 8 | v[6] << 16 | v[7] << 24);
-                    } else {
-                        *reinterpret_cast<uint4*>(out + col0) = make_uint4(v[0], v[1], v[2], v[3]);
-                        *reinterpret_cast<uint4*>(out + col0 + 4) = make_uint4(v[4], v[5], v[6], v[7]);
-                    }
-                } else {
-                    for (int j = 0; j < 8; ++j)
-                        if (col0 + j < M.cols) out[col0 + j] = (E)v[j];
-                }
-            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) prev[e] = v[e];
         }
+        store_lossless_row<P>(M, t, row0 + M.tile_rows - 1, col0, prev);
         end_tile(t);
     }
 }
@@ -618,6 +630,24 @@ __device__ __forceinline__ uint32_t join_pair(uint32_t raw_word, uint32_t sel, u
     return (r & 0x007F007Fu) | ((r << 8) & 0x80008000u) | (e0 << 7) | (e1 << 23);
 }
 
+__device__ __forceinline__ void store_bf16_row(const MatDesc& M, const Tile& t, uint32_t row, uint32_t col0,
+                                               const uint4& o) {
+    if (row < M.rows && t.valid && col0 < M.cols) {
+        uint16_t* out = static_cast<uint16_t*>(M.out) + (size_t)row * M.cols;
+        if (col0 + 8 <= M.cols && (M.cols & 7) == 0) {
+            *reinterpret_cast<uint4*>(out + col0) = o;
+        } else {
+            const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+            for (int j = 0; j < 8; ++j)
+                if (col0 + j < M.cols) out[col0 + j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+        }
+    }
+}
+
+// Order of the memory operations in a row, so that every wait of the in-order vector-memory
+// counter is for operations issued a row earlier: wait for this row's raw bytes (their load was
+// the last one issued in the previous row), top up the ring (its chunk load was issued before
+// that), store the previous row's values, issue the next row's raw load, decode.
 template <int N>
 __device__ __forceinline__ void split_pairs(const MatDesc& M, const Tables& T, Tile& t, uint64_t p0, uint64_t p1) {
     const __amdgpu_buffer_rsrc_t rs = payload_rsrc(M);
@@ -627,13 +657,17 @@ __device__ __forceinline__ void split_pairs(const MatDesc& M, const Tables& T, T
         const uint32_t tr = (uint32_t)(pair / M.pairs_c);
         const uint32_t tc = 2 * (uint32_t)(pair % M.pairs_c) + (t.sh ? 1u : 0u);
         t.valid = tc < M.tiles_c;
-        begin_tile(M, rs, (uint64_t)tr * M.tiles_c + tc, t);
         // a half without a tile reads the bytes of the tile row's first tile (in range, unused)
         const uint8_t* raw = M.raw + (uint64_t)tr * M.tile_rows * stride + (t.valid ? tc * 256u : 0u) + 8u * t.l;
-        uint2 next = *reinterpret_cast<const uint2*>(raw);
+        uint2 next = *reinterpret_cast<const uint2*>(raw);   // before the tile's first chunk loads
+        begin_tile(M, rs, (uint64_t)tr * M.tiles_c + tc, t);
+        const uint32_t row0 = tr * M.tile_rows, col0 = tc * 256 + 8 * t.l;
+        uint4 prev = make_uint4(0u, 0u, 0u, 0u);
         for (int rr = 0; rr < M.tile_rows; ++rr) {
-            top_up(t, rs);
             const uint2 cur = next;
+            asm volatile("" ::"v"(cur.x), "v"(cur.y));
+            top_up(t, rs);
+            if (rr > 0) store_bf16_row(M, t, row0 + rr - 1, col0, prev);
             if (rr + 1 < M.tile_rows) next = *reinterpret_cast<const uint2*>(raw + (uint64_t)(rr + 1) * stride);
             uint32_t e[8];
 #pragma unroll
@@ -642,21 +676,10 @@ __device__ __forceinline__ void split_pairs(const MatDesc& M, const Tables& T, T
                 e[k] = rans_step<N>(t, 0u, 0u, T.ent, v);
                 refill(t);
             }
-            const uint4 o = make_uint4(join_pair(cur.x, 0x0C010C00u, e[0], e[1]), join_pair(cur.x, 0x0C030C02u, e[2], e[3]),
-                                       join_pair(cur.y, 0x0C010C00u, e[4], e[5]), join_pair(cur.y, 0x0C030C02u, e[6], e[7]));
-            const uint32_t row = tr * M.tile_rows + rr;
-            const uint32_t col0 = tc * 256 + 8 * t.l;
-            if (row < M.rows && t.valid && col0 < M.cols) {
-                uint16_t* out = static_cast<uint16_t*>(M.out) + (size_t)row * M.cols;
-                if (col0 + 8 <= M.cols && (M.cols & 7) == 0) {
-                    *reinterpret_cast<uint4*>(out + col0) = o;
-                } else {
-                    const uint32_t w[4] = {o.x, o.y, o.z, o.w};
-                    for (int j = 0; j < 8; ++j)
-                        if (col0 + j < M.cols) out[col0 + j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
-                }
-            }
+            prev = make_uint4(join_pair(cur.x, 0x0C010C00u, e[0], e[1]), join_pair(cur.x, 0x0C030C02u, e[2], e[3]),
+                              join_pair(cur.y, 0x0C010C00u, e[4], e[5]), join_pair(cur.y, 0x0C030C02u, e[6], e[7]));
         }
+        store_bf16_row(M, t, row0 + M.tile_rows - 1, col0, prev);
         end_tile(t);
     }
 }

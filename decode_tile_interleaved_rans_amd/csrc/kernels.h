@@ -34,10 +34,10 @@ struct MatDesc {
 // Relative decode time of one tile pair, per tile row: a lossy row is 9 steps (coset + 8
 // coordinates) at 9 units each; a lossless row is one step per byte plane per element (8
 // elements) at 7.5 units, as measured on gfx950 (a lossless BF16 pair takes 1.47 times a lossy
-// pair); an exponent-coded BF16 row (8 steps plus joining the raw bytes) takes 0.92 of a lossy
+// pair); an exponent-coded BF16 row (8 steps plus joining the raw bytes) takes 0.89 of a lossy
 // row.
 inline uint32_t pair_cost_of(int mode, int tile_rows, int n_tables) {
-    return (uint32_t)tile_rows * (mode == 0 ? 81u : mode == 2 ? 74u : 60u * (uint32_t)n_tables);
+    return (uint32_t)tile_rows * (mode == 0 ? 81u : mode == 2 ? 72u : 60u * (uint32_t)n_tables);
 }
 
 struct GroupArgs {
