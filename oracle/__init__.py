@@ -76,6 +76,7 @@ def lib():
         L.or_f32_to_e4m3.restype = C.c_uint8
         L.or_rans_encode.argtypes = [C.c_int, vp, C.c_int, C.c_int, vp, vp, vp, C.c_int, vp, sz, C.POINTER(sz)]
         L.or_rans_decode.argtypes = [C.c_int, vp, C.c_int, C.c_int, vp, C.c_int, vp, sz, vp, vp, vp]
+        L.or_quantize_rows_e4m3.argtypes = [vp, i64, i64, vp, vp]
         _lib = L
     return _lib
 
@@ -253,3 +254,16 @@ def rans_decode(freqs: np.ndarray, prob_bits: int, tab: np.ndarray, tile: bytes,
     rc = lib().or_rans_decode(freqs.shape[0], _ptr(freqs), prob_bits, tab.shape[0], _ptr(tab), esc_sym,
                               _ptr(buf), len(tile), _ptr(sym), _ptr(esc), _ptr(fin))
     return rc, sym, esc, fin
+
+
+def quantize_rows_e4m3(x_bf16: np.ndarray):
+    """Per-row FP8 E4M3 codes [M, K] (uint8) and scales [M] (fp32) of BF16 activations given as
+    uint16 bit patterns."""
+    x = np.ascontiguousarray(x_bf16, np.uint16)
+    M, K = x.shape
+    q = np.zeros((M, K), np.uint8)
+    s = np.zeros(max(M, 1), np.float32)
+    rc = lib().or_quantize_rows_e4m3(_ptr(x), M, K, _ptr(q), _ptr(s))
+    if rc != 0:
+        raise OracleError(rc, "quantize_rows_e4m3")
+    return q, s[:M]

@@ -1531,3 +1531,35 @@ float or_row_scale(const void* w, int dt, int64_t R, int64_t C, int64_t r) {
     (void)R;
     return row_scale(w, dt, r, C);
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* FP8 linear forward: activations. [A, Abstract] lists FP8 among the containers the decoded    */
+/* weights go to; a layer that multiplies in FP8 also needs its activations in FP8. Reading     */
+/* (the pages give no rule): per-row (per-token) scaling to the E4M3 range, amax_m =            */
+/* max_k |x_mk| (exact in fp32), s_m = fp32(amax_m / 448), q_mk = E4M3(fp32(x_mk * fp32(448 /   */
+/* amax_m))) with the same saturating round-to-nearest-even cast as the weight container; a    */
+/* row with amax_m = 0 gets s_m = 0 and codes 0, and amax_m is raised to 2^-100 when smaller,   */
+/* so that 448 / amax_m stays finite. Y[m][n] is then s_m * s_w[n] * sum_k x8_mk w8_nk, in      */
+/* BF16. Inputs must be finite.                                                                 */
+/* ------------------------------------------------------------------------------------------ */
+int or_quantize_rows_e4m3(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s) {
+    if (M < 0 || K < 0 || (M * K > 0 && (!x || !q)) || (M > 0 && !s)) return OR_EINVAL;
+    for (int64_t m = 0; m < M; ++m) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = fabsf(f32_from_bits((uint32_t)x[m * K + k] << 16));
+            if (!isfinite(v)) return OR_ERANGE;
+            if (v > amax) amax = v;
+        }
+        if (amax == 0.0f) {
+            s[m] = 0.0f;
+            for (int64_t k = 0; k < K; ++k) q[m * K + k] = 0;
+            continue;
+        }
+        if (amax < 0x1p-100f) amax = 0x1p-100f;
+        s[m] = amax / 448.0f;
+        float inv = 448.0f / amax;
+        for (int64_t k = 0; k < K; ++k) q[m * K + k] = or_f32_to_e4m3(f32_from_bits((uint32_t)x[m * K + k] << 16) * inv);
+    }
+    return OR_OK;
+}
