@@ -25,7 +25,8 @@ STATUS = {0: "EP_OK", -1: "EP_EINVAL", -2: "EP_ECORRUPT", -3: "EP_EUNSUPPORTED",
           -5: "EP_EHIP", -6: "EP_ENOMEM", -7: "EP_EDEVICE"}
 EXPORTS = ["ep_compress", "ep_free", "ep_stream_info", "ep_upload", "ep_handle_info", "ep_decompress",
            "ep_decompress_many", "ep_decode_symbols", "ep_linear_forward", "ep_gemm_bf16", "ep_handle_check",
-           "ep_release", "ep_last_error", "ep_version"]
+           "ep_release", "ep_last_error", "ep_version", "ep_linear_forward_fp8", "ep_quantize_rows_fp8",
+           "ep_gemm_fp8"]
 
 
 class EPError(RuntimeError):
@@ -73,6 +74,9 @@ def lib() -> C.CDLL:
         L.ep_decode_symbols.argtypes = [vp, vp, vp]
         L.ep_linear_forward.argtypes = [vp, vp, i64, vp, vp, vp]
         L.ep_gemm_bf16.argtypes = [vp, vp, i64, i64, i64, vp, vp]
+        L.ep_linear_forward_fp8.argtypes = [vp, vp, i64, vp, vp, vp]
+        L.ep_quantize_rows_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.ep_gemm_fp8.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]
         L.ep_handle_check.argtypes = [vp, vp]
         L.ep_release.argtypes = [vp]
         L.ep_release.restype = None
@@ -286,22 +290,51 @@ def gemm_bf16(x, w, stream=None):
     return y
 
 
-class CompressedLinear:
-    """Linear layer that keeps only the compressed weight; forward decodes it inside the GEMM."""
+def quantize_rows_fp8(x, stream=None):
+    """Per-row FP8 E4M3 codes of BF16 rows and their fp32 scales (x = codes * scale[row])."""
+    torch = _torch()
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    sc = torch.empty(M, dtype=torch.float32, device=x.device)
+    _check(lib().ep_quantize_rows_fp8(C.c_void_p(x.data_ptr()), M, K, C.c_void_p(q.data_ptr()),
+                                      C.c_void_p(sc.data_ptr()), _stream_ptr(stream)), "ep_quantize_rows_fp8")
+    return q, sc
 
-    def __init__(self, stream: bytes, bias=None):
+
+def gemm_fp8(xq, xs, wq, ws, bias=None, stream=None):
+    """Y = diag(xs) Xq Wq^T diag(ws) (+ bias) from E4M3 codes (uint8 tensors), BF16 output."""
+    torch = _torch()
+    M, K = xq.shape
+    N = wq.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    bp = C.c_void_p(bias.data_ptr()) if bias is not None else None
+    _check(lib().ep_gemm_fp8(C.c_void_p(xq.data_ptr()), C.c_void_p(xs.data_ptr()), C.c_void_p(wq.data_ptr()),
+                             C.c_void_p(ws.data_ptr()), M, N, K, bp, C.c_void_p(y.data_ptr()), _stream_ptr(stream)),
+           "ep_gemm_fp8")
+    return y
+
+
+class CompressedLinear:
+    """Linear layer that keeps only the compressed weight; forward decodes it inside the GEMM.
+    compute="bf16" (default) multiplies the BF16-decoded weight with BF16 activations; "fp8"
+    decodes the weight to FP8 E4M3 with its row scales and quantizes the activations per row."""
+
+    def __init__(self, stream: bytes, bias=None, compute: str = "bf16"):
+        if compute not in ("bf16", "fp8"):
+            raise ValueError("compute must be 'bf16' or 'fp8'")
         self.stream = stream
         self.handle = Handle(stream)
         self.out_features, self.in_features = self.handle.shape
         self.bias = bias
+        self.compute = compute
 
     @classmethod
-    def from_linear(cls, linear, target_bpp: float = 4.0, **kw):
+    def from_linear(cls, linear, target_bpp: float = 4.0, compute: str = "bf16", **kw):
         s, _ = compress(linear.weight, target_bpp, **kw)
         bias = None
         if linear.bias is not None:
             bias = linear.bias.detach().to(device="cuda", dtype=_torch().bfloat16).contiguous()
-        return cls(s, bias)
+        return cls(s, bias, compute)
 
     @property
     def actual_bpp(self) -> float:
@@ -327,8 +360,9 @@ class CompressedLinear:
         x2 = x.reshape(-1, shp[-1]).to(torch.bfloat16).contiguous()
         y = torch.empty((x2.shape[0], self.out_features), dtype=torch.bfloat16, device=x.device)
         bp = C.c_void_p(self.bias.data_ptr()) if self.bias is not None else None
-        _check(lib().ep_linear_forward(self.handle.ptr, C.c_void_p(x2.data_ptr()), x2.shape[0], bp,
-                                       C.c_void_p(y.data_ptr()), _stream_ptr(stream)), "ep_linear_forward")
+        fn = lib().ep_linear_forward_fp8 if self.compute == "fp8" else lib().ep_linear_forward
+        _check(fn(self.handle.ptr, C.c_void_p(x2.data_ptr()), x2.shape[0], bp, C.c_void_p(y.data_ptr()),
+                  _stream_ptr(stream)), "ep_linear_forward" + ("_fp8" if self.compute == "fp8" else ""))
         return y.reshape(*shp[:-1], self.out_features)
 
     __call__ = forward

@@ -381,4 +381,81 @@ ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, co
     return EP_OK;
 }
 
+ep_status ep_quantize_rows_fp8(const void* dev_x, int64_t M, int64_t K, uint8_t* dev_q, float* dev_scale,
+                               void* hip_stream) {
+    if (M < 0 || K < 0) return fail(EP_EINVAL, "negative size");
+    if (M == 0) return EP_OK;
+    if (!dev_x || !dev_q || !dev_scale) return fail(EP_EINVAL, "null pointer");
+    if (K % 16 || M > INT32_MAX || K > INT32_MAX) return fail(EP_EINVAL, "K must be a multiple of 16");
+    if ((reinterpret_cast<uintptr_t>(dev_x) | reinterpret_cast<uintptr_t>(dev_q)) & 15)
+        return fail(EP_EINVAL, "X and Q must be 16-byte aligned");
+    hipError_t e = ep::launch_quantize_rows_f8(static_cast<const uint16_t*>(dev_x), (int)M, (int)K, (int)K, dev_q,
+                                               (int)K, dev_scale, static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? EP_OK : hip_fail(e, "quantize launch");
+}
+
+ep_status ep_gemm_fp8(const uint8_t* dev_xq, const float* dev_xs, const uint8_t* dev_wq, const float* dev_ws,
+                      int64_t M, int64_t N, int64_t K, const void* dev_bias, void* dev_y, void* hip_stream) {
+    if (M < 0 || N < 0 || K < 0) return fail(EP_EINVAL, "negative size");
+    if (M == 0 || N == 0) return EP_OK;
+    if (!dev_xq || !dev_xs || !dev_wq || !dev_ws || !dev_y) return fail(EP_EINVAL, "null pointer");
+    if (K % 16 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(EP_EINVAL, "K must be a multiple of 16");
+    if ((reinterpret_cast<uintptr_t>(dev_xq) | reinterpret_cast<uintptr_t>(dev_wq)) & 15)
+        return fail(EP_EINVAL, "X and W codes must be 16-byte aligned");
+    ep::GemmF8Args g{dev_xq, dev_xs, dev_wq, dev_ws, static_cast<const uint16_t*>(dev_bias), static_cast<uint16_t*>(dev_y),
+                     (int)M, (int)N, (int)K, (int)K, (int)K, (int)N};
+    hipError_t e = ep::launch_gemm_f8(g, static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? EP_OK : hip_fail(e, "fp8 gemm launch");
+}
+
+ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias, void* dev_y,
+                                void* hip_stream) {
+    constexpr size_t kSliceBytes = 128u << 20;
+    if (!w) return fail(EP_EINVAL, "null handle");
+    if (w->view.mode != EP_MODE_LOSSY_E8) return fail(EP_EUNSUPPORTED, "the linear forward takes a lossy stream");
+    const int64_t N = w->view.rows, K = w->view.cols;
+    if (M < 0) return fail(EP_EINVAL, "negative M");
+    if (M == 0 || N == 0) return EP_OK;
+    if (!dev_x || !dev_y) return fail(EP_EINVAL, "null pointer");
+    if (K % 16 || M > INT32_MAX) return fail(EP_EINVAL, "in_features must be a multiple of 16 for the FP8 forward");
+    if (reinterpret_cast<uintptr_t>(dev_x) & 15) return fail(EP_EINVAL, "X must be 16-byte aligned");
+    const int tr = w->view.tile_rows;
+    int64_t slice = (int64_t)(kSliceBytes / (size_t)K) / tr * tr;
+    if (slice < tr) slice = tr;
+    if (slice > N) slice = (N + tr - 1) / tr * tr;
+    // workspace: X codes [M][K] | X scales [M] | weight codes [slice][K] | weight scales [slice]
+    const size_t o_xs = up((size_t)M * (size_t)K, 256), o_wq = up(o_xs + 4 * (size_t)M, 256);
+    const size_t o_ws = up(o_wq + (size_t)slice * (size_t)K, 256), need = o_ws + 4 * (size_t)slice;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    uint16_t* base = nullptr;
+    int dev = 0;
+    hipError_t we = hipGetDevice(&dev);
+    if (we == hipSuccess) we = workspace(dev, s, need, &base);
+    if (we != hipSuccess) return hip_fail(we, "hipMalloc for the linear forward workspace");
+    uint8_t* ws8 = reinterpret_cast<uint8_t*>(base);
+    uint8_t* xq = ws8;
+    float* xs = reinterpret_cast<float*>(ws8 + o_xs);
+    uint8_t* wq = ws8 + o_wq;
+    float* wsc = reinterpret_cast<float*>(ws8 + o_ws);
+    hipError_t e = ep::launch_quantize_rows_f8(static_cast<const uint16_t*>(dev_x), (int)M, (int)K, (int)K, xq, (int)K,
+                                               xs, s);
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    const ep::MatDesc full = desc_for(w, ep::CT_F8E4M3, wq, wsc);
+    for (int64_t r0 = 0; r0 < N; r0 += slice) {
+        const int64_t rows = std::min<int64_t>(slice, N - r0);
+        ep::MatDesc d = full;                  // rows r0 .. r0 + rows of the weight
+        d.index += (size_t)(r0 / tr) * w->view.tiles_c;
+        d.row_scale += r0;
+        d.row_qmax += r0;
+        d.rows = (uint32_t)rows;
+        e = ep::launch_group(&d, 1, s);
+        if (e != hipSuccess) return hip_fail(e, "slice decode launch");
+        ep::GemmF8Args g{xq, xs, wq, wsc, dev_bias ? static_cast<const uint16_t*>(dev_bias) + r0 : nullptr,
+                         static_cast<uint16_t*>(dev_y) + r0, (int)M, (int)rows, (int)K, (int)K, (int)K, (int)N};
+        e = ep::launch_gemm_f8(g, s);
+        if (e != hipSuccess) return hip_fail(e, "slice fp8 gemm launch");
+    }
+    return EP_OK;
+}
+
 }  // extern "C"

@@ -24,6 +24,7 @@
 
 #include <cstdint>
 
+#include "casts.h"
 #include "gemm.h"
 
 namespace ep {
@@ -366,6 +367,181 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny(GemmArgs g) {
     }
 }
 
+// ----------------------------------------------------------------------------- FP8 (E4M3) GEMM
+// Same tiling as gemm_dma with one-byte elements: a K step is 128 E4M3 codes, i.e. the same
+// 128-byte LDS rows and 16-byte swizzled chunks, multiplied by two 32x32x64 FP8 MFMAs
+// (v_mfma_f32_32x32x64_f8f6f4, both operands in the E4M3 format). Lane l supplies A row l % 32
+// and B column l % 32 with 32 codes each; lanes l and l + 32 cover complementary K halves. A lane
+// takes the 16-byte chunks 4j + l / 32 and 4j + 2 + l / 32 of the row for MFMA j: A and B use
+// the same rule, so every product pairs equal k whatever order the unit sums them in. The
+// accumulator layout is that of every 32 x 32 MFMA (see above); the epilogue applies the row
+// scale of X and the row scale of W.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <int ROWS>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc_u8(const uint8_t* src, int ld, int r0, int rows) {
+    const int n = rows - r0 < ROWS ? rows - r0 : ROWS;
+    const int bytes = __builtin_amdgcn_readfirstlane((int)((size_t)(n > 0 ? n : 0) * ld));
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src + (size_t)r0 * ld), 0, bytes, 0x00020000);
+}
+
+template <int ROWS, int NW>
+__device__ __forceinline__ void dma_tile_u8(__amdgpu_buffer_rsrc_t rs, int ld, int k0, int K, uint8_t* lds) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rr = lane >> 3, kc = (lane & 7) ^ rr;
+    const int k = k0 + 16 * kc;
+#pragma unroll
+    for (int j = 0; j < ROWS / 8 / NW; ++j) {
+        const int g = wave + NW * j;
+        const uint32_t off = (uint32_t)((8 * g + rr) * ld + k) | ((uint32_t)((K - 1 - k) >> 31) & kOob);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + 1024 * g), 16, off, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ i32x8 frag_f8(const uint8_t* row, int r, int c0) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(row + ((c0 ^ (r & 7)) << 4));
+    const uint4 hi = *reinterpret_cast<const uint4*>(row + (((c0 + 2) ^ (r & 7)) << 4));
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+template <int BM, int BN, int WGM, int WGN, bool BIAS>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_f8(GemmF8Args g) {
+    constexpr int NW = WGM * WGN;
+    constexpr int TI = BM / WGM / 32, TJ = BN / WGN / 32;
+    constexpr int BK8 = 128;
+    constexpr int kStage = (BM + BN) * 128;
+    __shared__ __align__(1024) uint8_t lds[2 * kStage];
+    const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+    const int nblk = tiles_m * tiles_n;
+    int b = blockIdx.x;
+    if (nblk % 8 == 0) b = (b % 8) * (nblk / 8) + b / 8;
+    constexpr int G = kGroupM;
+    const int per_group = G * tiles_n, first_m = (b / per_group) * G;
+    const int gsize = tiles_m - first_m < G ? tiles_m - first_m : G;
+    const int tm = first_m + (b % per_group) % gsize, tn = (b % per_group) / gsize;
+    const int m0 = __builtin_amdgcn_readfirstlane(tm * BM), n0 = __builtin_amdgcn_readfirstlane(tn * BN);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = (wave / WGN) * (BM / WGM), wn = (wave % WGN) * (BN / WGN);
+    const __amdgpu_buffer_rsrc_t rx = operand_rsrc_u8<BM>(g.X, g.ldx, m0, g.M);
+    const __amdgpu_buffer_rsrc_t rw = operand_rsrc_u8<BN>(g.W, g.ldw, n0, g.N);
+
+    f32x16 acc[TI][TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
+
+    dma_tile_u8<BM, NW>(rx, g.ldx, 0, g.K, lds);
+    dma_tile_u8<BN, NW>(rw, g.ldw, 0, g.K, lds + BM * 128);
+    __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
+    __syncthreads();
+    const int nk = (g.K + BK8 - 1) / BK8;
+    for (int kt = 0; kt < nk; ++kt) {
+        uint8_t* cur = lds + (kt & 1) * kStage;
+        if (kt + 1 < nk) {
+            uint8_t* nxt = lds + ((kt + 1) & 1) * kStage;
+            dma_tile_u8<BM, NW>(rx, g.ldx, (kt + 1) * BK8, g.K, nxt);
+            dma_tile_u8<BN, NW>(rw, g.ldw, (kt + 1) * BK8, g.K, nxt + BM * 128);
+        }
+#pragma unroll
+        for (int js = 0; js < 2; ++js) {
+            i32x8 a[TI], bb[TJ];
+            const int c0 = 4 * js + (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < TI; ++i) {
+                const int r = wm + 32 * i + (lane & 31);
+                a[i] = frag_f8(cur + r * 128, r, c0);
+            }
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+                const int r = wn + 32 * j + (lane & 31);
+                bb[j] = frag_f8(cur + BM * 128 + r * 128, r, c0);
+            }
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bb[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+            const int col = n0 + wn + 32 * j + (lane & 31);
+            if (col >= g.N) continue;
+            const float sw = g.sw[col];
+            float bv = 0.0f;
+            if constexpr (BIAS) bv = __uint_as_float((uint32_t)g.bias[col] << 16);
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const int row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const float s0 = row < g.M ? g.sx[row] : 0.0f, s1 = row + 1 < g.M ? g.sx[row + 1] : 0.0f;
+                const uint32_t pk = pack_bf16x2(acc[i][j][r] * sw * s0 + bv, acc[i][j][r + 1] * sw * s1 + bv);
+                if (row < g.M) g.Y[(size_t)row * g.ldy + col] = (uint16_t)(pk & 0xFFFFu);
+                if (row + 1 < g.M) g.Y[(size_t)(row + 1) * g.ldy + col] = (uint16_t)(pk >> 16);
+            }
+        }
+}
+
+template <int BM, int BN, int WGM, int WGN>
+hipError_t launch_f8(const GemmF8Args& g, hipStream_t stream) {
+    const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+    if (g.bias)
+        hipLaunchKernelGGL((gemm_f8<BM, BN, WGM, WGN, true>), dim3(tiles), dim3(64 * WGM * WGN), 0, stream, g);
+    else
+        hipLaunchKernelGGL((gemm_f8<BM, BN, WGM, WGN, false>), dim3(tiles), dim3(64 * WGM * WGN), 0, stream, g);
+    return hipGetLastError();
+}
+
+// Per-row E4M3 quantization: one 256-thread block per row, two passes over the row (the second
+// from L2): the absolute maximum (wave reduction, then across the four waves in LDS), then the
+// codes, 8 elements per thread per iteration.
+__global__ __launch_bounds__(256) void quantize_rows_f8(const uint16_t* X, int K, int ldx, uint8_t* Q, int ldq, float* S) {
+    __shared__ float wmax[4];
+    const int m = blockIdx.x;
+    const uint16_t* x = X + (size_t)m * ldx;
+    float amax = 0.0f;
+    for (int k = 8 * threadIdx.x; k < K; k += 8 * 256) {
+        const uint4 v = *reinterpret_cast<const uint4*>(x + k);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            amax = fmaxf(amax, fabsf(__uint_as_float(w[i] << 16)));
+            amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    uint8_t* q = Q + (size_t)m * ldq;
+    if (amax == 0.0f) {
+        for (int k = 8 * threadIdx.x; k < K; k += 8 * 256) *reinterpret_cast<uint2*>(q + k) = make_uint2(0u, 0u);
+        if (threadIdx.x == 0) S[m] = 0.0f;
+        return;
+    }
+    amax = fmaxf(amax, 0x1p-100f);
+    const float inv = 448.0f / amax;
+    if (threadIdx.x == 0) S[m] = amax / 448.0f;
+    for (int k = 8 * threadIdx.x; k < K; k += 8 * 256) {
+        const uint4 v = *reinterpret_cast<const uint4*>(x + k);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t c[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            c[2 * i] = e4m3_rne_sat(__uint_as_float(w[i] << 16) * inv);
+            c[2 * i + 1] = e4m3_rne_sat(__uint_as_float(w[i] & 0xFFFF0000u) * inv);
+        }
+        *reinterpret_cast<uint2*>(q + k) =
+            make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
+    }
+}
+
 int gemm_device_cus() {
     static int cache[64] = {};
     int dev = 0;
@@ -399,6 +575,23 @@ hipError_t launch_skinny(const GemmArgs& g, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_gemm_f8(const GemmF8Args& g, hipStream_t stream) {
+    if (g.M <= 0 || g.N <= 0) return hipSuccess;
+    const long tiles256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
+    if (tiles256 >= gemm_device_cus()) return launch_f8<256, 256, 4, 4>(g, stream);
+    const long tiles128 = (long)((g.M + 127) / 128) * ((g.N + 127) / 128);
+    if (tiles128 >= 2L * gemm_device_cus()) return launch_f8<128, 128, 2, 2>(g, stream);
+    if (g.M <= 64) return launch_f8<64, 32, 2, 1>(g, stream);
+    return launch_f8<64, 64, 2, 2>(g, stream);
+}
+
+hipError_t launch_quantize_rows_f8(const uint16_t* X, int M, int K, int ldx, uint8_t* Q, int ldq, float* s,
+                                   hipStream_t stream) {
+    if (M <= 0) return hipSuccess;
+    hipLaunchKernelGGL(quantize_rows_f8, dim3(M), dim3(256), 0, stream, X, K, ldx, Q, ldq, s);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;

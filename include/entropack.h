@@ -150,6 +150,32 @@ ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, co
 ep_status ep_gemm_bf16(const void* dev_x, const void* dev_w, int64_t M, int64_t N, int64_t K,
                        void* dev_y, void* hip_stream);
 
+/* FP8 variant of ep_linear_forward: Y[M][N] = s_x[m] s_w[n] sum_k x8[m][k] w8[n][k] (+ bias), BF16
+ * output. The weight is decoded, slice by slice as in ep_linear_forward, into the FP8 E4M3
+ * container with its per-row scale s_w (the FP8 container of "EntroPack: Fast and Accurate
+ * Entropy-Coded Weight Compression at Arbitrary Bitrates", Abstract), the activations are
+ * quantized per row as ep_quantize_rows_fp8 does, and both meet in the gfx950 FP8 MFMA with fp32
+ * accumulation. Same workspace rules as ep_linear_forward. dev_x: [M][K] bf16, 16-byte aligned,
+ * finite; dev_bias: [N] bf16 or NULL; dev_y: [M][N] bf16. Requires a lossy stream and
+ * K % 16 == 0. Asynchronous on hip_stream. */
+ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias,
+                                void* dev_y, void* hip_stream);
+
+/* Per-row FP8 E4M3 quantization of BF16 rows, as the FP8 forward applies it to its activations:
+ * amax = max |x| over the row (raised to 2^-100 when smaller, unless zero), scale = amax / 448,
+ * code = E4M3(x * (448 / amax)) rounded to nearest even and saturated at +-448; a zero row gets
+ * scale 0 and codes 0. dev_x: [M][K] bf16 (finite), dev_q: [M][K] codes, dev_scale: [M] fp32;
+ * K % 16 == 0, dev_x and dev_q 16-byte aligned. Asynchronous on hip_stream. */
+ep_status ep_quantize_rows_fp8(const void* dev_x, int64_t M, int64_t K, uint8_t* dev_q, float* dev_scale,
+                               void* hip_stream);
+
+/* Plain FP8 GEMM, the one ep_linear_forward_fp8 runs on each decoded slice, for overhead
+ * comparisons: Y[m][n] = xs[m] ws[n] sum_k xq[m][k] wq[n][k] (+ bias[n]); xq [M][K] and wq [N][K]
+ * E4M3 codes (16-byte aligned), xs [M] and ws [N] fp32, bias [N] bf16 or NULL, Y [M][N] bf16.
+ * Requires K % 16 == 0. Asynchronous on hip_stream. */
+ep_status ep_gemm_fp8(const uint8_t* dev_xq, const float* dev_xs, const uint8_t* dev_wq, const float* dev_ws,
+                      int64_t M, int64_t N, int64_t K, const void* dev_bias, void* dev_y, void* hip_stream);
+
 /* Synchronize hip_stream and read the handle's device error flag, which kernels set when a
  * tile's words run out or overrun, or a lane's final rANS state differs from its initial
  * value (or, as an internal consistency check, when a decode kernel finds its LDS tables

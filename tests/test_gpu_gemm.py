@@ -160,3 +160,101 @@ def test_compressed_linear_save_and_reload_in_a_fresh_process(tmp_path):
             ) % (root, str(path), str(tmp_path / "x.npy"), str(out))
     subprocess.run([sys.executable, "-c", code], check=True, timeout=300)
     assert np.array_equal(np.load(out), y.cpu().view(torch.int16).numpy())
+
+
+# ---------------------------------------------------------------- FP8 forward
+# The weight decoded to the FP8 E4M3 container with its row scales (EntroPack paper, Abstract:
+# FP8 among the containers) multiplied with per-row E4M3 activations on the FP8 MFMA. Reference:
+# the oracle's FP8 decode and activation quantizer, then the exact product of the dequantized
+# codes in fp64. The bar, relative L2 <= 3e-3, is set by the BF16 rounding of Y (about 1.1e-3
+# RMS); the fp32 accumulation of exact E4M3 products adds far less.
+def e4m3(codes: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def fp8_reference(xq, xs, wq, ws, bias=None):
+    y = (e4m3(xq) @ e4m3(wq).T) * xs[:, None].astype(np.float64) * ws[None, :].astype(np.float64)
+    return y if bias is None else y + bias[None, :]
+
+
+@pytest.mark.parametrize("M,K", [(1, 16), (7, 784), (300, 2048), (64, 16384)])
+def test_quantize_rows_fp8_matches_oracle(M, K):
+    rng = np.random.default_rng(M * K)
+    x = W.to_bf16_bits(rng.standard_t(3, (M, K)) * np.exp(rng.normal(0, 2, (M, 1))))
+    if M > 2:
+        x[1] = 0
+        x[2] = 0
+        x[2, 3] = 0x0001
+    q, s = ep.quantize_rows_fp8(bf16_tensor(x).cuda())
+    torch.cuda.synchronize()
+    qo, so = oracle.quantize_rows_e4m3(x)
+    assert np.array_equal(q.cpu().numpy(), qo)
+    assert np.array_equal(s.cpu().numpy(), so)
+
+
+# shapes cover every FP8 tile choice: 64 x 32 tiles for M <= 64, 64 x 64, 128 x 128 (2 x 256 of them
+# or more) and 256 x 256 (256 or more), with ragged M and N and K not a multiple of the 128 K step
+@pytest.mark.parametrize("M,N,K", [(16, 256, 512), (64, 4100, 1040), (300, 1000, 784), (1, 8, 16),
+                                   (2000, 4000, 144), (4100, 4000, 272), (33, 17, 4112)])
+def test_gemm_fp8_matches_fp64(M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    x = W.to_bf16_bits(rng.normal(0, 1, (M, K)))
+    w = W.to_bf16_bits(rng.standard_t(5, (N, K)) * 0.02)
+    xq, xs = oracle.quantize_rows_e4m3(x)
+    wq, ws = oracle.quantize_rows_e4m3(w)
+    b = W.to_bf16_bits(rng.normal(0, 0.1, N))
+    y = ep.gemm_fp8(torch.from_numpy(xq).cuda(), torch.from_numpy(xs).cuda(), torch.from_numpy(wq).cuda(),
+                    torch.from_numpy(ws).cuda(), bias=bf16_tensor(b).cuda())
+    torch.cuda.synchronize()
+    ref = fp8_reference(xq, xs, wq, ws, W.bf16_bits_to_f32(b).astype(np.float64))
+    assert rel_l2(y.float().cpu().numpy(), ref) < 3e-3
+
+
+def fp8_linear_case(M, N, K, target, seed, bias=False, rows=None):
+    rng = np.random.default_rng(seed)
+    w = (0.02 * rng.standard_t(5, (N, K))).astype(np.float32)
+    x = W.to_bf16_bits(rng.normal(0, 1, (M, K)))
+    s, _ = ep.compress(w, target)
+    b = bf16_tensor(W.to_bf16_bits(rng.normal(0, 0.1, N))).cuda() if bias else None
+    layer = ep.CompressedLinear(s, bias=b, compute="fp8")
+    y = layer(bf16_tensor(x).cuda())
+    torch.cuda.synchronize()
+    layer.handle.check()
+    rows = np.arange(M) if rows is None else rows
+    wq, ws = oracle.decompress(s, oracle.F8E4M3, n_threads=16)
+    xq, xs = oracle.quantize_rows_e4m3(x[rows])
+    ref = fp8_reference(xq, xs, wq, ws, b.float().cpu().numpy().astype(np.float64) if bias else None)
+    w_bf16 = W.bf16_bits_to_f32(oracle.decompress(s, oracle.BF16, n_threads=16)[0])
+    ref_bf16 = W.bf16_bits_to_f32(x[rows]) @ w_bf16.T
+    if bias:
+        ref_bf16 = ref_bf16 + b.float().cpu().numpy()[None, :]
+    return y.float().cpu().numpy()[rows], ref, ref_bf16
+
+
+@pytest.mark.parametrize("M,N,K,target", [(16, 512, 1024, 4.0), (256, 768, 2048, 4.5), (33, 300, 272, 3.0),
+                                          (4, 4096, 512, 6.0)])
+def test_linear_forward_fp8_matches_quantized_reference(M, N, K, target):
+    y, ref, ref_bf16 = fp8_linear_case(M, N, K, target, seed=M + N)
+    assert rel_l2(y, ref) < 3e-3
+    # FP8 activations and weights against the BF16 path: E4M3 rounding of both operands
+    assert rel_l2(y, ref_bf16) < 0.08
+
+
+def test_linear_forward_fp8_with_bias_and_multi_slice():
+    # 9000 x 16384 weight: 128 MiB slices of 8192 rows of E4M3 codes -> two slices, the last ragged
+    y, ref, _ = fp8_linear_case(64, 9000, 16384, 4.0, seed=5, bias=True)
+    assert rel_l2(y, ref) < 3e-3
+
+
+def test_linear_forward_fp8_prefill_sampled_rows():
+    M, N, K = 4096, 8192, 8192
+    w, xb = W.prefill_case()
+    s, _ = ep.compress(w, 4.5, dtype=ep.BF16)
+    layer = ep.CompressedLinear(s, compute="fp8")
+    y = layer(bf16_tensor(xb).cuda())
+    torch.cuda.synchronize()
+    layer.handle.check()
+    rows = np.random.default_rng(6).choice(M, 32, replace=False)
+    wq, ws = oracle.decompress(s, oracle.F8E4M3, n_threads=16)
+    xq, xs = oracle.quantize_rows_e4m3(xb[rows])
+    assert rel_l2(y[rows].float().cpu().numpy(), fp8_reference(xq, xs, wq, ws)) < 3e-3
