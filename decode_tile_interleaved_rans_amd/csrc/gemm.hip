@@ -497,22 +497,34 @@ hipError_t launch_f8(const GemmF8Args& g, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Per-row E4M3 quantization: one 256-thread block per row, two passes over the row (the second
-// from L2): the absolute maximum (wave reduction, then across the four waves in LDS), then the
-// codes, 8 elements per thread per iteration.
+// Per-row E4M3 quantization: one 256-thread block per row. CH > 0: each thread holds its CH
+// chunks of 8 elements in registers (K <= 2048 CH), so the row is read once; CH = 0: two passes
+// over the row (the second from L2). The absolute maximum is reduced within each wave, then
+// across the four waves in LDS.
+template <int CH>
 __global__ __launch_bounds__(256) void quantize_rows_f8(const uint16_t* X, int K, int ldx, uint8_t* Q, int ldq, float* S) {
     __shared__ float wmax[4];
     const int m = blockIdx.x;
     const uint16_t* x = X + (size_t)m * ldx;
+    constexpr int R = CH > 0 ? CH : 1;
+    uint4 v[R];
     float amax = 0.0f;
-    for (int k = 8 * threadIdx.x; k < K; k += 8 * 256) {
-        const uint4 v = *reinterpret_cast<const uint4*>(x + k);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    auto absmax8 = [](const uint4& c, float a) {
+        const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            amax = fmaxf(amax, fabsf(__uint_as_float(w[i] << 16)));
-            amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+        for (int i = 0; i < 4; ++i) a = fmaxf(a, fmaxf(fabsf(__uint_as_float(w[i] << 16)), fabsf(__uint_as_float(w[i] & 0xFFFF0000u))));
+        return a;
+    };
+    if constexpr (CH > 0) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int k = 8 * (threadIdx.x + 256 * c);
+            v[c] = k < K ? *reinterpret_cast<const uint4*>(x + k) : make_uint4(0u, 0u, 0u, 0u);
         }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) amax = absmax8(v[c], amax);
+    } else {
+        for (int k = 8 * threadIdx.x; k < K; k += 8 * 256) amax = absmax8(*reinterpret_cast<const uint4*>(x + k), amax);
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
@@ -520,7 +532,7 @@ __global__ __launch_bounds__(256) void quantize_rows_f8(const uint16_t* X, int K
     __syncthreads();
     amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     uint8_t* q = Q + (size_t)m * ldq;
-    if (amax == 0.0f) {
+    if (amax == 0.0f) {                                        // a zero row: scale 0, codes 0 (+0)
         for (int k = 8 * threadIdx.x; k < K; k += 8 * 256) *reinterpret_cast<uint2*>(q + k) = make_uint2(0u, 0u);
         if (threadIdx.x == 0) S[m] = 0.0f;
         return;
@@ -528,18 +540,105 @@ __global__ __launch_bounds__(256) void quantize_rows_f8(const uint16_t* X, int K
     amax = fmaxf(amax, 0x1p-100f);
     const float inv = 448.0f / amax;
     if (threadIdx.x == 0) S[m] = amax / 448.0f;
-    for (int k = 8 * threadIdx.x; k < K; k += 8 * 256) {
-        const uint4 v = *reinterpret_cast<const uint4*>(x + k);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t c[8];
+    // v_cvt_pk_fp8_f32: two fp32 values to OCP E4M3 codes, rounded to nearest even; |x inv| <= 448
+    // up to one rounding of the product, which rounds back to 448, so no code saturates
+    auto codes8 = [inv](const uint4& c) {
+        const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+        auto lo = [inv](uint32_t v) { return __uint_as_float(v << 16) * inv; };
+        auto hi = [inv](uint32_t v) { return __uint_as_float(v & 0xFFFF0000u) * inv; };
+        int r0 = __builtin_amdgcn_cvt_pk_fp8_f32(lo(w[0]), hi(w[0]), 0, false);
+        r0 = __builtin_amdgcn_cvt_pk_fp8_f32(lo(w[1]), hi(w[1]), r0, true);
+        int r1 = __builtin_amdgcn_cvt_pk_fp8_f32(lo(w[2]), hi(w[2]), 0, false);
+        r1 = __builtin_amdgcn_cvt_pk_fp8_f32(lo(w[3]), hi(w[3]), r1, true);
+        return make_uint2((uint32_t)r0, (uint32_t)r1);
+    };
+    if constexpr (CH > 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            c[2 * i] = e4m3_rne_sat(__uint_as_float(w[i] << 16) * inv);
-            c[2 * i + 1] = e4m3_rne_sat(__uint_as_float(w[i] & 0xFFFF0000u) * inv);
+        for (int c = 0; c < CH; ++c) {
+            const int k = 8 * (threadIdx.x + 256 * c);
+            if (k < K) *reinterpret_cast<uint2*>(q + k) = codes8(v[c]);
         }
-        *reinterpret_cast<uint2*>(q + k) =
-            make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
+    } else {
+        for (int k = 8 * threadIdx.x; k < K; k += 8 * 256)
+            *reinterpret_cast<uint2*>(q + k) = codes8(*reinterpret_cast<const uint4*>(x + k));
     }
+}
+
+// Skinny FP8 GEMM for M <= 64, as gemm_skinny: a block owns 16 output columns, 8 waves split K in
+// 128-code chunks, W streams from HBM into registers, 16x16x128 FP8 MFMA (v_mfma_f32_16x16x128_f8f6f4):
+// lane l supplies row l % 16 of A and column l % 16 of B with the 32 codes 32 (l / 16) .. + 31 of
+// the chunk (the same rule for both operands, so equal k meet) and receives C[4 (l / 16) + i][l % 16].
+template <int MT, bool BIAS>
+__global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_f8(GemmF8Args g) {
+    __shared__ float red[kSkinnyWaves][MT][256];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, kq = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int nrows = g.N - n0 < 16 ? g.N - n0 : 16;
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(g.W + (size_t)n0 * g.ldw), 0, (int)((size_t)nrows * g.ldw), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(g.X), 0, (int)((size_t)g.M * g.ldx), 0x00020000);
+    const uint32_t woff = (uint32_t)r * g.ldw;
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{};
+    const int nkc = (g.K + 127) / 128;
+    for (int kb = wave; kb < nkc; kb += kSkinnyWaves * kSkinnyUnroll) {
+        uint4 bw[kSkinnyUnroll][2], ax[kSkinnyUnroll][MT][2];
+#pragma unroll
+        for (int u = 0; u < kSkinnyUnroll; ++u) {
+            const int kc = kb + u * kSkinnyWaves;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k = kc * 128 + 32 * kq + 16 * h;
+                const bool in = kc < nkc && k < g.K;
+                bw[u][h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, in ? woff + (uint32_t)k : kOob, 0, 0));
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const uint32_t xo = (uint32_t)(mt * 16 + r) * g.ldx + (uint32_t)k;
+                    ax[u][mt][h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, in ? xo : kOob, 0, 0));
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kSkinnyUnroll; ++u) {
+            const i32x8 b8 = {(int)bw[u][0].x, (int)bw[u][0].y, (int)bw[u][0].z, (int)bw[u][0].w,
+                              (int)bw[u][1].x, (int)bw[u][1].y, (int)bw[u][1].z, (int)bw[u][1].w};
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const i32x8 a8 = {(int)ax[u][mt][0].x, (int)ax[u][mt][0].y, (int)ax[u][mt][0].z, (int)ax[u][mt][0].w,
+                                  (int)ax[u][mt][1].x, (int)ax[u][mt][1].y, (int)ax[u][mt][1].z, (int)ax[u][mt][1].w};
+                acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[mt], 0, 0, 0, 0, 0, 0);
+            }
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][mt][(4 * kq + i) * 16 + r] = acc[mt][i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < MT * 256; e += 64 * kSkinnyWaves) {
+        const int mt = e >> 8, row = (e >> 4) & 15, col = e & 15;
+        const int m = mt * 16 + row, nn = n0 + col;
+        if (m >= g.M || nn >= g.N) continue;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kSkinnyWaves; ++w) v += red[w][mt][e & 255];
+        v = v * g.sw[nn] * g.sx[m];
+        if constexpr (BIAS) v += __uint_as_float((uint32_t)g.bias[nn] << 16);
+        g.Y[(size_t)m * g.ldy + nn] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+    }
+}
+
+template <int MT>
+hipError_t launch_skinny_f8(const GemmF8Args& g, hipStream_t stream) {
+    const int blocks = (g.N + 15) / 16;
+    if (g.bias)
+        hipLaunchKernelGGL((gemm_skinny_f8<MT, true>), dim3(blocks), dim3(64 * kSkinnyWaves), 0, stream, g);
+    else
+        hipLaunchKernelGGL((gemm_skinny_f8<MT, false>), dim3(blocks), dim3(64 * kSkinnyWaves), 0, stream, g);
+    return hipGetLastError();
 }
 
 int gemm_device_cus() {
@@ -582,14 +681,21 @@ hipError_t launch_gemm_f8(const GemmF8Args& g, hipStream_t stream) {
     if (tiles256 >= gemm_device_cus()) return launch_f8<256, 256, 4, 4>(g, stream);
     const long tiles128 = (long)((g.M + 127) / 128) * ((g.N + 127) / 128);
     if (tiles128 >= 2L * gemm_device_cus()) return launch_f8<128, 128, 2, 2>(g, stream);
-    if (g.M <= 64) return launch_f8<64, 32, 2, 1>(g, stream);
+    if (g.M <= 16) return launch_skinny_f8<1>(g, stream);
+    if (g.M <= 32) return launch_skinny_f8<2>(g, stream);
+    if (g.M <= 64) return launch_skinny_f8<4>(g, stream);
     return launch_f8<64, 64, 2, 2>(g, stream);
 }
 
 hipError_t launch_quantize_rows_f8(const uint16_t* X, int M, int K, int ldx, uint8_t* Q, int ldq, float* s,
                                    hipStream_t stream) {
     if (M <= 0) return hipSuccess;
-    hipLaunchKernelGGL(quantize_rows_f8, dim3(M), dim3(256), 0, stream, X, K, ldx, Q, ldq, s);
+    const int chunks = (K + 2047) / 2048;                  // 8-element chunks per thread
+    if (chunks <= 1) hipLaunchKernelGGL(quantize_rows_f8<1>, dim3(M), dim3(256), 0, stream, X, K, ldx, Q, ldq, s);
+    else if (chunks <= 2) hipLaunchKernelGGL(quantize_rows_f8<2>, dim3(M), dim3(256), 0, stream, X, K, ldx, Q, ldq, s);
+    else if (chunks <= 4) hipLaunchKernelGGL(quantize_rows_f8<4>, dim3(M), dim3(256), 0, stream, X, K, ldx, Q, ldq, s);
+    else if (chunks <= 8) hipLaunchKernelGGL(quantize_rows_f8<8>, dim3(M), dim3(256), 0, stream, X, K, ldx, Q, ldq, s);
+    else hipLaunchKernelGGL(quantize_rows_f8<0>, dim3(M), dim3(256), 0, stream, X, K, ldx, Q, ldq, s);
     return hipGetLastError();
 }
 

@@ -183,8 +183,10 @@ def test_quantize_rows_fp8_matches_oracle(M, K):
     x = W.to_bf16_bits(rng.standard_t(3, (M, K)) * np.exp(rng.normal(0, 2, (M, 1))))
     if M > 2:
         x[1] = 0
+        x[1, ::3] = 0x8000                         # a zero row with -0.0 entries: codes +0
         x[2] = 0
         x[2, 3] = 0x0001
+        x[0, 1] = 0x8000                           # -0.0 in a non-zero row keeps its sign
     q, s = ep.quantize_rows_fp8(bf16_tensor(x).cuda())
     torch.cuda.synchronize()
     qo, so = oracle.quantize_rows_e4m3(x)
