@@ -12,8 +12,8 @@ Prints one JSON line (rank 0, N = 1): decoded-weight GB/s (container bytes writt
 the roofline of the step's one grouped decode launch from HIP events on the launch stream,
 the two lossless BF16 codings side by side (byte planes, and the exponent-coded variant), the
 fused decode + GEMM forward of an 8192 x 8192 weight at 4.5 bpp against the plain BF16 GEMM
-(M = 4096, 256, 16), and the oracle's CPU decode of one step on the host cores as a reported
-baseline.
+(M = 4096, 256, 16), the same forward with FP8 compute against the plain FP8 GEMM, and the
+oracle's CPU decode of one step on the host cores as a reported baseline.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-gemm]
 """
@@ -107,6 +107,7 @@ def fused_gemm_section(torch, ep, reps: int = 15):
     s, bpp = ep.compress(w, 4.5, dtype=ep.BF16)
     log(f"encoded 8192x8192 at target 4.5: actual {bpp:.4f} bpp in {time.time() - t0:.2f} s")
     layer = ep.CompressedLinear(s)
+    layer8 = ep.CompressedLinear(s, compute="fp8")
     Wt = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda()
     Xf = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
     N, K = Wt.shape
@@ -141,13 +142,17 @@ def fused_gemm_section(torch, ep, reps: int = 15):
     out = {"workload": "W 0.02 t5 bf16 [8192, 8192] at 4.5 bpp, X N(0,1) bf16 [M, 8192], Y = X W^T bf16, "
                        "fp32 accumulate",
            "actual_bpp": round(bpp, 4), "stream_bytes": len(s), "decode_full_us": round(t_dec, 2),
-           "reps": reps, "timing": "median of per-rep HIP events, the three variants interleaved within each "
+           "reps": reps, "timing": "median of per-rep HIP events, the five variants interleaved within each "
                                    "rep, 1 GiB cache flush before every timed call"}
+    wq, ws = ep.quantize_rows_fp8(Wt)                  # plain FP8 baseline: the weight pre-quantized
     for M in (4096, 256, 16):
         X = Xf[:M].contiguous()
-        (t_f, t_f_min), (t_o, _), (t_t, _) = timed([lambda: layer(X), lambda: ep.gemm_bf16(X, Wt),
-                                                     lambda: torch.matmul(X, Wt.t())])
+        xq, xs = ep.quantize_rows_fp8(X)
+        (t_f, t_f_min), (t_o, _), (t_t, _), (t_f8, _), (t_o8, _) = timed(
+            [lambda: layer(X), lambda: ep.gemm_bf16(X, Wt), lambda: torch.matmul(X, Wt.t()),
+             lambda: layer8(X), lambda: ep.gemm_fp8(xq, xs, wq, ws)])
         layer.handle.check()
+        layer8.handle.check()
         fl = 2.0 * M * N * K
         out[f"M{M}"] = {
             "fused_us": round(t_f, 2), "fused_min_us": round(t_f_min, 2), "own_gemm_us": round(t_o, 2),
@@ -155,11 +160,17 @@ def fused_gemm_section(torch, ep, reps: int = 15):
             "overhead_vs_own_gemm": round(t_f / t_o - 1, 4), "overhead_vs_torch": round(t_f / t_t - 1, 4),
             "fused_tflops": round(fl / t_f / 1e6, 1), "own_gemm_tflops": round(fl / t_o / 1e6, 1),
             "torch_tflops": round(fl / t_t / 1e6, 1),
+            # FP8 compute: weight decoded to E4M3 + row scales, activations quantized per row
+            "fp8_fused_us": round(t_f8, 2), "fp8_own_gemm_us": round(t_o8, 2),
+            "fp8_overhead_vs_own_fp8_gemm": round(t_f8 / t_o8 - 1, 4),
+            "fp8_fused_vs_torch_bf16": round(t_f8 / t_t - 1, 4),
+            "fp8_fused_tflops": round(fl / t_f8 / 1e6, 1), "fp8_own_gemm_tflops": round(fl / t_o8 / 1e6, 1),
             # HBM-bound view for small M: X + compressed W + Y
             "fused_hbm_frac": round((2 * M * K + len(s) + 2 * M * N) / t_f / 1e3 / HBM_PEAK_GBS, 4),
         }
-        log(f"fused GEMM M={M}: fused {t_f:.1f} us, own GEMM {t_o:.1f} us, torch {t_t:.1f} us")
-    del flush, wdec, Wt, Xf, layer
+        log(f"fused GEMM M={M}: fused {t_f:.1f} us, own GEMM {t_o:.1f} us, torch {t_t:.1f} us; "
+            f"FP8 fused {t_f8:.1f} us, own FP8 GEMM {t_o8:.1f} us")
+    del flush, wdec, Wt, Xf, layer, layer8, wq, ws
     torch.cuda.empty_cache()
     return out
 

@@ -37,7 +37,6 @@
 #include <set>
 #include <type_traits>
 
-#include "casts.h"
 #include "kernels.h"
 
 namespace ep {
@@ -301,8 +300,7 @@ struct Conv<CT_F16> {
 };
 template <>
 struct Conv<CT_F8E4M3> {
-    using T = uint8_t;
-    __device__ static uint32_t f(float q, float, float h, uint32_t, uint32_t) { return e4m3_rne_sat(q * h); }
+    using T = uint8_t;      // converted pairwise in store_block
 };
 template <>
 struct Conv<CT_I8> {
@@ -338,6 +336,17 @@ __device__ __forceinline__ void store_block(const MatDesc& M, uint32_t row, uint
             else pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, f16x2));
             v[j] = pk & 0xFFFFu;
             v[j + 1] = pk >> 16;
+        }
+    } else if constexpr (CT == CT_F8E4M3) {
+        // two values per v_cvt_pk_fp8_f32 (OCP E4M3, round to nearest even) of the fp32 products,
+        // clamped to +-448 first (med3), which makes the cast saturating
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+            const float a = __builtin_amdgcn_fmed3f(q[j] * h, -448.0f, 448.0f);
+            const float b = __builtin_amdgcn_fmed3f(q[j + 1] * h, -448.0f, 448.0f);
+            const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+            v[j] = pk & 0xFFu;
+            v[j + 1] = (pk >> 8) & 0xFFu;
         }
     } else {
 #pragma unroll

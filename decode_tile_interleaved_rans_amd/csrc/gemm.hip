@@ -24,7 +24,6 @@
 
 #include <cstdint>
 
-#include "casts.h"
 #include "gemm.h"
 
 namespace ep {
