@@ -339,3 +339,22 @@ def test_c5_mixed_rate_set_all_containers():
         del outs, scales
     for h in hs:
         h.release()
+
+
+def test_fp8_container_saturates_on_very_wide_rows():
+    """A row's normalized values reach sqrt(C) (one non-zero entry in a unit-RMS row), so with
+    C = 2^18 the FP8 values q * step / 2 pass 448 and must saturate to the largest E4M3 code."""
+    R, Cc = 16, 1 << 18
+    rng = np.random.default_rng(12)
+    w = np.zeros((R, Cc), np.float32)
+    w[:, 5] = rng.choice([-1.0, 1.0], R)
+    w[:, 1000:1008] = rng.normal(0, 1e-3, (R, 8))
+    s, _ = ep.compress(w, 4.0)
+    want, wscale = oracle.decompress(s, oracle.F8E4M3, n_threads=16)
+    assert np.all((want[:, 5] & 0x7F) == 0x7E), "the oracle saturates at 448"
+    h = ep.upload(s)
+    out, scale = h.decompress(torch.float8_e4m3fn)
+    torch.cuda.synchronize()
+    h.check()
+    assert np.array_equal(bits(out), want)
+    assert np.array_equal(scale.cpu().numpy(), wscale)
