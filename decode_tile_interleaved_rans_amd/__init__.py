@@ -26,7 +26,7 @@ STATUS = {0: "EP_OK", -1: "EP_EINVAL", -2: "EP_ECORRUPT", -3: "EP_EUNSUPPORTED",
 EXPORTS = ["ep_compress", "ep_free", "ep_stream_info", "ep_upload", "ep_handle_info", "ep_decompress",
            "ep_decompress_many", "ep_decode_symbols", "ep_linear_forward", "ep_gemm_bf16", "ep_handle_check",
            "ep_release", "ep_last_error", "ep_version", "ep_linear_forward_fp8", "ep_quantize_rows_fp8",
-           "ep_gemm_fp8"]
+           "ep_gemm_fp8", "ep_compress_device"]
 
 
 class EPError(RuntimeError):
@@ -64,6 +64,8 @@ def lib() -> C.CDLL:
         vp, i64, sz = C.c_void_p, C.c_int64, C.c_size_t
         L.ep_compress.argtypes = [vp, C.c_int, i64, i64, C.POINTER(EncodeOpts), C.POINTER(C.POINTER(C.c_uint8)),
                                   C.POINTER(sz), C.POINTER(C.c_double)]
+        L.ep_compress_device.argtypes = [vp, C.c_int, i64, i64, C.POINTER(EncodeOpts), vp,
+                                         C.POINTER(C.POINTER(C.c_uint8)), C.POINTER(sz), C.POINTER(C.c_double)]
         L.ep_free.argtypes = [vp]
         L.ep_free.restype = None
         L.ep_stream_info.argtypes = [C.c_char_p, sz, C.POINTER(Info)]
@@ -148,6 +150,27 @@ def compress(w, target_bpp: float = 4.0, *, mode: int = LOSSY, prob_bits: int = 
     bpp = C.c_double()
     _check(lib().ep_compress(arr.ctypes.data_as(C.c_void_p), code, R, Cc, C.byref(opts), C.byref(out), C.byref(n),
                              C.byref(bpp)), "ep_compress")
+    data = C.string_at(out, n.value)
+    lib().ep_free(out)
+    return data, bpp.value
+
+
+def compress_device(w, target_bpp: float = 4.0, *, prob_bits: int = 12, tile_rows: int = 16,
+                    stream=None) -> tuple[bytes, float]:
+    """Lossy compression on the GPU of a 2-D weight in device memory (torch tensor: float32,
+    bfloat16 or float16); the same bytes as compress() on the same values."""
+    if w.dim() != 2:
+        raise ValueError("compress_device takes a 2-D [out_features, in_features] matrix")
+    t = w.detach().contiguous()
+    if not t.is_cuda:
+        raise ValueError("compress_device takes a tensor in device memory")
+    R, Cc = t.shape
+    opts = EncodeOpts(LOSSY, float(target_bpp), prob_bits, tile_rows, 0)
+    out = C.POINTER(C.c_uint8)()
+    n = C.c_size_t()
+    bpp = C.c_double()
+    _check(lib().ep_compress_device(C.c_void_p(t.data_ptr()), _dtype_code(t.dtype), R, Cc, C.byref(opts),
+                                    _stream_ptr(stream), C.byref(out), C.byref(n), C.byref(bpp)), "ep_compress_device")
     data = C.string_at(out, n.value)
     lib().ep_free(out)
     return data, bpp.value

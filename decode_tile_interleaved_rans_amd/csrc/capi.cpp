@@ -381,6 +381,37 @@ ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, co
     return EP_OK;
 }
 
+ep_status ep_compress_device(const void* dev_w, ep_dtype src, int64_t rows, int64_t cols, const ep_encode_opts* opts,
+                             void* hip_stream, uint8_t** out_stream, size_t* out_len, double* actual_bpp) {
+    if (!out_stream || !out_len) return fail(EP_EINVAL, "null output pointer");
+    if (rows < 0 || cols < 0) return fail(EP_EINVAL, "negative shape");
+    if (rows * cols > 0 && !dev_w) return fail(EP_EINVAL, "null input");
+    if (rows > 0xFFFFFFFFll || cols >= (1ll << 28)) return fail(EP_ERANGE, "shape too large (cols must be < 2^28)");
+    ep_encode_opts o = opts ? *opts : ep_encode_opts{EP_MODE_LOSSY_E8, 4.0, 12, 16, 0};
+    if (o.mode != EP_MODE_LOSSY_E8) return fail(EP_EUNSUPPORTED, "the device encoder codes the lossy mode");
+    if (o.prob_bits < 10 || o.prob_bits > 12) return fail(EP_EINVAL, "prob_bits must be 10..12");
+    if (o.tile_rows != 16 && o.tile_rows != 32) return fail(EP_EINVAL, "tile_rows must be 16 or 32");
+    if (src != EP_F32 && src != EP_BF16 && src != EP_F16)
+        return fail(EP_EUNSUPPORTED, "lossy mode takes F32, BF16 or F16 input");
+    if (!(o.target_bpp > 0.0 && o.target_bpp <= 32.0)) return fail(EP_EINVAL, "target_bpp must be in (0, 32]");
+    std::vector<uint8_t> buf;
+    std::string why;
+    ep_status st;
+    try {
+        st = ep::encode_lossy_device(dev_w, src, rows, cols, o, static_cast<hipStream_t>(hip_stream), &buf, &why);
+    } catch (const std::bad_alloc&) {
+        return fail(EP_ENOMEM, "host allocation failed while encoding");
+    }
+    if (st != EP_OK) return fail(st, why);
+    uint8_t* p = static_cast<uint8_t*>(std::malloc(buf.size() ? buf.size() : 1));
+    if (!p) return fail(EP_ENOMEM, "host allocation failed for the stream");
+    if (!buf.empty()) std::memcpy(p, buf.data(), buf.size());
+    *out_stream = p;
+    *out_len = buf.size();
+    if (actual_bpp) *actual_bpp = rows * cols > 0 ? 8.0 * (double)buf.size() / ((double)rows * (double)cols) : 0.0;
+    return EP_OK;
+}
+
 ep_status ep_quantize_rows_fp8(const void* dev_x, int64_t M, int64_t K, uint8_t* dev_q, float* dev_scale,
                                void* hip_stream) {
     if (M < 0 || K < 0) return fail(EP_EINVAL, "negative size");

@@ -15,8 +15,11 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <functional>
 #include <string>
 #include <vector>
+
+#include <hip/hip_runtime.h>
 
 #include "entropack.h"
 
@@ -68,5 +71,22 @@ void fill_info(const StreamView& v, ep_info* info);
 // Host encoder.
 ep_status encode(const void* w, int dtype, int64_t rows, int64_t cols, const ep_encode_opts& o,
                  std::vector<uint8_t>* out, std::string* why);
+
+// Pieces of the host encoder that the device encoder shares (same arithmetic, so that both
+// produce the same bytes).
+constexpr int kSampleBlocks = 65536;   // rate-search sample
+constexpr int kSearchIters = 48;       // log-bisection steps of the rate search
+constexpr int32_t kValueSpan = 1 << 15;
+bool normalize_frequencies(const uint64_t cnt[256], int n, uint32_t f[256]);
+double sample_estimate(const uint64_t (*cnt)[256], const uint64_t* totals, int64_t sb);
+float choose_step(double U, double target, const std::function<double(double)>& est);
+void serialize_lossy(int dt, int64_t R, int64_t C, int tile_rows, int n, const std::vector<Table>& tables, float step,
+                     float target, const std::vector<float>& scale, const std::vector<uint16_t>& qmax,
+                     std::vector<uint8_t>&& payload, std::vector<uint32_t>&& offsets, uint32_t n_esc,
+                     std::vector<uint8_t>* out, const uint32_t* payload_crc = nullptr);
+
+// Device encoder (lossy mode): the same stream as encode() from a weight in device memory.
+ep_status encode_lossy_device(const void* dev_w, int dt, int64_t rows, int64_t cols, const ep_encode_opts& o,
+                              hipStream_t stream, std::vector<uint8_t>* out, std::string* why);
 
 }  // namespace ep

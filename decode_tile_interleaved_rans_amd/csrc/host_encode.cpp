@@ -36,9 +36,6 @@
 namespace ep {
 namespace {
 
-constexpr int kSampleBlocks = 65536;
-constexpr int kSearchIters = 48;
-constexpr int32_t kValueSpan = 1 << 15;   // |x| <= 16385 by the step guard; histogram offset
 
 // ------------------------------------------------------------------------------ threading
 template <class F>
@@ -291,7 +288,7 @@ struct TileSet {
 void serialize(int mode, int dt, int64_t R, int64_t C, int tile_rows, int n, const std::vector<Table>& tables,
                float step, float target, const std::vector<float>& scale, const std::vector<uint16_t>& qmax,
                const TileSet& ts, uint32_t n_esc, std::vector<uint8_t>* out,
-               const std::vector<uint8_t>* raw = nullptr) {
+               const std::vector<uint8_t>* raw = nullptr, const uint32_t* payload_crc = nullptr) {
     const uint64_t meta_rows = mode == EP_MODE_LOSSY_E8 ? (uint64_t)R : 0;
     uint64_t tables_len = 0;
     for (const Table& t : tables) tables_len += 6 + 2 * (uint64_t)t.width;
@@ -326,7 +323,7 @@ void serialize(int mode, int dt, int64_t R, int64_t C, int tile_rows, int n, con
     w64(s + kOffIndex, o_idx);
     w64(s + kOffPayload, o_pay);
     w64(s + kTotalLen, total);
-    w32(s + kPayloadCrc, crc32(ts.payload.data(), ts.payload.size()));
+    w32(s + kPayloadCrc, payload_crc ? *payload_crc : crc32(ts.payload.data(), ts.payload.size()));
     if (raw) {
         w64(s + kOffRaw, o_raw);
         w32(s + kRawCrc, crc32(raw->data(), raw->size()));
@@ -396,6 +393,46 @@ struct Quantizer {
     }
 };
 
+// Payload estimate of a sample of sb blocks from its 17 windowed tables: the empirical entropy
+// of every table plus 16 bits per escape, per weight.
+double estimate_bits(const uint64_t (*cnt)[256], const uint64_t* totals, int64_t sb) {
+    double bits = 0.0;
+    for (int t = 0; t < kLossyTables; ++t) {
+        const double tot = (double)totals[t];
+        for (int s = 0; s < 256; ++s) {
+            if (!cnt[t][s]) continue;
+            const double c = (double)cnt[t][s];
+            bits -= c * std::log2(c / tot);
+        }
+        bits += 16.0 * (double)cnt[t][kEscape];
+    }
+    return bits / (8.0 * (double)sb);
+}
+
+// Log-bisection of the step between max(2^-12, guard) and 64 on the estimate est(step), keeping
+// the side at or under the target; guard = 2 (U + 1) / 32767 keeps every coordinate inside the
+// int16 escape range (U = max |w / s_r|).
+template <class Est>
+float search_step(double U, double target, Est&& est) {
+    const double guard = 2.0 * (U + 1.0) / 32767.0;
+    double lo = std::max(std::ldexp(1.0, -12), guard), hi = 64.0, pick;
+    if (est(lo) <= target) {
+        pick = lo;
+    } else if (est(hi) > target) {
+        pick = hi;
+    } else {
+        for (int it = 0; it < kSearchIters; ++it) {
+            double mid = std::sqrt(lo * hi);
+            if (est(mid) > target) lo = mid;
+            else hi = mid;
+        }
+        pick = hi;
+    }
+    float step = (float)pick;
+    if ((double)step < guard) step = std::nextafter(step, INFINITY);
+    return step;
+}
+
 double sampled_bpp(const Quantizer& Q, int64_t nb, int64_t sb, double delta, int threads, std::vector<Block>& blk,
                    std::vector<Hist>& hist) {
     const int64_t kb = (Q.C + 7) / 8;
@@ -414,20 +451,13 @@ double sampled_bpp(const Quantizer& Q, int64_t nb, int64_t sb, double delta, int
         hist[0].add(B.b);
         for (int j = 0; j < 8; ++j) hist[1 + 2 * j + B.b].add((B.q[j] - B.b) / 2);
     }
-    double bits = 0.0;
+    uint64_t cnt[kLossyTables][256], totals[kLossyTables];
     for (int t = 0; t < kLossyTables; ++t) {
         int32_t lo, width;
-        uint64_t cnt[256];
-        window_counts(hist[t], &lo, &width, cnt);
-        const double tot = (double)hist[t].total;
-        for (int s = 0; s < 256; ++s) {
-            if (!cnt[s]) continue;
-            const double c = (double)cnt[s];
-            bits -= c * std::log2(c / tot);
-        }
-        bits += 16.0 * (double)cnt[kEscape];
+        window_counts(hist[t], &lo, &width, cnt[t]);
+        totals[t] = hist[t].total;
     }
-    return bits / (8.0 * (double)sb);
+    return estimate_bits(cnt, totals, sb);
 }
 
 ep_status encode_lossy(const void* w, int dt, int64_t R, int64_t C, const ep_encode_opts& o, int threads,
@@ -470,23 +500,7 @@ ep_status encode_lossy(const void* w, int dt, int64_t R, int64_t C, const ep_enc
         const int64_t sb = std::min<int64_t>(nb, kSampleBlocks);
         std::vector<Block> blk(sb);
         std::vector<Hist> hist(kLossyTables);
-        auto est = [&](double d) { return sampled_bpp(Q, nb, sb, d, threads, blk, hist); };
-        const double guard = 2.0 * (U + 1.0) / 32767.0;
-        double lo = std::max(std::ldexp(1.0, -12), guard), hi = 64.0, pick;
-        if (est(lo) <= o.target_bpp) {
-            pick = lo;
-        } else if (est(hi) > o.target_bpp) {
-            pick = hi;
-        } else {
-            for (int it = 0; it < kSearchIters; ++it) {
-                double mid = std::sqrt(lo * hi);
-                if (est(mid) > o.target_bpp) lo = mid;
-                else hi = mid;
-            }
-            pick = hi;
-        }
-        step = (float)pick;
-        if ((double)step < guard) step = std::nextafter(step, INFINITY);
+        step = search_step(U, o.target_bpp, [&](double d) { return sampled_bpp(Q, nb, sb, d, threads, blk, hist); });
     }
     // full quantization, row-parallel, with per-worker table histograms
     std::vector<int16_t> q(Rp * Cp, 0);
@@ -682,6 +696,27 @@ ep_status encode_lossless_exp(const void* w, int64_t R, int64_t C, const ep_enco
 }
 
 }  // namespace
+
+bool normalize_frequencies(const uint64_t cnt[256], int n, uint32_t f[256]) { return normalize_freq(cnt, n, f); }
+
+double sample_estimate(const uint64_t (*cnt)[256], const uint64_t* totals, int64_t sb) {
+    return estimate_bits(cnt, totals, sb);
+}
+
+float choose_step(double U, double target, const std::function<double(double)>& est) {
+    return search_step(U, target, est);
+}
+
+void serialize_lossy(int dt, int64_t R, int64_t C, int tile_rows, int n, const std::vector<Table>& tables, float step,
+                     float target, const std::vector<float>& scale, const std::vector<uint16_t>& qmax,
+                     std::vector<uint8_t>&& payload, std::vector<uint32_t>&& offsets, uint32_t n_esc,
+                     std::vector<uint8_t>* out, const uint32_t* payload_crc) {
+    TileSet ts;
+    ts.payload = std::move(payload);
+    ts.offsets = std::move(offsets);
+    serialize(EP_MODE_LOSSY_E8, dt, R, C, tile_rows, n, tables, step, target, scale, qmax, ts, n_esc, out, nullptr,
+              payload_crc);
+}
 
 ep_status encode(const void* w, int dt, int64_t R, int64_t C, const ep_encode_opts& o, std::vector<uint8_t>* out,
                  std::string* why) {

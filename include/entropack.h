@@ -93,7 +93,21 @@ ep_status ep_compress(const void* host_w, ep_dtype src, int64_t rows, int64_t co
                       const ep_encode_opts* opts, uint8_t** out_stream, size_t* out_len,
                       double* actual_bpp);
 
-/* Free a buffer returned by ep_compress. NULL is allowed. */
+/* Device encoder of the lossy mode: the same stream as ep_compress, byte for byte, computed on the
+ * GPU from a weight already in device memory (row scales, the sampled rate search, the E8
+ * quantization, the model and the tile rANS coding all run as kernels; the method's "fast
+ * encoding", "EntroPack: Fast and Accurate Entropy-Coded Weight Compression at Arbitrary
+ * Bitrates", Abstract). dev_w: [rows][cols] elements of src (EP_F32, EP_BF16, EP_F16) on the
+ * current device; opts as for ep_compress (mode must be EP_MODE_LOSSY_E8; n_threads is unused).
+ * The call synchronizes hip_stream; device scratch (about 2.3 bytes per weight plus 18 KiB per
+ * 16-row tile for the word stacks) is allocated and freed inside the call. *out_stream is
+ * library-allocated (free with ep_free). Errors: as ep_compress, plus EP_EHIP / EP_ENOMEM for
+ * device failures and EP_EUNSUPPORTED for a lossless mode. */
+ep_status ep_compress_device(const void* dev_w, ep_dtype src, int64_t rows, int64_t cols,
+                             const ep_encode_opts* opts, void* hip_stream, uint8_t** out_stream,
+                             size_t* out_len, double* actual_bpp);
+
+/* Free a buffer returned by ep_compress or ep_compress_device. NULL is allowed. */
 void ep_free(void* p);
 
 /* Validate a host stream (magic, version, section bounds, every table summing to 2^n, tile
