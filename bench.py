@@ -214,6 +214,33 @@ def lossless_section(torch, ep, reps: int = 10):
     return out
 
 
+def encoder_section(torch, ep, reps: int = 3):
+    """The lossy encoders on the 8192 x 8192 BF16 weight at 4.5 bpp: the device encoder (weight in
+    device memory, stream returned to the host) against the threaded host encoder; both produce
+    the same bytes (checked). Wall-clock medians of reps calls."""
+    from decode_tile_interleaved_rans_amd import workloads as W
+    w, _ = W.prefill_case()
+    t = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda()
+    ep.compress_device(t, 4.5)
+    torch.cuda.synchronize()
+    dev, host = [], []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        sd, _ = ep.compress_device(t, 4.5)
+        t1 = time.perf_counter()
+        sh, _ = ep.compress(w, 4.5, dtype=ep.BF16)
+        t2 = time.perf_counter()
+        if sd != sh:
+            raise RuntimeError("device and host encoders disagree")
+        dev.append(t1 - t0)
+        host.append(t2 - t1)
+    d, h = float(np.median(dev)), float(np.median(host))
+    log(f"encoders 8192^2 at 4.5: device {1e3 * d:.1f} ms, host {1e3 * h:.1f} ms")
+    return {"workload": "W 0.02 t5 bf16 [8192, 8192] at 4.5 bpp, stream to host memory", "device_ms": round(1e3 * d, 2),
+            "host_ms": round(1e3 * h, 2), "host_threads": os.cpu_count(), "device_gweights_per_s": round(w.size / d / 1e9, 3),
+            "host_gweights_per_s": round(w.size / h / 1e9, 3), "identical_streams": True}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -312,6 +339,7 @@ def main():
     sets.clear()
     torch.cuda.empty_cache()
     lossless = lossless_section(torch, ep)
+    encoders = encoder_section(torch, ep)
     fused = None
     if not args.no_gemm:
         fused = fused_gemm_section(torch, ep, reps=args.gemm_reps)
@@ -333,6 +361,7 @@ def main():
         "roofline": roofline,
         "per_decode": per_item,
         "lossless_bf16_codings": lossless,
+        "encoders": encoders,
         "fused_gemm": fused,
         "cpu_baseline": cpu,
     }

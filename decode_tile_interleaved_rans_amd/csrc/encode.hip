@@ -5,9 +5,9 @@
 // Arbitrary Bitrates", Abstract: rows scaled to unit size, E8 lattice quantization, a conditional
 // coordinate model, a step chosen from a size estimate on a sample, tile-wise entropy coding) run
 // as kernels:
-//   row_scales     one thread per row sums w^2 in fp64 in column order (the order fixes the
-//                  rounding, so it matches the host), then s_r = fp32(sqrt(sum / C))
-//   row_umax       max |w / s_r| over the matrix (an exact maximum, any order)
+//   row_stats      one thread per row sums w^2 in fp64 in column order (the order fixes the
+//                  rounding, so it matches the host), then s_r = fp32(sqrt(sum / C)), and the
+//                  row's max |w / s_r| (an exact maximum)
 //   quantize       nearest E8 point of 8-column blocks at a given step: the rate-search sample
 //                  (strided blocks) or every block of the padded matrix; per-table value
 //                  histograms (LDS bins for |x| < 128, global atomics beyond), doubled
@@ -19,7 +19,7 @@
 //                  tile's steps and stacks its escape and renormalization words at positions given
 //                  by wave ballots (escapes, then refills, each in descending lane order)
 //   assemble       each tile's 32 states and its words in reading order at the tile's offset
-//   chunk_crc      CRC-32 of 4 KiB payload chunks, combined on the host
+//   chunk_crc      CRC-32 of 512-byte payload chunks, combined on the host
 // The host part keeps what is order-sensitive in floating point or tiny: the entropy estimate of
 // each bisection step (same summation as the host encoder), the frequency normalization, the tile
 // offsets and the header.
@@ -113,35 +113,48 @@ __device__ __forceinline__ void block_y(const void* w, const float* scale, int64
 }
 
 // ----------------------------------------------------------------------------- row statistics
+// One thread per row: the fp64 sum of squares in column order (16-byte loads when every row is
+// 16-byte aligned, the same order either way) and max |w|. max_j |w_j| / s_r equals the largest of
+// the quotients |w_j| / s_r, since a correctly rounded division by s_r > 0 is monotone, so one
+// division per row gives the row's max |w / s_r|.
 template <int DT>
-__global__ __launch_bounds__(64) void row_scales(const void* w, int64_t R, int64_t C, float* scale, int* bad) {
+__device__ __forceinline__ void accumulate(double v, double& acc, double& amax, bool& finite) {
+    finite = finite && isfinite(v);
+    acc += v * v;
+    amax = fmax(amax, fabs(v));
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(64) void row_stats(const void* w, int64_t R, int64_t C, float* scale, int* bad,
+                                                unsigned long long* umax) {
     const int64_t r = (int64_t)blockIdx.x * 64 + threadIdx.x;
     if (r >= R) return;
-    double acc = 0.0;
+    double acc = 0.0, amax = 0.0;
     bool finite = true;
-    for (int64_t j = 0; j < C; ++j) {
-        const double v = widen_d<DT>(w, r * C + j);
-        finite = finite && isfinite(v);
-        acc += v * v;
+    if constexpr (VEC) {
+        constexpr int E = DT == EP_F32 ? 4 : 8;                 // elements per 16 bytes
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const char*>(w) + (size_t)r * C * (16 / E));
+        for (int64_t j = 0; j < C / E; ++j) {
+            const uint4 v = p[j];
+            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+            if constexpr (DT == EP_F32) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) accumulate<DT>((double)__uint_as_float(u[i]), acc, amax, finite);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint16_t h = (uint16_t)(u[i >> 1] >> (16 * (i & 1)));
+                    accumulate<DT>(widen_d<DT>(&h, 0), acc, amax, finite);
+                }
+            }
+        }
+    } else {
+        for (int64_t j = 0; j < C; ++j) accumulate<DT>(widen_d<DT>(w, r * C + j), acc, amax, finite);
     }
     const float s = C ? (float)sqrt(acc / (double)C) : 0.0f;
     scale[r] = s;
     if (!finite || !isfinite(s)) atomicOr(bad, 1);
-}
-
-template <int DT>
-__global__ __launch_bounds__(256) void row_umax(const void* w, int64_t R, int64_t C, const float* scale,
-                                                unsigned long long* umax) {
-    double m = 0.0;
-    const int64_t n = R * C;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-        const int64_t r = i / C;
-        if (scale[r] == 0.0f) continue;
-        m = fmax(m, fabs(widen_d<DT>(w, i) / (double)scale[r]));
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
-    if ((threadIdx.x & 63) == 0) atomicMax(umax, (unsigned long long)__double_as_longlong(m));   // m >= 0
+    if (s != 0.0f && finite) atomicMax(umax, (unsigned long long)__double_as_longlong(amax / (double)s));
 }
 
 // ----------------------------------------------------------------------------- quantization
@@ -436,8 +449,8 @@ __global__ __launch_bounds__(256) void assemble(const uint32_t* states, const ui
     if ((nw & 1) && lane == 0) wd[nw] = 0;
 }
 
-// CRC-32 (IEEE, reflected 0xEDB88320) of each 4 KiB chunk of the payload.
-constexpr int64_t kCrcChunk = 4096;
+// CRC-32 (IEEE, reflected 0xEDB88320) of each 512-byte chunk of the payload.
+constexpr int64_t kCrcChunk = 512;
 
 __global__ __launch_bounds__(256) void chunk_crc(const uint8_t* p, int64_t n, uint32_t* out) {
     __shared__ uint32_t tab[256];
@@ -481,9 +494,6 @@ uint32_t x_pow_8n(uint64_t nbytes) {                          // x^(8 n) mod P
     }
     return r;
 }
-uint32_t crc_concat(uint32_t crc_a, uint32_t crc_b, uint64_t len_b) {
-    return gf2_mulmod(x_pow_8n(len_b), crc_a) ^ crc_b;
-}
 
 struct DevBuf {
     void* p = nullptr;
@@ -523,15 +533,15 @@ ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_o
     std::vector<float> scale(R, 0.0f);
     unsigned long long umax_bits = 0;
     if (R > 0) {
-        hipLaunchKernelGGL(row_scales<DT>, dim3((unsigned)((R + 63) / 64)), dim3(64), 0, s, w, R, C, d_scale.as<float>(),
-                           d_flag.as<int>());
+        const size_t esize = DT == EP_F32 ? 4 : 2;
+        const bool vec = ((size_t)C * esize) % 16 == 0 && (reinterpret_cast<uintptr_t>(w) & 15) == 0;
+        if (vec)
+            hipLaunchKernelGGL((row_stats<DT, true>), dim3((unsigned)((R + 63) / 64)), dim3(64), 0, s, w, R, C,
+                               d_scale.as<float>(), d_flag.as<int>(), d_umax.as<unsigned long long>());
+        else
+            hipLaunchKernelGGL((row_stats<DT, false>), dim3((unsigned)((R + 63) / 64)), dim3(64), 0, s, w, R, C,
+                               d_scale.as<float>(), d_flag.as<int>(), d_umax.as<unsigned long long>());
         EP_HIP(hipGetLastError());
-        if (R * C > 0) {
-            const int64_t blocks = std::min<int64_t>((R * C + 255) / 256, 8192);
-            hipLaunchKernelGGL(row_umax<DT>, dim3((unsigned)blocks), dim3(256), 0, s, w, R, C, d_scale.as<float>(),
-                               d_umax.as<unsigned long long>());
-            EP_HIP(hipGetLastError());
-        }
         EP_HIP(hipMemcpyAsync(scale.data(), d_scale.p, sizeof(float) * R, hipMemcpyDeviceToHost, s));
     }
     int flag = 0;
@@ -650,7 +660,7 @@ ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_o
     // tiles
     const int64_t tiles_c = Cp / 256, n_tiles = (Rp / tr) * tiles_c;
     const int64_t cap = 64 * 9 * (int64_t)tr;                // words a tile can stack at most
-    DevBuf d_fc, d_lo, d_wd, d_stack, d_states, d_words, d_nesc, d_off, d_payload, d_crc;
+    DevBuf d_fc, d_lo, d_wd, d_stack, d_states, d_words, d_nesc;
     EP_HIP(d_fc.alloc(sizeof(uint32_t) * kTables * 256));
     EP_HIP(d_lo.alloc(sizeof(int32_t) * kTables));
     EP_HIP(d_wd.alloc(sizeof(int32_t) * kTables));
@@ -682,8 +692,8 @@ ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_o
         acc += 128 + 2 * (uint64_t)words[t] + 2 * (uint64_t)(words[t] & 1);
         offsets[t + 1] = (uint32_t)(acc / 4);
     }
-    std::vector<uint8_t> payload(acc);
     uint32_t crc = 0;
+    DevBuf d_off, d_payload, d_crc;
     if (n_tiles > 0) {
         EP_HIP(d_off.alloc(sizeof(uint64_t) * n_tiles));
         EP_HIP(d_payload.alloc(acc));
@@ -698,15 +708,21 @@ ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_o
                            (int64_t)acc, d_crc.as<uint32_t>());
         EP_HIP(hipGetLastError());
         std::vector<uint32_t> crcs(n_chunks);
-        EP_HIP(hipMemcpyAsync(payload.data(), d_payload.p, acc, hipMemcpyDeviceToHost, s));
         EP_HIP(hipMemcpyAsync(crcs.data(), d_crc.p, sizeof(uint32_t) * n_chunks, hipMemcpyDeviceToHost, s));
         EP_HIP(hipStreamSynchronize(s));
+        const uint32_t op_full = x_pow_8n(kCrcChunk);             // every chunk but the last is full
         crc = crcs[0];
-        for (int64_t i = 1; i < n_chunks; ++i)
-            crc = crc_concat(crc, crcs[i], std::min<uint64_t>(kCrcChunk, acc - (uint64_t)i * kCrcChunk));
+        for (int64_t i = 1; i < n_chunks; ++i) {
+            const uint64_t len = std::min<uint64_t>(kCrcChunk, acc - (uint64_t)i * kCrcChunk);
+            crc = gf2_mulmod(len == (uint64_t)kCrcChunk ? op_full : x_pow_8n(len), crc) ^ crcs[i];
+        }
     }
-    serialize_lossy(DT, R, C, tr, n, tables, step, (float)o.target_bpp, scale, qmax, std::move(payload),
-                    std::move(offsets), n_esc, out, n_tiles > 0 ? &crc : nullptr);
+    const uint64_t o_pay = serialize_lossy(DT, R, C, tr, n, tables, step, (float)o.target_bpp, scale, qmax, acc,
+                                           std::move(offsets), n_esc, n_tiles > 0 ? crc : 0u, out);
+    if (n_tiles > 0) {
+        EP_HIP(hipMemcpyAsync(out->data() + o_pay, d_payload.p, acc, hipMemcpyDeviceToHost, s));
+        EP_HIP(hipStreamSynchronize(s));
+    }
     return EP_OK;
 }
 

@@ -80,10 +80,12 @@ constexpr int32_t kValueSpan = 1 << 15;
 bool normalize_frequencies(const uint64_t cnt[256], int n, uint32_t f[256]);
 double sample_estimate(const uint64_t (*cnt)[256], const uint64_t* totals, int64_t sb);
 float choose_step(double U, double target, const std::function<double(double)>& est);
-void serialize_lossy(int dt, int64_t R, int64_t C, int tile_rows, int n, const std::vector<Table>& tables, float step,
-                     float target, const std::vector<float>& scale, const std::vector<uint16_t>& qmax,
-                     std::vector<uint8_t>&& payload, std::vector<uint32_t>&& offsets, uint32_t n_esc,
-                     std::vector<uint8_t>* out, const uint32_t* payload_crc = nullptr);
+// Header, row metadata, tables and tile index of a lossy stream whose payload (payload_len bytes,
+// CRC-32 payload_crc) the caller writes itself at the returned offset of *out.
+uint64_t serialize_lossy(int dt, int64_t R, int64_t C, int tile_rows, int n, const std::vector<Table>& tables,
+                         float step, float target, const std::vector<float>& scale, const std::vector<uint16_t>& qmax,
+                         uint64_t payload_len, std::vector<uint32_t>&& offsets, uint32_t n_esc, uint32_t payload_crc,
+                         std::vector<uint8_t>* out);
 
 // Device encoder (lossy mode): the same stream as encode() from a weight in device memory.
 ep_status encode_lossy_device(const void* dev_w, int dt, int64_t rows, int64_t cols, const ep_encode_opts& o,

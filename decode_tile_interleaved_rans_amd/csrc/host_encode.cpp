@@ -283,9 +283,11 @@ inline uint32_t f32bits(float f) {
 struct TileSet {
     std::vector<uint8_t> payload;
     std::vector<uint32_t> offsets;   // [n_tiles + 1], 4-byte units
+    uint64_t external_len = 0;       // payload bytes the caller writes itself (payload empty)
 };
 
-void serialize(int mode, int dt, int64_t R, int64_t C, int tile_rows, int n, const std::vector<Table>& tables,
+// Returns the payload's offset in the stream.
+uint64_t serialize(int mode, int dt, int64_t R, int64_t C, int tile_rows, int n, const std::vector<Table>& tables,
                float step, float target, const std::vector<float>& scale, const std::vector<uint16_t>& qmax,
                const TileSet& ts, uint32_t n_esc, std::vector<uint8_t>* out,
                const std::vector<uint8_t>* raw = nullptr, const uint32_t* payload_crc = nullptr) {
@@ -299,7 +301,7 @@ void serialize(int mode, int dt, int64_t R, int64_t C, int tile_rows, int n, con
     const uint64_t o_idx = up16(o_tab + tables_len);
     const uint64_t o_raw = raw ? up16(o_idx + 4 * ((uint64_t)n_tiles + 1)) : 0;
     const uint64_t o_pay = raw ? up16(o_raw + raw->size()) : up16(o_idx + 4 * ((uint64_t)n_tiles + 1));
-    const uint64_t total = o_pay + ts.payload.size();
+    const uint64_t total = o_pay + (ts.payload.empty() ? ts.external_len : ts.payload.size());
     out->assign(total, 0);
     uint8_t* s = out->data();
     std::memcpy(s + kMagic, "EPK1", 4);
@@ -343,6 +345,7 @@ void serialize(int mode, int dt, int64_t R, int64_t C, int tile_rows, int n, con
     }
     for (uint32_t i = 0; i <= n_tiles; ++i) w32(s + o_idx + 4 * (uint64_t)i, ts.offsets[i]);
     if (!ts.payload.empty()) std::memcpy(s + o_pay, ts.payload.data(), ts.payload.size());
+    return o_pay;
 }
 
 // Encode all tiles: fill(tile, tab, sym, esc) lays out one tile's symbols.
@@ -707,15 +710,15 @@ float choose_step(double U, double target, const std::function<double(double)>& 
     return search_step(U, target, est);
 }
 
-void serialize_lossy(int dt, int64_t R, int64_t C, int tile_rows, int n, const std::vector<Table>& tables, float step,
-                     float target, const std::vector<float>& scale, const std::vector<uint16_t>& qmax,
-                     std::vector<uint8_t>&& payload, std::vector<uint32_t>&& offsets, uint32_t n_esc,
-                     std::vector<uint8_t>* out, const uint32_t* payload_crc) {
+uint64_t serialize_lossy(int dt, int64_t R, int64_t C, int tile_rows, int n, const std::vector<Table>& tables,
+                         float step, float target, const std::vector<float>& scale, const std::vector<uint16_t>& qmax,
+                         uint64_t payload_len, std::vector<uint32_t>&& offsets, uint32_t n_esc, uint32_t payload_crc,
+                         std::vector<uint8_t>* out) {
     TileSet ts;
-    ts.payload = std::move(payload);
     ts.offsets = std::move(offsets);
-    serialize(EP_MODE_LOSSY_E8, dt, R, C, tile_rows, n, tables, step, target, scale, qmax, ts, n_esc, out, nullptr,
-              payload_crc);
+    ts.external_len = payload_len;
+    return serialize(EP_MODE_LOSSY_E8, dt, R, C, tile_rows, n, tables, step, target, scale, qmax, ts, n_esc, out,
+                     nullptr, &payload_crc);
 }
 
 ep_status encode(const void* w, int dt, int64_t R, int64_t C, const ep_encode_opts& o, std::vector<uint8_t>* out,
