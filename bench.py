@@ -253,6 +253,8 @@ def main():
     ap.add_argument("--gemm-only", action="store_true",
                     help="profiling aid: run only the fused decode + GEMM measurement and print its JSON")
     ap.add_argument("--gemm-reps", type=int, default=15, help="timed reps per variant in the GEMM measurement")
+    ap.add_argument("--step-only", action="store_true",
+                    help="profiling aid: time only the decode step (no lossless, encoder, GEMM or CPU sections)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the decode path has no cross-GPU step (tiles, rows and "
@@ -338,13 +340,14 @@ def main():
                 for i in range(len(items))}
     sets.clear()
     torch.cuda.empty_cache()
-    lossless = lossless_section(torch, ep)
-    encoders = encoder_section(torch, ep)
-    fused = None
-    if not args.no_gemm:
+    lossless = encoders = fused = None
+    if not args.step_only:
+        lossless = lossless_section(torch, ep)
+        encoders = encoder_section(torch, ep)
+    if not args.no_gemm and not args.step_only:
         fused = fused_gemm_section(torch, ep, reps=args.gemm_reps)
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and not args.step_only:
         log("timing the oracle on the host cores")
         cpu = cpu_baseline(items)
     line = {
