@@ -241,6 +241,46 @@ def encoder_section(torch, ep, reps: int = 3):
             "host_gweights_per_s": round(w.size / h / 1e9, 3), "identical_streams": True}
 
 
+def dit_model_section(torch, ep, steps: int = 10):
+    """Full-model decode of the DiT-like denoiser (30 blocks x [11520, 3840], [3840, 3840],
+    [10240, 3840] x 2, [3840, 10240], 5.31 G weights, seeded 0.02 t5 BF16 at 4.0 bpp) to BF16 per
+    simulated step, as grouped launches of 30 matrices. The 30 blocks hold distinct device copies
+    of block 0's five streams: the same bytes moved and the same work as 150 distinct streams,
+    without 145 more host encodes. Only with --dit-model (it needs about 14 GB of device memory and
+    a minute of host encoding)."""
+    from decode_tile_interleaved_rans_amd import workloads as W
+    streams = [ep.compress(W.dit_matrix(0, m), 4.0, dtype=ep.BF16)[0] for m in range(5)]
+    hs, outs = [], []
+    for _ in range(30):
+        for m in range(5):
+            hs.append(ep.upload(streams[m]))
+            outs.append(torch.empty(W.DIT_BLOCK_SHAPES[m], dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+    in_b = 30 * sum(len(x) for x in streams)
+    out_b = sum(o.numel() * 2 for o in outs)
+    for _ in range(2):
+        ep.decompress_many(hs, outs)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        ep.decompress_many(hs, outs)
+    b.record()
+    torch.cuda.synchronize()
+    for h in hs:
+        h.check()
+    if not torch.equal(outs[17 * 5 + 2], outs[2]):
+        raise RuntimeError("copies of one stream decoded differently")
+    ms = a.elapsed_time(b) / steps
+    weights = sum(o.numel() for o in outs)
+    log(f"DiT-like model step: {ms:.3f} ms")
+    return {"workload": "DiT-like 30 blocks x 5 linear weights, 5.31 G weights, 0.02 t5 bf16 at 4.0 bpp -> BF16",
+            "ms_per_step": round(ms, 4), "gb_in": round(in_b / 1e9, 3), "gb_out": round(out_b / 1e9, 3),
+            "output_gbs": round(out_b / ms / 1e6, 1), "algorithmic_gbs": round((in_b + out_b) / ms / 1e6, 1),
+            "hbm_frac": round((in_b + out_b) / ms / 1e6 / HBM_PEAK_GBS, 4),
+            "tweights_per_s": round(weights / ms / 1e9, 4), "steps": steps}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -253,6 +293,8 @@ def main():
     ap.add_argument("--gemm-only", action="store_true",
                     help="profiling aid: run only the fused decode + GEMM measurement and print its JSON")
     ap.add_argument("--gemm-reps", type=int, default=15, help="timed reps per variant in the GEMM measurement")
+    ap.add_argument("--dit-model", action="store_true",
+                    help="also time the full-model decode step of the DiT-like denoiser (5.31 G weights)")
     ap.add_argument("--step-only", action="store_true",
                     help="profiling aid: time only the decode step (no lossless, encoder, GEMM or CPU sections)")
     args = ap.parse_args()
@@ -346,6 +388,7 @@ def main():
         encoders = encoder_section(torch, ep)
     if not args.no_gemm and not args.step_only:
         fused = fused_gemm_section(torch, ep, reps=args.gemm_reps)
+    dit = dit_model_section(torch, ep) if args.dit_model else None
     cpu = None
     if not args.no_cpu and not args.step_only:
         log("timing the oracle on the host cores")
@@ -365,6 +408,7 @@ def main():
         "per_decode": per_item,
         "lossless_bf16_codings": lossless,
         "encoders": encoders,
+        "dit_model": dit,
         "fused_gemm": fused,
         "cpu_baseline": cpu,
     }

@@ -241,3 +241,30 @@ def test_load_rejects_a_damaged_file(tmp_path):
     with pytest.raises(ep.EPError) as e:
         ep.load(path)
     assert e.value.status == -2
+
+
+def test_new_entry_points_reject_bad_arguments_before_any_device_work():
+    """Argument checks of the FP8 forward, the quantizer, the FP8 GEMM and the device encoder
+    return EP_EINVAL / EP_EUNSUPPORTED / EP_ERANGE without touching a device."""
+    import ctypes as C
+    L = ep.lib()
+    out = C.POINTER(C.c_uint8)()
+    n = C.c_size_t()
+    assert L.ep_linear_forward_fp8(None, None, 4, None, None, None) == -1           # null handle
+    assert L.ep_quantize_rows_fp8(None, 4, 32, None, None, None) == -1              # null pointers
+    assert L.ep_quantize_rows_fp8(C.c_void_p(16), 4, 24, C.c_void_p(16), C.c_void_p(16), None) == -1   # K % 16
+    assert L.ep_gemm_fp8(C.c_void_p(16), C.c_void_p(16), C.c_void_p(16), C.c_void_p(16), 4, 4, 24, None,
+                         C.c_void_p(16), None) == -1                                  # K % 16
+    assert L.ep_gemm_fp8(None, None, None, None, 0, 4, 16, None, None, None) == 0    # empty: nothing to do
+    assert L.ep_compress_device(None, ep.F32, 4, 4, None, None, C.byref(out), C.byref(n), None) == -1
+    opts = ep.EncodeOpts(ep.LOSSLESS, 0.0, 12, 16, 0)
+    assert L.ep_compress_device(C.c_void_p(16), ep.BF16, 4, 4, C.byref(opts), None, C.byref(out), C.byref(n),
+                                None) == -3                                           # lossless: host encoder only
+    opts = ep.EncodeOpts(ep.LOSSY, 4.0, 12, 16, 0)
+    assert L.ep_compress_device(C.c_void_p(16), ep.U8, 4, 4, C.byref(opts), None, C.byref(out), C.byref(n),
+                                None) == -3                                           # lossy takes float input
+    assert L.ep_compress_device(C.c_void_p(16), ep.F32, 4, 1 << 28, C.byref(opts), None, C.byref(out), C.byref(n),
+                                None) == -4                                           # too wide
+    opts = ep.EncodeOpts(ep.LOSSY, 0.0, 12, 16, 0)
+    assert L.ep_compress_device(C.c_void_p(16), ep.F32, 4, 4, C.byref(opts), None, C.byref(out), C.byref(n),
+                                None) == -1                                           # target must be > 0
