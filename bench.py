@@ -12,7 +12,7 @@ Prints one JSON line (rank 0, N = 1): decoded-weight GB/s (container bytes writt
 the roofline of the step's one grouped decode launch from HIP events on the launch stream,
 the two lossless BF16 codings side by side (byte planes, and the exponent-coded variant), the
 fused decode + GEMM forward of an 8192 x 8192 weight at 4.5 bpp against the plain BF16 GEMM
-(M = 4096, 256, 16), the same forward with FP8 compute against the plain FP8 GEMM, and the
+(M = 4096, 256, 16, 1), the same forward with FP8 compute against the plain FP8 GEMM, and the
 oracle's CPU decode of one step on the host cores as a reported baseline.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-gemm]
@@ -98,7 +98,8 @@ def fused_gemm_section(torch, ep, reps: int = 15):
     """Fused decode + BF16 MFMA GEMM against the plain BF16 GEMM on the uncompressed weight.
 
     Workload: W = 0.02 t5 bf16 [8192, 8192] coded at 4.5 bpp, X ~ N(0, 1) bf16 [M, 8192],
-    Y = X W^T in BF16 with fp32 accumulation, M = 4096 (prefill), 256 and 16. Each rep is timed
+    Y = X W^T in BF16 with fp32 accumulation, M = 4096 (prefill), 256, 16 and 1 (M <= 4 runs the
+    fused decode + matrix-vector kernel). Each rep is timed
     with HIP events on the launch stream and a 1 GiB buffer is rewritten between reps, so neither
     the weight nor the activations are served from the Infinity Cache."""
     from decode_tile_interleaved_rans_amd import workloads as W
@@ -145,7 +146,7 @@ def fused_gemm_section(torch, ep, reps: int = 15):
            "reps": reps, "timing": "median of per-rep HIP events, the five variants interleaved within each "
                                    "rep, 1 GiB cache flush before every timed call"}
     wq, ws = ep.quantize_rows_fp8(Wt)                  # plain FP8 baseline: the weight pre-quantized
-    for M in (4096, 256, 16):
+    for M in (4096, 256, 16, 1):
         X = Xf[:M].contiguous()
         xq, xs = ep.quantize_rows_fp8(X)
         (t_f, t_f_min), (t_o, _), (t_t, _), (t_f8, _), (t_o8, _) = timed(

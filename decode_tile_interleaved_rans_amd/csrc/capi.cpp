@@ -351,12 +351,30 @@ ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, co
     if (!dev_x || !dev_y) return fail(EP_EINVAL, "null pointer");
     if (K % 8 || M > INT32_MAX) return fail(EP_EINVAL, "in_features must be a multiple of 8");
     if (reinterpret_cast<uintptr_t>(dev_x) & 15) return fail(EP_EINVAL, "X must be 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if (M <= 4) {
+        // a few activation rows: decoding fused with the matrix-vector products, the weight never
+        // written out; fp32 accumulation in the workspace, then rounding (+ bias) to BF16
+        uint16_t* acc = nullptr;
+        int dev = 0;
+        hipError_t we = hipGetDevice(&dev);
+        if (we == hipSuccess) we = workspace(dev, s, sizeof(float) * (size_t)M * (size_t)N, &acc);
+        if (we != hipSuccess) return hip_fail(we, "hipMalloc for the linear forward workspace");
+        float* yacc = reinterpret_cast<float*>(acc);
+        ep::MatDesc d = desc_for(w, M == 1 ? ep::CT_GEMV1 : M == 2 ? ep::CT_GEMV2 : ep::CT_GEMV4, yacc, nullptr);
+        d.gemv_x = static_cast<const uint16_t*>(dev_x);
+        d.gemv_m = (uint8_t)M;
+        hipError_t e = ep::launch_gemv_zero(yacc, M * N, s);
+        if (e == hipSuccess) e = ep::launch_gemv(d, s);
+        if (e == hipSuccess)
+            e = ep::launch_gemv_finish(yacc, static_cast<const uint16_t*>(dev_bias), static_cast<uint16_t*>(dev_y), M, N, s);
+        return e == hipSuccess ? EP_OK : hip_fail(e, "fused matrix-vector launch");
+    }
     const int tr = w->view.tile_rows;
     int64_t slice = (int64_t)(kSliceBytes / (2 * (size_t)K)) / tr * tr;
     if (slice < tr) slice = tr;
     if (slice > N) slice = (N + tr - 1) / tr * tr;
     const size_t need = (size_t)slice * (size_t)K * 2;
-    hipStream_t s = static_cast<hipStream_t>(hip_stream);
     uint16_t* scratch = nullptr;
     int dev = 0;
     hipError_t we = hipGetDevice(&dev);

@@ -386,7 +386,28 @@ struct PairRows {
     uint32_t tc, row0;
     float sc_l;
     uint32_t qm_l;
+    float xv[4][8];        // fused matrix-vector product: the lane's 8 activation columns per row m
 };
+
+constexpr int gemv_rows(int CT) { return CT >= CT_GEMV1 ? CT - 100 : 0; }
+
+// Sum over the 64 lanes of a wave with DPP moves (no LDS traffic): quad swaps, half-row and row
+// mirrors give every lane its 16-lane row's sum; row broadcasts 15 and 31 then carry rows 0-2
+// into row 3, so lane 63 holds the total.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false);
+    return v + __builtin_bit_cast(float, t);
+}
+__device__ __forceinline__ float wave_sum_to_lane63(float v) {
+    v = dpp_add<0xB1, 0xF>(v);      // quad_perm [1, 0, 3, 2]
+    v = dpp_add<0x4E, 0xF>(v);      // quad_perm [2, 3, 0, 1]
+    v = dpp_add<0x141, 0xF>(v);     // row_half_mirror
+    v = dpp_add<0x140, 0xF>(v);     // row_mirror
+    v = dpp_add<0x142, 0xA>(v);     // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xC>(v);     // row_bcast:31 into rows 2 and 3
+    return v;
+}
 
 template <int CT>
 __device__ __forceinline__ void begin_pair(const MatDesc& M, __amdgpu_buffer_rsrc_t rs, uint64_t pair, bool live,
@@ -401,6 +422,23 @@ __device__ __forceinline__ void begin_pair(const MatDesc& M, __amdgpu_buffer_rsr
     P.sc_l = mine ? M.row_scale[my_row] : 0.0f;
     P.qm_l = 0;
     if constexpr (CT == CT_I8) P.qm_l = mine ? M.row_qmax[my_row] : 0u;
+    if constexpr (gemv_rows(CT) > 0) {
+        // the lane's 8 columns of each activation row; zeros past the matrix or the tile pair
+        const uint32_t col0 = P.tc * 256 + 8 * t.l;
+#pragma unroll
+        for (int m = 0; m < gemv_rows(CT); ++m) {
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (t.valid && col0 < M.cols && m < M.gemv_m)
+                v = *reinterpret_cast<const uint4*>(M.gemv_x + (size_t)m * M.cols + col0);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                P.xv[m][2 * i] = __uint_as_float(w[i] << 16);
+                P.xv[m][2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+                asm volatile("" ::"v"(P.xv[m][2 * i]), "v"(P.xv[m][2 * i + 1]));
+            }
+        }
+    }
     // Wait for these loads here, once per pair: first used inside the row loop, their wait would
     // land inside it, on every row, and (the vector-memory counter being in order) would also
     // wait for the ring chunk just prefetched.
@@ -410,20 +448,43 @@ __device__ __forceinline__ void begin_pair(const MatDesc& M, __amdgpu_buffer_rsr
 template <int CT>
 __device__ __forceinline__ void store_row(const MatDesc& M, const Tile& t, const PairRows& P, int rr, const float* q,
                                           float h) {
-    const uint32_t row = P.row0 + rr;
-    const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, P.sc_l), rr));
-    if (row >= M.rows) return;
-    const float alpha = h * sc;
-    uint32_t k = 1, magic = 0;
-    if constexpr (CT == CT_I8) {
-        const uint32_t qm = (uint32_t)__builtin_amdgcn_readlane((int)P.qm_l, rr);
-        k = qm > 127u ? (qm + 126u) / 127u : 1u;
-        magic = 0xFFFFFFFFu / (2u * k) + 1u;
-    }
-    const uint32_t col0 = t.valid ? P.tc * 256 + 8 * t.l : 0xFFFFFFF0u;     // no tile: out of range
-    store_block<CT>(M, row, col0, q, alpha, h, k, magic);
-    if constexpr (CT == CT_F8E4M3 || CT == CT_I8) {
-        if (P.tc == 0 && t.l == 0) M.scale_out[row] = CT == CT_F8E4M3 ? sc : alpha * (float)k;
+    if constexpr (gemv_rows(CT) > 0) {
+        // fused matrix-vector product: the row's dot products with every activation row, summed
+        // over the wave (both tiles of the pair cover the same rows) and added to Y by lane 63
+        constexpr int MT = gemv_rows(CT);
+        const uint32_t row = P.row0 + rr;
+        const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, P.sc_l), rr));
+        if (row >= M.rows) return;
+        const float alpha = h * sc;
+        float s[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc += P.xv[m][i] * q[i];
+            s[m] = wave_sum_to_lane63(acc * alpha);
+        }
+        if ((threadIdx.x & 63) == 63) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                if (m < M.gemv_m) atomicAdd(static_cast<float*>(M.out) + (size_t)m * M.rows + row, s[m]);
+        }
+    } else {
+        const uint32_t row = P.row0 + rr;
+        const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, P.sc_l), rr));
+        if (row >= M.rows) return;
+        const float alpha = h * sc;
+        uint32_t k = 1, magic = 0;
+        if constexpr (CT == CT_I8) {
+            const uint32_t qm = (uint32_t)__builtin_amdgcn_readlane((int)P.qm_l, rr);
+            k = qm > 127u ? (qm + 126u) / 127u : 1u;
+            magic = 0xFFFFFFFFu / (2u * k) + 1u;
+        }
+        const uint32_t col0 = t.valid ? P.tc * 256 + 8 * t.l : 0xFFFFFFF0u;     // no tile: out of range
+        store_block<CT>(M, row, col0, q, alpha, h, k, magic);
+        if constexpr (CT == CT_F8E4M3 || CT == CT_I8) {
+            if (P.tc == 0 && t.l == 0) M.scale_out[row] = CT == CT_F8E4M3 ? sc : alpha * (float)k;
+        }
     }
 }
 
@@ -681,7 +742,10 @@ __device__ __forceinline__ void split_pairs(const MatDesc& M, const Tables& T, T
 // (pair_cost), matrix i spans cost units [cost_start[i], cost_start[i + 1]), and block k owns
 // the pairs whose first unit falls in [k C, (k + 1) C). A block walks its range one matrix
 // segment at a time and restages the decode tables when it crosses into the next matrix.
-__global__ __launch_bounds__(64 * kWaves) void decode_group(GroupArgs g) {
+// GEMV = 0: the general grouped decode; GEMV = CT_GEMV1/2/4: the fused matrix-vector product of
+// lossy matrices (a kernel of its own, so that its registers do not weigh on the decode kernel).
+template <int GEMV>
+__device__ __forceinline__ void group_body(const GroupArgs& g) {
     extern __shared__ __align__(16) uint8_t smem[];
     // the lookups address the LUTs absolutely: the dynamic LDS must start at address 0
     if ((uint32_t)(size_t)(lds_u8*)smem != 0u) {
@@ -705,7 +769,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_group(GroupArgs g) {
         Tile t[kChains];
 #pragma unroll
         for (int c = 0; c < kChains; ++c) init_lane(t[c], smem + lds_table_bytes(M.n_tables, M.prob_bits, lossy), c);
-        if (lossy) {
+        if constexpr (GEMV > 0) {
+            switch (M.prob_bits) {
+                case 10: lossy_pairs<GEMV, 10>(M, T, t, p0, p1); break;
+                case 11: lossy_pairs<GEMV, 11>(M, T, t, p0, p1); break;
+                default: lossy_pairs<GEMV, 12>(M, T, t, p0, p1); break;
+            }
+        } else if (lossy) {
             switch (M.prob_bits) {
                 case 10: lossy_dispatch<10>(M, T, t, p0, p1); break;
                 case 11: lossy_dispatch<11>(M, T, t, p0, p1); break;
@@ -724,6 +794,25 @@ __global__ __launch_bounds__(64 * kWaves) void decode_group(GroupArgs g) {
         for (int c = 0; c < kChains; ++c)
             if (t[c].err) atomicOr(M.err, t[c].err);
     }
+}
+
+__global__ __launch_bounds__(64 * kWaves) void decode_group(GroupArgs g) { group_body<0>(g); }
+
+template <int CT>
+__global__ __launch_bounds__(64 * kWaves) void decode_gemv(GroupArgs g) { group_body<CT>(g); }
+
+__global__ __launch_bounds__(256) void gemv_zero(float* y, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) y[i] = 0.0f;
+}
+
+__global__ __launch_bounds__(256) void gemv_finish(const float* yacc, const uint16_t* bias, uint16_t* y, int64_t M,
+                                                   int64_t N) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= M * N) return;
+    float v = yacc[i];
+    if (bias) v += __uint_as_float((uint32_t)bias[i % N] << 16);
+    y[i] = (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v, 0.0f}, bf16x2)) & 0xFFFFu);
 }
 
 int device_cus() {
@@ -776,6 +865,49 @@ hipError_t launch_group(const MatDesc* mats, int count, hipStream_t stream) {
     hipError_t e = allow_lds(k);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_group, dim3((unsigned)used), dim3(64 * kWaves), lds, stream, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv(const MatDesc& m, hipStream_t stream) {
+    if (m.mode != 0 || m.gemv_m == 0 || m.gemv_m > gemv_rows(m.container)) return hipErrorInvalidValue;
+    GroupArgs g{};
+    g.count = 1;
+    g.m[0] = m;
+    const uint64_t pairs = (uint64_t)((m.rows + m.tile_rows - 1) / m.tile_rows) * m.pairs_c;
+    const uint64_t total = pairs * m.pair_cost;
+    g.cost_start[0] = 0;
+    g.cost_start[1] = total;
+    if (total == 0) return hipSuccess;
+    const uint64_t blocks = (uint64_t)device_cus();
+    g.block_cost = (total + blocks - 1) / blocks;
+    const uint64_t used = (total + g.block_cost - 1) / g.block_cost;
+    const size_t lds = lds_table_bytes(m.n_tables, m.prob_bits, true) + (size_t)kWaves * kChains * 2 * kRingBytes;
+    const void* k;
+    switch (m.container) {
+        case CT_GEMV1: k = reinterpret_cast<const void*>(decode_gemv<CT_GEMV1>); break;
+        case CT_GEMV2: k = reinterpret_cast<const void*>(decode_gemv<CT_GEMV2>); break;
+        default: k = reinterpret_cast<const void*>(decode_gemv<CT_GEMV4>); break;
+    }
+    hipError_t e = allow_lds(k);
+    if (e != hipSuccess) return e;
+    switch (m.container) {
+        case CT_GEMV1: hipLaunchKernelGGL(decode_gemv<CT_GEMV1>, dim3((unsigned)used), dim3(64 * kWaves), lds, stream, g); break;
+        case CT_GEMV2: hipLaunchKernelGGL(decode_gemv<CT_GEMV2>, dim3((unsigned)used), dim3(64 * kWaves), lds, stream, g); break;
+        default: hipLaunchKernelGGL(decode_gemv<CT_GEMV4>, dim3((unsigned)used), dim3(64 * kWaves), lds, stream, g); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_zero(float* yacc, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(gemv_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, yacc, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_finish(const float* yacc, const uint16_t* bias, uint16_t* y, int64_t M, int64_t N,
+                              hipStream_t stream) {
+    if (M * N <= 0) return hipSuccess;
+    hipLaunchKernelGGL(gemv_finish, dim3((unsigned)((M * N + 255) / 256)), dim3(256), 0, stream, yacc, bias, y, M, N);
     return hipGetLastError();
 }
 

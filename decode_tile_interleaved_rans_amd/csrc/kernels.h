@@ -8,7 +8,11 @@
 namespace ep {
 
 // container codes (the first four equal the ep_dtype values)
-enum Container : int { CT_BF16 = 1, CT_F16 = 2, CT_F8E4M3 = 3, CT_I8 = 4, CT_Q16 = 100 };
+enum Container : int {
+    CT_BF16 = 1, CT_F16 = 2, CT_F8E4M3 = 3, CT_I8 = 4, CT_Q16 = 100,
+    // fused matrix-vector products Y[m] += W x[m] for m < 1, 2 or 4 activation rows (see launch_gemv)
+    CT_GEMV1 = 101, CT_GEMV2 = 102, CT_GEMV4 = 104
+};
 
 constexpr int kMaxGroup = 32;        // matrices per grouped launch (kernel-argument space)
 
@@ -21,13 +25,17 @@ struct MatDesc {
     const uint8_t* raw;         // [Rp][Cp] sign/mantissa bytes (exponent-coded lossless BF16)
     const uint8_t* tables;      // decode tables (see table_blob_bytes)
     void* out;                  // [rows][cols] container elements
-    float* scale_out;           // [rows] for FP8 / INT8, else unused
+    union {
+        float* scale_out;       // [rows] for FP8 / INT8, else unused
+        const uint16_t* gemv_x; // fused matrix-vector product: X [gemv_m][cols] bf16 (out: fp32 Y [gemv_m][rows])
+    };
     int* err;                   // device error flag (bit 0: word count, bit 1: final state)
     uint32_t rows, cols, tiles_c, pairs_c;
     uint32_t payload_bytes;     // size of the tile payload (buffer-load bounds)
     float step;
     uint8_t prob_bits, tile_rows, container, n_tables;
     uint8_t mode;               // 0 lossy E8 coordinates, 1 lossless byte planes, 2 exponent-coded BF16
+    uint8_t gemv_m;             // activation rows of a fused matrix-vector product
     uint32_t pair_cost;         // relative decode time of one tile pair (load balancing)
 };
 
@@ -67,5 +75,21 @@ __host__ __device__ inline size_t lds_table_bytes(int n_tables, int prob_bits, b
 
 // Launch one grouped decode of up to kMaxGroup matrices (lossy and lossless may be mixed).
 hipError_t launch_group(const MatDesc* mats, int count, hipStream_t stream);
+
+// Fused decode and matrix-vector product of one lossy matrix W [rows][cols] with gemv_m <= 4 BF16
+// activation rows: every wave multiplies the weights it has just decoded (fp32 q alpha_r, never
+// stored) by the activations and adds each row's dot products into the fp32 output m.out
+// [gemv_m][rows], which must hold zeros (or a partial sum) on entry. m.container must be
+// CT_GEMV1, CT_GEMV2 or CT_GEMV4 (at least gemv_m) and cols a multiple of 8.
+hipError_t launch_gemv(const MatDesc& m, hipStream_t stream);
+
+// Zero n floats with a kernel (no memset node, so that the call can be captured in a graph).
+hipError_t launch_gemv_zero(float* yacc, int64_t n, hipStream_t stream);
+
+// Y [M][N] bf16 = Yacc [M][N] fp32 rounded to nearest even (+ bias [N] bf16).
+hipError_t launch_gemv_finish(const float* yacc, const uint16_t* bias, uint16_t* y, int64_t M, int64_t N,
+                              hipStream_t stream);
+
+static_assert(sizeof(GroupArgs) <= 4096, "kernel argument space");
 
 }  // namespace ep

@@ -79,6 +79,18 @@ def test_linear_forward_matches_decoded_fp32_gemm(M, N, K, target):
     assert rel_l2(y, x @ w_hat.T) < 2e-2
 
 
+@pytest.mark.parametrize("M,N,K,target,bias", [(1, 4096, 4096, 4.5, False), (2, 300, 264, 3.0, True),
+                                                (3, 1000, 776, 6.0, True), (4, 17, 4104, 4.0, False),
+                                                (1, 11520, 3840, 4.0, True)])
+def test_fused_matrix_vector_few_rows(M, N, K, target, bias):
+    """M <= 4 runs the fused decode + matrix-vector kernel (weights never stored): against the
+    oracle-decoded BF16 weight in fp32; the kernel multiplies the unrounded fp32 weights, which
+    differ from the BF16 container by at most half a BF16 step."""
+    y, x, w_hat, b = linear_case(M, N, K, target, seed=M * 7 + N, bias=bias)
+    ref = x @ w_hat.T + (b[None, :] if bias else 0.0)
+    assert rel_l2(y, ref) < 2e-2
+
+
 def test_linear_forward_with_bias_and_multi_slice():
     # 5000 x 16384 weight: 128 MiB slices of 4096 rows -> two slices, the last one ragged
     M, N, K = 64, 5000, 16384
