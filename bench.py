@@ -294,6 +294,8 @@ def main():
     ap.add_argument("--gemm-only", action="store_true",
                     help="profiling aid: run only the fused decode + GEMM measurement and print its JSON")
     ap.add_argument("--gemm-reps", type=int, default=15, help="timed reps per variant in the GEMM measurement")
+    ap.add_argument("--encoder-only", action="store_true",
+                    help="profiling aid: run only the encoder comparison and print its JSON")
     ap.add_argument("--dit-model", action="store_true",
                     help="also time the full-model decode step of the DiT-like denoiser (5.31 G weights)")
     ap.add_argument("--step-only", action="store_true",
@@ -316,6 +318,9 @@ def main():
         del src, dst
     if args.gemm_only:
         print(json.dumps(fused_gemm_section(torch, ep, reps=args.gemm_reps)), flush=True)
+        return
+    if args.encoder_only:
+        print(json.dumps(encoder_section(torch, ep)), flush=True)
         return
     items, (R, C) = c2_items()
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16}

@@ -191,7 +191,7 @@ ep_status ep_compress(const void* host_w, ep_dtype src, int64_t rows, int64_t co
     } else {
         return fail(EP_EINVAL, "unknown mode");
     }
-    std::vector<uint8_t> buf;
+    ep::Bytes buf;
     std::string why;
     ep_status st;
     try {
@@ -200,12 +200,10 @@ ep_status ep_compress(const void* host_w, ep_dtype src, int64_t rows, int64_t co
         return fail(EP_ENOMEM, "host allocation failed while encoding");
     }
     if (st != EP_OK) return fail(st, why);
-    uint8_t* p = static_cast<uint8_t*>(std::malloc(buf.size() ? buf.size() : 1));
-    if (!p) return fail(EP_ENOMEM, "host allocation failed");
-    std::memcpy(p, buf.data(), buf.size());
-    *out_stream = p;
-    *out_len = buf.size();
-    if (actual_bpp) *actual_bpp = rows * cols > 0 ? 8.0 * (double)buf.size() / ((double)rows * (double)cols) : 0.0;
+    const size_t len = buf.size();
+    *out_stream = buf.release();
+    *out_len = len;
+    if (actual_bpp) *actual_bpp = rows * cols > 0 ? 8.0 * (double)len / ((double)rows * (double)cols) : 0.0;
     return EP_OK;
 }
 
@@ -412,7 +410,7 @@ ep_status ep_compress_device(const void* dev_w, ep_dtype src, int64_t rows, int6
     if (src != EP_F32 && src != EP_BF16 && src != EP_F16)
         return fail(EP_EUNSUPPORTED, "lossy mode takes F32, BF16 or F16 input");
     if (!(o.target_bpp > 0.0 && o.target_bpp <= 32.0)) return fail(EP_EINVAL, "target_bpp must be in (0, 32]");
-    std::vector<uint8_t> buf;
+    ep::Bytes buf;
     std::string why;
     ep_status st;
     try {
@@ -421,12 +419,10 @@ ep_status ep_compress_device(const void* dev_w, ep_dtype src, int64_t rows, int6
         return fail(EP_ENOMEM, "host allocation failed while encoding");
     }
     if (st != EP_OK) return fail(st, why);
-    uint8_t* p = static_cast<uint8_t*>(std::malloc(buf.size() ? buf.size() : 1));
-    if (!p) return fail(EP_ENOMEM, "host allocation failed for the stream");
-    if (!buf.empty()) std::memcpy(p, buf.data(), buf.size());
-    *out_stream = p;
-    *out_len = buf.size();
-    if (actual_bpp) *actual_bpp = rows * cols > 0 ? 8.0 * (double)buf.size() / ((double)rows * (double)cols) : 0.0;
+    const size_t len = buf.size();
+    *out_stream = buf.release();
+    *out_len = len;
+    if (actual_bpp) *actual_bpp = rows * cols > 0 ? 8.0 * (double)len / ((double)rows * (double)cols) : 0.0;
     return EP_OK;
 }
 

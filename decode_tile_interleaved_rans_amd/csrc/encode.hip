@@ -28,6 +28,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "ep_internal.h"
@@ -510,6 +511,36 @@ struct DevBuf {
     T* as() const { return static_cast<T*>(p); }
 };
 
+// Device scratch of the encoder, kept per device between calls and grown to the largest matrix
+// encoded so far (allocation and release of a few hundred MB per call would cost more than the
+// kernels); calls on one device take turns on it.
+struct Scratch {
+    DevBuf buf;
+    size_t cap = 0;
+    hipError_t need(size_t n) {
+        if (n <= cap) return hipSuccess;
+        buf.reset();
+        cap = 0;
+        hipError_t e = buf.alloc(n);
+        if (e == hipSuccess) cap = n;
+        return e;
+    }
+    void* p() const { return buf.p; }
+    template <class T>
+    T* as() const { return static_cast<T*>(buf.p); }
+};
+
+struct EncoderScratch {
+    std::mutex mu;
+    Scratch scale, flag, umax, hist, vmin, vmax, win, q, coset, qmax, fc, lo, wd, stack, states, words, nesc, off,
+        payload, crc;
+};
+
+EncoderScratch& encoder_scratch(int device) {
+    static EncoderScratch per_device[64];
+    return per_device[device & 63];
+}
+
 #define EP_HIP(call)                                                         \
     do {                                                                     \
         hipError_t e_ = (call);                                              \
@@ -521,15 +552,16 @@ struct DevBuf {
 
 template <int DT>
 ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_opts& o, hipStream_t s,
-                          std::vector<uint8_t>* out, std::string* why) {
+                          Bytes* out, std::string* why, EncoderScratch& X) {
     const int tr = o.tile_rows, n = o.prob_bits;
     const int64_t Rp = (R + tr - 1) / tr * tr, Cp = (C + 255) / 256 * 256, kb = Cp / 8;
-    DevBuf d_scale, d_flag, d_umax, d_hist, d_vmin, d_vmax, d_win, d_q, d_coset, d_qmax;
-    EP_HIP(d_scale.alloc(sizeof(float) * std::max<int64_t>(R, 1)));
-    EP_HIP(d_flag.alloc(sizeof(int)));
-    EP_HIP(d_umax.alloc(sizeof(unsigned long long)));
-    EP_HIP(hipMemsetAsync(d_flag.p, 0, sizeof(int), s));
-    EP_HIP(hipMemsetAsync(d_umax.p, 0, sizeof(unsigned long long), s));
+    Scratch &d_scale = X.scale, &d_flag = X.flag, &d_umax = X.umax, &d_hist = X.hist, &d_vmin = X.vmin,
+            &d_vmax = X.vmax, &d_win = X.win, &d_q = X.q, &d_coset = X.coset, &d_qmax = X.qmax;
+    EP_HIP(d_scale.need(sizeof(float) * std::max<int64_t>(R, 1)));
+    EP_HIP(d_flag.need(sizeof(int)));
+    EP_HIP(d_umax.need(sizeof(unsigned long long)));
+    EP_HIP(hipMemsetAsync(d_flag.p(), 0, sizeof(int), s));
+    EP_HIP(hipMemsetAsync(d_umax.p(), 0, sizeof(unsigned long long), s));
     std::vector<float> scale(R, 0.0f);
     unsigned long long umax_bits = 0;
     if (R > 0) {
@@ -542,11 +574,11 @@ ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_o
             hipLaunchKernelGGL((row_stats<DT, false>), dim3((unsigned)((R + 63) / 64)), dim3(64), 0, s, w, R, C,
                                d_scale.as<float>(), d_flag.as<int>(), d_umax.as<unsigned long long>());
         EP_HIP(hipGetLastError());
-        EP_HIP(hipMemcpyAsync(scale.data(), d_scale.p, sizeof(float) * R, hipMemcpyDeviceToHost, s));
+        EP_HIP(hipMemcpyAsync(scale.data(), d_scale.p(), sizeof(float) * R, hipMemcpyDeviceToHost, s));
     }
     int flag = 0;
-    EP_HIP(hipMemcpyAsync(&flag, d_flag.p, sizeof(int), hipMemcpyDeviceToHost, s));
-    EP_HIP(hipMemcpyAsync(&umax_bits, d_umax.p, sizeof(umax_bits), hipMemcpyDeviceToHost, s));
+    EP_HIP(hipMemcpyAsync(&flag, d_flag.p(), sizeof(int), hipMemcpyDeviceToHost, s));
+    EP_HIP(hipMemcpyAsync(&umax_bits, d_umax.p(), sizeof(umax_bits), hipMemcpyDeviceToHost, s));
     EP_HIP(hipStreamSynchronize(s));
     if (flag & 1) {
         *why = "lossy input holds a non-finite value (or a row whose sum of squares overflows)";
@@ -555,10 +587,10 @@ ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_o
     double U;
     std::memcpy(&U, &umax_bits, sizeof U);
 
-    EP_HIP(d_hist.alloc(sizeof(unsigned long long) * kTables * kSpan2));
-    EP_HIP(d_vmin.alloc(sizeof(int) * kTables));
-    EP_HIP(d_vmax.alloc(sizeof(int) * kTables));
-    EP_HIP(d_win.alloc(sizeof(WindowOut) * kTables));
+    EP_HIP(d_hist.need(sizeof(unsigned long long) * kTables * kSpan2));
+    EP_HIP(d_vmin.need(sizeof(int) * kTables));
+    EP_HIP(d_vmax.need(sizeof(int) * kTables));
+    EP_HIP(d_win.need(sizeof(WindowOut) * kTables));
     std::vector<WindowOut> win(kTables);
     QuantArgs qa{};
     qa.w = w;
@@ -574,9 +606,9 @@ ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_o
     // histograms of one quantization pass, windowed per table, copied to win
     auto run_pass = [&](double delta) -> ep_status {
         std::vector<int> init_min(kTables, INT32_MAX), init_max(kTables, INT32_MIN);
-        EP_HIP(hipMemsetAsync(d_hist.p, 0, sizeof(unsigned long long) * kTables * kSpan2, s));
-        EP_HIP(hipMemcpyAsync(d_vmin.p, init_min.data(), sizeof(int) * kTables, hipMemcpyHostToDevice, s));
-        EP_HIP(hipMemcpyAsync(d_vmax.p, init_max.data(), sizeof(int) * kTables, hipMemcpyHostToDevice, s));
+        EP_HIP(hipMemsetAsync(d_hist.p(), 0, sizeof(unsigned long long) * kTables * kSpan2, s));
+        EP_HIP(hipMemcpyAsync(d_vmin.p(), init_min.data(), sizeof(int) * kTables, hipMemcpyHostToDevice, s));
+        EP_HIP(hipMemcpyAsync(d_vmax.p(), init_max.data(), sizeof(int) * kTables, hipMemcpyHostToDevice, s));
         qa.delta = delta;
         if (qa.n_blocks > 0) {
             hipLaunchKernelGGL(quantize<DT>, dim3((unsigned)((qa.n_blocks + 255) / 256)), dim3(256), 0, s, qa);
@@ -585,7 +617,7 @@ ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_o
         hipLaunchKernelGGL(windows, dim3(kTables), dim3(1024), 0, s, d_hist.as<unsigned long long>(), d_vmin.as<int>(),
                            d_vmax.as<int>(), d_win.as<WindowOut>());
         EP_HIP(hipGetLastError());
-        EP_HIP(hipMemcpyAsync(win.data(), d_win.p, sizeof(WindowOut) * kTables, hipMemcpyDeviceToHost, s));
+        EP_HIP(hipMemcpyAsync(win.data(), d_win.p(), sizeof(WindowOut) * kTables, hipMemcpyDeviceToHost, s));
         EP_HIP(hipStreamSynchronize(s));
         return EP_OK;
     };
@@ -614,11 +646,11 @@ ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_o
     }
 
     // full quantization of the padded matrix
-    EP_HIP(d_q.alloc(sizeof(int16_t) * Rp * Cp));
-    EP_HIP(d_coset.alloc(Rp * kb));
-    EP_HIP(d_qmax.alloc(sizeof(unsigned int) * std::max<int64_t>(R, 1)));
-    EP_HIP(hipMemsetAsync(d_qmax.p, 0, sizeof(unsigned int) * std::max<int64_t>(R, 1), s));
-    EP_HIP(hipMemsetAsync(d_flag.p, 0, sizeof(int), s));
+    EP_HIP(d_q.need(sizeof(int16_t) * Rp * Cp));
+    EP_HIP(d_coset.need(Rp * kb));
+    EP_HIP(d_qmax.need(sizeof(unsigned int) * std::max<int64_t>(R, 1)));
+    EP_HIP(hipMemsetAsync(d_qmax.p(), 0, sizeof(unsigned int) * std::max<int64_t>(R, 1), s));
+    EP_HIP(hipMemsetAsync(d_flag.p(), 0, sizeof(int), s));
     qa.sample = 0;
     qa.n_blocks = Rp * kb;
     qa.qn = qa.rn = 0;
@@ -626,13 +658,13 @@ ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_o
     qa.coset = d_coset.as<uint8_t>();
     qa.qmax = d_qmax.as<unsigned int>();
     if (ep_status st = run_pass((double)step); st != EP_OK) return st;
-    EP_HIP(hipMemcpy(&flag, d_flag.p, sizeof(int), hipMemcpyDeviceToHost));
+    EP_HIP(hipMemcpy(&flag, d_flag.p(), sizeof(int), hipMemcpyDeviceToHost));
     if (flag & 2) {
         *why = "lattice coordinate beyond the int16 escape range";
         return EP_ERANGE;
     }
     std::vector<unsigned int> qmax32(R);
-    if (R > 0) EP_HIP(hipMemcpy(qmax32.data(), d_qmax.p, sizeof(unsigned int) * R, hipMemcpyDeviceToHost));
+    if (R > 0) EP_HIP(hipMemcpy(qmax32.data(), d_qmax.p(), sizeof(unsigned int) * R, hipMemcpyDeviceToHost));
     std::vector<uint16_t> qmax(R);
     for (int64_t r = 0; r < R; ++r) qmax[r] = (uint16_t)qmax32[r];
     std::vector<Table> tables(kTables);
@@ -655,23 +687,23 @@ ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_o
         lo[t] = win[t].lo;
         width[t] = win[t].width;
     }
-    d_hist.reset();
 
     // tiles
     const int64_t tiles_c = Cp / 256, n_tiles = (Rp / tr) * tiles_c;
     const int64_t cap = 64 * 9 * (int64_t)tr;                // words a tile can stack at most
-    DevBuf d_fc, d_lo, d_wd, d_stack, d_states, d_words, d_nesc;
-    EP_HIP(d_fc.alloc(sizeof(uint32_t) * kTables * 256));
-    EP_HIP(d_lo.alloc(sizeof(int32_t) * kTables));
-    EP_HIP(d_wd.alloc(sizeof(int32_t) * kTables));
-    EP_HIP(d_stack.alloc(sizeof(uint16_t) * std::max<int64_t>(n_tiles, 1) * cap));
-    EP_HIP(d_states.alloc(sizeof(uint32_t) * 32 * std::max<int64_t>(n_tiles, 1)));
-    EP_HIP(d_words.alloc(sizeof(uint32_t) * std::max<int64_t>(n_tiles, 1)));
-    EP_HIP(d_nesc.alloc(sizeof(unsigned int)));
-    EP_HIP(hipMemcpyAsync(d_fc.p, fc.data(), sizeof(uint32_t) * kTables * 256, hipMemcpyHostToDevice, s));
-    EP_HIP(hipMemcpyAsync(d_lo.p, lo.data(), sizeof(int32_t) * kTables, hipMemcpyHostToDevice, s));
-    EP_HIP(hipMemcpyAsync(d_wd.p, width.data(), sizeof(int32_t) * kTables, hipMemcpyHostToDevice, s));
-    EP_HIP(hipMemsetAsync(d_nesc.p, 0, sizeof(unsigned int), s));
+    Scratch &d_fc = X.fc, &d_lo = X.lo, &d_wd = X.wd, &d_stack = X.stack, &d_states = X.states, &d_words = X.words,
+            &d_nesc = X.nesc;
+    EP_HIP(d_fc.need(sizeof(uint32_t) * kTables * 256));
+    EP_HIP(d_lo.need(sizeof(int32_t) * kTables));
+    EP_HIP(d_wd.need(sizeof(int32_t) * kTables));
+    EP_HIP(d_stack.need(sizeof(uint16_t) * std::max<int64_t>(n_tiles, 1) * cap));
+    EP_HIP(d_states.need(sizeof(uint32_t) * 32 * std::max<int64_t>(n_tiles, 1)));
+    EP_HIP(d_words.need(sizeof(uint32_t) * std::max<int64_t>(n_tiles, 1)));
+    EP_HIP(d_nesc.need(sizeof(unsigned int)));
+    EP_HIP(hipMemcpyAsync(d_fc.p(), fc.data(), sizeof(uint32_t) * kTables * 256, hipMemcpyHostToDevice, s));
+    EP_HIP(hipMemcpyAsync(d_lo.p(), lo.data(), sizeof(int32_t) * kTables, hipMemcpyHostToDevice, s));
+    EP_HIP(hipMemcpyAsync(d_wd.p(), width.data(), sizeof(int32_t) * kTables, hipMemcpyHostToDevice, s));
+    EP_HIP(hipMemsetAsync(d_nesc.p(), 0, sizeof(unsigned int), s));
     std::vector<uint32_t> words(n_tiles);
     unsigned int n_esc = 0;
     if (n_tiles > 0) {
@@ -680,8 +712,8 @@ ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_o
                     d_words.as<uint32_t>(), d_nesc.as<unsigned int>()};
         hipLaunchKernelGGL(encode_tiles, dim3((unsigned)((n_tiles + 7) / 8)), dim3(256), 0, s, ta);
         EP_HIP(hipGetLastError());
-        EP_HIP(hipMemcpyAsync(words.data(), d_words.p, sizeof(uint32_t) * n_tiles, hipMemcpyDeviceToHost, s));
-        EP_HIP(hipMemcpyAsync(&n_esc, d_nesc.p, sizeof(unsigned int), hipMemcpyDeviceToHost, s));
+        EP_HIP(hipMemcpyAsync(words.data(), d_words.p(), sizeof(uint32_t) * n_tiles, hipMemcpyDeviceToHost, s));
+        EP_HIP(hipMemcpyAsync(&n_esc, d_nesc.p(), sizeof(unsigned int), hipMemcpyDeviceToHost, s));
         EP_HIP(hipStreamSynchronize(s));
     }
     std::vector<uint32_t> offsets(n_tiles + 1, 0);
@@ -693,13 +725,13 @@ ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_o
         offsets[t + 1] = (uint32_t)(acc / 4);
     }
     uint32_t crc = 0;
-    DevBuf d_off, d_payload, d_crc;
+    Scratch &d_off = X.off, &d_payload = X.payload, &d_crc = X.crc;
     if (n_tiles > 0) {
-        EP_HIP(d_off.alloc(sizeof(uint64_t) * n_tiles));
-        EP_HIP(d_payload.alloc(acc));
+        EP_HIP(d_off.need(sizeof(uint64_t) * n_tiles));
+        EP_HIP(d_payload.need(acc));
         const int64_t n_chunks = (int64_t)((acc + kCrcChunk - 1) / kCrcChunk);
-        EP_HIP(d_crc.alloc(sizeof(uint32_t) * n_chunks));
-        EP_HIP(hipMemcpyAsync(d_off.p, byte_off.data(), sizeof(uint64_t) * n_tiles, hipMemcpyHostToDevice, s));
+        EP_HIP(d_crc.need(sizeof(uint32_t) * n_chunks));
+        EP_HIP(hipMemcpyAsync(d_off.p(), byte_off.data(), sizeof(uint64_t) * n_tiles, hipMemcpyHostToDevice, s));
         hipLaunchKernelGGL(assemble, dim3((unsigned)((n_tiles + 3) / 4)), dim3(256), 0, s, d_states.as<uint32_t>(),
                            d_words.as<uint32_t>(), d_stack.as<uint16_t>(), cap, d_off.as<uint64_t>(), n_tiles,
                            d_payload.as<uint8_t>());
@@ -708,7 +740,7 @@ ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_o
                            (int64_t)acc, d_crc.as<uint32_t>());
         EP_HIP(hipGetLastError());
         std::vector<uint32_t> crcs(n_chunks);
-        EP_HIP(hipMemcpyAsync(crcs.data(), d_crc.p, sizeof(uint32_t) * n_chunks, hipMemcpyDeviceToHost, s));
+        EP_HIP(hipMemcpyAsync(crcs.data(), d_crc.p(), sizeof(uint32_t) * n_chunks, hipMemcpyDeviceToHost, s));
         EP_HIP(hipStreamSynchronize(s));
         const uint32_t op_full = x_pow_8n(kCrcChunk);             // every chunk but the last is full
         crc = crcs[0];
@@ -720,7 +752,7 @@ ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_o
     const uint64_t o_pay = serialize_lossy(DT, R, C, tr, n, tables, step, (float)o.target_bpp, scale, qmax, acc,
                                            std::move(offsets), n_esc, n_tiles > 0 ? crc : 0u, out);
     if (n_tiles > 0) {
-        EP_HIP(hipMemcpyAsync(out->data() + o_pay, d_payload.p, acc, hipMemcpyDeviceToHost, s));
+        EP_HIP(hipMemcpyAsync(out->data() + o_pay, d_payload.p(), acc, hipMemcpyDeviceToHost, s));
         EP_HIP(hipStreamSynchronize(s));
     }
     return EP_OK;
@@ -729,11 +761,18 @@ ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_o
 }  // namespace
 
 ep_status encode_lossy_device(const void* dev_w, int dt, int64_t rows, int64_t cols, const ep_encode_opts& o,
-                              hipStream_t stream, std::vector<uint8_t>* out, std::string* why) {
+                              hipStream_t stream, Bytes* out, std::string* why) {
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) {
+        *why = std::string("hipGetDevice: ") + hipGetErrorString(e);
+        return EP_EHIP;
+    }
+    EncoderScratch& X = encoder_scratch(dev);
+    std::lock_guard<std::mutex> lock(X.mu);
     switch (dt) {
-        case EP_F32: return encode_lossy_dt<EP_F32>(dev_w, rows, cols, o, stream, out, why);
-        case EP_BF16: return encode_lossy_dt<EP_BF16>(dev_w, rows, cols, o, stream, out, why);
-        case EP_F16: return encode_lossy_dt<EP_F16>(dev_w, rows, cols, o, stream, out, why);
+        case EP_F32: return encode_lossy_dt<EP_F32>(dev_w, rows, cols, o, stream, out, why, X);
+        case EP_BF16: return encode_lossy_dt<EP_BF16>(dev_w, rows, cols, o, stream, out, why, X);
+        case EP_F16: return encode_lossy_dt<EP_F16>(dev_w, rows, cols, o, stream, out, why, X);
         default:
             *why = "lossy mode takes F32, BF16 or F16 input";
             return EP_EUNSUPPORTED;

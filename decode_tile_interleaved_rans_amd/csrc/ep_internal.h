@@ -15,7 +15,9 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <cstdlib>
 #include <functional>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -47,6 +49,32 @@ struct Table {
     uint32_t freq[256];    // normalized frequency per symbol (escape at 255 for lossy tables)
 };
 
+// A malloc-backed byte buffer: streams are built in place and handed to the caller, who frees
+// them with ep_free, so no copy of a stream is made on the way out.
+struct Bytes {
+    uint8_t* p = nullptr;
+    size_t n = 0;
+    Bytes() = default;
+    Bytes(const Bytes&) = delete;
+    Bytes& operator=(const Bytes&) = delete;
+    ~Bytes() { std::free(p); }
+    // size uninitialized bytes; throws std::bad_alloc when the allocation fails
+    void allocate(size_t size) {
+        std::free(p);
+        p = static_cast<uint8_t*>(std::malloc(size ? size : 1));
+        n = p ? size : 0;
+        if (!p) throw std::bad_alloc();
+    }
+    uint8_t* data() { return p; }
+    size_t size() const { return n; }
+    uint8_t* release() {
+        uint8_t* r = p;
+        p = nullptr;
+        n = 0;
+        return r;
+    }
+};
+
 // A validated stream (views into the caller's bytes).
 struct StreamView {
     const uint8_t* base = nullptr;
@@ -70,7 +98,7 @@ void fill_info(const StreamView& v, ep_info* info);
 
 // Host encoder.
 ep_status encode(const void* w, int dtype, int64_t rows, int64_t cols, const ep_encode_opts& o,
-                 std::vector<uint8_t>* out, std::string* why);
+                 Bytes* out, std::string* why);
 
 // Pieces of the host encoder that the device encoder shares (same arithmetic, so that both
 // produce the same bytes).
@@ -85,10 +113,10 @@ float choose_step(double U, double target, const std::function<double(double)>& 
 uint64_t serialize_lossy(int dt, int64_t R, int64_t C, int tile_rows, int n, const std::vector<Table>& tables,
                          float step, float target, const std::vector<float>& scale, const std::vector<uint16_t>& qmax,
                          uint64_t payload_len, std::vector<uint32_t>&& offsets, uint32_t n_esc, uint32_t payload_crc,
-                         std::vector<uint8_t>* out);
+                         Bytes* out);
 
 // Device encoder (lossy mode): the same stream as encode() from a weight in device memory.
 ep_status encode_lossy_device(const void* dev_w, int dt, int64_t rows, int64_t cols, const ep_encode_opts& o,
-                              hipStream_t stream, std::vector<uint8_t>* out, std::string* why);
+                              hipStream_t stream, Bytes* out, std::string* why);
 
 }  // namespace ep

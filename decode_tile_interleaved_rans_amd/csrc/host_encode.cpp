@@ -289,7 +289,7 @@ struct TileSet {
 // Returns the payload's offset in the stream.
 uint64_t serialize(int mode, int dt, int64_t R, int64_t C, int tile_rows, int n, const std::vector<Table>& tables,
                float step, float target, const std::vector<float>& scale, const std::vector<uint16_t>& qmax,
-               const TileSet& ts, uint32_t n_esc, std::vector<uint8_t>* out,
+               const TileSet& ts, uint32_t n_esc, Bytes* out,
                const std::vector<uint8_t>* raw = nullptr, const uint32_t* payload_crc = nullptr) {
     const uint64_t meta_rows = mode == EP_MODE_LOSSY_E8 ? (uint64_t)R : 0;
     uint64_t tables_len = 0;
@@ -302,8 +302,9 @@ uint64_t serialize(int mode, int dt, int64_t R, int64_t C, int tile_rows, int n,
     const uint64_t o_raw = raw ? up16(o_idx + 4 * ((uint64_t)n_tiles + 1)) : 0;
     const uint64_t o_pay = raw ? up16(o_raw + raw->size()) : up16(o_idx + 4 * ((uint64_t)n_tiles + 1));
     const uint64_t total = o_pay + (ts.payload.empty() ? ts.external_len : ts.payload.size());
-    out->assign(total, 0);
+    out->allocate(total);
     uint8_t* s = out->data();
+    std::memset(s, 0, o_pay);                       // header, metadata and padding; the payload follows
     std::memcpy(s + kMagic, "EPK1", 4);
     w16(s + kVersion, 1);
     s[kMode] = (uint8_t)mode;
@@ -464,7 +465,7 @@ double sampled_bpp(const Quantizer& Q, int64_t nb, int64_t sb, double delta, int
 }
 
 ep_status encode_lossy(const void* w, int dt, int64_t R, int64_t C, const ep_encode_opts& o, int threads,
-                       std::vector<uint8_t>* out, std::string* why) {
+                       Bytes* out, std::string* why) {
     const int tr = o.tile_rows, n = o.prob_bits;
     const int64_t Rp = (R + tr - 1) / tr * tr, Cp = (C + kTileCols - 1) / kTileCols * kTileCols;
     const int64_t kb = Cp / 8;
@@ -591,7 +592,7 @@ ep_status encode_lossy(const void* w, int dt, int64_t R, int64_t C, const ep_enc
 
 // ------------------------------------------------------------------------------ lossless
 ep_status encode_lossless(const void* w, int dt, int64_t R, int64_t C, const ep_encode_opts& o, int threads,
-                          std::vector<uint8_t>* out, std::string* why) {
+                          Bytes* out, std::string* why) {
     const int tr = o.tile_rows, n = o.prob_bits;
     const int P = element_bytes(dt);
     const int64_t Rp = (R + tr - 1) / tr * tr, Cp = (C + kTileCols - 1) / kTileCols * kTileCols;
@@ -654,7 +655,7 @@ ep_status encode_lossless(const void* w, int dt, int64_t R, int64_t C, const ep_
 // mantissa are stored uncoded as (sign << 7) | mantissa in a raw plane [Rp][Cp] shaped like the
 // zero-padded matrix, so that the decoder reads each lane's 8 bytes of a row with one load.
 ep_status encode_lossless_exp(const void* w, int64_t R, int64_t C, const ep_encode_opts& o, int threads,
-                              std::vector<uint8_t>* out, std::string* why) {
+                              Bytes* out, std::string* why) {
     const int tr = o.tile_rows, n = o.prob_bits;
     const int64_t Rp = (R + tr - 1) / tr * tr, Cp = (C + kTileCols - 1) / kTileCols * kTileCols;
     const uint16_t* src = static_cast<const uint16_t*>(w);
@@ -713,7 +714,7 @@ float choose_step(double U, double target, const std::function<double(double)>& 
 uint64_t serialize_lossy(int dt, int64_t R, int64_t C, int tile_rows, int n, const std::vector<Table>& tables,
                          float step, float target, const std::vector<float>& scale, const std::vector<uint16_t>& qmax,
                          uint64_t payload_len, std::vector<uint32_t>&& offsets, uint32_t n_esc, uint32_t payload_crc,
-                         std::vector<uint8_t>* out) {
+                         Bytes* out) {
     TileSet ts;
     ts.offsets = std::move(offsets);
     ts.external_len = payload_len;
@@ -721,7 +722,7 @@ uint64_t serialize_lossy(int dt, int64_t R, int64_t C, int tile_rows, int n, con
                      nullptr, &payload_crc);
 }
 
-ep_status encode(const void* w, int dt, int64_t R, int64_t C, const ep_encode_opts& o, std::vector<uint8_t>* out,
+ep_status encode(const void* w, int dt, int64_t R, int64_t C, const ep_encode_opts& o, Bytes* out,
                  std::string* why) {
     int threads = o.n_threads > 0 ? o.n_threads : (int)std::max(1u, std::thread::hardware_concurrency());
     threads = std::min(threads, 64);

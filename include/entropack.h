@@ -99,8 +99,9 @@ ep_status ep_compress(const void* host_w, ep_dtype src, int64_t rows, int64_t co
  * encoding", "EntroPack: Fast and Accurate Entropy-Coded Weight Compression at Arbitrary
  * Bitrates", Abstract). dev_w: [rows][cols] elements of src (EP_F32, EP_BF16, EP_F16) on the
  * current device; opts as for ep_compress (mode must be EP_MODE_LOSSY_E8; n_threads is unused).
- * The call synchronizes hip_stream; device scratch (about 2.3 bytes per weight plus 18 KiB per
- * 16-row tile for the word stacks) is allocated and freed inside the call. *out_stream is
+ * The call synchronizes hip_stream. Device scratch (about 2.3 bytes per weight plus 18 KiB per
+ * 16-row tile for the word stacks) is kept per device after the call, grown to the largest
+ * matrix encoded, and reused; concurrent calls on one device take turns. *out_stream is
  * library-allocated (free with ep_free). Errors: as ep_compress, plus EP_EHIP / EP_ENOMEM for
  * device failures and EP_EUNSUPPORTED for a lossless mode. */
 ep_status ep_compress_device(const void* dev_w, ep_dtype src, int64_t rows, int64_t cols,
