@@ -94,6 +94,9 @@ ep::MatDesc desc_for(const ep_handle* h, int container, void* out, float* scale)
     d.n_tables = (uint8_t)v.n_tables;
     d.mode = (uint8_t)v.mode;
     d.pair_cost = ep::pair_cost_of(v.mode, v.tile_rows, v.n_tables);
+    if (v.mode == EP_MODE_LOSSY_E8)
+        for (int t = 1; t < v.n_tables && t <= 16; ++t)
+            if (v.tables[t].freq[ep::kEscape] != 0) d.esc_tables |= (uint16_t)(1u << (t - 1));
     return d;
 }
 

@@ -70,6 +70,13 @@ __device__ __forceinline__ float materialize(float v) {
     asm volatile("" : "+v"(v));
     return v;
 }
+// The signed 16-bit value in the high half of v as fp32, in one conversion (SDWA word select with
+// sign extension).
+__device__ __forceinline__ float hi16_to_f32(uint32_t v) {
+    float r;
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1" : "=v"(r) : "v"(v));
+    return r;
+}
 __device__ __forceinline__ uint32_t f16_rne(float v) {
     _Float16 h = (_Float16)materialize(v);               // v_cvt_f16_f32: round to nearest even
     return (uint32_t)__builtin_bit_cast(uint16_t, h);
@@ -532,26 +539,30 @@ __device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Til
                 for (int c = 0; c < C; ++c) top_up(t[c], rs);
             }
             // all chains' step j in one basic block, so the scheduler can interleave the chains;
-            // the rare escapes branch once for all chains
+            // the rare escapes branch once for all chains, and only where either coset's table j
+            // can decode the escape symbol (a uniform test)
             uint2 e[C];
             const uint2* ent_j[C];
-            bool esc[C];
-            uint64_t any = 0;
 #pragma unroll
             for (int c = 0; c < C; ++c) ent_j[c] = ent_b[c] + 2 * j * 256;
             rans_steps<N, C>(t, (2 * j) << N, base, ent_j, e);
             refill_all<C>(t);
 #pragma unroll
-            for (int c = 0; c < C; ++c) {
-                q[c][j] = (float)((int32_t)e[c].y >> 16);
-                esc[c] = (int32_t)e[c].x < 0;
-                any |= __ballot(esc[c]);
-            }
-            if (any) {
+            for (int c = 0; c < C; ++c) q[c][j] = hi16_to_f32(e[c].y);
+            if ((M.esc_tables >> (2 * j)) & 3u) {
+                bool esc[C];
+                uint64_t any = 0;
 #pragma unroll
                 for (int c = 0; c < C; ++c) {
-                    const uint32_t w = take_words(t[c], esc[c]);
-                    if (esc[c]) q[c][j] = (float)(2 * (int32_t)(int16_t)w + b[c]);
+                    esc[c] = (int32_t)e[c].x < 0;
+                    any |= __ballot(esc[c]);
+                }
+                if (any) {
+#pragma unroll
+                    for (int c = 0; c < C; ++c) {
+                        const uint32_t w = take_words(t[c], esc[c]);
+                        if (esc[c]) q[c][j] = (float)(2 * (int32_t)(int16_t)w + b[c]);
+                    }
                 }
             }
         }

@@ -36,6 +36,8 @@ struct MatDesc {
     uint8_t prob_bits, tile_rows, container, n_tables;
     uint8_t mode;               // 0 lossy E8 coordinates, 1 lossless byte planes, 2 exponent-coded BF16
     uint8_t gemv_m;             // activation rows of a fused matrix-vector product
+    uint16_t esc_tables;        // lossy: bit 2j + b set when coordinate table 1 + 2j + b can decode
+                                // the escape symbol (its frequency is not zero)
     uint32_t pair_cost;         // relative decode time of one tile pair (load balancing)
 };
 

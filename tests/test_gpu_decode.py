@@ -151,6 +151,23 @@ def test_escapes_and_small_rows():
     assert_parity(s)
 
 
+def test_escapes_in_some_tables_only():
+    # outliers only at column position 3 of every 8-block: only the coordinate tables of position 3
+    # (tables 7 and 8) can decode the escape symbol, so the kernel takes its escape test at that
+    # step alone and skips it at the other seven; several tiles and a ragged tail
+    rng = np.random.default_rng(9)
+    w = rng.normal(0, 0.01, (80, 1000)).astype(np.float32)
+    m = np.zeros(w.shape, bool)
+    m[:, 3::8] = rng.random((80, 125)) < 0.01
+    w[m] = 3.0 * np.sign(rng.normal(size=int(m.sum())))
+    s, _ = ep.compress(w, 4.0)
+    assert ep.stream_info(s)["n_escapes"] > 0
+    _, _, f = oracle.tables(s)
+    esc = [t for t in range(1, 17) if f[t, 255] > 0]
+    assert esc and set(esc) <= {7, 8}, esc
+    assert_parity(s)
+
+
 def test_degenerate_matrices():
     for w in [np.zeros((40, 300), np.float32), np.full((16, 256), 0.5, np.float32)]:
         s, _ = ep.compress(w, 4.0)
