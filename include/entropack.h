@@ -149,12 +149,14 @@ ep_status ep_decode_symbols(const ep_handle* h, int16_t* dev_q, void* hip_stream
 /* Compressed linear layer forward: Y[M][N] = X[M][K] * W^T (+ bias), W = the decoded BF16
  * weight [N][K] of handle w, fp32 accumulation, BF16 output ("EntroPack PyTorch Guide", section
  * "Replace one linear layer before a whole model"). For M <= 4 the decode kernel itself forms the
- * products (the decoded fp32 weights are multiplied by the activations in registers and summed
- * into an fp32 accumulator in the workspace; the weight is never written). For larger M the
- * weight is decoded once per call, up to 128 MiB of BF16 rows at a time, into a library-owned
- * workspace that stays in the Infinity Cache, and each slice is multiplied by the BF16 MFMA
- * GEMM; no decoded copy of W outlives the call. The workspace belongs to the (device, hip_stream) pair: calls on one stream reuse it in
- * order, calls on different streams get different workspaces; it is allocated on first use
+ * products (the decoded fp32 weights, not rounded to BF16, are multiplied by the activations in
+ * registers and summed into an fp32 accumulator in the workspace by atomic additions, whose order
+ * varies, so two calls may differ in the last bits; the weight is never written). For larger M
+ * the weight is decoded once per call, up to 128 MiB of BF16 rows at a time, into a
+ * library-owned workspace that stays in the Infinity Cache, and each slice is multiplied by the
+ * BF16 MFMA GEMM (deterministic); no decoded copy of W outlives the call. The workspace belongs
+ * to the (device, hip_stream) pair: calls on one stream reuse it in order, calls on different
+ * streams get different workspaces; it is allocated on first use
  * (hipMalloc, which may synchronize the device) and kept until the process ends.
  *   dev_x: [M][K] bf16, 16-byte aligned; dev_bias: [N] bf16 or NULL; dev_y: [M][N] bf16.
  * Requires a lossy stream and K % 8 == 0. Asynchronous on hip_stream. */
