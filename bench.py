@@ -89,9 +89,17 @@ def cpu_baseline(items, budget_s: float = 10.0):
         if time.time() - t0 >= budget_s or steps >= 50:
             break
     dt = time.time() - t0
+    # one core: one lossy and the lossless matrix of the step
+    one = [it for it in items if it[0] in ("lossy4.0_bf16", "lossless_bf16")]
+    t1 = time.time()
+    one_bytes = sum(oracle.decompress(s, odt[ct], n_threads=1)[0].nbytes for _, s, ct, _ in one)
+    dt1 = time.time() - t1
     return {"value": out_bytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{steps} full step(s) of the same workload (7 full-matrix decodes each) decoded by the "
-                      f"oracle with {cores} threads in {dt:.1f} s"}
+                      f"oracle with {cores} threads in {dt:.1f} s",
+            "one_core": {"value": one_bytes / dt1 / 1e9, "unit": "GB/s",
+                         "sample": f"the 4.0 bpp and the lossless 4096x4096 decodes of the step on one thread "
+                                   f"in {dt1:.1f} s"}}
 
 
 def fused_gemm_section(torch, ep, reps: int = 15):
