@@ -290,6 +290,103 @@ def dit_model_section(torch, ep, steps: int = 10):
             "tweights_per_s": round(weights / ms / 1e9, 4), "steps": steps}
 
 
+def mixed_section(torch, ep, steps: int = 5, reps: int = 5):
+    """The 64-matrix mixed-rate set: rows and cols from {2048, 4096, 8192}, targets uniform in
+    [2.5, 6.0] (workloads.mixed_rate_set), 1.55 G weights of 0.02 t5 BF16. The weights are drawn
+    on the GPU (torch's generator seeded with the matrix seed; t5 = z / sqrt(chi2_5 / 5) from six
+    normals) and coded by the device encoder, to keep the host out of the run. Timed: the whole set
+    decoded to BF16, to FP8 E4M3 (+ row scales) and to INT8 (+ row scales), each as grouped
+    launches of 32; then the compressed BF16 forward of all 64 layers against torch.matmul on the
+    decoded BF16 weights at M = 16, 256 and 4096 (X ~ N(0, 1) bf16, seeded 500 + i)."""
+    from decode_tile_interleaved_rans_amd import workloads as W
+    specs = W.mixed_rate_set()
+    streams, hs, bpps = [], [], []
+    t0 = time.time()
+    for R, Cc, tgt, seed, _ in specs:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        z = torch.randn((R, Cc), generator=g, device="cuda")
+        v = torch.zeros((R, Cc), device="cuda")
+        for _ in range(5):
+            v += torch.randn((R, Cc), generator=g, device="cuda").square()
+        w = (0.02 * z / torch.sqrt(v / 5.0)).to(torch.bfloat16)
+        del z, v
+        st, bpp = ep.compress_device(w, tgt)
+        del w
+        streams.append(st)
+        bpps.append(bpp)
+        hs.append(ep.upload(st))
+    log(f"mixed set: 64 matrices drawn and coded on the GPU in {time.time() - t0:.1f} s")
+    n_w = sum(R * Cc for R, Cc, *_ in specs)
+    in_b = sum(len(x) for x in streams)
+    out = {"workload": "64 matrices, rows/cols in {2048, 4096, 8192}, targets U[2.5, 6.0], 0.02 t5 bf16, "
+                       f"{n_w / 1e9:.3f} G weights, {in_b / 1e9:.3f} GB of streams",
+           "actual_bpp_mean": round(float(np.mean(bpps)), 4)}
+    dec = {}
+    for name, dt, eb, scaled in (("bf16", torch.bfloat16, 2, False), ("fp8", torch.float8_e4m3fn, 1, True),
+                                 ("int8", torch.int8, 1, True)):
+        outs = [torch.empty((R, Cc), dtype=dt, device="cuda") for R, Cc, *_ in specs]
+        scs = [torch.empty(R, dtype=torch.float32, device="cuda") for R, *_ in specs] if scaled else None
+        ep.decompress_many(hs, outs, scs)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            ep.decompress_many(hs, outs, scs)
+        b.record()
+        torch.cuda.synchronize()
+        for h in hs:
+            h.check()
+        ms = a.elapsed_time(b) / steps
+        alg = in_b + n_w * eb + (sum(R for R, *_ in specs) * 4 * 2 if scaled else 0)
+        dec[name] = {"ms": round(ms, 4), "output_gbs": round(n_w * eb / ms / 1e6, 1),
+                     "algorithmic_gbs": round(alg / ms / 1e6, 1), "hbm_frac": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4),
+                     "tweights_per_s": round(n_w / ms / 1e9, 4)}
+        if name != "bf16":
+            del outs
+        else:
+            wd = outs
+        del scs
+        log(f"mixed set to {name}: {ms:.3f} ms")
+    out["decode"] = dec
+    layers = [ep.CompressedLinear(st) for st in streams]
+    fused = {}
+    for M in (16, 256, 4096):
+        xs = []
+        for (R, Cc, _, _, xseed) in specs:
+            g = torch.Generator(device="cuda")
+            g.manual_seed(xseed)
+            xs.append(torch.randn((M, Cc), generator=g, device="cuda").to(torch.bfloat16))
+        for lay, x in zip(layers, xs):
+            lay(x)
+        for x, w in zip(xs, wd):
+            torch.matmul(x, w.T)
+        torch.cuda.synchronize()
+        tf, tt = [], []
+        for _ in range(reps):
+            a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            a.record()
+            for lay, x in zip(layers, xs):
+                lay(x)
+            b.record()
+            for x, w in zip(xs, wd):
+                torch.matmul(x, w.T)
+            c.record()
+            torch.cuda.synchronize()
+            tf.append(a.elapsed_time(b))
+            tt.append(b.elapsed_time(c))
+        f, t = float(np.median(tf)), float(np.median(tt))
+        fused[f"M{M}"] = {"fused_ms": round(f, 4), "torch_matmul_ms": round(t, 4), "overhead_vs_torch": round(f / t - 1, 4)}
+        log(f"mixed set forward M={M}: fused {f:.3f} ms, torch {t:.3f} ms")
+        del xs
+    out["forward_64_layers"] = fused
+    for h in hs:
+        h.release()
+    del layers, wd
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,6 +403,7 @@ def main():
                     help="profiling aid: run only the encoder comparison and print its JSON")
     ap.add_argument("--dit-model", action="store_true",
                     help="also time the full-model decode step of the DiT-like denoiser (5.31 G weights)")
+    ap.add_argument("--no-mixed", action="store_true", help="skip the 64-matrix mixed-rate set")
     ap.add_argument("--step-only", action="store_true",
                     help="profiling aid: time only the decode step (no lossless, encoder, GEMM or CPU sections)")
     args = ap.parse_args()
@@ -403,6 +501,7 @@ def main():
     if not args.no_gemm and not args.step_only:
         fused = fused_gemm_section(torch, ep, reps=args.gemm_reps)
     dit = dit_model_section(torch, ep) if args.dit_model else None
+    mixed = mixed_section(torch, ep) if not args.step_only and not args.no_mixed else None
     cpu = None
     if not args.no_cpu and not args.step_only:
         log("timing the oracle on the host cores")
@@ -423,6 +522,7 @@ def main():
         "lossless_bf16_codings": lossless,
         "encoders": encoders,
         "dit_model": dit,
+        "mixed_rate_set": mixed,
         "fused_gemm": fused,
         "cpu_baseline": cpu,
     }
