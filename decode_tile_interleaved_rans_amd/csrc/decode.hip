@@ -388,11 +388,12 @@ __device__ __forceinline__ void store_block(const MatDesc& M, uint32_t row, uint
 
 // ----------------------------------------------------------------------------- lossy kernel
 // Rows of one tile pair: tile coordinates and the per-row scales, one row per lane, read back
-// per row with readlane.
+// per row with readlane. INT8: the row's divisor k and its reciprocal multiplier, computed once
+// per pair by each lane for its row (a vector division per pair instead of a scalar one per row).
 struct PairRows {
     uint32_t tc, row0;
     float sc_l;
-    uint32_t qm_l;
+    uint32_t k_l, magic_l;
     float xv[4][8];        // fused matrix-vector product: the lane's 8 activation columns per row m
 };
 
@@ -427,8 +428,13 @@ __device__ __forceinline__ void begin_pair(const MatDesc& M, __amdgpu_buffer_rsr
     const uint32_t my_row = P.row0 + t.l;
     const bool mine = t.l < M.tile_rows && my_row < M.rows;
     P.sc_l = mine ? M.row_scale[my_row] : 0.0f;
-    P.qm_l = 0;
-    if constexpr (CT == CT_I8) P.qm_l = mine ? M.row_qmax[my_row] : 0u;
+    P.k_l = 1;
+    P.magic_l = 0;
+    if constexpr (CT == CT_I8) {
+        const uint32_t qm = mine ? M.row_qmax[my_row] : 0u;
+        P.k_l = qm > 127u ? (qm + 126u) / 127u : 1u;
+        P.magic_l = 0xFFFFFFFFu / (2u * P.k_l) + 1u;
+    }
     if constexpr (gemv_rows(CT) > 0) {
         // the lane's 8 columns of each activation row; zeros past the matrix or the tile pair
         const uint32_t col0 = P.tc * 256 + 8 * t.l;
@@ -449,7 +455,7 @@ __device__ __forceinline__ void begin_pair(const MatDesc& M, __amdgpu_buffer_rsr
     // Wait for these loads here, once per pair: first used inside the row loop, their wait would
     // land inside it, on every row, and (the vector-memory counter being in order) would also
     // wait for the ring chunk just prefetched.
-    asm volatile("" ::"v"(P.sc_l), "v"(P.qm_l), "v"(t.x));
+    asm volatile("" ::"v"(P.sc_l), "v"(P.k_l), "v"(P.magic_l), "v"(t.x));
 }
 
 template <int CT>
@@ -483,9 +489,8 @@ __device__ __forceinline__ void store_row(const MatDesc& M, const Tile& t, const
         const float alpha = h * sc;
         uint32_t k = 1, magic = 0;
         if constexpr (CT == CT_I8) {
-            const uint32_t qm = (uint32_t)__builtin_amdgcn_readlane((int)P.qm_l, rr);
-            k = qm > 127u ? (qm + 126u) / 127u : 1u;
-            magic = 0xFFFFFFFFu / (2u * k) + 1u;
+            k = (uint32_t)__builtin_amdgcn_readlane((int)P.k_l, rr);
+            magic = (uint32_t)__builtin_amdgcn_readlane((int)P.magic_l, rr);
         }
         const uint32_t col0 = t.valid ? P.tc * 256 + 8 * t.l : 0xFFFFFFF0u;     // no tile: out of range
         store_block<CT>(M, row, col0, q, alpha, h, k, magic);
