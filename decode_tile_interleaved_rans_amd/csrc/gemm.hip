@@ -189,19 +189,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt(GemmArgs g) {
 
 // Tiled kernel with direct global -> LDS loads (buffer_load ... lds): a wave's load instruction
 // writes its 64 lanes' 16 bytes to 1 KiB of LDS in lane order, 8 operand rows of 128 bytes, so no
-// registers stage the tiles. Rows are unpadded and their eight 16-byte K chunks swizzled (chunk c
-// of row r at slot c ^ (r % 8)), which keeps the MFMA fragment reads free of bank conflicts. Two
-// LDS stages: the loads of step k + 1 run while step k multiplies.
+// registers stage the tiles. Rows are unpadded and their eight 16-byte K chunks swizzled: chunk c
+// of row r sits at slot c ^ ((r / 2) % 8). A fragment read has 16 lanes on 16 consecutive rows at
+// the same chunk in each LDS cycle; with 128-byte rows the 16-byte bank group of (r, slot) is
+// 8 (r % 2) + slot of 16, so the slots of the even rows and of the odd rows must each be distinct,
+// which (r / 2) % 8 gives (the plain r % 8 put rows r and r + 8 on one bank group: counters showed
+// half of the LDS cycles lost to conflicts). Two LDS stages: the loads of step k + 1 run while
+// step k multiplies.
 typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int chunk_swizzle(int r) { return (r >> 1) & 7; }
 
 template <int ROWS, int NW>
 __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, int ld, int k0, int K, uint8_t* lds) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rr = lane >> 3, kc = (lane & 7) ^ rr;          // row within the 8-row group; its chunk
-    const int k = k0 + 8 * kc;
+    const int rr = lane >> 3;                                 // row within the 8-row group
 #pragma unroll
     for (int j = 0; j < ROWS / 8 / NW; ++j) {
         const int g = wave + NW * j;                          // 8-row group of this instruction
+        const int k = k0 + 8 * ((lane & 7) ^ chunk_swizzle(8 * g + rr));   // the chunk for this slot
         const uint32_t off = (uint32_t)((8 * g + rr) * ld + k) * 2u | ((uint32_t)((K - 1 - k) >> 31) & kOob);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + 1024 * g), 16, off, 0, 0, 0);
     }
@@ -252,12 +258,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_dma(GemmArgs g) {
 #pragma unroll
             for (int i = 0; i < TI; ++i) {
                 const int r = wm + 32 * i + (lane & 31);
-                a[i] = *reinterpret_cast<const bf16x8*>(cur + r * 128 + ((kc ^ (r & 7)) << 4));
+                a[i] = *reinterpret_cast<const bf16x8*>(cur + r * 128 + ((kc ^ chunk_swizzle(r)) << 4));
             }
 #pragma unroll
             for (int j = 0; j < TJ; ++j) {
                 const int r = wn + 32 * j + (lane & 31);
-                bb[j] = *reinterpret_cast<const bf16x8*>(cur + BM * 128 + r * 128 + ((kc ^ (r & 7)) << 4));
+                bb[j] = *reinterpret_cast<const bf16x8*>(cur + BM * 128 + r * 128 + ((kc ^ chunk_swizzle(r)) << 4));
             }
 #pragma unroll
             for (int i = 0; i < TI; ++i)
@@ -387,19 +393,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc_u8(const uint8_t*
 template <int ROWS, int NW>
 __device__ __forceinline__ void dma_tile_u8(__amdgpu_buffer_rsrc_t rs, int ld, int k0, int K, uint8_t* lds) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rr = lane >> 3, kc = (lane & 7) ^ rr;
-    const int k = k0 + 16 * kc;
+    const int rr = lane >> 3;
 #pragma unroll
     for (int j = 0; j < ROWS / 8 / NW; ++j) {
         const int g = wave + NW * j;
+        const int k = k0 + 16 * ((lane & 7) ^ chunk_swizzle(8 * g + rr));
         const uint32_t off = (uint32_t)((8 * g + rr) * ld + k) | ((uint32_t)((K - 1 - k) >> 31) & kOob);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + 1024 * g), 16, off, 0, 0, 0);
     }
 }
 
 __device__ __forceinline__ i32x8 frag_f8(const uint8_t* row, int r, int c0) {
-    const uint4 lo = *reinterpret_cast<const uint4*>(row + ((c0 ^ (r & 7)) << 4));
-    const uint4 hi = *reinterpret_cast<const uint4*>(row + (((c0 + 2) ^ (r & 7)) << 4));
+    const uint4 lo = *reinterpret_cast<const uint4*>(row + ((c0 ^ chunk_swizzle(r)) << 4));
+    const uint4 hi = *reinterpret_cast<const uint4*>(row + (((c0 + 2) ^ chunk_swizzle(r)) << 4));
     return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
