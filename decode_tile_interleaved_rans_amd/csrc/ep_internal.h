@@ -40,8 +40,9 @@ enum HeaderField : int {
     kTileColsField = 18, kLanesField = 20, kProbBits = 22, kNumTables = 23, kStep = 24,
     kTarget = 28, kNumTiles = 32, kNumEscapes = 36, kOffScale = 40, kOffQmax = 48,
     kOffTables = 56, kOffIndex = 64, kOffPayload = 72, kTotalLen = 80, kPayloadCrc = 88,
-    kOffRaw = 96, kRawCrc = 104
+    kOffRaw = 96, kRawCrc = 104, kMetaCrc = 112
 };
+constexpr int kFormatVersion = 2;      // 2: the metadata CRC-32 at byte 112
 
 struct Table {
     int32_t lo = 0;        // first coordinate value of the window (lossless: 0)
@@ -91,6 +92,11 @@ struct StreamView {
 
 int element_bytes(int dtype);
 uint32_t crc32(const uint8_t* p, size_t n);
+// CRC-32 of every stream byte outside the payload, the raw plane (exponent-coded mode; raw_len 0
+// otherwise) and the metadata CRC field itself: header bytes [0, 112) and [116, 128), the row
+// metadata, tables, tile index and all padding. Together with the payload and raw-plane CRCs it
+// makes every bit of a stream checked.
+uint32_t meta_crc32(const uint8_t* s, uint64_t off_raw, uint64_t raw_len, uint64_t off_payload);
 
 // Validation (host). Returns EP_OK or EP_ECORRUPT with a message in *why.
 ep_status parse_stream(const uint8_t* s, size_t len, StreamView* out, std::string* why);

@@ -306,7 +306,7 @@ uint64_t serialize(int mode, int dt, int64_t R, int64_t C, int tile_rows, int n,
     uint8_t* s = out->data();
     std::memset(s, 0, o_pay);                       // header, metadata and padding; the payload follows
     std::memcpy(s + kMagic, "EPK1", 4);
-    w16(s + kVersion, 1);
+    w16(s + kVersion, kFormatVersion);
     s[kMode] = (uint8_t)mode;
     s[kDtype] = (uint8_t)dt;
     w32(s + kRows, (uint32_t)R);
@@ -345,6 +345,7 @@ uint64_t serialize(int mode, int dt, int64_t R, int64_t C, int tile_rows, int n,
         for (int k = 0; k < t.width; ++k, p += 2) w16(p, t.freq[k]);
     }
     for (uint32_t i = 0; i <= n_tiles; ++i) w32(s + o_idx + 4 * (uint64_t)i, ts.offsets[i]);
+    w32(s + kMetaCrc, meta_crc32(s, o_raw, raw ? raw->size() : 0, o_pay));
     if (!ts.payload.empty()) std::memcpy(s + o_pay, ts.payload.data(), ts.payload.size());
     return o_pay;
 }

@@ -51,10 +51,25 @@ int element_bytes(int dtype) {
     }
 }
 
-uint32_t crc32(const uint8_t* p, size_t n) {
+namespace {
+uint32_t crc32_add(uint32_t c, const uint8_t* p, size_t n) {
     static const CrcTable T;
-    uint32_t c = 0xFFFFFFFFu;
     for (size_t i = 0; i < n; ++i) c = T.t[(c ^ p[i]) & 0xFF] ^ (c >> 8);
+    return c;
+}
+}  // namespace
+
+uint32_t crc32(const uint8_t* p, size_t n) { return ~crc32_add(0xFFFFFFFFu, p, n); }
+
+uint32_t meta_crc32(const uint8_t* s, uint64_t off_raw, uint64_t raw_len, uint64_t off_payload) {
+    const uint64_t after = kMetaCrc + 4;
+    uint32_t c = crc32_add(0xFFFFFFFFu, s, kMetaCrc);
+    if (raw_len) {
+        c = crc32_add(c, s + after, off_raw - after);
+        c = crc32_add(c, s + off_raw + raw_len, off_payload - (off_raw + raw_len));
+    } else {
+        c = crc32_add(c, s + after, off_payload - after);
+    }
     return ~c;
 }
 
@@ -62,7 +77,7 @@ ep_status parse_stream(const uint8_t* s, size_t len, StreamView* v, std::string*
     *v = StreamView{};
     if (!s || len < (size_t)kHeaderBytes) return bad(why, "stream shorter than its 128-byte header");
     if (std::memcmp(s, "EPK1", 4) != 0) return bad(why, "bad magic (not an EPK1 stream)");
-    if (r16(s + kVersion) != 1) return bad(why, "unsupported stream version");
+    if (r16(s + kVersion) != (uint32_t)kFormatVersion) return bad(why, "unsupported stream version");
     v->base = s;
     v->len = len;
     v->mode = s[kMode];
@@ -158,6 +173,8 @@ ep_status parse_stream(const uint8_t* s, size_t len, StreamView* v, std::string*
     }
     if (4 * prev != v->payload_len) return bad(why, "tile index does not end at the payload end");
     if (crc32(s + v->off_payload, v->payload_len) != r32(s + kPayloadCrc)) return bad(why, "payload CRC-32 mismatch");
+    if (meta_crc32(s, v->off_raw, v->raw_len, v->off_payload) != r32(s + kMetaCrc))
+        return bad(why, "metadata CRC-32 mismatch (header, row metadata, tables or tile index damaged)");
     if (lossy)
         for (int64_t r = 0; r < v->rows; ++r) {
             float sc = rf32(s + v->off_scale + 4 * r);

@@ -111,9 +111,10 @@ ep_status ep_compress_device(const void* dev_w, ep_dtype src, int64_t rows, int6
 /* Free a buffer returned by ep_compress or ep_compress_device. NULL is allowed. */
 void ep_free(void* p);
 
-/* Validate a host stream (magic, version, section bounds, every table summing to 2^n, tile
- * offsets, payload CRC-32) and summarize it. Host only; no device work. EP_ECORRUPT on any
- * inconsistency. */
+/* Validate a host stream (magic, format version 2, section bounds, every table summing to 2^n,
+ * tile offsets, and three CRC-32s: the payload's, the raw plane's and the metadata's, which
+ * covers every other byte, so any single-bit corruption is refused) and summarize it. Host only;
+ * no device work. EP_ECORRUPT on any inconsistency. */
 ep_status ep_stream_info(const uint8_t* host_stream, size_t len, ep_info* out);
 
 /* Validate a host stream and copy it to the current device together with its decode tables.

@@ -84,15 +84,17 @@ static uint64_t get64(const uint8_t* p) {
 static float f32_from_bits(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
 static uint32_t bits_from_f32(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
 
-/* CRC-32 (IEEE), bit by bit from the reflected polynomial. */
-static uint32_t crc32_ieee(const uint8_t* p, size_t n) {
-    uint32_t c = 0xFFFFFFFFu;
+/* CRC-32 (IEEE), bit by bit from the reflected polynomial; crc32_more continues a register over
+   further bytes (start 0xFFFFFFFF, final value complemented), so that disjoint ranges can be
+   checked as one message. */
+static uint32_t crc32_more(uint32_t c, const uint8_t* p, size_t n) {
     for (size_t i = 0; i < n; ++i) {
         c ^= p[i];
         for (int k = 0; k < 8; ++k) c = (c & 1u) ? (c >> 1) ^ 0xEDB88320u : (c >> 1);
     }
-    return c ^ 0xFFFFFFFFu;
+    return c;
 }
+static uint32_t crc32_ieee(const uint8_t* p, size_t n) { return crc32_more(0xFFFFFFFFu, p, n) ^ 0xFFFFFFFFu; }
 
 /* ------------------------------------------------------------------------------------------ */
 /* number formats, from their definitions                                                      */
@@ -678,16 +680,34 @@ float or_select_step(const void* w, int dt, int64_t R, int64_t C, double target)
 /* 16-byte boundary: row_scale f32[R], row_qmax u16[R] (both empty in lossless mode), tables    */
 /* (per table: i16 lo, u16 S, u16 escape frequency, u16 freq[S]), tile_index u32[n_tiles + 1]   */
 /* (offsets in 4-byte units from the payload start), in the exponent-coded mode the raw plane   */
-/* u8[Rp][Cp] (offset and CRC-32 in header bytes 96 and 104), payload. [G, "Start with a tensor */
-/* round trip"]: the reported bitrate includes the metadata, so actual_bpp = 8 total / (R C).   */
+/* u8[Rp][Cp] (offset and CRC-32 in header bytes 96 and 104), payload. Format version 2: header */
+/* bytes 112..115 hold the CRC-32 of every other byte outside the payload and the raw plane.    */
+/* [G, "Start with a tensor round trip"]: the reported bitrate includes the metadata, so        */
+/* actual_bpp = 8 total / (R C).                                                                 */
 /* ------------------------------------------------------------------------------------------ */
 enum {
     H_MAGIC = 0, H_VERSION = 4, H_MODE = 6, H_DTYPE = 7, H_ROWS = 8, H_COLS = 12,
     H_TILE_ROWS = 16, H_TILE_COLS = 18, H_LANES = 20, H_PROB_BITS = 22, H_NTABLES = 23,
     H_STEP = 24, H_TARGET = 28, H_NTILES = 32, H_NESC = 36, H_OFF_SCALE = 40, H_OFF_QMAX = 48,
     H_OFF_TABLES = 56, H_OFF_INDEX = 64, H_OFF_PAYLOAD = 72, H_TOTAL = 80, H_CRC = 88,
-    H_OFF_RAW = 96, H_RAW_CRC = 104    /* exponent-coded mode only; zero in the other modes */
+    H_OFF_RAW = 96, H_RAW_CRC = 104,   /* exponent-coded mode only; zero in the other modes */
+    H_META_CRC = 112                   /* CRC-32 of all bytes but the payload, the raw plane and this field */
 };
+#define FORMAT_VERSION 2
+
+/* The metadata CRC-32 (reading R22 of the format: with the payload and raw-plane CRCs, every bit of
+   a stream is covered): the message is the stream with the payload, the raw plane (if any) and the
+   four CRC bytes at 112 left out, in stream order. */
+static uint32_t meta_crc(const uint8_t* s, uint64_t o_raw, uint64_t raw_len, uint64_t o_pl) {
+    uint32_t c = crc32_more(0xFFFFFFFFu, s, H_META_CRC);
+    uint64_t from = H_META_CRC + 4;
+    if (raw_len > 0) {
+        c = crc32_more(c, s + from, (size_t)(o_raw - from));
+        from = o_raw + raw_len;
+    }
+    c = crc32_more(c, s + from, (size_t)(o_pl - from));
+    return c ^ 0xFFFFFFFFu;
+}
 
 static size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 
@@ -713,7 +733,7 @@ static int dtype_planes(int dt) { return elem_bytes(dt); }
 static int parse_stream(const uint8_t* s, size_t len, parsed* P) {
     memset(P, 0, sizeof *P);
     if (!s || len < HEADER_BYTES) return OR_ECORRUPT;
-    if (memcmp(s + H_MAGIC, "EPK1", 4) != 0 || get16(s + H_VERSION) != 1) return OR_ECORRUPT;
+    if (memcmp(s + H_MAGIC, "EPK1", 4) != 0 || get16(s + H_VERSION) != FORMAT_VERSION) return OR_ECORRUPT;
     P->mode = s[H_MODE];
     P->dtype = s[H_DTYPE];
     P->R = get32(s + H_ROWS);
@@ -800,6 +820,7 @@ static int parse_stream(const uint8_t* s, size_t len, parsed* P) {
     }
     if (4 * prev != P->payload_len) return OR_ECORRUPT;
     if (crc32_ieee(P->payload, (size_t)P->payload_len) != get32(s + H_CRC)) return OR_ECORRUPT;
+    if (meta_crc(s, o_raw, P->raw_len, o_pl) != get32(s + H_META_CRC)) return OR_ECORRUPT;
     if (P->mode == MODE_LOSSY)
         for (int64_t r = 0; r < P->R; ++r) {
             float v = f32_from_bits(get32(P->scale_bytes + 4 * r));
@@ -856,7 +877,7 @@ static int serialize(bytes_out* o, int mode, int dt, int64_t R, int64_t C, int t
     uint8_t* s = o->buf;
     memset(s, 0, (size_t)total);
     memcpy(s + H_MAGIC, "EPK1", 4);
-    put16(s + H_VERSION, 1);
+    put16(s + H_VERSION, FORMAT_VERSION);
     s[H_MODE] = (uint8_t)mode;
     s[H_DTYPE] = (uint8_t)dt;
     put32(s + H_ROWS, (uint32_t)R);
@@ -896,6 +917,7 @@ static int serialize(bytes_out* o, int mode, int dt, int64_t R, int64_t C, int t
     }
     for (uint32_t i = 0; i <= n_tiles; ++i) put32(s + o_ix + 4 * (uint64_t)i, tile_off[i]);
     memcpy(s + o_pl, payload, (size_t)payload_len);
+    put32(s + H_META_CRC, meta_crc(s, o_raw, raw ? raw_len : 0, o_pl));
     o->len = (size_t)total;
     return OR_OK;
 }

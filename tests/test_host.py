@@ -165,6 +165,31 @@ def test_stream_info_matches_oracle():
     assert a["meta_bytes"] + a["payload_bytes"] == len(s)
 
 
+def test_every_single_bit_flip_is_rejected():
+    # the payload, raw-plane and metadata CRC-32s leave no bit of a stream unchecked; the host
+    # validator must refuse every single-bit corruption (a flipped row scale, step, shape or table
+    # window would otherwise decode to a wrong tensor without an error)
+    rng = np.random.default_rng(3)
+    w = rng.normal(0, 0.02, (16, 256)).astype(np.float32)
+    w[2, 9] = 1.0
+    streams = [ep.compress(w, 2.0)[0],
+               ep.lossless_compress(W.student_t_rowscaled(16, 256, seed=4), dtype=ep.BF16, exponent_coded=True)[0],
+               ep.lossless_compress(rng.integers(0, 40, (16, 256)).astype(np.uint8))[0]]
+    for st in streams:
+        ep.stream_info(st)
+        accepted = []
+        for i in range(len(st)):
+            for b in range(8):
+                bad = bytearray(st)
+                bad[i] ^= 1 << b
+                try:
+                    ep.stream_info(bytes(bad))
+                    accepted.append((i, b))
+                except ep.EPError as e:
+                    assert e.status == -2
+        assert not accepted, accepted[:10]
+
+
 def test_validation_errors():
     w = W.gaussian_with_outliers(64, 512, seed=3)
     s, _ = ep.compress(w, 4.0)

@@ -309,6 +309,48 @@ def header_field(s: bytes, off: int, size: int) -> int:
     return int.from_bytes(s[off:off + size], "little")
 
 
+def test_metadata_crc_covers_every_byte_but_payload_and_raw_plane(c1_stream):
+    # format version 2 (reading R22): header bytes 112..115 hold the CRC-32 of the stream with the
+    # payload, the raw plane and these four bytes left out; zlib's CRC-32 is the reference
+    _, s, _ = c1_stream
+    assert header_field(s, 4, 2) == 2
+    o_pl = header_field(s, 72, 8)
+    assert zlib.crc32(s[:112] + s[116:o_pl]) == header_field(s, 112, 4)
+    x = W.student_t_rowscaled(32, 512, seed=1)
+    se, _ = oracle.compress(x, dtype=oracle.BF16, mode=oracle.LOSSLESS_EXP)
+    o_raw, o_pl = header_field(se, 96, 8), header_field(se, 72, 8)
+    raw_len = 32 * 512                                # Rp x Cp of the padded matrix
+    assert zlib.crc32(se[:112] + se[116:o_raw] + se[o_raw + raw_len:o_pl]) == header_field(se, 112, 4)
+    old = bytearray(s)
+    old[4] = 1                                        # a version-1 header is refused
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.info(bytes(old))
+    assert e.value.rc == -2
+
+
+def test_every_single_bit_flip_is_rejected():
+    # three CRC-32s (payload, raw plane, metadata) leave no bit of a stream unchecked
+    rng = np.random.default_rng(3)
+    w = rng.normal(0, 0.02, (16, 256)).astype(np.float32)
+    w[2, 9] = 1.0                                     # an escape
+    streams = [oracle.compress(w, 2.0)[0],
+               oracle.compress(W.student_t_rowscaled(16, 256, seed=4), dtype=oracle.BF16, mode=oracle.LOSSLESS_EXP)[0],
+               oracle.compress(rng.integers(0, 40, (16, 256)).astype(np.uint8), dtype=oracle.U8, mode=oracle.LOSSLESS)[0]]
+    for st in streams:
+        oracle.info(st)
+        accepted = []
+        for i in range(len(st)):
+            for b in range(8):
+                bad = bytearray(st)
+                bad[i] ^= 1 << b
+                try:
+                    oracle.info(bytes(bad))
+                    accepted.append((i, b))
+                except oracle.OracleError:
+                    pass
+        assert not accepted, accepted[:10]
+
+
 def exp_cases():
     cases = {k: v for k, v in lossless_cases().items() if v[1] == oracle.BF16}
     rng = np.random.default_rng(11)
