@@ -234,7 +234,7 @@ def test_grouped_decode_matches_single():
 
 
 def test_device_flag_on_inconsistent_stream():
-    """A stream that passes host validation (CRC recomputed) but whose lane state was altered:
+    """A stream that passes host validation (CRCs recomputed) but whose lane state was altered:
     the kernel's bounded reads keep it in range and the final-state check raises the flag."""
     import zlib
     w = W.gaussian_with_outliers(64, 512, seed=8)
@@ -243,6 +243,7 @@ def test_device_flag_on_inconsistent_stream():
     bad = bytearray(s)
     bad[off_pay + 4 * 3 + 1] ^= 0x10                       # tile 0, lane 3 state
     bad[88:92] = zlib.crc32(bytes(bad[off_pay:])).to_bytes(4, "little")
+    bad[112:116] = zlib.crc32(bytes(bad[:112] + bad[116:off_pay])).to_bytes(4, "little")   # the header changed
     h = ep.upload(bytes(bad))
     h.decompress(torch.bfloat16)
     with pytest.raises(ep.EPError) as e:
