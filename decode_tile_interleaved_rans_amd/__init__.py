@@ -368,14 +368,15 @@ class CompressedLinear:
         save(path, self.stream, self.bias)
 
     @classmethod
-    def load(cls, path):
-        """Rebuild a layer from a file written by save(); the bias goes to the current GPU."""
+    def load(cls, path, compute: str = "bf16"):
+        """Rebuild a layer from a file written by save(); the bias goes to the current GPU. The
+        compute mode is a choice of the forward, not part of the artifact."""
         stream, bias = load(path)
         b = None
         if bias is not None:
             torch = _torch()
             b = torch.from_numpy(bias.view("int16")).view(torch.bfloat16).cuda()
-        return cls(stream, b)
+        return cls(stream, b, compute)
 
     def forward(self, x, stream=None):
         torch = _torch()

@@ -159,19 +159,22 @@ def test_compressed_linear_save_and_reload_in_a_fresh_process(tmp_path):
     layer = ep.CompressedLinear.from_linear(lin, 4.0)
     x = bf16_tensor(W.activations(24, 768, 77))
     y = layer(x.cuda())
+    y8 = ep.CompressedLinear(layer.stream, layer.bias, "fp8")(x.cuda())
     torch.cuda.synchronize()
     path = tmp_path / "layer.npz"
     layer.save(path)
     np.save(tmp_path / "x.npy", W.activations(24, 768, 77))
-    out = tmp_path / "y.npy"
+    out, out8 = tmp_path / "y.npy", tmp_path / "y8.npy"
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     code = ("import sys, numpy as np, torch; sys.path.insert(0, %r); import decode_tile_interleaved_rans_amd as ep; "
-            "layer = ep.CompressedLinear.load(%r); "
+            "layer = ep.CompressedLinear.load(%r); layer8 = ep.CompressedLinear.load(%r, compute='fp8'); "
             "x = torch.from_numpy(np.load(%r).view(np.int16)).view(torch.bfloat16).cuda(); "
-            "y = layer(x); torch.cuda.synchronize(); np.save(%r, y.cpu().view(torch.int16).numpy())"
-            ) % (root, str(path), str(tmp_path / "x.npy"), str(out))
+            "y = layer(x); y8 = layer8(x); torch.cuda.synchronize(); "
+            "np.save(%r, y.cpu().view(torch.int16).numpy()); np.save(%r, y8.cpu().view(torch.int16).numpy())"
+            ) % (root, str(path), str(path), str(tmp_path / "x.npy"), str(out), str(out8))
     subprocess.run([sys.executable, "-c", code], check=True, timeout=300)
     assert np.array_equal(np.load(out), y.cpu().view(torch.int16).numpy())
+    assert np.array_equal(np.load(out8), y8.cpu().view(torch.int16).numpy())
 
 
 # ---------------------------------------------------------------- FP8 forward
