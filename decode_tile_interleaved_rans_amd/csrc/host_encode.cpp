@@ -29,6 +29,8 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <exception>
+#include <mutex>
 #include <thread>
 
 #include "ep_internal.h"
@@ -38,6 +40,9 @@ namespace {
 
 
 // ------------------------------------------------------------------------------ threading
+// Items 0..n-1 over up to `threads` workers taking the next item from a shared counter. An
+// exception in a worker stops the others at their next item and is rethrown here after the join;
+// if a thread cannot be started, the workers already running (or this thread) do all the items.
 template <class F>
 void parallel_for(int64_t n, int threads, F&& fn) {
     if (n <= 0) return;
@@ -47,13 +52,28 @@ void parallel_for(int64_t n, int threads, F&& fn) {
         return;
     }
     std::atomic<int64_t> next{0};
+    std::atomic<bool> failed{false};
+    std::exception_ptr error;
+    std::mutex error_mu;
+    auto work = [&](int k) {
+        try {
+            for (int64_t i = next.fetch_add(1); i < n && !failed.load(); i = next.fetch_add(1)) fn(i, k);
+        } catch (...) {
+            std::lock_guard<std::mutex> g(error_mu);
+            if (!error) error = std::current_exception();
+            failed = true;
+        }
+    };
     std::vector<std::thread> pool;
     pool.reserve(t);
-    for (int k = 0; k < t; ++k)
-        pool.emplace_back([&, k] {
-            for (int64_t i = next.fetch_add(1); i < n; i = next.fetch_add(1)) fn(i, k);
-        });
+    try {
+        for (int k = 0; k < t; ++k) pool.emplace_back(work, k);
+    } catch (...) {
+        // no more threads: the running ones share the remaining items
+    }
+    if (pool.empty()) work(0);
     for (auto& th : pool) th.join();
+    if (error) std::rethrow_exception(error);
 }
 
 // ------------------------------------------------------------------------------ element access
