@@ -32,10 +32,12 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <mutex>
 #include <set>
 #include <type_traits>
+#include <utility>
 
 #include "kernels.h"
 
@@ -831,30 +833,34 @@ __global__ __launch_bounds__(256) void gemv_finish(const float* yacc, const uint
     y[i] = (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v, 0.0f}, bf16x2)) & 0xFFFFu);
 }
 
-int device_cus() {
-    static int cache[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cache[dev]) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) v = 0;
-        cache[dev] = v > 0 ? v : 256;
-    }
-    return cache[dev];
-}
 
-// Allow a kernel the full 160 KiB of LDS once.
+// Allow a kernel the full 160 KiB of LDS, once per device.
 hipError_t allow_lds(const void* kernel) {
     static std::mutex mu;
-    static std::set<const void*> done;
+    static std::set<std::pair<int, const void*>> done;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
     std::lock_guard<std::mutex> g(mu);
-    if (done.count(kernel)) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e == hipSuccess) done.insert(kernel);
+    if (done.count({dev, kernel})) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e == hipSuccess) done.insert({dev, kernel});
     return e;
 }
 
 }  // namespace
+
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
 
 hipError_t launch_group(const MatDesc* mats, int count, hipStream_t stream) {
     if (count <= 0) return hipSuccess;

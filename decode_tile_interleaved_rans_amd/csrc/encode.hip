@@ -536,9 +536,11 @@ struct EncoderScratch {
         payload, crc;
 };
 
+constexpr int kMaxDevices = 64;
+
 EncoderScratch& encoder_scratch(int device) {
-    static EncoderScratch per_device[64];
-    return per_device[device & 63];
+    static EncoderScratch per_device[kMaxDevices];
+    return per_device[device];
 }
 
 #define EP_HIP(call)                                                         \
@@ -766,6 +768,10 @@ ep_status encode_lossy_device(const void* dev_w, int dt, int64_t rows, int64_t c
     if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) {
         *why = std::string("hipGetDevice: ") + hipGetErrorString(e);
         return EP_EHIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        *why = "the device encoder supports device ordinals below 64";
+        return EP_EUNSUPPORTED;
     }
     EncoderScratch& X = encoder_scratch(dev);
     std::lock_guard<std::mutex> lock(X.mu);

@@ -25,6 +25,7 @@
 #include <cstdint>
 
 #include "gemm.h"
+#include "kernels.h"
 
 namespace ep {
 namespace {
@@ -646,18 +647,6 @@ hipError_t launch_skinny_f8(const GemmF8Args& g, hipStream_t stream) {
     return hipGetLastError();
 }
 
-int gemm_device_cus() {
-    static int cache[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cache[dev]) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) v = 0;
-        cache[dev] = v > 0 ? v : 256;
-    }
-    return cache[dev];
-}
-
 template <int BM, int BN, int WGM, int WGN, int PF>
 hipError_t launch_tiled(const GemmArgs& g, hipStream_t stream) {
     const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
@@ -683,9 +672,9 @@ hipError_t launch_skinny(const GemmArgs& g, hipStream_t stream) {
 hipError_t launch_gemm_f8(const GemmF8Args& g, hipStream_t stream) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
     const long tiles256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
-    if (tiles256 >= gemm_device_cus()) return launch_f8<256, 256, 4, 4>(g, stream);
+    if (tiles256 >= device_cus()) return launch_f8<256, 256, 4, 4>(g, stream);
     const long tiles128 = (long)((g.M + 127) / 128) * ((g.N + 127) / 128);
-    if (tiles128 >= 2L * gemm_device_cus()) return launch_f8<128, 128, 2, 2>(g, stream);
+    if (tiles128 >= 2L * device_cus()) return launch_f8<128, 128, 2, 2>(g, stream);
     if (g.M <= 16) return launch_skinny_f8<1>(g, stream);
     if (g.M <= 32) return launch_skinny_f8<2>(g, stream);
     if (g.M <= 64) return launch_skinny_f8<4>(g, stream);
@@ -712,9 +701,9 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
     if (g.M <= 32) return launch_skinny<2>(g, stream);
     if (g.M <= 64) return launch_skinny<4>(g, stream);
     const long tiles256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
-    if (tiles256 >= gemm_device_cus()) return launch_dma<256, 256, 4, 4>(g, stream);
+    if (tiles256 >= device_cus()) return launch_dma<256, 256, 4, 4>(g, stream);
     const long tiles128 = (long)((g.M + 127) / 128) * ((g.N + 127) / 128);
-    if (tiles128 >= 2L * gemm_device_cus()) return launch_tiled<128, 128, 2, 2, kPrefetch>(g, stream);
+    if (tiles128 >= 2L * device_cus()) return launch_tiled<128, 128, 2, 2, kPrefetch>(g, stream);
     return launch_tiled<64, 64, 2, 2, kPrefetch>(g, stream);
 }
 

@@ -75,6 +75,9 @@ __host__ __device__ inline size_t lds_table_bytes(int n_tables, int prob_bits, b
     return table_blob_bytes(lossy ? n_tables - 1 : n_tables, prob_bits);
 }
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cus();
+
 // Launch one grouped decode of up to kMaxGroup matrices (lossy and lossless may be mixed).
 hipError_t launch_group(const MatDesc* mats, int count, hipStream_t stream);
 
