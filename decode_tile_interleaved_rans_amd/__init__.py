@@ -217,6 +217,19 @@ def load(path):
     return stream, bias
 
 
+def _need(t, name: str, dtype, shape=None, min_numel: int | None = None):
+    """Argument check before a device pointer crosses the C ABI: the kernels trust sizes, so a
+    tensor of the wrong shape, dtype, layout or device would be read or written out of bounds."""
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous tensor on the GPU")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} needs at least {min_numel} elements")
+
+
 # ------------------------------------------------------------------------------------ device side
 class Handle:
     """A validated stream resident on the current GPU."""
@@ -240,6 +253,8 @@ class Handle:
             raise ValueError("use decode_symbols_into for int16 outputs")
         if tuple(out.shape) != self.shape or not out.is_contiguous() or not out.is_cuda:
             raise ValueError(f"output must be a contiguous CUDA tensor of shape {self.shape}")
+        if row_scale is not None:
+            _need(row_scale, "row_scale", torch.float32, min_numel=self.shape[0])
         sp = C.c_void_p(row_scale.data_ptr()) if row_scale is not None else None
         _check(lib().ep_decompress(self._h, code, C.c_void_p(out.data_ptr()), sp, _stream_ptr(stream)),
                "ep_decompress")
@@ -294,7 +309,14 @@ def decompress(stream: bytes, dtype=None, device: str = "cuda"):
 
 def decompress_many(handles, outs, scales=None, stream=None):
     """One grouped call over several uploaded matrices."""
+    torch = _torch()
     n = len(handles)
+    if len(outs) != n or (scales is not None and len(scales) != n):
+        raise ValueError("handles, outs and scales must have the same length")
+    for i, (h, o) in enumerate(zip(handles, outs)):
+        _need(o, f"outs[{i}]", o.dtype, shape=h.shape)
+        if scales is not None and scales[i] is not None:
+            _need(scales[i], f"scales[{i}]", torch.float32, min_numel=h.shape[0])
     hs = (C.c_void_p * n)(*[h.ptr.value for h in handles])
     cts = (C.c_int * n)(*[_dtype_code(o.dtype) for o in outs])
     os_ = (C.c_void_p * n)(*[o.data_ptr() for o in outs])
@@ -307,6 +329,8 @@ def gemm_bf16(x, w, stream=None):
     torch = _torch()
     M, K = x.shape
     N = w.shape[0]
+    _need(x, "x", torch.bfloat16)
+    _need(w, "w", torch.bfloat16, shape=(N, K))
     y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _check(lib().ep_gemm_bf16(C.c_void_p(x.data_ptr()), C.c_void_p(w.data_ptr()), M, N, K, C.c_void_p(y.data_ptr()),
                               _stream_ptr(stream)), "ep_gemm_bf16")
@@ -317,6 +341,7 @@ def quantize_rows_fp8(x, stream=None):
     """Per-row FP8 E4M3 codes of BF16 rows and their fp32 scales (x = codes * scale[row])."""
     torch = _torch()
     M, K = x.shape
+    _need(x, "x", torch.bfloat16)
     q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     sc = torch.empty(M, dtype=torch.float32, device=x.device)
     _check(lib().ep_quantize_rows_fp8(C.c_void_p(x.data_ptr()), M, K, C.c_void_p(q.data_ptr()),
@@ -329,6 +354,12 @@ def gemm_fp8(xq, xs, wq, ws, bias=None, stream=None):
     torch = _torch()
     M, K = xq.shape
     N = wq.shape[0]
+    _need(xq, "xq", torch.uint8)
+    _need(wq, "wq", torch.uint8, shape=(N, K))
+    _need(xs, "xs", torch.float32, shape=(M,))
+    _need(ws, "ws", torch.float32, shape=(N,))
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, shape=(N,))
     y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
     bp = C.c_void_p(bias.data_ptr()) if bias is not None else None
     _check(lib().ep_gemm_fp8(C.c_void_p(xq.data_ptr()), C.c_void_p(xs.data_ptr()), C.c_void_p(wq.data_ptr()),
@@ -381,6 +412,10 @@ class CompressedLinear:
     def forward(self, x, stream=None):
         torch = _torch()
         shp = x.shape
+        if shp[-1] != self.in_features or not x.is_cuda:
+            raise ValueError(f"input must be a GPU tensor with last dimension {self.in_features}, got {tuple(shp)}")
+        if self.bias is not None:
+            _need(self.bias, "bias", torch.bfloat16, shape=(self.out_features,))
         x2 = x.reshape(-1, shp[-1]).to(torch.bfloat16).contiguous()
         y = torch.empty((x2.shape[0], self.out_features), dtype=torch.bfloat16, device=x.device)
         bp = C.c_void_p(self.bias.data_ptr()) if self.bias is not None else None

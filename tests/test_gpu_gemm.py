@@ -275,3 +275,32 @@ def test_linear_forward_fp8_prefill_sampled_rows():
     wq, ws = oracle.decompress(s, oracle.F8E4M3, n_threads=16)
     xq, xs = oracle.quantize_rows_e4m3(xb[rows])
     assert rel_l2(y[rows].float().cpu().numpy(), fp8_reference(xq, xs, wq, ws)) < 3e-3
+
+
+def test_binding_refuses_mismatched_tensors():
+    """The kernels trust the sizes they are given, so the binding checks every tensor before its
+    pointer crosses the C ABI: wrong shapes, dtypes or layouts raise before anything is launched."""
+    w = W.student_t(64, 256, 21)
+    s, _ = ep.compress(w, 4.0, dtype=ep.BF16)
+    layer = ep.CompressedLinear(s)
+    with pytest.raises(ValueError):
+        layer(torch.zeros((4, 255), dtype=torch.bfloat16, device="cuda"))          # wrong in_features
+    x = torch.zeros((32, 256), dtype=torch.bfloat16, device="cuda")
+    wt = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        ep.gemm_bf16(x, torch.zeros((64, 128), dtype=torch.bfloat16, device="cuda"))  # K mismatch
+    with pytest.raises(ValueError):
+        ep.gemm_bf16(x, wt.float())                                                  # wrong dtype
+    with pytest.raises(ValueError):
+        ep.gemm_bf16(x.t().contiguous().t(), wt)                                      # not row-major
+    xq, xs = ep.quantize_rows_fp8(x)
+    wq, ws = ep.quantize_rows_fp8(wt)
+    with pytest.raises(ValueError):
+        ep.gemm_fp8(xq, xs[:16].contiguous(), wq, ws)                               # short scales
+    h = ep.upload(s)
+    with pytest.raises(ValueError):
+        ep.decompress_many([h], [torch.empty((64, 128), dtype=torch.bfloat16, device="cuda")])
+    with pytest.raises(ValueError):
+        h.decompress_into(torch.empty((64, 256), dtype=torch.float8_e4m3fn, device="cuda"),
+                          torch.empty(8, dtype=torch.float32, device="cuda"))         # short row scales
+    torch.cuda.synchronize()
