@@ -272,7 +272,7 @@ ep_status ep_upload(const uint8_t* host_stream, size_t len, void* hip_stream, ep
         if (e == hipSuccess) e = hipMemsetAsync(h->dev + h->err_off, 0, 256, s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         if (e != hipSuccess) {
-            hipFree(h->dev);
+            (void)hipFree(h->dev);
             return hip_fail(e, "copying the stream to the device");
         }
         // the view's pointers referred to the caller's bytes: drop them
