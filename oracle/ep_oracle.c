@@ -901,7 +901,7 @@ static int serialize(bytes_out* o, int mode, int dt, int64_t R, int64_t C, int t
     if (raw) {
         put64(s + H_OFF_RAW, o_raw);
         put32(s + H_RAW_CRC, crc32_ieee(raw, (size_t)raw_len));
-        memcpy(s + o_raw, raw, (size_t)raw_len);
+        if (raw_len) memcpy(s + o_raw, raw, (size_t)raw_len);
     }
     for (uint64_t r = 0; r < rows_meta; ++r) {
         put32(s + o_sc + 4 * r, bits_from_f32(scale[r]));
@@ -916,7 +916,7 @@ static int serialize(bytes_out* o, int mode, int dt, int64_t R, int64_t C, int t
         for (int32_t k = 0; k < S[t]; ++k, pos += 2) put16(s + pos, f[t][k]);
     }
     for (uint32_t i = 0; i <= n_tiles; ++i) put32(s + o_ix + 4 * (uint64_t)i, tile_off[i]);
-    memcpy(s + o_pl, payload, (size_t)payload_len);
+    if (payload_len) memcpy(s + o_pl, payload, (size_t)payload_len);   /* an empty matrix has no payload */
     put32(s + H_META_CRC, meta_crc(s, o_raw, raw ? raw_len : 0, o_pl));
     o->len = (size_t)total;
     return OR_OK;
