@@ -89,6 +89,26 @@ def test_c2_student_t_4096(target):
     assert_parity(s, names=("bf16", "f16"))
 
 
+def test_c2_bench_step_as_one_grouped_launch():
+    # the launch the benchmark times: the 4096^2 matrix at 3.0 / 4.0 / 4.5 bpp to BF16 and FP16
+    # plus its lossless BF16 stream, seven matrices in one grouped decode, each output bit-exact
+    w = W.student_t_rowscaled(4096, 4096, 2)
+    items = []
+    for t in (3.0, 4.0, 4.5):
+        s, _ = ep.compress(w, t, dtype=ep.BF16)
+        items += [(s, torch.bfloat16, oracle.BF16), (s, torch.float16, oracle.F16)]
+    ll, _ = ep.lossless_compress(w, dtype=ep.BF16)
+    items.append((ll, torch.bfloat16, None))
+    hs = [ep.upload(s) for s, _, _ in items]
+    outs = [torch.empty((4096, 4096), dtype=tdt, device="cuda") for _, tdt, _ in items]
+    ep.decompress_many(hs, outs)
+    torch.cuda.synchronize()
+    for h, (s, _, odt), o in zip(hs, items, outs):
+        h.check()
+        want = w if odt is None else oracle.decompress(s, odt, n_threads=16)[0]
+        assert np.array_equal(bits(o), want), mismatch_report("bench-step output", bits(o), want)
+
+
 def test_c2_lossless_bf16_roundtrip():
     w = W.student_t_rowscaled(4096, 4096, 2)
     s, bpp = ep.lossless_compress(w, dtype=ep.BF16)

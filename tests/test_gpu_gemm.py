@@ -111,6 +111,13 @@ def test_linear_forward_prefill_sampled_rows():
     rows = np.random.default_rng(4).choice(M, 32, replace=False)
     ref = W.bf16_bits_to_f32(xb[rows]) @ w_hat.T
     assert rel_l2(y[rows].float().cpu().numpy(), ref) < 2e-2
+    # the token counts the benchmark also times on this weight: M = 1 (fused matrix-vector
+    # kernel) and M = 16 (decode-once slice + skinny GEMM)
+    for m in (1, 16):
+        ym = layer(X[:m].contiguous())
+        torch.cuda.synchronize()
+        refm = W.bf16_bits_to_f32(xb[:m]) @ w_hat.T
+        assert rel_l2(ym.float().cpu().numpy(), refm) < 2e-2, m
 
 
 def test_c5_linear_forward_token_counts():
