@@ -37,6 +37,15 @@ def test_library_exports_every_declared_symbol():
     assert b"gfx950" in L.ep_version()
 
 
+def test_header_is_plain_c():
+    # the C ABI header compiles as C11 on its own, warnings as errors (no C++ constructs leak)
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-x", "c",
+                        os.path.join(root, "include", "entropack.h")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def oracle_and_product(w, target, dtype=None, mode=0, prob_bits=12, tile_rows=16, threads=4):
     so, bo = oracle.compress(w, target, dtype=dtype, mode=mode, prob_bits=prob_bits, tile_rows=tile_rows)
     sp, bp = ep.compress(w, target, dtype=dtype, mode=mode, prob_bits=prob_bits, tile_rows=tile_rows,
