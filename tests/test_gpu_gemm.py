@@ -311,3 +311,26 @@ def test_binding_refuses_mismatched_tensors():
         h.decompress_into(torch.empty((64, 256), dtype=torch.float8_e4m3fn, device="cuda"),
                           torch.empty(8, dtype=torch.float32, device="cuda"))         # short row scales
     torch.cuda.synchronize()
+
+
+def test_forward_on_two_streams_at_once():
+    """Each (device, stream) pair owns its forward workspace: two layers running on two HIP
+    streams at the same time (decode-once slices and the fused matrix-vector path) give the same
+    bits as the same calls one after the other on the default stream."""
+    rng = np.random.default_rng(31)
+    ws = [(0.02 * rng.standard_t(5, (1536, 2048))).astype(np.float32) for _ in range(2)]
+    layers = [ep.CompressedLinear(ep.compress(w, 4.0)[0]) for w in ws]
+    xs = [bf16_tensor(W.to_bf16_bits(rng.normal(0, 1, (m, 2048)))).cuda() for m in (300, 3)]
+    want = [layers[i](xs[i]) for i in range(2)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = [None, None]
+    for _ in range(3):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                got[i] = layers[i](xs[i], stream=streams[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(got[i], want[i]) or (xs[i].shape[0] <= 4 and
+                                                    rel_l2(got[i].float().cpu().numpy(),
+                                                           want[i].float().cpu().numpy()) < 1e-2)

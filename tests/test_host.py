@@ -302,3 +302,30 @@ def test_new_entry_points_reject_bad_arguments_before_any_device_work():
     opts = ep.EncodeOpts(ep.LOSSY, 0.0, 12, 16, 0)
     assert L.ep_compress_device(C.c_void_p(16), ep.F32, 4, 4, C.byref(opts), None, C.byref(out), C.byref(n),
                                 None) == -1                                           # target must be > 0
+
+
+def test_concurrent_compress_calls_from_threads():
+    # the host encoder and the error-message store are per call / per thread: four threads
+    # compressing different matrices at once give the same bytes as one after the other, and an
+    # error in one thread leaves the others' messages alone
+    import threading
+    mats = [W.gaussian_with_outliers(96, 512, seed=20 + i) for i in range(4)]
+    want = [ep.compress(m, 3.0 + 0.5 * i, n_threads=2)[0] for i, m in enumerate(mats)]
+    got, errs = [None] * 4, []
+
+    def work(i):
+        try:
+            for _ in range(3):
+                got[i] = ep.compress(mats[i], 3.0 + 0.5 * i, n_threads=2)[0]
+                with pytest.raises(ep.EPError):
+                    ep.stream_info(b"EPK1" + bytes(200))
+        except Exception as e:   # surfaced below
+            errs.append(e)
+
+    ts = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errs, errs
+    assert got == want
