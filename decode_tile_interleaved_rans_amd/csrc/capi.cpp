@@ -172,8 +172,21 @@ bool container_ok(const ep_handle* h, int ct) {
     return ct == EP_BF16 || ct == EP_F16 || ct == EP_F8E4M3 || ct == EP_I8;
 }
 
+// A handle's device copy lives on the device it was uploaded to; a kernel on another device must
+// not be handed its pointers.
+ep_status on_its_device(const ep_handle* h) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev != h->device)
+        return fail(EP_EINVAL, "the handle was uploaded to device " + std::to_string(h->device) + " but device " +
+                                   std::to_string(dev) + " is current");
+    return EP_OK;
+}
+
 ep_status check_decode_args(const ep_handle* h, ep_dtype ct, void* out, float* scale) {
     if (!h) return fail(EP_EINVAL, "null handle");
+    if (ep_status st = on_its_device(h); st != EP_OK) return st;
     if (!container_ok(h, ct))
         return fail(EP_EUNSUPPORTED, h->view.mode != EP_MODE_LOSSY_E8
                                          ? "a lossless stream decodes only to its own dtype"
@@ -327,6 +340,7 @@ ep_status ep_decompress_many(const ep_handle* const* hs, const ep_dtype* contain
 ep_status ep_decode_symbols(const ep_handle* h, int16_t* dev_q, void* hip_stream) {
     return guarded([&]() -> ep_status {
         if (!h) return fail(EP_EINVAL, "null handle");
+        if (ep_status st = on_its_device(h); st != EP_OK) return st;
         if (h->view.mode != EP_MODE_LOSSY_E8) return fail(EP_EUNSUPPORTED, "symbols exist only for lossy streams");
         if (!dev_q && h->view.rows * h->view.cols > 0) return fail(EP_EINVAL, "null output pointer");
         std::vector<ep::MatDesc> one{desc_for(h, ep::CT_Q16, dev_q, nullptr)};
@@ -381,6 +395,7 @@ ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, co
     return guarded([&]() -> ep_status {
         constexpr size_t kSliceBytes = 128u << 20;
         if (!w) return fail(EP_EINVAL, "null handle");
+        if (ep_status st = on_its_device(w); st != EP_OK) return st;
         if (w->view.mode != EP_MODE_LOSSY_E8) return fail(EP_EUNSUPPORTED, "the linear forward takes a lossy stream");
         const int64_t N = w->view.rows, K = w->view.cols;
         if (M < 0) return fail(EP_EINVAL, "negative M");
@@ -504,6 +519,7 @@ ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M
     return guarded([&]() -> ep_status {
         constexpr size_t kSliceBytes = 128u << 20;
         if (!w) return fail(EP_EINVAL, "null handle");
+        if (ep_status st = on_its_device(w); st != EP_OK) return st;
         if (w->view.mode != EP_MODE_LOSSY_E8) return fail(EP_EUNSUPPORTED, "the linear forward takes a lossy stream");
         const int64_t N = w->view.rows, K = w->view.cols;
         if (M < 0) return fail(EP_EINVAL, "negative M");

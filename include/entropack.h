@@ -23,6 +23,8 @@
  *   - Ownership: buffers returned by ep_compress belong to the caller and are freed with
  *     ep_free; ep_handle objects belong to the caller and are freed with ep_release; device
  *     outputs are always allocated by the caller.
+ *   - Devices: a handle lives on the device that was current at ep_upload; calls that launch
+ *     work for it return EP_EINVAL when another device is current.
  *   - Thread safety: distinct handles may be used from distinct threads; a handle is immutable
  *     after ep_upload except for its device error flag.
  */
