@@ -164,6 +164,7 @@ def compress_device(w, target_bpp: float = 4.0, *, prob_bits: int = 12, tile_row
     t = w.detach().contiguous()
     if not t.is_cuda:
         raise ValueError("compress_device takes a tensor in device memory")
+    _need(t, "w", t.dtype)
     R, Cc = t.shape
     opts = EncodeOpts(LOSSY, float(target_bpp), prob_bits, tile_rows, 0)
     out = C.POINTER(C.c_uint8)()
@@ -222,6 +223,8 @@ def _need(t, name: str, dtype, shape=None, min_numel: int | None = None):
     tensor of the wrong shape, dtype, layout or device would be read or written out of bounds."""
     if not (t.is_cuda and t.is_contiguous()):
         raise ValueError(f"{name} must be a contiguous tensor on the GPU")
+    if t.device.index != _torch().cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, but the current device is cuda:{_torch().cuda.current_device()}")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
