@@ -267,6 +267,10 @@ ep_status ep_upload(const uint8_t* host_stream, size_t len, void* hip_stream, ep
         ep_status st = ep::parse_stream(host_stream, len, &h->view, &why);
         if (st != EP_OK) return fail(st, why);
         ep::fill_info(h->view, &h->info);
+        // the decode kernels address a stream's tile payload through one buffer resource, whose
+        // size field is 32 bits
+        if (h->view.payload_len >= (1ull << 32))
+            return fail(EP_ERANGE, "tile payload of 4 GiB or more: split the matrix into several streams");
         std::vector<uint8_t> blob = build_tables(h->view);
         h->stream_off = 0;
         h->tables_off = up(len, 256);

@@ -121,7 +121,9 @@ ep_status ep_stream_info(const uint8_t* host_stream, size_t len, ep_info* out);
 
 /* Validate a host stream and copy it to the current device together with its decode tables.
  * Synchronizes hip_stream before returning (the host buffer may be freed afterwards).
- * *out receives the handle. Errors: EP_ECORRUPT, EP_ENOMEM, EP_EHIP. */
+ * *out receives the handle. Errors: EP_ECORRUPT, EP_ERANGE (a tile payload of 4 GiB or more,
+ * beyond the decoder's 32-bit payload addressing: code such a matrix as several streams),
+ * EP_ENOMEM, EP_EHIP. */
 ep_status ep_upload(const uint8_t* host_stream, size_t len, void* hip_stream, ep_handle** out);
 
 /* Summary of an uploaded stream (same fields as ep_stream_info). */
