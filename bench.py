@@ -410,6 +410,10 @@ def main():
     ap.add_argument("--gemm-reps", type=int, default=15, help="timed reps per variant in the GEMM measurement")
     ap.add_argument("--encoder-only", action="store_true",
                     help="profiling aid: run only the encoder comparison and print its JSON")
+    ap.add_argument("--dit-only", action="store_true",
+                    help="profiling aid: run only the full-model step of the DiT-like denoiser and print its JSON")
+    ap.add_argument("--mixed-only", action="store_true",
+                    help="profiling aid: run only the 64-matrix mixed-rate set and print its JSON")
     ap.add_argument("--no-dit", action="store_true",
                     help="skip the full-model decode step of the DiT-like denoiser (5.31 G weights)")
     ap.add_argument("--no-mixed", action="store_true", help="skip the 64-matrix mixed-rate set")
@@ -436,6 +440,12 @@ def main():
         return
     if args.encoder_only:
         print(json.dumps(encoder_section(torch, ep)), flush=True)
+        return
+    if args.dit_only:
+        print(json.dumps(dit_model_section(torch, ep)), flush=True)
+        return
+    if args.mixed_only:
+        print(json.dumps(mixed_section(torch, ep)), flush=True)
         return
     items, (R, C) = c2_items()
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16}
