@@ -6,8 +6,9 @@
 // both operand tiles (rows x 64 K of X and of W, K contiguous, as the MFMA wants 8 consecutive K
 // per lane) are staged in LDS, double-buffered; global loads go through buffer resources (rows
 // past the matrix and K past the end read as zero). Each wave computes its (BM / WGM) x
-// (BN / WGN) part as MFMA tiles. 256 x 256 tiles with 16 waves (gemm_dma, 16 x 16 MFMA tiles,
-// 4% faster than 32 x 32 ones with the same bits out) load straight from global memory into LDS;
+// (BN / WGN) part as MFMA tiles. 256 x 256 tiles with 8 waves of 128 x 64 (gemm_dma, 16 x 16 MFMA
+// tiles: 4% faster than 32 x 32 ones, and 8 waves 2% faster than 16 of 64 x 64, with the same bits
+// out) load straight from global memory into LDS;
 // 128 x 128 and 64 x 64 tiles with 4 waves (gemm_nt, 32 x 32 MFMA tiles) go through two register
 // stages and a padded LDS layout. Tile choice (launch_gemm): 256 x 256 when every CU
 // gets a block, 128 x 128 when every CU gets two, else 64 x 64; the skinny kernel streams W
@@ -705,7 +706,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
     if (g.M <= 32) return launch_skinny<2>(g, stream);
     if (g.M <= 64) return launch_skinny<4>(g, stream);
     const long tiles256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
-    if (tiles256 >= device_cus()) return launch_dma<256, 256, 4, 4>(g, stream);
+    if (tiles256 >= device_cus()) return launch_dma<256, 256, 2, 4>(g, stream);
     const long tiles128 = (long)((g.M + 127) / 128) * ((g.N + 127) / 128);
     if (tiles128 >= 2L * device_cus()) return launch_tiled<128, 128, 2, 2, kPrefetch>(g, stream);
     return launch_tiled<64, 64, 2, 2, kPrefetch>(g, stream);
