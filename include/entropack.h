@@ -26,7 +26,10 @@
  *   - Devices: a handle lives on the device that was current at ep_upload; calls that launch
  *     work for it return EP_EINVAL when another device is current.
  *   - Thread safety: distinct handles may be used from distinct threads; a handle is immutable
- *     after ep_upload except for its device error flag.
+ *     after ep_upload except for its device error flag. The library's own shared state (per-device
+ *     kernel attributes and CU counts, the linear forwards' workspaces) is guarded internally;
+ *     each (device, stream) pair has its own workspace, so forwards on distinct streams may run
+ *     concurrently, and forwards on one stream are ordered by that stream.
  */
 #ifndef ENTROPACK_H
 #define ENTROPACK_H
