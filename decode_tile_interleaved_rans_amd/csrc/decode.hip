@@ -568,7 +568,9 @@ __device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Til
 #pragma unroll
                     for (int c = 0; c < C; ++c) {
                         const uint32_t w = take_words(t[c], esc[c]);
-                        if (esc[c]) q[c][j] = (float)(2 * (int32_t)(int16_t)w + b[c]);
+                        // the doubled coordinate is an int16 on every path (table values
+                        // wrap the same way when the tables are built)
+                        if (esc[c]) q[c][j] = (float)(int32_t)(int16_t)(2 * (int32_t)(int16_t)w + b[c]);
                     }
                 }
             }

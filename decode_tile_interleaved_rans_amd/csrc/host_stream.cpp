@@ -150,7 +150,10 @@ ep_status parse_stream(const uint8_t* s, size_t len, StreamView* v, std::string*
         if (T.width < 1 || T.width > (lossy ? 255 : 256) || pos + 2 * (uint64_t)T.width > v->off_index)
             return bad(why, "table window width out of range");
         if (!lossy && (T.lo != 0 || T.width != 256 || esc != 0)) return bad(why, "lossless tables cover 0..255 without escape");
-        if (lossy && T.lo + T.width - 1 > 32767) return bad(why, "table window beyond int16");
+        // a coordinate x must give a doubled coordinate 2x + b that fits int16 (the range the
+        // encoder's step bound keeps every value in)
+        if (lossy && t > 0 && (T.lo < -16384 || T.lo + T.width - 1 > 16383))
+            return bad(why, "table window beyond the doubled-coordinate range");
         if (lossy && t == 0 && (T.lo < 0 || T.lo + T.width - 1 > 1 || esc != 0)) return bad(why, "coset table must cover {0,1}");
         std::memset(T.freq, 0, sizeof T.freq);
         uint64_t sum = esc;

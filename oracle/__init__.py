@@ -62,6 +62,7 @@ def lib():
         L.or_e8_nearest_batch.argtypes = [vp, i64, vp, vp]
         L.or_e8_nearest_batch.restype = None
         L.or_normalize.argtypes = [vp, C.c_int, vp]
+        L.or_choose_window.argtypes = [vp, i64, vp, vp, vp]
         L.or_estimate_bpp.argtypes = [vp, C.c_int, i64, i64, C.c_double]
         L.or_estimate_bpp.restype = C.c_double
         L.or_select_step.argtypes = [vp, C.c_int, i64, i64, C.c_double]
@@ -196,6 +197,17 @@ def normalize(counts, prob_bits: int = 12) -> np.ndarray:
     if rc != 0:
         raise OracleError(rc, "normalize")
     return f
+
+
+def choose_window(values) -> tuple[int, int, int]:
+    """The oracle's window rule applied to a list of coordinate values: (window start, width,
+    number of values outside the window)."""
+    v = np.ascontiguousarray(np.asarray(values, np.int32))
+    lo, S, ne = C.c_int32(), C.c_int32(), C.c_uint64()
+    rc = lib().or_choose_window(_ptr(v), len(v), C.byref(lo), C.byref(S), C.byref(ne))
+    if rc != 0:
+        raise OracleError(rc, "choose_window")
+    return lo.value, S.value, ne.value
 
 
 def estimate_bpp(w: np.ndarray, delta: float, dtype: int | None = None) -> float:

@@ -27,6 +27,11 @@
  *   E8 nearest point       pinned: brute-force search, lattice invariants, second moment of E8
  *   row scale              pinned: closed form
  *   table normalization    pinned: invariants (sum, support), single-symbol case
+ *   table windows          pinned: brute force over every window start (constructed ties, best
+ *                          window at either end of the range, random heavy tails) and the tables
+ *                          of real streams against histograms of their decoded coordinates
+ *   lossy tile layout      pinned: an independent Python reader of the stream bytes gives the
+ *                          decoder's coordinates and cosets (escapes, ragged shapes, 32-row tiles)
  *   rANS tile coder        pinned: exact round trips, final state, an independent Python decoder
  *   rate search            pinned: monotone estimate, Gaussian closed form, |payload - target|
  *   containers             pinned: library casts (torch CPU) for BF16/FP16/FP8, integer closed form
@@ -317,6 +322,26 @@ static void choose_window(const value_hist* h, sym_table* T) {
         inside += T->cnt[s];
     }
     T->cnt[ESC_SYM] = h->total - inside;
+}
+
+/* The window rule on its own, for its pins: the histogram of n coordinate values (each within
+ * [-32768, 32767]), then choose_window; returns the window start, width and escape count. */
+int or_choose_window(const int32_t* values, int64_t n, int32_t* lo, int32_t* S, uint64_t* n_escaped) {
+    value_hist h;
+    sym_table T;
+    h.hist = (uint64_t*)malloc(sizeof(uint64_t) * HIST_SPAN);
+    if (!h.hist) return OR_ENOMEM;
+    hist_reset(&h);
+    for (int64_t i = 0; i < n; ++i) {
+        if (values[i] < -HIST_OFF || values[i] >= HIST_SPAN - HIST_OFF) { free(h.hist); return OR_EINVAL; }
+        hist_add(&h, values[i]);
+    }
+    choose_window(&h, &T);
+    *lo = T.lo;
+    *S = T.S;
+    *n_escaped = T.cnt[ESC_SYM];
+    free(h.hist);
+    return OR_OK;
 }
 
 /* Normalization of counts to frequencies summing to M = 2^n (reading):
@@ -796,7 +821,9 @@ static int parse_stream(const uint8_t* s, size_t len, parsed* P) {
         int maxS = P->mode == MODE_LOSSY ? 255 : 256;
         if (S < 1 || S > maxS || pos + 2 * (uint64_t)S > o_ix) return OR_ECORRUPT;
         if (P->mode != MODE_LOSSY && (lo != 0 || S != 256 || esc != 0)) return OR_ECORRUPT;
-        if (P->mode == MODE_LOSSY && lo + S - 1 > 32767) return OR_ECORRUPT;
+        /* reading: a coordinate x must give a doubled coordinate 2x + b that fits int16, the
+         * range the encoder's step bound keeps every value in */
+        if (P->mode == MODE_LOSSY && t > 0 && (lo < -16384 || lo + S - 1 > 16383)) return OR_ECORRUPT;
         if (P->mode == MODE_LOSSY && t == 0 && (lo < 0 || lo + S - 1 > 1 || esc != 0)) return OR_ECORRUPT;
         uint64_t sum = esc;
         memset(P->freq[t], 0, sizeof P->freq[t]);
