@@ -1,21 +1,22 @@
 """Benchmark of the gfx950 tile-rANS decode path on one MI355X.
 
-Default workload (a "step"): the 4096 x 4096 BF16 Student-t(5) matrix with log-normal row scales,
-compressed at 3.0, 4.0 and 4.5 bits per weight, each decoded to BF16 and to FP16, plus the
-lossless BF16 tile-rANS decode of the same matrix: seven full-matrix decodes per step, issued as
-one grouped launch (the kernel balances lossy and lossless tiles by their cost). Inputs are
-resident in HBM before timing starts; several copies of the step's buffers are used in rotation
-(> 2 GB between reuses) so that neither the compressed input nor the output of a step is still
-in the 256 MB Infinity Cache.
+Headline workload (a "step"): one full-model decode of the DiT-like denoiser, the largest
+single-GPU configuration: 30 blocks x 5 linear weights ([11520, 3840], [3840, 3840],
+[10240, 3840] x 2, [3840, 10240]), 150 distinct matrices, 5.31 G weights of 0.02 t(5) BF16 coded
+at 4.0 bits per weight, decoded to BF16 as five grouped launches of 30 matrices (one decode
+kernel each). The weights are drawn on the GPU (seed 3000 + 5 b + m) and coded by the device
+encoder before timing; inputs are resident in HBM, and a step moves 13.4 GB, far beyond the
+256 MB Infinity Cache.
 
-Prints one JSON line (rank 0, N = 1): decoded-weight GB/s (container bytes written per second),
-the roofline of the step's one grouped decode launch from HIP events on the launch stream,
-the two lossless BF16 codings side by side (byte planes, and the exponent-coded variant), the
-fused decode + GEMM forward of an 8192 x 8192 weight at 4.5 bpp against the plain BF16 GEMM
-(M = 4096, 256, 16, 1), the same forward with FP8 compute against the plain FP8 GEMM, and the
-oracle's CPU decode of one step on the host cores as a reported baseline.
+Prints one JSON line (rank 0, N = 1): decoded-weight GB/s (container bytes written per second
+over K back-to-back steps), the roofline of one 30-matrix decode launch from HIP events on the
+launch stream, the oracle's CPU decode of a bounded sample of the same streams, and extra
+sections: the 4096 x 4096 seven-decode step, the two lossless BF16 codings, the encoders, the
+fused decode + GEMM forward of an 8192 x 8192 weight (M = 4096, 256, 16, 1, BF16 and FP8
+compute) and the 64-matrix mixed-rate set.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-gemm]
+    python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-gemm] [--step-only]
+    python bench.py --trace-summary DIR/..._kernel_trace.csv --kernel decode_group --skip N
 """
 from __future__ import annotations
 
@@ -34,19 +35,24 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
 
 
-PROFILE = os.path.join(ROOT, "profiles", "decode_group_4096sq_step.txt")
+PROFILE_DIT = os.path.join(ROOT, "profiles", "decode_group_dit_model_counters.txt")
+PROFILE_C2 = os.path.join(ROOT, "profiles", "decode_group_4096sq_step.txt")
 
 
-def profiled_traffic():
-    """HBM bytes per grouped decode launch from the committed rocprofv3 counter summary, or None
-    when the decode kernel source changed since the counters were taken."""
+def decode_source_sha() -> str:
+    """SHA-256 of the decode kernel's sources (the key of the committed counter summaries)."""
     import hashlib
+    src = os.path.join(ROOT, "decode_tile_interleaved_rans_amd", "csrc")
+    return hashlib.sha256(open(os.path.join(src, "decode.hip"), "rb").read() +
+                          open(os.path.join(src, "kernels.h"), "rb").read()).hexdigest()
+
+
+def profiled_traffic(path: str):
+    """HBM bytes per decode launch from a committed rocprofv3 counter summary, or None when the
+    decode kernel's source changed since the counters were taken."""
     try:
-        kv = dict(l.split(": ", 1) for l in open(PROFILE).read().splitlines() if l and not l.startswith("#"))
-        src = os.path.join(ROOT, "decode_tile_interleaved_rans_amd", "csrc")
-        sha = hashlib.sha256(open(os.path.join(src, "decode.hip"), "rb").read() +
-                             open(os.path.join(src, "kernels.h"), "rb").read()).hexdigest()
-        return int(kv["traffic_bytes_per_launch"]) if kv.get("kernel_source_sha256") == sha else None
+        kv = dict(l.split(": ", 1) for l in open(path).read().splitlines() if l and not l.startswith("#"))
+        return int(kv["traffic_bytes_per_launch"]) if kv.get("kernel_source_sha256") == decode_source_sha() else None
     except (OSError, KeyError, ValueError):
         return None
 
@@ -55,51 +61,90 @@ def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def cpu_baseline(sample, budget_s: float = 10.0):
+    """The oracle decoding a bounded sample of the headline workload's streams to BF16 on the host
+    cores: whole DiT-like blocks (5 matrices each, in block order) with 16 threads until about
+    budget_s seconds have passed, then block 0 on one thread."""
+    import oracle
+    cores = min(16, os.cpu_count() or 1)
+    t0 = time.time()
+    out_bytes, blocks = 0, 0
+    for b, streams in enumerate(sample):
+        for st in streams:
+            out, _ = oracle.decompress(st, oracle.BF16, n_threads=cores)
+            out_bytes += out.nbytes
+            del out
+        blocks += 1
+        if time.time() - t0 >= budget_s:
+            break
+    dt = time.time() - t0
+    t1 = time.time()
+    one_bytes = 0
+    for st in sample[0]:
+        out, _ = oracle.decompress(st, oracle.BF16, n_threads=1)
+        one_bytes += out.nbytes
+        del out
+    dt1 = time.time() - t1
+    return {"value": round(out_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{blocks} of the 30 DiT-like blocks (5 matrices, 177 M weights each; the streams the GPU "
+                      f"decodes) decoded to BF16 by the oracle with {cores} threads in {dt:.1f} s",
+            "one_core": {"value": round(one_bytes / dt1 / 1e9, 4), "unit": "GB/s",
+                         "sample": f"block 0 (5 matrices) decoded to BF16 on one thread in {dt1:.1f} s"}}
+
+
 def c2_items():
-    """(name, stream bytes, container, rows, cols) of one step of the 4096^2 workload."""
+    """(name, stream bytes, container, actual bpp) of the 4096 x 4096 seven-decode step."""
     import decode_tile_interleaved_rans_amd as ep
     from decode_tile_interleaved_rans_amd import workloads as W
     w = W.student_t_rowscaled(4096, 4096, 2)
     items = []
     for t in (3.0, 4.0, 4.5):
-        t0 = time.time()
         s, bpp = ep.compress(w, t, dtype=ep.BF16)
-        log(f"encoded 4096x4096 at target {t}: actual {bpp:.4f} bpp in {time.time() - t0:.2f} s")
         items.append((f"lossy{t}_bf16", s, "bf16", bpp))
         items.append((f"lossy{t}_f16", s, "f16", bpp))
-    t0 = time.time()
     s, bpp = ep.lossless_compress(w, dtype=ep.BF16)
-    log(f"lossless bf16: {bpp:.4f} bpp in {time.time() - t0:.2f} s")
     items.append(("lossless_bf16", s, "bf16", bpp))
     return items, w.shape
 
 
-def cpu_baseline(items, budget_s: float = 10.0):
-    import oracle
-    cores = min(16, os.cpu_count() or 1)
-    odt = {"bf16": oracle.BF16, "f16": oracle.F16}
-    t0 = time.time()
-    steps = 0
-    out_bytes = 0
-    while True:
-        for name, s, ct, _ in items:
-            out, _ = oracle.decompress(s, odt[ct], n_threads=cores)
-            out_bytes += out.nbytes
-        steps += 1
-        if time.time() - t0 >= budget_s or steps >= 50:
-            break
-    dt = time.time() - t0
-    # one core: one lossy and the lossless matrix of the step
-    one = [it for it in items if it[0] in ("lossy4.0_bf16", "lossless_bf16")]
-    t1 = time.time()
-    one_bytes = sum(oracle.decompress(s, odt[ct], n_threads=1)[0].nbytes for _, s, ct, _ in one)
-    dt1 = time.time() - t1
-    return {"value": out_bytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{steps} full step(s) of the same workload (7 full-matrix decodes each) decoded by the "
-                      f"oracle with {cores} threads in {dt:.1f} s",
-            "one_core": {"value": one_bytes / dt1 / 1e9, "unit": "GB/s",
-                         "sample": f"the 4.0 bpp and the lossless 4096x4096 decodes of the step on one thread "
-                                   f"in {dt1:.1f} s"}}
+def c2_step_section(torch, ep, steps: int = 20):
+    """The 4096 x 4096 BF16 Student-t(5) matrix with log-normal row scales at 3.0 / 4.0 / 4.5 bpp,
+    each decoded to BF16 and FP16, plus its lossless BF16 decode: seven decodes in one grouped
+    launch. Rotating copies of the step's buffers (> 2.5 GB between reuses) keep the Infinity
+    Cache from serving repeats; per-launch HIP events on the launch stream."""
+    items, (R, C) = c2_items()
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}
+    out_b = len(items) * R * C * 2
+    in_b = sum(len(s) for _, s, _, _ in items)
+    n_sets = max(2, math.ceil(2.5e9 / (out_b + in_b)))
+    sets = [([ep.upload(s) for _, s, _, _ in items],
+             [torch.empty((R, C), dtype=tdt[ct], device="cuda") for _, _, ct, _ in items]) for _ in range(n_sets)]
+    for k in range(3):
+        ep.decompress_many(*sets[k % n_sets])
+    torch.cuda.synchronize()
+    ev = []
+    for k in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        ep.decompress_many(*sets[k % n_sets])
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    for hs, _ in sets:
+        for h in hs:
+            h.check()
+    us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    t = float(np.mean(us))
+    sets.clear()
+    torch.cuda.empty_cache()
+    log(f"4096^2 seven-decode step: {t:.1f} us per launch")
+    return {"workload": "4096x4096 bf16 Student-t(5)x0.015 rows scaled by lognormal(0.5); lossy at 3.0/4.0/4.5 bpp "
+                        "decoded to BF16 and FP16 + lossless BF16 decode, one grouped launch",
+            "avg_launch_us": round(t, 2), "launch_us_min": round(min(us), 2), "bytes_per_launch": in_b + out_b,
+            "algorithmic_gbs": round((in_b + out_b) / t / 1e3, 1),
+            "hbm_frac": round((in_b + out_b) / t / 1e3 / HBM_PEAK_GBS, 4),
+            "output_gbs": round(out_b / t / 1e3, 1), "traffic": profiled_traffic(PROFILE_C2),
+            "per_decode": {n: {"actual_bpp": round(bpp, 4), "stream_bytes": len(s)} for n, s, _, bpp in items}}
 
 
 def fused_gemm_section(torch, ep, reps: int = 15):
@@ -250,60 +295,139 @@ def encoder_section(torch, ep, reps: int = 3):
             "host_gweights_per_s": round(w.size / h / 1e9, 3), "identical_streams": True}
 
 
-def gpu_student_t(torch, rows: int, cols: int, seed: int, scale: float):
-    """scale * t(nu=5) as BF16 on the GPU: z / sqrt(chi2_5 / 5) from six normals of torch's generator
-    seeded with `seed` (so that large weight sets need no host generation)."""
-    g = torch.Generator(device="cuda")
-    g.manual_seed(seed)
-    z = torch.randn((rows, cols), generator=g, device="cuda")
-    v = torch.zeros((rows, cols), device="cuda")
-    for _ in range(5):
-        v += torch.randn((rows, cols), generator=g, device="cuda").square()
-    return (scale * z / torch.sqrt(v / 5.0)).to(torch.bfloat16)
-
-
-def dit_model_section(torch, ep, steps: int = 10):
-    """Full-model decode of the DiT-like denoiser (30 blocks x [11520, 3840], [3840, 3840],
-    [10240, 3840] x 2, [3840, 10240], 5.31 G weights of 0.02 t5 BF16 at 4.0 bpp) to BF16 per
-    simulated step, as grouped launches of 30 matrices. All 150 matrices are distinct: drawn on the
-    GPU (seed 3000 + 5 b + m) and coded by the device encoder, a few seconds in all."""
+def dit_step(torch, ep, steps: int, warmup: int, cpu_blocks: int = 10):
+    """The headline step: the DiT-like model decoded to BF16 as five grouped launches of 30
+    matrices. Returns the timing record and the host bytes of the first cpu_blocks blocks' streams
+    (the CPU baseline's sample)."""
     from decode_tile_interleaved_rans_amd import workloads as W
     t0 = time.time()
-    hs, outs, in_b = [], [], 0
+    hs, outs, in_sizes, sample = [], [], [], []
     for b in range(W.DIT_BLOCKS):
+        blk = []
         for m, (R, Cc) in enumerate(W.DIT_BLOCK_SHAPES):
-            w = gpu_student_t(torch, R, Cc, 3000 + 5 * b + m, 0.02)
+            w = W.gpu_student_t(R, Cc, 3000 + 5 * b + m, 0.02)
             st, _ = ep.compress_device(w, 4.0)
             del w
             hs.append(ep.upload(st))
-            in_b += len(st)
+            in_sizes.append(len(st))
             outs.append(torch.empty((R, Cc), dtype=torch.bfloat16, device="cuda"))
+            if b < cpu_blocks:
+                blk.append(st)
+        if blk:
+            sample.append(blk)
     torch.cuda.synchronize()
     log(f"DiT-like model: 150 matrices drawn and coded on the GPU in {time.time() - t0:.1f} s")
-    out_b = sum(o.numel() * 2 for o in outs)
-    for _ in range(2):
-        ep.decompress_many(hs, outs)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(steps):
-        ep.decompress_many(hs, outs)
-    b.record()
+    G = 30
+    groups = [(hs[i:i + G], outs[i:i + G]) for i in range(0, len(hs), G)]
+    group_bytes = [sum(in_sizes[i:i + G]) + sum(o.numel() * 2 for o in outs[i:i + G]) for i in range(0, len(hs), G)]
+
+    def step():
+        for gh, go in groups:
+            ep.decompress_many(gh, go)
+
+    for _ in range(warmup):
+        step()
     torch.cuda.synchronize()
     for h in hs:
         h.check()
-        h.release()
-    ms = a.elapsed_time(b) / steps
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    a.record()
+    for _ in range(steps):
+        step()                                       # back to back, no events between launches
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = a.elapsed_time(b)
+    # per-launch durations: HIP events around each 30-matrix launch on the launch stream (the
+    # current stream), over K further steps
+    ev = []
+    for _ in range(steps):
+        for k, (gh, go) in enumerate(groups):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ep.decompress_many(gh, go)
+            e1.record()
+            ev.append((k, e0, e1))
+    torch.cuda.synchronize()
+    for h in hs:
+        h.check()
+    durs = [e0.elapsed_time(e1) / 1e3 for _, e0, e1 in ev]
+    bytes_launch = float(np.mean([group_bytes[k] for k, _, _ in ev]))
+    t_launch = float(np.mean(durs))
+    out_b = sum(o.numel() * 2 for o in outs)
+    in_b = sum(in_sizes)
     weights = sum(o.numel() for o in outs)
-    del outs
+    for h in hs:
+        h.release()
+    del outs, groups, hs
     torch.cuda.empty_cache()
-    log(f"DiT-like model step: {ms:.3f} ms")
-    return {"workload": "DiT-like 30 blocks x 5 linear weights, 150 distinct matrices, 5.31 G weights, "
-                        "0.02 t5 bf16 at 4.0 bpp -> BF16",
-            "ms_per_step": round(ms, 4), "gb_in": round(in_b / 1e9, 3), "gb_out": round(out_b / 1e9, 3),
-            "output_gbs": round(out_b / ms / 1e6, 1), "algorithmic_gbs": round((in_b + out_b) / ms / 1e6, 1),
-            "hbm_frac": round((in_b + out_b) / ms / 1e6 / HBM_PEAK_GBS, 4),
-            "tweights_per_s": round(weights / ms / 1e9, 4), "steps": steps}
+    sec = ms / 1e3
+    achieved = bytes_launch / t_launch / 1e9
+    log(f"DiT-like model step: {ms / steps:.3f} ms; one 30-matrix launch {t_launch * 1e6:.1f} us")
+    rec = {
+        "value": round(out_b * steps / sec / 1e9, 2), "ms_per_step": round(ms / steps, 4), "wall_s": round(wall, 4),
+        "weights_per_s": round(weights * steps / sec / 1e9, 3),
+        "hbm_frac_step": round((in_b + out_b) * steps / sec / 1e9 / HBM_PEAK_GBS, 4),
+        "gb_in": round(in_b / 1e9, 3), "gb_out": round(out_b / 1e9, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(PROFILE_DIT),
+                     "kernel": "decode_group (one grouped launch of 30 DiT-like matrices -> BF16)",
+                     "avg_launch_us": round(t_launch * 1e6, 2), "launch_us_min": round(min(durs) * 1e6, 2),
+                     "bytes_per_launch": int(bytes_launch), "launches_timed": len(durs)},
+    }
+    return rec, sample
+
+
+def kernel_matches(name: str, kernel: str) -> bool:
+    """Whether a profiler's kernel name (namespaces, template arguments, parameter list) is `kernel`."""
+    import re
+    return re.search(r"(^|::|\s)" + re.escape(kernel) + r"\s*[(<]", name) is not None
+
+
+def trace_summary(path: str, kernel: str, skip: int) -> str:
+    """Text summary of a rocprofv3 kernel-trace CSV: the launches of `kernel` after the first
+    `skip` (warm-up) ones, their mean / min / max duration, and the decode sources' hash."""
+    import csv
+    rows = [r for r in csv.DictReader(open(path)) if kernel_matches(r["Kernel_Name"], kernel)]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows[skip:]]
+    lines = [f"kernel: {kernel}", f"launches_in_trace: {len(rows)}", f"skipped_warmup_launches: {skip}",
+             f"launches_summarized: {len(d)}", f"mean_us: {np.mean(d):.2f}", f"min_us: {np.min(d):.2f}",
+             f"max_us: {np.max(d):.2f}", f"median_us: {np.median(d):.2f}",
+             f"kernel_source_sha256: {decode_source_sha()}"]
+    return "\n".join(lines)
+
+
+def pmc_summary(path: str, kernel: str, skip: int) -> str:
+    """Text summary of a rocprofv3 counter-collection CSV: per counter, the values (KiB) of the
+    dispatches of `kernel` after the first `skip`, and the largest value among copy kernels (the
+    calibration copy of --copy-calibration)."""
+    import csv
+    vals, copies = {}, {}
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r.get("Dispatch_Id", 0) or 0))
+    seen = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        cname = r["Counter_Name"]
+        v = float(r["Counter_Value"])
+        if kernel_matches(name, kernel):
+            k = seen.setdefault(cname, 0)
+            seen[cname] = k + 1
+            if k >= skip:
+                vals.setdefault(cname, []).append(v)
+        elif "copy" in name.lower():
+            copies[cname] = max(copies.get(cname, 0.0), v)
+    lines = []
+    for c, v in vals.items():
+        lines.append(f"{c}_dispatches: {len(v)}")
+        lines.append(f"{c}_kib_mean: {np.mean(v):.1f}")
+        lines.append(f"{c}_kib_values: " + " / ".join(f"{x:.0f}" for x in v[:8]))
+    for c, v in copies.items():
+        lines.append(f"copy_{c}_kib: {v:.0f}")
+    lines.append(f"kernel_source_sha256: {decode_source_sha()}")
+    return "\n".join(lines)
 
 
 def mixed_section(torch, ep, steps: int = 5, reps: int = 5):
@@ -319,7 +443,7 @@ def mixed_section(torch, ep, steps: int = 5, reps: int = 5):
     streams, hs, bpps = [], [], []
     t0 = time.time()
     for R, Cc, tgt, seed, _ in specs:
-        w = gpu_student_t(torch, R, Cc, seed, 0.02)
+        w = W.gpu_student_t(R, Cc, seed, 0.02)
         st, bpp = ep.compress_device(w, tgt)
         del w
         streams.append(st)
@@ -410,16 +534,26 @@ def main():
     ap.add_argument("--gemm-reps", type=int, default=15, help="timed reps per variant in the GEMM measurement")
     ap.add_argument("--encoder-only", action="store_true",
                     help="profiling aid: run only the encoder comparison and print its JSON")
-    ap.add_argument("--dit-only", action="store_true",
-                    help="profiling aid: run only the full-model step of the DiT-like denoiser and print its JSON")
+    ap.add_argument("--c2-only", action="store_true",
+                    help="profiling aid: run only the 4096 x 4096 seven-decode step and print its JSON")
     ap.add_argument("--mixed-only", action="store_true",
                     help="profiling aid: run only the 64-matrix mixed-rate set and print its JSON")
-    ap.add_argument("--no-dit", action="store_true",
-                    help="skip the full-model decode step of the DiT-like denoiser (5.31 G weights)")
     ap.add_argument("--no-mixed", action="store_true", help="skip the 64-matrix mixed-rate set")
     ap.add_argument("--step-only", action="store_true",
-                    help="profiling aid: time only the decode step (no lossless, encoder, GEMM or CPU sections)")
+                    help="profiling aid: time only the headline step (no other sections, no CPU baseline)")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="summarize a rocprofv3 kernel-trace CSV (no GPU work) and exit")
+    ap.add_argument("--pmc-summary", metavar="CSV",
+                    help="summarize a rocprofv3 counter-collection CSV (no GPU work) and exit")
+    ap.add_argument("--kernel", default="decode_group", help="kernel name for --trace-summary / --pmc-summary")
+    ap.add_argument("--skip", type=int, default=0, help="warm-up launches to leave out in --trace-summary")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.kernel, args.skip))
+        return
+    if args.pmc_summary:
+        print(pmc_summary(args.pmc_summary, args.kernel, args.skip))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the decode path has no cross-GPU step (tiles, rows and "
               "matrices shard without exchange), so run it with --gpus 1.", file=sys.stderr)
@@ -441,109 +575,43 @@ def main():
     if args.encoder_only:
         print(json.dumps(encoder_section(torch, ep)), flush=True)
         return
-    if args.dit_only:
-        print(json.dumps(dit_model_section(torch, ep)), flush=True)
+    if args.c2_only:
+        print(json.dumps(c2_step_section(torch, ep)), flush=True)
         return
     if args.mixed_only:
         print(json.dumps(mixed_section(torch, ep)), flush=True)
         return
-    items, (R, C) = c2_items()
-    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}
-    step_out_bytes = sum(R * C * 2 for _ in items)
-    step_in_bytes = sum(len(s) for _, s, _, _ in items)
-    set_bytes = step_out_bytes + step_in_bytes
-    n_sets = max(2, math.ceil(2.5e9 / set_bytes))
-    log(f"step: {len(items)} decodes, {step_in_bytes / 1e6:.1f} MB in, {step_out_bytes / 1e6:.1f} MB out; "
-        f"{n_sets} rotating buffer sets")
-    sets = []
-    for k in range(n_sets):
-        hs = [ep.upload(s) for _, s, _, _ in items]
-        outs = [torch.empty((R, C), dtype=tdt[ct], device="cuda") for _, _, ct, _ in items]
-        sets.append((hs, outs))
-    torch.cuda.synchronize()
-
-    def step(k: int):
-        hs, outs = sets[k % n_sets]
-        ep.decompress_many(hs, outs)                # the whole step: one grouped launch
-
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-    for hs, _ in sets:
-        for h in hs:
-            h.check()
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    t_start.record()
-    for k in range(args.steps):
-        step(args.warmup + k)                        # back to back, no events between launches
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms = t_start.elapsed_time(t_end)
-    for hs, _ in sets:
-        for h in hs:
-            h.check()
-    sec = ms / 1e3
-    value = step_out_bytes * args.steps / sec / 1e9
-    weights_per_s = len(items) * R * C * args.steps / sec
-
-    # the step's kernel: one grouped decode of the seven matrices; algorithmic bytes =
-    # stream bytes read + container bytes written. Its launch duration: HIP events around each of
-    # K further launches on the launch stream (the current stream), after the timed region; the
-    # timed region's average also holds the fences between back-to-back kernels
-    launch_bytes = sum(len(items[i][1]) + 2 * R * C for i in range(len(items)))
-    durs = []
-    for k in range(args.steps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        step(args.warmup + k)
-        b.record()
-        durs.append((a, b))
-    torch.cuda.synchronize()
-    durs = [a.elapsed_time(b) / 1e3 for a, b in durs]
-    t_launch = float(np.mean(durs))
-    achieved = launch_bytes / t_launch / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(),
-                "kernel": "decode_group (7 matrices: 3.0/4.0/4.5 bpp x BF16/FP16 + lossless BF16)",
-                "avg_launch_us": round(t_launch * 1e6, 2), "bytes_per_launch": launch_bytes,
-                "launch_us_min": round(min(durs) * 1e6, 2)}
-    per_item = {items[i][0]: {"actual_bpp": round(items[i][3], 4), "stream_bytes": len(items[i][1])}
-                for i in range(len(items))}
-    sets.clear()
-    torch.cuda.empty_cache()
-    lossless = encoders = fused = None
+    head, sample = dit_step(torch, ep, args.steps, args.warmup, cpu_blocks=0 if args.no_cpu or args.step_only else 10)
+    c2 = lossless = encoders = fused = mixed = cpu = None
     if not args.step_only:
+        c2 = c2_step_section(torch, ep)
         lossless = lossless_section(torch, ep)
         encoders = encoder_section(torch, ep)
-    if not args.no_gemm and not args.step_only:
-        fused = fused_gemm_section(torch, ep, reps=args.gemm_reps)
-    dit = dit_model_section(torch, ep) if not args.step_only and not args.no_dit else None
-    mixed = mixed_section(torch, ep) if not args.step_only and not args.no_mixed else None
-    cpu = None
-    if not args.no_cpu and not args.step_only:
-        log("timing the oracle on the host cores")
-        cpu = cpu_baseline(items)
+        if not args.no_gemm:
+            fused = fused_gemm_section(torch, ep, reps=args.gemm_reps)
+        if not args.no_mixed:
+            mixed = mixed_section(torch, ep)
+        if not args.no_cpu:
+            log("timing the oracle on the host cores")
+            cpu = cpu_baseline(sample)
     line = {
         "metric": "decoded weight GB/s + % HBM roofline; fused decode+GEMM overhead vs BF16",
-        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms / args.steps, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "u32 rANS state -> fp32 -> bf16/f16", "data": "synthetic",
-        "config": {"workload": "4096x4096 bf16 Student-t(5)x0.015 rows scaled by lognormal(0.5); lossy at "
-                               "3.0/4.0/4.5 bpp decoded to BF16 and FP16 + lossless BF16 decode (7 decodes/step)",
-                   "rows": R, "cols": C, "tile": "16x256, 32 rANS lanes", "prob_bits": 12},
-        "weights_per_s": round(weights_per_s / 1e9, 3), "weights_per_s_unit": "Gweights/s",
-        "hbm_frac_step": round((step_out_bytes + step_in_bytes) * args.steps / sec / 1e9 / HBM_PEAK_GBS, 4),
-        "wall_s": round(wall, 4),
-        "roofline": roofline,
-        "per_decode": per_item,
+        "value": head["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u32 rANS state -> fp32 -> bf16", "data": "synthetic",
+        "config": {"workload": "DiT-like 30-block denoiser, full-model decode per step: 150 distinct matrices "
+                               "(per block [11520,3840], [3840,3840], [10240,3840] x2, [3840,10240]), 5.31 G weights "
+                               "of 0.02 t(5) bf16 at 4.0 bpp -> BF16, five grouped launches of 30",
+                   "matrices": 150, "weights": 5308416000, "target_bpp": 4.0, "gb_in": head["gb_in"],
+                   "gb_out": head["gb_out"], "tile": "16x256, 32 rANS lanes", "prob_bits": 12},
+        "weights_per_s": head["weights_per_s"], "weights_per_s_unit": "Gweights/s",
+        "hbm_frac_step": head["hbm_frac_step"], "wall_s": head["wall_s"],
+        "roofline": head["roofline"],
+        "c2_step_4096sq": c2,
         "lossless_bf16_codings": lossless,
         "encoders": encoders,
-        "dit_model": dit,
-        "mixed_rate_set": mixed,
         "fused_gemm": fused,
+        "mixed_rate_set": mixed,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -264,15 +264,18 @@ class Handle:
         return out
 
     def decompress(self, dtype=None, stream=None):
-        """Decode into a new tensor. FP8 / INT8 return (values, per-row fp32 scale)."""
+        """Decode into a new tensor. FP8 / INT8 return (values, per-row fp32 scale). The outputs
+        are allocated on the stream the decode runs on."""
         torch = _torch()
         if dtype is None:
             dtype = _torch_dtype(self.info["src_dtype"]) if self.info["mode"] != LOSSY else torch.bfloat16
-        out = torch.empty(self.shape, dtype=dtype, device="cuda")
-        scale = None
-        if self.info["mode"] == LOSSY and dtype in (torch.float8_e4m3fn, torch.int8):
-            scale = torch.empty(self.shape[0], dtype=torch.float32, device="cuda")
-        self.decompress_into(out, scale, stream)
+        s = stream if stream is not None else torch.cuda.current_stream()
+        with torch.cuda.stream(s):
+            out = torch.empty(self.shape, dtype=dtype, device="cuda")
+            scale = None
+            if self.info["mode"] == LOSSY and dtype in (torch.float8_e4m3fn, torch.int8):
+                scale = torch.empty(self.shape[0], dtype=torch.float32, device="cuda")
+            self.decompress_into(out, scale, s)
         return (out, scale) if scale is not None else out
 
     def decode_symbols(self, stream=None):
@@ -372,9 +375,17 @@ def gemm_fp8(xq, xs, wq, ws, bias=None, stream=None):
 
 
 class CompressedLinear:
-    """Linear layer that keeps only the compressed weight; forward decodes it inside the GEMM.
-    compute="bf16" (default) multiplies the BF16-decoded weight with BF16 activations; "fp8"
-    decodes the weight to FP8 E4M3 with its row scales and quantizes the activations per row."""
+    """Linear layer that keeps only the compressed weight and decodes it on every forward
+    ("EntroPack PyTorch Guide", section "Replace one linear layer before a whole model").
+
+    compute="bf16" (default): for up to 4 activation rows the decode kernel forms the products
+    itself (the weight is never written); for more rows the weight is decoded once per call into
+    a scratch slice that stays in the Infinity Cache and the BF16 MFMA GEMM reads it from there.
+    compute="fp8": the weight is decoded to FP8 E4M3 with its row scales, the activations are
+    quantized per row, and the FP8 MFMA GEMM multiplies the codes.
+
+    The forward takes BF16 activations. Other dtypes are refused unless cast=True is passed, so a
+    precision change is never silent ("Diagnose compression failures in the correct order")."""
 
     def __init__(self, stream: bytes, bias=None, compute: str = "bf16"):
         if compute not in ("bf16", "fp8"):
@@ -412,19 +423,37 @@ class CompressedLinear:
             b = torch.from_numpy(bias.view("int16")).view(torch.bfloat16).cuda()
         return cls(stream, b, compute)
 
-    def forward(self, x, stream=None):
+    def forward(self, x, stream=None, cast: bool = False):
+        """Y = X W^T (+ bias) in BF16 on `stream` (default: the current stream). x must be BF16,
+        or cast=True to convert it first. With an explicit stream other than the current one, that
+        stream first waits for the work queued on the current stream (which produced x), and the
+        conversion and the output allocation run on it."""
         torch = _torch()
         shp = x.shape
         if shp[-1] != self.in_features or not x.is_cuda:
             raise ValueError(f"input must be a GPU tensor with last dimension {self.in_features}, got {tuple(shp)}")
+        if x.dtype != torch.bfloat16 and not cast:
+            raise ValueError(f"the forward takes bfloat16 activations, got {x.dtype}; pass cast=True to convert")
+        if x.device.index != torch.cuda.current_device():
+            raise ValueError(f"x is on {x.device}, but the current device is cuda:{torch.cuda.current_device()}")
         if self.bias is not None:
             _need(self.bias, "bias", torch.bfloat16, shape=(self.out_features,))
-        x2 = x.reshape(-1, shp[-1]).to(torch.bfloat16).contiguous()
-        y = torch.empty((x2.shape[0], self.out_features), dtype=torch.bfloat16, device=x.device)
-        bp = C.c_void_p(self.bias.data_ptr()) if self.bias is not None else None
-        fn = lib().ep_linear_forward_fp8 if self.compute == "fp8" else lib().ep_linear_forward
-        _check(fn(self.handle.ptr, C.c_void_p(x2.data_ptr()), x2.shape[0], bp, C.c_void_p(y.data_ptr()),
-                  _stream_ptr(stream)), "ep_linear_forward" + ("_fp8" if self.compute == "fp8" else ""))
+        cur = torch.cuda.current_stream()
+        s = stream if stream is not None else cur
+        other = s.cuda_stream != cur.cuda_stream
+        if other:
+            s.wait_stream(cur)
+        with torch.cuda.stream(s):
+            x2 = x.reshape(-1, shp[-1]).to(torch.bfloat16).contiguous()
+            y = torch.empty((x2.shape[0], self.out_features), dtype=torch.bfloat16, device=x.device)
+            bp = C.c_void_p(self.bias.data_ptr()) if self.bias is not None else None
+            fn = lib().ep_linear_forward_fp8 if self.compute == "fp8" else lib().ep_linear_forward
+            _check(fn(self.handle.ptr, C.c_void_p(x2.data_ptr()), x2.shape[0], bp, C.c_void_p(y.data_ptr()),
+                      C.c_void_p(s.cuda_stream)), "ep_linear_forward" + ("_fp8" if self.compute == "fp8" else ""))
+        if other:
+            x2.record_stream(s)             # x (or its converted copy) is read on s after this returns
+            if self.bias is not None:
+                self.bias.record_stream(s)
         return y.reshape(*shp[:-1], self.out_features)
 
     __call__ = forward

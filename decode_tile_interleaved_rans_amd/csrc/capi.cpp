@@ -131,39 +131,96 @@ hipError_t launch_all(const std::vector<ep::MatDesc>& ds, hipStream_t stream) {
     return hipSuccess;
 }
 
-// Library-owned device workspaces, one per (device, stream), grown on demand and kept until the
-// process ends (work queued on the stream may still use a workspace after a call returns).
-hipError_t workspace(int device, hipStream_t stream, size_t need, uint16_t** out) {
-    struct Entry {
-        int device;
-        hipStream_t stream;
-        uint16_t* ptr;
-        size_t bytes;
-    };
-    static std::mutex mu;
-    static std::vector<Entry> pool;
-    std::lock_guard<std::mutex> lock(mu);
-    for (Entry& e : pool) {
-        if (e.device != device || e.stream != stream) continue;
-        if (e.bytes < need) {
-            // earlier calls on this stream may still read the old buffer: wait for them
-            hipError_t r = hipStreamSynchronize(stream);
-            if (r == hipSuccess) r = hipFree(e.ptr);
-            if (r != hipSuccess) return r;
-            e.ptr = nullptr;
-            e.bytes = 0;
-            r = hipMalloc(reinterpret_cast<void**>(&e.ptr), need);
-            if (r != hipSuccess) return r;
-            e.bytes = need;
-        }
-        *out = e.ptr;
-        return hipSuccess;
+// Library-owned device workspaces of the linear forwards, one per (device, stream). A forward
+// holds the pool's lock from taking its workspace until its launches are queued and an event is
+// recorded behind them (WsLease::queued). A buffer is freed only after its entry's event has
+// completed: when it must grow, or when its device has more than kMaxWsPerDevice entries and it
+// is the least recently used one (the stream it served may be gone; its event is still valid).
+// So no queued launch reads freed memory, and no caller holds a pointer that another frees.
+struct WsEntry {
+    int device;
+    hipStream_t stream;
+    void* ptr;
+    size_t bytes;
+    hipEvent_t done;            // recorded behind the last forward that used the buffer
+    uint64_t tick;              // last use, for eviction
+};
+constexpr int kMaxWsPerDevice = 4;
+std::mutex g_ws_mu;
+std::vector<WsEntry> g_ws;
+uint64_t g_ws_tick = 0;
+
+hipError_t ws_retire(WsEntry& e) {
+    hipError_t r = hipSuccess;
+    if (e.done) {
+        r = hipEventSynchronize(e.done);
+        const hipError_t r2 = hipEventDestroy(e.done);
+        if (r == hipSuccess) r = r2;
+        e.done = nullptr;
     }
-    Entry e{device, stream, nullptr, need};
-    hipError_t r = hipMalloc(reinterpret_cast<void**>(&e.ptr), need);
-    if (r != hipSuccess) return r;
-    pool.push_back(e);
-    *out = e.ptr;
+    if (e.ptr) {
+        const hipError_t r2 = hipFree(e.ptr);
+        if (r == hipSuccess) r = r2;
+        e.ptr = nullptr;
+    }
+    e.bytes = 0;
+    return r;
+}
+
+// Device scratch of one forward: the pool's buffer for (device, stream), held under the pool lock.
+struct WsLease {
+    std::unique_lock<std::mutex> lock;
+    WsEntry* entry = nullptr;
+    hipStream_t stream = nullptr;
+    void* ptr = nullptr;
+    size_t bytes = 0;
+    // After the forward's launches are queued: mark the buffer as in use by them.
+    hipError_t queued() { return entry ? hipEventRecord(entry->done, stream) : hipSuccess; }
+};
+
+hipError_t ws_acquire(int device, hipStream_t stream, size_t need, WsLease* L) {
+    L->lock = std::unique_lock<std::mutex>(g_ws_mu);
+    L->stream = stream;
+    WsEntry* e = nullptr;
+    for (WsEntry& x : g_ws)
+        if (x.device == device && x.stream == stream) e = &x;
+    if (!e) {
+        int count = 0;
+        size_t lru = g_ws.size();
+        for (size_t i = 0; i < g_ws.size(); ++i) {
+            if (g_ws[i].device != device) continue;
+            ++count;
+            if (lru == g_ws.size() || g_ws[i].tick < g_ws[lru].tick) lru = i;
+        }
+        if (count >= kMaxWsPerDevice) {
+            hipError_t r = ws_retire(g_ws[lru]);
+            g_ws.erase(g_ws.begin() + (std::ptrdiff_t)lru);
+            if (r != hipSuccess) return r;
+        }
+        WsEntry n{device, stream, nullptr, 0, nullptr, 0};
+        hipError_t r = hipEventCreateWithFlags(&n.done, hipEventDisableTiming);
+        if (r != hipSuccess) return r;
+        g_ws.push_back(n);
+        e = &g_ws.back();
+    }
+    if (e->bytes < need) {
+        // earlier forwards on this stream may still read the old buffer: wait for them
+        hipError_t r = hipEventSynchronize(e->done);
+        if (r == hipSuccess && e->ptr) r = hipFree(e->ptr);
+        e->ptr = nullptr;
+        e->bytes = 0;
+        if (r != hipSuccess) return r;
+        r = hipMalloc(&e->ptr, need);
+        if (r != hipSuccess) {
+            e->ptr = nullptr;
+            return r;
+        }
+        e->bytes = need;
+    }
+    e->tick = ++g_ws_tick;
+    L->entry = e;
+    L->ptr = e->ptr;
+    L->bytes = e->bytes;
     return hipSuccess;
 }
 
@@ -196,6 +253,74 @@ ep_status check_decode_args(const ep_handle* h, ep_dtype ct, void* out, float* s
     if (wants_scale && !scale && h->view.rows > 0) return fail(EP_EINVAL, "F8E4M3 and I8 need a row-scale output");
     if (!wants_scale && scale) return fail(EP_EINVAL, "row-scale output given for a container without one");
     return EP_OK;
+}
+
+// Compressed linear forward. The weight is decoded once per call, one slice of output rows at a
+// time, into the forward's scratch, and each slice's GEMM writes its columns of Y. A slice of at
+// most kSliceBytes is large enough to keep every CU's decode block busy and, with the
+// activations, small enough to stay in the 256 MB Infinity Cache between the decode that writes
+// it and the GEMM that reads it (128 MiB measured best against 64 and 256 for M = 256 ... 4096).
+ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias, void* dev_y,
+                         hipStream_t s) {
+    constexpr size_t kSliceBytes = 128u << 20;
+    if (!w) return fail(EP_EINVAL, "null handle");
+    if (ep_status st = on_its_device(w); st != EP_OK) return st;
+    if (w->view.mode != EP_MODE_LOSSY_E8) return fail(EP_EUNSUPPORTED, "the linear forward takes a lossy stream");
+    const int64_t N = w->view.rows, K = w->view.cols;
+    if (M < 0) return fail(EP_EINVAL, "negative M");
+    if (M == 0 || N == 0) return EP_OK;
+    if (!dev_x || !dev_y) return fail(EP_EINVAL, "null pointer");
+    if (K % 8 || M > INT32_MAX) return fail(EP_EINVAL, "in_features must be a multiple of 8");
+    if (reinterpret_cast<uintptr_t>(dev_x) & 15) return fail(EP_EINVAL, "X must be 16-byte aligned");
+    int dev = 0;
+    hipError_t he = hipGetDevice(&dev);
+    if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
+    WsLease ws;
+    if (M <= 4) {
+        // a few activation rows: decoding fused with the matrix-vector products, the weight never
+        // written out; fp32 accumulation in the scratch, then rounding (+ bias) to BF16
+        const size_t need = sizeof(float) * (size_t)M * (size_t)N;
+        if ((he = ws_acquire(dev, s, need, &ws)) != hipSuccess) {
+            return hip_fail(he, "hipMalloc for the linear forward workspace");
+        }
+        float* yacc = static_cast<float*>(ws.ptr);
+        ep::MatDesc d = desc_for(w, M == 1 ? ep::CT_GEMV1 : M == 2 ? ep::CT_GEMV2 : ep::CT_GEMV4, yacc, nullptr);
+        d.gemv_x = static_cast<const uint16_t*>(dev_x);
+        d.gemv_m = (uint8_t)M;
+        hipError_t e = ep::launch_gemv_zero(yacc, M * N, s);
+        if (e == hipSuccess) e = ep::launch_gemv(d, s);
+        if (e == hipSuccess)
+            e = ep::launch_gemv_finish(yacc, static_cast<const uint16_t*>(dev_bias), static_cast<uint16_t*>(dev_y), M, N, s);
+        if (e == hipSuccess) e = ws.queued();
+        return e == hipSuccess ? EP_OK : hip_fail(e, "fused matrix-vector launch");
+    }
+    const int tr = w->view.tile_rows;
+    int64_t slice = (int64_t)(kSliceBytes / (2 * (size_t)K)) / tr * tr;
+    if (slice < tr) slice = tr;
+    if (slice > N) slice = (N + tr - 1) / tr * tr;
+    const size_t need = (size_t)slice * (size_t)K * 2;
+    if ((he = ws_acquire(dev, s, need, &ws)) != hipSuccess) {
+        return hip_fail(he, "hipMalloc for the linear forward workspace");
+    }
+    uint16_t* scratch = static_cast<uint16_t*>(ws.ptr);
+    const ep::MatDesc full = desc_for(w, ep::CT_BF16, scratch, nullptr);
+    for (int64_t r0 = 0; r0 < N; r0 += slice) {
+        const int64_t rows = std::min<int64_t>(slice, N - r0);
+        ep::MatDesc d = full;                  // rows r0 .. r0 + rows of the weight
+        d.index += (size_t)(r0 / tr) * w->view.tiles_c;
+        d.row_scale += r0;
+        d.row_qmax += r0;
+        d.rows = (uint32_t)rows;
+        hipError_t e = ep::launch_group(&d, 1, s);
+        if (e != hipSuccess) return hip_fail(e, "slice decode launch");
+        ep::GemmArgs g{static_cast<const uint16_t*>(dev_x), scratch,
+                       dev_bias ? static_cast<const uint16_t*>(dev_bias) + r0 : nullptr,
+                       static_cast<uint16_t*>(dev_y) + r0, (int)M, (int)rows, (int)K, (int)K, (int)K, (int)N};
+        e = ep::launch_gemm(g, s);
+        if (e != hipSuccess) return hip_fail(e, "slice gemm launch");
+    }
+    he = ws.queued();
+    return he == hipSuccess ? EP_OK : hip_fail(he, "recording the workspace event");
 }
 
 }  // namespace
@@ -389,70 +514,10 @@ ep_status ep_gemm_bf16(const void* dev_x, const void* dev_w, int64_t M, int64_t 
     });
 }
 
-// Compressed linear forward. The weight is decoded once per call, one slice of output rows at a
-// time, into the (device, stream) workspace of at most kSliceBytes, and each slice's GEMM writes
-// its columns of Y. A slice is large enough to keep every CU's decode block busy and, with the
-// activations, small enough to stay in the 256 MB Infinity Cache between the decode that writes
-// it and the GEMM that reads it (128 MiB measured best against 64 and 256 for M = 256 ... 4096).
 ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias, void* dev_y,
                             void* hip_stream) {
     return guarded([&]() -> ep_status {
-        constexpr size_t kSliceBytes = 128u << 20;
-        if (!w) return fail(EP_EINVAL, "null handle");
-        if (ep_status st = on_its_device(w); st != EP_OK) return st;
-        if (w->view.mode != EP_MODE_LOSSY_E8) return fail(EP_EUNSUPPORTED, "the linear forward takes a lossy stream");
-        const int64_t N = w->view.rows, K = w->view.cols;
-        if (M < 0) return fail(EP_EINVAL, "negative M");
-        if (M == 0 || N == 0) return EP_OK;
-        if (!dev_x || !dev_y) return fail(EP_EINVAL, "null pointer");
-        if (K % 8 || M > INT32_MAX) return fail(EP_EINVAL, "in_features must be a multiple of 8");
-        if (reinterpret_cast<uintptr_t>(dev_x) & 15) return fail(EP_EINVAL, "X must be 16-byte aligned");
-        hipStream_t s = static_cast<hipStream_t>(hip_stream);
-        if (M <= 4) {
-            // a few activation rows: decoding fused with the matrix-vector products, the weight never
-            // written out; fp32 accumulation in the workspace, then rounding (+ bias) to BF16
-            uint16_t* acc = nullptr;
-            int dev = 0;
-            hipError_t we = hipGetDevice(&dev);
-            if (we == hipSuccess) we = workspace(dev, s, sizeof(float) * (size_t)M * (size_t)N, &acc);
-            if (we != hipSuccess) return hip_fail(we, "hipMalloc for the linear forward workspace");
-            float* yacc = reinterpret_cast<float*>(acc);
-            ep::MatDesc d = desc_for(w, M == 1 ? ep::CT_GEMV1 : M == 2 ? ep::CT_GEMV2 : ep::CT_GEMV4, yacc, nullptr);
-            d.gemv_x = static_cast<const uint16_t*>(dev_x);
-            d.gemv_m = (uint8_t)M;
-            hipError_t e = ep::launch_gemv_zero(yacc, M * N, s);
-            if (e == hipSuccess) e = ep::launch_gemv(d, s);
-            if (e == hipSuccess)
-                e = ep::launch_gemv_finish(yacc, static_cast<const uint16_t*>(dev_bias), static_cast<uint16_t*>(dev_y), M, N, s);
-            return e == hipSuccess ? EP_OK : hip_fail(e, "fused matrix-vector launch");
-        }
-        const int tr = w->view.tile_rows;
-        int64_t slice = (int64_t)(kSliceBytes / (2 * (size_t)K)) / tr * tr;
-        if (slice < tr) slice = tr;
-        if (slice > N) slice = (N + tr - 1) / tr * tr;
-        const size_t need = (size_t)slice * (size_t)K * 2;
-        uint16_t* scratch = nullptr;
-        int dev = 0;
-        hipError_t we = hipGetDevice(&dev);
-        if (we == hipSuccess) we = workspace(dev, s, need, &scratch);
-        if (we != hipSuccess) return hip_fail(we, "hipMalloc for the linear forward workspace");
-        const ep::MatDesc full = desc_for(w, ep::CT_BF16, scratch, nullptr);
-        for (int64_t r0 = 0; r0 < N; r0 += slice) {
-            const int64_t rows = std::min<int64_t>(slice, N - r0);
-            ep::MatDesc d = full;                  // rows r0 .. r0 + rows of the weight
-            d.index += (size_t)(r0 / tr) * w->view.tiles_c;
-            d.row_scale += r0;
-            d.row_qmax += r0;
-            d.rows = (uint32_t)rows;
-            hipError_t e = ep::launch_group(&d, 1, s);
-            if (e != hipSuccess) return hip_fail(e, "slice decode launch");
-            ep::GemmArgs g{static_cast<const uint16_t*>(dev_x), scratch,
-                           dev_bias ? static_cast<const uint16_t*>(dev_bias) + r0 : nullptr,
-                           static_cast<uint16_t*>(dev_y) + r0, (int)M, (int)rows, (int)K, (int)K, (int)K, (int)N};
-            e = ep::launch_gemm(g, s);
-            if (e != hipSuccess) return hip_fail(e, "slice gemm launch");
-        }
-        return EP_OK;
+        return linear_forward(w, dev_x, M, dev_bias, dev_y, static_cast<hipStream_t>(hip_stream));
     });
 }
 
@@ -539,12 +604,12 @@ ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M
         const size_t o_xs = up((size_t)M * (size_t)K, 256), o_wq = up(o_xs + 4 * (size_t)M, 256);
         const size_t o_ws = up(o_wq + (size_t)slice * (size_t)K, 256), need = o_ws + 4 * (size_t)slice;
         hipStream_t s = static_cast<hipStream_t>(hip_stream);
-        uint16_t* base = nullptr;
         int dev = 0;
         hipError_t we = hipGetDevice(&dev);
-        if (we == hipSuccess) we = workspace(dev, s, need, &base);
+        WsLease ws;
+        if (we == hipSuccess) we = ws_acquire(dev, s, need, &ws);
         if (we != hipSuccess) return hip_fail(we, "hipMalloc for the linear forward workspace");
-        uint8_t* ws8 = reinterpret_cast<uint8_t*>(base);
+        uint8_t* ws8 = static_cast<uint8_t*>(ws.ptr);
         uint8_t* xq = ws8;
         float* xs = reinterpret_cast<float*>(ws8 + o_xs);
         uint8_t* wq = ws8 + o_wq;
@@ -567,7 +632,8 @@ ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M
             e = ep::launch_gemm_f8(g, s);
             if (e != hipSuccess) return hip_fail(e, "slice fp8 gemm launch");
         }
-        return EP_OK;
+        e = ws.queued();
+        return e == hipSuccess ? EP_OK : hip_fail(e, "recording the workspace event");
     });
 }
 

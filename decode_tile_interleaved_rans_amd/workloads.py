@@ -87,6 +87,20 @@ def mixed_rate_set(count: int = 64, seed: int = 5):
     return out
 
 
+def gpu_student_t(rows: int, cols: int, seed: int, scale: float = 0.02):
+    """scale * t(nu=5) as a BF16 torch tensor drawn on the current GPU: z / sqrt(chi2_5 / 5) from six
+    normals of torch's generator seeded with `seed`, so that large weight sets need no host
+    generation (the benchmark's full-model and mixed-rate sets, and their parity tests)."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    z = torch.randn((rows, cols), generator=g, device="cuda")
+    v = torch.zeros((rows, cols), device="cuda")
+    for _ in range(5):
+        v += torch.randn((rows, cols), generator=g, device="cuda").square()
+    return (scale * z / torch.sqrt(v / 5.0)).to(torch.bfloat16)
+
+
 def prefill_case(seed_w: int = 4, seed_x: int = 4004, n: int = 8192, k: int = 8192, m: int = 4096):
     """Fused-GEMM prefill case: W bf16 [n, k] = 0.02 t5 and X bf16 [m, k] ~ N(0, 1)."""
     return student_t(n, k, seed_w, 0.02), activations(m, k, seed_x)

@@ -88,6 +88,11 @@ typedef struct {
 typedef struct ep_handle ep_handle;   /* device-resident, validated stream */
 
 /* Compress a host matrix.
+ * Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", sections "Choose a compression
+ * contract" (a lossless BF16 config, lossless tile ANS across dtypes, a lossy target bitrate) and
+ * "Start with a tensor round trip" (the stored size, metadata included, is what counts); the lossy
+ * steps follow "EntroPack: Fast and Accurate Entropy-Coded Weight Compression at Arbitrary Bitrates",
+ * Abstract; readings R1-R16 fix what the pages leave open.
  *   host_w: [rows][cols] elements of dtype src (lossy: EP_F32, EP_BF16, EP_F16; lossless: any;
  *           exponent-coded lossless: EP_BF16).
  *   *out_stream receives a library-allocated byte buffer (free with ep_free), *out_len its size,
@@ -100,10 +105,11 @@ ep_status ep_compress(const void* host_w, ep_dtype src, int64_t rows, int64_t co
 
 /* Device encoder of the lossy mode: the same stream as ep_compress, byte for byte, computed on the
  * GPU from a weight already in device memory (row scales, the sampled rate search, the E8
- * quantization, the model and the tile rANS coding all run as kernels; the method's "fast
- * encoding", "EntroPack: Fast and Accurate Entropy-Coded Weight Compression at Arbitrary
- * Bitrates", Abstract). dev_w: [rows][cols] elements of src (EP_F32, EP_BF16, EP_F16) on the
- * current device; opts as for ep_compress (mode must be EP_MODE_LOSSY_E8; n_threads is unused).
+ * quantization, the model and the tile rANS coding all run as kernels).
+ * Source: "EntroPack: Fast and Accurate Entropy-Coded Weight Compression at Arbitrary Bitrates", Abstract (fast
+ * encoding); "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section
+ * "Replace one linear layer before a whole model" (conversion cost kept apart from inference).
+ * dev_w: [rows][cols] elements of src (EP_F32, EP_BF16, EP_F16) on the current device; opts as for ep_compress (mode must be EP_MODE_LOSSY_E8; n_threads is unused).
  * The call synchronizes hip_stream. Device scratch (about 2.3 bytes per weight plus 18 KiB per
  * 16-row tile for the word stacks) is kept per device after the call, grown to the largest
  * matrix encoded, and reused; concurrent calls on one device take turns. *out_stream is
@@ -113,26 +119,43 @@ ep_status ep_compress_device(const void* dev_w, ep_dtype src, int64_t rows, int6
                              const ep_encode_opts* opts, void* hip_stream, uint8_t** out_stream,
                              size_t* out_len, double* actual_bpp);
 
-/* Free a buffer returned by ep_compress or ep_compress_device. NULL is allowed. */
+/* Free a buffer returned by ep_compress or ep_compress_device. NULL is allowed.
+ * Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section
+ * "Start with a tensor round trip" (the stored representation ep_compress returns belongs to the
+ * caller). */
 void ep_free(void* p);
 
-/* Validate a host stream (magic, format version 2, section bounds, every table summing to 2^n,
+/* Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", sections
+ * "Start with a tensor round trip" (record the actual stored size and its metadata) and "Diagnose
+ * compression failures in the correct order" (the saved object must hold everything the decoder
+ * needs); reading R22 (three CRC-32s).
+ * Validate a host stream (magic, format version 2, section bounds, every table summing to 2^n,
  * tile offsets, and three CRC-32s: the payload's, the raw plane's and the metadata's, which
  * covers every other byte, so any single-bit corruption is refused) and summarize it. Host only;
  * no device work. EP_ECORRUPT on any inconsistency. */
 ep_status ep_stream_info(const uint8_t* host_stream, size_t len, ep_info* out);
 
-/* Validate a host stream and copy it to the current device together with its decode tables.
+/* Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", sections
+ * "Diagnose compression failures in the correct order" (a stream is checked before the decoder
+ * trusts it) and "Measure memory with clear boundaries" (loading is its own phase, apart from the
+ * inference call); reading R22.
+ * Validate a host stream and copy it to the current device together with its decode tables.
  * Synchronizes hip_stream before returning (the host buffer may be freed afterwards).
  * *out receives the handle. Errors: EP_ECORRUPT, EP_ERANGE (a tile payload of 4 GiB or more,
  * beyond the decoder's 32-bit payload addressing: code such a matrix as several streams),
  * EP_ENOMEM, EP_EHIP. */
 ep_status ep_upload(const uint8_t* host_stream, size_t len, void* hip_stream, ep_handle** out);
 
-/* Summary of an uploaded stream (same fields as ep_stream_info). */
+/* Summary of an uploaded stream (same fields as ep_stream_info).
+ * Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section
+ * "Start with a tensor round trip" (record the stored size). */
 ep_status ep_handle_info(const ep_handle* h, ep_info* out);
 
 /* Decode a whole matrix into a device container (the "decompress" call).
+ * Source: "EntroPack: Fast and Accurate Entropy-Coded Weight Compression at Arbitrary Bitrates", Abstract
+ * (fused symbol decoding and weight reconstruction on the GPU into BF16, FP16, FP8 or INT8, the
+ * bitrate independent of the container); "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section "Diagnose compression failures in the correct order" (no silent
+ * cast of the restored tensor: a container the stream cannot supply is refused); readings R17-R20.
  *   dev_out: [rows][cols] elements of `container`, row-major, 16-byte aligned when cols % 8 == 0
  *            for the vector-store path (any alignment of the element size is accepted).
  *   dev_row_scale: [rows] fp32 dequantization scales, written for EP_F8E4M3 and EP_I8 (the
@@ -142,21 +165,31 @@ ep_status ep_handle_info(const ep_handle* h, ep_info* out);
 ep_status ep_decompress(const ep_handle* h, ep_dtype container, void* dev_out,
                         float* dev_row_scale, void* hip_stream);
 
-/* Decode `count` matrices in one grouped launch. Arrays are host arrays of length count with
+/* Decode `count` matrices in one grouped launch.
+ * Source: "EntroPack: Fast and Accurate Entropy-Coded Weight Compression at Arbitrary Bitrates", Abstract
+ * (decode time grows with the weight count; diffusion denoising decodes every layer each step);
+ * "EntroPack 開源：模型壓縮不必只選 4 位元，如何配合顯示記憶體預算？", section "官方時間要保留原工作範圍"
+ * (the timing covers a whole denoise step). Arrays are host arrays of length count with
  * the same meaning as ep_decompress's arguments; NULL entries in dev_row_scales are allowed
  * where the container needs none. Asynchronous on hip_stream. */
 ep_status ep_decompress_many(const ep_handle* const* hs, const ep_dtype* containers,
                              void* const* dev_outs, float* const* dev_row_scales, int count,
                              void* hip_stream);
 
-/* Decode a lossy stream's lattice symbols: dev_q [rows][cols] int16 doubled coordinates
+/* Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section
+ * "Test saved artifacts and reloads before deployment" (the recovered quantized codes are what a
+ * quantize-then-entropy-code package reproduces exactly); readings R4, R7, R10.
+ * Decode a lossy stream's lattice symbols: dev_q [rows][cols] int16 doubled coordinates
  * q = 2p of the E8 point p (the reconstructed weight is q * step / 2 * row_scale).
  * EP_EUNSUPPORTED for lossless streams. Asynchronous on hip_stream. */
 ep_status ep_decode_symbols(const ep_handle* h, int16_t* dev_q, void* hip_stream);
 
 /* Compressed linear layer forward: Y[M][N] = X[M][K] * W^T (+ bias), W = the decoded BF16
- * weight [N][K] of handle w, fp32 accumulation, BF16 output ("EntroPack PyTorch Guide", section
- * "Replace one linear layer before a whole model"). For M <= 4 the decode kernel itself forms the
+ * weight [N][K] of handle w, fp32 accumulation, BF16 output.
+ * Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section
+ * "Replace one linear layer before a whole model" (CompressedLinear); "EntroPack: Fast and Accurate
+ * Entropy-Coded Weight Compression at Arbitrary Bitrates", Abstract (decoding fused into the GPU
+ * computation that uses the weight). For M <= 4 the decode kernel itself forms the
  * products (the decoded fp32 weights, not rounded to BF16, are multiplied by the activations in
  * registers and summed into an fp32 accumulator in the workspace by atomic additions, whose order
  * varies, so two calls may differ in the last bits; the weight is never written). For larger M
@@ -171,13 +204,19 @@ ep_status ep_decode_symbols(const ep_handle* h, int16_t* dev_q, void* hip_stream
 ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias,
                             void* dev_y, void* hip_stream);
 
-/* Plain BF16 GEMM, the one ep_linear_forward runs on each decoded slice, for overhead
+/* Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section
+ * "Replace one linear layer before a whole model" (evaluate the original layer beside the
+ * compressed copy on the same input): the uncompressed baseline of the compressed forward.
+ * Plain BF16 GEMM, the one ep_linear_forward runs on each decoded slice, for overhead
  * comparisons: Y[M][N] = X[M][K] * W^T, X [M][K] bf16, W [N][K] bf16, Y [M][N] bf16, fp32
  * accumulation. Requires K % 8 == 0 and 16-byte aligned X and W. Asynchronous on hip_stream. */
 ep_status ep_gemm_bf16(const void* dev_x, const void* dev_w, int64_t M, int64_t N, int64_t K,
                        void* dev_y, void* hip_stream);
 
-/* FP8 variant of ep_linear_forward: Y[M][N] = s_x[m] s_w[n] sum_k x8[m][k] w8[n][k] (+ bias), BF16
+/* Source: "EntroPack: Fast and Accurate Entropy-Coded Weight Compression at Arbitrary Bitrates",
+ * Abstract (the FP8 container); "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory
+ * Checks", section "Replace one linear layer before a whole model".
+ * FP8 variant of ep_linear_forward: Y[M][N] = s_x[m] s_w[n] sum_k x8[m][k] w8[n][k] (+ bias), BF16
  * output. The weight is decoded, slice by slice as in ep_linear_forward, into the FP8 E4M3
  * container with its per-row scale s_w (the FP8 container of "EntroPack: Fast and Accurate
  * Entropy-Coded Weight Compression at Arbitrary Bitrates", Abstract), the activations are
@@ -188,7 +227,9 @@ ep_status ep_gemm_bf16(const void* dev_x, const void* dev_w, int64_t M, int64_t 
 ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias,
                                 void* dev_y, void* hip_stream);
 
-/* Per-row FP8 E4M3 quantization of BF16 rows, as the FP8 forward applies it to its activations:
+/* Source: "EntroPack: Fast and Accurate Entropy-Coded Weight Compression at Arbitrary Bitrates", Abstract (FP8
+ * container); the activation scale rule is a reading (amax / 448 per row, like the weight rows).
+ * Per-row FP8 E4M3 quantization of BF16 rows, as the FP8 forward applies it to its activations:
  * amax = max |x| over the row (raised to 2^-100 when smaller, unless zero), scale = amax / 448,
  * code = E4M3(x * (448 / amax)) rounded to nearest even and saturated at +-448; a zero row gets
  * scale 0 and codes 0. dev_x: [M][K] bf16 (finite), dev_q: [M][K] codes, dev_scale: [M] fp32;
@@ -196,27 +237,39 @@ ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M
 ep_status ep_quantize_rows_fp8(const void* dev_x, int64_t M, int64_t K, uint8_t* dev_q, float* dev_scale,
                                void* hip_stream);
 
-/* Plain FP8 GEMM, the one ep_linear_forward_fp8 runs on each decoded slice, for overhead
+/* Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section
+ * "Replace one linear layer before a whole model" (the uncompressed baseline, here of the FP8
+ * forward).
+ * Plain FP8 GEMM, the one ep_linear_forward_fp8 runs on each decoded slice, for overhead
  * comparisons: Y[m][n] = xs[m] ws[n] sum_k xq[m][k] wq[n][k] (+ bias[n]); xq [M][K] and wq [N][K]
  * E4M3 codes (16-byte aligned), xs [M] and ws [N] fp32, bias [N] bf16 or NULL, Y [M][N] bf16.
  * Requires K % 16 == 0. Asynchronous on hip_stream. */
 ep_status ep_gemm_fp8(const uint8_t* dev_xq, const float* dev_xs, const uint8_t* dev_wq, const float* dev_ws,
                       int64_t M, int64_t N, int64_t K, const void* dev_bias, void* dev_y, void* hip_stream);
 
-/* Synchronize hip_stream and read the handle's device error flag, which kernels set when a
+/* Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section "Test
+ * saved artifacts and reloads before deployment" (a failed step must stop with a clear error);
+ * reading R12 (every lane ends at its initial state: a free integrity check).
+ * Synchronize hip_stream and read the handle's device error flag, which kernels set when a
  * tile's words run out or overrun, or a lane's final rANS state differs from its initial
  * value (or, as an internal consistency check, when a decode kernel finds its LDS tables
  * misplaced). EP_EDEVICE if set (the flag is then cleared), else EP_OK. */
 ep_status ep_handle_check(ep_handle* h, void* hip_stream);
 
 /* Free a handle and its device memory. NULL is allowed. The caller must ensure no queued
- * work still uses it. */
+ * work still uses it.
+ * Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section "Measure
+ * memory with clear boundaries" (the resident compressed weight is one device allocation). */
 void ep_release(ep_handle* h);
 
-/* Message for the last failed call on this thread ("" if none). */
+/* Message for the last failed call on this thread ("" if none).
+ * Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section "Test
+ * saved artifacts and reloads before deployment" (stop with a clear error). */
 const char* ep_last_error(void);
 
-/* Library build string (version, target architecture). */
+/* Library build string (version, target architecture).
+ * Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section "Check
+ * the installation and hardware combination" (record the library revision and the GPU). */
 const char* ep_version(void);
 
 #ifdef __cplusplus

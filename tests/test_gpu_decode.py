@@ -200,11 +200,15 @@ def test_degenerate_matrices():
     h.check()
 
 
-@pytest.mark.parametrize("dt", ["f16", "f32", "u8", "zeros"])
+@pytest.mark.parametrize("dt", ["f16", "f32", "u8", "f8e4m3", "i8", "zeros"])
 def test_lossless_other_dtypes(dt):
     rng = np.random.default_rng(6)
     shape = (37, 600)
-    if dt == "f16":
+    if dt == "f8e4m3":          # every E4M3 bit pattern occurs, NaN codes included
+        x, code, tdt = rng.integers(0, 256, shape).astype(np.uint8), ep.F8E4M3, torch.float8_e4m3fn
+    elif dt == "i8":
+        x, code, tdt = rng.integers(-128, 128, shape).astype(np.int8).view(np.uint8), ep.I8, torch.int8
+    elif dt == "f16":
         x, code, tdt = rng.normal(0, 1, shape).astype(np.float16).view(np.uint16), ep.F16, torch.float16
     elif dt == "f32":
         x, code, tdt = rng.normal(0, 1, shape).astype(np.float32).view(np.uint32), ep.F32, torch.float32

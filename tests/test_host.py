@@ -37,6 +37,18 @@ def test_library_exports_every_declared_symbol():
     assert b"gfx950" in L.ep_version()
 
 
+def test_every_declaration_cites_its_passage():
+    """Each exported call's comment names the page and section (or the reading) that defines it."""
+    src = open(os.path.join(ROOT, "include", "entropack.h")).read()
+    decls = list(re.finditer(r"^(?:const\s+)?\w+\*?\s+\**(ep_\w+)\s*\(", src, re.M))
+    assert len(decls) == len(declared_functions())
+    for m in decls:
+        before = src[:m.start()]
+        comment = before[before.rfind("/*"):]
+        assert comment.rstrip().endswith("*/"), m.group(1)
+        assert "Source:" in comment and ('"EntroPack' in comment or "reading R" in comment), m.group(1)
+
+
 def test_header_is_plain_c():
     # the C ABI header compiles as C11 on its own, warnings as errors (no C++ constructs leak)
     import subprocess
