@@ -40,11 +40,12 @@ PROFILE_C2 = os.path.join(ROOT, "profiles", "decode_group_4096sq_step.txt")
 
 
 def decode_source_sha() -> str:
-    """SHA-256 of the decode kernel's sources (the key of the committed counter summaries)."""
+    """SHA-256 of the decode kernel's sources, decode.hip, decode_core.h and kernels.h (the key of the
+    committed counter summaries)."""
     import hashlib
     src = os.path.join(ROOT, "decode_tile_interleaved_rans_amd", "csrc")
-    return hashlib.sha256(open(os.path.join(src, "decode.hip"), "rb").read() +
-                          open(os.path.join(src, "kernels.h"), "rb").read()).hexdigest()
+    return hashlib.sha256(b"".join(open(os.path.join(src, f), "rb").read()
+                                   for f in ("decode.hip", "decode_core.h", "kernels.h"))).hexdigest()
 
 
 def profiled_traffic(path: str):

@@ -15,6 +15,7 @@
 
 #include "entropack.h"
 #include "ep_internal.h"
+#include "fused.h"
 #include "gemm.h"
 #include "kernels.h"
 
@@ -293,6 +294,18 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
             e = ep::launch_gemv_finish(yacc, static_cast<const uint16_t*>(dev_bias), static_cast<uint16_t*>(dev_y), M, N, s);
         if (e == hipSuccess) e = ws.queued();
         return e == hipSuccess ? EP_OK : hip_fail(e, "fused matrix-vector launch");
+    }
+    if (const ep::MatDesc d = desc_for(w, ep::CT_BF16, nullptr, nullptr); ep::fused_fits(d, M)) {
+        // up to 64 activation rows: every tile pair decoded straight into the B operand of the
+        // BF16 MFMA (through LDS), its fp32 partial sums in the scratch, then summed in order
+        const size_t need = ep::fused_partial_bytes(d, M);
+        if ((he = ws_acquire(dev, s, need, &ws)) != hipSuccess) {
+            return hip_fail(he, "hipMalloc for the linear forward workspace");
+        }
+        hipError_t e = ep::launch_fused(d, static_cast<const uint16_t*>(dev_x), M, static_cast<float*>(ws.ptr),
+                                        static_cast<const uint16_t*>(dev_bias), static_cast<uint16_t*>(dev_y), s);
+        if (e == hipSuccess) e = ws.queued();
+        return e == hipSuccess ? EP_OK : hip_fail(e, "fused decode + MFMA launch");
     }
     const int tr = w->view.tile_rows;
     int64_t slice = (int64_t)(kSliceBytes / (2 * (size_t)K)) / tr * tr;
