@@ -26,7 +26,7 @@ STATUS = {0: "EP_OK", -1: "EP_EINVAL", -2: "EP_ECORRUPT", -3: "EP_EUNSUPPORTED",
 EXPORTS = ["ep_compress", "ep_free", "ep_stream_info", "ep_upload", "ep_handle_info", "ep_decompress",
            "ep_decompress_many", "ep_decode_symbols", "ep_linear_forward", "ep_gemm_bf16", "ep_handle_check",
            "ep_release", "ep_last_error", "ep_version", "ep_linear_forward_fp8", "ep_quantize_rows_fp8",
-           "ep_gemm_fp8", "ep_compress_device"]
+           "ep_gemm_fp8", "ep_compress_device", "ep_linear_forward_noalloc"]
 
 
 class EPError(RuntimeError):
@@ -75,6 +75,7 @@ def lib() -> C.CDLL:
         L.ep_decompress_many.argtypes = [vp, vp, vp, vp, C.c_int, vp]
         L.ep_decode_symbols.argtypes = [vp, vp, vp]
         L.ep_linear_forward.argtypes = [vp, vp, i64, vp, vp, vp]
+        L.ep_linear_forward_noalloc.argtypes = [vp, vp, i64, vp, vp, vp]
         L.ep_gemm_bf16.argtypes = [vp, vp, i64, i64, i64, vp, vp]
         L.ep_linear_forward_fp8.argtypes = [vp, vp, i64, vp, vp, vp]
         L.ep_quantize_rows_fp8.argtypes = [vp, i64, i64, vp, vp, vp]

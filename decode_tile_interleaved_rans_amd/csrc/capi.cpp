@@ -18,6 +18,7 @@
 #include "fused.h"
 #include "gemm.h"
 #include "kernels.h"
+#include "static_scratch.h"
 
 struct ep_handle {
     ep::StreamView view;        // header fields and tables (the view's byte pointers are not kept)
@@ -168,10 +169,11 @@ hipError_t ws_retire(WsEntry& e) {
     return r;
 }
 
-// Device scratch of one forward: the pool's buffer for (device, stream), held under the pool lock.
+// Device scratch of one forward: the pool's buffer for (device, stream), held under the pool
+// lock, or (no-allocation entry point) the caller-independent static buffer of the device.
 struct WsLease {
     std::unique_lock<std::mutex> lock;
-    WsEntry* entry = nullptr;
+    WsEntry* entry = nullptr;   // null for the static buffer
     hipStream_t stream = nullptr;
     void* ptr = nullptr;
     size_t bytes = 0;
@@ -256,13 +258,29 @@ ep_status check_decode_args(const ep_handle* h, ep_dtype ct, void* out, float* s
     return EP_OK;
 }
 
+// The device's static scratch for the no-allocation forward: the whole buffer, or EP_ERANGE when
+// a call needs more than it holds.
+ep_status take_static(size_t need, WsLease* L) {
+    if (need > ep::kStaticScratchBytes)
+        return fail(EP_ERANGE, "the call needs " + std::to_string(need) + " bytes of scratch, more than the " +
+                                   std::to_string(ep::kStaticScratchBytes) + " of the static buffer");
+    void* p = nullptr;
+    hipError_t e = ep::static_scratch(&p);
+    if (e != hipSuccess) return hip_fail(e, "locating the static scratch buffer");
+    L->entry = nullptr;
+    L->ptr = p;
+    L->bytes = ep::kStaticScratchBytes;
+    return EP_OK;
+}
+
 // Compressed linear forward. The weight is decoded once per call, one slice of output rows at a
 // time, into the forward's scratch, and each slice's GEMM writes its columns of Y. A slice of at
 // most kSliceBytes is large enough to keep every CU's decode block busy and, with the
 // activations, small enough to stay in the 256 MB Infinity Cache between the decode that writes
 // it and the GEMM that reads it (128 MiB measured best against 64 and 256 for M = 256 ... 4096).
+// `fixed`: the scratch is the device's static buffer (no allocation), whose size bounds the slice.
 ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias, void* dev_y,
-                         hipStream_t s) {
+                         hipStream_t s, bool fixed) {
     constexpr size_t kSliceBytes = 128u << 20;
     if (!w) return fail(EP_EINVAL, "null handle");
     if (ep_status st = on_its_device(w); st != EP_OK) return st;
@@ -281,7 +299,9 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
         // a few activation rows: decoding fused with the matrix-vector products, the weight never
         // written out; fp32 accumulation in the scratch, then rounding (+ bias) to BF16
         const size_t need = sizeof(float) * (size_t)M * (size_t)N;
-        if ((he = ws_acquire(dev, s, need, &ws)) != hipSuccess) {
+        if (fixed) {
+            if (ep_status st = take_static(need, &ws); st != EP_OK) return st;
+        } else if ((he = ws_acquire(dev, s, need, &ws)) != hipSuccess) {
             return hip_fail(he, "hipMalloc for the linear forward workspace");
         }
         float* yacc = static_cast<float*>(ws.ptr);
@@ -299,7 +319,9 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
         // up to 64 activation rows: every tile pair decoded straight into the B operand of the
         // BF16 MFMA (through LDS), its fp32 partial sums in the scratch, then summed in order
         const size_t need = ep::fused_partial_bytes(d, M);
-        if ((he = ws_acquire(dev, s, need, &ws)) != hipSuccess) {
+        if (fixed) {
+            if (ep_status st = take_static(need, &ws); st != EP_OK) return st;
+        } else if ((he = ws_acquire(dev, s, need, &ws)) != hipSuccess) {
             return hip_fail(he, "hipMalloc for the linear forward workspace");
         }
         hipError_t e = ep::launch_fused(d, static_cast<const uint16_t*>(dev_x), M, static_cast<float*>(ws.ptr),
@@ -308,11 +330,17 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
         return e == hipSuccess ? EP_OK : hip_fail(e, "fused decode + MFMA launch");
     }
     const int tr = w->view.tile_rows;
-    int64_t slice = (int64_t)(kSliceBytes / (2 * (size_t)K)) / tr * tr;
-    if (slice < tr) slice = tr;
+    const size_t cap = fixed ? ep::kStaticScratchBytes : kSliceBytes;
+    int64_t slice = (int64_t)(cap / (2 * (size_t)K)) / tr * tr;
+    if (slice < tr) {
+        if (fixed) return fail(EP_ERANGE, "in_features too large for the static scratch (one 16-row slice must fit)");
+        slice = tr;
+    }
     if (slice > N) slice = (N + tr - 1) / tr * tr;
     const size_t need = (size_t)slice * (size_t)K * 2;
-    if ((he = ws_acquire(dev, s, need, &ws)) != hipSuccess) {
+    if (fixed) {
+        if (ep_status st = take_static(need, &ws); st != EP_OK) return st;
+    } else if ((he = ws_acquire(dev, s, need, &ws)) != hipSuccess) {
         return hip_fail(he, "hipMalloc for the linear forward workspace");
     }
     uint16_t* scratch = static_cast<uint16_t*>(ws.ptr);
@@ -530,7 +558,14 @@ ep_status ep_gemm_bf16(const void* dev_x, const void* dev_w, int64_t M, int64_t 
 ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias, void* dev_y,
                             void* hip_stream) {
     return guarded([&]() -> ep_status {
-        return linear_forward(w, dev_x, M, dev_bias, dev_y, static_cast<hipStream_t>(hip_stream));
+        return linear_forward(w, dev_x, M, dev_bias, dev_y, static_cast<hipStream_t>(hip_stream), false);
+    });
+}
+
+ep_status ep_linear_forward_noalloc(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias,
+                                    void* dev_y, void* hip_stream) {
+    return guarded([&]() -> ep_status {
+        return linear_forward(w, dev_x, M, dev_bias, dev_y, static_cast<hipStream_t>(hip_stream), true);
     });
 }
 

@@ -204,6 +204,21 @@ ep_status ep_decode_symbols(const ep_handle* h, int16_t* dev_q, void* hip_stream
 ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias,
                             void* dev_y, void* hip_stream);
 
+/* For callers that cannot allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc): ep_linear_forward with its scratch in a static device array
+ * of 64 MiB per device instead of the library's workspace pool. It calls no hipMalloc, hipFree or
+ * allocating library routine; the array lives from library load until the process ends. Same
+ * arguments, results and paths as ep_linear_forward (the same kernels: for 5 <= M <= 64 the fused
+ * kernel's partial sums, for M <= 4 the fp32 accumulator, above that BF16 weight slices of at most
+ * 64 MiB, i.e. 64 MiB / (2 K) rows). EP_ERANGE when a call needs more than the array holds
+ * (M <= 4 with 4 M N > 64 MiB, the fused partials of very wide layers, or K > 2^21 for the slices).
+ * Every call on a device shares that device's array: calls that overlap in time on one device
+ * (other streams, other threads) race and must be serialized by the caller.
+ * Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section "Measure
+ * memory with clear boundaries" (temporary buffers of a call are part of its memory). */
+ep_status ep_linear_forward_noalloc(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias,
+                                    void* dev_y, void* hip_stream);
+
 /* Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section
  * "Replace one linear layer before a whole model" (evaluate the original layer beside the
  * compressed copy on the same input): the uncompressed baseline of the compressed forward.

@@ -1,0 +1,66 @@
+"""The no-allocation linear forward (ep_linear_forward_noalloc, for callers that cannot allocate
+device memory) against the pool-workspace forward (ep_linear_forward), both called through the C
+ABI, on two calls in a row with the second smaller than the first, on every forward path (fused
+matrix-vector products for M <= 4, the fused decode + MFMA kernel for 5 <= M <= 64, decode slices
++ GEMM above). Collected last: it runs after every other GPU test and also alone."""
+import ctypes as C
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import oracle
+import decode_tile_interleaved_rans_amd as ep
+from decode_tile_interleaved_rans_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def call(fn, h, x, bias):
+    M = x.shape[0]
+    y = torch.full((M, h.shape[0]), float("nan"), dtype=torch.bfloat16, device="cuda")
+    bp = C.c_void_p(bias.data_ptr()) if bias is not None else None
+    rc = fn(h.ptr, C.c_void_p(x.data_ptr()), M, bp, C.c_void_p(y.data_ptr()),
+            C.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0, ep.lib().ep_last_error()
+    return y
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+@pytest.mark.parametrize("Ms", [(96, 40), (4, 1), (300, 3)])
+def test_noalloc_forward_matches_pool_forward(Ms):
+    w = W.student_t(2048, 3072, seed=71)
+    s, _ = ep.compress(w, 4.0, dtype=ep.BF16)
+    h = ep.upload(s)
+    want, _ = oracle.decompress(s, oracle.BF16)
+    w_hat = W.bf16_bits_to_f32(want).astype(np.float64)
+    bias_bits = W.activations(1, 2048, 9)[0]
+    bias = bf16(bias_bits)
+    L = ep.lib()
+    for M in Ms:                                       # the second call is smaller than the first
+        xb = W.activations(M, 3072, 100 + M)
+        x = bf16(xb)
+        y_pool = call(L.ep_linear_forward, h, x, bias)
+        y_fixed = call(L.ep_linear_forward_noalloc, h, x, bias)
+        torch.cuda.synchronize()
+        h.check()
+        a = y_fixed.float().cpu().numpy()
+        b = y_pool.float().cpu().numpy()
+        assert np.isfinite(a).all()
+        if M > 4:
+            assert torch.equal(y_fixed, y_pool), M        # same kernels, deterministic order
+        else:
+            assert rel_l2(a, b) < 1e-3, M                 # fp32 atomics: summation order varies
+        ref = W.bf16_bits_to_f32(xb).astype(np.float64) @ w_hat.T + W.bf16_bits_to_f32(bias_bits)[None, :]
+        assert rel_l2(a, ref) < 2e-2, M
+    h.release()
