@@ -330,14 +330,19 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
         return e == hipSuccess ? EP_OK : hip_fail(e, "fused decode + MFMA launch");
     }
     const int tr = w->view.tile_rows;
-    const size_t cap = fixed ? ep::kStaticScratchBytes : kSliceBytes;
-    int64_t slice = (int64_t)(cap / (2 * (size_t)K)) / tr * tr;
+    // K splits of the GEMM, chosen for the whole layer so that every slice adds its partial sums in
+    // the same order; the split partial tiles of a slice follow its decoded rows in the scratch
+    const int splits = ep::gemm_splits((int)M, (int)N, (int)K);
+    const size_t part_per_row = splits > 1 ? (size_t)splits * (size_t)M * sizeof(float) : 0;
+    int64_t slice = (int64_t)(fixed ? ep::kStaticScratchBytes / (2 * (size_t)K + part_per_row)
+                                    : kSliceBytes / (2 * (size_t)K)) / tr * tr;
     if (slice < tr) {
         if (fixed) return fail(EP_ERANGE, "in_features too large for the static scratch (one 16-row slice must fit)");
         slice = tr;
     }
     if (slice > N) slice = (N + tr - 1) / tr * tr;
-    const size_t need = (size_t)slice * (size_t)K * 2;
+    const size_t slice_bytes = up((size_t)slice * (size_t)K * 2, 256);
+    const size_t need = slice_bytes + (size_t)slice * part_per_row;
     if (fixed) {
         if (ep_status st = take_static(need, &ws); st != EP_OK) return st;
     } else if ((he = ws_acquire(dev, s, need, &ws)) != hipSuccess) {
@@ -357,6 +362,9 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
         ep::GemmArgs g{static_cast<const uint16_t*>(dev_x), scratch,
                        dev_bias ? static_cast<const uint16_t*>(dev_bias) + r0 : nullptr,
                        static_cast<uint16_t*>(dev_y) + r0, (int)M, (int)rows, (int)K, (int)K, (int)K, (int)N};
+        g.splits = splits;
+        g.part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws.ptr) + slice_bytes);
+        g.part_bytes = (size_t)slice * part_per_row;
         e = ep::launch_gemm(g, s);
         if (e != hipSuccess) return hip_fail(e, "slice gemm launch");
     }
@@ -549,7 +557,20 @@ ep_status ep_gemm_bf16(const void* dev_x, const void* dev_w, int64_t M, int64_t 
             return fail(EP_EINVAL, "X and W must be 16-byte aligned");
         ep::GemmArgs g{static_cast<const uint16_t*>(dev_x), static_cast<const uint16_t*>(dev_w), nullptr,
                        static_cast<uint16_t*>(dev_y), (int)M, (int)N, (int)K, (int)K, (int)K, (int)N};
-        hipError_t e = ep::launch_gemm(g, static_cast<hipStream_t>(hip_stream));
+        hipStream_t s = static_cast<hipStream_t>(hip_stream);
+        g.splits = ep::gemm_splits((int)M, (int)N, (int)K);
+        WsLease ws;
+        if (g.splits > 1) {
+            // the fp32 partial tiles of a split-K product live in the stream's workspace
+            int dev = 0;
+            hipError_t he = hipGetDevice(&dev);
+            g.part_bytes = (size_t)g.splits * (size_t)M * (size_t)N * sizeof(float);
+            if (he == hipSuccess) he = ws_acquire(dev, s, g.part_bytes, &ws);
+            if (he != hipSuccess) return hip_fail(he, "hipMalloc for the GEMM workspace");
+            g.part = static_cast<float*>(ws.ptr);
+        }
+        hipError_t e = ep::launch_gemm(g, s);
+        if (e == hipSuccess) e = ws.queued();
         if (e != hipSuccess) return hip_fail(e, "gemm launch");
         return EP_OK;
     });
@@ -644,6 +665,29 @@ ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M
         if (!dev_x || !dev_y) return fail(EP_EINVAL, "null pointer");
         if (K % 16 || M > INT32_MAX) return fail(EP_EINVAL, "in_features must be a multiple of 16 for the FP8 forward");
         if (reinterpret_cast<uintptr_t>(dev_x) & 15) return fail(EP_EINVAL, "X must be 16-byte aligned");
+        hipStream_t s = static_cast<hipStream_t>(hip_stream);
+        int dev = 0;
+        hipError_t we = hipGetDevice(&dev);
+        if (we != hipSuccess) return hip_fail(we, "hipGetDevice");
+        if (const ep::MatDesc d = desc_for(w, ep::CT_F8E4M3, nullptr, nullptr); ep::fused_fits(d, M)) {
+            // up to 64 activation rows: the activations quantized per row, then every tile pair
+            // decoded straight into E4M3 codes as the B operand of the FP8 MFMA (through LDS)
+            // workspace: X codes [M][K] | X scales [M] | fp32 partial sums
+            const size_t o_xs = up((size_t)M * (size_t)K, 256), o_pt = up(o_xs + 4 * (size_t)M, 256);
+            const size_t need = o_pt + ep::fused_partial_bytes(d, M);
+            WsLease ws;
+            if ((we = ws_acquire(dev, s, need, &ws)) != hipSuccess)
+                return hip_fail(we, "hipMalloc for the linear forward workspace");
+            uint8_t* ws8 = static_cast<uint8_t*>(ws.ptr);
+            float* xs = reinterpret_cast<float*>(ws8 + o_xs);
+            hipError_t e = ep::launch_quantize_rows_f8(static_cast<const uint16_t*>(dev_x), (int)M, (int)K, (int)K, ws8,
+                                                       (int)K, xs, s);
+            if (e == hipSuccess)
+                e = ep::launch_fused_f8(d, ws8, xs, M, reinterpret_cast<float*>(ws8 + o_pt),
+                                        static_cast<const uint16_t*>(dev_bias), static_cast<uint16_t*>(dev_y), s);
+            if (e == hipSuccess) e = ws.queued();
+            return e == hipSuccess ? EP_OK : hip_fail(e, "fused FP8 decode + MFMA launch");
+        }
         const int tr = w->view.tile_rows;
         int64_t slice = (int64_t)(kSliceBytes / (size_t)K) / tr * tr;
         if (slice < tr) slice = tr;
@@ -651,11 +695,8 @@ ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M
         // workspace: X codes [M][K] | X scales [M] | weight codes [slice][K] | weight scales [slice]
         const size_t o_xs = up((size_t)M * (size_t)K, 256), o_wq = up(o_xs + 4 * (size_t)M, 256);
         const size_t o_ws = up(o_wq + (size_t)slice * (size_t)K, 256), need = o_ws + 4 * (size_t)slice;
-        hipStream_t s = static_cast<hipStream_t>(hip_stream);
-        int dev = 0;
-        hipError_t we = hipGetDevice(&dev);
         WsLease ws;
-        if (we == hipSuccess) we = ws_acquire(dev, s, need, &ws);
+        we = ws_acquire(dev, s, need, &ws);
         if (we != hipSuccess) return hip_fail(we, "hipMalloc for the linear forward workspace");
         uint8_t* ws8 = static_cast<uint8_t*>(ws.ptr);
         uint8_t* xq = ws8;

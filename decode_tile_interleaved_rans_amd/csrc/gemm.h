@@ -13,10 +13,23 @@ struct GemmArgs {
     const uint16_t* bias;   // [N] bf16 or null
     uint16_t* Y;            // [M][ldy] bf16
     int M, N, K, ldx, ldw, ldy;
+    int splits = 1;         // K splits (gemm_splits); above 1 the scratch below holds the partials
+    float* part = nullptr;  // fp32 [splits][M][N] partial tiles
+    size_t part_bytes = 0;  // its size
+    int kc = 0;             // K columns per split (set by the launcher)
 };
 
-// Requires K % 8 == 0 and 16-byte aligned rows (ldx, ldw multiples of 8, aligned bases).
+// Requires K % 8 == 0 and 16-byte aligned rows (ldx, ldw multiples of 8, aligned bases). With
+// splits > 1 every 256 x 256 output tile is computed by `splits` blocks over consecutive K ranges
+// of split_columns(K, splits) columns, whose fp32 partial tiles are then added in split order
+// (deterministic; hipErrorInvalidValue when the scratch is missing or short).
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
+
+// K splits for an M x N x K product: 1 for M <= 64 or when the 256 x 256 tiles fill the CUs, else
+// as many as fill the CUs, at most 8, each at least 256 columns. The result of an output element
+// depends only on (K, splits), so slices of N computed with the layer's count give the same bits.
+int gemm_splits(int M, int N, int K);
+int split_columns(int K, int splits);
 
 // FP8 GEMM: Y[m][n] = sx[m] * sw[n] * sum_k X[m][k] W[n][k] (+ bias[n]), X and W OCP E4M3 codes,
 // fp32 accumulation, BF16 output.

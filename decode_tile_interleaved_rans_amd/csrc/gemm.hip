@@ -218,7 +218,9 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, int ld, int 
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, bool BIAS>
+// SPLIT: blockIdx.y is the split index; the block multiplies K columns [split * g.kc, + g.kc) and
+// writes its fp32 partial tile to g.part[split][M][N] (gemm_split_sum adds the splits in order).
+template <int BM, int BN, int WGM, int WGN, bool BIAS, bool SPLIT = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_dma(GemmArgs g) {
     constexpr int NW = WGM * WGN;
     constexpr int TI = BM / WGM / 16, TJ = BN / WGN / 16;     // 16 x 16 MFMA tiles per wave
@@ -244,17 +246,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_dma(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{};
 
-    dma_tile<BM, NW>(rx, g.ldx, 0, g.K, lds);
-    dma_tile<BN, NW>(rw, g.ldw, 0, g.K, lds + BM * 128);
+    // K range of this block: all of K, or the split's g.kc columns (a multiple of BK)
+    const int kb = SPLIT ? (int)blockIdx.y * g.kc : 0;
+    const int ke = SPLIT ? (kb + g.kc < g.K ? kb + g.kc : g.K) : g.K;
+    dma_tile<BM, NW>(rx, g.ldx, kb, g.K, lds);
+    dma_tile<BN, NW>(rw, g.ldw, kb, g.K, lds + BM * 128);
     __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0): this wave's tile loads landed
     __syncthreads();
-    const int nk = (g.K + BK - 1) / BK;
+    const int nk = (ke - kb + BK - 1) / BK;
     for (int kt = 0; kt < nk; ++kt) {
         uint8_t* cur = lds + (kt & 1) * kStage;
         if (kt + 1 < nk) {
             uint8_t* nxt = lds + ((kt + 1) & 1) * kStage;
-            dma_tile<BM, NW>(rx, g.ldx, (kt + 1) * BK, g.K, nxt);
-            dma_tile<BN, NW>(rw, g.ldw, (kt + 1) * BK, g.K, nxt + BM * 128);
+            dma_tile<BM, NW>(rx, g.ldx, kb + (kt + 1) * BK, g.K, nxt);
+            dma_tile<BN, NW>(rw, g.ldw, kb + (kt + 1) * BK, g.K, nxt + BM * 128);
         }
 #pragma unroll
         for (int ks = 0; ks < BK; ks += 32) {
@@ -281,6 +286,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_dma(GemmArgs g) {
     }
 
     // C[4 (lane / 16) + r][lane % 16] of each 16 x 16 tile
+    if constexpr (SPLIT) {
+        float* part = g.part + (size_t)blockIdx.y * g.M * g.N;
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+                const int col = n0 + wn + 16 * j + (lane & 15);
+                if (col >= g.N) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = m0 + wm + 16 * i + 4 * (lane >> 4) + r;
+                    if (row < g.M) part[(size_t)row * g.N + col] = acc[i][j][r];
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -297,6 +318,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_dma(GemmArgs g) {
                 if (row + 1 < g.M) g.Y[(size_t)(row + 1) * g.ldy + col] = (uint16_t)(pk >> 16);
             }
         }
+}
+
+// Y [M][N] = sum over the splits of part[split][M][N] in split order (+ bias), BF16.
+__global__ __launch_bounds__(256) void gemm_split_sum(const float* part, int splits, const uint16_t* bias, uint16_t* Y,
+                                                      int M, int N, int ldy) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)M * N) return;
+    const int64_t plane = (int64_t)M * N;
+    float v = part[e];
+    for (int s = 1; s < splits; ++s) v += part[s * plane + e];
+    const int col = (int)(e % N), row = (int)(e / N);
+    if (bias) v += __uint_as_float((uint32_t)bias[col] << 16);
+    Y[(size_t)row * ldy + col] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
 }
 
 template <int BM, int BN, int WGM, int WGN>
@@ -698,6 +732,18 @@ hipError_t launch_quantize_rows_f8(const uint16_t* X, int M, int K, int ldx, uin
     return hipGetLastError();
 }
 
+int split_columns(int K, int splits) { return (K / splits + BK - 1) / BK * BK; }
+
+int gemm_splits(int M, int N, int K) {
+    if (M <= 64) return 1;
+    const long tiles256 = (long)((M + 255) / 256) * ((N + 255) / 256);
+    if (tiles256 >= device_cus()) return 1;
+    long s = (device_cus() + tiles256 - 1) / tiles256;
+    s = s < 8 ? s : 8;
+    while (s > 1 && K / s < 4 * BK) --s;
+    return (int)s;
+}
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
     // tile choice: the skinny kernel for a few rows of X; 256 x 256 tiles when every CU gets one,
@@ -707,6 +753,22 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
     if (g.M <= 64) return launch_skinny<4>(g, stream);
     const long tiles256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
     if (tiles256 >= device_cus()) return launch_dma<256, 256, 2, 4>(g, stream);
+    // too few 256 x 256 tiles to fill the CUs: K split over the blocks (the caller's choice, with
+    // room for the fp32 partial tiles), then the splits added in order
+    if (g.splits > 1) {
+        if (!g.part || g.part_bytes < (size_t)g.splits * g.M * g.N * sizeof(float)) return hipErrorInvalidValue;
+        GemmArgs h = g;
+        h.kc = split_columns(g.K, g.splits);
+        const int used = (g.K + h.kc - 1) / h.kc;
+        const dim3 grid((unsigned)tiles256, (unsigned)used);
+        hipLaunchKernelGGL((gemm_dma<256, 256, 2, 4, false, true>), grid, dim3(64 * 8), 0, stream, h);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t n = (int64_t)g.M * g.N;
+        hipLaunchKernelGGL(gemm_split_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, g.part, used, g.bias,
+                           g.Y, g.M, g.N, g.ldy);
+        return hipGetLastError();
+    }
     const long tiles128 = (long)((g.M + 127) / 128) * ((g.N + 127) / 128);
     if (tiles128 >= 2L * device_cus()) return launch_tiled<128, 128, 2, 2, kPrefetch>(g, stream);
     return launch_tiled<64, 64, 2, 2, kPrefetch>(g, stream);

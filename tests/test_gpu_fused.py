@@ -93,3 +93,32 @@ def test_full_size_layer_against_the_gemm_path():
     rows = [0, 7, 15]
     ref = W.bf16_bits_to_f32(xb[rows]).astype(np.float64) @ W.bf16_bits_to_f32(want).astype(np.float64).T
     assert rel_l2(y16[rows].float().cpu().numpy(), ref) < 5e-3
+
+
+def e4m3(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).double().numpy()
+
+
+@pytest.mark.parametrize("N,K,M,prob_bits", [(256, 1024, 16, 12), (200, 784, 33, 11), (48, 528, 64, 10),
+                                             (1000, 2048, 5, 11)])
+def test_fp8_fused_matches_oracle_codes(N, K, M, prob_bits):
+    """The FP8 forward for M <= 64 (the weight decoded into E4M3 codes straight into the B operand of
+    the FP8 MFMA): within 3e-3 of the fp64 product of the oracle's E4M3 weight codes and row scales
+    and the oracle's per-row activation codes and scales (K = 784 and 528: the last 32-code chunk
+    of a lane half past K)."""
+    w = W.student_t(N, K, seed=N + K)
+    s, _ = ep.compress(w, 4.5, dtype=ep.BF16, prob_bits=prob_bits)
+    bias_bits = W.activations(1, N, 3)[0]
+    layer = ep.CompressedLinear(s, bf16(bias_bits).cuda(), compute="fp8")
+    xb = W.activations(M, K, N + M)
+    x = bf16(xb).cuda()
+    y = layer(x)
+    y2 = layer(x)
+    torch.cuda.synchronize()
+    layer.handle.check()
+    wq, ws = oracle.decompress(s, oracle.F8E4M3)
+    xq, xs = oracle.quantize_rows_e4m3(xb)
+    ref = (e4m3(xq) @ e4m3(wq).T) * xs[:, None].astype(np.float64) * ws[None, :].astype(np.float64)
+    ref += W.bf16_bits_to_f32(bias_bits).astype(np.float64)[None, :]
+    assert rel_l2(y.float().cpu().numpy(), ref) < 3e-3
+    assert torch.equal(y, y2)

@@ -372,3 +372,19 @@ def test_matrix_vector_and_gemm_paths_agree():
     d = rel_l2(y4, y5[:4])
     print(f"M=4 (fused matrix-vector) vs M=5 (decode + GEMM): relative L2 {d:.2e}")
     assert d < 5e-3
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 8192, 2048), (300, 1000, 776), (512, 2048, 4096)])
+def test_split_k_gemm_is_deterministic_and_exact_to_fp32(M, N, K):
+    """Too few 256 x 256 tiles to fill the CUs: the K splits' fp32 partial tiles are added in split
+    order, so two calls give the same bits, and the result stays within the fp32 reference's bar."""
+    rng = np.random.default_rng(M + K)
+    x = W.to_bf16_bits(rng.normal(0, 1, (M, K)))
+    w = W.to_bf16_bits(rng.normal(0, 0.05, (N, K)))
+    X, Wt = bf16_tensor(x).cuda(), bf16_tensor(w).cuda()
+    y1 = ep.gemm_bf16(X, Wt)
+    y2 = ep.gemm_bf16(X, Wt)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    ref = W.bf16_bits_to_f32(x) @ W.bf16_bits_to_f32(w).T
+    assert rel_l2(y1.float().cpu().numpy(), ref) < 5e-3
