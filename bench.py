@@ -159,7 +159,8 @@ def fused_gemm_section(torch, ep, reps: int = 15):
     from decode_tile_interleaved_rans_amd import workloads as W
     w, xb = W.prefill_case()
     t0 = time.time()
-    s, bpp = ep.compress(w, 4.5, dtype=ep.BF16)
+    # coded as CompressedLinear.from_linear codes a layer: probability precision n = 11
+    s, bpp = ep.compress(w, 4.5, dtype=ep.BF16, prob_bits=ep.LAYER_PROB_BITS)
     log(f"encoded 8192x8192 at target 4.5: actual {bpp:.4f} bpp in {time.time() - t0:.2f} s")
     layer = ep.CompressedLinear(s)
     layer8 = ep.CompressedLinear(s, compute="fp8")
@@ -196,11 +197,11 @@ def fused_gemm_section(torch, ep, reps: int = 15):
     layer.handle.check()
     out = {"workload": "W 0.02 t5 bf16 [8192, 8192] at 4.5 bpp, X N(0,1) bf16 [M, 8192], Y = X W^T bf16, "
                        "fp32 accumulate",
-           "actual_bpp": round(bpp, 4), "stream_bytes": len(s), "decode_full_us": round(t_dec, 2),
+           "prob_bits": ep.LAYER_PROB_BITS, "actual_bpp": round(bpp, 4), "stream_bytes": len(s), "decode_full_us": round(t_dec, 2),
            "reps": reps, "timing": "median of per-rep HIP events, the five variants interleaved within each "
                                    "rep, 1 GiB cache flush before every timed call"}
     wq, ws = ep.quantize_rows_fp8(Wt)                  # plain FP8 baseline: the weight pre-quantized
-    for M in (4096, 256, 16, 1):
+    for M in (4096, 256, 64, 16, 1):
         X = Xf[:M].contiguous()
         xq, xs = ep.quantize_rows_fp8(X)
         (t_f, t_f_min), (t_o, _), (t_t, _), (t_f8, _), (t_o8, _) = timed(
@@ -435,6 +436,21 @@ def pmc_summary(path: str, kernel: str, skip: int) -> str:
     return "\n".join(lines)
 
 
+def pmc_table(path: str) -> str:
+    """Mean counter values per kernel of a rocprofv3 counter-collection CSV (one line per kernel and
+    counter: dispatches, mean)."""
+    import csv
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"]
+        key = (name[:120], r["Counter_Name"])
+        acc.setdefault(key, []).append(float(r["Counter_Value"]))
+    lines = []
+    for (name, c), v in sorted(acc.items()):
+        lines.append(f"{name} | {c} | dispatches {len(v)} | mean {np.mean(v):.1f}")
+    return "\n".join(lines)
+
+
 def mixed_section(torch, ep, steps: int = 5, reps: int = 5):
     """The 64-matrix mixed-rate set: rows and cols from {2048, 4096, 8192}, targets uniform in
     [2.5, 6.0] (workloads.mixed_rate_set), 1.55 G weights of 0.02 t5 BF16. The weights are drawn
@@ -550,6 +566,8 @@ def main():
                     help="profiling aid: time only the headline step (no other sections, no CPU baseline)")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="summarize a rocprofv3 kernel-trace CSV (no GPU work) and exit")
+    ap.add_argument("--pmc-table", metavar="CSV",
+                    help="mean counter values per kernel of a rocprofv3 counter CSV (no GPU work) and exit")
     ap.add_argument("--pmc-summary", metavar="CSV",
                     help="summarize a rocprofv3 counter-collection CSV (no GPU work) and exit")
     ap.add_argument("--kernel", default="decode_group", help="kernel name for --trace-summary / --pmc-summary")
@@ -557,6 +575,9 @@ def main():
     args = ap.parse_args()
     if args.trace_summary:
         print(trace_summary(args.trace_summary, args.kernel, args.skip))
+        return
+    if args.pmc_table:
+        print(pmc_table(args.pmc_table))
         return
     if args.pmc_summary:
         print(pmc_summary(args.pmc_summary, args.kernel, args.skip))

@@ -316,7 +316,7 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
         return e == hipSuccess ? EP_OK : hip_fail(e, "fused matrix-vector launch");
     }
     if (const ep::MatDesc d = desc_for(w, ep::CT_BF16, nullptr, nullptr); ep::fused_fits(d, M)) {
-        // up to 64 activation rows: every tile pair decoded straight into the B operand of the
+        // up to 16 activation rows: every tile pair decoded straight into the B operand of the
         // BF16 MFMA (through LDS), its fp32 partial sums in the scratch, then summed in order
         const size_t need = ep::fused_partial_bytes(d, M);
         if (fixed) {
@@ -670,7 +670,7 @@ ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M
         hipError_t we = hipGetDevice(&dev);
         if (we != hipSuccess) return hip_fail(we, "hipGetDevice");
         if (const ep::MatDesc d = desc_for(w, ep::CT_F8E4M3, nullptr, nullptr); ep::fused_fits(d, M)) {
-            // up to 64 activation rows: the activations quantized per row, then every tile pair
+            // up to 16 activation rows: the activations quantized per row, then every tile pair
             // decoded straight into E4M3 codes as the B operand of the FP8 MFMA (through LDS)
             // workspace: X codes [M][K] | X scales [M] | fp32 partial sums
             const size_t o_xs = up((size_t)M * (size_t)K, 256), o_pt = up(o_xs + 4 * (size_t)M, 256);

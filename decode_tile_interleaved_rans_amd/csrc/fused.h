@@ -11,8 +11,10 @@
 
 namespace ep {
 
-// Largest number of activation rows the fused kernel takes (four 16-row MFMA tiles).
-constexpr int kFusedMaxRows = 64;
+// Largest number of activation rows the fused kernel takes (one 16-row MFMA tile). Beyond it the
+// decode-then-GEMM path is as fast or faster: the partial-sum registers of a second M tile push
+// the kernel into register spills (measured at 32 and 64 rows).
+constexpr int kFusedMaxRows = 16;
 
 // Whether launch_fused takes this matrix and M (lossy, 16-row tiles, 1 <= M <= kFusedMaxRows,
 // cols % 8 == 0 and 64 x cols BF16 rows addressable with 32-bit offsets).

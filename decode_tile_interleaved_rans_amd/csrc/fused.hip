@@ -19,7 +19,7 @@ namespace ep {
 namespace {
 
 // ----------------------------------------------------------------------------- fused decode + MFMA
-// Decoding fused into the layer's matrix product for up to 64 activation rows: every weight is
+// Decoding fused into the layer's matrix product for up to 16 activation rows: every weight is
 // decoded once, straight into the B operand of v_mfma_f32_16x16x32_bf16, and never written to
 // memory. A wave decodes one tile pair (16 weight rows x 512 columns) as the decode kernel does,
 // keeping each decoded row as 8 packed BF16 values per lane (lane l: columns 8l .. 8l + 7 of the
@@ -319,8 +319,6 @@ __global__ __launch_bounds__(256) void fused_finish(const float* part, const uin
 }
 
 
-int fused_mt(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
-
 template <int N, int MT>
 hipError_t launch_mfma_n(const GroupArgs& g, uint64_t blocks, hipStream_t stream) {
     constexpr int W = N == 12 ? 8 : 12;
@@ -373,7 +371,8 @@ bool fused_fits(const MatDesc& m, int64_t M) {
 
 size_t fused_partial_bytes(const MatDesc& m, int64_t M) {
     const uint64_t pairs = (uint64_t)((m.rows + m.tile_rows - 1) / m.tile_rows) * m.pairs_c;
-    return (size_t)pairs * (size_t)fused_mt(M) * 256 * sizeof(float);
+    (void)M;                                        // one 16 x 16 tile of partial sums per pair
+    return (size_t)pairs * 256 * sizeof(float);
 }
 
 hipError_t launch_fused(const MatDesc& m, const uint16_t* x, int64_t M, float* part, const uint16_t* bias,
@@ -393,20 +392,11 @@ hipError_t launch_fused(const MatDesc& m, const uint16_t* x, int64_t M, float* p
     const uint64_t blocks = (uint64_t)device_cus();
     g.block_cost = (total + blocks - 1) / blocks;
     const uint64_t used = (total + g.block_cost - 1) / g.block_cost;
-    hipError_t e;
-    switch (fused_mt(M)) {
-        case 1: e = launch_mfma_mt<1>(g, used, stream); break;
-        case 2: e = launch_mfma_mt<2>(g, used, stream); break;
-        default: e = launch_mfma_mt<4>(g, used, stream); break;
-    }
+    hipError_t e = launch_mfma_mt<1>(g, used, stream);
     if (e != hipSuccess) return e;
     const int64_t outs = M * (int64_t)m.rows;
     const unsigned fb = (unsigned)((outs + 255) / 256);
-    switch (fused_mt(M)) {
-        case 1: hipLaunchKernelGGL(fused_finish<1>, dim3(fb), dim3(256), 0, stream, part, bias, y, (int)M, (int)m.rows, (int)m.pairs_c); break;
-        case 2: hipLaunchKernelGGL(fused_finish<2>, dim3(fb), dim3(256), 0, stream, part, bias, y, (int)M, (int)m.rows, (int)m.pairs_c); break;
-        default: hipLaunchKernelGGL(fused_finish<4>, dim3(fb), dim3(256), 0, stream, part, bias, y, (int)M, (int)m.rows, (int)m.pairs_c); break;
-    }
+    hipLaunchKernelGGL(fused_finish<1>, dim3(fb), dim3(256), 0, stream, part, bias, y, (int)M, (int)m.rows, (int)m.pairs_c);
     return hipGetLastError();
 }
 
@@ -428,21 +418,12 @@ hipError_t launch_fused_f8(const MatDesc& m, const uint8_t* xq, const float* xs,
     const uint64_t blocks = (uint64_t)device_cus();
     g.block_cost = (total + blocks - 1) / blocks;
     const uint64_t used = (total + g.block_cost - 1) / g.block_cost;
-    hipError_t e;
-    switch (fused_mt(M)) {
-        case 1: e = launch_mfma_f8_mt<1>(g, used, stream); break;
-        case 2: e = launch_mfma_f8_mt<2>(g, used, stream); break;
-        default: e = launch_mfma_f8_mt<4>(g, used, stream); break;
-    }
+    hipError_t e = launch_mfma_f8_mt<1>(g, used, stream);
     if (e != hipSuccess) return e;
     const int64_t outs = M * (int64_t)m.rows;
     const unsigned fb = (unsigned)((outs + 255) / 256);
     const float* sw = m.row_scale;
-    switch (fused_mt(M)) {
-        case 1: hipLaunchKernelGGL(fused_finish_f8<1>, dim3(fb), dim3(256), 0, stream, part, xs, sw, bias, y, (int)M, (int)m.rows, (int)m.pairs_c); break;
-        case 2: hipLaunchKernelGGL(fused_finish_f8<2>, dim3(fb), dim3(256), 0, stream, part, xs, sw, bias, y, (int)M, (int)m.rows, (int)m.pairs_c); break;
-        default: hipLaunchKernelGGL(fused_finish_f8<4>, dim3(fb), dim3(256), 0, stream, part, xs, sw, bias, y, (int)M, (int)m.rows, (int)m.pairs_c); break;
-    }
+    hipLaunchKernelGGL(fused_finish_f8<1>, dim3(fb), dim3(256), 0, stream, part, xs, sw, bias, y, (int)M, (int)m.rows, (int)m.pairs_c);
     return hipGetLastError();
 }
 

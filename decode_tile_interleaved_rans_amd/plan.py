@@ -30,7 +30,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import BF16, F32, compress, stream_info
+from . import BF16, F32, LAYER_PROB_BITS, compress, stream_info
 
 E8_G = 0.0716821                     # normalized second moment of the E8 lattice
 DEFAULT_GRID = tuple(np.round(np.arange(2.0, 8.0001, 0.25), 4))
@@ -58,7 +58,7 @@ def _weight_array(w):
     return (a, BF16) if a.dtype == np.uint16 else (a.astype(np.float32, copy=False), F32)
 
 
-def layer_candidates(w, grid=DEFAULT_GRID, prob_bits: int = 12, tile_rows: int = 16, n_threads: int = 0):
+def layer_candidates(w, grid=DEFAULT_GRID, prob_bits: int = LAYER_PROB_BITS, tile_rows: int = 16, n_threads: int = 0):
     """Encode one weight at every target of the grid; returns the candidates (real stream sizes
     and steps) and the streams."""
     arr, code = _weight_array(w)
@@ -111,7 +111,7 @@ def allocate(cands_by_layer: dict, sizes: dict, budget_bpp: float, sensitivity: 
 
 
 def plan_model(weights: dict, budget_bpp: float, sensitivity: dict | None = None, grid=DEFAULT_GRID,
-               prob_bits: int = 12, tile_rows: int = 16, n_threads: int = 0):
+               prob_bits: int = LAYER_PROB_BITS, tile_rows: int = 16, n_threads: int = 0):
     """Allocate bitrates over named weights under an average budget of budget_bpp stored bits per
     weight. Returns (record, streams): the record is JSON-serializable (per-layer target, actual
     bits per weight, bytes, step, estimated relative error, sensitivity, totals and the

@@ -208,7 +208,7 @@ ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, co
  * harnesses that forbid hipMalloc): ep_linear_forward with its scratch in a static device array
  * of 64 MiB per device instead of the library's workspace pool. It calls no hipMalloc, hipFree or
  * allocating library routine; the array lives from library load until the process ends. Same
- * arguments, results and paths as ep_linear_forward (the same kernels: for 5 <= M <= 64 the fused
+ * arguments, results and paths as ep_linear_forward (the same kernels: for 5 <= M <= 16 the fused
  * kernel's partial sums, for M <= 4 the fp32 accumulator, above that BF16 weight slices of at most
  * 64 MiB, i.e. 64 MiB / (2 K) rows). EP_ERANGE when a call needs more than the array holds
  * (M <= 4 with 4 M N > 64 MiB, the fused partials of very wide layers, or K > 2^21 for the slices).

@@ -1,4 +1,5 @@
-"""The decode fused into the compressed linear layer's matrix product (5 <= M <= 64 activation rows):
+"""The decode fused into the compressed linear layer's matrix product (5 <= M <= 16 activation rows;
+larger M takes the decode-then-GEMM path, which the M = 17 ... 64 cases below cover):
 every tile pair decoded straight into the B operand of the BF16 MFMA through LDS, never written
 out ("EntroPack: Fast and Accurate Entropy-Coded Weight Compression at Arbitrary Bitrates",
 Abstract; "EntroPack PyTorch Guide", section "Replace one linear layer before a whole model").
@@ -99,13 +100,13 @@ def e4m3(codes):
     return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).double().numpy()
 
 
-@pytest.mark.parametrize("N,K,M,prob_bits", [(256, 1024, 16, 12), (200, 784, 33, 11), (48, 528, 64, 10),
-                                             (1000, 2048, 5, 11)])
+@pytest.mark.parametrize("N,K,M,prob_bits", [(256, 1024, 16, 12), (200, 784, 12, 11), (48, 528, 9, 10),
+                                             (1000, 2048, 5, 11), (64, 1040, 40, 11)])
 def test_fp8_fused_matches_oracle_codes(N, K, M, prob_bits):
-    """The FP8 forward for M <= 64 (the weight decoded into E4M3 codes straight into the B operand of
+    """The FP8 forward for M <= 16 (the weight decoded into E4M3 codes straight into the B operand of
     the FP8 MFMA): within 3e-3 of the fp64 product of the oracle's E4M3 weight codes and row scales
     and the oracle's per-row activation codes and scales (K = 784 and 528: the last 32-code chunk
-    of a lane half past K)."""
+    of a lane half past K; M = 40 takes the decode-then-GEMM path)."""
     w = W.student_t(N, K, seed=N + K)
     s, _ = ep.compress(w, 4.5, dtype=ep.BF16, prob_bits=prob_bits)
     bias_bits = W.activations(1, N, 3)[0]

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
+import decode_tile_interleaved_rans_amd as ep
 from decode_tile_interleaved_rans_amd import plan as P
 from decode_tile_interleaved_rans_amd import workloads as W
 
@@ -25,7 +26,7 @@ def test_error_model_matches_oracle_decode(target):
     w = gauss(256, 1024, 1)
     cands, streams = P.layer_candidates(w, grid=(target,))
     c, s = cands[0], streams[0]
-    assert s == oracle.compress(w, target)[0]
+    assert s == oracle.compress(w, target, prob_bits=ep.LAYER_PROB_BITS)[0]
     q, _ = oracle.decode_symbols(s)
     d = oracle.info(s)
     scale = np.sqrt((w.astype(np.float64) ** 2).mean(1))

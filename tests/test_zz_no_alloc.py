@@ -1,7 +1,7 @@
 """The no-allocation linear forward (ep_linear_forward_noalloc, for callers that cannot allocate
 device memory) against the pool-workspace forward (ep_linear_forward), both called through the C
 ABI, on two calls in a row with the second smaller than the first, on every forward path (fused
-matrix-vector products for M <= 4, the fused decode + MFMA kernel for 5 <= M <= 64, decode slices
+matrix-vector products for M <= 4, the fused decode + MFMA kernel for 5 <= M <= 16, decode slices
 + GEMM above). Collected last: it runs after every other GPU test and also alone."""
 import ctypes as C
 
