@@ -51,7 +51,7 @@ def lib():
         build()
         L = C.CDLL(LIB)
         vp, i64, sz = C.c_void_p, C.c_int64, C.c_size_t
-        L.or_compress.argtypes = [vp, C.c_int, i64, i64, C.c_int, C.c_double, C.c_int, C.c_int,
+        L.or_compress.argtypes = [vp, C.c_int, i64, i64, C.c_int, C.c_double, C.c_int, C.c_int, C.c_int,
                                   C.POINTER(C.POINTER(C.c_uint8)), C.POINTER(sz), C.POINTER(C.c_double)]
         L.or_free.argtypes = [vp]
         L.or_decompress.argtypes = [vp, sz, C.c_int, vp, vp, C.c_int]
@@ -95,15 +95,18 @@ def _dtype_code(a: np.ndarray, dtype: int | None) -> int:
 
 
 def compress(w: np.ndarray, target_bpp: float = 4.0, *, dtype: int | None = None, mode: int = LOSSY,
-             prob_bits: int = 12, tile_rows: int = 16) -> tuple[bytes, float]:
-    """Encode a [R, C] matrix. 16-bit sources are passed as uint16 bit patterns with dtype=BF16/F16."""
+             prob_bits: int = 12, tile_rows: int = 16, layout: int = 0) -> tuple[bytes, float]:
+    """Encode a [R, C] matrix. 16-bit sources are passed as uint16 bit patterns with dtype=BF16/F16.
+    layout (lossy only): which block of a tile each of its 32 interleaved states codes per block
+    step; 0 = lane l takes block column l of each tile row in turn, 1 = lane l takes tile row
+    l mod tile_rows, block columns (32 / tile_rows) s + l // tile_rows (block_of in ep_oracle.c)."""
     w = np.ascontiguousarray(w)
     R, Cc = w.shape
     out = C.POINTER(C.c_uint8)()
     n = C.c_size_t()
     bpp = C.c_double()
     rc = lib().or_compress(_ptr(w), _dtype_code(w, dtype), R, Cc, mode, target_bpp, prob_bits, tile_rows,
-                           C.byref(out), C.byref(n), C.byref(bpp))
+                           layout, C.byref(out), C.byref(n), C.byref(bpp))
     if rc != 0:
         raise OracleError(rc, "compress")
     data = C.string_at(out, n.value)
@@ -112,13 +115,13 @@ def compress(w: np.ndarray, target_bpp: float = 4.0, *, dtype: int | None = None
 
 
 def info(stream: bytes) -> dict:
-    v = np.zeros(12, np.int64)
+    v = np.zeros(13, np.int64)
     f = np.zeros(2, np.float32)
     rc = lib().or_stream_info(stream, len(stream), _ptr(v), _ptr(f))
     if rc != 0:
         raise OracleError(rc, "stream_info")
     keys = ["rows", "cols", "mode", "dtype", "tile_rows", "prob_bits", "n_tiles", "n_escapes",
-            "payload_bytes", "meta_bytes", "state_bytes", "total_bytes"]
+            "payload_bytes", "meta_bytes", "state_bytes", "total_bytes", "layout"]
     d = {k: int(x) for k, x in zip(keys, v)}
     d["step"], d["target_bpp"] = float(f[0]), float(f[1])
     return d

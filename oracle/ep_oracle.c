@@ -30,8 +30,9 @@
  *   table windows          pinned: brute force over every window start (constructed ties, best
  *                          window at either end of the range, random heavy tails) and the tables
  *                          of real streams against histograms of their decoded coordinates
- *   lossy tile layout      pinned: an independent Python reader of the stream bytes gives the
- *                          decoder's coordinates and cosets (escapes, ragged shapes, 32-row tiles)
+ *   lossy tile layouts     pinned: an independent Python reader of the stream bytes gives the
+ *                          decoder's coordinates and cosets (escapes, ragged shapes, 32-row tiles,
+ *                          both layouts); both layouts decode to the same weights
  *   rANS tile coder        pinned: exact round trips, final state, an independent Python decoder
  *   rate search            pinned: monotone estimate, Gaussian closed form, |payload - target|
  *   containers             pinned: library casts (torch CPU) for BF16/FP16/FP8, integer closed form
@@ -706,7 +707,8 @@ float or_select_step(const void* w, int dt, int64_t R, int64_t C, double target)
 /* (per table: i16 lo, u16 S, u16 escape frequency, u16 freq[S]), tile_index u32[n_tiles + 1]   */
 /* (offsets in 4-byte units from the payload start), in the exponent-coded mode the raw plane   */
 /* u8[Rp][Cp] (offset and CRC-32 in header bytes 96 and 104), payload. Format version 2: header */
-/* bytes 112..115 hold the CRC-32 of every other byte outside the payload and the raw plane.    */
+/* bytes 112..115 hold the CRC-32 of every other byte outside the payload and the raw plane;    */
+/* byte 116 is the lossy tile layout (block_of), 0 in the lossless modes.                      */
 /* [G, "Start with a tensor round trip"]: the reported bitrate includes the metadata, so        */
 /* actual_bpp = 8 total / (R C).                                                                 */
 /* ------------------------------------------------------------------------------------------ */
@@ -716,7 +718,8 @@ enum {
     H_STEP = 24, H_TARGET = 28, H_NTILES = 32, H_NESC = 36, H_OFF_SCALE = 40, H_OFF_QMAX = 48,
     H_OFF_TABLES = 56, H_OFF_INDEX = 64, H_OFF_PAYLOAD = 72, H_TOTAL = 80, H_CRC = 88,
     H_OFF_RAW = 96, H_RAW_CRC = 104,   /* exponent-coded mode only; zero in the other modes */
-    H_META_CRC = 112                   /* CRC-32 of all bytes but the payload, the raw plane and this field */
+    H_META_CRC = 112,                  /* CRC-32 of all bytes but the payload, the raw plane and this field */
+    H_LAYOUT = 116                     /* lossy tile layout (reading R27): 0 or 1; 0 in the lossless modes */
 };
 #define FORMAT_VERSION 2
 
@@ -737,7 +740,7 @@ static uint32_t meta_crc(const uint8_t* s, uint64_t o_raw, uint64_t raw_len, uin
 static size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 
 typedef struct {
-    int mode, dtype, tile_rows, prob_bits, n_tables;
+    int mode, dtype, tile_rows, prob_bits, n_tables, layout;
     int64_t R, C, Rp, Cp, tiles_r, tiles_c;
     uint32_t n_tiles, n_esc;
     float step, target;
@@ -770,6 +773,8 @@ static int parse_stream(const uint8_t* s, size_t len, parsed* P) {
     P->target = f32_from_bits(get32(s + H_TARGET));
     P->n_tiles = get32(s + H_NTILES);
     P->n_esc = get32(s + H_NESC);
+    P->layout = s[H_LAYOUT];
+    if (P->layout > 1 || (P->layout != 0 && P->mode != MODE_LOSSY)) return OR_ECORRUPT;
     if (P->mode != MODE_LOSSY && P->mode != MODE_LOSSLESS && P->mode != MODE_LOSSLESS_EXP) return OR_ECORRUPT;
     if (P->mode == MODE_LOSSLESS_EXP && P->dtype != DT_BF16) return OR_ECORRUPT;
     if (P->mode == MODE_LOSSY && P->dtype != DT_F32 && P->dtype != DT_BF16 && P->dtype != DT_F16)
@@ -859,9 +864,25 @@ static int parse_stream(const uint8_t* s, size_t len, parsed* P) {
 /* ------------------------------------------------------------------------------------------ */
 /* Lossy encoder. [A, Abstract]: row normalization -> E8 -> conditional model -> sampled rate   */
 /* search -> tile entropy coding. Reading of the tile geometry: a tile covers tile_rows rows x  */
-/* 256 columns; lane l owns block column l (columns 8l..8l+7 of the tile); step 9r codes the    */
-/* coset bit of row r's block and steps 9r+1+j code coordinate j with table 1 + 2j + b.         */
+/* 256 columns, i.e. tile_rows x 32 E8 blocks of 8 columns, coded by 32 interleaved states in   */
+/* tile_rows block steps; at block step s, step 9s codes the coset bit of each lane's block and */
+/* steps 9s+1+j code its coordinate j with table 1 + 2j + b. Which block a lane codes at block  */
+/* step s is the layout (block_of).                                                             */
 /* ------------------------------------------------------------------------------------------ */
+/* Reading R27: the pages interleave 32 states per tile but do not say which state codes which  */
+/* block. Layout 0: lane l codes block column l of tile row s (the rows in turn). Layout 1: with */
+/* G = 32 / tile_rows lanes per row, lane l codes tile row l mod tile_rows at block column     */
+/* G s + floor(l / tile_rows), so every block step covers all tile rows. Both layouts code the  */
+/* same symbols with the same tables; only their order across the states differs.              */
+static void block_of(int layout, int tile_rows, int l, int s, int* rr, int* kk) {
+    if (layout == 0) {
+        *rr = s;
+        *kk = l;
+    } else {
+        *rr = l % tile_rows;
+        *kk = (LANES / tile_rows) * s + l / tile_rows;
+    }
+}
 static void lossy_symbol(const sym_table* T, int32_t x, uint8_t* sym, uint16_t* esc) {
     if (x >= T->lo && x < T->lo + T->S) { *sym = (uint8_t)(x - T->lo); *esc = 0; }
     else { *sym = ESC_SYM; *esc = (uint16_t)(int16_t)x; }
@@ -884,7 +905,7 @@ static int out_reserve(bytes_out* o, size_t extra) {
 }
 
 /* Writes header + metadata sections + payload. tables: n_tables entries (lo, S, f). */
-static int serialize(bytes_out* o, int mode, int dt, int64_t R, int64_t C, int tile_rows, int prob_bits,
+static int serialize(bytes_out* o, int mode, int dt, int64_t R, int64_t C, int tile_rows, int layout, int prob_bits,
                      int n_tables, const int32_t* lo, const int32_t* S, uint32_t (*f)[256],
                      float step, float target, const float* scale, const uint16_t* qmax,
                      const uint32_t* tile_off /* [n_tiles + 1], 4-byte units */, uint32_t n_tiles,
@@ -910,6 +931,7 @@ static int serialize(bytes_out* o, int mode, int dt, int64_t R, int64_t C, int t
     put32(s + H_ROWS, (uint32_t)R);
     put32(s + H_COLS, (uint32_t)C);
     put16(s + H_TILE_ROWS, (uint32_t)tile_rows);
+    s[H_LAYOUT] = (uint8_t)layout;
     put16(s + H_TILE_COLS, TILE_COLS);
     put16(s + H_LANES, LANES);
     s[H_PROB_BITS] = (uint8_t)prob_bits;
@@ -950,7 +972,7 @@ static int serialize(bytes_out* o, int mode, int dt, int64_t R, int64_t C, int t
 }
 
 static int encode_lossy(const void* w, int dt, int64_t R, int64_t C, double target, int prob_bits,
-                        int tile_rows, bytes_out* o) {
+                        int tile_rows, int layout, bytes_out* o) {
     int rc = OR_OK;
     int64_t Rp = ceil_div(R, tile_rows) * tile_rows, Cp = ceil_div(C, TILE_COLS) * TILE_COLS;
     int64_t kb = Cp / 8;
@@ -1031,11 +1053,13 @@ static int encode_lossy(const void* w, int dt, int64_t R, int64_t C, double targ
     tile_off[0] = 0;
     for (int64_t tr = 0; tr < tr_n; ++tr)
         for (int64_t tc = 0; tc < tc_n; ++tc) {
-            for (int rr = 0; rr < tile_rows; ++rr)
+            for (int bs = 0; bs < tile_rows; ++bs)
                 for (int l = 0; l < LANES; ++l) {
-                    int64_t r = tr * tile_rows + rr, k = tc * LANES + l;
+                    int rr, kk;
+                    block_of(layout, tile_rows, l, bs, &rr, &kk);
+                    int64_t r = tr * tile_rows + rr, k = tc * LANES + kk;
                     int b = coset[r * kb + k];
-                    int t0 = 9 * rr;
+                    int t0 = 9 * bs;
                     tab[t0 * LANES + l] = 0;
                     sym[t0 * LANES + l] = (uint8_t)(b - T[0].lo);
                     esc[t0 * LANES + l] = 0;
@@ -1052,7 +1076,7 @@ static int encode_lossy(const void* w, int dt, int64_t R, int64_t C, double targ
             pl.len += nbytes;
             tile_off[tr * tc_n + tc + 1] = (uint32_t)(pl.len / 4);
         }
-    rc = serialize(o, MODE_LOSSY, dt, R, C, tile_rows, prob_bits, N_LOSSY_TABLES, lo, S, f, step,
+    rc = serialize(o, MODE_LOSSY, dt, R, C, tile_rows, layout, prob_bits, N_LOSSY_TABLES, lo, S, f, step,
                    (float)target, scale, qmax, tile_off, n_tiles, pl.buf, pl.len, n_esc, NULL, 0);
     free(pl.buf);
 done:
@@ -1127,7 +1151,7 @@ static int encode_lossless(const void* w, int dt, int64_t R, int64_t C, int prob
             pl.len += rans_encode_tile(RT, prob_bits, n_steps, tab, sym, esc, -1, stack, pl.buf + pl.len);
             tile_off[tr * tc_n + tc + 1] = (uint32_t)(pl.len / 4);
         }
-    rc = serialize(o, MODE_LOSSLESS, dt, R, C, tile_rows, prob_bits, P, lo, S, f, 0.0f, 0.0f, NULL, NULL,
+    rc = serialize(o, MODE_LOSSLESS, dt, R, C, tile_rows, 0, prob_bits, P, lo, S, f, 0.0f, 0.0f, NULL, NULL,
                    tile_off, n_tiles, pl.buf, pl.len, 0, NULL, 0);
 done:
     for (int p = 0; p < 4; ++p) rans_table_free(&RT[p]);
@@ -1195,7 +1219,7 @@ static int encode_lossless_exp(const void* w, int64_t R, int64_t C, int prob_bit
             pl.len += rans_encode_tile(RT, prob_bits, n_steps, tab, sym, esc, -1, stack, pl.buf + pl.len);
             tile_off[tr * tc_n + tc + 1] = (uint32_t)(pl.len / 4);
         }
-    rc = serialize(o, MODE_LOSSLESS_EXP, DT_BF16, R, C, tile_rows, prob_bits, 1, lo, S, f, 0.0f, 0.0f, NULL, NULL,
+    rc = serialize(o, MODE_LOSSLESS_EXP, DT_BF16, R, C, tile_rows, 0, prob_bits, 1, lo, S, f, 0.0f, 0.0f, NULL, NULL,
                    tile_off, n_tiles, pl.buf, pl.len, 0, raw, (uint64_t)(Rp * Cp));
 done:
     rans_table_free(&RT[0]);
@@ -1204,10 +1228,11 @@ done:
 }
 
 int or_compress(const void* w, int src_dtype, int64_t rows, int64_t cols, int mode, double target_bpp,
-                int prob_bits, int tile_rows, uint8_t** out, size_t* out_len, double* actual_bpp) {
+                int prob_bits, int tile_rows, int layout, uint8_t** out, size_t* out_len, double* actual_bpp) {
     if (!out || !out_len || rows < 0 || cols < 0 || (rows * cols > 0 && !w)) return OR_EINVAL;
     if (rows > 0xFFFFFFFFll || cols >= (1ll << 28)) return OR_ERANGE;
     if (prob_bits < 10 || prob_bits > 12 || (tile_rows != 16 && tile_rows != 32)) return OR_EINVAL;
+    if (layout < 0 || layout > 1 || (layout != 0 && mode != MODE_LOSSY)) return OR_EINVAL;
     bytes_out o = { NULL, 0, 0 };
     int rc;
     if (mode == MODE_LOSSY) {
@@ -1215,7 +1240,7 @@ int or_compress(const void* w, int src_dtype, int64_t rows, int64_t cols, int mo
         if (!(target_bpp > 0.0 && target_bpp <= 32.0)) return OR_EINVAL;
         for (int64_t i = 0; i < rows * cols; ++i)
             if (!isfinite(src_value(w, src_dtype, i))) return OR_ERANGE;
-        rc = encode_lossy(w, src_dtype, rows, cols, target_bpp, prob_bits, tile_rows, &o);
+        rc = encode_lossy(w, src_dtype, rows, cols, target_bpp, prob_bits, tile_rows, layout, &o);
     } else if (mode == MODE_LOSSLESS) {
         if (elem_bytes(src_dtype) == 0) return OR_EUNSUPPORTED;
         rc = encode_lossless(w, src_dtype, rows, cols, prob_bits, tile_rows, &o);
@@ -1286,16 +1311,18 @@ static int decode_lossy_tile(const parsed* P, const decoder_tables* D, uint32_t 
     int rc = rans_decode_tile(D->T, P->prob_bits, n_steps, P->payload + 4 * a, (size_t)(4 * (b - a)),
                               lossy_tables, &ctx, ESC_SYM, sym, esc, NULL);
     if (rc != OR_OK) return rc;
-    for (int rr = 0; rr < P->tile_rows; ++rr)
+    for (int bs = 0; bs < P->tile_rows; ++bs)
         for (int l = 0; l < LANES; ++l) {
-            int t0 = 9 * rr;
+            int rr, kk;
+            block_of(P->layout, P->tile_rows, l, bs, &rr, &kk);
+            int t0 = 9 * bs;
             int cb = P->lo[0] + sym[t0 * LANES + l];
-            bt[rr * LANES + l] = (uint8_t)cb;
+            bt[rr * LANES + kk] = (uint8_t)cb;
             for (int j = 0; j < 8; ++j) {
                 int t = t0 + 1 + j, ti = 1 + 2 * j + cb;
                 uint8_t s = sym[t * LANES + l];
                 int32_t x = (s == ESC_SYM) ? (int32_t)(int16_t)esc[t * LANES + l] : P->lo[ti] + s;
-                qt[rr * TILE_COLS + 8 * l + j] = (int16_t)(2 * x + cb);
+                qt[rr * TILE_COLS + 8 * kk + j] = (int16_t)(2 * x + cb);
             }
         }
     return OR_OK;
@@ -1546,9 +1573,9 @@ int or_decompress_tiles(const uint8_t* s, size_t len, int container, const uint3
 }
 
 /* Header fields and section sizes of a validated stream, for the accounting tests.
- * info[0..11] = R, C, mode, dtype, tile_rows, prob_bits, n_tiles, n_escapes, payload bytes (the
+ * info[0..12] = R, C, mode, dtype, tile_rows, prob_bits, n_tiles, n_escapes, payload bytes (the
  * tile payload, plus the raw plane in the exponent-coded mode), metadata bytes (total - payload),
- * state bytes (4 * 32 * n_tiles), total bytes;
+ * state bytes (4 * 32 * n_tiles), total bytes, tile layout;
  * fstep receives the step and target. */
 int or_stream_info(const uint8_t* s, size_t len, int64_t* info, float* fstep) {
     parsed P;
@@ -1558,6 +1585,7 @@ int or_stream_info(const uint8_t* s, size_t len, int64_t* info, float* fstep) {
     info[5] = P.prob_bits; info[6] = P.n_tiles; info[7] = P.n_esc;
     info[8] = (int64_t)(P.payload_len + P.raw_len);       /* coded words plus uncoded raw bytes */
     info[9] = (int64_t)(len - P.payload_len - P.raw_len); info[10] = 4ll * LANES * P.n_tiles; info[11] = (int64_t)len;
+    info[12] = P.layout;
     fstep[0] = P.step;
     fstep[1] = P.target;
     return OR_OK;

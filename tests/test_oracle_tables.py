@@ -12,9 +12,12 @@ decoder would share any mistake in them.
 2. The lossy tile layout (tiles that decode on their own, same passage; readings R7, R10, R12, R13):
    an independent Python reader, written from the byte layout alone, decodes every tile of oracle
    streams (escapes included) and must give the oracle decoder's doubled coordinates and cosets:
-   step 9r codes row r's coset bit with table 0, steps 9r + 1 + j code coordinate j with table
-   1 + 2j + b chosen by the coset just decoded, lane l owns the 8-column block l, refill words then
-   escape words in ascending lane order."""
+   step 9s codes the coset bit of each lane's block with table 0, steps 9s + 1 + j code coordinate
+   j with table 1 + 2j + b chosen by the coset just decoded, refill words then escape words in
+   ascending lane order; in layout 0 lane l codes the 8-column block l of tile row s, in layout 1
+   (reading R27) the block of tile row l mod tile_rows at block column (32 / tile_rows) s +
+   l // tile_rows. Both layouts deal the same symbols to the states, so their streams must decode
+   to the same weights."""
 import struct
 
 import numpy as np
@@ -137,9 +140,21 @@ def read_lossy_stream(s: bytes):
     """Doubled coordinates [Rp, Cp] and cosets [Rp, Cp / 8] of a lossy stream, read from its bytes
     with the layout: 128-byte header, tables (i16 window start, u16 width, u16 escape frequency,
     u16 frequencies), tile index of u32 offsets in 4-byte units, tiles of 32 u32 states then u16
-    words."""
+    words. Header byte 116 says how a tile's 32 x tile_rows blocks are dealt to the states: 0, by
+    rows (block step = tile row, lane = block column); 1, by columns of lanes (lane l stays on
+    row l mod tile_rows and walks its blocks left to right, interleaved with the other lanes of
+    that row)."""
     assert s[:4] == b"EPK1" and s[6] == 0
     R, C, tr = u32(s, 8), u32(s, 12), u16(s, 16)
+    layout = s[116]
+    assert layout in (0, 1)
+    per_row = LANES // tr                                   # lanes sharing a row in layout 1
+
+    def block(bs, l):
+        """(tile row, block column) coded by lane l at block step bs."""
+        if layout == 0:
+            return bs, l
+        return l % tr, bs * per_row + l // tr
     assert u16(s, 18) == 256 and u16(s, 20) == LANES
     n, nt, ntiles = s[22], s[23], u32(s, 32)
     o_tb, o_ix, o_pl = u64(s, 56), u64(s, 64), u64(s, 72)
@@ -173,7 +188,7 @@ def read_lossy_stream(s: bytes):
         r0, c0 = (t // tiles_c) * tr, (t % tiles_c) * 256
         b = [0] * LANES
         for step in range(9 * tr):
-            rr, m = divmod(step, 9)
+            bs, m = divmod(step, 9)
             syms = [0] * LANES
             tabs = [0 if m == 0 else 1 + 2 * (m - 1) + b[l] for l in range(LANES)]
             for l in range(LANES):
@@ -187,16 +202,17 @@ def read_lossy_stream(s: bytes):
                     x[l] = (x[l] << 16) | words[k]
                     k += 1
             for l in range(LANES):                          # then escapes, ascending lanes
+                rr, kk = block(bs, l)
                 if m == 0:
                     b[l] = lo[0] + syms[l]
-                    cos[r0 + rr, c0 // 8 + l] = b[l]
+                    cos[r0 + rr, c0 // 8 + kk] = b[l]
                     continue
                 if syms[l] == 255:
                     v = struct.unpack("<h", struct.pack("<H", words[k]))[0]
                     k += 1
                 else:
                     v = lo[tabs[l]] + syms[l]
-                q[r0 + rr, c0 + 8 * l + (m - 1)] = 2 * v + b[l]
+                q[r0 + rr, c0 + 8 * kk + (m - 1)] = 2 * v + b[l]
         assert all(v == L for v in x), f"tile {t}: final states"
         assert len(words) - k in (0, 1), f"tile {t}: words left over"
     return q, cos, (R, C)
@@ -207,9 +223,11 @@ def read_lossy_stream(s: bytes):
     ((40, 300), 4.0, 10, 16),        # ragged: padding rows and columns
     ((64, 256), 6.0, 11, 32),        # 32-row tiles
 ])
-def test_python_reader_matches_oracle_decoder(shape, target, prob_bits, tile_rows):
+@pytest.mark.parametrize("layout", [0, 1])
+def test_python_reader_matches_oracle_decoder(shape, target, prob_bits, tile_rows, layout):
     w = W.gaussian_with_outliers(*shape, seed=31, outlier_frac=0.003)
-    s, _ = oracle.compress(w, target, prob_bits=prob_bits, tile_rows=tile_rows)
+    s, _ = oracle.compress(w, target, prob_bits=prob_bits, tile_rows=tile_rows, layout=layout)
+    assert oracle.info(s)["layout"] == layout
     q, cos, (R, C) = read_lossy_stream(s)
     qo, bo = oracle.decode_symbols(s)
     assert np.array_equal(q[:R, :C], qo.astype(np.int64))
@@ -240,3 +258,55 @@ def test_window_range_rule_rejects_out_of_range_tables():
     struct.pack_into("<h", ok, t1, -16384)
     struct.pack_into("<I", ok, 112, zlib.crc32(bytes(ok[:112] + ok[116:o_pl])))
     oracle.info(bytes(ok))
+
+
+@pytest.mark.parametrize("shape,tile_rows,target", [
+    ((48, 776), 16, 4.0),            # ragged rows and columns
+    ((64, 512), 32, 3.0),            # 32-row tiles: one lane per row
+    ((32, 1024), 16, 8.0),           # escapes
+])
+def test_layouts_decode_to_the_same_weights(shape, tile_rows, target):
+    """Reading R27: the layout changes only which state codes a block, so both layouts give the
+    same step, tables, escapes and decoded weights in every container (BF16, FP8 with its row
+    scales), and payloads of about the same size (the same symbols, coded by other states)."""
+    w = W.gaussian_with_outliers(*shape, seed=sum(shape), outlier_frac=0.002)
+    s0, _ = oracle.compress(w, target, tile_rows=tile_rows, layout=0)
+    s1, _ = oracle.compress(w, target, tile_rows=tile_rows, layout=1)
+    i0, i1 = oracle.info(s0), oracle.info(s1)
+    assert (i0["layout"], i1["layout"]) == (0, 1)
+    for k in ("step", "n_escapes", "n_tiles", "meta_bytes"):
+        assert i0[k] == i1[k], k
+    t0, t1 = oracle.tables(s0), oracle.tables(s1)
+    for a, b in zip(t0, t1):
+        assert np.array_equal(a, b)
+    assert abs(i0["payload_bytes"] - i1["payload_bytes"]) <= 0.01 * i0["payload_bytes"] + 64
+    assert np.array_equal(oracle.decompress(s0, oracle.BF16)[0], oracle.decompress(s1, oracle.BF16)[0])
+    f0, sc0 = oracle.decompress(s0, oracle.F8E4M3)
+    f1, sc1 = oracle.decompress(s1, oracle.F8E4M3)
+    assert np.array_equal(f0, f1) and np.array_equal(sc0, sc1)
+    if target >= 8.0:
+        assert i1["n_escapes"] > 0
+
+
+def test_layout_byte_is_validated():
+    """The layout byte (header byte 116) takes 0 or 1, and 1 only in the lossy mode: other values
+    are refused as corrupt even with the metadata checksum made consistent, and the encoder refuses
+    layout 1 for the lossless modes."""
+    import zlib
+    w = W.gaussian_with_outliers(16, 256, seed=9)
+    s, _ = oracle.compress(w, 4.0, layout=1)
+    bits = np.frombuffer(np.float32(w).astype(np.float32).tobytes(), np.uint32)
+    sl, _ = oracle.compress((bits >> 16).astype(np.uint16).reshape(w.shape), dtype=oracle.BF16,
+                            mode=oracle.LOSSLESS)
+    for stream, value in ((s, 2), (s, 255), (sl, 1)):
+        o_pl = u64(stream, 72)
+        bad = bytearray(stream)
+        bad[116] = value
+        struct.pack_into("<I", bad, 112, zlib.crc32(bytes(bad[:112] + bad[116:o_pl])))
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.info(bytes(bad))
+        assert e.value.rc == -2
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.compress((bits >> 16).astype(np.uint16).reshape(w.shape), dtype=oracle.BF16,
+                        mode=oracle.LOSSLESS, layout=1)
+    assert e.value.rc == -1
