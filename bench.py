@@ -152,8 +152,10 @@ def fused_gemm_section(torch, ep, reps: int = 15):
     """Fused decode + BF16 MFMA GEMM against the plain BF16 GEMM on the uncompressed weight.
 
     Workload: W = 0.02 t5 bf16 [8192, 8192] coded at 4.5 bpp, X ~ N(0, 1) bf16 [M, 8192],
-    Y = X W^T in BF16 with fp32 accumulation, M = 4096 (prefill), 256, 16 and 1 (M <= 4 runs the
-    fused decode + matrix-vector kernel). Each rep is timed
+    Y = X W^T in BF16 with fp32 accumulation, M = 4096 (prefill), 256, 64, 16 and 1. The weight is
+    coded twice: in layout 0 (fused decode + matrix-vector kernel for M <= 4, transposing fused
+    kernel for M <= 16) and in the row layout (every tile's rANS states on one tile row each; the
+    fused kernel multiplies straight from the decoder's registers for M <= 64). Each rep is timed
     with HIP events on the launch stream and a 1 GiB buffer is rewritten between reps, so neither
     the weight nor the activations are served from the Infinity Cache."""
     from decode_tile_interleaved_rans_amd import workloads as W
@@ -164,6 +166,9 @@ def fused_gemm_section(torch, ep, reps: int = 15):
     log(f"encoded 8192x8192 at target 4.5: actual {bpp:.4f} bpp in {time.time() - t0:.2f} s")
     layer = ep.CompressedLinear(s)
     layer8 = ep.CompressedLinear(s, compute="fp8")
+    sr, bppr = ep.compress(w, 4.5, dtype=ep.BF16, prob_bits=ep.LAYER_PROB_BITS, layout=ep.ROW_LAYOUT)
+    layer_r = ep.CompressedLinear(sr)
+    layer_r8 = ep.CompressedLinear(sr, compute="fp8")
     Wt = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda()
     Xf = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
     N, K = Wt.shape
@@ -193,22 +198,27 @@ def fused_gemm_section(torch, ep, reps: int = 15):
         return out
 
     wdec = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
-    (t_dec, _), = timed([lambda: layer.handle.decompress_into(wdec)])
+    (t_dec, _), (t_dec_r, _) = timed([lambda: layer.handle.decompress_into(wdec),
+                                      lambda: layer_r.handle.decompress_into(wdec)])
     layer.handle.check()
+    layer_r.handle.check()
     out = {"workload": "W 0.02 t5 bf16 [8192, 8192] at 4.5 bpp, X N(0,1) bf16 [M, 8192], Y = X W^T bf16, "
                        "fp32 accumulate",
            "prob_bits": ep.LAYER_PROB_BITS, "actual_bpp": round(bpp, 4), "stream_bytes": len(s), "decode_full_us": round(t_dec, 2),
+           "row_layout": {"actual_bpp": round(bppr, 4), "stream_bytes": len(sr), "decode_full_us": round(t_dec_r, 2)},
            "reps": reps, "timing": "median of per-rep HIP events, the five variants interleaved within each "
                                    "rep, 1 GiB cache flush before every timed call"}
     wq, ws = ep.quantize_rows_fp8(Wt)                  # plain FP8 baseline: the weight pre-quantized
-    for M in (4096, 256, 64, 16, 1):
+    for M in (4096, 256, 64, 32, 16, 4, 1):
         X = Xf[:M].contiguous()
         xq, xs = ep.quantize_rows_fp8(X)
-        (t_f, t_f_min), (t_o, _), (t_t, _), (t_f8, _), (t_o8, _) = timed(
+        (t_f, t_f_min), (t_o, _), (t_t, _), (t_f8, _), (t_o8, _), (t_r, t_r_min), (t_r8, _) = timed(
             [lambda: layer(X), lambda: ep.gemm_bf16(X, Wt), lambda: torch.matmul(X, Wt.t()),
-             lambda: layer8(X), lambda: ep.gemm_fp8(xq, xs, wq, ws)])
+             lambda: layer8(X), lambda: ep.gemm_fp8(xq, xs, wq, ws), lambda: layer_r(X), lambda: layer_r8(X)])
         layer.handle.check()
         layer8.handle.check()
+        layer_r.handle.check()
+        layer_r8.handle.check()
         fl = 2.0 * M * N * K
         out[f"M{M}"] = {
             "fused_us": round(t_f, 2), "fused_min_us": round(t_f_min, 2), "own_gemm_us": round(t_o, 2),
@@ -223,10 +233,15 @@ def fused_gemm_section(torch, ep, reps: int = 15):
             "fp8_fused_tflops": round(fl / t_f8 / 1e6, 1), "fp8_own_gemm_tflops": round(fl / t_o8 / 1e6, 1),
             # HBM-bound view for small M: X + compressed W + Y
             "fused_hbm_frac": round((2 * M * K + len(s) + 2 * M * N) / t_f / 1e3 / HBM_PEAK_GBS, 4),
+            # the same weight in the row layout
+            "row_layout": {"fused_us": round(t_r, 2), "fused_min_us": round(t_r_min, 2),
+                           "vs_decode_alone": round(t_r / t_dec_r, 4), "overhead_vs_own_gemm": round(t_r / t_o - 1, 4),
+                           "overhead_vs_torch": round(t_r / t_t - 1, 4), "fp8_fused_us": round(t_r8, 2),
+                           "fp8_overhead_vs_own_fp8_gemm": round(t_r8 / t_o8 - 1, 4)},
         }
         log(f"fused GEMM M={M}: fused {t_f:.1f} us, own GEMM {t_o:.1f} us, torch {t_t:.1f} us; "
-            f"FP8 fused {t_f8:.1f} us, own FP8 GEMM {t_o8:.1f} us")
-    del flush, wdec, Wt, Xf, layer, layer8, wq, ws
+            f"FP8 fused {t_f8:.1f} us, own FP8 GEMM {t_o8:.1f} us; row layout {t_r:.1f} us, FP8 {t_r8:.1f} us")
+    del flush, wdec, Wt, Xf, layer, layer8, layer_r, layer_r8, wq, ws
     torch.cuda.empty_cache()
     return out
 

@@ -25,6 +25,10 @@ F32, BF16, F16, F8E4M3, I8, U8 = 0, 1, 2, 3, 4, 5
 # 8; the stream is about 1% larger and the plain decode runs at the same speed.
 LAYER_PROB_BITS = 11
 LOSSY, LOSSLESS, LOSSLESS_EXP = 0, 1, 2
+# Lossy tile layouts (ep_encode_opts.layout): ROW_LAYOUT keeps each of a tile's 32 rANS states on
+# one tile row, so that every block step of a 16-row tile pair yields a 16 x 32 weight block, the B
+# operand of one BF16 MFMA, in the decoder's own registers.
+BLOCK_ROW_LAYOUT, ROW_LAYOUT = 0, 1
 STATUS = {0: "EP_OK", -1: "EP_EINVAL", -2: "EP_ECORRUPT", -3: "EP_EUNSUPPORTED", -4: "EP_ERANGE",
           -5: "EP_EHIP", -6: "EP_ENOMEM", -7: "EP_EDEVICE"}
 EXPORTS = ["ep_compress", "ep_free", "ep_stream_info", "ep_upload", "ep_handle_info", "ep_decompress",
@@ -41,7 +45,7 @@ class EPError(RuntimeError):
 
 class EncodeOpts(C.Structure):
     _fields_ = [("mode", C.c_int), ("target_bpp", C.c_double), ("prob_bits", C.c_int), ("tile_rows", C.c_int),
-                ("n_threads", C.c_int)]
+                ("n_threads", C.c_int), ("layout", C.c_int)]
 
 
 class Info(C.Structure):
@@ -49,7 +53,7 @@ class Info(C.Structure):
                 ("tile_rows", C.c_int32), ("prob_bits", C.c_int32), ("n_tiles", C.c_uint32),
                 ("n_escapes", C.c_uint32), ("step", C.c_float), ("target_bpp", C.c_float),
                 ("actual_bpp", C.c_double), ("total_bytes", C.c_uint64), ("payload_bytes", C.c_uint64),
-                ("state_bytes", C.c_uint64), ("meta_bytes", C.c_uint64)]
+                ("state_bytes", C.c_uint64), ("meta_bytes", C.c_uint64), ("layout", C.c_int32)]
 
     def as_dict(self) -> dict:
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -132,9 +136,12 @@ def _stream_ptr(stream=None):
 
 # ------------------------------------------------------------------------------------ host side
 def compress(w, target_bpp: float = 4.0, *, mode: int = LOSSY, prob_bits: int = 12, tile_rows: int = 16,
-             n_threads: int = 0, dtype: int | None = None) -> tuple[bytes, float]:
+             n_threads: int = 0, dtype: int | None = None, layout: int = 0) -> tuple[bytes, float]:
     """Compress a 2-D weight (torch tensor on any device, or numpy array) on the host.
-    Returns (stream bytes, actual bits per weight including every byte of metadata)."""
+    Returns (stream bytes, actual bits per weight including every byte of metadata).
+    layout (lossy only; ep_encode_opts.layout): 0 codes each tile row by row, 1 keeps every rANS
+    state on one tile row (ROW_LAYOUT), which the compressed linear forward multiplies straight
+    from the decoder's registers; both decode to the same weights."""
     if hasattr(w, "detach"):
         torch = _torch()
         code = _dtype_code(w.dtype)
@@ -149,7 +156,7 @@ def compress(w, target_bpp: float = 4.0, *, mode: int = LOSSY, prob_bits: int = 
     if arr.ndim != 2:
         raise ValueError("compress takes a 2-D [out_features, in_features] matrix")
     R, Cc = arr.shape
-    opts = EncodeOpts(mode, float(target_bpp), prob_bits, tile_rows, n_threads)
+    opts = EncodeOpts(mode, float(target_bpp), prob_bits, tile_rows, n_threads, layout)
     out = C.POINTER(C.c_uint8)()
     n = C.c_size_t()
     bpp = C.c_double()
@@ -161,7 +168,7 @@ def compress(w, target_bpp: float = 4.0, *, mode: int = LOSSY, prob_bits: int = 
 
 
 def compress_device(w, target_bpp: float = 4.0, *, prob_bits: int = 12, tile_rows: int = 16,
-                    stream=None) -> tuple[bytes, float]:
+                    stream=None, layout: int = 0) -> tuple[bytes, float]:
     """Lossy compression on the GPU of a 2-D weight in device memory (torch tensor: float32,
     bfloat16 or float16); the same bytes as compress() on the same values."""
     if w.dim() != 2:
@@ -171,7 +178,7 @@ def compress_device(w, target_bpp: float = 4.0, *, prob_bits: int = 12, tile_row
         raise ValueError("compress_device takes a tensor in device memory")
     _need(t, "w", t.dtype)
     R, Cc = t.shape
-    opts = EncodeOpts(LOSSY, float(target_bpp), prob_bits, tile_rows, 0)
+    opts = EncodeOpts(LOSSY, float(target_bpp), prob_bits, tile_rows, 0, layout)
     out = C.POINTER(C.c_uint8)()
     n = C.c_size_t()
     bpp = C.c_double()

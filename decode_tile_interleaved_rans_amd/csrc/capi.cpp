@@ -113,6 +113,7 @@ ep::MatDesc desc_for(const ep_handle* h, int container, void* out, float* scale)
     d.step = v.step;
     d.prob_bits = (uint8_t)v.prob_bits;
     d.tile_rows = (uint8_t)v.tile_rows;
+    d.layout = (uint8_t)v.layout;
     d.container = (uint8_t)container;
     d.n_tables = (uint8_t)v.n_tables;
     d.mode = (uint8_t)v.mode;
@@ -295,7 +296,7 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
     hipError_t he = hipGetDevice(&dev);
     if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
     WsLease ws;
-    if (M <= 4) {
+    if (M <= 4 && w->view.layout == 0) {
         // a few activation rows: decoding fused with the matrix-vector products, the weight never
         // written out; fp32 accumulation in the scratch, then rounding (+ bias) to BF16
         const size_t need = sizeof(float) * (size_t)M * (size_t)N;
@@ -316,8 +317,9 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
         return e == hipSuccess ? EP_OK : hip_fail(e, "fused matrix-vector launch");
     }
     if (const ep::MatDesc d = desc_for(w, ep::CT_BF16, nullptr, nullptr); ep::fused_fits(d, M)) {
-        // up to 16 activation rows: every tile pair decoded straight into the B operand of the
-        // BF16 MFMA (through LDS), its fp32 partial sums in the scratch, then summed in order
+        // up to 16 activation rows (64 in the row layout): every tile pair decoded straight into
+        // the B operand of the BF16 MFMA (through LDS in layout 0, from the decoder's registers in
+        // the row layout), its fp32 partial sums in the scratch, then summed in order
         const size_t need = ep::fused_partial_bytes(d, M);
         if (fixed) {
             if (ep_status st = take_static(need, &ws); st != EP_OK) return st;
@@ -389,9 +391,11 @@ ep_status ep_compress(const void* host_w, ep_dtype src, int64_t rows, int64_t co
         if (rows < 0 || cols < 0) return fail(EP_EINVAL, "negative shape");
         if (rows * cols > 0 && !host_w) return fail(EP_EINVAL, "null input");
         if (rows > 0xFFFFFFFFll || cols >= (1ll << 28)) return fail(EP_ERANGE, "shape too large (cols must be < 2^28)");
-        ep_encode_opts o = opts ? *opts : ep_encode_opts{EP_MODE_LOSSY_E8, 4.0, 12, 16, 0};
+        ep_encode_opts o = opts ? *opts : ep_encode_opts{EP_MODE_LOSSY_E8, 4.0, 12, 16, 0, 0};
         if (o.prob_bits < 10 || o.prob_bits > 12) return fail(EP_EINVAL, "prob_bits must be 10..12");
         if (o.tile_rows != 16 && o.tile_rows != 32) return fail(EP_EINVAL, "tile_rows must be 16 or 32");
+        if (o.layout < 0 || o.layout > 1 || (o.layout != 0 && o.mode != EP_MODE_LOSSY_E8))
+            return fail(EP_EINVAL, "layout must be 0, or 1 in the lossy mode");
         if (o.mode == EP_MODE_LOSSY_E8) {
             if (src != EP_F32 && src != EP_BF16 && src != EP_F16)
                 return fail(EP_EUNSUPPORTED, "lossy mode takes F32, BF16 or F16 input");
@@ -597,8 +601,9 @@ ep_status ep_compress_device(const void* dev_w, ep_dtype src, int64_t rows, int6
         if (rows < 0 || cols < 0) return fail(EP_EINVAL, "negative shape");
         if (rows * cols > 0 && !dev_w) return fail(EP_EINVAL, "null input");
         if (rows > 0xFFFFFFFFll || cols >= (1ll << 28)) return fail(EP_ERANGE, "shape too large (cols must be < 2^28)");
-        ep_encode_opts o = opts ? *opts : ep_encode_opts{EP_MODE_LOSSY_E8, 4.0, 12, 16, 0};
+        ep_encode_opts o = opts ? *opts : ep_encode_opts{EP_MODE_LOSSY_E8, 4.0, 12, 16, 0, 0};
         if (o.mode != EP_MODE_LOSSY_E8) return fail(EP_EUNSUPPORTED, "the device encoder codes the lossy mode");
+        if (o.layout < 0 || o.layout > 1) return fail(EP_EINVAL, "layout must be 0 or 1");
         if (o.prob_bits < 10 || o.prob_bits > 12) return fail(EP_EINVAL, "prob_bits must be 10..12");
         if (o.tile_rows != 16 && o.tile_rows != 32) return fail(EP_EINVAL, "tile_rows must be 16 or 32");
         if (src != EP_F32 && src != EP_BF16 && src != EP_F16)
@@ -670,8 +675,9 @@ ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M
         hipError_t we = hipGetDevice(&dev);
         if (we != hipSuccess) return hip_fail(we, "hipGetDevice");
         if (const ep::MatDesc d = desc_for(w, ep::CT_F8E4M3, nullptr, nullptr); ep::fused_fits(d, M)) {
-            // up to 16 activation rows: the activations quantized per row, then every tile pair
-            // decoded straight into E4M3 codes as the B operand of the FP8 MFMA (through LDS)
+            // up to 16 activation rows (64 in the row layout): the activations quantized per row,
+            // then every tile pair decoded straight into E4M3 codes as the B operand of the FP8
+            // MFMA (through LDS in layout 0, from the decoder's registers in the row layout)
             // workspace: X codes [M][K] | X scales [M] | fp32 partial sums
             const size_t o_xs = up((size_t)M * (size_t)K, 256), o_pt = up(o_xs + 4 * (size_t)M, 256);
             const size_t need = o_pt + ep::fused_partial_bytes(d, M);

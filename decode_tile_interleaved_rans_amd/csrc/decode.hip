@@ -80,12 +80,10 @@ struct Conv<CT_Q16> {
     __device__ static uint32_t f(float q, float, float, uint32_t, uint32_t) { return (uint32_t)(uint16_t)(int16_t)(int32_t)q; }
 };
 
+// The 8 container values of one block.
 template <int CT>
-__device__ __forceinline__ void store_block(const MatDesc& M, uint32_t row, uint32_t col0, const float* q, float alpha,
-                                   float h, uint32_t k, uint32_t magic) {
-    using T = typename Conv<CT>::T;
-    T* out = static_cast<T*>(M.out) + (size_t)row * M.cols;
-    uint32_t v[8];
+__device__ __forceinline__ void convert_block(const float* q, float alpha, float h, uint32_t k, uint32_t magic,
+                                              uint32_t* v) {
     if constexpr (CT == CT_BF16 || CT == CT_F16) {
         // two values per v_cvt_pk_{bf16,f16}_f32 (round to nearest even) of the rounded fp32 products
 #pragma unroll
@@ -112,6 +110,16 @@ __device__ __forceinline__ void store_block(const MatDesc& M, uint32_t row, uint
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = Conv<CT>::f(q[j], alpha, h, k, magic);
     }
+}
+
+// One block of a row shared by the whole wave (layout 0: the row is wave-uniform).
+template <int CT>
+__device__ __forceinline__ void store_block(const MatDesc& M, uint32_t row, uint32_t col0, const float* q, float alpha,
+                                   float h, uint32_t k, uint32_t magic) {
+    using T = typename Conv<CT>::T;
+    T* out = static_cast<T*>(M.out) + (size_t)row * M.cols;
+    uint32_t v[8];
+    convert_block<CT>(q, alpha, h, k, magic, v);
     if ((M.cols * (uint32_t)sizeof(T)) % 4 == 0) {
         // one unconditional buffer store per row: the resource spans this row, so dwords past its
         // end are dropped by the bounds check (whole dwords, as the row length is a multiple of 4)
@@ -126,6 +134,29 @@ __device__ __forceinline__ void store_block(const MatDesc& M, uint32_t row, uint
             __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, d), ro, off, 0, 0);
         }
     } else if (col0 + 8 <= M.cols && (M.cols & 7) == 0) {
+        if constexpr (sizeof(T) == 2) {
+            *reinterpret_cast<uint4*>(out + col0) =
+                make_uint4(v[0] | v[1] << 16, v[2] | v[3] << 16, v[4] | v[5] << 16, v[6] | v[7] << 16);
+        } else {
+            *reinterpret_cast<uint2*>(out + col0) =
+                make_uint2(v[0] | v[1] << 8 | v[2] << 16 | v[3] << 24, v[4] | v[5] << 8 | v[6] << 16 | v[7] << 24);
+        }
+    } else if (col0 < M.cols) {
+        for (int j = 0; j < 8; ++j)
+            if (col0 + j < M.cols) out[col0 + j] = (T)v[j];
+    }
+}
+
+// One block at a row of the lane's own (layout 1: the rows differ across the wave), through a
+// per-lane address; columns past the matrix are dropped.
+template <int CT>
+__device__ __forceinline__ void store_block_lane(const MatDesc& M, uint32_t row, uint32_t col0, const float* q,
+                                                 float alpha, float h, uint32_t k, uint32_t magic) {
+    using T = typename Conv<CT>::T;
+    uint32_t v[8];
+    convert_block<CT>(q, alpha, h, k, magic, v);
+    T* out = static_cast<T*>(M.out) + (size_t)row * M.cols;
+    if (col0 + 8 <= M.cols && (M.cols & 7) == 0) {
         if constexpr (sizeof(T) == 2) {
             *reinterpret_cast<uint4*>(out + col0) =
                 make_uint4(v[0] | v[1] << 16, v[2] | v[3] << 16, v[4] | v[5] << 16, v[6] | v[7] << 16);
@@ -159,10 +190,24 @@ __device__ __forceinline__ float wave_sum_to_lane63(float v) {
     return v;
 }
 
-template <int CT>
+// Stores the blocks of block step rr. Layout 0: tile row rr, block column l of lane l. Layout 1
+// (ROWS): tile row l mod tile_rows, block column (32 / tile_rows) rr + l / tile_rows, the lane's
+// own row scale.
+template <int CT, bool ROWS>
 __device__ __forceinline__ void store_row(const MatDesc& M, const Tile& t, const PairRows& P, int rr, const float* q,
                                           float h) {
-    if constexpr (gemv_rows(CT) > 0) {
+    if constexpr (ROWS) {
+        const bool r16 = M.tile_rows == 16;
+        const uint32_t row = P.row0 + ((uint32_t)t.l & (r16 ? 15u : 31u));
+        if (!t.valid || row >= M.rows) return;
+        const uint32_t blk = r16 ? 2u * (uint32_t)rr + ((uint32_t)t.l >> 4) : (uint32_t)rr;
+        const float alpha = h * P.sc_l;
+        store_block_lane<CT>(M, row, P.tc * 256 + 8 * blk, q, alpha, h, P.k_l, P.magic_l);
+        if constexpr (CT == CT_F8E4M3 || CT == CT_I8) {
+            if (P.tc == 0 && rr == 0 && (uint32_t)t.l < M.tile_rows)
+                M.scale_out[row] = CT == CT_F8E4M3 ? P.sc_l : alpha * (float)P.k_l;
+        }
+    } else if constexpr (gemv_rows(CT) > 0) {
         // fused matrix-vector product: the row's dot products with every activation row, summed
         // over the wave (both tiles of the pair cover the same rows) and added to Y by lane 63
         constexpr int MT = gemv_rows(CT);
@@ -203,7 +248,7 @@ __device__ __forceinline__ void store_row(const MatDesc& M, const Tile& t, const
 
 // Decode C tile pairs side by side (C independent rANS chains per lane, interleaved by the
 // compiler to hide LDS latency).
-template <int CT, int N, int C>
+template <int CT, int N, int C, bool ROWS>
 __device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Tile* t, const uint64_t* pair,
                                           uint64_t pend) {
     const float h = M.step * 0.5f;
@@ -213,7 +258,7 @@ __device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Til
     const __amdgpu_buffer_rsrc_t rs = payload_rsrc(M);
     PairRows P[C];
 #pragma unroll
-    for (int c = 0; c < C; ++c) begin_pair<CT>(M, rs, pair[c], pair[c] < pend, t[c], P[c]);
+    for (int c = 0; c < C; ++c) begin_pair<CT, ROWS>(M, rs, pair[c], pair[c] < pend, t[c], P[c]);
     // A row's values are stored after the next row's ring top-up: the top-up waits for its chunk
     // loads with the vector-memory counter, which also counts stores, so a store issued just
     // before it would be waited for too; issued after it, the store has a whole row to drain.
@@ -227,7 +272,7 @@ __device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Til
         for (int c = 0; c < C; ++c) top_up(t[c], rs);
         if (rr > 0) {
 #pragma unroll
-            for (int c = 0; c < C; ++c) store_row<CT>(M, t[c], P[c], rr - 1, qp[c], h);
+            for (int c = 0; c < C; ++c) store_row<CT, ROWS>(M, t[c], P[c], rr - 1, qp[c], h);
         }
 #pragma unroll
         for (int c = 0; c < C; ++c) b[c] = lo0 + (int)coset_step<N>(t[c], f0, f1);
@@ -280,7 +325,7 @@ __device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Til
             for (int j = 0; j < 8; ++j) qp[c][j] = q[c][j];
     }
 #pragma unroll
-    for (int c = 0; c < C; ++c) store_row<CT>(M, t[c], P[c], M.tile_rows - 1, qp[c], h);
+    for (int c = 0; c < C; ++c) store_row<CT, ROWS>(M, t[c], P[c], M.tile_rows - 1, qp[c], h);
 #pragma unroll
     for (int c = 0; c < C; ++c) end_tile(t[c]);
 }
@@ -297,7 +342,13 @@ __device__ __forceinline__ void lossy_pairs(const MatDesc& M, const Tables& T, T
         uint64_t pr[kChains];
 #pragma unroll
         for (int c = 0; c < kChains; ++c) pr[c] = p + (uint64_t)c * kWaves;
-        lossy_run<CT, N, kChains>(M, T, t, pr, p1);
+        if constexpr (gemv_rows(CT) == 0) {
+            if (M.layout) {                         // uniform: one layout per matrix
+                lossy_run<CT, N, kChains, true>(M, T, t, pr, p1);
+                continue;
+            }
+        }
+        lossy_run<CT, N, kChains, false>(M, T, t, pr, p1);
     }
 }
 
@@ -578,7 +629,8 @@ hipError_t launch_group(const MatDesc* mats, int count, hipStream_t stream) {
 }
 
 hipError_t launch_gemv(const MatDesc& m, hipStream_t stream) {
-    if (m.mode != 0 || m.gemv_m == 0 || m.gemv_m > gemv_rows(m.container)) return hipErrorInvalidValue;
+    // the matrix-vector kernel reads layout-0 streams (layout 1 goes to the MFMA kernel)
+    if (m.mode != 0 || m.layout != 0 || m.gemv_m == 0 || m.gemv_m > gemv_rows(m.container)) return hipErrorInvalidValue;
     GroupArgs g{};
     g.count = 1;
     g.m[0] = m;

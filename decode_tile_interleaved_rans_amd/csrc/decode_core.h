@@ -265,9 +265,11 @@ __device__ __forceinline__ void init_lane(Tile& t, uint8_t* ring_base, int chain
     t.valid = false;
 }
 
-// Rows of one tile pair: tile coordinates and the per-row scales, one row per lane, read back
-// per row with readlane. INT8: the row's divisor k and its reciprocal multiplier, computed once
-// per pair by each lane for its row (a vector division per pair instead of a scalar one per row).
+// Rows of one tile pair: tile coordinates and the per-row scales, one row per lane: in layout 0
+// lane l holds tile row l's, read back per row with readlane; in layout 1 the row the lane codes
+// (tile row l mod tile_rows), used by the lane itself. INT8: the row's divisor k and its
+// reciprocal multiplier, computed once per pair by each lane for its row (a vector division per
+// pair instead of a scalar one per row).
 struct PairRows {
     uint32_t tc, row0;
     float sc_l;
@@ -277,7 +279,7 @@ struct PairRows {
 
 constexpr int gemv_rows(int CT) { return CT >= CT_GEMV1 ? CT - 100 : 0; }
 
-template <int CT>
+template <int CT, bool ROWS = false>
 __device__ __forceinline__ void begin_pair(const MatDesc& M, __amdgpu_buffer_rsrc_t rs, uint64_t pair, bool live,
                                            Tile& t, PairRows& P) {
     const uint32_t tr = (uint32_t)(pair / M.pairs_c);
@@ -285,8 +287,9 @@ __device__ __forceinline__ void begin_pair(const MatDesc& M, __amdgpu_buffer_rsr
     t.valid = live && P.tc < M.tiles_c;
     begin_tile(M, rs, (uint64_t)tr * M.tiles_c + P.tc, t);
     P.row0 = tr * M.tile_rows;
-    const uint32_t my_row = P.row0 + t.l;
-    const bool mine = t.l < M.tile_rows && my_row < M.rows;
+    const uint32_t my_l = ROWS ? (uint32_t)t.l & (M.tile_rows - 1u) : (uint32_t)t.l;   // tile_rows: 16 or 32
+    const uint32_t my_row = P.row0 + my_l;
+    const bool mine = my_l < M.tile_rows && my_row < M.rows;
     P.sc_l = mine ? M.row_scale[my_row] : 0.0f;
     P.k_l = 1;
     P.magic_l = 0;

@@ -337,7 +337,7 @@ struct TileArgs {
     const int32_t* lo;            // [17]
     const int32_t* width;         // [17]
     int64_t kb, tiles_c, n_tiles;
-    int tile_rows, prob_bits;
+    int tile_rows, prob_bits, layout;
     uint16_t* stack;              // [n_tiles][cap] words in stack order
     int64_t cap;
     uint32_t* states;             // [n_tiles][32] final states
@@ -359,10 +359,11 @@ __global__ __launch_bounds__(256) void encode_tiles(TileArgs a) {
     uint32_t sp = 0;
     unsigned int esc_count = 0;
     uint16_t* st = a.stack + (live ? tile : 0) * a.cap;
-    const int64_t k = tc * 32 + l;                            // block column of this lane
     const uint32_t above = l == 31 ? 0u : ~0u << (l + 1);     // lanes above this one in the half
-    for (int rr = a.tile_rows - 1; rr >= 0; --rr) {
-        const int64_t r = tr * a.tile_rows + rr;
+    for (int bs = a.tile_rows - 1; bs >= 0; --bs) {
+        int rr, kk;                                           // the block this lane codes at step bs
+        block_of(a.layout, a.tile_rows, l, bs, &rr, &kk);
+        const int64_t r = tr * a.tile_rows + rr, k = tc * 32 + kk;
         int32_t qv[8];
         int b = 0;
         if (live) {
@@ -710,7 +711,7 @@ ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_o
     unsigned int n_esc = 0;
     if (n_tiles > 0) {
         TileArgs ta{d_q.as<int16_t>(), d_coset.as<uint8_t>(), d_fc.as<uint32_t>(), d_lo.as<int32_t>(), d_wd.as<int32_t>(),
-                    kb, tiles_c, n_tiles, tr, n, d_stack.as<uint16_t>(), cap, d_states.as<uint32_t>(),
+                    kb, tiles_c, n_tiles, tr, n, o.layout, d_stack.as<uint16_t>(), cap, d_states.as<uint32_t>(),
                     d_words.as<uint32_t>(), d_nesc.as<unsigned int>()};
         hipLaunchKernelGGL(encode_tiles, dim3((unsigned)((n_tiles + 7) / 8)), dim3(256), 0, s, ta);
         EP_HIP(hipGetLastError());
@@ -751,7 +752,7 @@ ep_status encode_lossy_dt(const void* w, int64_t R, int64_t C, const ep_encode_o
             crc = gf2_mulmod(len == (uint64_t)kCrcChunk ? op_full : x_pow_8n(len), crc) ^ crcs[i];
         }
     }
-    const uint64_t o_pay = serialize_lossy(DT, R, C, tr, n, tables, step, (float)o.target_bpp, scale, qmax, acc,
+    const uint64_t o_pay = serialize_lossy(DT, R, C, tr, o.layout, n, tables, step, (float)o.target_bpp, scale, qmax, acc,
                                            std::move(offsets), n_esc, n_tiles > 0 ? crc : 0u, out);
     if (n_tiles > 0) {
         EP_HIP(hipMemcpyAsync(out->data() + o_pay, d_payload.p(), acc, hipMemcpyDeviceToHost, s));

@@ -40,9 +40,25 @@ enum HeaderField : int {
     kTileColsField = 18, kLanesField = 20, kProbBits = 22, kNumTables = 23, kStep = 24,
     kTarget = 28, kNumTiles = 32, kNumEscapes = 36, kOffScale = 40, kOffQmax = 48,
     kOffTables = 56, kOffIndex = 64, kOffPayload = 72, kTotalLen = 80, kPayloadCrc = 88,
-    kOffRaw = 96, kRawCrc = 104, kMetaCrc = 112
+    kOffRaw = 96, kRawCrc = 104, kMetaCrc = 112, kLayout = 116
 };
 constexpr int kFormatVersion = 2;      // 2: the metadata CRC-32 at byte 112
+
+// Which block of a tile lane l codes at block step s (a tile is tile_rows x 32 blocks of 8
+// columns, coded in tile_rows block steps). The pages interleave 32 states per tile without fixing
+// this (reading R27). Layout 0: tile row s, block column l. Layout 1: tile row l mod tile_rows,
+// block column (32 / tile_rows) s + l / tile_rows, so every block step covers all tile rows: at
+// step s of a 16-row tile pair a wave holds a 16 x 32 block, one MFMA B operand. (constexpr:
+// callable from device code too.)
+constexpr void block_of(int layout, int tile_rows, int l, int s, int* rr, int* kk) {
+    if (layout == 0) {
+        *rr = s;
+        *kk = l;
+    } else {
+        *rr = l % tile_rows;
+        *kk = (kLanes / tile_rows) * s + l / tile_rows;
+    }
+}
 
 struct Table {
     int32_t lo = 0;        // first coordinate value of the window (lossless: 0)
@@ -81,6 +97,7 @@ struct StreamView {
     const uint8_t* base = nullptr;
     size_t len = 0;
     int mode = 0, dtype = 0, tile_rows = 16, prob_bits = 12, n_tables = 0;
+    int layout = 0;                      // lossy tile layout (block_of)
     int64_t rows = 0, cols = 0, tiles_r = 0, tiles_c = 0;
     uint32_t n_tiles = 0, n_escapes = 0;
     float step = 0.0f, target = 0.0f;
@@ -116,7 +133,7 @@ double sample_estimate(const uint64_t (*cnt)[256], const uint64_t* totals, int64
 float choose_step(double U, double target, const std::function<double(double)>& est);
 // Header, row metadata, tables and tile index of a lossy stream whose payload (payload_len bytes,
 // CRC-32 payload_crc) the caller writes itself at the returned offset of *out.
-uint64_t serialize_lossy(int dt, int64_t R, int64_t C, int tile_rows, int n, const std::vector<Table>& tables,
+uint64_t serialize_lossy(int dt, int64_t R, int64_t C, int tile_rows, int layout, int n, const std::vector<Table>& tables,
                          float step, float target, const std::vector<float>& scale, const std::vector<uint16_t>& qmax,
                          uint64_t payload_len, std::vector<uint32_t>&& offsets, uint32_t n_esc, uint32_t payload_crc,
                          Bytes* out);

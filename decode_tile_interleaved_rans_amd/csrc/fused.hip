@@ -284,6 +284,135 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_f8(GroupArgs g) {
     if (t.err) atomicOr(M.err, t.err);
 }
 
+// ----------------------------------------------------------------------------- row layout
+// Streams in the row layout (every rANS state of a tile stays on one tile row: lane l codes row
+// l mod 16 at block column 2 s + l / 16 in block step s) need no transposition at all: at block
+// step s of a tile pair, lane L holds the 8 weights of row n = L mod 16 in the 8 columns
+// c0(L) + 16 s, c0(L) = 512 pc + 256 (L / 32) + 8 ((L / 16) mod 2) (tile L / 32 of pair pc), i.e.
+// exactly its part of the B operand of a 16 x 16 x 32 MFMA whose K group L / 16 is those 8
+// columns. The lane converts them in registers (BF16 of q alpha_r with its own row's alpha_r, or
+// the E4M3 code of q h) and the MFMA consumes them at once, with the activations of the same 8
+// columns of row 16 mt + n as the A operand, loaded before the step's decode so that their latency
+// hides behind it. LDS holds only the decoder's tables and word rings, so the kernel runs 16 waves
+// per CU as the decode kernel does. The accumulators have the layout of the transposing kernel's,
+// so the partials and the finishing sums are the same.
+typedef long i64_t;
+
+template <int N, int MT, bool F8>
+__device__ __forceinline__ void rows_pair(const MatDesc& M, const Tables& T, Tile& t, uint64_t pair,
+                                          __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rx) {
+    const float h = M.step * 0.5f;
+    const uint2* coset = reinterpret_cast<const uint2*>(M.tables + ((size_t)M.n_tables << N));   // table 0
+    const uint32_t f0 = coset[0].x, f1 = coset[1].x;
+    const int lo0 = (int32_t)coset[0].y >> 16;
+    PairRows P;
+    begin_pair<F8 ? CT_F8E4M3 : CT_BF16, true>(M, rs, pair, true, t, P);
+    const float alpha = h * P.sc_l;                 // the lane's row (scale 0 past the matrix)
+    const int lane = threadIdx.x & 63, qg = lane >> 4, n = lane & 15;
+    const uint32_t K = M.cols;
+    const uint32_t c0 = (uint32_t)(pair % M.pairs_c) * 512u + (uint32_t)(qg >> 1) * 256u + 8u * (uint32_t)(qg & 1);
+    const uint32_t keep = t.valid ? 0xFFFFFFFFu : 0u;
+    constexpr uint32_t kEs = F8 ? 1u : 2u;          // activation bytes per element
+    f32x4_t acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < 16; ++s) {
+        const uint32_t kc = c0 + 16u * (uint32_t)s;
+        // columns past K read as zero (K % 8 == 0: a block is wholly inside or outside), and so do
+        // activation rows past M (past the end of the resource)
+        const uint32_t oob = (uint32_t)((int32_t)(K - 1u - kc) >> 31) & 0x80000000u;
+        uint4 ax[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const uint32_t off = (((uint32_t)(16 * mt + n) * K + kc) * kEs) | oob;
+            if constexpr (F8) {
+                const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rx, off, 0, 0));
+                ax[mt] = make_uint4(v.x, v.y, 0u, 0u);
+            } else {
+                ax[mt] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+            }
+        }
+        top_up(t, rs);
+        const int b = lo0 + (int)coset_step<N>(t, f0, f1);
+        refill(t);
+        const uint32_t base = (uint32_t)b << N;
+        const uint2* ent_b = T.ent + b * 256;
+        float q[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint2 e;
+            const uint2* ent_j = ent_b + 2 * j * 256;
+            rans_steps<N, 1>(&t, (2 * j) << N, &base, &ent_j, &e);
+            refill_all<1>(&t);
+            q[j] = hi16_to_f32(e.y);
+            if ((M.esc_tables >> (2 * j)) & 3u) {
+                const bool esc = (int32_t)e.x < 0;
+                if (__ballot(esc)) {
+                    const uint32_t w = take_words(t, esc);
+                    if (esc) q[j] = (float)(int32_t)(int16_t)(2 * (int32_t)(int16_t)w + b);
+                }
+            }
+        }
+        if constexpr (F8) {
+            uint32_t bw[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const float a0 = __builtin_amdgcn_fmed3f(q[4 * i] * h, -448.0f, 448.0f);
+                const float a1 = __builtin_amdgcn_fmed3f(q[4 * i + 1] * h, -448.0f, 448.0f);
+                const float a2 = __builtin_amdgcn_fmed3f(q[4 * i + 2] * h, -448.0f, 448.0f);
+                const float a3 = __builtin_amdgcn_fmed3f(q[4 * i + 3] * h, -448.0f, 448.0f);
+                const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+                bw[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, lo, true) & keep;
+            }
+            const i64_t bop = __builtin_bit_cast(i64_t, make_uint2(bw[0], bw[1]));
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+                    __builtin_bit_cast(i64_t, make_uint2(ax[mt].x, ax[mt].y)), bop, acc[mt], 0, 0, 0);
+        } else {
+            uint4 bw;
+            bw.x = pack_bf16(q[0] * alpha, q[1] * alpha) & keep;
+            bw.y = pack_bf16(q[2] * alpha, q[3] * alpha) & keep;
+            bw.z = pack_bf16(q[4] * alpha, q[5] * alpha) & keep;
+            bw.w = pack_bf16(q[6] * alpha, q[7] * alpha) & keep;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ax[mt]),
+                                                                  __builtin_bit_cast(bf16x8_t, bw), acc[mt], 0, 0, 0);
+        }
+    }
+    end_tile(t);
+    // partials [pair][mt][q][n][i] (fp32): 1 KiB per M tile, one 16-byte store per lane
+    float* part = static_cast<float*>(M.out) + pair * (uint64_t)(MT * 256);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        *reinterpret_cast<f32x4_t*>(part + ((mt * 4 + qg) * 16 + n) * 4) = acc[mt];
+}
+
+template <int N, int MT, bool F8>
+__global__ __launch_bounds__(64 * kWaves) void decode_mfma_rows(GroupArgs g) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const MatDesc& M = g.m[0];
+    if ((uint32_t)(size_t)(lds_u8*)smem != 0u) {
+        if (threadIdx.x == 0) atomicOr(M.err, kErrLayout);
+        return;
+    }
+    const uint64_t a = (uint64_t)blockIdx.x * g.block_cost;
+    const uint64_t b = std::min<uint64_t>(a + g.block_cost, g.cost_start[1]);
+    const uint64_t w = M.pair_cost;
+    const uint64_t p0 = (a + w - 1) / w, p1 = (b + w - 1) / w;
+    if (p0 >= p1) return;
+    const Tables T = stage_tables(M, smem, true);
+    Tile t;
+    init_lane(t, smem + lds_table_bytes(M.n_tables, M.prob_bits, true), 0);
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const __amdgpu_buffer_rsrc_t rs = payload_rsrc(M);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(M.gemv_x), 0, (int)((size_t)M.gemv_m * M.cols * (F8 ? 1 : 2)), 0x00020000);
+    for (uint64_t p = p0 + (uint64_t)wave; p < p1; p += kWaves) rows_pair<N, MT, F8>(M, T, t, p, rs, rx);
+    if (t.err) atomicOr(M.err, t.err);
+}
+
 // Y [M][N] bf16 = (sum over the tile row's pairs of the partials) x s_x[m] x s_w[n] (+ bias).
 template <int MT>
 __global__ __launch_bounds__(256) void fused_finish_f8(const float* part, const float* sx, const float* sw,
@@ -361,18 +490,69 @@ hipError_t launch_mfma_mt(const GroupArgs& g, uint64_t blocks, hipStream_t strea
     }
 }
 
+template <int N, int MT, bool F8>
+hipError_t launch_rows_n(const GroupArgs& g, uint64_t blocks, hipStream_t stream) {
+    const MatDesc& m = g.m[0];
+    const size_t lds = lds_table_bytes(m.n_tables, m.prob_bits, true) + (size_t)kWaves * 2 * kRingBytes;
+    const void* k = reinterpret_cast<const void*>(decode_mfma_rows<N, MT, F8>);
+    hipError_t e = allow_lds(k);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_mfma_rows<N, MT, F8>), dim3((unsigned)blocks), dim3(64 * kWaves), lds, stream, g);
+    return hipGetLastError();
+}
+
+template <int MT, bool F8>
+hipError_t launch_rows_mt(const GroupArgs& g, uint64_t blocks, hipStream_t stream) {
+    switch (g.m[0].prob_bits) {
+        case 10: return launch_rows_n<10, MT, F8>(g, blocks, stream);
+        case 11: return launch_rows_n<11, MT, F8>(g, blocks, stream);
+        default: return launch_rows_n<12, MT, F8>(g, blocks, stream);
+    }
+}
+
+// 16-row M tiles the kernel keeps per wave: 1 for the transposing kernel, up to 4 in the row layout.
+int fused_mt(const MatDesc& m, int64_t M) { return m.layout == 0 || M <= 16 ? 1 : M <= 32 ? 2 : 4; }
+
+template <bool F8>
+hipError_t launch_rows(const GroupArgs& g, int mt, uint64_t blocks, hipStream_t stream) {
+    switch (mt) {
+        case 1: return launch_rows_mt<1, F8>(g, blocks, stream);
+        case 2: return launch_rows_mt<2, F8>(g, blocks, stream);
+        default: return launch_rows_mt<4, F8>(g, blocks, stream);
+    }
+}
+
+hipError_t launch_finish(const float* part, const float* xs, const float* sw, const uint16_t* bias, uint16_t* y,
+                         int M, int rows, int pairs_c, int mt, hipStream_t stream) {
+    const unsigned fb = (unsigned)(((int64_t)M * rows + 255) / 256);
+    if (xs) {
+        switch (mt) {
+            case 1: hipLaunchKernelGGL(fused_finish_f8<1>, dim3(fb), dim3(256), 0, stream, part, xs, sw, bias, y, M, rows, pairs_c); break;
+            case 2: hipLaunchKernelGGL(fused_finish_f8<2>, dim3(fb), dim3(256), 0, stream, part, xs, sw, bias, y, M, rows, pairs_c); break;
+            default: hipLaunchKernelGGL(fused_finish_f8<4>, dim3(fb), dim3(256), 0, stream, part, xs, sw, bias, y, M, rows, pairs_c); break;
+        }
+    } else {
+        switch (mt) {
+            case 1: hipLaunchKernelGGL(fused_finish<1>, dim3(fb), dim3(256), 0, stream, part, bias, y, M, rows, pairs_c); break;
+            case 2: hipLaunchKernelGGL(fused_finish<2>, dim3(fb), dim3(256), 0, stream, part, bias, y, M, rows, pairs_c); break;
+            default: hipLaunchKernelGGL(fused_finish<4>, dim3(fb), dim3(256), 0, stream, part, bias, y, M, rows, pairs_c); break;
+        }
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool fused_fits(const MatDesc& m, int64_t M) {
     // X is addressed through one buffer resource with 32-bit byte offsets
-    return m.mode == 0 && m.tile_rows == 16 && M >= 1 && M <= kFusedMaxRows && (m.cols & 7) == 0 &&
-           (uint64_t)kFusedMaxRows * m.cols * 2 < (1ull << 31);
+    const int max_rows = m.layout ? kFusedMaxRowsRowLayout : kFusedMaxRows;
+    return m.mode == 0 && m.tile_rows == 16 && M >= 1 && M <= max_rows && (m.cols & 7) == 0 &&
+           (uint64_t)kFusedMaxRowsRowLayout * m.cols * 2 < (1ull << 31);
 }
 
 size_t fused_partial_bytes(const MatDesc& m, int64_t M) {
     const uint64_t pairs = (uint64_t)((m.rows + m.tile_rows - 1) / m.tile_rows) * m.pairs_c;
-    (void)M;                                        // one 16 x 16 tile of partial sums per pair
-    return (size_t)pairs * 256 * sizeof(float);
+    return (size_t)pairs * (size_t)fused_mt(m, M) * 256 * sizeof(float);   // a 16 x 16 fp32 tile per M tile
 }
 
 hipError_t launch_fused(const MatDesc& m, const uint16_t* x, int64_t M, float* part, const uint16_t* bias,
@@ -392,12 +572,10 @@ hipError_t launch_fused(const MatDesc& m, const uint16_t* x, int64_t M, float* p
     const uint64_t blocks = (uint64_t)device_cus();
     g.block_cost = (total + blocks - 1) / blocks;
     const uint64_t used = (total + g.block_cost - 1) / g.block_cost;
-    hipError_t e = launch_mfma_mt<1>(g, used, stream);
+    const int mt = fused_mt(m, M);
+    hipError_t e = m.layout ? launch_rows<false>(g, mt, used, stream) : launch_mfma_mt<1>(g, used, stream);
     if (e != hipSuccess) return e;
-    const int64_t outs = M * (int64_t)m.rows;
-    const unsigned fb = (unsigned)((outs + 255) / 256);
-    hipLaunchKernelGGL(fused_finish<1>, dim3(fb), dim3(256), 0, stream, part, bias, y, (int)M, (int)m.rows, (int)m.pairs_c);
-    return hipGetLastError();
+    return launch_finish(part, nullptr, nullptr, bias, y, (int)M, (int)m.rows, (int)m.pairs_c, mt, stream);
 }
 
 
@@ -418,13 +596,10 @@ hipError_t launch_fused_f8(const MatDesc& m, const uint8_t* xq, const float* xs,
     const uint64_t blocks = (uint64_t)device_cus();
     g.block_cost = (total + blocks - 1) / blocks;
     const uint64_t used = (total + g.block_cost - 1) / g.block_cost;
-    hipError_t e = launch_mfma_f8_mt<1>(g, used, stream);
+    const int mt = fused_mt(m, M);
+    hipError_t e = m.layout ? launch_rows<true>(g, mt, used, stream) : launch_mfma_f8_mt<1>(g, used, stream);
     if (e != hipSuccess) return e;
-    const int64_t outs = M * (int64_t)m.rows;
-    const unsigned fb = (unsigned)((outs + 255) / 256);
-    const float* sw = m.row_scale;
-    hipLaunchKernelGGL(fused_finish_f8<1>, dim3(fb), dim3(256), 0, stream, part, xs, sw, bias, y, (int)M, (int)m.rows, (int)m.pairs_c);
-    return hipGetLastError();
+    return launch_finish(part, xs, m.row_scale, bias, y, (int)M, (int)m.rows, (int)m.pairs_c, mt, stream);
 }
 
 }  // namespace ep

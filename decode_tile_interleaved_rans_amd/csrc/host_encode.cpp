@@ -307,7 +307,7 @@ struct TileSet {
 };
 
 // Returns the payload's offset in the stream.
-uint64_t serialize(int mode, int dt, int64_t R, int64_t C, int tile_rows, int n, const std::vector<Table>& tables,
+uint64_t serialize(int mode, int dt, int64_t R, int64_t C, int tile_rows, int layout, int n, const std::vector<Table>& tables,
                float step, float target, const std::vector<float>& scale, const std::vector<uint16_t>& qmax,
                const TileSet& ts, uint32_t n_esc, Bytes* out,
                const std::vector<uint8_t>* raw = nullptr, const uint32_t* payload_crc = nullptr) {
@@ -332,6 +332,7 @@ uint64_t serialize(int mode, int dt, int64_t R, int64_t C, int tile_rows, int n,
     w32(s + kRows, (uint32_t)R);
     w32(s + kCols, (uint32_t)C);
     w16(s + kTileRows, (uint32_t)tile_rows);
+    s[kLayout] = (uint8_t)layout;
     w16(s + kTileColsField, kTileCols);
     w16(s + kLanesField, kLanes);
     s[kProbBits] = (uint8_t)n;
@@ -581,11 +582,13 @@ ep_status encode_lossy(const void* w, int dt, int64_t R, int64_t C, const ep_enc
                               [&](int64_t tile, uint8_t* tab, uint8_t* sym, uint16_t* esc) {
         const int64_t r0 = tile / tiles_c * tr, k0 = tile % tiles_c * kLanes;
         uint32_t local = 0;
-        for (int rr = 0; rr < tr; ++rr)
+        for (int bs = 0; bs < tr; ++bs)
             for (int l = 0; l < kLanes; ++l) {
-                const int64_t r = r0 + rr, k = k0 + l;
+                int rr, kk;
+                block_of(o.layout, tr, l, bs, &rr, &kk);
+                const int64_t r = r0 + rr, k = k0 + kk;
                 const int b = coset[r * kb + k];
-                int base = 9 * rr * kLanes + l;
+                int base = 9 * bs * kLanes + l;
                 tab[base] = 0;
                 sym[base] = (uint8_t)(b - tables[0].lo);
                 esc[base] = 0;
@@ -607,7 +610,7 @@ ep_status encode_lossy(const void* w, int dt, int64_t R, int64_t C, const ep_enc
             }
         n_esc += local;
     });
-    serialize(EP_MODE_LOSSY_E8, dt, R, C, tr, n, tables, step, (float)o.target_bpp, scale, qmax, ts, n_esc.load(), out);
+    serialize(EP_MODE_LOSSY_E8, dt, R, C, tr, o.layout, n, tables, step, (float)o.target_bpp, scale, qmax, ts, n_esc.load(), out);
     return EP_OK;
 }
 
@@ -665,7 +668,7 @@ ep_status encode_lossless(const void* w, int dt, int64_t R, int64_t C, const ep_
                 }
     });
     (void)why;
-    serialize(EP_MODE_LOSSLESS, dt, R, C, tr, n, tables, 0.0f, 0.0f, {}, {}, ts, 0, out);
+    serialize(EP_MODE_LOSSLESS, dt, R, C, tr, 0, n, tables, 0.0f, 0.0f, {}, {}, ts, 0, out);
     return EP_OK;
 }
 
@@ -716,7 +719,7 @@ ep_status encode_lossless_exp(const void* w, int64_t R, int64_t C, const ep_enco
                     sym[idx] = (uint8_t)(element(r0 + rr, c0 + 8 * l + e) >> 7);
                 }
     });
-    serialize(EP_MODE_LOSSLESS_EXP, EP_BF16, R, C, tr, n, tables, 0.0f, 0.0f, {}, {}, ts, 0, out, &raw);
+    serialize(EP_MODE_LOSSLESS_EXP, EP_BF16, R, C, tr, 0, n, tables, 0.0f, 0.0f, {}, {}, ts, 0, out, &raw);
     return EP_OK;
 }
 
@@ -732,14 +735,14 @@ float choose_step(double U, double target, const std::function<double(double)>& 
     return search_step(U, target, est);
 }
 
-uint64_t serialize_lossy(int dt, int64_t R, int64_t C, int tile_rows, int n, const std::vector<Table>& tables,
+uint64_t serialize_lossy(int dt, int64_t R, int64_t C, int tile_rows, int layout, int n, const std::vector<Table>& tables,
                          float step, float target, const std::vector<float>& scale, const std::vector<uint16_t>& qmax,
                          uint64_t payload_len, std::vector<uint32_t>&& offsets, uint32_t n_esc, uint32_t payload_crc,
                          Bytes* out) {
     TileSet ts;
     ts.offsets = std::move(offsets);
     ts.external_len = payload_len;
-    return serialize(EP_MODE_LOSSY_E8, dt, R, C, tile_rows, n, tables, step, target, scale, qmax, ts, n_esc, out,
+    return serialize(EP_MODE_LOSSY_E8, dt, R, C, tile_rows, layout, n, tables, step, target, scale, qmax, ts, n_esc, out,
                      nullptr, &payload_crc);
 }
 

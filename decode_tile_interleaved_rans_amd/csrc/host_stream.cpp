@@ -85,6 +85,7 @@ ep_status parse_stream(const uint8_t* s, size_t len, StreamView* v, std::string*
     v->rows = r32(s + kRows);
     v->cols = r32(s + kCols);
     v->tile_rows = (int)r16(s + kTileRows);
+    v->layout = s[kLayout];
     v->prob_bits = s[kProbBits];
     v->n_tables = s[kNumTables];
     v->step = rf32(s + kStep);
@@ -99,6 +100,7 @@ ep_status parse_stream(const uint8_t* s, size_t len, StreamView* v, std::string*
         return bad(why, "lossy stream with a source dtype other than f32/bf16/f16");
     if (!lossy && element_bytes(v->dtype) == 0) return bad(why, "unknown source dtype");
     if (v->tile_rows != 16 && v->tile_rows != 32) return bad(why, "tile_rows must be 16 or 32");
+    if (v->layout > 1 || (v->layout != 0 && !lossy)) return bad(why, "tile layout must be 0, or 1 in the lossy mode");
     if (r16(s + kTileColsField) != (uint32_t)kTileCols || r16(s + kLanesField) != (uint32_t)kLanes)
         return bad(why, "tile width must be 256 columns and 32 lanes");
     if (v->prob_bits < 10 || v->prob_bits > 12) return bad(why, "prob_bits outside 10..12");
@@ -193,6 +195,7 @@ void fill_info(const StreamView& v, ep_info* info) {
     info->mode = v.mode;
     info->src_dtype = v.dtype;
     info->tile_rows = v.tile_rows;
+    info->layout = v.layout;
     info->prob_bits = v.prob_bits;
     info->n_tiles = v.n_tiles;
     info->n_escapes = v.n_escapes;

@@ -39,6 +39,7 @@ struct MatDesc {
     uint16_t esc_tables;        // lossy: bit 2j + b set when coordinate table 1 + 2j + b can decode
                                 // the escape symbol (its frequency is not zero)
     uint32_t pair_cost;         // relative decode time of one tile pair (load balancing)
+    uint8_t layout;             // lossy tile layout: 0 lane = block column, 1 lane = tile row (block_of)
 };
 
 // Relative decode time of one tile pair, per tile row: a lossy row is 9 steps (coset + 8

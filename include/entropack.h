@@ -64,13 +64,20 @@ typedef enum {
 } ep_mode;
 
 /* Encoder options. A NULL pointer means: lossy, target 4.0, prob_bits 12, tile_rows 16, all
- * host threads. */
+ * host threads, layout 0. */
 typedef struct {
     ep_mode mode;
     double target_bpp;     /* lossy only: target payload bits per weight (0 < t <= 32) */
     int prob_bits;         /* probability precision n (10..12); frequencies sum to 2^n */
     int tile_rows;         /* 16 or 32 rows per tile; tiles are tile_rows x 256 */
     int n_threads;         /* host encoder threads, 0 = all hardware threads */
+    int layout;            /* lossy tile layout (reading R27; 0 in the lossless modes): which 8-column
+                              block of a tile each of its 32 rANS states codes at block step s.
+                              0: tile row s, block column l (lane l). 1: tile row l mod tile_rows,
+                              block column (32 / tile_rows) s + l / tile_rows, so every block step
+                              covers all tile rows; the compressed linear forward multiplies
+                              layout-1 weights straight from the decoder's registers. Both layouts
+                              decode to the same weights. */
 } ep_encode_opts;
 
 /* Stream summary. actual_bpp = 8 * total_bytes / (rows * cols) (0 for an empty matrix).
@@ -83,6 +90,7 @@ typedef struct {
     float step, target_bpp;
     double actual_bpp;
     uint64_t total_bytes, payload_bytes, state_bytes, meta_bytes;
+    int32_t layout;        /* lossy tile layout (ep_encode_opts.layout) */
 } ep_info;
 
 typedef struct ep_handle ep_handle;   /* device-resident, validated stream */
@@ -189,13 +197,20 @@ ep_status ep_decode_symbols(const ep_handle* h, int16_t* dev_q, void* hip_stream
  * Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section
  * "Replace one linear layer before a whole model" (CompressedLinear); "EntroPack: Fast and Accurate
  * Entropy-Coded Weight Compression at Arbitrary Bitrates", Abstract (decoding fused into the GPU
- * computation that uses the weight). For M <= 4 the decode kernel itself forms the
- * products (the decoded fp32 weights, not rounded to BF16, are multiplied by the activations in
- * registers and summed into an fp32 accumulator in the workspace by atomic additions, whose order
- * varies, so two calls may differ in the last bits; the weight is never written). For larger M
- * the weight is decoded once per call, up to 128 MiB of BF16 rows at a time, into a
- * library-owned workspace that stays in the Infinity Cache, and each slice is multiplied by the
- * BF16 MFMA GEMM (deterministic); no decoded copy of W outlives the call. The workspace belongs
+ * computation that uses the weight). Paths:
+ *   - fused decode + MFMA, for M <= 64 on row-layout streams (ep_encode_opts.layout = 1) and for
+ *     5 <= M <= 16 on layout-0 streams: each tile pair is decoded once into the B operand of the
+ *     BF16 MFMA (row layout: straight from the decoder's registers; layout 0: transposed through
+ *     LDS), the weight never written; fp32 partial sums per tile pair in the workspace, summed in
+ *     column order (deterministic);
+ *   - M <= 4 on layout-0 streams: the decode kernel forms the products (the decoded fp32
+ *     weights, not rounded to BF16, times the activations in registers, summed into an fp32
+ *     accumulator in the workspace by atomic additions, whose order varies, so two calls may
+ *     differ in the last bits);
+ *   - otherwise the weight is decoded once per call, up to 128 MiB of BF16 rows at a time, into
+ *     the workspace, which stays in the Infinity Cache, and each slice is multiplied by the BF16
+ *     MFMA GEMM (deterministic); no decoded copy of W outlives the call.
+ * The fused and slice paths multiply the same BF16-rounded weights. The workspace belongs
  * to the (device, hip_stream) pair: calls on one stream reuse it in order, calls on different
  * streams get different workspaces; it is allocated on first use
  * (hipMalloc, which may synchronize the device) and kept until the process ends.
@@ -208,9 +223,9 @@ ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, co
  * harnesses that forbid hipMalloc): ep_linear_forward with its scratch in a static device array
  * of 64 MiB per device instead of the library's workspace pool. It calls no hipMalloc, hipFree or
  * allocating library routine; the array lives from library load until the process ends. Same
- * arguments, results and paths as ep_linear_forward (the same kernels: for 5 <= M <= 16 the fused
- * kernel's partial sums, for M <= 4 the fp32 accumulator, above that BF16 weight slices of at most
- * 64 MiB, i.e. 64 MiB / (2 K) rows). EP_ERANGE when a call needs more than the array holds
+ * arguments, results and paths as ep_linear_forward (the same kernels: the fused kernel's partial
+ * sums, the fp32 accumulator of M <= 4 on layout-0 streams, otherwise BF16 weight slices of at
+ * most 64 MiB, i.e. 64 MiB / (2 K) rows). EP_ERANGE when a call needs more than the array holds
  * (M <= 4 with 4 M N > 64 MiB, the fused partials of very wide layers, or K > 2^21 for the slices).
  * Every call on a device shares that device's array: calls that overlap in time on one device
  * (other streams, other threads) race and must be serialized by the caller.
@@ -232,11 +247,13 @@ ep_status ep_gemm_bf16(const void* dev_x, const void* dev_w, int64_t M, int64_t 
  * Abstract (the FP8 container); "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory
  * Checks", section "Replace one linear layer before a whole model".
  * FP8 variant of ep_linear_forward: Y[M][N] = s_x[m] s_w[n] sum_k x8[m][k] w8[n][k] (+ bias), BF16
- * output. The weight is decoded, slice by slice as in ep_linear_forward, into the FP8 E4M3
- * container with its per-row scale s_w (the FP8 container of "EntroPack: Fast and Accurate
- * Entropy-Coded Weight Compression at Arbitrary Bitrates", Abstract), the activations are
- * quantized per row as ep_quantize_rows_fp8 does, and both meet in the gfx950 FP8 MFMA with fp32
- * accumulation. Same workspace rules as ep_linear_forward. dev_x: [M][K] bf16, 16-byte aligned,
+ * output. The weight is decoded into the FP8 E4M3 container with its per-row scale s_w (the FP8
+ * container of "EntroPack: Fast and Accurate Entropy-Coded Weight Compression at Arbitrary
+ * Bitrates", Abstract), the activations are quantized per row as ep_quantize_rows_fp8 does, and
+ * both meet in the gfx950 FP8 MFMA with fp32 accumulation. For M <= 64 on row-layout streams and
+ * M <= 16 on layout-0 streams the codes go straight into the MFMA's B operand (fused, as in
+ * ep_linear_forward); otherwise the weight is decoded slice by slice into the workspace and
+ * multiplied by the FP8 GEMM. Same workspace rules as ep_linear_forward. dev_x: [M][K] bf16, 16-byte aligned,
  * finite; dev_bias: [N] bf16 or NULL; dev_y: [M][N] bf16. Requires a lossy stream and
  * K % 16 == 0. Asynchronous on hip_stream. */
 ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias,

@@ -87,7 +87,7 @@ int main(int argc, char** argv) {
         w[i] = (float)(0.02 * (uniform01() + uniform01() + uniform01() + uniform01() - 2.0) * 1.7320508);
 
     /* 1. lossless round trip, checked here */
-    ep_encode_opts lossless = {EP_MODE_LOSSLESS, 0.0, 12, 16, 0};
+    ep_encode_opts lossless = {EP_MODE_LOSSLESS, 0.0, 12, 16, 0, 0};
     uint8_t* s = NULL;
     size_t len = 0;
     double bpp = 0.0;
@@ -102,7 +102,7 @@ int main(int argc, char** argv) {
     printf("lossless fp32 round trip bit-exact at %.4f bpp\n", bpp);
 
     /* 2. lossy decode to BF16, written out for the oracle comparison */
-    ep_encode_opts lossy = {EP_MODE_LOSSY_E8, 4.0, 12, 16, 0};
+    ep_encode_opts lossy = {EP_MODE_LOSSY_E8, 4.0, 12, 16, 0, 0};
     st = ep_compress(w, EP_F32, R, C, &lossy, &s, &len, &bpp);
     if (st != EP_OK) return fail_ep("ep_compress (lossy)", st);
     ep_info info;

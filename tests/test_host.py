@@ -58,10 +58,11 @@ def test_header_is_plain_c():
     assert r.returncode == 0, r.stderr
 
 
-def oracle_and_product(w, target, dtype=None, mode=0, prob_bits=12, tile_rows=16, threads=4):
-    so, bo = oracle.compress(w, target, dtype=dtype, mode=mode, prob_bits=prob_bits, tile_rows=tile_rows)
+def oracle_and_product(w, target, dtype=None, mode=0, prob_bits=12, tile_rows=16, threads=4, layout=0):
+    so, bo = oracle.compress(w, target, dtype=dtype, mode=mode, prob_bits=prob_bits, tile_rows=tile_rows,
+                             layout=layout)
     sp, bp = ep.compress(w, target, dtype=dtype, mode=mode, prob_bits=prob_bits, tile_rows=tile_rows,
-                         n_threads=threads)
+                         n_threads=threads, layout=layout)
     return so, sp, bo, bp
 
 
@@ -96,6 +97,21 @@ def test_encoder_matches_oracle_fp16_and_escapes():
     so, sp, *_ = oracle_and_product(h, 7.0, dtype=ep.F16)
     assert so == sp
     assert oracle.info(so)["n_escapes"] > 0
+
+
+@pytest.mark.parametrize("shape,target,prob_bits,tile_rows", [
+    ((100, 300), 4.5, 10, 16), ((33, 513), 4.0, 11, 32), ((64, 512), 8.0, 12, 16), ((1, 9), 4.0, 11, 16),
+    ((0, 7), 4.0, 12, 16)])
+def test_encoder_matches_oracle_row_layout(shape, target, prob_bits, tile_rows):
+    """The row layout (each rANS state on one tile row, reading R27): the same bytes as the
+    oracle, ragged shapes, 32-row tiles, escapes and an empty matrix included."""
+    w = W.gaussian_with_outliers(*shape, seed=sum(shape), outlier_frac=0.003) if shape[0] else np.zeros(shape, np.float32)
+    so, sp, *_ = oracle_and_product(w, target, prob_bits=prob_bits, tile_rows=tile_rows, threads=3,
+                                    layout=ep.ROW_LAYOUT)
+    assert so == sp
+    assert ep.stream_info(sp)["layout"] == ep.ROW_LAYOUT == oracle.info(so)["layout"]
+    if target >= 8.0:
+        assert oracle.info(so)["n_escapes"] > 0
 
 
 def test_encoder_matches_oracle_degenerate():
@@ -314,6 +330,15 @@ def test_new_entry_points_reject_bad_arguments_before_any_device_work():
     opts = ep.EncodeOpts(ep.LOSSY, 0.0, 12, 16, 0)
     assert L.ep_compress_device(C.c_void_p(16), ep.F32, 4, 4, C.byref(opts), None, C.byref(out), C.byref(n),
                                 None) == -1                                           # target must be > 0
+    opts = ep.EncodeOpts(ep.LOSSY, 4.0, 12, 16, 0, 2)
+    assert L.ep_compress_device(C.c_void_p(16), ep.F32, 4, 4, C.byref(opts), None, C.byref(out), C.byref(n),
+                                None) == -1                                           # layout 0 or 1
+    w = np.zeros((4, 4), np.float32)
+    assert L.ep_compress(w.ctypes.data_as(C.c_void_p), ep.F32, 4, 4, C.byref(opts), C.byref(out), C.byref(n),
+                         None) == -1
+    opts = ep.EncodeOpts(ep.LOSSLESS, 0.0, 12, 16, 0, 1)                               # layout 1 is lossy only
+    assert L.ep_compress(w.ctypes.data_as(C.c_void_p), ep.F32, 4, 4, C.byref(opts), C.byref(out), C.byref(n),
+                         None) == -1
 
 
 def test_concurrent_compress_calls_from_threads():
