@@ -295,7 +295,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_f8(GroupArgs g) {
 // columns of row 16 mt + n as the A operand, loaded before the step's decode so that their latency
 // hides behind it. LDS holds only the decoder's tables and word rings, so the kernel runs 16 waves
 // per CU as the decode kernel does. The accumulators have the layout of the transposing kernel's,
-// so the partials and the finishing sums are the same.
+// so the partials and the finishing sums are the same. (Loading the activations of 2 or 4 steps
+// at once, so that whole 128-byte lines are requested together, measured no faster.)
 typedef long i64_t;
 
 template <int N, int MT, bool F8>
@@ -409,7 +410,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_rows(GroupArgs g) {
     const __amdgpu_buffer_rsrc_t rs = payload_rsrc(M);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(M.gemv_x), 0, (int)((size_t)M.gemv_m * M.cols * (F8 ? 1 : 2)), 0x00020000);
-    for (uint64_t p = p0 + (uint64_t)wave; p < p1; p += kWaves) rows_pair<N, MT, F8>(M, T, t, p, rs, rx);
+    // pairs in column-major order: the 16 waves of a block take the same 512 columns of 16
+    // consecutive tile rows, so their activation loads are the same lines at about the same time
+    // and the L1 serves them once (in row-major order each wave had its own columns, and with four
+    // M tiles their lines no longer fit the L1)
+    const uint32_t tiles_r = (M.rows + 15u) / 16u;
+    for (uint64_t p = p0 + (uint64_t)wave; p < p1; p += kWaves) {
+        const uint32_t pc = (uint32_t)p / tiles_r, tr = (uint32_t)p % tiles_r;
+        rows_pair<N, MT, F8>(M, T, t, (uint64_t)tr * M.pairs_c + pc, rs, rx);
+    }
     if (t.err) atomicOr(M.err, t.err);
 }
 
