@@ -333,7 +333,7 @@ __device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Til
 // Pairs [p0, p1) of one matrix: wave w decodes pairs p0 + w and p0 + w + 16 together, then
 // p0 + w + 32 and p0 + w + 48, ...: two independent chains per lane keep the SIMDs busy while
 // the other chain waits on LDS.
-template <int CT, int N>
+template <int CT, int N, bool ROWS = false>
 __device__ __forceinline__ void lossy_pairs(const MatDesc& M, const Tables& T, Tile* t, uint64_t p0, uint64_t p1) {
     // the wave's index is uniform across its lanes: keep it (and so the pair, tile row and row
     // addresses) in SGPRs
@@ -342,24 +342,18 @@ __device__ __forceinline__ void lossy_pairs(const MatDesc& M, const Tables& T, T
         uint64_t pr[kChains];
 #pragma unroll
         for (int c = 0; c < kChains; ++c) pr[c] = p + (uint64_t)c * kWaves;
-        if constexpr (gemv_rows(CT) == 0) {
-            if (M.layout) {                         // uniform: one layout per matrix
-                lossy_run<CT, N, kChains, true>(M, T, t, pr, p1);
-                continue;
-            }
-        }
-        lossy_run<CT, N, kChains, false>(M, T, t, pr, p1);
+        lossy_run<CT, N, kChains, ROWS>(M, T, t, pr, p1);
     }
 }
 
-template <int N>
+template <int N, bool ROWS>
 __device__ __forceinline__ void lossy_dispatch(const MatDesc& M, const Tables& T, Tile* t, uint64_t p0, uint64_t p1) {
     switch (M.container) {
-        case CT_BF16: lossy_pairs<CT_BF16, N>(M, T, t, p0, p1); break;
-        case CT_F16: lossy_pairs<CT_F16, N>(M, T, t, p0, p1); break;
-        case CT_F8E4M3: lossy_pairs<CT_F8E4M3, N>(M, T, t, p0, p1); break;
-        case CT_I8: lossy_pairs<CT_I8, N>(M, T, t, p0, p1); break;
-        default: lossy_pairs<CT_Q16, N>(M, T, t, p0, p1); break;
+        case CT_BF16: lossy_pairs<CT_BF16, N, ROWS>(M, T, t, p0, p1); break;
+        case CT_F16: lossy_pairs<CT_F16, N, ROWS>(M, T, t, p0, p1); break;
+        case CT_F8E4M3: lossy_pairs<CT_F8E4M3, N, ROWS>(M, T, t, p0, p1); break;
+        case CT_I8: lossy_pairs<CT_I8, N, ROWS>(M, T, t, p0, p1); break;
+        default: lossy_pairs<CT_Q16, N, ROWS>(M, T, t, p0, p1); break;
     }
 }
 
@@ -514,7 +508,9 @@ __device__ __forceinline__ void split_pairs(const MatDesc& M, const Tables& T, T
 // segment at a time and restages the decode tables when it crosses into the next matrix.
 // GEMV = 0: the general grouped decode; GEMV = CT_GEMV1/2/4: the fused matrix-vector product of
 // lossy matrices (a kernel of its own, so that its registers do not weigh on the decode kernel).
-template <int GEMV>
+// ROWS: lossy matrices in the row layout only (a kernel of its own too: sharing one kernel with the
+// layout-0 loop cost that loop 3% on gfx950).
+template <int GEMV, bool ROWS = false>
 __device__ __forceinline__ void group_body(const GroupArgs& g) {
     extern __shared__ __align__(16) uint8_t smem[];
     // the lookups address the LUTs absolutely: the dynamic LDS must start at address 0
@@ -545,12 +541,13 @@ __device__ __forceinline__ void group_body(const GroupArgs& g) {
                 case 11: lossy_pairs<GEMV, 11>(M, T, t, p0, p1); break;
                 default: lossy_pairs<GEMV, 12>(M, T, t, p0, p1); break;
             }
-        } else if (lossy) {
+        } else if (lossy || ROWS) {
             switch (M.prob_bits) {
-                case 10: lossy_dispatch<10>(M, T, t, p0, p1); break;
-                case 11: lossy_dispatch<11>(M, T, t, p0, p1); break;
-                default: lossy_dispatch<12>(M, T, t, p0, p1); break;
+                case 10: lossy_dispatch<10, ROWS>(M, T, t, p0, p1); break;
+                case 11: lossy_dispatch<11, ROWS>(M, T, t, p0, p1); break;
+                default: lossy_dispatch<12, ROWS>(M, T, t, p0, p1); break;
             }
+        } else if constexpr (ROWS) {
         } else if (M.mode == 2) {
             switch (M.prob_bits) {
                 case 10: split_pairs<10>(M, T, t[0], p0, p1); break;
@@ -567,6 +564,8 @@ __device__ __forceinline__ void group_body(const GroupArgs& g) {
 }
 
 __global__ __launch_bounds__(64 * kWaves) void decode_group(GroupArgs g) { group_body<0>(g); }
+
+__global__ __launch_bounds__(64 * kWaves) void decode_group_rows(GroupArgs g) { group_body<0, true>(g); }
 
 template <int CT>
 __global__ __launch_bounds__(64 * kWaves) void decode_gemv(GroupArgs g) { group_body<CT>(g); }
@@ -600,20 +599,23 @@ int device_cus() {
     return v;
 }
 
-hipError_t launch_group(const MatDesc* mats, int count, hipStream_t stream) {
+namespace {
+
+// One launch of `kernel` over the listed matrices, cost-balanced across the CUs.
+hipError_t launch_group_with(void (*kernel)(GroupArgs), const MatDesc* const* mats, int count, hipStream_t stream) {
     if (count <= 0) return hipSuccess;
-    if (count > kMaxGroup) return hipErrorInvalidValue;
     GroupArgs g{};
     g.count = count;
     uint64_t total = 0;
     size_t lds = 0;
     for (int i = 0; i < count; ++i) {
-        g.m[i] = mats[i];
+        const MatDesc& m = *mats[i];
+        g.m[i] = m;
         g.cost_start[i] = total;
-        const uint64_t pairs = (uint64_t)((mats[i].rows + mats[i].tile_rows - 1) / mats[i].tile_rows) * mats[i].pairs_c;
-        total += pairs * mats[i].pair_cost;
+        const uint64_t pairs = (uint64_t)((m.rows + m.tile_rows - 1) / m.tile_rows) * m.pairs_c;
+        total += pairs * m.pair_cost;
         if (pairs)
-            lds = std::max(lds, lds_table_bytes(mats[i].n_tables, mats[i].prob_bits, mats[i].mode == 0) +
+            lds = std::max(lds, lds_table_bytes(m.n_tables, m.prob_bits, m.mode == 0) +
                                     (size_t)kWaves * kChains * 2 * kRingBytes);
     }
     g.cost_start[count] = total;
@@ -621,11 +623,29 @@ hipError_t launch_group(const MatDesc* mats, int count, hipStream_t stream) {
     const uint64_t blocks = (uint64_t)device_cus();
     g.block_cost = (total + blocks - 1) / blocks;
     const uint64_t used = (total + g.block_cost - 1) / g.block_cost;
-    const void* k = reinterpret_cast<const void*>(decode_group);
-    hipError_t e = allow_lds(k);
+    hipError_t e = allow_lds(reinterpret_cast<const void*>(kernel));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_group, dim3((unsigned)used), dim3(64 * kWaves), lds, stream, g);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)used), dim3(64 * kWaves), lds, stream, g);
     return hipGetLastError();
+}
+
+}  // namespace
+
+// Lossy matrices in the row layout go to their own kernel (a second launch when a group mixes
+// layouts).
+hipError_t launch_group(const MatDesc* mats, int count, hipStream_t stream) {
+    if (count <= 0) return hipSuccess;
+    if (count > kMaxGroup) return hipErrorInvalidValue;
+    const MatDesc* plain[kMaxGroup];
+    const MatDesc* rows[kMaxGroup];
+    int np = 0, nr = 0;
+    for (int i = 0; i < count; ++i) {
+        if (mats[i].mode == 0 && mats[i].layout != 0) rows[nr++] = &mats[i];
+        else plain[np++] = &mats[i];
+    }
+    hipError_t e = launch_group_with(decode_group, plain, np, stream);
+    if (e == hipSuccess) e = launch_group_with(decode_group_rows, rows, nr, stream);
+    return e;
 }
 
 hipError_t launch_gemv(const MatDesc& m, hipStream_t stream) {
