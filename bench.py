@@ -12,8 +12,8 @@ Prints one JSON line (rank 0, N = 1): decoded-weight GB/s (container bytes writt
 over K back-to-back steps), the roofline of one 30-matrix decode launch from HIP events on the
 launch stream, the oracle's CPU decode of a bounded sample of the same streams, and extra
 sections: the 4096 x 4096 seven-decode step, the two lossless BF16 codings, the encoders, the
-fused decode + GEMM forward of an 8192 x 8192 weight (M = 4096, 256, 16, 1, BF16 and FP8
-compute) and the 64-matrix mixed-rate set.
+fused decode + GEMM forward of an 8192 x 8192 weight in both tile layouts (M = 4096 ... 1, BF16
+and FP8 compute) and the 64-matrix mixed-rate set.
 
     python bench.py [--steps K] [--warmup W] [--settle S] [--no-cpu] [--no-gemm] [--step-only]
     python bench.py --trace-summary DIR/..._kernel_trace.csv --kernel decode_group --skip N
@@ -474,20 +474,23 @@ def mixed_section(torch, ep, steps: int = 5, reps: int = 5):
     on the GPU (torch's generator seeded with the matrix seed; t5 = z / sqrt(chi2_5 / 5) from six
     normals) and coded by the device encoder, to keep the host out of the run. Timed: the whole set
     decoded to BF16, to FP8 E4M3 (+ row scales) and to INT8 (+ row scales), each as grouped
-    launches of 32; then the compressed BF16 forward of all 64 layers against torch.matmul on the
-    decoded BF16 weights at M = 16, 256 and 4096 (X ~ N(0, 1) bf16, seeded 500 + i)."""
+    launches of 32; then the compressed BF16 forward of all 64 layers (the same weights coded as
+    CompressedLinear.from_linear codes layers: row tile layout, prob_bits 11) against torch.matmul
+    on the decoded BF16 weights at M = 16, 256 and 4096 (X ~ N(0, 1) bf16, seeded 500 + i)."""
     from decode_tile_interleaved_rans_amd import workloads as W
     specs = W.mixed_rate_set()
-    streams, hs, bpps = [], [], []
+    streams, streams_r, hs, bpps = [], [], [], []
     t0 = time.time()
     for R, Cc, tgt, seed, _ in specs:
         w = W.gpu_student_t(R, Cc, seed, 0.02)
         st, bpp = ep.compress_device(w, tgt)
+        # the same weight in the tile layout of compressed layers, for the 64-layer forward
+        streams_r.append(ep.compress_device(w, tgt, prob_bits=ep.LAYER_PROB_BITS, layout=ep.LAYER_LAYOUT)[0])
         del w
         streams.append(st)
         bpps.append(bpp)
         hs.append(ep.upload(st))
-    log(f"mixed set: 64 matrices drawn and coded on the GPU in {time.time() - t0:.1f} s")
+    log(f"mixed set: 64 matrices drawn and coded on the GPU (both layouts) in {time.time() - t0:.1f} s")
     n_w = sum(R * Cc for R, Cc, *_ in specs)
     in_b = sum(len(x) for x in streams)
     out = {"workload": "64 matrices, rows/cols in {2048, 4096, 8192}, targets U[2.5, 6.0], 0.02 t5 bf16, "
@@ -520,7 +523,7 @@ def mixed_section(torch, ep, steps: int = 5, reps: int = 5):
         del scs
         log(f"mixed set to {name}: {ms:.3f} ms")
     out["decode"] = dec
-    layers = [ep.CompressedLinear(st) for st in streams]
+    layers = [ep.CompressedLinear(st) for st in streams_r]   # as CompressedLinear.from_linear codes layers
     fused = {}
     for M in (16, 256, 4096):
         xs = []

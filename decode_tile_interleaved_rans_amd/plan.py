@@ -30,7 +30,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import BF16, F32, LAYER_PROB_BITS, compress, stream_info
+from . import BF16, F32, LAYER_LAYOUT, LAYER_PROB_BITS, compress, stream_info
 
 E8_G = 0.0716821                     # normalized second moment of the E8 lattice
 DEFAULT_GRID = tuple(np.round(np.arange(2.0, 8.0001, 0.25), 4))
@@ -58,13 +58,15 @@ def _weight_array(w):
     return (a, BF16) if a.dtype == np.uint16 else (a.astype(np.float32, copy=False), F32)
 
 
-def layer_candidates(w, grid=DEFAULT_GRID, prob_bits: int = LAYER_PROB_BITS, tile_rows: int = 16, n_threads: int = 0):
-    """Encode one weight at every target of the grid; returns the candidates (real stream sizes
-    and steps) and the streams."""
+def layer_candidates(w, grid=DEFAULT_GRID, prob_bits: int = LAYER_PROB_BITS, tile_rows: int = 16, n_threads: int = 0,
+                     layout: int = LAYER_LAYOUT):
+    """Encode one weight at every target of the grid (the tile layout of compressed layers by
+    default); returns the candidates (real stream sizes and steps) and the streams."""
     arr, code = _weight_array(w)
     out, streams = [], []
     for t in grid:
-        s, bpp = compress(arr, float(t), dtype=code, prob_bits=prob_bits, tile_rows=tile_rows, n_threads=n_threads)
+        s, bpp = compress(arr, float(t), dtype=code, prob_bits=prob_bits, tile_rows=tile_rows, n_threads=n_threads,
+                          layout=layout)
         step = stream_info(s)["step"]
         out.append(Candidate(float(t), float(bpp), float(step), E8_G * float(step) ** 2, len(s)))
         streams.append(s)

@@ -26,7 +26,7 @@ def test_error_model_matches_oracle_decode(target):
     w = gauss(256, 1024, 1)
     cands, streams = P.layer_candidates(w, grid=(target,))
     c, s = cands[0], streams[0]
-    assert s == oracle.compress(w, target, prob_bits=ep.LAYER_PROB_BITS)[0]
+    assert s == oracle.compress(w, target, prob_bits=ep.LAYER_PROB_BITS, layout=ep.LAYER_LAYOUT)[0]
     q, _ = oracle.decode_symbols(s)
     d = oracle.info(s)
     scale = np.sqrt((w.astype(np.float64) ** 2).mean(1))
