@@ -10,6 +10,9 @@
  * 2. The same matrix is coded lossy at 4.0 bpp and decoded to BF16 on the GPU; the stream and
  *    the decoded bits are written to <dir>/lossy.epk and <dir>/lossy_bf16.bin for the test to
  *    compare with the oracle.
+ * 3. The same again in the row tile layout (ep_encode_opts.layout = 1): <dir>/rows.epk and
+ *    <dir>/rows_bf16.bin; the program checks that the stream reports the layout and that both
+ *    layouts decode to the same BF16 bits.
  * Exit status 0 on success; a message on stderr otherwise. */
 #include <stdint.h>
 #include <stdio.h>
@@ -120,6 +123,32 @@ int main(int argc, char** argv) {
     }
     ep_free(s);
     printf("lossy 4.0 bpp target, %.4f bpp actual, decoded to BF16\n", bpp);
+
+    /* 3. the row tile layout: the same weights, decoded by the row-layout kernel */
+    ep_encode_opts rows = {EP_MODE_LOSSY_E8, 4.0, 12, 16, 0, 1};
+    st = ep_compress(w, EP_F32, R, C, &rows, &s, &len, &bpp);
+    if (st != EP_OK) return fail_ep("ep_compress (row layout)", st);
+    st = ep_stream_info(s, len, &info);
+    if (st != EP_OK) return fail_ep("ep_stream_info (row layout)", st);
+    if (info.layout != 1) {
+        fprintf(stderr, "the row-layout stream reports layout %d\n", (int)info.layout);
+        return 1;
+    }
+    uint16_t* bf_rows = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(R * C));
+    if (!bf_rows) return 1;
+    if (gpu_decode(s, len, EP_BF16, bf_rows, sizeof(uint16_t) * (size_t)(R * C))) return 1;
+    if (memcmp(bf_rows, bf, sizeof(uint16_t) * (size_t)(R * C)) != 0) {
+        fprintf(stderr, "the two tile layouts decode to different weights\n");
+        return 1;
+    }
+    if (write_file(argv[1], "rows.epk", s, len) ||
+        write_file(argv[1], "rows_bf16.bin", bf_rows, sizeof(uint16_t) * (size_t)(R * C))) {
+        fprintf(stderr, "writing the outputs failed\n");
+        return 1;
+    }
+    ep_free(s);
+    free(bf_rows);
+    printf("row layout: %.4f bpp actual, the same BF16 weights\n", bpp);
     free(w);
     free(back);
     free(bf);

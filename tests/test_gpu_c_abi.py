@@ -1,7 +1,8 @@
 """The C ABI driven by a plain C program (tests/c_abi_roundtrip.c, compiled by
 __graft_entry__.build() with gcc against include/entropack.h and the HIP runtime): no Python and
-no PyTorch on the path. The program checks a lossless FP32 round trip itself; its lossy BF16
-decode is compared here with the oracle, bit for bit."""
+no PyTorch on the path. The program checks a lossless FP32 round trip itself, and that the row
+tile layout decodes to the same weights as layout 0; both lossy BF16 decodes are compared here
+with the oracle, bit for bit."""
 import os
 import subprocess
 
@@ -25,3 +26,8 @@ def test_c_program_round_trip(tmp_path):
     got = np.fromfile(tmp_path / "lossy_bf16.bin", dtype=np.uint16).reshape(300, 700)
     want, _ = oracle.decompress(stream, oracle.BF16)
     assert np.array_equal(got, want)
+    rows = (tmp_path / "rows.epk").read_bytes()
+    assert oracle.info(rows)["layout"] == 1
+    got_rows = np.fromfile(tmp_path / "rows_bf16.bin", dtype=np.uint16).reshape(300, 700)
+    want_rows, _ = oracle.decompress(rows, oracle.BF16)
+    assert np.array_equal(got_rows, want_rows) and np.array_equal(want_rows, want)

@@ -1,8 +1,10 @@
 """The no-allocation linear forward (ep_linear_forward_noalloc, for callers that cannot allocate
 device memory) against the pool-workspace forward (ep_linear_forward), both called through the C
-ABI, on two calls in a row with the second smaller than the first, on every forward path (fused
-matrix-vector products for M <= 4, the fused decode + MFMA kernel for 5 <= M <= 16, decode slices
-+ GEMM above). Collected last: it runs after every other GPU test and also alone."""
+ABI, on two calls in a row with the second smaller than the first, on every forward path: for a
+layout-0 stream the fused matrix-vector products (M <= 4), the transposing fused decode + MFMA
+kernel (5 <= M <= 16) and decode slices + GEMM above; for a row-layout stream the register-direct
+fused kernel (M <= 64, one to four M tiles) and the slices above. Collected last: it runs after
+every other GPU test and also alone."""
 import ctypes as C
 
 import numpy as np
@@ -37,10 +39,11 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
 
 
+@pytest.mark.parametrize("layout", [0, ep.ROW_LAYOUT])
 @pytest.mark.parametrize("Ms", [(96, 40), (4, 1), (300, 3)])
-def test_noalloc_forward_matches_pool_forward(Ms):
+def test_noalloc_forward_matches_pool_forward(Ms, layout):
     w = W.student_t(2048, 3072, seed=71)
-    s, _ = ep.compress(w, 4.0, dtype=ep.BF16)
+    s, _ = ep.compress(w, 4.0, dtype=ep.BF16, layout=layout)
     h = ep.upload(s)
     want, _ = oracle.decompress(s, oracle.BF16)
     w_hat = W.bf16_bits_to_f32(want).astype(np.float64)
@@ -57,7 +60,7 @@ def test_noalloc_forward_matches_pool_forward(Ms):
         a = y_fixed.float().cpu().numpy()
         b = y_pool.float().cpu().numpy()
         assert np.isfinite(a).all()
-        if M > 4:
+        if M > 4 or layout != 0:
             assert torch.equal(y_fixed, y_pool), M        # same kernels, deterministic order
         else:
             assert rel_l2(a, b) < 1e-3, M                 # fp32 atomics: summation order varies
