@@ -332,9 +332,16 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
         return e == hipSuccess ? EP_OK : hip_fail(e, "fused decode + MFMA launch");
     }
     const int tr = w->view.tile_rows;
+    // From kLtMinRows activation rows the slices are multiplied by hipBLASLt, whose tuned kernels
+    // beat the own 256 x 256 one at prefill sizes (4096 x 8192 x 8192: 363 against 441 us); below,
+    // the own kernel (split-K when its tiles cannot fill the CUs) is the faster one. Not in the
+    // no-allocation variant: the library's handle allocates on first use.
+    constexpr int64_t kLtMinRows = 1024;
+    constexpr size_t kLtWorkspace = 32u << 20;
+    const bool lt = !fixed && M >= kLtMinRows;
     // K splits of the GEMM, chosen for the whole layer so that every slice adds its partial sums in
     // the same order; the split partial tiles of a slice follow its decoded rows in the scratch
-    const int splits = ep::gemm_splits((int)M, (int)N, (int)K);
+    const int splits = lt ? 1 : ep::gemm_splits((int)M, (int)N, (int)K);
     const size_t part_per_row = splits > 1 ? (size_t)splits * (size_t)M * sizeof(float) : 0;
     int64_t slice = (int64_t)(fixed ? ep::kStaticScratchBytes / (2 * (size_t)K + part_per_row)
                                     : kSliceBytes / (2 * (size_t)K)) / tr * tr;
@@ -344,7 +351,8 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
     }
     if (slice > N) slice = (N + tr - 1) / tr * tr;
     const size_t slice_bytes = up((size_t)slice * (size_t)K * 2, 256);
-    const size_t need = slice_bytes + (size_t)slice * part_per_row;
+    const size_t o_lt = up(slice_bytes + (size_t)slice * part_per_row, 256);
+    const size_t need = o_lt + (lt ? kLtWorkspace : 0);
     if (fixed) {
         if (ep_status st = take_static(need, &ws); st != EP_OK) return st;
     } else if ((he = ws_acquire(dev, s, need, &ws)) != hipSuccess) {
@@ -367,7 +375,8 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
         g.splits = splits;
         g.part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws.ptr) + slice_bytes);
         g.part_bytes = (size_t)slice * part_per_row;
-        e = ep::launch_gemm(g, s);
+        e = lt ? ep::lt_gemm(g, reinterpret_cast<uint8_t*>(ws.ptr) + o_lt, kLtWorkspace, s) : hipErrorNotSupported;
+        if (e == hipErrorNotSupported) e = ep::launch_gemm(g, s);
         if (e != hipSuccess) return hip_fail(e, "slice gemm launch");
     }
     he = ws.queued();

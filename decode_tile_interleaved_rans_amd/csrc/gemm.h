@@ -31,6 +31,12 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
 int gemm_splits(int M, int N, int K);
 int split_columns(int K, int splits);
 
+// The same product (splits ignored) through hipBLASLt with up to ws_bytes of device workspace at
+// `workspace`: hipErrorNotSupported when the library offers no algorithm for the shape (the caller
+// then runs launch_gemm). Plans are cached per device and shape; calls from several threads are
+// serialized while they are queued. (gemm_lt.cpp)
+hipError_t lt_gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t stream);
+
 // FP8 GEMM: Y[m][n] = sx[m] * sw[n] * sum_k X[m][k] W[n][k] (+ bias[n]), X and W OCP E4M3 codes,
 // fp32 accumulation, BF16 output.
 struct GemmF8Args {

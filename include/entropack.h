@@ -209,7 +209,9 @@ ep_status ep_decode_symbols(const ep_handle* h, int16_t* dev_q, void* hip_stream
  *     differ in the last bits);
  *   - otherwise the weight is decoded once per call, up to 128 MiB of BF16 rows at a time, into
  *     the workspace, which stays in the Infinity Cache, and each slice is multiplied by the BF16
- *     MFMA GEMM (deterministic); no decoded copy of W outlives the call.
+ *     MFMA GEMM: the library's own kernel below 1024 rows, hipBLASLt's from 1024 rows (faster at
+ *     prefill sizes; its handle is created on the device's first such call); both deterministic
+ *     (tested); no decoded copy of W outlives the call.
  * The fused and slice paths multiply the same BF16-rounded weights. The workspace belongs
  * to the (device, hip_stream) pair: calls on one stream reuse it in order, calls on different
  * streams get different workspaces; it is allocated on first use
@@ -225,7 +227,9 @@ ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, co
  * allocating library routine; the array lives from library load until the process ends. Same
  * arguments, results and paths as ep_linear_forward (the same kernels: the fused kernel's partial
  * sums, the fp32 accumulator of M <= 4 on layout-0 streams, otherwise BF16 weight slices of at
- * most 64 MiB, i.e. 64 MiB / (2 K) rows). EP_ERANGE when a call needs more than the array holds
+ * most 64 MiB, i.e. 64 MiB / (2 K) rows, always multiplied by the library's own GEMM kernel, so
+ * results at 1024 rows and more may differ from ep_linear_forward's in the fp32 summation
+ * order). EP_ERANGE when a call needs more than the array holds
  * (M <= 4 with 4 M N > 64 MiB, the fused partials of very wide layers, or K > 2^21 for the slices).
  * Every call on a device shares that device's array: calls that overlap in time on one device
  * (other streams, other threads) race and must be serialized by the caller.

@@ -105,8 +105,10 @@ def test_linear_forward_prefill_sampled_rows():
     layer = ep.CompressedLinear(s)
     X = bf16_tensor(xb).cuda()
     y = layer(X)
+    y2 = layer(X)                                   # the GEMM library's kernel: the same bits again
     torch.cuda.synchronize()
     layer.handle.check()
+    assert torch.equal(y, y2)
     w_hat = W.bf16_bits_to_f32(oracle.decompress(s, oracle.BF16, n_threads=16)[0])
     rows = np.random.default_rng(4).choice(M, 32, replace=False)
     ref = W.bf16_bits_to_f32(xb[rows]) @ w_hat.T
@@ -118,6 +120,34 @@ def test_linear_forward_prefill_sampled_rows():
         torch.cuda.synchronize()
         refm = W.bf16_bits_to_f32(xb[:m]) @ w_hat.T
         assert rel_l2(ym.float().cpu().numpy(), refm) < 2e-2, m
+
+
+@pytest.mark.parametrize("layout", [0, ep.ROW_LAYOUT])
+def test_prefill_forward_through_the_gemm_library(layout):
+    """From 1024 activation rows the decoded slices are multiplied by hipBLASLt: a ragged N with a
+    bias (its bias epilogue) and two slices of a wide K, sampled rows within 2e-2 of the fp32
+    product of the oracle's weights, the same bits on a second call, and agreement with the own
+    GEMM on the same decoded weight within the fp32 summation order."""
+    M, N, K = 1024, 1000, 69632                     # 128 MiB slices of 960 rows: 960 + 40
+    w = W.student_t(N, K, seed=12)
+    s, _ = ep.compress(w, 4.0, dtype=ep.BF16, layout=layout)
+    bias_bits = W.activations(1, N, 13)[0]
+    layer = ep.CompressedLinear(s, bf16_tensor(bias_bits).cuda())
+    xb = W.activations(M, K, 14)
+    X = bf16_tensor(xb).cuda()
+    y = layer(X)
+    y2 = layer(X)
+    wd = layer.handle.decompress(torch.bfloat16)
+    yo = ep.gemm_bf16(X, wd)
+    torch.cuda.synchronize()
+    layer.handle.check()
+    assert torch.equal(y, y2)
+    b = W.bf16_bits_to_f32(bias_bits).astype(np.float64)
+    assert rel_l2(y.float().cpu().numpy(), yo.float().cpu().numpy() + b[None, :]) < 3e-3
+    w_hat = W.bf16_bits_to_f32(oracle.decompress(s, oracle.BF16, n_threads=16)[0]).astype(np.float64)
+    rows = np.random.default_rng(15).choice(M, 24, replace=False)
+    ref = W.bf16_bits_to_f32(xb[rows]).astype(np.float64) @ w_hat.T + b[None, :]
+    assert rel_l2(y[rows].float().cpu().numpy(), ref) < 2e-2
 
 
 def test_c5_linear_forward_token_counts():
