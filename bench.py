@@ -246,6 +246,70 @@ def fused_gemm_section(torch, ep, reps: int = 15):
     return out
 
 
+def dit_forward_section(torch, ep, tokens=(4096, 16), reps: int = 3):
+    """The DiT-like model's 150 linear layers as compressed layers (coded as
+    CompressedLinear.from_linear codes layers: row tile layout, prob_bits 11, 4.0 bpp target; the
+    same GPU-drawn weights as the headline step), their forwards in model order at M tokens
+    against torch.matmul on the same weights decoded to BF16 (X ~ N(0, 1) bf16 per input width,
+    seed 600). The linear-layer part of one denoising step: the pages time the whole step of their
+    image model with compressed against uncompressed weights; attention and the other layers of
+    that step are outside the method and not modeled here."""
+    from decode_tile_interleaved_rans_amd import workloads as W
+    t0 = time.time()
+    layers, ws = [], []
+    for b in range(W.DIT_BLOCKS):
+        for m, (R, Cc) in enumerate(W.DIT_BLOCK_SHAPES):
+            w = W.gpu_student_t(R, Cc, 3000 + 5 * b + m, 0.02)
+            st, _ = ep.compress_device(w, 4.0, prob_bits=ep.LAYER_PROB_BITS, layout=ep.LAYER_LAYOUT)
+            del w
+            lay = ep.CompressedLinear(st)
+            layers.append(lay)
+            ws.append(lay.handle.decompress(torch.bfloat16))
+    torch.cuda.synchronize()
+    for lay in layers:
+        lay.handle.check()
+    log(f"DiT-like forward: 150 layers coded and decoded in {time.time() - t0:.1f} s")
+    weights = sum(w.numel() for w in ws)
+    stream_bytes = sum(len(lay.stream) for lay in layers)
+    out = {"workload": "the DiT-like model's 150 linear layers (5.31 G weights, 4.0 bpp target, row tile layout, "
+                       "prob_bits 11) in model order, Y = X W^T bf16, against torch.matmul on the decoded BF16 weights",
+           "actual_bpp": round(8 * stream_bytes / weights, 4), "reps": reps}
+    for M in tokens:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(600)
+        xs = {c: torch.randn((M, c), generator=g, device="cuda").to(torch.bfloat16)
+              for c in sorted({Cc for _, Cc in W.DIT_BLOCK_SHAPES})}
+        xin = [xs[w.shape[1]] for w in ws]
+        for lay, x in zip(layers, xin):
+            lay(x)
+        for x, w in zip(xin, ws):
+            torch.matmul(x, w.T)
+        torch.cuda.synchronize()
+        tf, tt = [], []
+        for _ in range(reps):
+            a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            a.record()
+            for lay, x in zip(layers, xin):
+                lay(x)
+            b.record()
+            for x, w in zip(xin, ws):
+                torch.matmul(x, w.T)
+            c.record()
+            torch.cuda.synchronize()
+            tf.append(a.elapsed_time(b))
+            tt.append(b.elapsed_time(c))
+        for lay in layers:
+            lay.handle.check()
+        f, t = float(np.median(tf)), float(np.median(tt))
+        out[f"M{M}"] = {"compressed_ms": round(f, 3), "torch_matmul_ms": round(t, 3), "overhead_vs_torch": round(f / t - 1, 4),
+                        "tflops_compressed": round(2.0 * M * weights / f / 1e9, 1)}
+        log(f"DiT-like forward M={M}: compressed {f:.2f} ms, torch.matmul {t:.2f} ms")
+        del xs, xin
+    del layers, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def lossless_section(torch, ep, reps: int = 10):
     """The two lossless BF16 codings of the 4096 x 4096 matrix side by side, outside the step:
     byte-plane tile rANS (the step's lossless decode) and the exponent-coded variant (exponent
@@ -582,6 +646,8 @@ def main():
     ap.add_argument("--mixed-only", action="store_true",
                     help="profiling aid: run only the 64-matrix mixed-rate set and print its JSON")
     ap.add_argument("--no-mixed", action="store_true", help="skip the 64-matrix mixed-rate set")
+    ap.add_argument("--dit-forward-only", action="store_true",
+                    help="profiling aid: run only the DiT-like model's compressed linear forward and print its JSON")
     ap.add_argument("--step-only", action="store_true",
                     help="profiling aid: time only the headline step (no other sections, no CPU baseline)")
     ap.add_argument("--trace-summary", metavar="CSV",
@@ -629,9 +695,12 @@ def main():
     if args.mixed_only:
         print(json.dumps(mixed_section(torch, ep)), flush=True)
         return
+    if args.dit_forward_only:
+        print(json.dumps(dit_forward_section(torch, ep)), flush=True)
+        return
     head, sample = dit_step(torch, ep, args.steps, args.warmup, cpu_blocks=0 if args.no_cpu or args.step_only else 10,
                             settle=args.settle)
-    c2 = lossless = encoders = fused = mixed = cpu = None
+    c2 = lossless = encoders = fused = mixed = ditf = cpu = None
     if not args.step_only:
         c2 = c2_step_section(torch, ep)
         lossless = lossless_section(torch, ep)
@@ -640,6 +709,8 @@ def main():
             fused = fused_gemm_section(torch, ep, reps=args.gemm_reps)
         if not args.no_mixed:
             mixed = mixed_section(torch, ep)
+        if not args.no_gemm:
+            ditf = dit_forward_section(torch, ep)
         if not args.no_cpu:
             log("timing the oracle on the host cores")
             cpu = cpu_baseline(sample)
@@ -661,6 +732,7 @@ def main():
         "encoders": encoders,
         "fused_gemm": fused,
         "mixed_rate_set": mixed,
+        "dit_forward": ditf,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

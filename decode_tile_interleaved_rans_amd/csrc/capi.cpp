@@ -707,9 +707,15 @@ ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M
         int64_t slice = (int64_t)(kSliceBytes / (size_t)K) / tr * tr;
         if (slice < tr) slice = tr;
         if (slice > N) slice = (N + tr - 1) / tr * tr;
+        // from kLtMinRows rows the slices are multiplied by hipBLASLt (as in the BF16 forward)
+        constexpr int64_t kLtMinRows = 1024;
+        constexpr size_t kLtWorkspace = 32u << 20;
+        const bool lt = M >= kLtMinRows;
         // workspace: X codes [M][K] | X scales [M] | weight codes [slice][K] | weight scales [slice]
+        // | hipBLASLt workspace
         const size_t o_xs = up((size_t)M * (size_t)K, 256), o_wq = up(o_xs + 4 * (size_t)M, 256);
-        const size_t o_ws = up(o_wq + (size_t)slice * (size_t)K, 256), need = o_ws + 4 * (size_t)slice;
+        const size_t o_ws = up(o_wq + (size_t)slice * (size_t)K, 256), o_lt = up(o_ws + 4 * (size_t)slice, 256);
+        const size_t need = o_lt + (lt ? kLtWorkspace : 0);
         WsLease ws;
         we = ws_acquire(dev, s, need, &ws);
         if (we != hipSuccess) return hip_fail(we, "hipMalloc for the linear forward workspace");
@@ -733,7 +739,8 @@ ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M
             if (e != hipSuccess) return hip_fail(e, "slice decode launch");
             ep::GemmF8Args g{xq, xs, wq, wsc, dev_bias ? static_cast<const uint16_t*>(dev_bias) + r0 : nullptr,
                              static_cast<uint16_t*>(dev_y) + r0, (int)M, (int)rows, (int)K, (int)K, (int)K, (int)N};
-            e = ep::launch_gemm_f8(g, s);
+            e = lt ? ep::lt_gemm_f8(g, ws8 + o_lt, kLtWorkspace, s) : hipErrorNotSupported;
+            if (e == hipErrorNotSupported) e = ep::launch_gemm_f8(g, s);
             if (e != hipSuccess) return hip_fail(e, "slice fp8 gemm launch");
         }
         e = ws.queued();

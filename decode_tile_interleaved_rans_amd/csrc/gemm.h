@@ -31,12 +31,6 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
 int gemm_splits(int M, int N, int K);
 int split_columns(int K, int splits);
 
-// The same product (splits ignored) through hipBLASLt with up to ws_bytes of device workspace at
-// `workspace`: hipErrorNotSupported when the library offers no algorithm for the shape (the caller
-// then runs launch_gemm). Plans are cached per device and shape; calls from several threads are
-// serialized while they are queued. (gemm_lt.cpp)
-hipError_t lt_gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t stream);
-
 // FP8 GEMM: Y[m][n] = sx[m] * sw[n] * sum_k X[m][k] W[n][k] (+ bias[n]), X and W OCP E4M3 codes,
 // fp32 accumulation, BF16 output.
 struct GemmF8Args {
@@ -51,6 +45,15 @@ struct GemmF8Args {
 
 // Requires K % 16 == 0 and 16-byte aligned rows (ldx, ldw multiples of 16, aligned bases).
 hipError_t launch_gemm_f8(const GemmF8Args& g, hipStream_t stream);
+
+// The product of launch_gemm (splits ignored) through hipBLASLt with up to ws_bytes of device
+// workspace at `workspace`: hipErrorNotSupported when the library offers no algorithm for the shape
+// (the caller then runs launch_gemm). Plans are cached per device and shape; calls from several threads are
+// serialized while they are queued. (gemm_lt.cpp)
+hipError_t lt_gemm(const GemmArgs& g, void* workspace, size_t ws_bytes, hipStream_t stream);
+// The FP8 product of launch_gemm_f8 through hipBLASLt (E4M3 operands, the row scales as outer-vector
+// scales), same contract.
+hipError_t lt_gemm_f8(const GemmF8Args& g, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 // Per-row E4M3 quantization of BF16 rows: amax = max |x| (raised to 2^-100 when smaller and not
 // zero), s = amax / 448, q = E4M3(x * (448 / amax)); a zero row gets s = 0 and codes 0.

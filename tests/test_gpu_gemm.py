@@ -306,12 +306,37 @@ def test_linear_forward_fp8_prefill_sampled_rows():
     s, _ = ep.compress(w, 4.5, dtype=ep.BF16)
     layer = ep.CompressedLinear(s, compute="fp8")
     y = layer(bf16_tensor(xb).cuda())
+    y2 = layer(bf16_tensor(xb).cuda())              # the GEMM library's kernel: the same bits again
     torch.cuda.synchronize()
     layer.handle.check()
+    assert torch.equal(y, y2)
     rows = np.random.default_rng(6).choice(M, 32, replace=False)
     wq, ws = oracle.decompress(s, oracle.F8E4M3, n_threads=16)
     xq, xs = oracle.quantize_rows_e4m3(xb[rows])
     assert rel_l2(y[rows].float().cpu().numpy(), fp8_reference(xq, xs, wq, ws)) < 3e-3
+
+
+def test_fp8_prefill_with_bias_over_two_slices():
+    """The FP8 forward from 1024 rows (slices multiplied by hipBLASLt with the row scales as
+    outer-vector scales): a ragged N with a bias over two slices, against the fp64 product of the
+    oracle's codes and scales, repeatable bits."""
+    M, N, K = 1024, 1000, 139264                    # 128 MiB FP8 slices of 960 rows: 960 + 40
+    w = W.student_t(N, K, seed=16)
+    s, _ = ep.compress(w, 4.0, dtype=ep.BF16)
+    bias_bits = W.activations(1, N, 17)[0]
+    layer = ep.CompressedLinear(s, bf16_tensor(bias_bits).cuda(), compute="fp8")
+    xb = W.activations(M, K, 18)
+    X = bf16_tensor(xb).cuda()
+    y = layer(X)
+    y2 = layer(X)
+    torch.cuda.synchronize()
+    layer.handle.check()
+    assert torch.equal(y, y2)
+    rows = np.random.default_rng(19).choice(M, 16, replace=False)
+    wq, ws = oracle.decompress(s, oracle.F8E4M3, n_threads=16)
+    xq, xs = oracle.quantize_rows_e4m3(xb[rows])
+    ref = fp8_reference(xq, xs, wq, ws, W.bf16_bits_to_f32(bias_bits).astype(np.float64))
+    assert rel_l2(y[rows].float().cpu().numpy(), ref) < 3e-3
 
 
 def test_binding_refuses_mismatched_tensors():
