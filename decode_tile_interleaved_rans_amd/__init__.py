@@ -465,7 +465,8 @@ class CompressedLinear:
         if other:
             s.wait_stream(cur)
         with torch.cuda.stream(s):
-            x2 = x.reshape(-1, shp[-1]).to(torch.bfloat16).contiguous()
+            rows = int(np.prod(shp[:-1], dtype=np.int64))
+            x2 = x.reshape(rows, shp[-1]).to(torch.bfloat16).contiguous()
             y = torch.empty((x2.shape[0], self.out_features), dtype=torch.bfloat16, device=x.device)
             bp = C.c_void_p(self.bias.data_ptr()) if self.bias is not None else None
             fn = lib().ep_linear_forward_fp8 if self.compute == "fp8" else lib().ep_linear_forward

@@ -289,16 +289,17 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
     const int64_t N = w->view.rows, K = w->view.cols;
     if (M < 0) return fail(EP_EINVAL, "negative M");
     if (M == 0 || N == 0) return EP_OK;
-    if (!dev_x || !dev_y) return fail(EP_EINVAL, "null pointer");
+    if (!dev_y || (K > 0 && !dev_x)) return fail(EP_EINVAL, "null pointer");
     if (K % 8 || M > INT32_MAX) return fail(EP_EINVAL, "in_features must be a multiple of 8");
     if (reinterpret_cast<uintptr_t>(dev_x) & 15) return fail(EP_EINVAL, "X must be 16-byte aligned");
     int dev = 0;
     hipError_t he = hipGetDevice(&dev);
     if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
     WsLease ws;
-    if (M <= 4 && w->view.layout == 0) {
+    if (K == 0 || (M <= 4 && w->view.layout == 0)) {
         // a few activation rows: decoding fused with the matrix-vector products, the weight never
-        // written out; fp32 accumulation in the scratch, then rounding (+ bias) to BF16
+        // written out; fp32 accumulation in the scratch, then rounding (+ bias) to BF16 (also the
+        // empty product of in_features 0)
         const size_t need = sizeof(float) * (size_t)M * (size_t)N;
         if (fixed) {
             if (ep_status st = take_static(need, &ws); st != EP_OK) return st;
@@ -310,7 +311,8 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
         d.gemv_x = static_cast<const uint16_t*>(dev_x);
         d.gemv_m = (uint8_t)M;
         hipError_t e = ep::launch_gemv_zero(yacc, M * N, s);
-        if (e == hipSuccess) e = ep::launch_gemv(d, s);
+        // in_features 0: an empty sum, Y = bias (or zeros)
+        if (e == hipSuccess && K > 0) e = ep::launch_gemv(d, s);
         if (e == hipSuccess)
             e = ep::launch_gemv_finish(yacc, static_cast<const uint16_t*>(dev_bias), static_cast<uint16_t*>(dev_y), M, N, s);
         if (e == hipSuccess) e = ws.queued();
@@ -676,13 +678,25 @@ ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M
         const int64_t N = w->view.rows, K = w->view.cols;
         if (M < 0) return fail(EP_EINVAL, "negative M");
         if (M == 0 || N == 0) return EP_OK;
-        if (!dev_x || !dev_y) return fail(EP_EINVAL, "null pointer");
+        if (!dev_y || (K > 0 && !dev_x)) return fail(EP_EINVAL, "null pointer");
         if (K % 16 || M > INT32_MAX) return fail(EP_EINVAL, "in_features must be a multiple of 16 for the FP8 forward");
         if (reinterpret_cast<uintptr_t>(dev_x) & 15) return fail(EP_EINVAL, "X must be 16-byte aligned");
         hipStream_t s = static_cast<hipStream_t>(hip_stream);
         int dev = 0;
         hipError_t we = hipGetDevice(&dev);
         if (we != hipSuccess) return hip_fail(we, "hipGetDevice");
+        if (K == 0) {
+            // in_features 0: an empty sum, Y = bias (or zeros)
+            WsLease ws;
+            if ((we = ws_acquire(dev, s, sizeof(float) * (size_t)M * (size_t)N, &ws)) != hipSuccess)
+                return hip_fail(we, "hipMalloc for the linear forward workspace");
+            float* yacc = static_cast<float*>(ws.ptr);
+            hipError_t e = ep::launch_gemv_zero(yacc, M * N, s);
+            if (e == hipSuccess)
+                e = ep::launch_gemv_finish(yacc, static_cast<const uint16_t*>(dev_bias), static_cast<uint16_t*>(dev_y), M, N, s);
+            if (e == hipSuccess) e = ws.queued();
+            return e == hipSuccess ? EP_OK : hip_fail(e, "empty product launch");
+        }
         if (const ep::MatDesc d = desc_for(w, ep::CT_F8E4M3, nullptr, nullptr); ep::fused_fits(d, M)) {
             // up to 16 activation rows (64 in the row layout): the activations quantized per row,
             // then every tile pair decoded straight into E4M3 codes as the B operand of the FP8

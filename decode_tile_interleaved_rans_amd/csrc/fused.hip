@@ -422,6 +422,22 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_rows(GroupArgs g) {
     if (t.err) atomicOr(M.err, t.err);
 }
 
+// 0 + p[0] + p[1] + ... + p[n - 1] (stride MT x 256) in that order, with eight loads in flight at
+// a time (a loop of dependent additions would wait for each load in turn).
+template <int MT>
+__device__ __forceinline__ float sum_partials(const float* p, int n) {
+    float v = 0.0f;
+    for (int pc0 = 0; pc0 < n; pc0 += 8) {
+        float t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[j] = pc0 + j < n ? p[(uint64_t)(pc0 + j) * (MT * 256)] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (pc0 + j < n) v += t[j];
+    }
+    return v;
+}
+
 // Y [M][N] bf16 = (sum over the tile row's pairs of the partials) x s_x[m] x s_w[n] (+ bias).
 template <int MT>
 __global__ __launch_bounds__(256) void fused_finish_f8(const float* part, const float* sx, const float* sw,
@@ -433,8 +449,7 @@ __global__ __launch_bounds__(256) void fused_finish_f8(const float* part, const 
     const int tr = col >> 4, n = col & 15;
     const int mt = m >> 4, qg = (m >> 2) & 3, i = m & 3;
     const float* p = part + (uint64_t)tr * pairs_c * (MT * 256) + ((mt * 4 + qg) * 16 + n) * 4 + i;
-    float v = 0.0f;
-    for (int pc = 0; pc < pairs_c; ++pc) v += p[(uint64_t)pc * (MT * 256)];
+    float v = sum_partials<MT>(p, pairs_c);
     v = v * sw[col] * sx[m];
     if (bias) v += __uint_as_float((uint32_t)bias[col] << 16);
     y[e] = (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v, 0.0f}, bf16x2)) & 0xFFFFu);
@@ -450,8 +465,7 @@ __global__ __launch_bounds__(256) void fused_finish(const float* part, const uin
     const int tr = col >> 4, n = col & 15;
     const int mt = m >> 4, qg = (m >> 2) & 3, i = m & 3;
     const float* p = part + (uint64_t)tr * pairs_c * (MT * 256) + ((mt * 4 + qg) * 16 + n) * 4 + i;
-    float v = 0.0f;
-    for (int pc = 0; pc < pairs_c; ++pc) v += p[(uint64_t)pc * (MT * 256)];
+    float v = sum_partials<MT>(p, pairs_c);
     if (bias) v += __uint_as_float((uint32_t)bias[col] << 16);
     y[e] = (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v, 0.0f}, bf16x2)) & 0xFFFFu);
 }

@@ -216,8 +216,9 @@ ep_status ep_decode_symbols(const ep_handle* h, int16_t* dev_q, void* hip_stream
  * to the (device, hip_stream) pair: calls on one stream reuse it in order, calls on different
  * streams get different workspaces; it is allocated on first use
  * (hipMalloc, which may synchronize the device) and kept until the process ends.
- *   dev_x: [M][K] bf16, 16-byte aligned; dev_bias: [N] bf16 or NULL; dev_y: [M][N] bf16.
- * Requires a lossy stream and K % 8 == 0. Asynchronous on hip_stream. */
+ *   dev_x: [M][K] bf16, 16-byte aligned (may be NULL when K == 0); dev_bias: [N] bf16 or NULL;
+ * dev_y: [M][N] bf16. K == 0 gives Y = bias (or zeros). Requires a lossy stream and K % 8 == 0.
+ * Asynchronous on hip_stream. */
 ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias,
                             void* dev_y, void* hip_stream);
 
@@ -258,8 +259,8 @@ ep_status ep_gemm_bf16(const void* dev_x, const void* dev_w, int64_t M, int64_t 
  * M <= 16 on layout-0 streams the codes go straight into the MFMA's B operand (fused, as in
  * ep_linear_forward); otherwise the weight is decoded slice by slice into the workspace and
  * multiplied by the FP8 GEMM. Same workspace rules as ep_linear_forward. dev_x: [M][K] bf16, 16-byte aligned,
- * finite; dev_bias: [N] bf16 or NULL; dev_y: [M][N] bf16. Requires a lossy stream and
- * K % 16 == 0. Asynchronous on hip_stream. */
+ * finite (may be NULL when K == 0); dev_bias: [N] bf16 or NULL; dev_y: [M][N] bf16. K == 0 gives
+ * Y = bias (or zeros). Requires a lossy stream and K % 16 == 0. Asynchronous on hip_stream. */
 ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias,
                                 void* dev_y, void* hip_stream);
 

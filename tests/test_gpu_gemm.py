@@ -443,3 +443,52 @@ def test_split_k_gemm_is_deterministic_and_exact_to_fp32(M, N, K):
     assert torch.equal(y1, y2)
     ref = W.bf16_bits_to_f32(x) @ W.bf16_bits_to_f32(w).T
     assert rel_l2(y1.float().cpu().numpy(), ref) < 5e-3
+
+
+@pytest.mark.parametrize("compute", ["bf16", "fp8"])
+@pytest.mark.parametrize("layout", [0, ep.ROW_LAYOUT])
+def test_forward_with_no_input_features(layout, compute):
+    """in_features 0: every product is an empty sum, so Y = bias (or zeros) on every path (the
+    matrix-vector, fused and slice paths all take M here), and X may have no storage."""
+    s, _ = ep.compress(np.zeros((40, 0), np.float32), 4.0, layout=layout)
+    bias_bits = W.activations(1, 40, 7)[0]
+    for bias in (None, bf16_tensor(bias_bits).cuda()):
+        layer = ep.CompressedLinear(s, bias, compute=compute)
+        for M in (1, 5, 40, 100):
+            y = layer(torch.empty((M, 0), dtype=torch.bfloat16, device="cuda"))
+            torch.cuda.synchronize()
+            want = torch.zeros((M, 40), dtype=torch.bfloat16) if bias is None else bias.cpu()[None, :].expand(M, 40)
+            assert torch.equal(y.cpu(), want), (M, bias is None)
+
+
+def test_fused_forwards_on_two_streams_and_interleaved_layers():
+    """Fused forwards share nothing between calls but their stream's workspace: row-layout layers
+    of different heights called in turn on one stream, and on two streams at once (each stream with
+    its own workspace), give the bits of the first calls, BF16 and FP8."""
+    rng = np.random.default_rng(41)
+    shapes = [(2048, 1536), (520, 1024), (4096, 512)]
+    layers = []
+    for i, (N, K) in enumerate(shapes):
+        w = (0.02 * rng.standard_t(5, (N, K))).astype(np.float32)
+        s, _ = ep.compress(w, 4.0, prob_bits=ep.LAYER_PROB_BITS, layout=ep.ROW_LAYOUT)
+        b = bf16_tensor(W.to_bf16_bits(rng.normal(0, 0.1, N))).cuda() if i != 1 else None
+        layers += [ep.CompressedLinear(s, b), ep.CompressedLinear(s, b, compute="fp8")]
+    ms = [16, 40, 64, 3, 33, 1]
+    xs = [bf16_tensor(W.to_bf16_bits(rng.normal(0, 1, (m, lay.in_features)))).cuda() for m, lay in zip(ms, layers)]
+    want = [lay(x) for lay, x in zip(layers, xs)]
+    torch.cuda.synchronize()
+    for lay in layers:
+        lay.handle.check()
+    for _ in range(2):                               # in turn, reversed order, one stream
+        got = [lay(x) for lay, x in reversed(list(zip(layers, xs)))][::-1]
+        torch.cuda.synchronize()
+        assert all(torch.equal(g, w_) for g, w_ in zip(got, want))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(3):                               # two streams at once
+        got = [None] * len(layers)
+        for i, (lay, x) in enumerate(zip(layers, xs)):
+            st = streams[i % 2]
+            with torch.cuda.stream(st):
+                got[i] = lay(x, stream=st)
+        torch.cuda.synchronize()
+        assert all(torch.equal(g, w_) for g, w_ in zip(got, want))
