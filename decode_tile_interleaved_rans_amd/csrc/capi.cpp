@@ -663,7 +663,21 @@ ep_status ep_gemm_fp8(const uint8_t* dev_xq, const float* dev_xs, const uint8_t*
             return fail(EP_EINVAL, "X and W codes must be 16-byte aligned");
         ep::GemmF8Args g{dev_xq, dev_xs, dev_wq, dev_ws, static_cast<const uint16_t*>(dev_bias), static_cast<uint16_t*>(dev_y),
                          (int)M, (int)N, (int)K, (int)K, (int)K, (int)N};
-        hipError_t e = ep::launch_gemm_f8(g, static_cast<hipStream_t>(hip_stream));
+        hipStream_t s = static_cast<hipStream_t>(hip_stream);
+        // from 1024 rows hipBLASLt, as for the FP8 forward's slices (its workspace from the pool)
+        constexpr int64_t kLtMinRows = 1024;
+        constexpr size_t kLtWorkspace = 32u << 20;
+        hipError_t e = hipErrorNotSupported;
+        WsLease ws;
+        if (M >= kLtMinRows) {
+            int dev = 0;
+            e = hipGetDevice(&dev);
+            if (e == hipSuccess) e = ws_acquire(dev, s, kLtWorkspace, &ws);
+            if (e != hipSuccess) return hip_fail(e, "hipMalloc for the GEMM workspace");
+            e = ep::lt_gemm_f8(g, ws.ptr, kLtWorkspace, s);
+        }
+        if (e == hipErrorNotSupported) e = ep::launch_gemm_f8(g, s);
+        if (e == hipSuccess) e = ws.queued();
         return e == hipSuccess ? EP_OK : hip_fail(e, "fp8 gemm launch");
     });
 }

@@ -280,7 +280,10 @@ ep_status ep_quantize_rows_fp8(const void* dev_x, int64_t M, int64_t K, uint8_t*
  * Plain FP8 GEMM, the one ep_linear_forward_fp8 runs on each decoded slice, for overhead
  * comparisons: Y[m][n] = xs[m] ws[n] sum_k xq[m][k] wq[n][k] (+ bias[n]); xq [M][K] and wq [N][K]
  * E4M3 codes (16-byte aligned), xs [M] and ws [N] fp32, bias [N] bf16 or NULL, Y [M][N] bf16.
- * Requires K % 16 == 0. Asynchronous on hip_stream. */
+ * The library's own kernel below 1024 rows; hipBLASLt's from 1024 rows (the row scales as its
+ * outer-vector scales; 32 MiB of workspace from the (device, hip_stream) pool, see
+ * ep_linear_forward), falling back to the own kernel when it offers no algorithm; both
+ * deterministic. Requires K % 16 == 0. Asynchronous on hip_stream. */
 ep_status ep_gemm_fp8(const uint8_t* dev_xq, const float* dev_xs, const uint8_t* dev_wq, const float* dev_ws,
                       int64_t M, int64_t N, int64_t K, const void* dev_bias, void* dev_y, void* hip_stream);
 

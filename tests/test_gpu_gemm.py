@@ -248,8 +248,9 @@ def test_quantize_rows_fp8_matches_oracle(M, K):
 
 # shapes cover every FP8 tile choice: 64 x 32 tiles for M <= 64, 64 x 64, 128 x 128 (2 x 256 of them
 # or more) and 256 x 256 (256 or more), with ragged M and N and K not a multiple of the 128 K step
+# (2000, 4000, 144), (4100, 4000, 272) and (1024, 1000, 2064) go to hipBLASLt (1024 rows and more)
 @pytest.mark.parametrize("M,N,K", [(16, 256, 512), (64, 4100, 1040), (300, 1000, 784), (1, 8, 16),
-                                   (2000, 4000, 144), (4100, 4000, 272), (33, 17, 4112)])
+                                   (2000, 4000, 144), (4100, 4000, 272), (33, 17, 4112), (1024, 1000, 2064)])
 def test_gemm_fp8_matches_fp64(M, N, K):
     rng = np.random.default_rng(M + N + K)
     x = W.to_bf16_bits(rng.normal(0, 1, (M, K)))
@@ -257,11 +258,14 @@ def test_gemm_fp8_matches_fp64(M, N, K):
     xq, xs = oracle.quantize_rows_e4m3(x)
     wq, ws = oracle.quantize_rows_e4m3(w)
     b = W.to_bf16_bits(rng.normal(0, 0.1, N))
-    y = ep.gemm_fp8(torch.from_numpy(xq).cuda(), torch.from_numpy(xs).cuda(), torch.from_numpy(wq).cuda(),
-                    torch.from_numpy(ws).cuda(), bias=bf16_tensor(b).cuda())
+    args = (torch.from_numpy(xq).cuda(), torch.from_numpy(xs).cuda(), torch.from_numpy(wq).cuda(),
+            torch.from_numpy(ws).cuda())
+    y = ep.gemm_fp8(*args, bias=bf16_tensor(b).cuda())
+    y2 = ep.gemm_fp8(*args, bias=bf16_tensor(b).cuda())
     torch.cuda.synchronize()
     ref = fp8_reference(xq, xs, wq, ws, W.bf16_bits_to_f32(b).astype(np.float64))
     assert rel_l2(y.float().cpu().numpy(), ref) < 3e-3
+    assert torch.equal(y, y2), "two calls must give the same bits"
 
 
 def fp8_linear_case(M, N, K, target, seed, bias=False, rows=None):
