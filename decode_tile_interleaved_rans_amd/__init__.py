@@ -395,11 +395,14 @@ class CompressedLinear:
     """Linear layer that keeps only the compressed weight and decodes it on every forward
     ("EntroPack PyTorch Guide", section "Replace one linear layer before a whole model").
 
-    compute="bf16" (default): for up to 4 activation rows the decode kernel forms the products
-    itself (the weight is never written); for more rows the weight is decoded once per call into
-    a scratch slice that stays in the Infinity Cache and the BF16 MFMA GEMM reads it from there.
-    compute="fp8": the weight is decoded to FP8 E4M3 with its row scales, the activations are
-    quantized per row, and the FP8 MFMA GEMM multiplies the codes.
+    compute="bf16" (default): for up to 64 activation rows of a row-layout stream (the layout
+    from_linear codes) one kernel decodes every tile pair straight into the B operand of the BF16
+    MFMA and the weight is never written; a layout-0 stream is fused that way through LDS for 5 to
+    16 rows and by the decode kernel's own products for up to 4. For more rows the weight is decoded
+    once per call into scratch slices that stay in the Infinity Cache, and a BF16 MFMA GEMM reads
+    them from there (the library's own below 1024 rows, hipBLASLt's from 1024).
+    compute="fp8": the weight is decoded to FP8 E4M3 with its row scales and the activations are
+    quantized per row; the codes meet in the FP8 MFMA, fused in the same cases, else on slices.
 
     The forward takes BF16 activations. Other dtypes are refused unless cast=True is passed, so a
     precision change is never silent ("Diagnose compression failures in the correct order")."""
