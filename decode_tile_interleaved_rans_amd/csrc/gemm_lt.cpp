@@ -28,7 +28,20 @@ struct LtPlan {
     hipblasLtMatmulAlgo_t algo{};
     size_t ws = 0;
     bool ok = false;
+    uint64_t tick = 0;         // last use, for eviction
 };
+
+// Plans kept at most: a caller whose row count varies from call to call (serving with variable
+// token counts) would otherwise add a plan, and a heuristic query, per distinct M for ever.
+constexpr size_t kMaxPlans = 128;
+
+void destroy(LtPlan& p) {
+    if (p.a) hipblasLtMatrixLayoutDestroy(p.a);
+    if (p.b) hipblasLtMatrixLayoutDestroy(p.b);
+    if (p.d) hipblasLtMatrixLayoutDestroy(p.d);
+    if (p.desc) hipblasLtMatmulDescDestroy(p.desc);
+    p = LtPlan{};
+}
 
 using LtKey = std::tuple<int, int, int, int, int, int, int, bool, bool, size_t>;
 
@@ -40,6 +53,7 @@ struct LtShape {
 std::mutex g_mu;                                   // guards the maps and each plan's pointer attributes
 std::map<int, hipblasLtHandle_t> g_handles;        // per device, kept until the process ends
 std::map<LtKey, LtPlan> g_plans;
+uint64_t g_tick = 0;
 
 // Pointers a call sets on the shared descriptor (under the lock): bias and the FP8 scale vectors.
 void set_pointers(hipblasLtMatmulDesc_t d, const void* bias, const void* sa, const void* sb) {
@@ -102,8 +116,20 @@ hipError_t run(const LtShape& s, const void* W, const void* X, void* Y, const vo
     }
     const LtKey key{dev, s.M, s.N, s.K, s.ldx, s.ldw, s.ldy, s.bias, s.f8, ws_bytes};
     auto it = g_plans.find(key);
-    if (it == g_plans.end()) it = g_plans.emplace(key, make_plan(h, s, ws_bytes, bias, sa, sb)).first;
+    if (it == g_plans.end()) {
+        if (g_plans.size() >= kMaxPlans) {
+            // the least recently used plan goes; descriptors are host objects that a queued
+            // matmul no longer reads once hipblasLtMatmul has returned
+            auto lru = g_plans.begin();
+            for (auto j = g_plans.begin(); j != g_plans.end(); ++j)
+                if (j->second.tick < lru->second.tick) lru = j;
+            destroy(lru->second);
+            g_plans.erase(lru);
+        }
+        it = g_plans.emplace(key, make_plan(h, s, ws_bytes, bias, sa, sb)).first;
+    }
     LtPlan& p = it->second;
+    p.tick = ++g_tick;
     if (!p.ok) return hipErrorNotSupported;
     set_pointers(p.desc, bias, sa, sb);            // this call's vectors (the plan is per shape)
     const float alpha = 1.0f, beta = 0.0f;

@@ -496,3 +496,29 @@ def test_fused_forwards_on_two_streams_and_interleaved_layers():
                 got[i] = lay(x, stream=st)
         torch.cuda.synchronize()
         assert all(torch.equal(g, w_) for g, w_ in zip(got, want))
+
+
+def test_gemm_library_plan_cache_keeps_working_past_its_limit():
+    """hipBLASLt plans are cached per shape up to a fixed count, least recently used out first:
+    140 distinct row counts through the plain FP8 GEMM (hipBLASLt from 1024 rows), then the first
+    shape again, which gets a new plan and the same bits; sampled results match the fp64 product."""
+    rng = np.random.default_rng(77)
+    N, K = 256, 256
+    w = W.to_bf16_bits(rng.standard_t(5, (N, K)) * 0.02)
+    wq, ws = oracle.quantize_rows_e4m3(w)
+    wq_t, ws_t = torch.from_numpy(wq).cuda(), torch.from_numpy(ws).cuda()
+    x = W.to_bf16_bits(rng.normal(0, 1, (1024 + 140, K)))
+    xq, xs = oracle.quantize_rows_e4m3(x)
+    xq_t, xs_t = torch.from_numpy(xq).cuda(), torch.from_numpy(xs).cuda()
+    first = None
+    for M in range(1024, 1024 + 140):
+        y = ep.gemm_fp8(xq_t[:M].contiguous(), xs_t[:M].contiguous(), wq_t, ws_t)
+        if M == 1024:
+            first = y.clone()
+        if M % 35 == 0:
+            torch.cuda.synchronize()
+            ref = fp8_reference(xq[:M], xs[:M], wq, ws, None)
+            assert rel_l2(y.float().cpu().numpy(), ref) < 3e-3, M
+    again = ep.gemm_fp8(xq_t[:1024].contiguous(), xs_t[:1024].contiguous(), wq_t, ws_t)
+    torch.cuda.synchronize()
+    assert torch.equal(again, first)
