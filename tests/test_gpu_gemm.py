@@ -113,8 +113,8 @@ def test_linear_forward_prefill_sampled_rows():
     rows = np.random.default_rng(4).choice(M, 32, replace=False)
     ref = W.bf16_bits_to_f32(xb[rows]) @ w_hat.T
     assert rel_l2(y[rows].float().cpu().numpy(), ref) < 2e-2
-    # the token counts the benchmark also times on this weight: M = 1 (fused matrix-vector
-    # kernel) and M = 16 (decode-once slice + skinny GEMM)
+    # two more token counts on this weight: M = 1 (fused matrix-vector kernel) and M = 16 (the
+    # transposing fused decode + MFMA kernel)
     for m in (1, 16):
         ym = layer(X[:m].contiguous())
         torch.cuda.synchronize()
@@ -522,3 +522,31 @@ def test_gemm_library_plan_cache_keeps_working_past_its_limit():
     again = ep.gemm_fp8(xq_t[:1024].contiguous(), xs_t[:1024].contiguous(), wq_t, ws_t)
     torch.cuda.synchronize()
     assert torch.equal(again, first)
+
+
+@pytest.mark.parametrize("layout", [0, ep.ROW_LAYOUT])
+def test_benchmark_weight_every_forward_path(layout):
+    """The 8192 x 8192 benchmark weight coded as the benchmark codes it (4.5 bpp target, the layers'
+    11-bit probabilities) in each tile layout, through every forward path the benchmark times:
+    M = 1 and 4 (matrix-vector kernel in layout 0, register-direct fused kernel in the row layout),
+    16, 32 and 64 (fused kernels), 256 (decode-once slice + split-K GEMM) and 4096 (slice +
+    hipBLASLt), BF16 and FP8. Sampled rows within 5e-3 (BF16) of the fp64 product of the oracle's
+    BF16 weights and within 3e-3 (FP8) of the product of the oracle's E4M3 codes and scales."""
+    w, xb = W.prefill_case()
+    s, _ = ep.compress(w, 4.5, dtype=ep.BF16, prob_bits=ep.LAYER_PROB_BITS, layout=layout)
+    layer, layer8 = ep.CompressedLinear(s), ep.CompressedLinear(s, compute="fp8")
+    w_hat = W.bf16_bits_to_f32(oracle.decompress(s, oracle.BF16, n_threads=16)[0]).astype(np.float64)
+    wq, ws = oracle.decompress(s, oracle.F8E4M3, n_threads=16)
+    X = bf16_tensor(xb).cuda()
+    rng = np.random.default_rng(layout + 40)
+    for M in (1, 4, 16, 32, 64, 256, 4096):
+        rows = np.sort(rng.choice(M, min(M, 12), replace=False))
+        y = layer(X[:M].contiguous())
+        y8 = layer8(X[:M].contiguous())
+        torch.cuda.synchronize()
+        layer.handle.check()
+        ref = W.bf16_bits_to_f32(xb[rows]).astype(np.float64) @ w_hat.T
+        assert rel_l2(y[rows].float().cpu().numpy(), ref) < 5e-3, ("bf16", M)
+        xq, xs = oracle.quantize_rows_e4m3(xb[:M])
+        ref8 = fp8_reference(xq[rows], xs[rows], wq, ws)
+        assert rel_l2(y8[rows].float().cpu().numpy(), ref8) < 3e-3, ("fp8", M)
