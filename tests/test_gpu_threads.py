@@ -94,3 +94,64 @@ def test_concurrent_callers_on_separate_streams():
             if y64_first is None:
                 y64_first = y64
             assert torch.equal(y64, y64_first), where
+
+
+def test_concurrent_prefill_and_fused_forwards():
+    """Four threads on streams of their own run, at the same time, the forwards whose GEMM is
+    hipBLASLt's (1024 activation rows: BF16 slices, FP8 slices and the plain FP8 GEMM; the plan
+    cache and each call's descriptor pointers are shared under one lock) and the row-layout fused
+    kernel (40 rows). Every result must have the bits of the same call made alone first, and the
+    lone calls match the fp64 products of the oracle's weights on sampled rows."""
+    N, K, n_thr, iters = 1000, 2048, 4, 3
+    w = W.student_t(N, K, seed=33).astype(np.float32)
+    s, _ = ep.compress(w, 4.0, prob_bits=ep.LAYER_PROB_BITS, layout=ep.ROW_LAYOUT)
+    bias = torch.from_numpy(W.activations(1, N, 34)[0].view(np.int16)).view(torch.bfloat16).cuda()
+    layer, layer8 = ep.CompressedLinear(s, bias), ep.CompressedLinear(s, bias, compute="fp8")
+    xb = {m: W.activations(m, K, seed=600 + m) for m in (1024, 40)}
+    xg = {m: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda() for m, x in xb.items()}
+    wq, ws = ep.quantize_rows_fp8(torch.from_numpy(W.to_bf16_bits(w).view(np.int16)).view(torch.bfloat16).cuda())
+    xq, xs = ep.quantize_rows_fp8(xg[1024])
+
+    def calls(st=None):
+        return (layer.forward(xg[1024], stream=st), layer8.forward(xg[1024], stream=st),
+                ep.gemm_fp8(xq, xs, wq, ws, stream=st), layer.forward(xg[40], stream=st),
+                layer8.forward(xg[40], stream=st))
+
+    want = [y.cpu() for y in calls()]
+    torch.cuda.synchronize()
+    layer.handle.check()
+    w_hat = W.bf16_bits_to_f32(oracle.decompress(s, oracle.BF16, n_threads=8)[0]).astype(np.float64)
+    b64 = bias.float().cpu().numpy().astype(np.float64)
+    rows = np.arange(0, 1024, 97)
+    ref = W.bf16_bits_to_f32(xb[1024][rows]).astype(np.float64) @ w_hat.T + b64[None, :]
+    assert rel_l2(want[0][rows].float().numpy(), ref) < 2e-2
+    ref40 = W.bf16_bits_to_f32(xb[40]).astype(np.float64) @ w_hat.T + b64[None, :]
+    assert rel_l2(want[3].float().numpy(), ref40) < 2e-2
+
+    results, errors = [None] * n_thr, []
+    start = threading.Barrier(n_thr)
+
+    def worker(t):
+        try:
+            torch.cuda.set_device(0)
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                start.wait()
+                out = [calls(st) for _ in range(iters)]
+            st.synchronize()
+            results[t] = [[y.cpu() for y in it] for it in out]
+        except BaseException as e:                       # reported by the main thread
+            errors.append((t, repr(e)))
+            start.abort()
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(n_thr)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not any(th.is_alive() for th in threads), "a worker thread did not finish"
+    assert not errors, errors
+    for t, its in enumerate(results):
+        for i, ys in enumerate(its):
+            for j, (got, exp) in enumerate(zip(ys, want)):
+                assert torch.equal(got, exp), f"thread {t} iteration {i} call {j}"
