@@ -335,10 +335,12 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
     }
     const int tr = w->view.tile_rows;
     // From kLtMinRows activation rows the slices are multiplied by hipBLASLt, whose tuned kernels
-    // beat the own 256 x 256 one at prefill sizes (4096 x 8192 x 8192: 363 against 441 us); below,
-    // the own kernel (split-K when its tiles cannot fill the CUs) is the faster one. Not in the
-    // no-allocation variant: the library's handle allocates on first use.
-    constexpr int64_t kLtMinRows = 1024;
+    // beat the own 256 x 256 one there (4096 x 8192 x 8192: 363 against 441 us; nine layer shapes
+    // from 2048 to 8192 square at 512 and 768 rows: 14% and 22% less forward time, the same bits on
+    // every repeat); below, the own kernel (split-K when its tiles cannot fill the CUs) is faster on
+    // the large layers. Not in the no-allocation variant: the library's handle allocates on first
+    // use.
+    constexpr int64_t kLtMinRows = 512;
     constexpr size_t kLtWorkspace = 32u << 20;
     const bool lt = !fixed && M >= kLtMinRows;
     // K splits of the GEMM, chosen for the whole layer so that every slice adds its partial sums in
@@ -664,8 +666,8 @@ ep_status ep_gemm_fp8(const uint8_t* dev_xq, const float* dev_xs, const uint8_t*
         ep::GemmF8Args g{dev_xq, dev_xs, dev_wq, dev_ws, static_cast<const uint16_t*>(dev_bias), static_cast<uint16_t*>(dev_y),
                          (int)M, (int)N, (int)K, (int)K, (int)K, (int)N};
         hipStream_t s = static_cast<hipStream_t>(hip_stream);
-        // from 1024 rows hipBLASLt, as for the FP8 forward's slices (its workspace from the pool)
-        constexpr int64_t kLtMinRows = 1024;
+        // from kLtMinRows rows hipBLASLt, as for the FP8 forward's slices (its workspace from the pool)
+        constexpr int64_t kLtMinRows = 512;
         constexpr size_t kLtWorkspace = 32u << 20;
         hipError_t e = hipErrorNotSupported;
         WsLease ws;
@@ -736,7 +738,7 @@ ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M
         if (slice < tr) slice = tr;
         if (slice > N) slice = (N + tr - 1) / tr * tr;
         // from kLtMinRows rows the slices are multiplied by hipBLASLt (as in the BF16 forward)
-        constexpr int64_t kLtMinRows = 1024;
+        constexpr int64_t kLtMinRows = 512;
         constexpr size_t kLtWorkspace = 32u << 20;
         const bool lt = M >= kLtMinRows;
         // workspace: X codes [M][K] | X scales [M] | weight codes [slice][K] | weight scales [slice]
