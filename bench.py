@@ -209,7 +209,7 @@ def fused_gemm_section(torch, ep, reps: int = 15):
            "reps": reps, "timing": "median of per-rep HIP events, the five variants interleaved within each "
                                    "rep, 1 GiB cache flush before every timed call"}
     # plain FP8 baseline: ep.gemm_fp8 on the weight and activations pre-quantized per row
-    # (hipBLASLt from 512 rows, the library's own kernel below)
+    # (hipBLASLt from 512 rows, or 256 when N <= 4096 or K <= 2048; the library's own kernel else)
     wq, ws = ep.quantize_rows_fp8(Wt)
     for M in (4096, 256, 64, 32, 16, 4, 1):
         X = Xf[:M].contiguous()

@@ -274,6 +274,18 @@ ep_status take_static(size_t need, WsLease* L) {
     return EP_OK;
 }
 
+// Whether an M x N x K product of a decoded slice (or the plain FP8 GEMM) goes to hipBLASLt rather
+// than the library's own kernel: from 512 rows always, and from 256 rows when the own kernel's
+// 256 x 256 tiles need split-K to fill the CUs and its partial sums outweigh the work (N <= 4096)
+// or K is short (K <= 2048). Measured on nine layer shapes from 2048^2 to 8192^2: at 512 and 768
+// rows hipBLASLt cuts the summed forward time by 14% and 22%; at 256 and 384 rows it is 6-20%
+// faster on the shapes this rule sends to it and within noise on the other two (8192 x 4096,
+// 8192^2), where below 256 rows, or at 256 with both N > 4096 and K > 2048, the own kernel is as
+// fast or faster (8192^2 at 256 rows: 88 against 102 us). Every repeat gave the same bits.
+bool use_gemm_library(int64_t M, int64_t N, int64_t K) {
+    return M >= 512 || (M >= 256 && (N <= 4096 || K <= 2048));
+}
+
 // Compressed linear forward. The weight is decoded once per call, one slice of output rows at a
 // time, into the forward's scratch, and each slice's GEMM writes its columns of Y. A slice of at
 // most kSliceBytes is large enough to keep every CU's decode block busy and, with the
@@ -334,15 +346,12 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
         return e == hipSuccess ? EP_OK : hip_fail(e, "fused decode + MFMA launch");
     }
     const int tr = w->view.tile_rows;
-    // From kLtMinRows activation rows the slices are multiplied by hipBLASLt, whose tuned kernels
-    // beat the own 256 x 256 one there (4096 x 8192 x 8192: 363 against 441 us; nine layer shapes
-    // from 2048 to 8192 square at 512 and 768 rows: 14% and 22% less forward time, the same bits on
-    // every repeat); below, the own kernel (split-K when its tiles cannot fill the CUs) is faster on
-    // the large layers. Not in the no-allocation variant: the library's handle allocates on first
-    // use.
-    constexpr int64_t kLtMinRows = 512;
+    // Slices multiplied by hipBLASLt where use_gemm_library says so (its tuned kernels beat the own
+    // 256 x 256 one at prefill sizes: 4096 x 8192 x 8192, 363 against 441 us); elsewhere the own
+    // kernel, split-K when its tiles cannot fill the CUs. Not in the no-allocation variant: the
+    // library's handle allocates on first use.
     constexpr size_t kLtWorkspace = 32u << 20;
-    const bool lt = !fixed && M >= kLtMinRows;
+    const bool lt = !fixed && use_gemm_library(M, N, K);
     // K splits of the GEMM, chosen for the whole layer so that every slice adds its partial sums in
     // the same order; the split partial tiles of a slice follow its decoded rows in the scratch
     const int splits = lt ? 1 : ep::gemm_splits((int)M, (int)N, (int)K);
@@ -666,12 +675,12 @@ ep_status ep_gemm_fp8(const uint8_t* dev_xq, const float* dev_xs, const uint8_t*
         ep::GemmF8Args g{dev_xq, dev_xs, dev_wq, dev_ws, static_cast<const uint16_t*>(dev_bias), static_cast<uint16_t*>(dev_y),
                          (int)M, (int)N, (int)K, (int)K, (int)K, (int)N};
         hipStream_t s = static_cast<hipStream_t>(hip_stream);
-        // from kLtMinRows rows hipBLASLt, as for the FP8 forward's slices (its workspace from the pool)
-        constexpr int64_t kLtMinRows = 512;
+        // hipBLASLt where use_gemm_library says so, as for the FP8 forward's slices (its workspace
+        // from the pool)
         constexpr size_t kLtWorkspace = 32u << 20;
         hipError_t e = hipErrorNotSupported;
         WsLease ws;
-        if (M >= kLtMinRows) {
+        if (use_gemm_library(M, N, K)) {
             int dev = 0;
             e = hipGetDevice(&dev);
             if (e == hipSuccess) e = ws_acquire(dev, s, kLtWorkspace, &ws);
@@ -737,10 +746,9 @@ ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M
         int64_t slice = (int64_t)(kSliceBytes / (size_t)K) / tr * tr;
         if (slice < tr) slice = tr;
         if (slice > N) slice = (N + tr - 1) / tr * tr;
-        // from kLtMinRows rows the slices are multiplied by hipBLASLt (as in the BF16 forward)
-        constexpr int64_t kLtMinRows = 512;
+        // slices multiplied by hipBLASLt where use_gemm_library says so (as in the BF16 forward)
         constexpr size_t kLtWorkspace = 32u << 20;
-        const bool lt = M >= kLtMinRows;
+        const bool lt = use_gemm_library(M, N, K);
         // workspace: X codes [M][K] | X scales [M] | weight codes [slice][K] | weight scales [slice]
         // | hipBLASLt workspace
         const size_t o_xs = up((size_t)M * (size_t)K, 256), o_wq = up(o_xs + 4 * (size_t)M, 256);

@@ -209,9 +209,9 @@ ep_status ep_decode_symbols(const ep_handle* h, int16_t* dev_q, void* hip_stream
  *     differ in the last bits);
  *   - otherwise the weight is decoded once per call, up to 128 MiB of BF16 rows at a time, into
  *     the workspace, which stays in the Infinity Cache, and each slice is multiplied by the BF16
- *     MFMA GEMM: the library's own kernel below 512 rows, hipBLASLt's from 512 rows (faster at
- *     prefill sizes; its handle is created on the device's first such call); both deterministic
- *     (tested); no decoded copy of W outlives the call.
+ *     MFMA GEMM: hipBLASLt's from 512 rows, and from 256 when N <= 4096 or K <= 2048 (faster
+ *     there; its handle is created on the device's first such call), else the library's own; both
+ *     deterministic (tested); no decoded copy of W outlives the call.
  * The fused and slice paths multiply the same BF16-rounded weights. The workspace belongs
  * to the (device, hip_stream) pair: calls on one stream reuse it in order, calls on different
  * streams get different workspaces; it is allocated on first use
@@ -229,7 +229,7 @@ ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, co
  * arguments, results and paths as ep_linear_forward (the same kernels: the fused kernel's partial
  * sums, the fp32 accumulator of M <= 4 on layout-0 streams, otherwise BF16 weight slices of at
  * most 64 MiB, i.e. 64 MiB / (2 K) rows, always multiplied by the library's own GEMM kernel, so
- * results at 512 rows and more may differ from ep_linear_forward's in the fp32 summation
+ * results where ep_linear_forward uses hipBLASLt may differ from it in the fp32 summation
  * order). EP_ERANGE when a call needs more than the array holds
  * (M <= 4 with 4 M N > 64 MiB, the fused partials of very wide layers, or K > 2^21 for the slices).
  * Every call on a device shares that device's array: calls that overlap in time on one device
@@ -280,9 +280,9 @@ ep_status ep_quantize_rows_fp8(const void* dev_x, int64_t M, int64_t K, uint8_t*
  * Plain FP8 GEMM, the one ep_linear_forward_fp8 runs on each decoded slice, for overhead
  * comparisons: Y[m][n] = xs[m] ws[n] sum_k xq[m][k] wq[n][k] (+ bias[n]); xq [M][K] and wq [N][K]
  * E4M3 codes (16-byte aligned), xs [M] and ws [N] fp32, bias [N] bf16 or NULL, Y [M][N] bf16.
- * The library's own kernel below 512 rows; hipBLASLt's from 512 rows (the row scales as its
+ * hipBLASLt's from 512 rows, and from 256 when N <= 4096 or K <= 2048 (the row scales as its
  * outer-vector scales; 32 MiB of workspace from the (device, hip_stream) pool, see
- * ep_linear_forward), falling back to the own kernel when it offers no algorithm; both
+ * ep_linear_forward), else, or when it offers no algorithm, the library's own kernel; both
  * deterministic. Requires K % 16 == 0. Asynchronous on hip_stream. */
 ep_status ep_gemm_fp8(const uint8_t* dev_xq, const float* dev_xs, const uint8_t* dev_wq, const float* dev_ws,
                       int64_t M, int64_t N, int64_t K, const void* dev_bias, void* dev_y, void* hip_stream);

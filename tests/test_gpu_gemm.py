@@ -122,10 +122,11 @@ def test_linear_forward_prefill_sampled_rows():
         assert rel_l2(ym.float().cpu().numpy(), refm) < 2e-2, m
 
 
-@pytest.mark.parametrize("M", [512, 1024])
+@pytest.mark.parametrize("M", [256, 512, 1024])
 @pytest.mark.parametrize("layout", [0, ep.ROW_LAYOUT])
 def test_prefill_forward_through_the_gemm_library(layout, M):
-    """From 512 activation rows the decoded slices are multiplied by hipBLASLt: a ragged N with a
+    """From 512 activation rows (from 256 for this N <= 4096) the decoded slices are multiplied by
+    hipBLASLt: a ragged N with a
     bias (its bias epilogue) and two slices of a wide K, sampled rows within 2e-2 of the fp32
     product of the oracle's weights, the same bits on a second call, and agreement with the own
     GEMM on the same decoded weight within the fp32 summation order."""
@@ -249,8 +250,8 @@ def test_quantize_rows_fp8_matches_oracle(M, K):
 
 # shapes cover every FP8 tile choice: 64 x 32 tiles for M <= 64, 64 x 64, 128 x 128 (2 x 256 of them
 # or more) and 256 x 256 (256 or more), with ragged M and N and K not a multiple of the 128 K step
-# (2000, 4000, 144), (4100, 4000, 272), (1024, 1000, 2064) and (600, 520, 1040) go to hipBLASLt
-# (512 rows and more)
+# (2000, 4000, 144), (4100, 4000, 272), (1024, 1000, 2064), (600, 520, 1040) and (300, 1000, 784) go
+# to hipBLASLt (512 rows and more, or 256 and more with N <= 4096 or K <= 2048)
 @pytest.mark.parametrize("M,N,K", [(16, 256, 512), (64, 4100, 1040), (300, 1000, 784), (1, 8, 16),
                                    (2000, 4000, 144), (4100, 4000, 272), (33, 17, 4112), (1024, 1000, 2064),
                                    (600, 520, 1040)])
@@ -323,9 +324,9 @@ def test_linear_forward_fp8_prefill_sampled_rows():
     assert rel_l2(y[rows].float().cpu().numpy(), fp8_reference(xq, xs, wq, ws)) < 3e-3
 
 
-@pytest.mark.parametrize("M", [512, 1024])
+@pytest.mark.parametrize("M", [256, 512, 1024])
 def test_fp8_prefill_with_bias_over_two_slices(M):
-    """The FP8 forward from 512 rows (slices multiplied by hipBLASLt with the row scales as
+    """The FP8 forward from 512 rows (256 for this N; slices multiplied by hipBLASLt with the row scales as
     outer-vector scales): a ragged N with a bias over two slices, against the fp64 product of the
     oracle's codes and scales, repeatable bits."""
     N, K = 1000, 139264                             # 128 MiB FP8 slices of 960 rows: 960 + 40

@@ -40,7 +40,7 @@ def rel_l2(a, b):
 
 
 @pytest.mark.parametrize("layout", [0, ep.ROW_LAYOUT])
-@pytest.mark.parametrize("Ms", [(96, 40), (4, 1), (300, 3)])
+@pytest.mark.parametrize("Ms", [(96, 40), (4, 1), (300, 3), (200, 100)])
 def test_noalloc_forward_matches_pool_forward(Ms, layout):
     w = W.student_t(2048, 3072, seed=71)
     s, _ = ep.compress(w, 4.0, dtype=ep.BF16, layout=layout)
@@ -60,7 +60,11 @@ def test_noalloc_forward_matches_pool_forward(Ms, layout):
         a = y_fixed.float().cpu().numpy()
         b = y_pool.float().cpu().numpy()
         assert np.isfinite(a).all()
-        if M > 4 or layout != 0:
+        if M >= 256:
+            # the pool forward multiplies these slices with hipBLASLt (the no-allocation one with
+            # the library's own kernel): the fp32 summation order differs
+            assert rel_l2(a, b) < 3e-3, M
+        elif M > 4 or layout != 0:
             assert torch.equal(y_fixed, y_pool), M        # same kernels, deterministic order
         else:
             assert rel_l2(a, b) < 1e-3, M                 # fp32 atomics: summation order varies
