@@ -531,7 +531,9 @@ __device__ __forceinline__ void group_body(const GroupArgs& g) {
         if (p0 >= p1) continue;
         const bool lossy = M.mode == 0;
         __syncthreads();                            // every wave is done with the previous tables
-        const Tables T = stage_tables(M, smem, lossy);
+        Tables T;
+        if constexpr (ROWS) T = stage_lossy_tables_dma(M, smem);   // once per launch, mostly
+        else T = stage_tables(M, smem, lossy);
         Tile t[kChains];
 #pragma unroll
         for (int c = 0; c < kChains; ++c) init_lane(t[c], smem + lds_table_bytes(M.n_tables, M.prob_bits, lossy), c);

@@ -82,6 +82,39 @@ __device__ __forceinline__ Tables stage_tables(const MatDesc& M, uint8_t* smem, 
     return T;
 }
 
+// stage_tables for a lossy matrix by direct global -> LDS loads (buffer_load ... lds): each wave
+// instruction moves 1 KiB (64 lanes x 16 bytes) with no registers staging it, and a wave issues
+// all of its loads before it waits, where stage_tables' copy waits for each 16-byte load in turn
+// (four to six global round trips). For kernels that stage once per launch, mostly: the fused
+// kernels (row layout at M = 1: 77.0 -> 76.1 us) and the row-layout decode, whose launches are
+// mostly one layer's weight slice each. In the layout-0 decode, which restages per matrix inside
+// its pair loop, the resource and loop state pushed the scalar registers into spills (1160 more
+// v_readlane, DiT-like step 837 -> 872 us per launch). prob_bits >= 10: both arrays whole KiB.
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t src, uint8_t* dst, uint32_t bytes) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const uint32_t nw = blockDim.x >> 6;
+    for (uint32_t g = wave; g < bytes / 1024; g += nw)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + 1024 * g), 16, src + 1024 * g + 16 * lane, 0, 0, 0);
+}
+
+__device__ __forceinline__ Tables stage_lossy_tables_dma(const MatDesc& M, uint8_t* smem) {
+    const int n = M.prob_bits, nt = M.n_tables - 1;        // the coset table stays out of LDS
+    const uint32_t lut_bytes = (uint32_t)nt << n, ent_bytes = (uint32_t)nt * 2048u;
+    const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(M.tables), 0, (int)table_blob_bytes(M.n_tables, n), 0x00020000);
+    dma_to_lds(rt, 1u << n, smem, lut_bytes);
+    dma_to_lds(rt, ((uint32_t)M.n_tables << n) + 2048u, smem + lut_bytes, ent_bytes);
+    __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0): this wave's loads have landed
+    __syncthreads();
+    Tables T;
+    T.lut = smem;
+    T.ent = reinterpret_cast<const uint2*>(smem + lut_bytes);
+    return T;
+}
+
 // ----------------------------------------------------------------------------- one half-wave tile
 struct Tile {
     uint32_t x;            // rANS state of this lane

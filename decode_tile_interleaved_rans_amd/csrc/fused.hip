@@ -34,38 +34,6 @@ namespace {
 // pairs by fused_finish in column order, so the result does not depend on scheduling.
 constexpr int kFusedBuf = 4096;            // LDS transposition buffer per wave
 
-// The decode tables of matrix M into LDS as stage_tables places them, by direct global -> LDS loads
-// (buffer_load ... lds): each wave instruction moves 1 KiB (64 lanes x 16 bytes) with no registers
-// staging it, and a wave issues all of its loads before it waits, where stage_tables' copy waits
-// for each 16-byte load in turn. These kernels stage once per launch, so the one global round
-// trip instead of four to six shortens every call (row layout at M = 1: 77.0 -> 75.5 us).
-// (The decode kernels re-stage per matrix inside their pair loop; there the buffer resource and
-// loop state pushed the scalar registers into spills.) prob_bits >= 10 makes both arrays whole KiB.
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t src, uint8_t* dst, uint32_t bytes) {
-    const uint32_t lane = threadIdx.x & 63;
-    const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const uint32_t nw = blockDim.x >> 6;
-    for (uint32_t g = wave; g < bytes / 1024; g += nw)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + 1024 * g), 16, src + 1024 * g + 16 * lane, 0, 0, 0);
-}
-
-__device__ __forceinline__ Tables stage_lossy_tables(const MatDesc& M, uint8_t* smem) {
-    const int n = M.prob_bits, nt = M.n_tables - 1;        // the coset table stays out of LDS
-    const uint32_t lut_bytes = (uint32_t)nt << n, ent_bytes = (uint32_t)nt * 2048u;
-    const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(M.tables), 0, (int)table_blob_bytes(M.n_tables, n), 0x00020000);
-    dma_to_lds(rt, 1u << n, smem, lut_bytes);
-    dma_to_lds(rt, ((uint32_t)M.n_tables << n) + 2048u, smem + lut_bytes, ent_bytes);
-    __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0): this wave's loads have landed
-    __syncthreads();
-    Tables T;
-    T.lut = smem;
-    T.ent = reinterpret_cast<const uint2*>(smem + lut_bytes);
-    return T;
-}
-
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -176,7 +144,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma(GroupArgs g) {
     const uint64_t w = M.pair_cost;
     const uint64_t p0 = (a + w - 1) / w, p1 = (b + w - 1) / w;
     if (p0 >= p1) return;
-    const Tables T = stage_lossy_tables(M, smem);
+    const Tables T = stage_lossy_tables_dma(M, smem);
     const size_t tb = lds_table_bytes(M.n_tables, M.prob_bits, true);
     Tile t;
     init_lane(t, smem + tb, 0);
@@ -303,7 +271,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_f8(GroupArgs g) {
     const uint64_t w = M.pair_cost;
     const uint64_t p0 = (a + w - 1) / w, p1 = (b + w - 1) / w;
     if (p0 >= p1) return;
-    const Tables T = stage_lossy_tables(M, smem);
+    const Tables T = stage_lossy_tables_dma(M, smem);
     const size_t tb = lds_table_bytes(M.n_tables, M.prob_bits, true);
     Tile t;
     init_lane(t, smem + tb, 0);
@@ -435,7 +403,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_rows(GroupArgs g) {
     const uint64_t w = M.pair_cost;
     const uint64_t p0 = (a + w - 1) / w, p1 = (b + w - 1) / w;
     if (p0 >= p1) return;
-    const Tables T = stage_lossy_tables(M, smem);
+    const Tables T = stage_lossy_tables_dma(M, smem);
     Tile t;
     init_lane(t, smem + lds_table_bytes(M.n_tables, M.prob_bits, true), 0);
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
