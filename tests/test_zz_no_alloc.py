@@ -71,3 +71,52 @@ def test_noalloc_forward_matches_pool_forward(Ms, layout):
         ref = W.bf16_bits_to_f32(xb).astype(np.float64) @ w_hat.T + W.bf16_bits_to_f32(bias_bits)[None, :]
         assert rel_l2(a, ref) < 2e-2, M
     h.release()
+
+
+def test_noalloc_forwards_captured_in_a_hip_graph():
+    """What the no-allocation entry point is for: forwards captured into a HIP graph (after one
+    warm-up call per path, which resolves the static scratch), here the row-layout fused kernel
+    (40 rows), the layout-0 matrix-vector kernel (3 rows) and decode slices + GEMM (96 rows) in
+    one graph on one stream. Three replays, with eager work on the stream between them, each give
+    the eager calls' results (the same bits; the matrix-vector kernel's float atomics within 1e-3)."""
+    L = ep.lib()
+    cases = []
+    for layout, M, seed in ((ep.ROW_LAYOUT, 40, 81), (0, 3, 82), (0, 96, 83)):
+        w = W.student_t(1024, 2048, seed=seed)
+        s, _ = ep.compress(w, 4.0, dtype=ep.BF16, layout=layout)
+        h = ep.upload(s)
+        x = bf16(W.activations(M, 2048, seed + 10))
+        bias = bf16(W.activations(1, 1024, seed + 20)[0])
+        y = torch.empty((M, 1024), dtype=torch.bfloat16, device="cuda")
+        cases.append((h, x, bias, y))
+    st = torch.cuda.Stream()
+
+    def run_all():
+        for h, x, bias, y in cases:
+            rc = L.ep_linear_forward_noalloc(h.ptr, C.c_void_p(x.data_ptr()), x.shape[0], C.c_void_p(bias.data_ptr()),
+                                             C.c_void_p(y.data_ptr()), C.c_void_p(st.cuda_stream))
+            assert rc == 0, L.ep_last_error()
+
+    with torch.cuda.stream(st):
+        run_all()
+    torch.cuda.synchronize()
+    want = [y.clone() for *_, y in cases]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        run_all()
+    for _ in range(3):
+        for *_, y in cases:
+            y.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for (h, x, bias, y), w_ in zip(cases, want):
+            if x.shape[0] <= 4:
+                assert rel_l2(y.float().cpu().numpy(), w_.float().cpu().numpy()) < 1e-3
+            else:
+                assert torch.equal(y, w_), x.shape[0]
+        with torch.cuda.stream(st):                  # eager work between replays
+            torch.matmul(cases[2][1], cases[2][1].T)
+        torch.cuda.synchronize()
+    for h, *_ in cases:
+        h.check()
+        h.release()
