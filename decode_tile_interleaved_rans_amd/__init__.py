@@ -139,6 +139,28 @@ def _stream_ptr(stream=None):
     return C.c_void_p(s.cuda_stream)
 
 
+def _run_on(stream):
+    """(s, other) for a call that runs on `stream` (default: the current stream). With another
+    stream, s first waits for the work queued on the current stream (which produced the inputs);
+    the caller allocates its outputs under torch.cuda.stream(s) and, after the call, marks the
+    input tensors as used on s (_used_on), so that the caching allocator does not hand their
+    memory to other work while s may still read them."""
+    torch = _torch()
+    cur = torch.cuda.current_stream()
+    s = stream if stream is not None else cur
+    other = s.cuda_stream != cur.cuda_stream
+    if other:
+        s.wait_stream(cur)
+    return s, other
+
+
+def _used_on(s, other, *tensors):
+    if other:
+        for t in tensors:
+            if t is not None:
+                t.record_stream(s)
+
+
 # ------------------------------------------------------------------------------------ host side
 def compress(w, target_bpp: float = 4.0, *, mode: int = LOSSY, prob_bits: int = 12, tile_rows: int = 16,
              n_threads: int = 0, dtype: int | None = None, layout: int = 0) -> tuple[bytes, float]:
@@ -296,9 +318,14 @@ class Handle:
         return (out, scale) if scale is not None else out
 
     def decode_symbols(self, stream=None):
+        """Decode the lattice symbols into a new int16 tensor, allocated on the stream the decode
+        runs on."""
         torch = _torch()
-        q = torch.empty(self.shape, dtype=torch.int16, device="cuda")
-        _check(lib().ep_decode_symbols(self._h, C.c_void_p(q.data_ptr()), _stream_ptr(stream)), "ep_decode_symbols")
+        s = stream if stream is not None else torch.cuda.current_stream()
+        with torch.cuda.stream(s):
+            q = torch.empty(self.shape, dtype=torch.int16, device="cuda")
+        _check(lib().ep_decode_symbols(self._h, C.c_void_p(q.data_ptr()), C.c_void_p(s.cuda_stream)),
+               "ep_decode_symbols")
         return q
 
     def check(self, stream=None):
@@ -348,32 +375,41 @@ def decompress_many(handles, outs, scales=None, stream=None):
 
 
 def gemm_bf16(x, w, stream=None):
-    """Y = X W^T in BF16 with fp32 accumulation (the library's own MFMA GEMM)."""
+    """Y = X W^T in BF16 with fp32 accumulation (the library's own MFMA GEMM), on `stream`
+    (default: the current stream; another stream first waits for the current one)."""
     torch = _torch()
     M, K = x.shape
     N = w.shape[0]
     _need(x, "x", torch.bfloat16)
     _need(w, "w", torch.bfloat16, shape=(N, K))
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    s, other = _run_on(stream)
+    with torch.cuda.stream(s):
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _check(lib().ep_gemm_bf16(C.c_void_p(x.data_ptr()), C.c_void_p(w.data_ptr()), M, N, K, C.c_void_p(y.data_ptr()),
-                              _stream_ptr(stream)), "ep_gemm_bf16")
+                              C.c_void_p(s.cuda_stream)), "ep_gemm_bf16")
+    _used_on(s, other, x, w)
     return y
 
 
 def quantize_rows_fp8(x, stream=None):
-    """Per-row FP8 E4M3 codes of BF16 rows and their fp32 scales (x = codes * scale[row])."""
+    """Per-row FP8 E4M3 codes of BF16 rows and their fp32 scales (x = codes * scale[row]), on
+    `stream` (default: the current stream; another stream first waits for the current one)."""
     torch = _torch()
     M, K = x.shape
     _need(x, "x", torch.bfloat16)
-    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-    sc = torch.empty(M, dtype=torch.float32, device=x.device)
+    s, other = _run_on(stream)
+    with torch.cuda.stream(s):
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        sc = torch.empty(M, dtype=torch.float32, device=x.device)
     _check(lib().ep_quantize_rows_fp8(C.c_void_p(x.data_ptr()), M, K, C.c_void_p(q.data_ptr()),
-                                      C.c_void_p(sc.data_ptr()), _stream_ptr(stream)), "ep_quantize_rows_fp8")
+                                      C.c_void_p(sc.data_ptr()), C.c_void_p(s.cuda_stream)), "ep_quantize_rows_fp8")
+    _used_on(s, other, x)
     return q, sc
 
 
 def gemm_fp8(xq, xs, wq, ws, bias=None, stream=None):
-    """Y = diag(xs) Xq Wq^T diag(ws) (+ bias) from E4M3 codes (uint8 tensors), BF16 output."""
+    """Y = diag(xs) Xq Wq^T diag(ws) (+ bias) from E4M3 codes (uint8 tensors), BF16 output, on
+    `stream` (default: the current stream; another stream first waits for the current one)."""
     torch = _torch()
     M, K = xq.shape
     N = wq.shape[0]
@@ -383,11 +419,14 @@ def gemm_fp8(xq, xs, wq, ws, bias=None, stream=None):
     _need(ws, "ws", torch.float32, shape=(N,))
     if bias is not None:
         _need(bias, "bias", torch.bfloat16, shape=(N,))
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    s, other = _run_on(stream)
+    with torch.cuda.stream(s):
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
     bp = C.c_void_p(bias.data_ptr()) if bias is not None else None
     _check(lib().ep_gemm_fp8(C.c_void_p(xq.data_ptr()), C.c_void_p(xs.data_ptr()), C.c_void_p(wq.data_ptr()),
-                             C.c_void_p(ws.data_ptr()), M, N, K, bp, C.c_void_p(y.data_ptr()), _stream_ptr(stream)),
+                             C.c_void_p(ws.data_ptr()), M, N, K, bp, C.c_void_p(y.data_ptr()), C.c_void_p(s.cuda_stream)),
            "ep_gemm_fp8")
+    _used_on(s, other, xq, xs, wq, ws, bias)
     return y
 
 
@@ -463,11 +502,7 @@ class CompressedLinear:
             raise ValueError(f"x is on {x.device}, but the current device is cuda:{torch.cuda.current_device()}")
         if self.bias is not None:
             _need(self.bias, "bias", torch.bfloat16, shape=(self.out_features,))
-        cur = torch.cuda.current_stream()
-        s = stream if stream is not None else cur
-        other = s.cuda_stream != cur.cuda_stream
-        if other:
-            s.wait_stream(cur)
+        s, other = _run_on(stream)
         with torch.cuda.stream(s):
             rows = int(np.prod(shp[:-1], dtype=np.int64))
             x2 = x.reshape(rows, shp[-1]).to(torch.bfloat16).contiguous()
@@ -476,10 +511,7 @@ class CompressedLinear:
             fn = lib().ep_linear_forward_fp8 if self.compute == "fp8" else lib().ep_linear_forward
             _check(fn(self.handle.ptr, C.c_void_p(x2.data_ptr()), x2.shape[0], bp, C.c_void_p(y.data_ptr()),
                       C.c_void_p(s.cuda_stream)), "ep_linear_forward" + ("_fp8" if self.compute == "fp8" else ""))
-        if other:
-            x2.record_stream(s)             # x (or its converted copy) is read on s after this returns
-            if self.bias is not None:
-                self.bias.record_stream(s)
+        _used_on(s, other, x2, self.bias)   # x (or its converted copy) is read on s after this returns
         return y.reshape(*shp[:-1], self.out_features)
 
     __call__ = forward

@@ -178,8 +178,17 @@ struct WsLease {
     hipStream_t stream = nullptr;
     void* ptr = nullptr;
     size_t bytes = 0;
+    bool recorded = false;
     // After the forward's launches are queued: mark the buffer as in use by them.
-    hipError_t queued() { return entry ? hipEventRecord(entry->done, stream) : hipSuccess; }
+    hipError_t queued() {
+        recorded = true;
+        return entry ? hipEventRecord(entry->done, stream) : hipSuccess;
+    }
+    // A forward that stops on an error after some launches were queued still marks the buffer
+    // (before the lock, declared first, is released), so that a later grow waits for them.
+    ~WsLease() {
+        if (entry && !recorded) (void)hipEventRecord(entry->done, stream);
+    }
 };
 
 hipError_t ws_acquire(int device, hipStream_t stream, size_t need, WsLease* L) {
@@ -302,7 +311,8 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
     if (M < 0) return fail(EP_EINVAL, "negative M");
     if (M == 0 || N == 0) return EP_OK;
     if (!dev_y || (K > 0 && !dev_x)) return fail(EP_EINVAL, "null pointer");
-    if (K % 8 || M > INT32_MAX) return fail(EP_EINVAL, "in_features must be a multiple of 8");
+    if (M > INT32_MAX || N > INT32_MAX) return fail(EP_ERANGE, "M and out_features must be below 2^31");
+    if (K % 8) return fail(EP_EINVAL, "in_features must be a multiple of 8");
     if (reinterpret_cast<uintptr_t>(dev_x) & 15) return fail(EP_EINVAL, "X must be 16-byte aligned");
     int dev = 0;
     hipError_t he = hipGetDevice(&dev);
@@ -578,7 +588,8 @@ ep_status ep_gemm_bf16(const void* dev_x, const void* dev_w, int64_t M, int64_t 
         if (M < 0 || N < 0 || K < 0) return fail(EP_EINVAL, "negative size");
         if (M == 0 || N == 0) return EP_OK;
         if (!dev_x || !dev_w || !dev_y) return fail(EP_EINVAL, "null pointer");
-        if (K % 8 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(EP_EINVAL, "K must be a multiple of 8");
+        if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(EP_ERANGE, "M, N and K must be below 2^31");
+        if (K % 8) return fail(EP_EINVAL, "K must be a multiple of 8");
         if ((reinterpret_cast<uintptr_t>(dev_x) | reinterpret_cast<uintptr_t>(dev_w)) & 15)
             return fail(EP_EINVAL, "X and W must be 16-byte aligned");
         ep::GemmArgs g{static_cast<const uint16_t*>(dev_x), static_cast<const uint16_t*>(dev_w), nullptr,
@@ -654,7 +665,8 @@ ep_status ep_quantize_rows_fp8(const void* dev_x, int64_t M, int64_t K, uint8_t*
         if (M < 0 || K < 0) return fail(EP_EINVAL, "negative size");
         if (M == 0) return EP_OK;
         if (!dev_x || !dev_q || !dev_scale) return fail(EP_EINVAL, "null pointer");
-        if (K % 16 || M > INT32_MAX || K > INT32_MAX) return fail(EP_EINVAL, "K must be a multiple of 16");
+        if (M > INT32_MAX || K > INT32_MAX) return fail(EP_ERANGE, "M and K must be below 2^31");
+        if (K % 16) return fail(EP_EINVAL, "K must be a multiple of 16");
         if ((reinterpret_cast<uintptr_t>(dev_x) | reinterpret_cast<uintptr_t>(dev_q)) & 15)
             return fail(EP_EINVAL, "X and Q must be 16-byte aligned");
         hipError_t e = ep::launch_quantize_rows_f8(static_cast<const uint16_t*>(dev_x), (int)M, (int)K, (int)K, dev_q,
@@ -669,7 +681,8 @@ ep_status ep_gemm_fp8(const uint8_t* dev_xq, const float* dev_xs, const uint8_t*
         if (M < 0 || N < 0 || K < 0) return fail(EP_EINVAL, "negative size");
         if (M == 0 || N == 0) return EP_OK;
         if (!dev_xq || !dev_xs || !dev_wq || !dev_ws || !dev_y) return fail(EP_EINVAL, "null pointer");
-        if (K % 16 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(EP_EINVAL, "K must be a multiple of 16");
+        if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(EP_ERANGE, "M, N and K must be below 2^31");
+        if (K % 16) return fail(EP_EINVAL, "K must be a multiple of 16");
         if ((reinterpret_cast<uintptr_t>(dev_xq) | reinterpret_cast<uintptr_t>(dev_wq)) & 15)
             return fail(EP_EINVAL, "X and W codes must be 16-byte aligned");
         ep::GemmF8Args g{dev_xq, dev_xs, dev_wq, dev_ws, static_cast<const uint16_t*>(dev_bias), static_cast<uint16_t*>(dev_y),
@@ -704,7 +717,8 @@ ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M
         if (M < 0) return fail(EP_EINVAL, "negative M");
         if (M == 0 || N == 0) return EP_OK;
         if (!dev_y || (K > 0 && !dev_x)) return fail(EP_EINVAL, "null pointer");
-        if (K % 16 || M > INT32_MAX) return fail(EP_EINVAL, "in_features must be a multiple of 16 for the FP8 forward");
+        if (M > INT32_MAX || N > INT32_MAX) return fail(EP_ERANGE, "M and out_features must be below 2^31");
+        if (K % 16) return fail(EP_EINVAL, "in_features must be a multiple of 16 for the FP8 forward");
         if (reinterpret_cast<uintptr_t>(dev_x) & 15) return fail(EP_EINVAL, "X must be 16-byte aligned");
         hipStream_t s = static_cast<hipStream_t>(hip_stream);
         int dev = 0;

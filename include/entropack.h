@@ -217,8 +217,8 @@ ep_status ep_decode_symbols(const ep_handle* h, int16_t* dev_q, void* hip_stream
  * streams get different workspaces; it is allocated on first use
  * (hipMalloc, which may synchronize the device) and kept until the process ends.
  *   dev_x: [M][K] bf16, 16-byte aligned (may be NULL when K == 0); dev_bias: [N] bf16 or NULL;
- * dev_y: [M][N] bf16. K == 0 gives Y = bias (or zeros). Requires a lossy stream and K % 8 == 0.
- * Asynchronous on hip_stream. */
+ * dev_y: [M][N] bf16. K == 0 gives Y = bias (or zeros). Requires a lossy stream and K % 8 == 0
+ * (EP_EINVAL); M and N below 2^31 (EP_ERANGE). Asynchronous on hip_stream. */
 ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias,
                             void* dev_y, void* hip_stream);
 
@@ -244,7 +244,8 @@ ep_status ep_linear_forward_noalloc(const ep_handle* w, const void* dev_x, int64
  * compressed copy on the same input): the uncompressed baseline of the compressed forward.
  * Plain BF16 GEMM, the one ep_linear_forward runs on each decoded slice, for overhead
  * comparisons: Y[M][N] = X[M][K] * W^T, X [M][K] bf16, W [N][K] bf16, Y [M][N] bf16, fp32
- * accumulation. Requires K % 8 == 0 and 16-byte aligned X and W. Asynchronous on hip_stream. */
+ * accumulation. Requires K % 8 == 0 and 16-byte aligned X and W (EP_EINVAL); M, N and K below
+ * 2^31 (EP_ERANGE). Asynchronous on hip_stream. */
 ep_status ep_gemm_bf16(const void* dev_x, const void* dev_w, int64_t M, int64_t N, int64_t K,
                        void* dev_y, void* hip_stream);
 
@@ -260,7 +261,8 @@ ep_status ep_gemm_bf16(const void* dev_x, const void* dev_w, int64_t M, int64_t 
  * ep_linear_forward); otherwise the weight is decoded slice by slice into the workspace and
  * multiplied by the FP8 GEMM. Same workspace rules as ep_linear_forward. dev_x: [M][K] bf16, 16-byte aligned,
  * finite (may be NULL when K == 0); dev_bias: [N] bf16 or NULL; dev_y: [M][N] bf16. K == 0 gives
- * Y = bias (or zeros). Requires a lossy stream and K % 16 == 0. Asynchronous on hip_stream. */
+ * Y = bias (or zeros). Requires a lossy stream and K % 16 == 0 (EP_EINVAL); M and N below 2^31
+ * (EP_ERANGE). Asynchronous on hip_stream. */
 ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias,
                                 void* dev_y, void* hip_stream);
 
@@ -270,7 +272,8 @@ ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M
  * amax = max |x| over the row (raised to 2^-100 when smaller, unless zero), scale = amax / 448,
  * code = E4M3(x * (448 / amax)) rounded to nearest even and saturated at +-448; a zero row gets
  * scale 0 and codes 0. dev_x: [M][K] bf16 (finite), dev_q: [M][K] codes, dev_scale: [M] fp32;
- * K % 16 == 0, dev_x and dev_q 16-byte aligned. Asynchronous on hip_stream. */
+ * K % 16 == 0, dev_x and dev_q 16-byte aligned (EP_EINVAL); M and K below 2^31 (EP_ERANGE).
+ * Asynchronous on hip_stream. */
 ep_status ep_quantize_rows_fp8(const void* dev_x, int64_t M, int64_t K, uint8_t* dev_q, float* dev_scale,
                                void* hip_stream);
 
@@ -283,7 +286,8 @@ ep_status ep_quantize_rows_fp8(const void* dev_x, int64_t M, int64_t K, uint8_t*
  * hipBLASLt's from 512 rows, and from 256 when N <= 4096 or K <= 2048 (the row scales as its
  * outer-vector scales; 32 MiB of workspace from the (device, hip_stream) pool, see
  * ep_linear_forward), else, or when it offers no algorithm, the library's own kernel; both
- * deterministic. Requires K % 16 == 0. Asynchronous on hip_stream. */
+ * deterministic. Requires K % 16 == 0 (EP_EINVAL); M, N and K below 2^31 (EP_ERANGE).
+ * Asynchronous on hip_stream. */
 ep_status ep_gemm_fp8(const uint8_t* dev_xq, const float* dev_xs, const uint8_t* dev_wq, const float* dev_ws,
                       int64_t M, int64_t N, int64_t K, const void* dev_bias, void* dev_y, void* hip_stream);
 

@@ -420,6 +420,39 @@ def test_forward_on_a_side_stream_with_fp32_input():
     assert rel_l2(y.float().cpu().numpy(), ref) < 2e-2
 
 
+def test_helpers_on_a_side_stream_match_the_current_stream():
+    """gemm_bf16, quantize_rows_fp8, gemm_fp8 and decode_symbols with an explicit side stream:
+    the side stream waits for the producer of the inputs (queued on the current stream just
+    before), the outputs are allocated on it, and the results are the bits of the same calls on
+    the current stream (every one of these kernels is deterministic)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8)
+    a = torch.randn(300, 1040, generator=g, device="cuda")
+    wf = torch.randn(520, 1040, generator=g, device="cuda")
+    s, _ = ep.compress(W.student_t(256, 1024, seed=62), 4.0, dtype=ep.BF16)
+    h = ep.upload(s)
+    side = torch.cuda.Stream()
+    results = []
+    for stream in (None, side):
+        x = (a * 0.5).to(torch.bfloat16)            # produced on the current stream right before the calls
+        w = (wf * 0.25).to(torch.bfloat16)
+        y = ep.gemm_bf16(x, w, stream=stream)
+        xq, xs = ep.quantize_rows_fp8(x, stream=stream)
+        wq, ws = ep.quantize_rows_fp8(w, stream=stream)
+        y8 = ep.gemm_fp8(xq, xs, wq, ws, stream=stream)
+        q = h.decode_symbols(stream=stream)
+        del x, w                                     # the allocator must not reuse them while `side` reads
+        if stream is not None:
+            stream.synchronize()
+        torch.cuda.synchronize()
+        results.append((y, xq, xs, y8, q))
+    h.check()
+    for u, v in zip(*results):
+        assert torch.equal(u, v)
+    qo, _ = oracle.decode_symbols(s)
+    assert np.array_equal(results[1][4].cpu().numpy(), qo)
+
+
 def test_matrix_vector_and_gemm_paths_agree():
     """M <= 4 multiplies the unrounded fp32 weights inside the decode (fp32 atomics), M >= 5 the
     BF16-rounded weights in the GEMM: the same rows computed both ways stay within the BF16

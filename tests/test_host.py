@@ -306,8 +306,8 @@ def test_load_rejects_a_damaged_file(tmp_path):
 
 
 def test_new_entry_points_reject_bad_arguments_before_any_device_work():
-    """Argument checks of the FP8 forward, the quantizer, the FP8 GEMM and the device encoder
-    return EP_EINVAL / EP_EUNSUPPORTED / EP_ERANGE without touching a device."""
+    """Argument checks of the FP8 forward, the quantizer, the BF16 and FP8 GEMMs and the device
+    encoder return EP_EINVAL / EP_EUNSUPPORTED / EP_ERANGE without touching a device."""
     import ctypes as C
     L = ep.lib()
     out = C.POINTER(C.c_uint8)()
@@ -318,6 +318,11 @@ def test_new_entry_points_reject_bad_arguments_before_any_device_work():
     assert L.ep_gemm_fp8(C.c_void_p(16), C.c_void_p(16), C.c_void_p(16), C.c_void_p(16), 4, 4, 24, None,
                          C.c_void_p(16), None) == -1                                  # K % 16
     assert L.ep_gemm_fp8(None, None, None, None, 0, 4, 16, None, None, None) == 0    # empty: nothing to do
+    p16 = C.c_void_p(16)
+    assert L.ep_gemm_fp8(p16, p16, p16, p16, 4, 1 << 31, 16, None, p16, None) == -4  # N past 32-bit sizes
+    assert L.ep_quantize_rows_fp8(p16, 1 << 31, 32, p16, p16, None) == -4           # M past 32-bit sizes
+    assert L.ep_gemm_bf16(p16, p16, 4, 4, 12, p16, None) == -1                      # K % 8
+    assert L.ep_gemm_bf16(p16, p16, 1 << 31, 4, 16, p16, None) == -4                # M past 32-bit sizes
     assert L.ep_compress_device(None, ep.F32, 4, 4, None, None, C.byref(out), C.byref(n), None) == -1
     opts = ep.EncodeOpts(ep.LOSSLESS, 0.0, 12, 16, 0)
     assert L.ep_compress_device(C.c_void_p(16), ep.BF16, 4, 4, C.byref(opts), None, C.byref(out), C.byref(n),
