@@ -185,6 +185,12 @@ ep_status parse_stream(const uint8_t* s, size_t len, StreamView* v, std::string*
             float sc = rf32(s + v->off_scale + 4 * r);
             if (!(std::isfinite(sc) && sc >= 0.0f)) return bad(why, "row scale not finite and >= 0");
         }
+    // an intact stream wider than the encoders write (they refuse cols >= 2^28): the decode
+    // kernels address an output row through a buffer resource of cols x element bytes (< 2^31)
+    if (v->cols >= (1ll << 28)) {
+        if (why) *why = "stream with 2^28 or more columns (beyond the supported width)";
+        return EP_ERANGE;
+    }
     return EP_OK;
 }
 

@@ -140,7 +140,8 @@ void ep_free(void* p);
  * Validate a host stream (magic, format version 2, section bounds, every table summing to 2^n,
  * tile offsets, and three CRC-32s: the payload's, the raw plane's and the metadata's, which
  * covers every other byte, so any single-bit corruption is refused) and summarize it. Host only;
- * no device work. EP_ECORRUPT on any inconsistency. */
+ * no device work. EP_ECORRUPT on any inconsistency; EP_ERANGE for an intact stream of 2^28 or more
+ * columns (wider than the encoders write and the decoders address). */
 ep_status ep_stream_info(const uint8_t* host_stream, size_t len, ep_info* out);
 
 /* Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", sections
@@ -149,9 +150,9 @@ ep_status ep_stream_info(const uint8_t* host_stream, size_t len, ep_info* out);
  * inference call); reading R22.
  * Validate a host stream and copy it to the current device together with its decode tables.
  * Synchronizes hip_stream before returning (the host buffer may be freed afterwards).
- * *out receives the handle. Errors: EP_ECORRUPT, EP_ERANGE (a tile payload of 4 GiB or more,
- * beyond the decoder's 32-bit payload addressing: code such a matrix as several streams),
- * EP_ENOMEM, EP_EHIP. */
+ * *out receives the handle. Errors: EP_ECORRUPT, EP_ERANGE (2^28 or more columns, or a tile
+ * payload of 4 GiB or more, beyond the decoder's 32-bit payload addressing: code such a matrix as
+ * several streams), EP_ENOMEM, EP_EHIP. */
 ep_status ep_upload(const uint8_t* host_stream, size_t len, void* hip_stream, ep_handle** out);
 
 /* Summary of an uploaded stream (same fields as ep_stream_info).

@@ -253,6 +253,45 @@ def test_validation_errors():
     assert info["n_tiles"] == 8
 
 
+def wide_lossless_u8_stream(cols: int) -> bytes:
+    """An intact one-row lossless U8 stream of `cols` columns with an all-zero payload (every tile
+    holding just its 32 states), put together from a small encoder-written stream: the shape,
+    section offsets, tile index and both CRC-32s rewritten (the validator does not decode)."""
+    import zlib
+    base, _ = ep.lossless_compress(np.zeros((1, 256), np.uint8))
+    r64 = lambda o: int.from_bytes(base[o:o + 8], "little")
+    off_tables, off_index = r64(56), r64(64)
+    tables = base[off_tables:off_index]
+    n_tiles = -(-cols // 256)
+    index = (np.arange(n_tiles + 1, dtype=np.uint32) * 32).tobytes()
+    off_payload = -(-(off_index + len(index)) // 16) * 16
+    payload = bytes(128 * n_tiles)
+    total = off_payload + len(payload)
+    h = bytearray(base[:128])
+    h[12:16] = cols.to_bytes(4, "little")
+    h[32:36] = n_tiles.to_bytes(4, "little")
+    h[64:72] = off_index.to_bytes(8, "little")
+    h[72:80] = off_payload.to_bytes(8, "little")
+    h[80:88] = total.to_bytes(8, "little")
+    h[88:92] = zlib.crc32(payload).to_bytes(4, "little")
+    body = bytes(h[:off_tables]) + tables + index + bytes(off_payload - off_index - len(index))
+    meta = zlib.crc32(body[:112] + body[116:])
+    body = body[:112] + meta.to_bytes(4, "little") + body[116:]
+    return body + payload
+
+
+def test_stream_wider_than_the_encoders_write_is_refused():
+    """The encoders refuse 2^28 or more columns (the decode kernels address an output row with 32-bit
+    byte offsets); an intact stream that wide is refused by the validator with EP_ERANGE, and one
+    tile narrower passes (so the refusal is the width rule, not a flaw of the constructed stream)."""
+    ok = wide_lossless_u8_stream((1 << 28) - 256)
+    assert ep.stream_info(ok)["cols"] == (1 << 28) - 256
+    del ok
+    with pytest.raises(ep.EPError) as e:
+        ep.stream_info(wide_lossless_u8_stream(1 << 28))
+    assert e.value.status == -4
+
+
 def test_bad_arguments():
     w = np.zeros((4, 4), np.float32)
     with pytest.raises(ep.EPError) as e:
