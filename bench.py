@@ -209,7 +209,8 @@ def fused_gemm_section(torch, ep, reps: int = 15):
            "reps": reps, "timing": "median of per-rep HIP events, the five variants interleaved within each "
                                    "rep, 1 GiB cache flush before every timed call"}
     # plain FP8 baseline: ep.gemm_fp8 on the weight and activations pre-quantized per row
-    # (hipBLASLt from 512 rows, or 256 when N <= 4096 or K <= 2048; the library's own kernel else)
+    # (hipBLASLt from 512 rows, above 64 when K <= 4096, from 256 when N <= 4096; the library's own
+    # kernel else)
     wq, ws = ep.quantize_rows_fp8(Wt)
     for M in (4096, 256, 64, 32, 16, 4, 1):
         X = Xf[:M].contiguous()
@@ -248,7 +249,7 @@ def fused_gemm_section(torch, ep, reps: int = 15):
     return out
 
 
-def dit_forward_section(torch, ep, tokens=(4096, 16), reps: int = 3):
+def dit_forward_section(torch, ep, tokens=(4096, 256, 16), reps: int = 3):
     """The DiT-like model's 150 linear layers as compressed layers (coded as
     CompressedLinear.from_linear codes layers: row tile layout, prob_bits 11, 4.0 bpp target; the
     same GPU-drawn weights as the headline step), their forwards in model order at M tokens

@@ -439,8 +439,8 @@ class CompressedLinear:
     MFMA and the weight is never written; a layout-0 stream is fused that way through LDS for 5 to
     16 rows and by the decode kernel's own products for up to 4. For more rows the weight is decoded
     once per call into scratch slices that stay in the Infinity Cache, and a BF16 MFMA GEMM reads
-    them from there (hipBLASLt's from 512 rows, or from 256 when out_features <= 4096 or in_features
-    <= 2048; else the library's own).
+    them from there (hipBLASLt's from 512 rows, above 64 when in_features <= 4096, from 256 when
+    out_features <= 4096; else the library's own).
     compute="fp8": the weight is decoded to FP8 E4M3 with its row scales and the activations are
     quantized per row; the codes meet in the FP8 MFMA, fused in the same cases, else on slices.
 

@@ -284,15 +284,16 @@ ep_status take_static(size_t need, WsLease* L) {
 }
 
 // Whether an M x N x K product of a decoded slice (or the plain FP8 GEMM) goes to hipBLASLt rather
-// than the library's own kernel: from 512 rows always, and from 256 rows when the own kernel's
-// 256 x 256 tiles need split-K to fill the CUs and its partial sums outweigh the work (N <= 4096)
-// or K is short (K <= 2048). Measured on nine layer shapes from 2048^2 to 8192^2: at 512 and 768
-// rows hipBLASLt cuts the summed forward time by 14% and 22%; at 256 and 384 rows it is 6-20%
-// faster on the shapes this rule sends to it and within noise on the other two (8192 x 4096,
-// 8192^2), where below 256 rows, or at 256 with both N > 4096 and K > 2048, the own kernel is as
-// fast or faster (8192^2 at 256 rows: 88 against 102 us). Every repeat gave the same bits.
+// than the library's own kernel: from 512 rows always; above the fused kernel's 64 rows when K is
+// at most 4096 (the own kernel's split-K only pays on long K); from 256 rows when N <= 4096 (its
+// 256 x 256 tiles then need split-K to fill the CUs). Measured as whole forwards on 13 layer
+// shapes (2048^2 ... 8192^2 and the DiT-like 11520 x 3840, 10240 x 3840, 3840 x 10240, 3840^2):
+// at 512 and 768 rows hipBLASLt cuts the summed time by 14% and 22%; from 65 to 384 rows the
+// K <= 4096 part cuts it by 4-9% (BF16) and 1-5% (FP8), e.g. 11520 x 3840 at 128 rows 124 -> 99 us;
+// the own kernel stays faster on long K with few rows (8192^2 at 256 rows: 88 against 102 us,
+// 4096 x 16384 at 128 rows: 97 against 121 us). Every repeat gave the same bits.
 bool use_gemm_library(int64_t M, int64_t N, int64_t K) {
-    return M >= 512 || (M >= 256 && (N <= 4096 || K <= 2048));
+    return M >= 512 || (M > 64 && K <= 4096) || (M >= 256 && N <= 4096);
 }
 
 // Compressed linear forward. The weight is decoded once per call, one slice of output rows at a

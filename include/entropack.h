@@ -210,7 +210,7 @@ ep_status ep_decode_symbols(const ep_handle* h, int16_t* dev_q, void* hip_stream
  *     differ in the last bits);
  *   - otherwise the weight is decoded once per call, up to 128 MiB of BF16 rows at a time, into
  *     the workspace, which stays in the Infinity Cache, and each slice is multiplied by the BF16
- *     MFMA GEMM: hipBLASLt's from 512 rows, and from 256 when N <= 4096 or K <= 2048 (faster
+ *     MFMA GEMM: hipBLASLt's from 512 rows, above 64 when K <= 4096, from 256 when N <= 4096 (faster
  *     there; its handle is created on the device's first such call), else the library's own; both
  *     deterministic (tested); no decoded copy of W outlives the call.
  * The fused and slice paths multiply the same BF16-rounded weights. The workspace belongs
@@ -284,7 +284,7 @@ ep_status ep_quantize_rows_fp8(const void* dev_x, int64_t M, int64_t K, uint8_t*
  * Plain FP8 GEMM, the one ep_linear_forward_fp8 runs on each decoded slice, for overhead
  * comparisons: Y[m][n] = xs[m] ws[n] sum_k xq[m][k] wq[n][k] (+ bias[n]); xq [M][K] and wq [N][K]
  * E4M3 codes (16-byte aligned), xs [M] and ws [N] fp32, bias [N] bf16 or NULL, Y [M][N] bf16.
- * hipBLASLt's from 512 rows, and from 256 when N <= 4096 or K <= 2048 (the row scales as its
+ * hipBLASLt's from 512 rows, above 64 when K <= 4096, from 256 when N <= 4096 (the row scales as its
  * outer-vector scales; 32 MiB of workspace from the (device, hip_stream) pool, see
  * ep_linear_forward), else, or when it offers no algorithm, the library's own kernel; both
  * deterministic. Requires K % 16 == 0 (EP_EINVAL); M, N and K below 2^31 (EP_ERANGE).

@@ -251,7 +251,7 @@ def test_quantize_rows_fp8_matches_oracle(M, K):
 # shapes cover every FP8 tile choice: 64 x 32 tiles for M <= 64, 64 x 64, 128 x 128 (2 x 256 of them
 # or more) and 256 x 256 (256 or more), with ragged M and N and K not a multiple of the 128 K step
 # (2000, 4000, 144), (4100, 4000, 272), (1024, 1000, 2064), (600, 520, 1040) and (300, 1000, 784) go
-# to hipBLASLt (512 rows and more, or 256 and more with N <= 4096 or K <= 2048)
+# to hipBLASLt (512 rows and more, more than 64 with K <= 4096, or 256 and more with N <= 4096)
 @pytest.mark.parametrize("M,N,K", [(16, 256, 512), (64, 4100, 1040), (300, 1000, 784), (1, 8, 16),
                                    (2000, 4000, 144), (4100, 4000, 272), (33, 17, 4112), (1024, 1000, 2064),
                                    (600, 520, 1040)])
