@@ -45,7 +45,22 @@ namespace ep {
 namespace {
 
 // ----------------------------------------------------------------------------- stores
-// Decoded coordinates are carried as fp32 values (exact: |q| < 2^17).
+// Decoded coordinates are carried as fp32 values (exact: |q| < 2^17) for the floating-point
+// containers and as int32 (the bit pattern kept in the same float slot) for INT8 and the raw
+// coordinates, which then need no conversion to float and back.
+template <int CT>
+constexpr bool int_coords() { return CT == CT_I8 || CT == CT_Q16; }
+template <int CT>
+__device__ __forceinline__ float coord_of(int32_t q) {
+    if constexpr (int_coords<CT>()) return __int_as_float(q);
+    else return (float)q;
+}
+// The value field of a table entry (the doubled coordinate in the high half) as a coordinate.
+template <int CT>
+__device__ __forceinline__ float coord_of_entry(uint32_t ey) {
+    if constexpr (int_coords<CT>()) return __int_as_float((int32_t)ey >> 16);
+    else return hi16_to_f32(ey);
+}
 template <int CT>
 struct Conv;
 template <>
@@ -68,7 +83,7 @@ struct Conv<CT_I8> {
     // round-half-away(q / k) = floor((2|q| + k) / 2k), by a multiply with ceil(2^32 / 2k); exact
     // because (2|q| + k) * 2k < 2^32.
     __device__ static uint32_t f(float qf, float, float, uint32_t k, uint32_t magic) {
-        const int32_t q = (int32_t)qf;
+        const int32_t q = __float_as_int(qf);
         const uint32_t a = (uint32_t)(q < 0 ? -q : q);
         const int32_t v = (int32_t)__umulhi(2u * a + k, magic);
         return (uint32_t)(uint8_t)(int8_t)(q < 0 ? -v : v);
@@ -77,7 +92,7 @@ struct Conv<CT_I8> {
 template <>
 struct Conv<CT_Q16> {
     using T = uint16_t;
-    __device__ static uint32_t f(float q, float, float, uint32_t, uint32_t) { return (uint32_t)(uint16_t)(int16_t)(int32_t)q; }
+    __device__ static uint32_t f(float q, float, float, uint32_t, uint32_t) { return (uint32_t)(uint16_t)__float_as_int(q); }
 };
 
 // The 8 container values of one block.
@@ -105,6 +120,15 @@ __device__ __forceinline__ void convert_block(const float* q, float alpha, float
             const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
             v[j] = pk & 0xFFu;
             v[j + 1] = (pk >> 8) & 0xFFu;
+        }
+    } else if constexpr (CT == CT_I8) {
+        if (k == 1) {
+            // the row's largest |q| is at most 127: the INT8 value is the coordinate itself
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = (uint32_t)__float_as_int(q[j]) & 0xFFu;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = Conv<CT>::f(q[j], alpha, h, k, magic);
         }
     } else {
 #pragma unroll
@@ -299,7 +323,7 @@ __device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Til
             rans_steps<N, C>(t, (2 * j) << N, base, ent_j, e);
             refill_all<C>(t);
 #pragma unroll
-            for (int c = 0; c < C; ++c) q[c][j] = hi16_to_f32(e[c].y);
+            for (int c = 0; c < C; ++c) q[c][j] = coord_of_entry<CT>(e[c].y);
             if ((M.esc_tables >> (2 * j)) & 3u) {
                 bool esc[C];
                 uint64_t any = 0;
@@ -314,7 +338,7 @@ __device__ __forceinline__ void lossy_run(const MatDesc& M, const Tables& T, Til
                         const uint32_t w = take_words(t[c], esc[c]);
                         // the doubled coordinate is an int16 on every path (table values
                         // wrap the same way when the tables are built)
-                        if (esc[c]) q[c][j] = (float)(int32_t)(int16_t)(2 * (int32_t)(int16_t)w + b[c]);
+                        if (esc[c]) q[c][j] = coord_of<CT>((int32_t)(int16_t)(2 * (int32_t)(int16_t)w + b[c]));
                     }
                 }
             }
