@@ -321,23 +321,23 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
     WsLease ws;
     if (K == 0 || (M <= 4 && w->view.layout == 0)) {
         // a few activation rows: decoding fused with the matrix-vector products, the weight never
-        // written out; fp32 accumulation in the scratch, then rounding (+ bias) to BF16 (also the
-        // empty product of in_features 0)
-        const size_t need = sizeof(float) * (size_t)M * (size_t)N;
+        // written out; fp32 partial sums per tile pair column in the scratch, then their sum in
+        // column order, rounded (+ bias) to BF16 (also the empty product of in_features 0)
+        const int64_t pcs = K > 0 ? (int64_t)((w->view.tiles_c + 1) / 2) : 0;
+        const size_t need = std::max<size_t>(256, sizeof(float) * (size_t)pcs * (size_t)M * (size_t)N);
         if (fixed) {
             if (ep_status st = take_static(need, &ws); st != EP_OK) return st;
         } else if ((he = ws_acquire(dev, s, need, &ws)) != hipSuccess) {
             return hip_fail(he, "hipMalloc for the linear forward workspace");
         }
-        float* yacc = static_cast<float*>(ws.ptr);
-        ep::MatDesc d = desc_for(w, M == 1 ? ep::CT_GEMV1 : M == 2 ? ep::CT_GEMV2 : ep::CT_GEMV4, yacc, nullptr);
+        float* part = static_cast<float*>(ws.ptr);
+        ep::MatDesc d = desc_for(w, M == 1 ? ep::CT_GEMV1 : M == 2 ? ep::CT_GEMV2 : ep::CT_GEMV4, part, nullptr);
         d.gemv_x = static_cast<const uint16_t*>(dev_x);
         d.gemv_m = (uint8_t)M;
-        hipError_t e = ep::launch_gemv_zero(yacc, M * N, s);
-        // in_features 0: an empty sum, Y = bias (or zeros)
-        if (e == hipSuccess && K > 0) e = ep::launch_gemv(d, s);
+        hipError_t e = pcs > 0 ? ep::launch_gemv(d, s) : hipSuccess;
         if (e == hipSuccess)
-            e = ep::launch_gemv_finish(yacc, static_cast<const uint16_t*>(dev_bias), static_cast<uint16_t*>(dev_y), M, N, s);
+            e = ep::launch_gemv_finish(part, pcs, static_cast<const uint16_t*>(dev_bias), static_cast<uint16_t*>(dev_y), M,
+                                       N, s);
         if (e == hipSuccess) e = ws.queued();
         return e == hipSuccess ? EP_OK : hip_fail(e, "fused matrix-vector launch");
     }
@@ -727,14 +727,8 @@ ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M
         if (we != hipSuccess) return hip_fail(we, "hipGetDevice");
         if (K == 0) {
             // in_features 0: an empty sum, Y = bias (or zeros)
-            WsLease ws;
-            if ((we = ws_acquire(dev, s, sizeof(float) * (size_t)M * (size_t)N, &ws)) != hipSuccess)
-                return hip_fail(we, "hipMalloc for the linear forward workspace");
-            float* yacc = static_cast<float*>(ws.ptr);
-            hipError_t e = ep::launch_gemv_zero(yacc, M * N, s);
-            if (e == hipSuccess)
-                e = ep::launch_gemv_finish(yacc, static_cast<const uint16_t*>(dev_bias), static_cast<uint16_t*>(dev_y), M, N, s);
-            if (e == hipSuccess) e = ws.queued();
+            const hipError_t e = ep::launch_gemv_finish(nullptr, 0, static_cast<const uint16_t*>(dev_bias),
+                                                        static_cast<uint16_t*>(dev_y), M, N, s);
             return e == hipSuccess ? EP_OK : hip_fail(e, "empty product launch");
         }
         if (const ep::MatDesc d = desc_for(w, ep::CT_F8E4M3, nullptr, nullptr); ep::fused_fits(d, M)) {

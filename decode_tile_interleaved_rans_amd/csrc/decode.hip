@@ -232,25 +232,38 @@ __device__ __forceinline__ void store_row(const MatDesc& M, const Tile& t, const
                 M.scale_out[row] = CT == CT_F8E4M3 ? P.sc_l : alpha * (float)P.k_l;
         }
     } else if constexpr (gemv_rows(CT) > 0) {
-        // fused matrix-vector product: the row's dot products with every activation row, summed
-        // over the wave (both tiles of the pair cover the same rows) and added to Y by lane 63
+        // fused matrix-vector product: the row's BF16 weights bf16(q alpha_r), the values the
+        // decode stores (so the products are those of the GEMM path, each exact in fp32), times
+        // every activation row, summed over the wave (both tiles of the pair cover the same row);
+        // lane 63 stores the pair's partial sum, and the finishing kernel adds a row's partials in
+        // pair order, so the result does not depend on the schedule
         constexpr int MT = gemv_rows(CT);
         const uint32_t row = P.row0 + rr;
         const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, P.sc_l), rr));
         if (row >= M.rows) return;
         const float alpha = h * sc;
+        float w[8];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+            f32x2 p = {materialize(q[j] * alpha), materialize(q[j + 1] * alpha)};
+            const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+            w[j] = __uint_as_float(pk << 16);
+            w[j + 1] = __uint_as_float(pk & 0xFFFF0000u);
+        }
         float s[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             float acc = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc += P.xv[m][i] * q[i];
-            s[m] = wave_sum_to_lane63(acc * alpha);
+            for (int i = 0; i < 8; ++i) acc += P.xv[m][i] * w[i];
+            s[m] = wave_sum_to_lane63(acc);
         }
         if ((threadIdx.x & 63) == 63) {
+            // partials [pair column][m][row]; lane 63 holds the pair's odd tile, tc = 2 pc + 1
+            float* part = static_cast<float*>(M.out) + (size_t)(P.tc >> 1) * M.gemv_m * M.rows + row;
 #pragma unroll
             for (int m = 0; m < MT; ++m)
-                if (m < M.gemv_m) atomicAdd(static_cast<float*>(M.out) + (size_t)m * M.rows + row, s[m]);
+                if (m < M.gemv_m) part[(size_t)m * M.rows] = s[m];
         }
     } else {
         const uint32_t row = P.row0 + rr;
@@ -596,16 +609,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_group_rows(GroupArgs g) { 
 template <int CT>
 __global__ __launch_bounds__(64 * kWaves) void decode_gemv(GroupArgs g) { group_body<CT>(g); }
 
-__global__ __launch_bounds__(256) void gemv_zero(float* y, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) y[i] = 0.0f;
-}
-
-__global__ __launch_bounds__(256) void gemv_finish(const float* yacc, const uint16_t* bias, uint16_t* y, int64_t M,
-                                                   int64_t N) {
+// Y [M][N] bf16 = the sum, in pair-column order, of the partials [pcs][M][N] (+ bias [N] bf16),
+// rounded to nearest even; pcs = 0 (an empty product) gives the bias or zeros.
+__global__ __launch_bounds__(256) void gemv_finish(const float* part, int64_t pcs, const uint16_t* bias, uint16_t* y,
+                                                   int64_t M, int64_t N) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= M * N) return;
-    float v = yacc[i];
+    float v = 0.0f;
+    for (int64_t p = 0; p < pcs; ++p) v += part[p * M * N + i];
     if (bias) v += __uint_as_float((uint32_t)bias[i % N] << 16);
     y[i] = (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v, 0.0f}, bf16x2)) & 0xFFFFu);
 }
@@ -705,19 +716,12 @@ hipError_t launch_gemv(const MatDesc& m, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_gemv_zero(float* yacc, int64_t n, hipStream_t stream) {
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(gemv_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, yacc, n);
-    return hipGetLastError();
-}
-
-hipError_t launch_gemv_finish(const float* yacc, const uint16_t* bias, uint16_t* y, int64_t M, int64_t N,
-                              hipStream_t stream) {
+hipError_t launch_gemv_finish(const float* part, int64_t pcs, const uint16_t* bias, uint16_t* y, int64_t M,
+                              int64_t N, hipStream_t stream) {
     if (M * N <= 0) return hipSuccess;
-    hipLaunchKernelGGL(gemv_finish, dim3((unsigned)((M * N + 255) / 256)), dim3(256), 0, stream, yacc, bias, y, M, N);
+    hipLaunchKernelGGL(gemv_finish, dim3((unsigned)((M * N + 255) / 256)), dim3(256), 0, stream, part, pcs, bias, y,
+                       M, N);
     return hipGetLastError();
 }
-
-
 
 }  // namespace ep

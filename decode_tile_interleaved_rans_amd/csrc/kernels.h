@@ -10,7 +10,7 @@ namespace ep {
 // container codes (the first four equal the ep_dtype values)
 enum Container : int {
     CT_BF16 = 1, CT_F16 = 2, CT_F8E4M3 = 3, CT_I8 = 4, CT_Q16 = 100,
-    // fused matrix-vector products Y[m] += W x[m] for m < 1, 2 or 4 activation rows (see launch_gemv)
+    // fused matrix-vector products W x[m] for m < 1, 2 or 4 activation rows (see launch_gemv)
     CT_GEMV1 = 101, CT_GEMV2 = 102, CT_GEMV4 = 104
 };
 
@@ -27,7 +27,7 @@ struct MatDesc {
     void* out;                  // [rows][cols] container elements
     union {
         float* scale_out;       // [rows] for FP8 / INT8, else unused
-        const uint16_t* gemv_x; // fused matrix-vector product: X [gemv_m][cols] bf16 (out: fp32 Y [gemv_m][rows])
+        const uint16_t* gemv_x; // fused matrix-vector product: X [gemv_m][cols] bf16 (out: fp32 partials)
     };
     int* err;                   // device error flag (bit 0: word count, bit 1: final state)
     uint32_t rows, cols, tiles_c, pairs_c;
@@ -82,18 +82,16 @@ int device_cus();
 // Launch one grouped decode of up to kMaxGroup matrices (lossy and lossless may be mixed).
 hipError_t launch_group(const MatDesc* mats, int count, hipStream_t stream);
 
-// Fused decode and matrix-vector product of one lossy matrix W [rows][cols] with gemv_m <= 4 BF16
-// activation rows: every wave multiplies the weights it has just decoded (fp32 q alpha_r, never
-// stored) by the activations and adds each row's dot products into the fp32 output m.out
-// [gemv_m][rows], which must hold zeros (or a partial sum) on entry. m.container must be
-// CT_GEMV1, CT_GEMV2 or CT_GEMV4 (at least gemv_m) and cols a multiple of 8.
+// Fused decode and matrix-vector product of one lossy layout-0 matrix W [rows][cols] with
+// gemv_m <= 4 BF16 activation rows: every wave multiplies the BF16 weights it has just decoded
+// (bf16(q alpha_r), never stored) by the activations and writes each row's sums over its tile pair
+// to the fp32 partials m.out [pairs_c][gemv_m][rows] (every entry of a row < rows written once).
+// m.container must be CT_GEMV1, CT_GEMV2 or CT_GEMV4 (at least gemv_m) and cols a multiple of 8.
 hipError_t launch_gemv(const MatDesc& m, hipStream_t stream);
 
-// Zero n floats with a kernel (no memset node, so that the call can be captured in a graph).
-hipError_t launch_gemv_zero(float* yacc, int64_t n, hipStream_t stream);
-
-// Y [M][N] bf16 = Yacc [M][N] fp32 rounded to nearest even (+ bias [N] bf16).
-hipError_t launch_gemv_finish(const float* yacc, const uint16_t* bias, uint16_t* y, int64_t M, int64_t N,
+// Y [M][N] bf16 = sum over p < pcs, in order, of part [p][M][N] (+ bias [N] bf16), rounded to
+// nearest even; pcs = 0 gives the bias (or zeros) and reads no partials.
+hipError_t launch_gemv_finish(const float* part, int64_t pcs, const uint16_t* bias, uint16_t* y, int64_t M, int64_t N,
                               hipStream_t stream);
 
 static_assert(sizeof(GroupArgs) <= 4096, "kernel argument space");

@@ -204,10 +204,10 @@ ep_status ep_decode_symbols(const ep_handle* h, int16_t* dev_q, void* hip_stream
  *     BF16 MFMA (row layout: straight from the decoder's registers; layout 0: transposed through
  *     LDS), the weight never written; fp32 partial sums per tile pair in the workspace, summed in
  *     column order (deterministic);
- *   - M <= 4 on layout-0 streams: the decode kernel forms the products (the decoded fp32
- *     weights, not rounded to BF16, times the activations in registers, summed into an fp32
- *     accumulator in the workspace by atomic additions, whose order varies, so two calls may
- *     differ in the last bits);
+ *   - M <= 4 on layout-0 streams: the decode kernel forms the products (the decoded weights
+ *     rounded to BF16 as the decode stores them, times the activations in registers), one fp32
+ *     partial sum per row and tile pair column in the workspace, added in column order
+ *     (deterministic);
  *   - otherwise the weight is decoded once per call, up to 128 MiB of BF16 rows at a time, into
  *     the workspace, which stays in the Infinity Cache, and each slice is multiplied by the BF16
  *     MFMA GEMM: hipBLASLt's from 512 rows, above 64 when K <= 4096, from 256 when N <= 4096 (faster
@@ -227,12 +227,13 @@ ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, co
  * harnesses that forbid hipMalloc): ep_linear_forward with its scratch in a static device array
  * of 64 MiB per device instead of the library's workspace pool. It calls no hipMalloc, hipFree or
  * allocating library routine; the array lives from library load until the process ends. Same
- * arguments, results and paths as ep_linear_forward (the same kernels: the fused kernel's partial
- * sums, the fp32 accumulator of M <= 4 on layout-0 streams, otherwise BF16 weight slices of at
+ * arguments, results and paths as ep_linear_forward (the same kernels: the fused kernels' partial
+ * sums, those of M <= 4 on layout-0 streams, otherwise BF16 weight slices of at
  * most 64 MiB, i.e. 64 MiB / (2 K) rows, always multiplied by the library's own GEMM kernel, so
  * results where ep_linear_forward uses hipBLASLt may differ from it in the fp32 summation
  * order). EP_ERANGE when a call needs more than the array holds
- * (M <= 4 with 4 M N > 64 MiB, the fused partials of very wide layers, or K > 2^21 for the slices).
+ * (M <= 4 on layout-0 streams with 4 M N ceil(K / 512) > 64 MiB, the fused partials of very wide
+ * layers, or K > 2^21 for the slices).
  * Every call on a device shares that device's array: calls that overlap in time on one device
  * (other streams, other threads) race and must be serialized by the caller.
  * Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section "Measure
