@@ -39,7 +39,7 @@ STATUS = {0: "EP_OK", -1: "EP_EINVAL", -2: "EP_ECORRUPT", -3: "EP_EUNSUPPORTED",
 EXPORTS = ["ep_compress", "ep_free", "ep_stream_info", "ep_upload", "ep_handle_info", "ep_decompress",
            "ep_decompress_many", "ep_decode_symbols", "ep_linear_forward", "ep_gemm_bf16", "ep_handle_check",
            "ep_release", "ep_last_error", "ep_version", "ep_linear_forward_fp8", "ep_quantize_rows_fp8",
-           "ep_gemm_fp8", "ep_compress_device", "ep_linear_forward_noalloc"]
+           "ep_gemm_fp8", "ep_compress_device", "ep_linear_forward_noalloc", "ep_linear_forward_many"]
 
 
 class EPError(RuntimeError):
@@ -89,6 +89,7 @@ def lib() -> C.CDLL:
         L.ep_decode_symbols.argtypes = [vp, vp, vp]
         L.ep_linear_forward.argtypes = [vp, vp, i64, vp, vp, vp]
         L.ep_linear_forward_noalloc.argtypes = [vp, vp, i64, vp, vp, vp]
+        L.ep_linear_forward_many.argtypes = [vp, C.c_int, vp, i64, vp, vp, vp]
         L.ep_gemm_bf16.argtypes = [vp, vp, i64, i64, i64, vp, vp]
         L.ep_linear_forward_fp8.argtypes = [vp, vp, i64, vp, vp, vp]
         L.ep_quantize_rows_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
@@ -515,3 +516,41 @@ class CompressedLinear:
         return y.reshape(*shp[:-1], self.out_features)
 
     __call__ = forward
+
+
+def linear_forward_many(layers, x, stream=None):
+    """[layer(x) for layer in layers] for BF16 CompressedLinear layers that take the same input x
+    (BF16, [..., in_features] on the GPU), each output the same bits as the layer's own forward. Up
+    to 64 activation rows of row-layout layers with one prob_bits decode in one fused launch
+    (ep_linear_forward_many), so that small layers share the GPU's rounds of tile pairs; other
+    cases run the layers one by one."""
+    torch = _torch()
+    layers = list(layers)
+    if not layers:
+        return []
+    if len(layers) > 32 or any(l.compute != "bf16" for l in layers):
+        return [l(x, stream=stream) for l in layers]
+    K = layers[0].in_features
+    shp = x.shape
+    if any(l.in_features != K for l in layers) or shp[-1] != K or not x.is_cuda:
+        raise ValueError("the layers must share in_features, and x must be a GPU tensor of that last dimension")
+    if x.dtype != torch.bfloat16:
+        raise ValueError(f"the forward takes bfloat16 activations, got {x.dtype}")
+    if x.device.index != torch.cuda.current_device():
+        raise ValueError(f"x is on {x.device}, but the current device is cuda:{torch.cuda.current_device()}")
+    for l in layers:
+        if l.bias is not None:
+            _need(l.bias, "bias", torch.bfloat16, shape=(l.out_features,))
+    s, other = _run_on(stream)
+    with torch.cuda.stream(s):
+        rows = int(np.prod(shp[:-1], dtype=np.int64))
+        x2 = x.reshape(rows, K).contiguous()
+        ys = [torch.empty((rows, l.out_features), dtype=torch.bfloat16, device=x.device) for l in layers]
+        n = len(layers)
+        hs = (C.c_void_p * n)(*[l.handle.ptr.value for l in layers])
+        bs = (C.c_void_p * n)(*[(l.bias.data_ptr() if l.bias is not None else None) for l in layers])
+        os_ = (C.c_void_p * n)(*[y.data_ptr() for y in ys])
+        _check(lib().ep_linear_forward_many(hs, n, C.c_void_p(x2.data_ptr()), rows, bs, os_, C.c_void_p(s.cuda_stream)),
+               "ep_linear_forward_many")
+    _used_on(s, other, x2, *[l.bias for l in layers])
+    return [y.reshape(*shp[:-1], l.out_features) for y, l in zip(ys, layers)]

@@ -621,6 +621,64 @@ ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, co
     });
 }
 
+ep_status ep_linear_forward_many(const ep_handle* const* w, int count, const void* dev_x, int64_t M,
+                                 const void* const* dev_bias, void* const* dev_y, void* hip_stream) {
+    return guarded([&]() -> ep_status {
+        if (count < 0 || count > ep::kMaxGroup) return fail(EP_ERANGE, "count must be 0 ... 32");
+        if (count == 0) return EP_OK;
+        if (!w || !dev_y) return fail(EP_EINVAL, "null pointer");
+        hipStream_t s = static_cast<hipStream_t>(hip_stream);
+        // every layer checked before anything is queued
+        for (int i = 0; i < count; ++i) {
+            if (!w[i] || !dev_y[i]) return fail(EP_EINVAL, "null handle or output at layer " + std::to_string(i));
+            if (ep_status st = on_its_device(w[i]); st != EP_OK) return st;
+            if (w[i]->view.mode != EP_MODE_LOSSY_E8) return fail(EP_EUNSUPPORTED, "the linear forward takes a lossy stream");
+            if (w[i]->view.cols != w[0]->view.cols) return fail(EP_EINVAL, "the layers take inputs of different widths");
+        }
+        const int64_t K = w[0]->view.cols;
+        if (M < 0) return fail(EP_EINVAL, "negative M");
+        if (M == 0) return EP_OK;
+        if (K > 0 && !dev_x) return fail(EP_EINVAL, "null pointer");
+        std::vector<ep::MatDesc> ds;
+        bool nonempty = true;
+        for (int i = 0; i < count; ++i) {
+            ds.push_back(desc_for(w[i], ep::CT_BF16, nullptr, nullptr));
+            nonempty = nonempty && w[i]->view.rows > 0;
+        }
+        if (K == 0 || !nonempty || !ep::fused_many_fits(ds.data(), count, M)) {
+            // not one fused launch: each layer's own forward, in order
+            for (int i = 0; i < count; ++i)
+                if (ep_status st = linear_forward(w[i], dev_x, M, dev_bias ? dev_bias[i] : nullptr, dev_y[i], s, false);
+                    st != EP_OK)
+                    return st;
+            return EP_OK;
+        }
+        if (M > INT32_MAX) return fail(EP_ERANGE, "M must be below 2^31");
+        if (K % 8) return fail(EP_EINVAL, "in_features must be a multiple of 8");
+        if (reinterpret_cast<uintptr_t>(dev_x) & 15) return fail(EP_EINVAL, "X must be 16-byte aligned");
+        int dev = 0;
+        hipError_t he = hipGetDevice(&dev);
+        if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
+        std::vector<size_t> off(count + 1, 0);
+        for (int i = 0; i < count; ++i) off[i + 1] = off[i] + up(ep::fused_partial_bytes(ds[i], M), 256);
+        WsLease ws;
+        if ((he = ws_acquire(dev, s, off[count], &ws)) != hipSuccess)
+            return hip_fail(he, "hipMalloc for the linear forward workspace");
+        std::vector<float*> parts(count);
+        std::vector<const uint16_t*> bias(count);
+        std::vector<uint16_t*> ys(count);
+        for (int i = 0; i < count; ++i) {
+            parts[i] = reinterpret_cast<float*>(static_cast<uint8_t*>(ws.ptr) + off[i]);
+            bias[i] = dev_bias ? static_cast<const uint16_t*>(dev_bias[i]) : nullptr;
+            ys[i] = static_cast<uint16_t*>(dev_y[i]);
+        }
+        hipError_t e = ep::launch_fused_many(ds.data(), count, static_cast<const uint16_t*>(dev_x), M, parts.data(),
+                                             bias.data(), ys.data(), s);
+        if (e == hipSuccess) e = ws.queued();
+        return e == hipSuccess ? EP_OK : hip_fail(e, "grouped fused decode + MFMA launch");
+    });
+}
+
 ep_status ep_linear_forward_noalloc(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias,
                                     void* dev_y, void* hip_stream) {
     return guarded([&]() -> ep_status {

@@ -37,6 +37,17 @@ size_t fused_partial_bytes(const MatDesc& m, int64_t M);
 hipError_t launch_fused(const MatDesc& m, const uint16_t* x, int64_t M, float* part, const uint16_t* bias,
                         uint16_t* y, hipStream_t stream);
 
+// Whether launch_fused_many takes these matrices and M: 1 to kMaxGroup matrices that fused_fits
+// each, all in the row layout, with one probability precision and one input width.
+bool fused_many_fits(const MatDesc* ms, int count, int64_t M);
+
+// launch_fused for several matrices that take the same activations X (bf16 [M][cols]) in one
+// decode + MFMA launch: matrix i writes its partial sums to parts[i] (fused_partial_bytes of it)
+// and Y_i = X W_i^T (+ bias[i], bf16 or null) to y[i] (bf16 [M][rows_i]), each the same bits as
+// launch_fused of that matrix alone.
+hipError_t launch_fused_many(const MatDesc* ms, int count, const uint16_t* x, int64_t M, float* const* parts,
+                             const uint16_t* const* bias, uint16_t* const* y, hipStream_t stream);
+
 // FP8 variant: the tile pairs decoded into E4M3 codes (the FP8 container) multiplied by per-row
 // E4M3 activation codes xq [M][cols] (scales xs [M]) on v_mfma_f32_16x16x128_f8f6f4 (layout 0) or
 // v_mfma_f32_16x16x32_fp8_fp8 (row layout); y = (sum of the partials) x xs[m] x row_scale[n]

@@ -513,6 +513,48 @@ hipError_t launch_mfma_mt(const GroupArgs& g, uint64_t blocks, hipStream_t strea
     }
 }
 
+// decode_mfma_rows over several row-layout matrices in one launch (layers that take the same
+// activations, e.g. the gate and up projections of a gated FFN): the matrices' tile pairs are laid
+// out matrix by matrix and weighted by their decode cost, each block owns an equal share and
+// restages the decode tables when its share crosses into the next matrix, and every matrix writes
+// its own partial sums, so each layer's result is the single-layer kernel's. A layer of fewer tile
+// pairs than the CU's wave slots, or one whose last round of pairs is mostly empty, shares its
+// rounds with the others instead of ending on a pair's latency. Same probability precision N and
+// input width for all matrices.
+template <int N, int MT>
+__global__ __launch_bounds__(64 * kWaves) void decode_mfma_rows_many(GroupArgs g) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    if ((uint32_t)(size_t)(lds_u8*)smem != 0u) {
+        if (threadIdx.x == 0)
+            for (int i = 0; i < g.count; ++i) atomicOr(g.m[i].err, kErrLayout);
+        return;
+    }
+    const uint64_t a = (uint64_t)blockIdx.x * g.block_cost;
+    const uint64_t b = std::min<uint64_t>(a + g.block_cost, g.cost_start[g.count]);
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    for (int mi = 0; mi < g.count; ++mi) {
+        const uint64_t cs = g.cost_start[mi], ce = g.cost_start[mi + 1];
+        if (ce <= a || cs >= b) continue;
+        const MatDesc& M = g.m[mi];
+        const uint64_t w = M.pair_cost;
+        const uint64_t p0 = (std::max(a, cs) - cs + w - 1) / w, p1 = (std::min(b, ce) - cs + w - 1) / w;
+        if (p0 >= p1) continue;
+        __syncthreads();                            // every wave is done with the previous tables
+        const Tables T = stage_lossy_tables_dma(M, smem);
+        Tile t;
+        init_lane(t, smem + lds_table_bytes(M.n_tables, M.prob_bits, true), 0);
+        const __amdgpu_buffer_rsrc_t rs = payload_rsrc(M);
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(M.gemv_x), 0, (int)((size_t)M.gemv_m * M.cols * 2), 0x00020000);
+        const uint32_t tiles_r = (M.rows + 15u) / 16u;          // column-major pair order, as above
+        for (uint64_t p = p0 + (uint64_t)wave; p < p1; p += kWaves) {
+            const uint32_t pc = (uint32_t)p / tiles_r, tr = (uint32_t)p % tiles_r;
+            rows_pair<N, MT, false>(M, T, t, (uint64_t)tr * M.pairs_c + pc, rs, rx);
+        }
+        if (t.err) atomicOr(M.err, t.err);
+    }
+}
+
 template <int N, int MT, bool F8>
 hipError_t launch_rows_n(const GroupArgs& g, uint64_t blocks, hipStream_t stream) {
     const MatDesc& m = g.m[0];
@@ -542,6 +584,26 @@ hipError_t launch_rows(const GroupArgs& g, int mt, uint64_t blocks, hipStream_t 
         case 1: return launch_rows_mt<1, F8>(g, blocks, stream);
         case 2: return launch_rows_mt<2, F8>(g, blocks, stream);
         default: return launch_rows_mt<4, F8>(g, blocks, stream);
+    }
+}
+
+template <int N, int MT>
+hipError_t launch_rows_many_n(const GroupArgs& g, uint64_t blocks, hipStream_t stream) {
+    const MatDesc& m = g.m[0];
+    const size_t lds = lds_table_bytes(m.n_tables, m.prob_bits, true) + (size_t)kWaves * 2 * kRingBytes;
+    const void* k = reinterpret_cast<const void*>(decode_mfma_rows_many<N, MT>);
+    hipError_t e = allow_lds(k);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_mfma_rows_many<N, MT>), dim3((unsigned)blocks), dim3(64 * kWaves), lds, stream, g);
+    return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_rows_many_mt(const GroupArgs& g, uint64_t blocks, hipStream_t stream) {
+    switch (g.m[0].prob_bits) {
+        case 10: return launch_rows_many_n<10, MT>(g, blocks, stream);
+        case 11: return launch_rows_many_n<11, MT>(g, blocks, stream);
+        default: return launch_rows_many_n<12, MT>(g, blocks, stream);
     }
 }
 
@@ -623,6 +685,52 @@ hipError_t launch_fused_f8(const MatDesc& m, const uint8_t* xq, const float* xs,
     hipError_t e = m.layout ? launch_rows<true>(g, mt, used, stream) : launch_mfma_f8_mt<1>(g, used, stream);
     if (e != hipSuccess) return e;
     return launch_finish(part, xs, m.row_scale, bias, y, (int)M, (int)m.rows, (int)m.pairs_c, mt, stream);
+}
+
+bool fused_many_fits(const MatDesc* ms, int count, int64_t M) {
+    if (count < 1 || count > kMaxGroup) return false;
+    for (int i = 0; i < count; ++i)
+        if (!fused_fits(ms[i], M) || ms[i].layout != 1 || ms[i].prob_bits != ms[0].prob_bits ||
+            ms[i].cols != ms[0].cols)
+            return false;
+    return true;
+}
+
+hipError_t launch_fused_many(const MatDesc* ms, int count, const uint16_t* x, int64_t M, float* const* parts,
+                             const uint16_t* const* bias, uint16_t* const* y, hipStream_t stream) {
+    if (!fused_many_fits(ms, count, M)) return hipErrorInvalidValue;
+    GroupArgs g{};
+    g.count = count;
+    uint64_t total = 0;
+    for (int i = 0; i < count; ++i) {
+        g.m[i] = ms[i];
+        g.m[i].gemv_x = x;
+        g.m[i].gemv_m = (uint8_t)M;
+        g.m[i].out = parts[i];
+        g.cost_start[i] = total;
+        total += (uint64_t)((ms[i].rows + ms[i].tile_rows - 1) / ms[i].tile_rows) * ms[i].pairs_c * ms[i].pair_cost;
+    }
+    g.cost_start[count] = total;
+    const int mt = fused_mt(ms[0], M);
+    if (total > 0) {
+        const uint64_t blocks = (uint64_t)device_cus();
+        g.block_cost = (total + blocks - 1) / blocks;
+        const uint64_t used = (total + g.block_cost - 1) / g.block_cost;
+        hipError_t e;
+        switch (mt) {
+            case 1: e = launch_rows_many_mt<1>(g, used, stream); break;
+            case 2: e = launch_rows_many_mt<2>(g, used, stream); break;
+            default: e = launch_rows_many_mt<4>(g, used, stream); break;
+        }
+        if (e != hipSuccess) return e;
+    }
+    for (int i = 0; i < count; ++i) {
+        if ((uint64_t)ms[i].rows * ms[i].cols == 0) continue;
+        hipError_t e = launch_finish(parts[i], nullptr, nullptr, bias[i], y[i], (int)M, (int)ms[i].rows,
+                                     (int)ms[i].pairs_c, mt, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace ep

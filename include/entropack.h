@@ -223,6 +223,28 @@ ep_status ep_decode_symbols(const ep_handle* h, int16_t* dev_q, void* hip_stream
 ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias,
                             void* dev_y, void* hip_stream);
 
+/* Several compressed linear layers that take the same input: Y_i = X * W_i^T (+ bias_i) for
+ * i < count, each Y_i the same bits as ep_linear_forward(w[i], dev_x, M, dev_bias[i], dev_y[i]).
+ * When every layer is a row-layout stream (ep_encode_opts.layout = 1) with the same prob_bits and
+ * 1 <= M <= 64 (the fused path of ep_linear_forward), one kernel decodes all of their tile pairs
+ * into the BF16 MFMA, cost-balanced across the layers, so that a layer whose last round of tile
+ * pairs would leave most wave slots idle (e.g. the gate and up projections of a gated FFN, 4800
+ * pairs each at 10240 x 3840 for 4096 slots) shares its rounds with the others; otherwise the
+ * layers run one ep_linear_forward each, in order.
+ * Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section
+ * "Replace one linear layer before a whole model" (compressed layers inside a model's forward);
+ * "EntroPack: Fast and Accurate Entropy-Coded Weight Compression at Arbitrary Bitrates", Abstract
+ * (decoding fused with the computation that uses the weights). Grouping layers that share an
+ * input is this library's scheduling, not a step of the method.
+ *   w: count handles, all with the same in_features K; dev_x: [M][K] bf16, 16-byte aligned (may be
+ * NULL when K == 0); dev_bias: NULL or count pointers (each [N_i] bf16 or NULL); dev_y: count
+ * pointers to [M][N_i] bf16. count in 0 ... 32 (EP_ERANGE otherwise); different in_features or a
+ * null handle or output give EP_EINVAL before anything is queued; a lossless stream
+ * EP_EUNSUPPORTED. The workspace is the (device, hip_stream) pair's, as for ep_linear_forward.
+ * Asynchronous on hip_stream. */
+ep_status ep_linear_forward_many(const ep_handle* const* w, int count, const void* dev_x, int64_t M,
+                                 const void* const* dev_bias, void* const* dev_y, void* hip_stream);
+
 /* For callers that cannot allocate device memory (code under stream capture, tight serving loops,
  * harnesses that forbid hipMalloc): ep_linear_forward with its scratch in a static device array
  * of 64 MiB per device instead of the library's workspace pool. It calls no hipMalloc, hipFree or
