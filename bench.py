@@ -307,9 +307,10 @@ def dit_forward_section(torch, ep, tokens=(4096, 256, 16), reps: int = 3):
         out[f"M{M}"] = {"compressed_ms": round(f, 3), "torch_matmul_ms": round(t, 3), "overhead_vs_torch": round(f / t - 1, 4),
                         "tflops_compressed": round(2.0 * M * weights / f / 1e9, 1)}
         log(f"DiT-like forward M={M}: compressed {f:.2f} ms, torch.matmul {t:.2f} ms")
-        if M <= 64:
+        if True:
             # the gate and up projections of each block take the same input: one grouped call
-            # (ep_linear_forward_many) instead of two forwards; the other layers as above
+            # (ep_linear_forward_many: one fused launch up to 64 rows, one grouped slice decode
+            # above) instead of two forwards; the other layers as above
             def grouped():
                 for blk in range(W.DIT_BLOCKS):
                     L5 = layers[5 * blk:5 * blk + 5]

@@ -296,6 +296,11 @@ bool use_gemm_library(int64_t M, int64_t N, int64_t K) {
     return M >= 512 || (M > 64 && K <= 4096) || (M >= 256 && N <= 4096);
 }
 
+// Largest BF16 slice of a layer's weight decoded at once (see linear_forward), and the hipBLASLt
+// workspace of a slice GEMM.
+constexpr size_t kSliceBytes = 128u << 20;
+constexpr size_t kLtWorkspace = 32u << 20;
+
 // Compressed linear forward. The weight is decoded once per call, one slice of output rows at a
 // time, into the forward's scratch, and each slice's GEMM writes its columns of Y. A slice of at
 // most kSliceBytes is large enough to keep every CU's decode block busy and, with the
@@ -304,7 +309,6 @@ bool use_gemm_library(int64_t M, int64_t N, int64_t K) {
 // `fixed`: the scratch is the device's static buffer (no allocation), whose size bounds the slice.
 ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias, void* dev_y,
                          hipStream_t s, bool fixed) {
-    constexpr size_t kSliceBytes = 128u << 20;
     if (!w) return fail(EP_EINVAL, "null handle");
     if (ep_status st = on_its_device(w); st != EP_OK) return st;
     if (w->view.mode != EP_MODE_LOSSY_E8) return fail(EP_EUNSUPPORTED, "the linear forward takes a lossy stream");
@@ -361,7 +365,6 @@ ep_status linear_forward(const ep_handle* w, const void* dev_x, int64_t M, const
     // 256 x 256 one at prefill sizes: 4096 x 8192 x 8192, 363 against 441 us); elsewhere the own
     // kernel, split-K when its tiles cannot fill the CUs. Not in the no-allocation variant: the
     // library's handle allocates on first use.
-    constexpr size_t kLtWorkspace = 32u << 20;
     const bool lt = !fixed && use_gemm_library(M, N, K);
     // K splits of the GEMM, chosen for the whole layer so that every slice adds its partial sums in
     // the same order; the split partial tiles of a slice follow its decoded rows in the scratch
@@ -645,8 +648,53 @@ ep_status ep_linear_forward_many(const ep_handle* const* w, int count, const voi
             ds.push_back(desc_for(w[i], ep::CT_BF16, nullptr, nullptr));
             nonempty = nonempty && w[i]->view.rows > 0;
         }
-        if (K == 0 || !nonempty || !ep::fused_many_fits(ds.data(), count, M)) {
-            // not one fused launch: each layer's own forward, in order
+        const bool fused = K > 0 && nonempty && ep::fused_many_fits(ds.data(), count, M);
+        // More rows: when every layer's own forward would decode it as one whole-layer slice and
+        // multiply it by hipBLASLt, the slices of all layers are decoded by one grouped launch and
+        // then multiplied one by one (the same slices and GEMMs, so the same bits), while the group's
+        // slices stay within the Infinity Cache's reach (192 MiB).
+        bool grouped_slices = !fused && count > 1 && K > 0 && K % 8 == 0 && M > 64 && M <= INT32_MAX && dev_x &&
+                              !(reinterpret_cast<uintptr_t>(dev_x) & 15);
+        size_t slice_total = 0;
+        for (int i = 0; i < count && grouped_slices; ++i) {
+            const int64_t N = w[i]->view.rows;
+            grouped_slices = N > 0 && N <= INT32_MAX && (size_t)N * (size_t)K * 2 <= kSliceBytes &&
+                             use_gemm_library(M, N, K);
+            slice_total += up((size_t)N * (size_t)K * 2, 256);
+        }
+        if (grouped_slices && slice_total <= (192u << 20)) {
+            int dev = 0;
+            hipError_t he = hipGetDevice(&dev);
+            if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
+            WsLease ws;
+            if ((he = ws_acquire(dev, s, slice_total + kLtWorkspace, &ws)) != hipSuccess)
+                return hip_fail(he, "hipMalloc for the linear forward workspace");
+            uint8_t* base = static_cast<uint8_t*>(ws.ptr);
+            std::vector<ep::MatDesc> dd;
+            std::vector<uint16_t*> sl;
+            size_t o = 0;
+            for (int i = 0; i < count; ++i) {
+                sl.push_back(reinterpret_cast<uint16_t*>(base + o));
+                dd.push_back(desc_for(w[i], ep::CT_BF16, sl.back(), nullptr));
+                o += up((size_t)w[i]->view.rows * (size_t)K * 2, 256);
+            }
+            hipError_t e = launch_all(dd, s);
+            for (int i = 0; i < count && e == hipSuccess; ++i) {
+                const int N = (int)w[i]->view.rows;
+                ep::GemmArgs g{static_cast<const uint16_t*>(dev_x), sl[i],
+                               dev_bias ? static_cast<const uint16_t*>(dev_bias[i]) : nullptr,
+                               static_cast<uint16_t*>(dev_y[i]), (int)M, N, (int)K, (int)K, (int)K, N};
+                g.splits = 1;
+                g.part = nullptr;
+                g.part_bytes = 0;
+                e = ep::lt_gemm(g, base + slice_total, kLtWorkspace, s);
+                if (e == hipErrorNotSupported) e = ep::launch_gemm(g, s);
+            }
+            if (e == hipSuccess) e = ws.queued();
+            return e == hipSuccess ? EP_OK : hip_fail(e, "grouped slice decode + GEMM launch");
+        }
+        if (!fused) {
+            // each layer's own forward, in order
             for (int i = 0; i < count; ++i)
                 if (ep_status st = linear_forward(w[i], dev_x, M, dev_bias ? dev_bias[i] : nullptr, dev_y[i], s, false);
                     st != EP_OK)
@@ -749,7 +797,6 @@ ep_status ep_gemm_fp8(const uint8_t* dev_xq, const float* dev_xs, const uint8_t*
         hipStream_t s = static_cast<hipStream_t>(hip_stream);
         // hipBLASLt where use_gemm_library says so, as for the FP8 forward's slices (its workspace
         // from the pool)
-        constexpr size_t kLtWorkspace = 32u << 20;
         hipError_t e = hipErrorNotSupported;
         WsLease ws;
         if (use_gemm_library(M, N, K)) {
@@ -768,7 +815,6 @@ ep_status ep_gemm_fp8(const uint8_t* dev_xq, const float* dev_xs, const uint8_t*
 ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias, void* dev_y,
                                 void* hip_stream) {
     return guarded([&]() -> ep_status {
-        constexpr size_t kSliceBytes = 128u << 20;
         if (!w) return fail(EP_EINVAL, "null handle");
         if (ep_status st = on_its_device(w); st != EP_OK) return st;
         if (w->view.mode != EP_MODE_LOSSY_E8) return fail(EP_EUNSUPPORTED, "the linear forward takes a lossy stream");
@@ -814,7 +860,6 @@ ep_status ep_linear_forward_fp8(const ep_handle* w, const void* dev_x, int64_t M
         if (slice < tr) slice = tr;
         if (slice > N) slice = (N + tr - 1) / tr * tr;
         // slices multiplied by hipBLASLt where use_gemm_library says so (as in the BF16 forward)
-        constexpr size_t kLtWorkspace = 32u << 20;
         const bool lt = use_gemm_library(M, N, K);
         // workspace: X codes [M][K] | X scales [M] | weight codes [slice][K] | weight scales [slice]
         // | hipBLASLt workspace

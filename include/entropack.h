@@ -229,8 +229,11 @@ ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, co
  * 1 <= M <= 64 (the fused path of ep_linear_forward), one kernel decodes all of their tile pairs
  * into the BF16 MFMA, cost-balanced across the layers, so that a layer whose last round of tile
  * pairs would leave most wave slots idle (e.g. the gate and up projections of a gated FFN, 4800
- * pairs each at 10240 x 3840 for 4096 slots) shares its rounds with the others; otherwise the
- * layers run one ep_linear_forward each, in order.
+ * pairs each at 10240 x 3840 for 4096 slots) shares its rounds with the others. Above 64 rows, when
+ * every layer's own forward would decode it as one slice (N_i K <= 64 Mi) multiplied by hipBLASLt
+ * and the group's slices total at most 192 MiB, one grouped launch decodes all the slices and each
+ * is then multiplied as its own forward would. Otherwise the layers run one ep_linear_forward
+ * each, in order.
  * Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section
  * "Replace one linear layer before a whole model" (compressed layers inside a model's forward);
  * "EntroPack: Fast and Accurate Entropy-Coded Weight Compression at Arbitrary Bitrates", Abstract

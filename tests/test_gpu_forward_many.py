@@ -1,10 +1,13 @@
 """The grouped compressed linear forward (ep_linear_forward_many): layers that take the same input
 are decoded into the BF16 MFMA by one launch when they are row-layout streams with one prob_bits
-and M <= 64, and must give, layer by layer, the same bits as their own forwards (the same per-pair
-partial sums, added in the same order); other groups run the layers one by one. Cases: ragged
-shapes and biases at M = 1, 16, 33, 64 (one to four M tiles), the DiT-like gate and up projections,
-the fallbacks (a layout-0 layer, mixed prob_bits, M = 65), the fp64 product of the oracle's
-weights, and the C ABI refusing layers of different input widths before any launch."""
+and M <= 64; above 64 rows, when every layer would be one whole-layer slice multiplied by
+hipBLASLt, their slices are decoded by one grouped launch and multiplied one by one. Either way
+each layer must give the same bits as its own forward (the same partial sums added in the same
+order, or the same slices and GEMMs); other groups run the layers one by one. Cases: ragged shapes
+and biases at M = 1, 16, 33, 64 (one to four M tiles), grouped slices at 100 and 600 rows with
+mixed tile layouts, the DiT-like gate and up projections at 16 and 256 rows, the fallbacks (a
+layout-0 layer, mixed prob_bits, M = 65 with K > 4096 rows for the own GEMM), the fp64 product of
+the oracle's weights, and the C ABI refusing layers of different input widths before any launch."""
 import ctypes as C
 
 import numpy as np
@@ -61,10 +64,19 @@ def test_group_against_the_oracle():
         assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 5e-3
 
 
-def test_dit_like_gate_and_up():
+@pytest.mark.parametrize("M", [16, 256])
+def test_dit_like_gate_and_up(M):
     R, K = W.DIT_BLOCK_SHAPES[2]                  # [10240, 3840] twice: 4800 tile pairs each
     layers = [layer(R, K, sd, bias=False, target=4.0)[0] for sd in (21, 22)]
-    same_as_own_forwards(layers, bf16(W.activations(16, K, 23)).cuda())
+    same_as_own_forwards(layers, bf16(W.activations(M, K, 23)).cuda())
+
+
+@pytest.mark.parametrize("M", [100, 600])
+def test_prefill_group_slices(M):
+    K = 1024
+    layers = [layer(N, K, sd, bias=sd % 2 == 0, layout=lay)[0]
+              for N, sd, lay in [(700, 51, ep.ROW_LAYOUT), (256, 52, 0), (1000, 53, ep.ROW_LAYOUT)]]
+    same_as_own_forwards(layers, bf16(W.activations(M, K, 54)).cuda())
 
 
 @pytest.mark.parametrize("case", ["layout0", "prob_bits", "M65", "one"])
@@ -76,7 +88,8 @@ def test_groups_that_run_layer_by_layer(case):
     elif case == "prob_bits":
         layers, M = [a, layer(96, K, 33, prob_bits=12)[0]], 8
     elif case == "M65":
-        layers, M = [a, layer(96, K, 34)[0]], 65
+        K = 4608                                  # above 4096: the own GEMM, layer by layer
+        layers, M = [layer(160, K, 36)[0], layer(96, K, 34)[0]], 65
     else:
         layers, M = [a], 5
     same_as_own_forwards(layers, bf16(W.activations(M, K, 35)).cuda())
