@@ -13,6 +13,10 @@
  * 3. The same again in the row tile layout (ep_encode_opts.layout = 1): <dir>/rows.epk and
  *    <dir>/rows_bf16.bin; the program checks that the stream reports the layout and that both
  *    layouts decode to the same BF16 bits.
+ * 4. Two row-layout layers of input width 512 (96 and 40 outputs) and 8 BF16 activation rows:
+ *    ep_linear_forward_many must give the same bits as one ep_linear_forward per layer (checked
+ *    here); the streams, X and both outputs go to <dir>/layer{0,1}.epk, x_bf16.bin and
+ *    y{0,1}_bf16.bin for the test to compare with the oracle's weights.
  * Exit status 0 on success; a message on stderr otherwise. */
 #include <stdint.h>
 #include <stdio.h>
@@ -149,6 +153,72 @@ int main(int argc, char** argv) {
     ep_free(s);
     free(bf_rows);
     printf("row layout: %.4f bpp actual, the same BF16 weights\n", bpp);
+
+    /* 4. two layers sharing an input: the grouped forward against one forward per layer */
+    enum { K = 512, M = 8 };
+    const int64_t N[2] = {96, 40};
+    ep_handle* hl[2] = {NULL, NULL};
+    void* dy[2][2] = {{NULL, NULL}, {NULL, NULL}};   /* [layer][per-layer, grouped] */
+    void* dx = NULL;
+    uint16_t xh[M * K];
+    for (int i = 0; i < M * K; ++i) {
+        const float v = (float)(uniform01() + uniform01() + uniform01() + uniform01() - 2.0);
+        uint32_t u;
+        memcpy(&u, &v, 4);
+        xh[i] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);      /* BF16, nearest even */
+    }
+    if (hipMalloc(&dx, sizeof xh) != hipSuccess || hipMemcpy(dx, xh, sizeof xh, hipMemcpyHostToDevice) != hipSuccess) {
+        fprintf(stderr, "activation upload failed\n");
+        return 1;
+    }
+    for (int l = 0; l < 2; ++l) {
+        float* wl = (float*)malloc(sizeof(float) * (size_t)(N[l] * K));
+        if (!wl) return 1;
+        for (int64_t i = 0; i < N[l] * K; ++i)
+            wl[i] = (float)(0.02 * (uniform01() + uniform01() + uniform01() + uniform01() - 2.0) * 1.7320508);
+        ep_encode_opts lo = {EP_MODE_LOSSY_E8, 4.5, 11, 16, 0, 1};
+        st = ep_compress(wl, EP_F32, N[l], K, &lo, &s, &len, &bpp);
+        free(wl);
+        if (st != EP_OK) return fail_ep("ep_compress (layer)", st);
+        char name[32];
+        snprintf(name, sizeof name, "layer%d.epk", l);
+        if (write_file(argv[1], name, s, len)) return 1;
+        st = ep_upload(s, len, NULL, &hl[l]);
+        ep_free(s);
+        if (st != EP_OK) return fail_ep("ep_upload (layer)", st);
+        for (int v = 0; v < 2; ++v)
+            if (hipMalloc(&dy[l][v], sizeof(uint16_t) * (size_t)(M * N[l])) != hipSuccess) return fail_hip("hipMalloc", hipErrorOutOfMemory);
+        st = ep_linear_forward(hl[l], dx, M, NULL, dy[l][0], NULL);
+        if (st != EP_OK) return fail_ep("ep_linear_forward", st);
+    }
+    void* ys[2] = {dy[0][1], dy[1][1]};
+    st = ep_linear_forward_many((const ep_handle* const*)hl, 2, dx, M, NULL, ys, NULL);
+    if (st != EP_OK) return fail_ep("ep_linear_forward_many", st);
+    for (int l = 0; l < 2; ++l) {
+        uint16_t* a = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(M * N[l]));
+        uint16_t* b = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(M * N[l]));
+        if (!a || !b) return 1;
+        if (hipMemcpy(a, dy[l][0], sizeof(uint16_t) * (size_t)(M * N[l]), hipMemcpyDeviceToHost) != hipSuccess ||
+            hipMemcpy(b, dy[l][1], sizeof(uint16_t) * (size_t)(M * N[l]), hipMemcpyDeviceToHost) != hipSuccess)
+            return fail_hip("hipMemcpy", hipErrorUnknown);
+        if (memcmp(a, b, sizeof(uint16_t) * (size_t)(M * N[l])) != 0) {
+            fprintf(stderr, "layer %d: the grouped forward differs from the layer's own\n", l);
+            return 1;
+        }
+        char name[32];
+        snprintf(name, sizeof name, "y%d_bf16.bin", l);
+        if (write_file(argv[1], name, b, sizeof(uint16_t) * (size_t)(M * N[l]))) return 1;
+        free(a);
+        free(b);
+        st = ep_handle_check(hl[l], NULL);
+        if (st != EP_OK) return fail_ep("ep_handle_check (layer)", st);
+        (void)hipFree(dy[l][0]);
+        (void)hipFree(dy[l][1]);
+        ep_release(hl[l]);
+    }
+    if (write_file(argv[1], "x_bf16.bin", xh, sizeof xh)) return 1;
+    (void)hipFree(dx);
+    printf("grouped forward of two layers: the same bits as one forward per layer\n");
     free(w);
     free(back);
     free(bf);

@@ -1,8 +1,9 @@
 """The C ABI driven by a plain C program (tests/c_abi_roundtrip.c, compiled by
 __graft_entry__.build() with gcc against include/entropack.h and the HIP runtime): no Python and
-no PyTorch on the path. The program checks a lossless FP32 round trip itself, and that the row
-tile layout decodes to the same weights as layout 0; both lossy BF16 decodes are compared here
-with the oracle, bit for bit."""
+no PyTorch on the path. The program checks a lossless FP32 round trip itself, that the row tile
+layout decodes to the same weights as layout 0, and that the grouped linear forward gives the same
+bits as one forward per layer; both lossy BF16 decodes are compared here with the oracle, bit for
+bit, and the forwards with the fp64 product of the oracle's weights."""
 import os
 import subprocess
 
@@ -31,3 +32,12 @@ def test_c_program_round_trip(tmp_path):
     got_rows = np.fromfile(tmp_path / "rows_bf16.bin", dtype=np.uint16).reshape(300, 700)
     want_rows, _ = oracle.decompress(rows, oracle.BF16)
     assert np.array_equal(got_rows, want_rows) and np.array_equal(want_rows, want)
+    assert "grouped forward" in r.stdout
+    x = np.fromfile(tmp_path / "x_bf16.bin", dtype=np.uint16).reshape(8, 512)
+    x64 = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for l, n in enumerate((96, 40)):
+        wq, _ = oracle.decompress((tmp_path / f"layer{l}.epk").read_bytes(), oracle.BF16)
+        ref = x64 @ (wq.astype(np.uint32) << 16).view(np.float32).astype(np.float64).T
+        y = np.fromfile(tmp_path / f"y{l}_bf16.bin", dtype=np.uint16).reshape(8, n)
+        got = (y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 5e-3
