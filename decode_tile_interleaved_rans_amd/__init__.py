@@ -39,7 +39,8 @@ STATUS = {0: "EP_OK", -1: "EP_EINVAL", -2: "EP_ECORRUPT", -3: "EP_EUNSUPPORTED",
 EXPORTS = ["ep_compress", "ep_free", "ep_stream_info", "ep_upload", "ep_handle_info", "ep_decompress",
            "ep_decompress_many", "ep_decode_symbols", "ep_linear_forward", "ep_gemm_bf16", "ep_handle_check",
            "ep_release", "ep_last_error", "ep_version", "ep_linear_forward_fp8", "ep_quantize_rows_fp8",
-           "ep_gemm_fp8", "ep_compress_device", "ep_linear_forward_noalloc", "ep_linear_forward_many"]
+           "ep_gemm_fp8", "ep_compress_device", "ep_linear_forward_noalloc", "ep_linear_forward_many",
+           "ep_linear_forward_fp8_many"]
 
 
 class EPError(RuntimeError):
@@ -90,6 +91,7 @@ def lib() -> C.CDLL:
         L.ep_linear_forward.argtypes = [vp, vp, i64, vp, vp, vp]
         L.ep_linear_forward_noalloc.argtypes = [vp, vp, i64, vp, vp, vp]
         L.ep_linear_forward_many.argtypes = [vp, C.c_int, vp, i64, vp, vp, vp]
+        L.ep_linear_forward_fp8_many.argtypes = [vp, C.c_int, vp, i64, vp, vp, vp]
         L.ep_gemm_bf16.argtypes = [vp, vp, i64, i64, i64, vp, vp]
         L.ep_linear_forward_fp8.argtypes = [vp, vp, i64, vp, vp, vp]
         L.ep_quantize_rows_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
@@ -519,16 +521,18 @@ class CompressedLinear:
 
 
 def linear_forward_many(layers, x, stream=None):
-    """[layer(x) for layer in layers] for BF16 CompressedLinear layers that take the same input x
-    (BF16, [..., in_features] on the GPU), each output the same bits as the layer's own forward. Up
-    to 64 activation rows of row-layout layers with one prob_bits decode in one fused launch
-    (ep_linear_forward_many), so that small layers share the GPU's rounds of tile pairs; other
-    cases run the layers one by one."""
+    """[layer(x) for layer in layers] for CompressedLinear layers of one compute mode that take the
+    same input x (BF16, [..., in_features] on the GPU), each output the same bits as the layer's own
+    forward. Up to 64 activation rows of row-layout layers with one prob_bits decode in one fused
+    launch (ep_linear_forward_many, ep_linear_forward_fp8_many), so that small layers share the
+    GPU's rounds of tile pairs; above 64 rows BF16 layers can share one slice decode; other cases
+    run the layers one by one."""
     torch = _torch()
     layers = list(layers)
     if not layers:
         return []
-    if len(layers) > 32 or any(l.compute != "bf16" for l in layers):
+    fp8 = layers[0].compute == "fp8"
+    if len(layers) > 32 or any(l.compute != layers[0].compute for l in layers):
         return [l(x, stream=stream) for l in layers]
     K = layers[0].in_features
     shp = x.shape
@@ -550,7 +554,8 @@ def linear_forward_many(layers, x, stream=None):
         hs = (C.c_void_p * n)(*[l.handle.ptr.value for l in layers])
         bs = (C.c_void_p * n)(*[(l.bias.data_ptr() if l.bias is not None else None) for l in layers])
         os_ = (C.c_void_p * n)(*[y.data_ptr() for y in ys])
-        _check(lib().ep_linear_forward_many(hs, n, C.c_void_p(x2.data_ptr()), rows, bs, os_, C.c_void_p(s.cuda_stream)),
-               "ep_linear_forward_many")
+        fn = lib().ep_linear_forward_fp8_many if fp8 else lib().ep_linear_forward_many
+        _check(fn(hs, n, C.c_void_p(x2.data_ptr()), rows, bs, os_, C.c_void_p(s.cuda_stream)),
+               "ep_linear_forward_fp8_many" if fp8 else "ep_linear_forward_many")
     _used_on(s, other, x2, *[l.bias for l in layers])
     return [y.reshape(*shp[:-1], l.out_features) for y, l in zip(ys, layers)]

@@ -727,6 +727,68 @@ ep_status ep_linear_forward_many(const ep_handle* const* w, int count, const voi
     });
 }
 
+ep_status ep_linear_forward_fp8_many(const ep_handle* const* w, int count, const void* dev_x, int64_t M,
+                                     const void* const* dev_bias, void* const* dev_y, void* hip_stream) {
+    return guarded([&]() -> ep_status {
+        if (count < 0 || count > ep::kMaxGroup) return fail(EP_ERANGE, "count must be 0 ... 32");
+        if (count == 0) return EP_OK;
+        if (!w || !dev_y) return fail(EP_EINVAL, "null pointer");
+        hipStream_t s = static_cast<hipStream_t>(hip_stream);
+        for (int i = 0; i < count; ++i) {
+            if (!w[i] || !dev_y[i]) return fail(EP_EINVAL, "null handle or output at layer " + std::to_string(i));
+            if (ep_status st = on_its_device(w[i]); st != EP_OK) return st;
+            if (w[i]->view.mode != EP_MODE_LOSSY_E8) return fail(EP_EUNSUPPORTED, "the linear forward takes a lossy stream");
+            if (w[i]->view.cols != w[0]->view.cols) return fail(EP_EINVAL, "the layers take inputs of different widths");
+        }
+        const int64_t K = w[0]->view.cols;
+        if (M < 0) return fail(EP_EINVAL, "negative M");
+        if (M == 0) return EP_OK;
+        if (K > 0 && !dev_x) return fail(EP_EINVAL, "null pointer");
+        std::vector<ep::MatDesc> ds;
+        bool nonempty = true;
+        for (int i = 0; i < count; ++i) {
+            ds.push_back(desc_for(w[i], ep::CT_F8E4M3, nullptr, nullptr));
+            nonempty = nonempty && w[i]->view.rows > 0;
+        }
+        if (K == 0 || K % 16 || !nonempty || !ep::fused_many_fits(ds.data(), count, M)) {
+            // each layer's own FP8 forward, in order
+            for (int i = 0; i < count; ++i)
+                if (ep_status st = ep_linear_forward_fp8(w[i], dev_x, M, dev_bias ? dev_bias[i] : nullptr, dev_y[i], hip_stream);
+                    st != EP_OK)
+                    return st;
+            return EP_OK;
+        }
+        if (reinterpret_cast<uintptr_t>(dev_x) & 15) return fail(EP_EINVAL, "X must be 16-byte aligned");
+        int dev = 0;
+        hipError_t he = hipGetDevice(&dev);
+        if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
+        // workspace: X codes [M][K] | X scales [M] | each layer's fp32 partial sums
+        const size_t o_xs = up((size_t)M * (size_t)K, 256);
+        std::vector<size_t> off(count + 1, up(o_xs + 4 * (size_t)M, 256));
+        for (int i = 0; i < count; ++i) off[i + 1] = off[i] + up(ep::fused_partial_bytes(ds[i], M), 256);
+        WsLease ws;
+        if ((he = ws_acquire(dev, s, off[count], &ws)) != hipSuccess)
+            return hip_fail(he, "hipMalloc for the linear forward workspace");
+        uint8_t* ws8 = static_cast<uint8_t*>(ws.ptr);
+        float* xs = reinterpret_cast<float*>(ws8 + o_xs);
+        std::vector<float*> parts(count);
+        std::vector<const uint16_t*> bias(count);
+        std::vector<uint16_t*> ys(count);
+        for (int i = 0; i < count; ++i) {
+            parts[i] = reinterpret_cast<float*>(ws8 + off[i]);
+            bias[i] = dev_bias ? static_cast<const uint16_t*>(dev_bias[i]) : nullptr;
+            ys[i] = static_cast<uint16_t*>(dev_y[i]);
+        }
+        // the activations quantized once for the group, as each layer's own forward quantizes them
+        hipError_t e = ep::launch_quantize_rows_f8(static_cast<const uint16_t*>(dev_x), (int)M, (int)K, (int)K, ws8,
+                                                   (int)K, xs, s);
+        if (e == hipSuccess)
+            e = ep::launch_fused_many_f8(ds.data(), count, ws8, xs, M, parts.data(), bias.data(), ys.data(), s);
+        if (e == hipSuccess) e = ws.queued();
+        return e == hipSuccess ? EP_OK : hip_fail(e, "grouped fused FP8 decode + MFMA launch");
+    });
+}
+
 ep_status ep_linear_forward_noalloc(const ep_handle* w, const void* dev_x, int64_t M, const void* dev_bias,
                                     void* dev_y, void* hip_stream) {
     return guarded([&]() -> ep_status {

@@ -48,6 +48,13 @@ bool fused_many_fits(const MatDesc* ms, int count, int64_t M);
 hipError_t launch_fused_many(const MatDesc* ms, int count, const uint16_t* x, int64_t M, float* const* parts,
                              const uint16_t* const* bias, uint16_t* const* y, hipStream_t stream);
 
+// launch_fused_many in FP8: the E4M3 codes xq [M][cols] and row scales xs [M] of the shared
+// activations, each matrix finished with its own row scales (cols % 16 == 0), each y[i] the same
+// bits as launch_fused_f8 of that matrix alone.
+hipError_t launch_fused_many_f8(const MatDesc* ms, int count, const uint8_t* xq, const float* xs, int64_t M,
+                                float* const* parts, const uint16_t* const* bias, uint16_t* const* y,
+                                hipStream_t stream);
+
 // FP8 variant: the tile pairs decoded into E4M3 codes (the FP8 container) multiplied by per-row
 // E4M3 activation codes xq [M][cols] (scales xs [M]) on v_mfma_f32_16x16x128_f8f6f4 (layout 0) or
 // v_mfma_f32_16x16x32_fp8_fp8 (row layout); y = (sum of the partials) x xs[m] x row_scale[n]

@@ -521,7 +521,7 @@ hipError_t launch_mfma_mt(const GroupArgs& g, uint64_t blocks, hipStream_t strea
 // pairs than the CU's wave slots, or one whose last round of pairs is mostly empty, shares its
 // rounds with the others instead of ending on a pair's latency. Same probability precision N and
 // input width for all matrices.
-template <int N, int MT>
+template <int N, int MT, bool F8>
 __global__ __launch_bounds__(64 * kWaves) void decode_mfma_rows_many(GroupArgs g) {
     extern __shared__ __align__(16) uint8_t smem[];
     if ((uint32_t)(size_t)(lds_u8*)smem != 0u) {
@@ -545,11 +545,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_rows_many(GroupArgs g
         init_lane(t, smem + lds_table_bytes(M.n_tables, M.prob_bits, true), 0);
         const __amdgpu_buffer_rsrc_t rs = payload_rsrc(M);
         const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(M.gemv_x), 0, (int)((size_t)M.gemv_m * M.cols * 2), 0x00020000);
+            const_cast<uint16_t*>(M.gemv_x), 0, (int)((size_t)M.gemv_m * M.cols * (F8 ? 1 : 2)), 0x00020000);
         const uint32_t tiles_r = (M.rows + 15u) / 16u;          // column-major pair order, as above
         for (uint64_t p = p0 + (uint64_t)wave; p < p1; p += kWaves) {
             const uint32_t pc = (uint32_t)p / tiles_r, tr = (uint32_t)p % tiles_r;
-            rows_pair<N, MT, false>(M, T, t, (uint64_t)tr * M.pairs_c + pc, rs, rx);
+            rows_pair<N, MT, F8>(M, T, t, (uint64_t)tr * M.pairs_c + pc, rs, rx);
         }
         if (t.err) atomicOr(M.err, t.err);
     }
@@ -587,23 +587,23 @@ hipError_t launch_rows(const GroupArgs& g, int mt, uint64_t blocks, hipStream_t 
     }
 }
 
-template <int N, int MT>
+template <int N, int MT, bool F8>
 hipError_t launch_rows_many_n(const GroupArgs& g, uint64_t blocks, hipStream_t stream) {
     const MatDesc& m = g.m[0];
     const size_t lds = lds_table_bytes(m.n_tables, m.prob_bits, true) + (size_t)kWaves * 2 * kRingBytes;
-    const void* k = reinterpret_cast<const void*>(decode_mfma_rows_many<N, MT>);
+    const void* k = reinterpret_cast<const void*>(decode_mfma_rows_many<N, MT, F8>);
     hipError_t e = allow_lds(k);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_mfma_rows_many<N, MT>), dim3((unsigned)blocks), dim3(64 * kWaves), lds, stream, g);
+    hipLaunchKernelGGL((decode_mfma_rows_many<N, MT, F8>), dim3((unsigned)blocks), dim3(64 * kWaves), lds, stream, g);
     return hipGetLastError();
 }
 
-template <int MT>
+template <int MT, bool F8>
 hipError_t launch_rows_many_mt(const GroupArgs& g, uint64_t blocks, hipStream_t stream) {
     switch (g.m[0].prob_bits) {
-        case 10: return launch_rows_many_n<10, MT>(g, blocks, stream);
-        case 11: return launch_rows_many_n<11, MT>(g, blocks, stream);
-        default: return launch_rows_many_n<12, MT>(g, blocks, stream);
+        case 10: return launch_rows_many_n<10, MT, F8>(g, blocks, stream);
+        case 11: return launch_rows_many_n<11, MT, F8>(g, blocks, stream);
+        default: return launch_rows_many_n<12, MT, F8>(g, blocks, stream);
     }
 }
 
@@ -696,15 +696,19 @@ bool fused_many_fits(const MatDesc* ms, int count, int64_t M) {
     return true;
 }
 
-hipError_t launch_fused_many(const MatDesc* ms, int count, const uint16_t* x, int64_t M, float* const* parts,
-                             const uint16_t* const* bias, uint16_t* const* y, hipStream_t stream) {
-    if (!fused_many_fits(ms, count, M)) return hipErrorInvalidValue;
+namespace {
+// launch_fused_many and launch_fused_many_f8: x the BF16 activations, or the E4M3 codes with their
+// row scales xs (F8)
+template <bool F8>
+hipError_t fused_many(const MatDesc* ms, int count, const void* x, const float* xs, int64_t M, float* const* parts,
+                      const uint16_t* const* bias, uint16_t* const* y, hipStream_t stream) {
+    if (!fused_many_fits(ms, count, M) || (F8 && (ms[0].cols & 15))) return hipErrorInvalidValue;
     GroupArgs g{};
     g.count = count;
     uint64_t total = 0;
     for (int i = 0; i < count; ++i) {
         g.m[i] = ms[i];
-        g.m[i].gemv_x = x;
+        g.m[i].gemv_x = static_cast<const uint16_t*>(x);
         g.m[i].gemv_m = (uint8_t)M;
         g.m[i].out = parts[i];
         g.cost_start[i] = total;
@@ -718,19 +722,30 @@ hipError_t launch_fused_many(const MatDesc* ms, int count, const uint16_t* x, in
         const uint64_t used = (total + g.block_cost - 1) / g.block_cost;
         hipError_t e;
         switch (mt) {
-            case 1: e = launch_rows_many_mt<1>(g, used, stream); break;
-            case 2: e = launch_rows_many_mt<2>(g, used, stream); break;
-            default: e = launch_rows_many_mt<4>(g, used, stream); break;
+            case 1: e = launch_rows_many_mt<1, F8>(g, used, stream); break;
+            case 2: e = launch_rows_many_mt<2, F8>(g, used, stream); break;
+            default: e = launch_rows_many_mt<4, F8>(g, used, stream); break;
         }
         if (e != hipSuccess) return e;
     }
     for (int i = 0; i < count; ++i) {
         if ((uint64_t)ms[i].rows * ms[i].cols == 0) continue;
-        hipError_t e = launch_finish(parts[i], nullptr, nullptr, bias[i], y[i], (int)M, (int)ms[i].rows,
-                                     (int)ms[i].pairs_c, mt, stream);
+        hipError_t e = launch_finish(parts[i], F8 ? xs : nullptr, F8 ? ms[i].row_scale : nullptr, bias[i], y[i], (int)M,
+                                     (int)ms[i].rows, (int)ms[i].pairs_c, mt, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
+}  // namespace
 
+hipError_t launch_fused_many(const MatDesc* ms, int count, const uint16_t* x, int64_t M, float* const* parts,
+                             const uint16_t* const* bias, uint16_t* const* y, hipStream_t stream) {
+    return fused_many<false>(ms, count, x, nullptr, M, parts, bias, y, stream);
+}
+
+hipError_t launch_fused_many_f8(const MatDesc* ms, int count, const uint8_t* xq, const float* xs, int64_t M,
+                                float* const* parts, const uint16_t* const* bias, uint16_t* const* y,
+                                hipStream_t stream) {
+    return fused_many<true>(ms, count, xq, xs, M, parts, bias, y, stream);
+}
 }  // namespace ep

@@ -248,6 +248,20 @@ ep_status ep_linear_forward(const ep_handle* w, const void* dev_x, int64_t M, co
 ep_status ep_linear_forward_many(const ep_handle* const* w, int count, const void* dev_x, int64_t M,
                                  const void* const* dev_bias, void* const* dev_y, void* hip_stream);
 
+/* ep_linear_forward_many in FP8: Y_i the same bits as ep_linear_forward_fp8(w[i], dev_x, M,
+ * dev_bias[i], dev_y[i]) for every layer. When the layers are row-layout streams with one
+ * prob_bits, 1 <= M <= 64 and K % 16 == 0, the activations are quantized once per row to E4M3 for
+ * the group and one kernel decodes every layer's tile pairs into E4M3 codes for the FP8 MFMA, each
+ * layer finished with its own row scales; otherwise one ep_linear_forward_fp8 per layer, in order.
+ * Source: "EntroPack PyTorch Guide: Lossless Weights, Bitrates and Memory Checks", section
+ * "Replace one linear layer before a whole model"; "EntroPack: Fast and Accurate Entropy-Coded
+ * Weight Compression at Arbitrary Bitrates", Abstract (FP8 among the containers the decode fills).
+ * Grouping layers that share an input is this library's scheduling, not a step of the method.
+ * Arguments, checks and errors as ep_linear_forward_many, plus K % 16 == 0 (EP_EINVAL, from the
+ * per-layer forwards). */
+ep_status ep_linear_forward_fp8_many(const ep_handle* const* w, int count, const void* dev_x, int64_t M,
+                                     const void* const* dev_bias, void* const* dev_y, void* hip_stream);
+
 /* For callers that cannot allocate device memory (code under stream capture, tight serving loops,
  * harnesses that forbid hipMalloc): ep_linear_forward with its scratch in a static device array
  * of 64 MiB per device instead of the library's workspace pool. It calls no hipMalloc, hipFree or

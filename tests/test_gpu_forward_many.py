@@ -106,3 +106,13 @@ def test_abi_refuses_different_input_widths():
     assert rc == -1 and b"widths" in ep.lib().ep_last_error()
     with pytest.raises(ValueError):
         ep.linear_forward_many([a, b], x)
+
+
+@pytest.mark.parametrize("M", [1, 16, 64, 80])
+def test_fp8_group_equals_each_layer(M):
+    """ep_linear_forward_fp8_many: the activations quantized once for the group, every layer the
+    same bits as its own FP8 forward (one launch up to 64 rows, layer by layer above)."""
+    K = 768
+    built = [layer(N, K, sd, bias=sd % 2 == 1) for N, sd in [(300, 61), (512, 62), (40, 63)]]
+    layers = [ep.CompressedLinear(s, b, compute="fp8") for _, s, b in built]
+    same_as_own_forwards(layers, bf16(W.activations(M, K, 64)).cuda())
